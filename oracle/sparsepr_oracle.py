@@ -1,0 +1,527 @@
+"""Plain CPU oracle of one SparsePR attention call (test infrastructure only).
+
+Every function follows one step of the method as the pages describe it, in
+the pages' order; the citation legend is in ``oracle/__init__.py``.  Floating
+point is fp64 everywhere except the two k-means assignment decisions, which
+are taken in fp32 because the GPU kernels take them in fp32 (an argmin is a
+floating-point decision of an integer and both sides must decide in the same
+precision).  Group statistics that feed the router are sequential fp64 sums
+in ascending token order, so the GPU can reproduce them bit for bit.
+
+Readings where the pages are silent (numbers refer to the table of readings
+kept with the design notes; each is a field of ``OracleConfig``):
+  U1  M_s = min(256, N) sampled queries, partial Fisher-Yates driven by
+      splitmix64 seeded with seed XOR (bh * 0x9E3779B97F4A7C15).
+  U2  key coordinates = top r_K = min(32, d, M_s) eigenvectors of M_K scaled
+      by sqrt(eigenvalue) and the softmax scale s.
+  U3  Lloyd k-means, strided seeds floor((j + 1/2) N / G), T = 10 steps, ties
+      to the lowest index, empty clusters keep their centroid.
+  U4  query coordinates are raw (uncentred) logits against the means of the
+      raw keys of each non-empty K/V group.
+  U5  one key k-means, then one query k-means; never re-cluster keys.
+  U6  permuted order: groups in label order, ascending token index inside.
+  U7  router: greedy prefix over estimated per-pair log-probability with a
+      mandatory best cell per query group.
+  U8  pair budget floor(rho N^2) - M N per head.
+  U10 probe allocation stratified over non-empty query groups.
+  U11 probe rows keep their exact dense output.
+  U12 SVD of the unweighted, uncentred probe residuals; rank cut 1e-6 sigma_1.
+  U13 weighted ridge with an unpenalised intercept and absolute lambda.
+  U14 softmax scale s = float32(1/sqrt(d)).
+
+Parity pins live in tests/test_oracle_pins.py.  Functions without a pin that
+is independent of this file: none at present.
+"""
+
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Dict, List, Optional
+
+import numpy as np
+
+MASK64 = (1 << 64) - 1
+GOLDEN64 = 0x9E3779B97F4A7C15
+
+
+# ----------------------------------------------------------------------------
+# configuration
+# ----------------------------------------------------------------------------
+@dataclasses.dataclass
+class OracleConfig:
+    density: float = 0.25          # target executed-pair density rho (probes included)
+    probe_rows: int = 64           # M per (b, h)
+    n_kv_groups: int = 16          # G_K
+    n_q_groups: int = 16           # G_Q
+    residual_rank: int = 32        # r
+    ridge_lambda: float = 1e-3     # absolute lambda
+    kmeans_iters: int = 10         # T
+    n_sample_q: int = 256          # M_s upper bound
+    key_coord_rank: int = 32       # r_K upper bound
+    scale: float = 0.0             # 0 => float32(1/sqrt(d))
+    seed: int = 0
+    partition_mode: str = "response_coupled"   # or "independent"
+    rank_cut: float = 1e-6
+
+
+def softmax_scale(cfg: OracleConfig, d: int) -> float:
+    """Softmax scale as the library uses it: a float32 value promoted to fp64 (U14)."""
+    s = cfg.scale if cfg.scale > 0 else 1.0 / math.sqrt(d)
+    return float(np.float32(s))
+
+
+def budget_pairs(density: float, n: int, m: int) -> int:
+    """Routed-pair budget per head: floor(rho * N^2) - M * N.
+
+    The executed-pair density counts the exact probe rows as well as the
+    routed cells ([TS] 2.C; [NE] NE/exec), so the probes' M*N pairs come out
+    of the budget first (U8).  rho arrives as a float32 value.
+    """
+    rho = float(np.float32(density))
+    return int(math.floor(rho * float(n) * float(n))) - m * n
+
+
+# ----------------------------------------------------------------------------
+# a1: sampled queries and the key-response metric
+# ----------------------------------------------------------------------------
+def splitmix64(state: int):
+    """splitmix64 stream (Steele, Lea and Flood 2014): yields 64-bit outputs."""
+    while True:
+        state = (state + GOLDEN64) & MASK64
+        z = state
+        z = ((z ^ (z >> 30)) * 0xBF58476D1CE4E5B9) & MASK64
+        z = ((z ^ (z >> 27)) * 0x94D049BB133111EB) & MASK64
+        yield z ^ (z >> 31)
+
+
+def sample_queries(n: int, m_s: int, seed: int, bh: int) -> np.ndarray:
+    """A random sample of m_s distinct query rows, sorted ascending.
+
+    The method draws a small random batch of queries to probe every key
+    ([NE] NE/method; [TS] 2.A).  U1: partial Fisher-Yates over 0..n-1 driven by
+    splitmix64 whose state is seed XOR (bh * golden-ratio constant); step j
+    swaps slot j with slot j + (next mod (n - j)).
+    """
+    gen = splitmix64((seed ^ ((bh * GOLDEN64) & MASK64)) & MASK64)
+    swapped: Dict[int, int] = {}
+    out = []
+    for j in range(m_s):
+        t = j + next(gen) % (n - j)
+        vj = swapped.get(j, j)
+        vt = swapped.get(t, t)
+        swapped[j] = vt
+        swapped[t] = vj
+        out.append(vt)
+    return np.sort(np.array(out, dtype=np.int64))
+
+
+def key_metric(q: np.ndarray, sample: np.ndarray) -> np.ndarray:
+    """M_K = Q_s^T Q_s / M_s from the sampled query rows ([TS] 2.A)."""
+    qs = q[sample].astype(np.float64)
+    return qs.T @ qs / float(len(sample))
+
+
+# ----------------------------------------------------------------------------
+# a2-a3: key-response coordinates
+# ----------------------------------------------------------------------------
+def key_coordinates(k: np.ndarray, m_k: np.ndarray, r_k: int, s: float):
+    """Key-response coordinates z_j = s * Lambda_r^{1/2} U_r^T k_j.
+
+    Keys are clustered by how the sampled queries respond to them, through
+    k-means on the eigenvectors of M_K ([TS] 2.A); the response of a key is its
+    logit profile under the sampled queries ([NE] NE/method, the quoted note on
+    key-response coordinates).  Scaling the projection by sqrt(eigenvalue) and
+    by s makes squared distances equal mean squared logit differences when no
+    eigenvector is dropped (U2).  Returns (Z, eigenvalues, eigenvectors) with
+    eigenvalues in descending order.
+    """
+    lam, vec = np.linalg.eigh(m_k)
+    order = np.argsort(-lam, kind="stable")
+    lam = lam[order][:r_k]
+    vec = vec[:, order][:, :r_k]
+    lam_c = np.clip(lam, 0.0, None)
+    z = s * (k.astype(np.float64) @ vec) * np.sqrt(lam_c)[None, :]
+    return z, lam, vec
+
+
+# ----------------------------------------------------------------------------
+# a4/a8: Lloyd k-means
+# ----------------------------------------------------------------------------
+def strided_seeds(n: int, g: int) -> np.ndarray:
+    """Seed indices floor((j + 1/2) n / g), j < g (U3)."""
+    j = np.arange(g, dtype=np.int64)
+    return ((2 * j + 1) * n) // (2 * g)
+
+
+def _seq_mean(rows: np.ndarray) -> np.ndarray:
+    """Mean of rows summed one after another in the given order (fp64)."""
+    return np.add.accumulate(rows.astype(np.float64), axis=0)[-1] / float(rows.shape[0])
+
+
+def kmeans(x: np.ndarray, g: int, iters: int):
+    """Lloyd's k-means with the readings of U3.
+
+    Each step assigns every point to its nearest centre (argmin of
+    ||c||^2 - 2 x.c in float32, lowest index on ties) and then moves every
+    non-empty centre to the fp64 mean of its members; empty centres stay put.
+    Returns the labels of the last assignment and the final centres.
+    """
+    n = x.shape[0]
+    x64 = x.astype(np.float64)
+    c = x64[strided_seeds(n, g)].copy()
+    labels = np.zeros(n, dtype=np.int64)
+    x32 = x64.astype(np.float32)
+    for _ in range(iters):
+        c32 = c.astype(np.float32)
+        dist = (c32 * c32).sum(axis=1)[None, :] - np.float32(2.0) * (x32 @ c32.T)
+        labels = np.argmin(dist, axis=1)
+        for j in range(g):
+            members = np.nonzero(labels == j)[0]
+            if members.size:
+                c[j] = _seq_mean(x64[members])
+    return labels.astype(np.int64), c
+
+
+# ----------------------------------------------------------------------------
+# a5: grouping / permutation
+# ----------------------------------------------------------------------------
+def group_by_labels(labels: np.ndarray, g: int):
+    """Stable grouping: perm (position -> token), counts, exclusive offsets.
+
+    Tokens are laid out group after group so every group is contiguous
+    ([TS] 2.C; [NE] NE/exec); U6 fixes label order and ascending token index.
+    """
+    perm = np.argsort(labels, kind="stable").astype(np.int64)
+    counts = np.bincount(labels, minlength=g).astype(np.int64)
+    offsets = np.zeros(g + 1, dtype=np.int64)
+    offsets[1:] = np.cumsum(counts)
+    return perm, counts, offsets
+
+
+def group_means(x: np.ndarray, perm: np.ndarray, offsets: np.ndarray) -> np.ndarray:
+    """fp64 mean of each group's rows, summed in ascending token order.
+
+    Empty groups get NaN rows (they are never used).
+    """
+    g = len(offsets) - 1
+    out = np.full((g, x.shape[1]), np.nan)
+    for j in range(g):
+        a, b = offsets[j], offsets[j + 1]
+        if b > a:
+            out[j] = _seq_mean(x[perm[a:b]])
+    return out
+
+
+# ----------------------------------------------------------------------------
+# a7: query-response coordinates
+# ----------------------------------------------------------------------------
+def query_coordinates(q: np.ndarray, cbar_nonempty: np.ndarray, s: float) -> np.ndarray:
+    """u_{i,h} = s * q_i . cbar_h: each query's pre-softmax logits against the
+    K/V group centres ([TS] 2.A, [NE] NE/method).  U4: raw, uncentred."""
+    return s * (q.astype(np.float64) @ cbar_nonempty.T)
+
+
+# ----------------------------------------------------------------------------
+# a10: router
+# ----------------------------------------------------------------------------
+def route(qbar: np.ndarray, nq: np.ndarray, cbar: np.ndarray, nk: np.ndarray,
+          s: float, density: float, n: int, m: int) -> dict:
+    """Grant (query-group, key-group) cells under the pair budget.
+
+    The budget is spent in true pairs, the product of the two groups' token
+    counts, not in cells ([NE] NE/exec).  U7: the estimated log-probability of
+    one key of group h for a query of group g is
+        key_gh = mu_gh - log sum_h' n_h' exp(mu_gh'),  mu_gh = s qbar_g . cbar_h,
+    every non-empty g first gets its best cell argmax_h mu_gh, then the other
+    cells are taken in order (key desc, g asc, h asc) as the longest prefix
+    that fits.  mu is a sequential fp64 dot product without fused multiply-add.
+    """
+    gq, gk = len(nq), len(nk)
+    d = qbar.shape[1]
+    valid_q = nq > 0
+    valid_k = nk > 0
+    cost = np.outer(nq, nk).astype(np.int64)
+    result = {"mu": None, "key": None, "mandatory": np.full(gq, -1, dtype=np.int64)}
+    if float(np.float32(density)) >= 1.0:
+        granted = valid_q[:, None] & valid_k[None, :]
+        result.update(granted=granted, budget=n * n, mandatory_cost=0)
+        return _route_stats(result, cost, n, m)
+
+    qz = np.where(valid_q[:, None], qbar, 0.0)
+    cz = np.where(valid_k[:, None], cbar, 0.0)
+    acc = np.zeros((gq, gk))
+    for t in range(d):
+        acc = acc + np.multiply.outer(qz[:, t], cz[:, t])
+    mu = acc * s
+    mu = np.where(np.isnan(mu), -np.inf, mu)
+    key = np.full((gq, gk), -np.inf)
+    mandatory = np.full(gq, -1, dtype=np.int64)
+    hs = np.nonzero(valid_k)[0]
+    for g in range(gq):
+        if not valid_q[g] or hs.size == 0:
+            continue
+        row = mu[g]
+        best = hs[0]
+        for h in hs:
+            if row[h] > row[best]:
+                best = h
+        mandatory[g] = best
+        mx = row[best]
+        if not np.isfinite(mx):
+            continue
+        tot = 0.0
+        for h in hs:
+            tot = tot + float(nk[h]) * math.exp(row[h] - mx)
+        ell = mx + math.log(tot)
+        key[g, hs] = row[hs] - ell
+
+    budget = budget_pairs(density, n, m)
+    granted = np.zeros((gq, gk), dtype=bool)
+    mand_cost = 0
+    for g in range(gq):
+        if mandatory[g] >= 0:
+            granted[g, mandatory[g]] = True
+            mand_cost += int(cost[g, mandatory[g]])
+    cand_g, cand_h = np.nonzero(valid_q[:, None] & valid_k[None, :] & ~granted)
+    cand_key = key[cand_g, cand_h]
+    order = np.lexsort((cand_h, cand_g, -cand_key))
+    cum = np.cumsum(cost[cand_g[order], cand_h[order]])
+    take = int(np.searchsorted(cum, budget - mand_cost, side="right")) if cum.size else 0
+    granted[cand_g[order[:take]], cand_h[order[:take]]] = True
+    result.update(mu=mu, key=key, mandatory=mandatory, granted=granted, budget=budget,
+                  mandatory_cost=mand_cost, order_g=cand_g[order], order_h=cand_h[order],
+                  n_prefix=take)
+    return _route_stats(result, cost, n, m)
+
+
+def _route_stats(result: dict, cost: np.ndarray, n: int, m: int) -> dict:
+    granted = result["granted"]
+    routed = int(cost[granted].sum())
+    result["routed_pairs"] = routed
+    result["rho_route"] = routed / float(n * n)
+    result["rho_exec"] = (routed + m * n) / float(n * n)
+    result["over_budget"] = routed > result["budget"]
+    gq = granted.shape[0]
+    rowptr = np.zeros(gq + 1, dtype=np.int64)
+    cols: List[int] = []
+    for g in range(gq):
+        hh = np.nonzero(granted[g])[0]
+        cols.extend(int(h) for h in hh)
+        rowptr[g + 1] = len(cols)
+    result["csr_rowptr"] = rowptr
+    result["csr_cols"] = np.array(cols, dtype=np.int64)
+    return result
+
+
+# ----------------------------------------------------------------------------
+# a11: probes
+# ----------------------------------------------------------------------------
+def select_probes(offsets: np.ndarray, m: int):
+    """Probe rows stratified by query group, and their design weights.
+
+    Probes are taken evenly from every query group so each group has exact rows
+    ([NE] NE/method, "query-group-stratified"; [TS] 2.B, M << N_q); 64 per head
+    by default.  U10 fixes the integer rule.  Positions are in permuted order;
+    weights are n_g / m_g normalised to sum to M.
+    """
+    sizes = np.diff(offsets)
+    ne = [g for g in range(len(sizes)) if sizes[g] > 0]
+    gp = len(ne)
+    mg = np.zeros(len(sizes), dtype=np.int64)
+    if m <= 0 or gp == 0:
+        return np.zeros(0, dtype=np.int64), np.zeros(0), mg
+    if m >= gp:
+        base, rem = divmod(m, gp)
+        carry = 0
+        for rank, g in enumerate(ne):
+            want = base + (1 if rank < rem else 0) + carry
+            mg[g] = min(want, sizes[g])
+            carry = want - mg[g]
+        while carry > 0:
+            for g in ne:
+                add = min(carry, sizes[g] - mg[g])
+                mg[g] += add
+                carry -= add
+                if carry == 0:
+                    break
+    else:
+        for j in range(m):
+            mg[ne[((2 * j + 1) * gp) // (2 * m)]] += 1
+    pos, raw = [], []
+    for g in ne:
+        for t in range(mg[g]):
+            pos.append(offsets[g] + ((2 * t + 1) * sizes[g]) // (2 * mg[g]))
+            raw.append(sizes[g] / mg[g])
+    raw = np.array(raw, dtype=np.float64)
+    w = raw * (m / raw.sum())
+    return np.array(pos, dtype=np.int64), w, mg
+
+
+# ----------------------------------------------------------------------------
+# a12-a13: attention
+# ----------------------------------------------------------------------------
+def _softmax_rows(logits: np.ndarray) -> np.ndarray:
+    mx = logits.max(axis=1, keepdims=True)
+    p = np.exp(logits - mx)
+    return p / p.sum(axis=1, keepdims=True)
+
+
+def dense_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, s: float) -> np.ndarray:
+    """softmax(s q k^T) v in fp64, rows of q against all keys."""
+    return _softmax_rows(s * (q.astype(np.float64) @ k.astype(np.float64).T)) @ v.astype(np.float64)
+
+
+def sparse_attention(qp: np.ndarray, kp: np.ndarray, vp: np.ndarray, granted: np.ndarray,
+                     off_q: np.ndarray, off_k: np.ndarray, s: float) -> np.ndarray:
+    """Block-sparse output in permuted order.
+
+    Every query row attends only to the keys of the K/V groups granted to its
+    query group, with softmax over exactly those keys ([TS] 2.C).
+    """
+    n, d = qp.shape
+    out = np.zeros((n, d))
+    for g in range(len(off_q) - 1):
+        a, b = off_q[g], off_q[g + 1]
+        if b <= a:
+            continue
+        idx = np.concatenate([np.arange(off_k[h], off_k[h + 1]) for h in np.nonzero(granted[g])[0]]
+                             + [np.zeros(0, dtype=np.int64)])
+        if idx.size == 0:
+            out[a:b] = np.nan
+            continue
+        out[a:b] = dense_attention(qp[a:b], kp[idx], vp[idx], s)
+    return out
+
+
+# ----------------------------------------------------------------------------
+# a14: probe-fitted residual reconstruction
+# ----------------------------------------------------------------------------
+def fit_residual(r: np.ndarray, x: np.ndarray, w: np.ndarray, rank: int, lam: float,
+                 cut: float = 1e-6) -> dict:
+    """Fit R ~ b + x B inside the top singular subspace of the probe residuals.
+
+    The residual of a probe row is its exact dense output minus its sparse
+    output ([TS] 2.B).  It is modelled as an affine function of the sparse
+    output, fitted per call with ridge regularisation ([TS] 2.B; [DG] weighted
+    affine fit; [NE] NE/method ridge regression), and the map is confined to the
+    span of the leading right singular vectors of the probe residuals ([TS] 2.B;
+    [NE] NE/method keeps 16).  U12/U13: unweighted uncentred SVD of R, rank
+    r' = min(rank, M, d, #{sigma > cut sigma_1}); weighted least squares with an
+    unpenalised intercept:
+        W = (Xc^T D Xc + lam I)^-1 Xc^T D Yc,  Y = R V,  b' = ybar - xbar W,
+        B = W V^T,  b = b' V^T.
+    """
+    m, d = r.shape
+    out = {"rank": 0, "sigma": np.zeros(0), "V": np.zeros((d, 0)), "W": np.zeros((d, 0)),
+           "B": np.zeros((d, d)), "b": np.zeros(d)}
+    if m == 0:
+        return out
+    _, sig, vt = np.linalg.svd(r, full_matrices=False)
+    out["sigma"] = sig
+    if sig.size == 0 or not (sig[0] > 0):
+        return out
+    rp = int(min(rank, m, d, int((sig > cut * sig[0]).sum())))
+    if rp == 0:
+        return out
+    v = vt[:rp].T
+    y = r @ v
+    ws = w.sum()
+    xbar = (w[:, None] * x).sum(axis=0) / ws
+    ybar = (w[:, None] * y).sum(axis=0) / ws
+    xc = x - xbar
+    yc = y - ybar
+    a = xc.T @ (w[:, None] * xc) + lam * np.eye(d)
+    wmat = np.linalg.solve(a, xc.T @ (w[:, None] * yc))
+    bprime = ybar - xbar @ wmat
+    out.update(rank=rp, V=v, W=wmat, bprime=bprime, B=wmat @ v.T, b=bprime @ v.T,
+               xbar=xbar, ybar=ybar)
+    return out
+
+
+# ----------------------------------------------------------------------------
+# whole call
+# ----------------------------------------------------------------------------
+def sparsepr_head(q: np.ndarray, k: np.ndarray, v: np.ndarray, cfg: OracleConfig, bh: int = 0,
+                  q_labels: Optional[np.ndarray] = None,
+                  kv_labels: Optional[np.ndarray] = None) -> dict:
+    """One (batch, head) slice of a SparsePR call, every intermediate returned.
+
+    Stage order follows the latency chain the pages account for: partition
+    construction, routing, tensor reorder, sparse attention, exact probe rows,
+    residual fit, correction, output restoration ([NE] NE/exec).  Passing both
+    label arrays skips partitioning (used to check later stages in isolation).
+    """
+    n, d = q.shape
+    s = softmax_scale(cfg, d)
+    q64, k64, v64 = (t.astype(np.float64) for t in (q, k, v))
+    res: dict = {"scale": s}
+    gk, gq = cfg.n_kv_groups, cfg.n_q_groups
+
+    if kv_labels is None or q_labels is None:
+        if cfg.partition_mode == "response_coupled":
+            m_s = min(cfg.n_sample_q, n)
+            sample = sample_queries(n, m_s, cfg.seed, bh)
+            m_k = key_metric(q64, sample)
+            r_k = min(cfg.key_coord_rank, d, m_s)
+            z, lam, vec = key_coordinates(k64, m_k, r_k, s)
+            kv_labels, _ = kmeans(z, gk, cfg.kmeans_iters)
+            perm_k, nk, off_k = group_by_labels(kv_labels, gk)
+            cbar = group_means(k64, perm_k, off_k)
+            u = query_coordinates(q64, cbar[nk > 0], s)
+            q_labels, _ = kmeans(u, gq, cfg.kmeans_iters)
+            res.update(sample=sample, m_k=m_k, eigvals=lam, eigvecs=vec, z=z, u=u)
+        elif cfg.partition_mode == "independent":
+            kv_labels, _ = kmeans(k64, gk, cfg.kmeans_iters)
+            q_labels, _ = kmeans(q64, gq, cfg.kmeans_iters)
+        else:
+            raise ValueError(cfg.partition_mode)
+
+    kv_labels = np.asarray(kv_labels, dtype=np.int64)
+    q_labels = np.asarray(q_labels, dtype=np.int64)
+    perm_k, nk, off_k = group_by_labels(kv_labels, gk)
+    perm_q, nq, off_q = group_by_labels(q_labels, gq)
+    cbar = group_means(k64, perm_k, off_k)
+    qbar = group_means(q64, perm_q, off_q)
+    m = min(cfg.probe_rows, n)
+    rt = route(qbar, nq, cbar, nk, s, cfg.density, n, m)
+
+    qp, kp, vp = q64[perm_q], k64[perm_k], v64[perm_k]
+    o_sp = sparse_attention(qp, kp, vp, rt["granted"], off_q, off_k, s)
+
+    probes, w, mg = select_probes(off_q, m)
+    o_de = dense_attention(qp[probes], kp, vp, s) if probes.size else np.zeros((0, d))
+    resid = o_de - o_sp[probes]
+    fit = fit_residual(resid, o_sp[probes], w, cfg.residual_rank, cfg.ridge_lambda, cfg.rank_cut)
+
+    corrected = o_sp + fit["b"][None, :] + o_sp @ fit["B"]
+    corrected[probes] = o_de
+    out = np.empty_like(corrected)
+    out[perm_q] = corrected
+    hard = np.empty_like(o_sp)
+    hard[perm_q] = o_sp
+
+    res.update(q_labels=q_labels, kv_labels=kv_labels, perm_q=perm_q, perm_k=perm_k,
+               nq=nq, nk=nk, off_q=off_q, off_k=off_k, qbar=qbar, cbar=cbar, route=rt,
+               o_sparse_perm=o_sp, probes=probes, probe_weights=w, probes_per_group=mg,
+               o_dense_probe=o_de, residual=resid, fit=fit, out=out, hard_drop=hard)
+    return res
+
+
+def sparsepr_call(q, k, v, cfg: OracleConfig, return_heads: bool = False):
+    """Full call over [B, H, N, d] arrays (NumPy or CPU torch tensors).
+
+    Returns the corrected output as fp64 [B, H, N, d] (and the per-head
+    intermediates when asked).
+    """
+    q, k, v = (np.asarray(t.float().numpy() if hasattr(t, "numpy") else t) for t in (q, k, v))
+    b_, h_, n, d = q.shape
+    out = np.zeros((b_, h_, n, d))
+    heads = []
+    for b in range(b_):
+        for h in range(h_):
+            r = sparsepr_head(q[b, h], k[b, h], v[b, h], cfg, bh=b * h_ + h)
+            out[b, h] = r["out"]
+            if return_heads:
+                heads.append(r)
+    return (out, heads) if return_heads else out
