@@ -1,0 +1,707 @@
+// Attention kernels for gfx950: block-sparse flash attention over the
+// group-permuted layout, exact probe rows, probe-row overwrite, dense baseline.
+//
+// Sources (page title, section):
+//   [TS] "Resumen Técnico: SparsePR ..." (gist.science) 2.C: tokens are permuted into
+//        group-contiguous order and attention runs over variable-size blocks; 2.B:
+//        probe rows are evaluated exactly and R = O_dense - O_sparse; the fitted map
+//        corrects the unprobed rows.
+//   [NE] news explainer reposted from 科技行者, section "稀疏执行怎么落地，误差怎么算才公平":
+//        the output restoration step returns rows to token order.
+//
+// Work decomposition: a workgroup owns up to 128 rows of one query group and
+// streams the concatenation of that group's granted key groups ("virtual key
+// sequence") in 64-key tiles, so only the end of the whole sequence is ragged,
+// not every granted cell.
+#include <string.h>
+
+#include "sp_kernels.h"
+
+namespace sp {
+
+struct AttnArgs {
+  View4 qv, kv, vv;       // row addressing of the (permuted or original) inputs
+  MutView4 o;
+  const int* perm_q;      // position -> token (null: identity)
+  const int* off_k;
+  const int* csr_ptr;
+  const int* csr_col;
+  const int* tiles;
+  const int* ntiles;
+  int max_tiles;
+  const float* fitW;
+  const float* fitV;
+  const float* fitb;
+  const int* fitrank;
+  int R;
+  int N, GK, GQ;
+  float scale;
+  int correct;
+  int dense;
+};
+
+__device__ inline int seg_find(const int* sv, int n, int v) {
+  int lo = 0, hi = n - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (sv[mid] <= v) lo = mid;
+    else hi = mid - 1;
+  }
+  return lo;
+}
+
+// exclusive scan of one int per thread over the block (blockDim multiple of 64)
+__device__ inline int block_excl_scan(int v, int* tmp, int* total) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, nw = blockDim.x >> 6;
+  int inc = v;
+  for (int o = 1; o < 64; o <<= 1) {
+    const int t = __shfl_up(inc, o, 64);
+    if (lane >= o) inc += t;
+  }
+  if (lane == 63) tmp[w] = inc;
+  __syncthreads();
+  int base = 0, tot = 0;
+  for (int i = 0; i < nw; ++i) {
+    if (i < w) base += tmp[i];
+    tot += tmp[i];
+  }
+  __syncthreads();
+  *total = tot;
+  return base + inc - v;
+}
+
+// Resolve the work item and build the virtual key sequence of its query group.
+// Returns false when the workgroup has nothing to do.
+template <int PER>
+__device__ inline bool setup_item(const AttnArgs& a, int bh, int tile, int* seg_v, int* seg_p, int* tmp,
+                                  int* g_out, int* row0, int* nrows, int* nseg, int* L) {
+  const int tid = threadIdx.x;
+  if (a.dense) {
+    *row0 = tile * kTileRows;
+    if (*row0 >= a.N) return false;
+    *nrows = min(kTileRows, a.N - *row0);
+    *g_out = 0;
+    if (tid == 0) {
+      seg_v[0] = 0;
+      seg_p[0] = 0;
+      seg_v[1] = a.N;
+    }
+    *nseg = 1;
+    *L = a.N;
+    __syncthreads();
+    return true;
+  }
+  if (tile >= a.ntiles[bh]) return false;
+  const int* e = a.tiles + ((long long)bh * a.max_tiles + tile) * 4;
+  const int g = e[0];
+  *g_out = g;
+  *row0 = e[1];
+  *nrows = e[2];
+  const int* cp = a.csr_ptr + (long long)bh * (a.GQ + 1);
+  const int c0 = cp[g], nc = cp[g + 1] - c0;
+  const int* cols = a.csr_col + (long long)bh * a.GQ * a.GK + c0;
+  const int* offk = a.off_k + (long long)bh * (a.GK + 1);
+  int lens[PER];
+  int lsum = 0;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int idx = PER * tid + i;
+    int l = 0;
+    if (idx < nc) {
+      const int h = cols[idx];
+      l = offk[h + 1] - offk[h];
+      seg_p[idx] = offk[h];
+    }
+    lens[i] = l;
+    lsum += l;
+  }
+  int total;
+  int ex = block_excl_scan(lsum, tmp, &total);
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int idx = PER * tid + i;
+    if (idx < nc) seg_v[idx] = ex;
+    ex += lens[i];
+  }
+  if (tid == 0) seg_v[nc] = total;
+  *nseg = nc;
+  *L = total;
+  __syncthreads();
+  return true;
+}
+
+// ============================================================================
+// bf16 MFMA kernel.  Per wave: 32 query rows.  S^T = K Q^T (A = K tile from
+// LDS, B = Q rows in registers) so each lane holds one query row; the online
+// softmax needs one cross-half exchange.  O^T = V^T P^T with V transposed in
+// LDS; the contraction order over keys inside a 16-key step follows the S^T
+// register layout (keys 16s + 4h + {0..3} and 16s + 8 + 4h + {0..3}).
+// ============================================================================
+template <int D>
+__global__ __launch_bounds__(256, 2) void k_sparse_attn_mfma(AttnArgs a) {
+  constexpr int KS = D / 16, DB = D / 32;
+  constexpr int LDK = D + 8, LDV = 64 + 8;
+  constexpr int CPR = D / 8;
+  __shared__ __attribute__((aligned(16))) bf16_t Ks[64 * LDK];
+  __shared__ __attribute__((aligned(16))) bf16_t Vt[D * LDV];
+  __shared__ int seg_v[kMaxGroups + 1], seg_p[kMaxGroups + 1];
+  __shared__ int tmp[8];
+  const int bh = blockIdx.y, tile = blockIdx.x, tid = threadIdx.x;
+  const int w = tid >> 6, lane = tid & 63, half = lane >> 5, col = lane & 31;
+  int g, row0, nrows, nseg, L;
+  if (!setup_item<4>(a, bh, tile, seg_v, seg_p, tmp, &g, &row0, &nrows, &nseg, &L)) return;
+  const bool wave_active = 32 * w < nrows;
+  const int qr = 32 * w + col;
+  const bool qvalid = qr < nrows;
+
+  const bf16_t* qb = static_cast<const bf16_t*>(a.qv.p);
+  const bf16_t* kb = static_cast<const bf16_t*>(a.kv.p);
+  const bf16_t* vb = static_cast<const bf16_t*>(a.vv.p);
+  bf16x8 qf[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    uint4 u = make_uint4(0, 0, 0, 0);
+    if (qvalid) u = *reinterpret_cast<const uint4*>(qb + a.qv.row_off(bh, row0 + qr) + 16 * ks + 8 * half);
+    qf[ks] = __builtin_bit_cast(bf16x8, u);
+  }
+  f32x16 o[DB];
+#pragma unroll
+  for (int b = 0; b < DB; ++b) o[b] = f32x16{};
+  float m = -INFINITY, l = 0.f;
+  const float c = a.scale * 1.4426950408889634f;
+
+  for (int kt0 = 0; kt0 < L; kt0 += 64) {
+#pragma unroll
+    for (int i = 0; i < (64 * CPR) / 256; ++i) {
+      const int e = tid + 256 * i;
+      const int r = e / CPR, c8 = e - (e / CPR) * CPR;
+      const int v = kt0 + r;
+      uint4 kv4 = make_uint4(0, 0, 0, 0), vv4 = make_uint4(0, 0, 0, 0);
+      if (v < L) {
+        const int s = seg_find(seg_v, nseg, v);
+        const int prow = seg_p[s] + v - seg_v[s];
+        kv4 = *reinterpret_cast<const uint4*>(kb + a.kv.row_off(bh, prow) + 8 * c8);
+        vv4 = *reinterpret_cast<const uint4*>(vb + a.vv.row_off(bh, prow) + 8 * c8);
+      }
+      *reinterpret_cast<uint4*>(Ks + r * LDK + 8 * c8) = kv4;
+      const bf16_t* ve = reinterpret_cast<const bf16_t*>(&vv4);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) Vt[(8 * c8 + j) * LDV + r] = ve[j];
+    }
+    __syncthreads();
+    if (wave_active) {
+      f32x16 sacc[2];
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        sacc[kt] = f32x16{};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const bf16x8 kf = *reinterpret_cast<const bf16x8*>(Ks + (32 * kt + col) * LDK + 16 * ks + 8 * half);
+          sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], sacc[kt], 0, 0, 0);
+        }
+      }
+      float mloc = -INFINITY;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = 32 * kt + (r & 3) + 8 * (r >> 2) + 4 * half;
+          float sv = sacc[kt][r] * c;
+          if (kt0 + key >= L) sv = -INFINITY;
+          sacc[kt][r] = sv;
+          mloc = fmaxf(mloc, sv);
+        }
+      mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
+      const float mnew = fmaxf(m, mloc);
+      const float mb = mnew == -INFINITY ? 0.f : mnew;
+      const float alpha = exp2f(m - mb);
+      float psum = 0.f;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float pv = exp2f(sacc[kt][r] - mb);
+          sacc[kt][r] = pv;
+          psum += pv;
+        }
+      l = l * alpha + psum;
+      m = mnew;
+#pragma unroll
+      for (int b = 0; b < DB; ++b) o[b] *= alpha;
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        const int kt = st >> 1, rb = 8 * (st & 1);
+        uint4 pk;
+        pk.x = (uint32_t)f32_to_bf16(sacc[kt][rb + 0]) | ((uint32_t)f32_to_bf16(sacc[kt][rb + 1]) << 16);
+        pk.y = (uint32_t)f32_to_bf16(sacc[kt][rb + 2]) | ((uint32_t)f32_to_bf16(sacc[kt][rb + 3]) << 16);
+        pk.z = (uint32_t)f32_to_bf16(sacc[kt][rb + 4]) | ((uint32_t)f32_to_bf16(sacc[kt][rb + 5]) << 16);
+        pk.w = (uint32_t)f32_to_bf16(sacc[kt][rb + 6]) | ((uint32_t)f32_to_bf16(sacc[kt][rb + 7]) << 16);
+        const bf16x8 pf = __builtin_bit_cast(bf16x8, pk);
+#pragma unroll
+        for (int b = 0; b < DB; ++b) {
+          const bf16_t* vrow = Vt + (32 * b + col) * LDV + 16 * st + 4 * half;
+          const uint2 lo = *reinterpret_cast<const uint2*>(vrow);
+          const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 8);
+          const bf16x8 vf = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+          o[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, o[b], 0, 0, 0);
+        }
+      }
+    }
+    __syncthreads();
+  }
+
+  // ---- epilogue: normalise, correct (b + x W V^T), restore token order
+  const float ltot = l + __shfl_xor(l, 32, 64);
+  const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
+  float x[DB][16];
+#pragma unroll
+  for (int b = 0; b < DB; ++b)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) x[b][r] = o[b][r] * inv;
+  const int rank = (a.correct && a.fitrank) ? a.fitrank[bh] : 0;
+  if (rank > 0) {
+    float* Wl = reinterpret_cast<float*>(Ks);  // D x 33 floats fit in the K tile region
+    float* Vl = reinterpret_cast<float*>(Vt);
+    float corr[DB][16];
+    const float* fb = a.fitb + (long long)bh * D;
+#pragma unroll
+    for (int b = 0; b < DB; ++b)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) corr[b][r] = fb[32 * b + (r & 3) + 8 * (r >> 2) + 4 * half];
+    const float* fw = a.fitW + (long long)bh * D * a.R;
+    const float* fv = a.fitV + (long long)bh * D * a.R;
+    for (int j0 = 0; j0 < rank; j0 += 32) {
+      const int nj = min(32, rank - j0);
+      __syncthreads();
+      for (int e = tid; e < D * 32; e += 256) {
+        const int dm = e >> 5, j = e & 31;
+        Wl[dm * 33 + j] = j < nj ? fw[(long long)dm * a.R + j0 + j] : 0.f;
+        Vl[dm * 33 + j] = j < nj ? fv[(long long)dm * a.R + j0 + j] : 0.f;
+      }
+      __syncthreads();
+      if (wave_active) {
+        float t[32];
+#pragma unroll
+        for (int j = 0; j < 32; ++j) t[j] = 0.f;
+#pragma unroll
+        for (int b = 0; b < DB; ++b)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int dm = 32 * b + (r & 3) + 8 * (r >> 2) + 4 * half;
+            const float xv = x[b][r];
+#pragma unroll
+            for (int j = 0; j < 32; ++j) t[j] += xv * Wl[dm * 33 + j];
+          }
+#pragma unroll
+        for (int j = 0; j < 32; ++j) t[j] += __shfl_xor(t[j], 32, 64);
+#pragma unroll
+        for (int b = 0; b < DB; ++b)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int dm = 32 * b + (r & 3) + 8 * (r >> 2) + 4 * half;
+            float acc = 0.f;
+#pragma unroll
+            for (int j = 0; j < 32; ++j) acc += t[j] * Vl[dm * 33 + j];
+            corr[b][r] += acc;
+          }
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < DB; ++b)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) x[b][r] += corr[b][r];
+  }
+  if (!(wave_active && qvalid)) return;
+  const int pos = row0 + qr;
+  const int token = a.perm_q ? a.perm_q[(long long)bh * a.N + pos] : pos;
+  bf16_t* orow = static_cast<bf16_t*>(a.o.p) + a.o.row_off(bh, token);
+#pragma unroll
+  for (int b = 0; b < DB; ++b)
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const int dm = 32 * b + 8 * r4 + 4 * half;
+      uint2 pk;
+      pk.x = (uint32_t)f32_to_bf16(x[b][4 * r4 + 0]) | ((uint32_t)f32_to_bf16(x[b][4 * r4 + 1]) << 16);
+      pk.y = (uint32_t)f32_to_bf16(x[b][4 * r4 + 2]) | ((uint32_t)f32_to_bf16(x[b][4 * r4 + 3]) << 16);
+      *reinterpret_cast<uint2*>(orow + dm) = pk;
+    }
+}
+
+// ============================================================================
+// Vector-ALU kernel (fp32 inputs; also usable for bf16).  128 rows x 4 threads.
+// ============================================================================
+template <typename T, int D>
+__global__ __launch_bounds__(512) void k_sparse_attn_vec(AttnArgs a) {
+  constexpr int DQ = D / 4;
+  __shared__ float Kt[32][D + 1];
+  __shared__ float Vs[32][D + 1];
+  __shared__ int seg_v[kMaxGroups + 1], seg_p[kMaxGroups + 1];
+  __shared__ int tmp[8];
+  const int bh = blockIdx.y, tile = blockIdx.x, tid = threadIdx.x;
+  int g, row0, nrows, nseg, L;
+  if (!setup_item<2>(a, bh, tile, seg_v, seg_p, tmp, &g, &row0, &nrows, &nseg, &L)) return;
+  const int rl = tid >> 2, sub = tid & 3;
+  const bool valid = rl < nrows;
+  const T* qb = static_cast<const T*>(a.qv.p);
+  const T* kb = static_cast<const T*>(a.kv.p);
+  const T* vb = static_cast<const T*>(a.vv.p);
+  float q[DQ], o[DQ];
+#pragma unroll
+  for (int i = 0; i < DQ; ++i) {
+    q[i] = valid ? Elem<T>::load(qb + a.qv.row_off(bh, row0 + rl) + sub + 4 * i) : 0.f;
+    o[i] = 0.f;
+  }
+  float m = -INFINITY, l = 0.f;
+  const float c = a.scale * 1.4426950408889634f;
+  for (int kt0 = 0; kt0 < L; kt0 += 32) {
+    for (int e = tid; e < 32 * D; e += 512) {
+      const int r = e / D, cc = e - (e / D) * D;
+      const int v = kt0 + r;
+      float kx = 0.f, vx = 0.f;
+      if (v < L) {
+        const int s = seg_find(seg_v, nseg, v);
+        const int prow = seg_p[s] + v - seg_v[s];
+        kx = Elem<T>::load(kb + a.kv.row_off(bh, prow) + cc);
+        vx = Elem<T>::load(vb + a.vv.row_off(bh, prow) + cc);
+      }
+      Kt[r][cc] = kx;
+      Vs[r][cc] = vx;
+    }
+    __syncthreads();
+    float sc[32];
+    float mloc = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+      float p = 0.f;
+#pragma unroll
+      for (int i = 0; i < DQ; ++i) p += q[i] * Kt[j][sub + 4 * i];
+      p += __shfl_xor(p, 1, 64);
+      p += __shfl_xor(p, 2, 64);
+      sc[j] = (kt0 + j < L) ? p * c : -INFINITY;
+      mloc = fmaxf(mloc, sc[j]);
+    }
+    const float mnew = fmaxf(m, mloc);
+    const float mb = mnew == -INFINITY ? 0.f : mnew;
+    const float alpha = exp2f(m - mb);
+    float psum = 0.f;
+#pragma unroll
+    for (int i = 0; i < DQ; ++i) o[i] *= alpha;
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+      const float p = exp2f(sc[j] - mb);
+      psum += p;
+#pragma unroll
+      for (int i = 0; i < DQ; ++i) o[i] += p * Vs[j][sub + 4 * i];
+    }
+    l = l * alpha + psum;
+    m = mnew;
+    __syncthreads();
+  }
+  const float inv = l > 0.f ? 1.f / l : 0.f;
+  float x[DQ];
+#pragma unroll
+  for (int i = 0; i < DQ; ++i) x[i] = o[i] * inv;
+  const int rank = (a.correct && a.fitrank) ? a.fitrank[bh] : 0;
+  if (rank > 0) {
+    const float* fw = a.fitW + (long long)bh * D * a.R;
+    const float* fv = a.fitV + (long long)bh * D * a.R;
+    const float* fb = a.fitb + (long long)bh * D;
+    float corr[DQ];
+#pragma unroll
+    for (int i = 0; i < DQ; ++i) corr[i] = fb[sub + 4 * i];
+    for (int j = 0; j < rank; ++j) {
+      float t = 0.f;
+#pragma unroll
+      for (int i = 0; i < DQ; ++i) t += x[i] * fw[(long long)(sub + 4 * i) * a.R + j];
+      t += __shfl_xor(t, 1, 64);
+      t += __shfl_xor(t, 2, 64);
+#pragma unroll
+      for (int i = 0; i < DQ; ++i) corr[i] += t * fv[(long long)(sub + 4 * i) * a.R + j];
+    }
+#pragma unroll
+    for (int i = 0; i < DQ; ++i) x[i] += corr[i];
+  }
+  if (!valid) return;
+  const int pos = row0 + rl;
+  const int token = a.perm_q ? a.perm_q[(long long)bh * a.N + pos] : pos;
+  T* orow = static_cast<T*>(a.o.p) + a.o.row_off(bh, token);
+#pragma unroll
+  for (int i = 0; i < DQ; ++i) Elem<T>::store(orow + sub + 4 * i, x[i]);
+}
+
+// ============================================================================
+// Probe rows: exact dense output and the sparse output under the probe's own
+// granted cells, from one pass over a key chunk (split-K), then a merge.
+// ============================================================================
+struct ProbeArgs {
+  View4 qv, kv, vv;  // permuted arrays
+  const int* ppos;
+  const int* pgroup;
+  const int* kgroup;
+  const uint32_t* gmask;
+  int gwords;
+  int N, M, GQ, n_pchunk;
+  float scale;
+  float* ppart;  // [BH, n_pchunk, 2, M, D + 2]
+  float* ode;
+  float* osp;
+};
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void k_probe_attn_vec(ProbeArgs a) {
+  constexpr int DQ = D / 4;
+  __shared__ float Kt[32][D + 1];
+  __shared__ float Vs[32][D + 1];
+  __shared__ int kg[32];
+  __shared__ uint32_t msk[64][33];
+  const int bh = blockIdx.z, pb = blockIdx.y, ch = blockIdx.x, tid = threadIdx.x;
+  const int rl = tid >> 2, sub = tid & 3;
+  const int p = pb * 64 + rl;
+  const bool valid = p < a.M;
+  for (int e = tid; e < 64 * a.gwords; e += 256) {
+    const int r = e / a.gwords, wd = e - (e / a.gwords) * a.gwords;
+    const int pp = pb * 64 + r;
+    msk[r][wd] = pp < a.M ? a.gmask[((long long)bh * a.GQ + a.pgroup[(long long)bh * a.M + pp]) * a.gwords + wd] : 0u;
+  }
+  const T* qb = static_cast<const T*>(a.qv.p);
+  const T* kb = static_cast<const T*>(a.kv.p);
+  const T* vb = static_cast<const T*>(a.vv.p);
+  float q[DQ], od[DQ], os[DQ];
+  const int prow = valid ? a.ppos[(long long)bh * a.M + p] : 0;
+#pragma unroll
+  for (int i = 0; i < DQ; ++i) {
+    q[i] = valid ? Elem<T>::load(qb + a.qv.row_off(bh, prow) + sub + 4 * i) : 0.f;
+    od[i] = 0.f;
+    os[i] = 0.f;
+  }
+  float md = -INFINITY, ld = 0.f, ms = -INFINITY, ls = 0.f;
+  const float c = a.scale * 1.4426950408889634f;
+  const int k0 = ch * kProbeChunk, k1 = min(a.N, k0 + kProbeChunk);
+  for (int kt0 = k0; kt0 < k1; kt0 += 32) {
+    __syncthreads();
+    for (int e = tid; e < 32 * D; e += 256) {
+      const int r = e / D, cc = e - (e / D) * D;
+      const int v = kt0 + r;
+      float kx = 0.f, vx = 0.f;
+      if (v < k1) {
+        kx = Elem<T>::load(kb + a.kv.row_off(bh, v) + cc);
+        vx = Elem<T>::load(vb + a.vv.row_off(bh, v) + cc);
+      }
+      Kt[r][cc] = kx;
+      Vs[r][cc] = vx;
+    }
+    if (tid < 32) kg[tid] = (kt0 + tid < k1) ? a.kgroup[(long long)bh * a.N + kt0 + tid] : 0;
+    __syncthreads();
+    float sc[32];
+    float mld = -INFINITY, mls = -INFINITY;
+    uint32_t gbits = 0;
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+      float s = 0.f;
+#pragma unroll
+      for (int i = 0; i < DQ; ++i) s += q[i] * Kt[j][sub + 4 * i];
+      s += __shfl_xor(s, 1, 64);
+      s += __shfl_xor(s, 2, 64);
+      const bool in = kt0 + j < k1;
+      sc[j] = in ? s * c : -INFINITY;
+      const int h = kg[j];
+      const bool gr = in && ((msk[rl][h >> 5] >> (h & 31)) & 1u);
+      gbits |= (gr ? 1u : 0u) << j;
+      mld = fmaxf(mld, sc[j]);
+      if (gr) mls = fmaxf(mls, sc[j]);
+    }
+    const float mnd = fmaxf(md, mld), mns = fmaxf(ms, mls);
+    const float mbd = mnd == -INFINITY ? 0.f : mnd, mbs = mns == -INFINITY ? 0.f : mns;
+    const float ad = exp2f(md - mbd), as = exp2f(ms - mbs);
+#pragma unroll
+    for (int i = 0; i < DQ; ++i) {
+      od[i] *= ad;
+      os[i] *= as;
+    }
+    float sd = 0.f, ss = 0.f;
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+      const float pd = exp2f(sc[j] - mbd);
+      const float ps = ((gbits >> j) & 1u) ? exp2f(sc[j] - mbs) : 0.f;
+      sd += pd;
+      ss += ps;
+#pragma unroll
+      for (int i = 0; i < DQ; ++i) {
+        const float vx = Vs[j][sub + 4 * i];
+        od[i] += pd * vx;
+        os[i] += ps * vx;
+      }
+    }
+    ld = ld * ad + sd;
+    ls = ls * as + ss;
+    md = mnd;
+    ms = mns;
+  }
+  if (!valid) return;
+  float* base = a.ppart + (((long long)bh * a.n_pchunk + ch) * 2) * a.M * (D + 2);
+  float* pd = base + (long long)p * (D + 2);
+  float* ps = base + ((long long)a.M + p) * (D + 2);
+#pragma unroll
+  for (int i = 0; i < DQ; ++i) {
+    pd[sub + 4 * i] = od[i];
+    ps[sub + 4 * i] = os[i];
+  }
+  if (sub == 0) {
+    pd[D] = md;
+    pd[D + 1] = ld;
+    ps[D] = ms;
+    ps[D + 1] = ls;
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void k_probe_merge(ProbeArgs a) {
+  const int bh = blockIdx.x;
+  for (int e = threadIdx.x; e < 2 * a.M * D; e += 256) {
+    const int which = e / (a.M * D);
+    const int rem = e - which * a.M * D;
+    const int p = rem / D, dm = rem - (rem / D) * D;
+    float mx = -INFINITY;
+    for (int ch = 0; ch < a.n_pchunk; ++ch) {
+      const float* pr = a.ppart + ((((long long)bh * a.n_pchunk + ch) * 2 + which) * a.M + p) * (D + 2);
+      mx = fmaxf(mx, pr[D]);
+    }
+    float num = 0.f, den = 0.f;
+    if (mx > -INFINITY) {
+      for (int ch = 0; ch < a.n_pchunk; ++ch) {
+        const float* pr = a.ppart + ((((long long)bh * a.n_pchunk + ch) * 2 + which) * a.M + p) * (D + 2);
+        if (pr[D] == -INFINITY) continue;
+        const float f = exp2f(pr[D] - mx);
+        num += f * pr[dm];
+        den += f * pr[D + 1];
+      }
+    }
+    const float val = den > 0.f ? num / den : 0.f;
+    float* out = which == 0 ? a.ode : a.osp;
+    out[((long long)bh * a.M + p) * D + dm] = val;
+  }
+}
+
+// probe rows keep their exact dense output
+template <typename T>
+__global__ __launch_bounds__(256) void k_probe_overwrite(MutView4 o, const int* perm_q, const int* ppos,
+                                                         const float* ode, int N, int M, int D) {
+  const int bh = blockIdx.x;
+  for (int e = threadIdx.x; e < M * D; e += 256) {
+    const int p = e / D, dm = e - (e / D) * D;
+    const int token = perm_q[(long long)bh * N + ppos[(long long)bh * M + p]];
+    T* row = static_cast<T*>(o.p) + o.row_off(bh, token);
+    Elem<T>::store(row + dm, ode[((long long)bh * M + p) * D + dm]);
+  }
+}
+
+// ============================================================================
+// launchers
+// ============================================================================
+static AttnArgs attn_args(const Plan& p, bool correct) {
+  AttnArgs a;
+  const long long nd = (long long)p.N * p.d;
+  a.qv = View4{p.qp, (long long)p.H * nd, nd, p.d, p.H};
+  a.kv = View4{p.kp, (long long)p.H * nd, nd, p.d, p.H};
+  a.vv = View4{p.vp, (long long)p.H * nd, nd, p.d, p.H};
+  a.o = p.o;
+  a.perm_q = p.perm_q;
+  a.off_k = p.off_k;
+  a.csr_ptr = p.csr_ptr;
+  a.csr_col = p.csr_col;
+  a.tiles = p.tiles;
+  a.ntiles = p.ntiles;
+  a.max_tiles = p.max_tiles;
+  a.fitW = p.fitW;
+  a.fitV = p.fitV;
+  a.fitb = p.fitb;
+  a.fitrank = p.fitrank;
+  a.R = p.R > 0 ? p.R : 1;
+  a.N = p.N;
+  a.GK = p.GK;
+  a.GQ = p.GQ;
+  a.scale = p.scale;
+  a.correct = correct && p.M > 0 ? 1 : 0;
+  a.dense = 0;
+  return a;
+}
+
+static hipError_t launch_attn(const AttnArgs& a, int grid_x, int BH, int d, int dtype, hipStream_t s) {
+  dim3 g(grid_x, BH);
+  if (dtype == SPARSEPR_BF16) {
+    if (d == 128) hipLaunchKernelGGL(k_sparse_attn_mfma<128>, g, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL(k_sparse_attn_mfma<64>, g, dim3(256), 0, s, a);
+  } else {
+    if (d == 128) hipLaunchKernelGGL((k_sparse_attn_vec<float, 128>), g, dim3(512), 0, s, a);
+    else hipLaunchKernelGGL((k_sparse_attn_vec<float, 64>), g, dim3(512), 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_sparse_attention(const Plan& p, bool correct, hipStream_t s) {
+  AttnArgs a = attn_args(p, correct);
+  return launch_attn(a, p.max_tiles, p.BH, p.d, p.dtype, s);
+}
+
+hipError_t launch_dense_attention(const View4& q, const View4& k, const View4& v, const MutView4& o, int BH,
+                                  int N, int d, int dtype, float scale, hipStream_t s) {
+  AttnArgs a;
+  memset(&a, 0, sizeof(a));
+  a.qv = q;
+  a.kv = k;
+  a.vv = v;
+  a.o = o;
+  a.N = N;
+  a.scale = scale;
+  a.dense = 1;
+  a.R = 1;
+  return launch_attn(a, (N + kTileRows - 1) / kTileRows, BH, d, dtype, s);
+}
+
+hipError_t launch_probe_attention(const Plan& p, hipStream_t s) {
+  if (p.M <= 0) return hipSuccess;
+  ProbeArgs a;
+  const long long nd = (long long)p.N * p.d;
+  a.qv = View4{p.qp, (long long)p.H * nd, nd, p.d, p.H};
+  a.kv = View4{p.kp, (long long)p.H * nd, nd, p.d, p.H};
+  a.vv = View4{p.vp, (long long)p.H * nd, nd, p.d, p.H};
+  a.ppos = p.ppos;
+  a.pgroup = p.pgroup;
+  a.kgroup = p.kgroup;
+  a.gmask = p.gmask;
+  a.gwords = p.gwords;
+  a.N = p.N;
+  a.M = p.M;
+  a.GQ = p.GQ;
+  a.n_pchunk = p.n_pchunk;
+  a.scale = p.scale;
+  a.ppart = p.ppart;
+  a.ode = p.ode;
+  a.osp = p.osp;
+  dim3 g(p.n_pchunk, (p.M + 63) / 64, p.BH);
+  if (p.dtype == SPARSEPR_BF16) {
+    if (p.d == 128) hipLaunchKernelGGL((k_probe_attn_vec<bf16_t, 128>), g, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((k_probe_attn_vec<bf16_t, 64>), g, dim3(256), 0, s, a);
+  } else {
+    if (p.d == 128) hipLaunchKernelGGL((k_probe_attn_vec<float, 128>), g, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((k_probe_attn_vec<float, 64>), g, dim3(256), 0, s, a);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (p.d == 128) hipLaunchKernelGGL(k_probe_merge<128>, dim3(p.BH), dim3(256), 0, s, a);
+  else hipLaunchKernelGGL(k_probe_merge<64>, dim3(p.BH), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_probe_overwrite(const Plan& p, hipStream_t s) {
+  if (p.M <= 0) return hipSuccess;
+  if (p.dtype == SPARSEPR_BF16)
+    hipLaunchKernelGGL(k_probe_overwrite<bf16_t>, dim3(p.BH), dim3(256), 0, s, p.o, p.perm_q, p.ppos, p.ode, p.N,
+                       p.M, p.d);
+  else
+    hipLaunchKernelGGL(k_probe_overwrite<float>, dim3(p.BH), dim3(256), 0, s, p.o, p.perm_q, p.ppos, p.ode, p.N,
+                       p.M, p.d);
+  return hipGetLastError();
+}
+
+}  // namespace sp

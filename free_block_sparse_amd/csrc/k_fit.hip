@@ -1,0 +1,383 @@
+// Probe-Fitted Residual Reconstruction: the per-call fit, fp64, one workgroup
+// per (b,h).
+//
+// Sources (page title, section):
+//   [TS] "Resumen Técnico: SparsePR ..." (gist.science) 2.B: the residual of the probe
+//        rows R = O_dense - O_sparse is modelled as R ~ b + xB with x the sparse
+//        output, fitted per call with ridge regularisation, and the correction is
+//        confined to the span of the leading singular vectors of the probe residuals.
+//   [DG] "Partition the Support, Reconstruct the Residual: ..." (ai-feeds.com digest),
+//        方法/关键模块 2: the affine fit is weighted.
+//   [NE] news explainer reposted from 科技行者, section "SparsePR：先把误差聚拢，再用少量
+//        “抽查”去纠正": ridge regression; the 16 leading singular directions are kept.
+//
+// Computation (readings: unweighted uncentred SVD of R; weighted least squares
+// with an unpenalised intercept; absolute lambda):
+//   Gram of R (the smaller side) -> Jacobi eigen -> sigma, right singular
+//   vectors V (r' = min(r, M, d, #{sigma > cut sigma_1}));  Y = R V;
+//   weighted means xbar, ybar;  W = (Xc^T D Xc + lambda I)^-1 Xc^T D Yc, solved
+//   in the M x M dual form when M <= d;  b = (ybar - xbar W) V^T.
+// All matrices live in a per-(b,h) global scratch slice (L2 resident).
+#include "sp_kernels.h"
+
+namespace sp {
+
+struct FitArgs {
+  const float* ode;
+  const float* osp;
+  const double* pw;
+  int M, d, R, Rcfg;
+  double lambda, cut;
+  double* scratch;  // per bh: kFitScratch doubles
+  float* W;
+  float* V;
+  float* b;
+  int* rank;
+  double* sig;
+  sparsepr_head_stats* stats;
+};
+
+constexpr long long kFitScratch = kFitScratchDoubles;
+
+__device__ inline void block_sync() { __syncthreads(); }
+
+// Parallel cyclic Jacobi on a symmetric n x n matrix (n even) with eigenvector
+// accumulation.  All threads of the block call it.
+__device__ void jacobi_sym_f64(double* A, double* V, int n, double* rcs, int* rpq, int* stop, double* red) {
+  const int tid = threadIdx.x, nt = blockDim.x;
+  const int hp = n / 2;
+  for (int e = tid; e < n * n; e += nt) V[e] = (e / n == e % n) ? 1.0 : 0.0;
+  block_sync();
+  for (int sweep = 0; sweep < 60; ++sweep) {
+    double off = 0.0, tot = 0.0;
+    for (int e = tid; e < n * n; e += nt) {
+      const double x = A[e];
+      tot += x * x;
+      if (e / n != e % n) off += x * x;
+    }
+    off = wave_sum_d(off);
+    tot = wave_sum_d(tot);
+    if ((tid & 63) == 0) {
+      red[2 * (tid >> 6)] = off;
+      red[2 * (tid >> 6) + 1] = tot;
+    }
+    block_sync();
+    if (tid == 0) {
+      double o = 0.0, t = 0.0;
+      for (int w = 0; w < nt / 64; ++w) {
+        o += red[2 * w];
+        t += red[2 * w + 1];
+      }
+      *stop = !(o > 1e-26 * t);
+    }
+    block_sync();
+    if (*stop) break;
+    for (int r = 0; r < n - 1; ++r) {
+      for (int k = tid; k < hp; k += nt) {
+        const int a0 = k, b0 = n - 1 - k;
+        const int pa = a0 == 0 ? 0 : ((a0 - 1 + r) % (n - 1)) + 1;
+        const int pb = b0 == 0 ? 0 : ((b0 - 1 + r) % (n - 1)) + 1;
+        const int p = pa < pb ? pa : pb, q = pa < pb ? pb : pa;
+        const double app = A[p * n + p], aqq = A[q * n + q], apq = A[p * n + q];
+        double c = 1.0, s = 0.0;
+        if (apq != 0.0) {
+          const double th = (aqq - app) / (2.0 * apq);
+          double t;
+          if (fabs(th) > 1e150) t = 0.5 / th;
+          else t = (th >= 0.0 ? 1.0 : -1.0) / (fabs(th) + sqrt(1.0 + th * th));
+          c = 1.0 / sqrt(1.0 + t * t);
+          s = t * c;
+        }
+        rcs[2 * k] = c;
+        rcs[2 * k + 1] = s;
+        rpq[2 * k] = p;
+        rpq[2 * k + 1] = q;
+      }
+      block_sync();
+      for (int blk = tid; blk < hp * hp; blk += nt) {
+        const int ia = blk / hp, ib = blk - (blk / hp) * hp;
+        const int pa = rpq[2 * ia], qa = rpq[2 * ia + 1], pb = rpq[2 * ib], qb = rpq[2 * ib + 1];
+        const double ca = rcs[2 * ia], sa = rcs[2 * ia + 1], cb = rcs[2 * ib], sb = rcs[2 * ib + 1];
+        const double x00 = A[pa * n + pb], x01 = A[pa * n + qb];
+        const double x10 = A[qa * n + pb], x11 = A[qa * n + qb];
+        const double t00 = ca * x00 - sa * x10, t01 = ca * x01 - sa * x11;
+        const double t10 = sa * x00 + ca * x10, t11 = sa * x01 + ca * x11;
+        A[pa * n + pb] = cb * t00 - sb * t01;
+        A[pa * n + qb] = sb * t00 + cb * t01;
+        A[qa * n + pb] = cb * t10 - sb * t11;
+        A[qa * n + qb] = sb * t10 + cb * t11;
+      }
+      for (int task = tid; task < n * hp; task += nt) {
+        const int i = task / hp, ib = task - (task / hp) * hp;
+        const int pb = rpq[2 * ib], qb = rpq[2 * ib + 1];
+        const double cb = rcs[2 * ib], sb = rcs[2 * ib + 1];
+        const double v1 = V[i * n + pb], v2 = V[i * n + qb];
+        V[i * n + pb] = cb * v1 - sb * v2;
+        V[i * n + qb] = sb * v1 + cb * v2;
+      }
+      block_sync();
+    }
+  }
+}
+
+// In-place Cholesky (lower) of an SPD n x n matrix; returns false on a
+// non-positive pivot.  All threads call it.
+__device__ bool cholesky_f64(double* K, int n, int* bad) {
+  const int tid = threadIdx.x, nt = blockDim.x;
+  if (tid == 0) *bad = 0;
+  block_sync();
+  for (int k = 0; k < n; ++k) {
+    if (tid == 0) {
+      const double piv = K[k * n + k];
+      if (!(piv > 0.0)) *bad = 1;
+      K[k * n + k] = sqrt(piv > 0.0 ? piv : 1.0);
+    }
+    block_sync();
+    const double lkk = K[k * n + k];
+    for (int i = k + 1 + tid; i < n; i += nt) K[i * n + k] /= lkk;
+    block_sync();
+    const int m = n - k - 1;
+    for (int e = tid; e < m * m; e += nt) {
+      const int i = k + 1 + e / m, j = k + 1 + e % m;
+      if (j <= i) K[i * n + j] -= K[i * n + k] * K[j * n + k];
+    }
+    block_sync();
+  }
+  return *bad == 0;
+}
+
+__global__ __launch_bounds__(256) void k_fit(FitArgs a) {
+  __shared__ double rcs[2 * 64];
+  __shared__ int rpq[2 * 64];
+  __shared__ double red[8];
+  __shared__ int stop, bad;
+  __shared__ double sig_s[kMaxProbe + 1];
+  __shared__ int idx_s[kMaxProbe + 1];
+  __shared__ int rk_s;
+  __shared__ double wsum_s;
+  const int bh = blockIdx.x, tid = threadIdx.x, nt = blockDim.x;
+  const int M = a.M, d = a.d, Rmax = a.R;  // Rmax: column stride of the W and V outputs
+  double* S = a.scratch + (long long)bh * kFitScratch;
+  double* Rm = S;                    // M x d
+  double* G = S + 256 * 128;         // ne x ne
+  double* U = G + 128 * 128;         // ne x ne
+  double* Vr = U + 128 * 128;        // d x R (fp64)
+  double* K = Vr + 128 * 64;         // ridge system, up to 128 x 128
+  double* Z = K + 128 * 128;         // M x R right-hand sides / solutions (up to 256 x 64)
+  const float* ode = a.ode + (long long)bh * M * d;
+  const float* osp = a.osp + (long long)bh * M * d;
+  const double* w = a.pw + (long long)bh * M;
+
+  for (int e = tid; e < M * d; e += nt) Rm[e] = (double)ode[e] - (double)osp[e];
+  const bool small = M <= d;
+  const int n = small ? M : d;
+  const int ne = n + (n & 1);
+  block_sync();
+  for (int e = tid; e < ne * ne; e += nt) {
+    const int i = e / ne, j = e - (e / ne) * ne;
+    double acc = 0.0;
+    if (i < n && j < n) {
+      if (small)
+        for (int k = 0; k < d; ++k) acc += Rm[i * d + k] * Rm[j * d + k];
+      else
+        for (int mm = 0; mm < M; ++mm) acc += Rm[mm * d + i] * Rm[mm * d + j];
+    }
+    G[e] = acc;
+  }
+  block_sync();
+  jacobi_sym_f64(G, U, ne, rcs, rpq, &stop, red);
+  // eigenvalues, descending with ties by index
+  for (int i = tid; i < ne; i += nt) {
+    const double li = G[i * ne + i];
+    int r = 0;
+    for (int j = 0; j < ne; ++j) {
+      const double lj = G[j * ne + j];
+      r += (lj > li) || (lj == li && j < i);
+    }
+    sig_s[r] = sqrt(li > 0.0 ? li : 0.0);
+    idx_s[r] = i;
+  }
+  block_sync();
+  if (tid == 0) {
+    const double s1 = sig_s[0];
+    int cnt = 0;
+    if (s1 > 0.0 && s1 < INFINITY)
+      for (int i = 0; i < n; ++i) cnt += sig_s[i] > a.cut * s1;
+    int rk = a.Rcfg;
+    if (M < rk) rk = M;
+    if (d < rk) rk = d;
+    if (cnt < rk) rk = cnt;
+    rk_s = rk;
+    double ws = 0.0;
+    for (int i = 0; i < M; ++i) ws += w[i];
+    wsum_s = ws;
+    for (int i = 0; i < kMaxProbe && i < n; ++i) a.sig[(long long)bh * kMaxProbe + i] = sig_s[i];
+  }
+  block_sync();
+  int rk = rk_s;
+  // right singular vectors
+  for (int e = tid; e < d * rk; e += nt) {
+    const int dm = e / rk, k = e - (e / rk) * rk;
+    const int ci = idx_s[k];
+    double v;
+    if (small) {
+      double acc = 0.0;
+      for (int mm = 0; mm < M; ++mm) acc += Rm[mm * d + dm] * U[mm * ne + ci];
+      v = acc / sig_s[k];
+    } else {
+      v = U[dm * ne + ci];
+    }
+    Vr[dm * Rmax + k] = v;
+  }
+  block_sync();
+  // Y = R Vr (M x rk) into Z region first rows; weighted means
+  double* Yc = Z;                      // M x rk
+  __shared__ double xb[128];
+  __shared__ double yb[64];
+  for (int e = tid; e < M * rk; e += nt) {
+    const int mm = e / rk, k = e - (e / rk) * rk;
+    double acc = 0.0;
+    for (int dm = 0; dm < d; ++dm) acc += Rm[mm * d + dm] * Vr[dm * Rmax + k];
+    Yc[mm * rk + k] = acc;
+  }
+  block_sync();
+  const double ws = wsum_s;
+  for (int dm = tid; dm < d; dm += nt) {
+    double acc = 0.0;
+    for (int mm = 0; mm < M; ++mm) acc += w[mm] * (double)osp[mm * d + dm];
+    xb[dm] = acc / ws;
+  }
+  for (int k = tid; k < rk; k += nt) {
+    double acc = 0.0;
+    for (int mm = 0; mm < M; ++mm) acc += w[mm] * Yc[mm * rk + k];
+    yb[k] = acc / ws;
+  }
+  block_sync();
+  // centre Y
+  for (int e = tid; e < M * rk; e += nt) Yc[e] -= yb[e % rk];
+  block_sync();
+  bool ok = rk > 0;
+  if (rk > 0) {
+    if (small) {
+      // dual: K = D^1/2 Xc Xc^T D^1/2 + lambda I  (M x M), rhs = D^1/2 Yc
+      for (int e = tid; e < M * M; e += nt) {
+        const int i = e / M, j = e - (e / M) * M;
+        double acc = 0.0;
+        for (int dm = 0; dm < d; ++dm)
+          acc += ((double)osp[i * d + dm] - xb[dm]) * ((double)osp[j * d + dm] - xb[dm]);
+        K[e] = sqrt(w[i] * w[j]) * acc + (i == j ? a.lambda : 0.0);
+      }
+      for (int e = tid; e < M * rk; e += nt) Yc[e] *= sqrt(w[e / rk]);
+      block_sync();
+      ok = cholesky_f64(K, M, &bad);
+      if (ok) {
+        // solve L L^T z = rhs for every column (one thread per column)
+        for (int k = tid; k < rk; k += nt) {
+          for (int i = 0; i < M; ++i) {
+            double s = Yc[i * rk + k];
+            for (int j = 0; j < i; ++j) s -= K[i * M + j] * Yc[j * rk + k];
+            Yc[i * rk + k] = s / K[i * M + i];
+          }
+          for (int i = M - 1; i >= 0; --i) {
+            double s = Yc[i * rk + k];
+            for (int j = i + 1; j < M; ++j) s -= K[j * M + i] * Yc[j * rk + k];
+            Yc[i * rk + k] = s / K[i * M + i];
+          }
+        }
+        block_sync();
+        // W = Xc^T D^1/2 Z  (d x rk) -> stored in G region
+        for (int e = tid; e < d * rk; e += nt) {
+          const int dm = e / rk, k = e - (e / rk) * rk;
+          double acc = 0.0;
+          for (int mm = 0; mm < M; ++mm) acc += ((double)osp[mm * d + dm] - xb[dm]) * sqrt(w[mm]) * Yc[mm * rk + k];
+          G[dm * rk + k] = acc;
+        }
+      }
+    } else {
+      // primal: K = Xc^T D Xc + lambda I (d x d), rhs = Xc^T D Yc (d x rk) in G region
+      for (int e = tid; e < d * d; e += nt) {
+        const int i = e / d, j = e - (e / d) * d;
+        double acc = 0.0;
+        for (int mm = 0; mm < M; ++mm)
+          acc += w[mm] * ((double)osp[mm * d + i] - xb[i]) * ((double)osp[mm * d + j] - xb[j]);
+        K[e] = acc + (i == j ? a.lambda : 0.0);
+      }
+      for (int e = tid; e < d * rk; e += nt) {
+        const int i = e / rk, k = e - (e / rk) * rk;
+        double acc = 0.0;
+        for (int mm = 0; mm < M; ++mm) acc += w[mm] * ((double)osp[mm * d + i] - xb[i]) * Yc[mm * rk + k];
+        G[e] = acc;
+      }
+      block_sync();
+      ok = cholesky_f64(K, d, &bad);
+      if (ok) {
+        for (int k = tid; k < rk; k += nt) {
+          for (int i = 0; i < d; ++i) {
+            double s = G[i * rk + k];
+            for (int j = 0; j < i; ++j) s -= K[i * d + j] * G[j * rk + k];
+            G[i * rk + k] = s / K[i * d + i];
+          }
+          for (int i = d - 1; i >= 0; --i) {
+            double s = G[i * rk + k];
+            for (int j = i + 1; j < d; ++j) s -= K[j * d + i] * G[j * rk + k];
+            G[i * rk + k] = s / K[i * d + i];
+          }
+        }
+      }
+    }
+    block_sync();
+  }
+  if (!ok) rk = 0;
+  // outputs: W (d x R) and V (d x R) zero beyond rk, b = (ybar - xbar W) V^T
+  __shared__ double bp[64];
+  for (int k = tid; k < rk; k += nt) {
+    double acc = yb[k];
+    for (int dm = 0; dm < d; ++dm) acc -= xb[dm] * G[dm * rk + k];
+    bp[k] = acc;
+  }
+  block_sync();
+  float* Wo = a.W + (long long)bh * d * Rmax;
+  float* Vo = a.V + (long long)bh * d * Rmax;
+  for (int e = tid; e < d * Rmax; e += nt) {
+    const int dm = e / Rmax, k = e - (e / Rmax) * Rmax;
+    Wo[e] = k < rk ? (float)G[dm * rk + k] : 0.f;
+    Vo[e] = k < rk ? (float)Vr[dm * Rmax + k] : 0.f;
+  }
+  for (int dm = tid; dm < d; dm += nt) {
+    double acc = 0.0;
+    for (int k = 0; k < rk; ++k) acc += bp[k] * Vr[dm * Rmax + k];
+    a.b[(long long)bh * d + dm] = (float)acc;
+  }
+  if (tid == 0) {
+    a.rank[bh] = rk;
+    if (a.stats) {
+      a.stats[bh].residual_rank = rk;
+      for (int i = 0; i < 4; ++i) a.stats[bh].sigma[i] = i < n ? sig_s[i] : 0.0;
+    }
+  }
+}
+
+hipError_t launch_fit(const Plan& p, hipStream_t s) {
+  if (p.M <= 0) return hipSuccess;
+  FitArgs a;
+  a.ode = p.ode;
+  a.osp = p.osp;
+  a.pw = p.pw;
+  a.M = p.M;
+  a.d = p.d;
+  a.R = p.R > 0 ? p.R : 1;
+  a.Rcfg = p.R;
+  a.lambda = (double)p.lambda;
+  a.cut = (double)p.rank_cut;
+  a.scratch = p.fitscratch;
+  a.W = p.fitW;
+  a.V = p.fitV;
+  a.b = p.fitb;
+  a.rank = p.fitrank;
+  a.sig = p.fitsig;
+  a.stats = p.stats;
+  hipLaunchKernelGGL(k_fit, dim3(p.BH), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace sp

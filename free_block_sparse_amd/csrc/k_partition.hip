@@ -1,0 +1,707 @@
+// Response-Coupled Partitioning kernels for gfx950.
+//
+// Sources (page title, section):
+//   [TS] "Resumen Técnico: SparsePR – Atención Dispersa Libre de Entrenamiento ..."
+//        (gist.science), 2.A: sampled queries define M_K = Q_s^T Q_s / M_s; keys are
+//        grouped by k-means on the eigenvectors of M_K into paired K/V groups; the
+//        group centres define query coordinates (pre-softmax logits); queries are
+//        grouped by k-means on those; one asymmetric pass.
+//   [NE] news explainer reposted from 科技行者, section "SparsePR：先把误差聚拢，再用少量
+//        “抽查”去纠正": a random small batch of queries probes every key; a key's
+//        coordinates are its logit profile under that batch.
+//   2.C of [TS] and the [NE] section "稀疏执行怎么落地，误差怎么算才公平": tokens are laid
+//        out group by group so every group is contiguous.
+//
+// Both k-means run Lloyd steps on raw bf16 rows (or split fp32 rows) against
+// "centre images": for a metric M, argmin_g ||A x - mu_g||^2 equals
+// argmin_g (c_g - 2 x . y_g) with y_g = M xbar_g and c_g = xbar_g . y_g, so one
+// bf16 MFMA product with a fused argmin does the assignment.  Centre images
+// are kept as hi + lo bf16 pairs (16 significant bits).
+#include "sp_kernels.h"
+
+namespace sp {
+
+// ============================================================================
+// a1: query sample (partial Fisher-Yates on splitmix64) and M_K
+// ============================================================================
+template <typename T, int D>
+__global__ __launch_bounds__(256) void k_sample_metric(SampleArgs a) {
+  const int bh = blockIdx.x, tid = threadIdx.x;
+  __shared__ int slot[256];
+  __shared__ int far_pos[256];
+  __shared__ int far_val[256];
+  __shared__ int far_cnt;
+  __shared__ int srt[256];
+  __shared__ float qs[64][D + 1];
+  const int Ms = a.Ms, N = a.N;
+  slot[tid] = tid;
+  if (tid == 0) far_cnt = 0;
+  __syncthreads();
+  if (tid < 64) {
+    volatile int* vslot = slot;
+    volatile int* vfp = far_pos;
+    volatile int* vfv = far_val;
+    volatile int* vcnt = &far_cnt;
+    uint64_t st = a.seed ^ ((uint64_t)bh * kGolden64);
+    for (int j = 0; j < Ms; ++j) {
+      st += kGolden64;
+      uint64_t z = st;
+      z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+      z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+      z ^= z >> 31;
+      const long long t = (long long)j + (long long)(z % (uint64_t)(N - j));
+      const int vj = vslot[j];
+      int vt;
+      int found = -1;
+      if (t < Ms) {
+        vt = vslot[t];
+      } else {
+        const int cnt = *vcnt;
+        for (int base = 0; base < cnt; base += 64) {
+          const int kk = base + tid;
+          const bool hit = kk < cnt && vfp[kk] == (int)t;
+          const unsigned long long m = __ballot(hit);
+          if (m) {
+            found = base + __ffsll((long long)m) - 1;
+            break;
+          }
+        }
+        vt = found >= 0 ? vfv[found] : (int)t;
+      }
+      if (tid == 0) {
+        vslot[j] = vt;
+        if (t < Ms) {
+          vslot[t] = vj;
+        } else if (found >= 0) {
+          vfv[found] = vj;
+        } else {
+          const int c = *vcnt;
+          vfp[c] = (int)t;
+          vfv[c] = vj;
+          *vcnt = c + 1;
+        }
+      }
+    }
+  }
+  __syncthreads();
+  srt[tid] = tid < Ms ? slot[tid] : 0x7fffffff;
+  __syncthreads();
+  for (int k = 2; k <= 256; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      const int ixj = tid ^ j;
+      if (ixj > tid) {
+        const int a0 = srt[tid], a1 = srt[ixj];
+        const bool up = (tid & k) == 0;
+        if ((a0 > a1) == up) {
+          srt[tid] = a1;
+          srt[ixj] = a0;
+        }
+      }
+      __syncthreads();
+    }
+  }
+  if (tid < Ms) a.sample[(long long)bh * Ms + tid] = srt[tid];
+
+  constexpr int TB = D / 16;
+  const int i0 = (tid >> 4) * TB, j0 = (tid & 15) * TB;
+  float acc[TB][TB];
+#pragma unroll
+  for (int x = 0; x < TB; ++x)
+#pragma unroll
+    for (int y = 0; y < TB; ++y) acc[x][y] = 0.f;
+  const T* qbase = static_cast<const T*>(a.q.p);
+  for (int c0 = 0; c0 < Ms; c0 += 64) {
+    const int nr = min(64, Ms - c0);
+    __syncthreads();
+    for (int e = tid; e < nr * D; e += 256) {
+      const int r = e / D, col = e - (e / D) * D;
+      qs[r][col] = Elem<T>::load(qbase + a.q.row_off(bh, srt[c0 + r]) + col);
+    }
+    __syncthreads();
+    for (int r = 0; r < nr; ++r) {
+      float xi[TB], xj[TB];
+#pragma unroll
+      for (int t = 0; t < TB; ++t) {
+        xi[t] = qs[r][i0 + t];
+        xj[t] = qs[r][j0 + t];
+      }
+#pragma unroll
+      for (int x = 0; x < TB; ++x)
+#pragma unroll
+        for (int y = 0; y < TB; ++y) acc[x][y] += xi[x] * xj[y];
+    }
+  }
+  const float inv = 1.0f / (float)Ms;
+  float* mk = a.mk + (long long)bh * D * D;
+#pragma unroll
+  for (int x = 0; x < TB; ++x)
+#pragma unroll
+    for (int y = 0; y < TB; ++y) mk[(i0 + x) * D + j0 + y] = acc[x][y] * inv;
+}
+
+// ============================================================================
+// a2: symmetric eigensolver (parallel cyclic Jacobi, round-robin pairing).
+// Matrix and eigenvectors live in LDS; one workgroup per (b,h).
+// ============================================================================
+__device__ inline void rr_pair(int k, int r, int n, int* p, int* q) {
+  const int a = k, b = n - 1 - k;
+  const int pa = a == 0 ? 0 : ((a - 1 + r) % (n - 1)) + 1;
+  const int pb = b == 0 ? 0 : ((b - 1 + r) % (n - 1)) + 1;
+  *p = pa < pb ? pa : pb;
+  *q = pa < pb ? pb : pa;
+}
+
+template <int D>
+__global__ __launch_bounds__(1024) void k_key_eig(EigArgs a) {
+  constexpr int LD = D + 1;
+  constexpr int HP = D / 2;
+  __shared__ float A[D * LD];
+  __shared__ float V[D * LD];
+  __shared__ float rc[HP], rs[HP];
+  __shared__ int rp[HP], rq[HP];
+  __shared__ float red[2][32];
+  __shared__ int stop;
+  const int bh = blockIdx.x, tid = threadIdx.x, nt = blockDim.x;
+  const float* mk = a.mk + (long long)bh * D * D;
+  for (int e = tid; e < D * D; e += nt) {
+    const int i = e / D, j = e - (e / D) * D;
+    A[i * LD + j] = mk[e];
+    V[i * LD + j] = i == j ? 1.f : 0.f;
+  }
+  __syncthreads();
+  for (int sweep = 0; sweep < 40; ++sweep) {
+    float off = 0.f, tot = 0.f;
+    for (int e = tid; e < D * D; e += nt) {
+      const int i = e / D, j = e - (e / D) * D;
+      const float x = A[i * LD + j];
+      tot += x * x;
+      if (i != j) off += x * x;
+    }
+    off = wave_sum(off);
+    tot = wave_sum(tot);
+    if ((tid & 63) == 0) {
+      red[0][tid >> 6] = off;
+      red[1][tid >> 6] = tot;
+    }
+    __syncthreads();
+    if (tid == 0) {
+      float o = 0.f, t = 0.f;
+      for (int w = 0; w < nt / 64; ++w) {
+        o += red[0][w];
+        t += red[1][w];
+      }
+      stop = !(o > 1e-13f * t);
+    }
+    __syncthreads();
+    if (stop) break;
+    for (int r = 0; r < D - 1; ++r) {
+      if (tid < HP) {
+        int p, q;
+        rr_pair(tid, r, D, &p, &q);
+        const float app = A[p * LD + p], aqq = A[q * LD + q], apq = A[p * LD + q];
+        float c = 1.f, s = 0.f;
+        if (apq != 0.f) {
+          const float th = (aqq - app) / (2.f * apq);
+          float t;
+          if (fabsf(th) > 1e18f) t = 0.5f / th;
+          else t = (th >= 0.f ? 1.f : -1.f) / (fabsf(th) + sqrtf(1.f + th * th));
+          c = 1.f / sqrtf(1.f + t * t);
+          s = t * c;
+        }
+        rc[tid] = c;
+        rs[tid] = s;
+        rp[tid] = p;
+        rq[tid] = q;
+      }
+      __syncthreads();
+      for (int blk = tid; blk < HP * HP; blk += nt) {
+        const int ia = blk / HP, ib = blk - (blk / HP) * HP;
+        const int pa = rp[ia], qa = rq[ia], pb = rp[ib], qb = rq[ib];
+        const float ca = rc[ia], sa = rs[ia], cb = rc[ib], sb = rs[ib];
+        const float x00 = A[pa * LD + pb], x01 = A[pa * LD + qb];
+        const float x10 = A[qa * LD + pb], x11 = A[qa * LD + qb];
+        // T = Ja^T X, X' = T Jb with J = [[c, s], [-s, c]]
+        const float t00 = ca * x00 - sa * x10, t01 = ca * x01 - sa * x11;
+        const float t10 = sa * x00 + ca * x10, t11 = sa * x01 + ca * x11;
+        A[pa * LD + pb] = cb * t00 - sb * t01;
+        A[pa * LD + qb] = sb * t00 + cb * t01;
+        A[qa * LD + pb] = cb * t10 - sb * t11;
+        A[qa * LD + qb] = sb * t10 + cb * t11;
+      }
+      for (int task = tid; task < D * HP; task += nt) {
+        const int i = task / HP, ib = task - (task / HP) * HP;
+        const int pb = rp[ib], qb = rq[ib];
+        const float cb = rc[ib], sb = rs[ib];
+        const float v1 = V[i * LD + pb], v2 = V[i * LD + qb];
+        V[i * LD + pb] = cb * v1 - sb * v2;
+        V[i * LD + qb] = sb * v1 + cb * v2;
+      }
+      __syncthreads();
+    }
+  }
+  // rank eigenvalues (descending, ties by index) and emit the coordinate map
+  for (int i = tid; i < D; i += nt) {
+    const float li = A[i * LD + i];
+    int rank = 0;
+    for (int j = 0; j < D; ++j) {
+      const float lj = A[j * LD + j];
+      rank += (lj > li) || (lj == li && j < i);
+    }
+    if (a.eigval) a.eigval[(long long)bh * D + rank] = li;
+    if (rank < a.rK) {
+      const float f = a.scale * sqrtf(fmaxf(li, 0.f));
+      float* km = a.kmap + (long long)bh * D * a.rK;
+      for (int k = 0; k < D; ++k) km[k * a.rK + rank] = f * V[k * LD + i];
+    }
+  }
+}
+
+// ============================================================================
+// a3: key-response coordinates z = K kmap (fp32), stored also as hi/lo bf16
+// ============================================================================
+template <typename T, int D>
+__global__ __launch_bounds__(256) void k_key_coords(CoordArgs a) {
+  __shared__ float km[D][64];
+  __shared__ float kr[64][D + 1];
+  const int bh = blockIdx.y, tid = threadIdx.x;
+  const int n0 = blockIdx.x * 64;
+  const int rK = a.rK, rKpad = a.rKpad, N = a.N;
+  const float* kmap = a.kmap + (long long)bh * D * rK;
+  for (int e = tid; e < D * rK; e += 256) km[e / rK][e % rK] = kmap[e];
+  const T* kb = static_cast<const T*>(a.k.p);
+  for (int e = tid; e < 64 * D; e += 256) {
+    const int r = e / D, c = e - (e / D) * D;
+    const int n = n0 + r;
+    kr[r][c] = n < N ? Elem<T>::load(kb + a.k.row_off(bh, n) + c) : 0.f;
+  }
+  __syncthreads();
+  const int r = tid >> 2;
+  const int n = n0 + r;
+  if (n >= N) return;
+  const long long zrow = (long long)bh * N + n;
+  for (int j = tid & 3; j < rKpad; j += 4) {
+    float acc = 0.f;
+    if (j < rK) {
+      for (int c = 0; c < D; ++c) acc += kr[r][c] * km[c][j];
+      a.z32[zrow * rK + j] = acc;
+    }
+    const bf16_t hi = f32_to_bf16(acc);
+    a.zhi[zrow * rKpad + j] = hi;
+    a.zlo[zrow * rKpad + j] = f32_to_bf16(acc - bf16_to_f32(hi));
+  }
+}
+
+// fp32 raw rows -> hi/lo bf16 pair (fp32 inputs only)
+__global__ __launch_bounds__(256) void k_split_rows(SplitArgs a) {
+  const int bh = blockIdx.y;
+  const long long e = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (e >= (long long)a.N * a.D) return;
+  const int n = (int)(e / a.D), c = (int)(e - (e / a.D) * a.D);
+  const float x = static_cast<const float*>(a.x.p)[a.x.row_off(bh, n) + c];
+  const bf16_t hi = f32_to_bf16(x);
+  const long long o = ((long long)bh * a.N + n) * a.D + c;
+  a.hi[o] = hi;
+  a.lo[o] = f32_to_bf16(x - bf16_to_f32(hi));
+}
+
+// ============================================================================
+// a4/a8: Lloyd assignment.  One bf16 MFMA product of centre images (A, 32
+// centres x 16 dims) against point rows (B, 16 dims x 32 points) per k-step,
+// fused with the argmin.  256 points per workgroup, 64 per wave.
+// MFMA 32x32x16 lane layout: A[m][k]: m = lane%32, k = 8*(lane/32)+j;
+// B[k][n]: k = 8*(lane/32)+j, n = lane%32; D[i][j]: j = lane%32,
+// i = (r%4) + 8*(r/4) + 4*(lane/32) for accumulator register r.
+// ============================================================================
+template <int D, bool LO>
+__global__ __launch_bounds__(256) void k_kmeans_assign(AssignArgs a) {
+  constexpr int KS = D / 16;
+  constexpr int LDI = D + 8;  // padded LDS row (bank spread)
+  __shared__ __attribute__((aligned(16))) bf16_t sh[32 * LDI];
+  __shared__ __attribute__((aligned(16))) bf16_t sl[32 * LDI];
+  __shared__ float sbias[32];
+  __shared__ int hist[kMaxGroups];
+  const int bh = blockIdx.y, chunk = blockIdx.x;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int N = a.N, G = a.G;
+  const int half = lane >> 5, col = lane & 31;
+  const int nb = chunk * kChunk + wave * 64;
+
+  for (int g = tid; g < G; g += 256) hist[g] = 0;
+
+  bf16x8 ph[2][KS];
+  bf16x8 pl[2][LO ? KS : 1];
+  const bf16_t* hib = static_cast<const bf16_t*>(a.pts.p);
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int n = nb + 32 * t + col;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      uint4 v = make_uint4(0, 0, 0, 0);
+      uint4 w = make_uint4(0, 0, 0, 0);
+      if (n < N) {
+        v = *reinterpret_cast<const uint4*>(hib + a.pts.row_off(bh, n) + 16 * ks + 8 * half);
+        if (LO) w = *reinterpret_cast<const uint4*>(a.pts_lo + ((long long)bh * N + n) * D + 16 * ks + 8 * half);
+      }
+      ph[t][ks] = __builtin_bit_cast(bf16x8, v);
+      if (LO) pl[t][LO ? ks : 0] = __builtin_bit_cast(bf16x8, w);
+    }
+  }
+  float best[2] = {INFINITY, INFINITY};
+  int bidx[2] = {0, 0};
+  const bf16_t* yh = a.yhi + (long long)bh * a.gstride * a.ystride;
+  const bf16_t* yl = a.ylo + (long long)bh * a.gstride * a.ystride;
+  const float* yb = a.ybias + (long long)bh * a.gstride;
+  for (int c0 = 0; c0 < G; c0 += 32) {
+    __syncthreads();
+    for (int e = tid; e < 32 * (D / 8); e += 256) {
+      const int r = e / (D / 8), cc = e - (e / (D / 8)) * (D / 8);
+      const int c = c0 + r;
+      uint4 vh = make_uint4(0, 0, 0, 0), vl = make_uint4(0, 0, 0, 0);
+      if (c < G) {
+        vh = *reinterpret_cast<const uint4*>(yh + (long long)c * a.ystride + cc * 8);
+        vl = *reinterpret_cast<const uint4*>(yl + (long long)c * a.ystride + cc * 8);
+      }
+      *reinterpret_cast<uint4*>(sh + r * LDI + cc * 8) = vh;
+      *reinterpret_cast<uint4*>(sl + r * LDI + cc * 8) = vl;
+    }
+    if (tid < 32) sbias[tid] = (c0 + tid < G) ? yb[c0 + tid] : INFINITY;
+    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      f32x16 acc = {};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const bf16x8 ah = *reinterpret_cast<const bf16x8*>(sh + col * LDI + 16 * ks + 8 * half);
+        const bf16x8 al = *reinterpret_cast<const bf16x8*>(sl + col * LDI + 16 * ks + 8 * half);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, ph[t][ks], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, ph[t][ks], acc, 0, 0, 0);
+        if (LO) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, pl[t][LO ? ks : 0], acc, 0, 0, 0);
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int i = (r & 3) + 8 * (r >> 2) + 4 * half;
+        const float dist = sbias[i] - 2.0f * acc[r];
+        if (dist < best[t]) {
+          best[t] = dist;
+          bidx[t] = c0 + i;
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const float ob = __shfl_xor(best[t], 32, 64);
+    const int oi = __shfl_xor(bidx[t], 32, 64);
+    if (ob < best[t] || (ob == best[t] && oi < bidx[t])) {
+      best[t] = ob;
+      bidx[t] = oi;
+    }
+  }
+  __syncthreads();
+  if (half == 0) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int n = nb + 32 * t + col;
+      if (n < N) {
+        a.labels[(long long)bh * N + n] = bidx[t];
+        atomicAdd(&hist[bidx[t]], 1);
+      }
+    }
+  }
+  __syncthreads();
+  int* cnt = a.counts + ((long long)bh * a.nchunk + chunk) * a.gstride;
+  for (int g = tid; g < G; g += 256) cnt[g] = hist[g];
+}
+
+// histogram of given labels (partition supplied by the caller); labels outside
+// [0, G) are clamped
+__global__ __launch_bounds__(256) void k_count_labels(CountArgs a) {
+  __shared__ int hist[kMaxGroups];
+  const int bh = blockIdx.y, chunk = blockIdx.x, tid = threadIdx.x;
+  for (int g = tid; g < a.G; g += 256) hist[g] = 0;
+  __syncthreads();
+  const int n = chunk * kChunk + tid;
+  if (n < a.N) {
+    int l = a.in_labels[(long long)bh * a.N + n];
+    l = l < 0 ? 0 : (l >= a.G ? a.G - 1 : l);
+    a.labels[(long long)bh * a.N + n] = l;
+    atomicAdd(&hist[l], 1);
+  }
+  __syncthreads();
+  int* cnt = a.counts + ((long long)bh * a.nchunk + chunk) * a.gstride;
+  for (int g = tid; g < a.G; g += 256) cnt[g] = hist[g];
+}
+
+// ============================================================================
+// a5: counting sort -- chunk offsets (group-major, chunk-minor) and stable scatter
+// ============================================================================
+__global__ __launch_bounds__(1024) void k_group_scan(ScanArgs a) {
+  __shared__ int tot[kMaxGroups];
+  const int bh = blockIdx.x, tid = threadIdx.x;
+  const int G = a.G, nch = a.nchunk;
+  const int* cnt = a.counts + (long long)bh * nch * a.gstride;
+  for (int g = tid; g < G; g += 1024) {
+    int s = 0;
+    for (int c = 0; c < nch; ++c) s += cnt[(long long)c * a.gstride + g];
+    tot[g] = s;
+  }
+  __syncthreads();
+  // inclusive Hillis-Steele scan over G <= 1024 entries
+  for (int o = 1; o < G; o <<= 1) {
+    int v = 0;
+    if (tid < G && tid >= o) v = tot[tid - o];
+    __syncthreads();
+    if (tid < G) tot[tid] += v;
+    __syncthreads();
+  }
+  int* off = a.off + (long long)bh * a.offstride;
+  int* co = a.chunkoff + (long long)bh * nch * a.gstride;
+  for (int g = tid; g < G; g += 1024) {
+    int base = g == 0 ? 0 : tot[g - 1];
+    off[g] = base;
+    for (int c = 0; c < nch; ++c) {
+      co[(long long)c * a.gstride + g] = base;
+      base += cnt[(long long)c * a.gstride + g];
+    }
+  }
+  if (tid == 0) off[G] = a.N;
+}
+
+__global__ __launch_bounds__(256) void k_group_scatter(ScatterArgs a) {
+  __shared__ int lab[kChunk];
+  const int bh = blockIdx.y, chunk = blockIdx.x, tid = threadIdx.x;
+  const int n = chunk * kChunk + tid;
+  lab[tid] = n < a.N ? a.labels[(long long)bh * a.N + n] : -1;
+  __syncthreads();
+  if (n >= a.N) return;
+  const int my = lab[tid];
+  int rank = 0;
+  for (int j = 0; j < tid; ++j) rank += lab[j] == my;
+  const int pos = a.chunkoff[((long long)bh * a.nchunk + chunk) * a.gstride + my] + rank;
+  a.perm[(long long)bh * a.N + pos] = n;
+  if (a.out_labels) a.out_labels[(long long)bh * a.N + n] = my;
+}
+
+// ============================================================================
+// centre update: fp64 mean of each group's point rows summed in ascending token
+// order; then centre image y = M mean (or the mean itself) and bias mean . y
+// ============================================================================
+template <typename TP>
+__global__ __launch_bounds__(256) void k_centre_update(UpdateArgs a) {
+  __shared__ double smean[8][128];
+  __shared__ double sprod[8][128];
+  const int bh = blockIdx.y, tid = threadIdx.x;
+  const int Dimg = a.Dimg, Dp = a.Dp;
+  const int gpb = min(8, 256 / Dimg);
+  const int gl = tid / Dimg, j = tid - (tid / Dimg) * Dimg;
+  const int g = blockIdx.x * gpb + gl;
+  const bool gval = gl < gpb && g < a.G;
+  const TP* xb = static_cast<const TP*>(a.pts.p);
+  double mean = 0.0;
+  bool keep_old = false;
+  int n_g = 0;
+  if (gval && j < Dp) {
+    if (a.init) {
+      const long long idx = ((2LL * g + 1) * a.N) / (2LL * a.G);
+      mean = (double)Elem<TP>::load(xb + a.pts.row_off(bh, idx) + j);
+      n_g = 1;
+    } else {
+      const int* off = a.off + (long long)bh * a.offstride;
+      const int* perm = a.perm + (long long)bh * a.N;
+      const int a0 = off[g], a1 = off[g + 1];
+      n_g = a1 - a0;
+      if (n_g > 0) {
+        double s = 0.0;
+        for (int m = a0; m < a1; ++m) s = __dadd_rn(s, (double)Elem<TP>::load(xb + a.pts.row_off(bh, perm[m]) + j));
+        mean = s / (double)n_g;
+      } else {
+        keep_old = true;
+      }
+    }
+    if (a.means_out) {
+      a.means_out[((long long)bh * a.mo_gstride + g) * Dp + j] = n_g > 0 ? mean : __builtin_nan("");
+    }
+  }
+  if (a.means_only) return;
+  double* cm = a.cmean + ((long long)bh * a.gstride + (gval ? g : 0)) * a.cstride;
+  if (gval && j < Dp) {
+    if (keep_old) mean = cm[j];
+    cm[j] = mean;
+  }
+  if (gl < 8) smean[gl][j] = (gval && j < Dp) ? mean : 0.0;
+  __syncthreads();
+  double y = 0.0;
+  if (gval && j < Dp) {
+    if (a.metric) {
+      const float* M = a.metric + (long long)bh * Dp * Dp;
+      for (int k = 0; k < Dp; ++k) y += (double)M[k * Dp + j] * smean[gl][k];
+    } else {
+      y = mean;
+    }
+  }
+  if (gl < 8) sprod[gl][j] = (gval && j < Dp) ? y * smean[gl][j] : 0.0;
+  __syncthreads();
+  if (!gval) return;
+  const long long yo = ((long long)bh * a.gstride + g) * a.ystride + j;
+  const float yf = (float)y;
+  const bf16_t hi = f32_to_bf16(yf);
+  a.yhi[yo] = hi;
+  a.ylo[yo] = f32_to_bf16(yf - bf16_to_f32(hi));
+  if (j == 0) {
+    double b = 0.0;
+    for (int k = 0; k < Dp; ++k) b += sprod[gl][k];
+    a.ybias[(long long)bh * a.gstride + g] = (float)b;
+  }
+}
+
+// M_Q = s^2 sum over non-empty key groups of cbar_h cbar_h^T
+__global__ __launch_bounds__(1024) void k_query_metric(QMetricArgs a) {
+  const int bh = blockIdx.x, d = a.d;
+  const double* cb = a.cbar + (long long)bh * a.GK * d;
+  const int* off = a.off_k + (long long)bh * (a.GK + 1);
+  const double s2 = (double)a.scale * (double)a.scale;
+  for (int e = threadIdx.x; e < d * d; e += blockDim.x) {
+    const int i = e / d, j = e - (e / d) * d;
+    double acc = 0.0;
+    for (int h = 0; h < a.GK; ++h)
+      if (off[h + 1] > off[h]) acc += cb[(long long)h * d + i] * cb[(long long)h * d + j];
+    a.mq[(long long)bh * d * d + e] = (float)(s2 * acc);
+  }
+}
+
+// ============================================================================
+// a9: gather Q, K, V into group-contiguous order; key-group id per position
+// ============================================================================
+template <typename T>
+__global__ __launch_bounds__(256) void k_gather(GatherArgs a) {
+  const int bh = blockIdx.y;
+  constexpr int VEC = 16 / sizeof(T);
+  const int cpr = a.d / VEC;  // 16-byte chunks per row
+  const int rows_per_blk = 256 / cpr;
+  const int r = threadIdx.x / cpr, c = threadIdx.x - (threadIdx.x / cpr) * cpr;
+  const int pos = blockIdx.x * rows_per_blk + r;
+  if (pos >= a.N) return;
+  const long long dst = ((long long)bh * a.N + pos) * a.d + c * VEC;
+  const int tq = a.perm_q[(long long)bh * a.N + pos];
+  const int tk = a.perm_k[(long long)bh * a.N + pos];
+  *reinterpret_cast<uint4*>(static_cast<T*>(a.qp) + dst) =
+      *reinterpret_cast<const uint4*>(static_cast<const T*>(a.q.p) + a.q.row_off(bh, tq) + c * VEC);
+  *reinterpret_cast<uint4*>(static_cast<T*>(a.kp) + dst) =
+      *reinterpret_cast<const uint4*>(static_cast<const T*>(a.k.p) + a.k.row_off(bh, tk) + c * VEC);
+  *reinterpret_cast<uint4*>(static_cast<T*>(a.vp) + dst) =
+      *reinterpret_cast<const uint4*>(static_cast<const T*>(a.v.p) + a.v.row_off(bh, tk) + c * VEC);
+  if (c == 0) a.kgroup[(long long)bh * a.N + pos] = a.kv_labels[(long long)bh * a.N + tk];
+}
+
+// ============================================================================
+// launchers
+// ============================================================================
+#define SP_LAUNCH(k, g, b, s, ...)                                   \
+  do {                                                               \
+    hipLaunchKernelGGL(k, g, b, 0, s, __VA_ARGS__);                  \
+    hipError_t e_ = hipGetLastError();                               \
+    if (e_ != hipSuccess) return e_;                                 \
+  } while (0)
+
+hipError_t launch_sample_metric(const Plan& p, hipStream_t s) {
+  SampleArgs a{p.q, p.N, p.Ms, p.seed, p.sample, p.mk};
+  if (p.dtype == SPARSEPR_BF16) {
+    if (p.d == 128) SP_LAUNCH((k_sample_metric<bf16_t, 128>), dim3(p.BH), dim3(256), s, a);
+    else SP_LAUNCH((k_sample_metric<bf16_t, 64>), dim3(p.BH), dim3(256), s, a);
+  } else {
+    if (p.d == 128) SP_LAUNCH((k_sample_metric<float, 128>), dim3(p.BH), dim3(256), s, a);
+    else SP_LAUNCH((k_sample_metric<float, 64>), dim3(p.BH), dim3(256), s, a);
+  }
+  return hipSuccess;
+}
+
+hipError_t launch_key_eig(const Plan& p, hipStream_t s) {
+  EigArgs a{p.mk, p.eigval, p.kmap, p.rK, p.scale};
+  if (p.d == 128) SP_LAUNCH(k_key_eig<128>, dim3(p.BH), dim3(1024), s, a);
+  else SP_LAUNCH(k_key_eig<64>, dim3(p.BH), dim3(1024), s, a);
+  return hipSuccess;
+}
+
+hipError_t launch_key_coords(const Plan& p, hipStream_t s) {
+  CoordArgs a{p.k, p.kmap, p.N, p.rK, p.rKpad, p.z32, p.zhi, p.zlo};
+  dim3 g((p.N + 63) / 64, p.BH);
+  if (p.dtype == SPARSEPR_BF16) {
+    if (p.d == 128) SP_LAUNCH((k_key_coords<bf16_t, 128>), g, dim3(256), s, a);
+    else SP_LAUNCH((k_key_coords<bf16_t, 64>), g, dim3(256), s, a);
+  } else {
+    if (p.d == 128) SP_LAUNCH((k_key_coords<float, 128>), g, dim3(256), s, a);
+    else SP_LAUNCH((k_key_coords<float, 64>), g, dim3(256), s, a);
+  }
+  return hipSuccess;
+}
+
+hipError_t launch_split_rows(const Plan& p, const View4& x, hipStream_t s) {
+  SplitArgs a{x, p.N, p.d, p.phi, p.plo};
+  dim3 g((unsigned)(((long long)p.N * p.d + 255) / 256), p.BH);
+  SP_LAUNCH(k_split_rows, g, dim3(256), s, a);
+  return hipSuccess;
+}
+
+hipError_t launch_assign(const Plan& p, const AssignArgs& a, int D, bool lo, hipStream_t s) {
+  dim3 g(p.nchunk, p.BH);
+  if (D == 16) {
+    if (lo) SP_LAUNCH((k_kmeans_assign<16, true>), g, dim3(256), s, a);
+    else SP_LAUNCH((k_kmeans_assign<16, false>), g, dim3(256), s, a);
+  } else if (D == 32) {
+    if (lo) SP_LAUNCH((k_kmeans_assign<32, true>), g, dim3(256), s, a);
+    else SP_LAUNCH((k_kmeans_assign<32, false>), g, dim3(256), s, a);
+  } else if (D == 48) {
+    if (lo) SP_LAUNCH((k_kmeans_assign<48, true>), g, dim3(256), s, a);
+    else SP_LAUNCH((k_kmeans_assign<48, false>), g, dim3(256), s, a);
+  } else if (D == 64) {
+    if (lo) SP_LAUNCH((k_kmeans_assign<64, true>), g, dim3(256), s, a);
+    else SP_LAUNCH((k_kmeans_assign<64, false>), g, dim3(256), s, a);
+  } else if (D == 128) {
+    if (lo) SP_LAUNCH((k_kmeans_assign<128, true>), g, dim3(256), s, a);
+    else SP_LAUNCH((k_kmeans_assign<128, false>), g, dim3(256), s, a);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipSuccess;
+}
+
+hipError_t launch_count_labels(const Plan& p, const CountArgs& a, hipStream_t s) {
+  SP_LAUNCH(k_count_labels, dim3(p.nchunk, p.BH), dim3(256), s, a);
+  return hipSuccess;
+}
+
+hipError_t launch_group_scan(const Plan& p, const ScanArgs& a, hipStream_t s) {
+  SP_LAUNCH(k_group_scan, dim3(p.BH), dim3(1024), s, a);
+  return hipSuccess;
+}
+
+hipError_t launch_group_scatter(const Plan& p, const ScatterArgs& a, hipStream_t s) {
+  SP_LAUNCH(k_group_scatter, dim3(p.nchunk, p.BH), dim3(256), s, a);
+  return hipSuccess;
+}
+
+hipError_t launch_centre_update(const Plan& p, const UpdateArgs& a, int pts_type, hipStream_t s) {
+  const int gpb = (256 / a.Dimg) < 8 ? (256 / a.Dimg) : 8;
+  dim3 g((a.G + gpb - 1) / gpb, p.BH);
+  if (pts_type == 0) SP_LAUNCH(k_centre_update<bf16_t>, g, dim3(256), s, a);
+  else SP_LAUNCH(k_centre_update<float>, g, dim3(256), s, a);
+  return hipSuccess;
+}
+
+hipError_t launch_query_metric(const Plan& p, hipStream_t s) {
+  QMetricArgs a{p.cbar, p.off_k, p.GK, p.d, p.scale, p.mq};
+  SP_LAUNCH(k_query_metric, dim3(p.BH), dim3(1024), s, a);
+  return hipSuccess;
+}
+
+hipError_t launch_gather(const Plan& p, hipStream_t s) {
+  GatherArgs a{p.q, p.k, p.v, p.perm_q, p.perm_k, p.kv_labels, p.qp, p.kp, p.vp, p.kgroup, p.N, p.d};
+  const int vec = 16 / p.esize;
+  const int rows_per_blk = 256 / (p.d / vec);
+  dim3 g((p.N + rows_per_blk - 1) / rows_per_blk, p.BH);
+  if (p.dtype == SPARSEPR_BF16) SP_LAUNCH(k_gather<bf16_t>, g, dim3(256), s, a);
+  else SP_LAUNCH(k_gather<float>, g, dim3(256), s, a);
+  return hipSuccess;
+}
+
+}  // namespace sp

@@ -1,0 +1,527 @@
+// Router and probe selection kernels for gfx950.
+//
+// Sources (page title, section):
+//   [NE] news explainer reposted from 科技行者, section "稀疏执行怎么落地，误差怎么算才公平":
+//        (query-group, key-group) cells are chosen under a budget counted in true
+//        pairs, the product of the two groups' token counts; rho_route is the
+//        selected fraction of the Q x K matrix; the executed density also counts
+//        the exact probe rows.
+//   [TS] "Resumen Técnico: SparsePR ..." (gist.science) 2.C: rho_exec includes routed
+//        sparse cells and exact probe rows.
+//   [NE] section "SparsePR：先把误差聚拢，再用少量“抽查”去纠正": probes are picked evenly
+//        from every query group (query-group-stratified), 64 rows per head.
+//
+// Rule (a reading; the pages give no formula): mu_gh = s qbar_g . cbar_h is the
+// logit of the mean query of group g against the mean key of group h;
+// key_gh = mu_gh - log sum_h' n_h' exp(mu_gh') estimates the attention
+// probability of one key of h for a query of g.  Every non-empty query group
+// first gets its best cell; the other cells are taken in order (key desc,
+// g asc, h asc) as the longest prefix that fits the budget.  mu is a
+// sequential fp64 dot product without fused multiply-add, so the selection is
+// reproducible bit for bit.
+#include "sp_kernels.h"
+
+namespace sp {
+
+struct RouteArgs {
+  const double* qbar;  // [BH, GQ, d]
+  const double* cbar;  // [BH, GK, d]
+  const int* off_q;    // [BH, GQ + 1]
+  const int* off_k;    // [BH, GK + 1]
+  int GQ, GK, d, N, M;
+  double s;
+  long long budget;
+  int dense_route;
+  double* mu;
+  uint64_t* ckey;
+  int* mand;
+  long long* thr;
+  int* csr_ptr;
+  int* csr_col;
+  uint32_t* gmask;
+  int gwords;
+  long long* lg;
+  int* tiles;
+  int* ntiles;
+  int max_tiles;
+  sparsepr_head_stats* stats;
+};
+
+constexpr uint64_t kExcluded = ~0ull;
+
+// ---------------------------------------------------------------- mu
+__global__ __launch_bounds__(256) void k_route_mu(RouteArgs a) {
+  constexpr int GB = 16;
+  __shared__ double sq[GB][128];
+  const int bh = blockIdx.y, g0 = blockIdx.x * GB, tid = threadIdx.x, d = a.d;
+  const int* offq = a.off_q + (long long)bh * (a.GQ + 1);
+  const int* offk = a.off_k + (long long)bh * (a.GK + 1);
+  for (int e = tid; e < GB * d; e += 256) {
+    const int gi = e / d, k = e - (e / d) * d;
+    const int g = g0 + gi;
+    double v = 0.0;
+    if (g < a.GQ && offq[g + 1] > offq[g]) v = a.qbar[((long long)bh * a.GQ + g) * d + k];
+    sq[gi][k] = v;
+  }
+  __syncthreads();
+  const int ng = min(GB, a.GQ - g0);
+  for (int h = tid; h < a.GK; h += 256) {
+    const bool vh = offk[h + 1] > offk[h];
+    const double* c = a.cbar + ((long long)bh * a.GK + h) * d;
+    double acc[GB];
+#pragma unroll
+    for (int gi = 0; gi < GB; ++gi) acc[gi] = 0.0;
+    for (int k = 0; k < d; ++k) {
+      const double ck = vh ? c[k] : 0.0;
+#pragma unroll
+      for (int gi = 0; gi < GB; ++gi) acc[gi] = __dadd_rn(acc[gi], __dmul_rn(sq[gi][k], ck));
+    }
+    for (int gi = 0; gi < ng; ++gi) {
+      double m = __dmul_rn(acc[gi], a.s);
+      if (m != m) m = -INFINITY;
+      a.mu[((long long)bh * a.GQ + g0 + gi) * a.GK + h] = m;
+    }
+  }
+}
+
+// ---------------------------------------------------------------- keys
+__global__ __launch_bounds__(256) void k_route_keys(RouteArgs a) {
+  __shared__ double term[kMaxGroups];
+  __shared__ double rmax[4];
+  __shared__ int rarg[4];
+  __shared__ double ell_s;
+  __shared__ int best_s;
+  const int bh = blockIdx.y, g = blockIdx.x, tid = threadIdx.x;
+  const int GK = a.GK;
+  const int* offq = a.off_q + (long long)bh * (a.GQ + 1);
+  const int* offk = a.off_k + (long long)bh * (a.GK + 1);
+  const long long row = ((long long)bh * a.GQ + g) * GK;
+  const int nq = offq[g + 1] - offq[g];
+  if (nq <= 0) {
+    for (int h = tid; h < GK; h += 256) a.ckey[row + h] = kExcluded;
+    if (tid == 0) a.mand[(long long)bh * a.GQ + g] = -1;
+    return;
+  }
+  // first maximum of mu over non-empty key groups
+  double bm = -INFINITY;
+  int bi = 0x7fffffff;
+  for (int h = tid; h < GK; h += 256) {
+    if (offk[h + 1] <= offk[h]) continue;
+    const double m = a.mu[row + h];
+    if (bi == 0x7fffffff || m > bm) {  // strided per-thread scan keeps the first maximum
+      bm = m;
+      bi = h;
+    }
+  }
+  for (int o = 32; o > 0; o >>= 1) {
+    const double om = __shfl_xor(bm, o, 64);
+    const int oi = __shfl_xor(bi, o, 64);
+    const bool take = (oi != 0x7fffffff) && (bi == 0x7fffffff || om > bm || (om == bm && oi < bi));
+    if (take) {
+      bm = om;
+      bi = oi;
+    }
+  }
+  if ((tid & 63) == 0) {
+    rmax[tid >> 6] = bm;
+    rarg[tid >> 6] = bi;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    double m = rmax[0];
+    int i = rarg[0];
+    for (int w = 1; w < 4; ++w) {
+      const int oi = rarg[w];
+      const double om = rmax[w];
+      if (oi != 0x7fffffff && (i == 0x7fffffff || om > m || (om == m && oi < i))) {
+        m = om;
+        i = oi;
+      }
+    }
+    best_s = i;
+    rmax[0] = m;
+  }
+  __syncthreads();
+  const int best = best_s;
+  const double mx = rmax[0];
+  const bool finite = best != 0x7fffffff && mx > -INFINITY && mx < INFINITY;
+  for (int h = tid; h < GK; h += 256) {
+    double t = 0.0;
+    if (finite && offk[h + 1] > offk[h]) t = __dmul_rn((double)(offk[h + 1] - offk[h]), exp(__dsub_rn(a.mu[row + h], mx)));
+    term[h] = t;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    double tot = 0.0;
+    for (int h = 0; h < GK; ++h)
+      if (offk[h + 1] > offk[h]) tot = __dadd_rn(tot, term[h]);
+    ell_s = finite ? __dadd_rn(mx, log(tot)) : 0.0;
+    a.mand[(long long)bh * a.GQ + g] = best == 0x7fffffff ? -1 : best;
+  }
+  __syncthreads();
+  const double ell = ell_s;
+  for (int h = tid; h < GK; h += 256) {
+    uint64_t ck = kExcluded;
+    if (offk[h + 1] > offk[h] && h != best) {
+      double key = finite ? __dsub_rn(a.mu[row + h], ell) : -INFINITY;
+      if (key != key) key = -INFINITY;
+      ck = ~ord_f64(key);
+    }
+    a.ckey[row + h] = ck;
+  }
+}
+
+// ---------------------------------------------------------------- select
+// Weighted radix select over the 88-bit composite (descending key, cell index):
+// find the first cell in sorted order whose cumulative cost exceeds the budget
+// left after the mandatory cells.
+__device__ inline void comp_digits(uint64_t ck, uint32_t cell, int pass, int* dig) {
+  *dig = pass < 8 ? (int)((ck >> (56 - 8 * pass)) & 255u) : (int)((cell >> (16 - 8 * (pass - 8))) & 255u);
+}
+
+__device__ inline bool comp_prefix_eq(uint64_t ck, uint32_t cell, int nbits, uint64_t ph, uint32_t pl) {
+  if (nbits == 0) return true;
+  if (nbits <= 64) {
+    const int sh = 64 - nbits;
+    return sh == 0 ? ck == ph : (ck >> sh) == (ph >> sh);
+  }
+  if (ck != ph) return false;
+  const int sh = 24 - (nbits - 64);
+  return (cell >> sh) == (pl >> sh);
+}
+
+// -1: below prefix, 0: equal at nbits, 1: above
+__device__ inline int comp_cmp_prefix(uint64_t ck, uint32_t cell, int nbits, uint64_t ph, uint32_t pl) {
+  if (nbits == 0) return 0;
+  if (nbits <= 64) {
+    const int sh = 64 - nbits;
+    const uint64_t a = sh == 0 ? ck : (ck >> sh), b = sh == 0 ? ph : (ph >> sh);
+    return a < b ? -1 : (a > b ? 1 : 0);
+  }
+  if (ck != ph) return ck < ph ? -1 : 1;
+  const int sh = 24 - (nbits - 64);
+  const uint32_t a = cell >> sh, b = pl >> sh;
+  return a < b ? -1 : (a > b ? 1 : 0);
+}
+
+// thr layout: [0] prefix_hi, [1] prefix_lo, [2] nbits, [3] mode (0 none, 1 all, 2 exclusive, 3 inclusive)
+__device__ inline bool thr_grants(const long long* thr, uint64_t ck, uint32_t cell) {
+  const int mode = (int)thr[3];
+  if (mode == 0) return false;
+  if (mode == 1) return true;
+  const int c = comp_cmp_prefix(ck, cell, (int)thr[2], (uint64_t)thr[0], (uint32_t)thr[1]);
+  return c < 0 || (mode == 3 && c == 0);
+}
+
+__global__ __launch_bounds__(1024) void k_route_select(RouteArgs a) {
+  __shared__ int nq[kMaxGroups], nk[kMaxGroups];
+  __shared__ unsigned long long hist[16][256];
+  __shared__ long long red[16];
+  __shared__ long long rem_s;
+  __shared__ unsigned long long ph_s;
+  __shared__ unsigned pl_s;
+  __shared__ int nbits_s, done_s, mode_s;
+  const int bh = blockIdx.x, tid = threadIdx.x, wave = tid >> 6;
+  const int GQ = a.GQ, GK = a.GK;
+  const int* offq = a.off_q + (long long)bh * (GQ + 1);
+  const int* offk = a.off_k + (long long)bh * (GK + 1);
+  for (int g = tid; g < GQ; g += 1024) nq[g] = offq[g + 1] - offq[g];
+  for (int h = tid; h < GK; h += 1024) nk[h] = offk[h + 1] - offk[h];
+  __syncthreads();
+  long long* thr = a.thr + (long long)bh * 4;
+  if (a.dense_route) {
+    if (tid == 0) {
+      thr[0] = 0;
+      thr[1] = 0;
+      thr[2] = 0;
+      thr[3] = 1;
+    }
+    return;
+  }
+  long long cm = 0;
+  const int* mand = a.mand + (long long)bh * GQ;
+  for (int g = tid; g < GQ; g += 1024)
+    if (mand[g] >= 0) cm += (long long)nq[g] * nk[mand[g]];
+  for (int o = 32; o > 0; o >>= 1) cm += __shfl_xor(cm, o, 64);
+  if ((tid & 63) == 0) red[wave] = cm;
+  __syncthreads();
+  if (tid == 0) {
+    long long t = 0;
+    for (int w = 0; w < 16; ++w) t += red[w];
+    rem_s = a.budget - t;
+    ph_s = 0;
+    pl_s = 0;
+    nbits_s = 0;
+    done_s = rem_s < 0 ? 1 : 0;
+    mode_s = rem_s < 0 ? 0 : 2;
+  }
+  __syncthreads();
+  const uint64_t* ck = a.ckey + (long long)bh * GQ * GK;
+  const int ncell = GQ * GK;
+  for (int pass = 0; pass < 11 && !done_s; ++pass) {
+    for (int e = tid; e < 16 * 256; e += 1024) (&hist[0][0])[e] = 0ull;
+    __syncthreads();
+    const int nbits = nbits_s;
+    const uint64_t ph = ph_s;
+    const uint32_t pl = pl_s;
+    for (int c = tid; c < ncell; c += 1024) {
+      const uint64_t k = ck[c];
+      if (k == kExcluded) continue;
+      if (!comp_prefix_eq(k, (uint32_t)c, nbits, ph, pl)) continue;
+      int dig;
+      comp_digits(k, (uint32_t)c, pass, &dig);
+      const int g = c / GK, h = c - (c / GK) * GK;
+      atomicAdd(&hist[wave][dig], (unsigned long long)((long long)nq[g] * nk[h]));
+    }
+    __syncthreads();
+    if (tid < 256) {
+      unsigned long long t = 0;
+      for (int w = 0; w < 16; ++w) t += hist[w][tid];
+      hist[0][tid] = t;
+    }
+    __syncthreads();
+    if (tid == 0) {
+      long long acc = 0;
+      int chosen = -1;
+      for (int b = 0; b < 256; ++b) {
+        const long long hb = (long long)hist[0][b];
+        if (acc + hb > rem_s) {
+          chosen = b;
+          break;
+        }
+        acc += hb;
+      }
+      if (chosen < 0) {
+        mode_s = 3;  // every remaining candidate fits
+        done_s = 1;
+      } else {
+        rem_s -= acc;
+        if (pass < 8) ph_s |= (uint64_t)chosen << (56 - 8 * pass);
+        else pl_s |= (uint32_t)chosen << (16 - 8 * (pass - 8));
+        nbits_s = nbits + 8;
+      }
+    }
+    __syncthreads();
+  }
+  if (tid == 0) {
+    thr[0] = (long long)ph_s;
+    thr[1] = (long long)pl_s;
+    thr[2] = nbits_s;
+    thr[3] = mode_s;
+  }
+}
+
+// ---------------------------------------------------------------- CSR, masks, tiles, stats
+__global__ __launch_bounds__(256) void k_route_emit(RouteArgs a) {
+  __shared__ int nq[kMaxGroups], nk[kMaxGroups], cnt[kMaxGroups], tcnt[kMaxGroups];
+  __shared__ long long lsh[kMaxGroups];
+  __shared__ long long thr[4];
+  const int bh = blockIdx.x, tid = threadIdx.x;
+  const int GQ = a.GQ, GK = a.GK;
+  const int* offq = a.off_q + (long long)bh * (GQ + 1);
+  const int* offk = a.off_k + (long long)bh * (GK + 1);
+  const uint64_t* ck = a.ckey + (long long)bh * GQ * GK;
+  const int* mand = a.mand + (long long)bh * GQ;
+  for (int g = tid; g < GQ; g += 256) nq[g] = offq[g + 1] - offq[g];
+  for (int h = tid; h < GK; h += 256) nk[h] = offk[h + 1] - offk[h];
+  if (tid < 4) thr[tid] = a.thr[(long long)bh * 4 + tid];
+  __syncthreads();
+  uint32_t* gm = a.gmask + (long long)bh * GQ * a.gwords;
+  for (int g = tid; g < GQ; g += 256) {
+    int c = 0;
+    long long L = 0;
+    for (int w = 0; w < a.gwords; ++w) {
+      uint32_t bits = 0;
+      for (int b = 0; b < 32; ++b) {
+        const int h = 32 * w + b;
+        if (h >= GK) break;
+        bool gr = false;
+        if (nq[g] > 0 && nk[h] > 0) {
+          const uint32_t cell = (uint32_t)(g * GK + h);
+          gr = (h == mand[g]) || (ck[cell] != kExcluded && thr_grants(thr, ck[cell], cell));
+        }
+        if (gr) {
+          bits |= 1u << b;
+          ++c;
+          L += nk[h];
+        }
+      }
+      gm[(long long)g * a.gwords + w] = bits;
+    }
+    cnt[g] = c;
+    lsh[g] = L;
+    tcnt[g] = nq[g] > 0 ? (nq[g] + kTileRows - 1) / kTileRows : 0;
+    a.lg[(long long)bh * GQ + g] = L;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    // exclusive scans (sequential; G <= 1024)
+    int* rp = a.csr_ptr + (long long)bh * (GQ + 1);
+    int acc = 0, tacc = 0;
+    long long routed = 0, mandc = 0;
+    int neq = 0, nek = 0;
+    for (int g = 0; g < GQ; ++g) {
+      rp[g] = acc;
+      const int c = cnt[g];
+      cnt[g] = acc;
+      acc += c;
+      const int tc = tcnt[g];
+      tcnt[g] = tacc;
+      tacc += tc;
+      routed += (long long)nq[g] * lsh[g];
+      if (nq[g] > 0) {
+        ++neq;
+        if (mand[g] >= 0) mandc += (long long)nq[g] * nk[mand[g]];
+      }
+    }
+    rp[GQ] = acc;
+    for (int h = 0; h < GK; ++h) nek += nk[h] > 0;
+    a.ntiles[bh] = tacc;
+    sparsepr_head_stats st;
+    const double nn = (double)a.N * (double)a.N;
+    st.routed_pairs = routed;
+    st.budget_pairs = a.budget;
+    st.mandatory_pairs = mandc;
+    st.probe_pairs = (long long)a.M * a.N;
+    st.granted_cells = acc;
+    st.nonempty_q_groups = neq;
+    st.nonempty_kv_groups = nek;
+    st.probe_rows = a.M;
+    st.residual_rank = 0;
+    st.over_budget = a.dense_route ? 0 : (routed > a.budget ? 1 : 0);
+    st.q_tiles = tacc;
+    st.reserved = 0;
+    st.rho_route = (double)routed / nn;
+    st.rho_exec = (double)(routed + (long long)a.M * a.N) / nn;
+    for (int i = 0; i < 4; ++i) st.sigma[i] = 0.0;
+    a.stats[bh] = st;
+  }
+  __syncthreads();
+  int* cols = a.csr_col + (long long)bh * GQ * GK;
+  int* tl = a.tiles + (long long)bh * a.max_tiles * 4;
+  for (int g = tid; g < GQ; g += 256) {
+    int j = cnt[g];
+    for (int w = 0; w < a.gwords; ++w) {
+      uint32_t bits = gm[(long long)g * a.gwords + w];
+      while (bits) {
+        const int b = __ffs((int)bits) - 1;
+        bits &= bits - 1;
+        cols[j++] = 32 * w + b;
+      }
+    }
+    int t0 = tcnt[g];
+    for (int r = 0; r < nq[g]; r += kTileRows) {
+      int* e = tl + (long long)t0 * 4;
+      e[0] = g;
+      e[1] = offq[g] + r;
+      e[2] = min(kTileRows, nq[g] - r);
+      e[3] = 0;
+      ++t0;
+    }
+  }
+}
+
+hipError_t launch_route(const Plan& p, hipStream_t s) {
+  RouteArgs a;
+  a.qbar = p.qbar;
+  a.cbar = p.cbar;
+  a.off_q = p.off_q;
+  a.off_k = p.off_k;
+  a.GQ = p.GQ;
+  a.GK = p.GK;
+  a.d = p.d;
+  a.N = p.N;
+  a.M = p.M;
+  a.s = (double)p.scale;
+  a.budget = p.budget;
+  a.dense_route = p.dense_route ? 1 : 0;
+  a.mu = p.mu;
+  a.ckey = p.ckey;
+  a.mand = p.mand;
+  a.thr = p.thr;
+  a.csr_ptr = p.csr_ptr;
+  a.csr_col = p.csr_col;
+  a.gmask = p.gmask;
+  a.gwords = p.gwords;
+  a.lg = p.lg;
+  a.tiles = p.tiles;
+  a.ntiles = p.ntiles;
+  a.max_tiles = p.max_tiles;
+  a.stats = p.stats;
+  hipLaunchKernelGGL(k_route_mu, dim3((p.GQ + 15) / 16, p.BH), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(k_route_keys, dim3(p.GQ, p.BH), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(k_route_select, dim3(p.BH), dim3(1024), 0, s, a);
+  hipLaunchKernelGGL(k_route_emit, dim3(p.BH), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- probes
+struct ProbeSelArgs {
+  const int* off_q;
+  int GQ, M;
+  int* ppos;
+  int* pgroup;
+  double* pw;
+};
+
+__global__ __launch_bounds__(64) void k_probe_select(ProbeSelArgs a) {
+  __shared__ int ne[kMaxGroups];
+  __shared__ int mg[kMaxGroups];
+  const int bh = blockIdx.x;
+  if (threadIdx.x != 0 || a.M <= 0) return;
+  const int* off = a.off_q + (long long)bh * (a.GQ + 1);
+  int gp = 0;
+  for (int g = 0; g < a.GQ; ++g) {
+    mg[g] = 0;
+    if (off[g + 1] > off[g]) ne[gp++] = g;
+  }
+  const int M = a.M;
+  if (M >= gp) {
+    const int base = M / gp, rem = M - (M / gp) * gp;
+    long long carry = 0;
+    for (int r = 0; r < gp; ++r) {
+      const int g = ne[r];
+      const long long want = base + (r < rem ? 1 : 0) + carry;
+      const long long sz = off[g + 1] - off[g];
+      const long long m = want < sz ? want : sz;
+      mg[g] = (int)m;
+      carry = want - m;
+    }
+    while (carry > 0) {
+      for (int r = 0; r < gp && carry > 0; ++r) {
+        const int g = ne[r];
+        const long long room = (long long)(off[g + 1] - off[g]) - mg[g];
+        const long long add = carry < room ? carry : room;
+        mg[g] += (int)add;
+        carry -= add;
+      }
+    }
+  } else {
+    for (int j = 0; j < M; ++j) mg[ne[((2LL * j + 1) * gp) / (2LL * M)]] += 1;
+  }
+  int k = 0;
+  double tot = 0.0;
+  for (int r = 0; r < gp; ++r) {
+    const int g = ne[r];
+    const long long sz = off[g + 1] - off[g];
+    for (int t = 0; t < mg[g]; ++t) {
+      a.ppos[(long long)bh * M + k] = off[g] + (int)(((2LL * t + 1) * sz) / (2LL * mg[g]));
+      a.pgroup[(long long)bh * M + k] = g;
+      const double w = (double)sz / (double)mg[g];
+      a.pw[(long long)bh * M + k] = w;
+      tot += w;
+      ++k;
+    }
+  }
+  const double f = (double)M / tot;
+  for (int i = 0; i < M; ++i) a.pw[(long long)bh * M + i] *= f;
+}
+
+hipError_t launch_probe_select(const Plan& p, hipStream_t s) {
+  if (p.M <= 0) return hipSuccess;
+  ProbeSelArgs a{p.off_q, p.GQ, p.M, p.ppos, p.pgroup, p.pw};
+  hipLaunchKernelGGL(k_probe_select, dim3(p.BH), dim3(64), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace sp

@@ -1,0 +1,104 @@
+// Host-side call plan: validated shape, method settings and the carve-up of
+// the caller's workspace.  Pure host code; no HIP calls.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "sp_common.h"
+
+namespace sp {
+
+constexpr int kChunk = 256;      // points per k-means assignment workgroup
+constexpr int kTileRows = 128;   // query rows per sparse-attention workgroup
+constexpr int kProbeChunk = 2048;  // keys per probe-attention workgroup
+constexpr int kMaxProbe = 256;
+constexpr int kMaxRank = 64;
+constexpr int kMaxGroups = 1024;
+constexpr long long kFitScratchDoubles = 7LL * 128 * 128;  // per (b,h) fit scratch
+
+struct Plan {
+  // shape and settings
+  int B, H, BH, N, d, dtype, esize;
+  int GK, GQ, Gmax, M, R, Ms, rK, rKpad, T, mode;
+  int Dk;            // key-side k-means point dimension (padded to 16)
+  int nchunk;        // ceil(N / kChunk)
+  int max_tiles;     // per (b,h) upper bound of query tiles
+  int n_pchunk;      // probe key chunks per (b,h)
+  int gwords;        // ceil(GK / 32)
+  float scale, density, lambda, rank_cut;
+  unsigned long long seed;
+  long long budget;  // routed-pair budget per (b,h)
+  bool dense_route;  // density >= 1: every cell granted
+
+  View4 q, k, v;
+  MutView4 o;
+
+  // ---- workspace (device pointers) ----
+  int* sample;            // [BH, Ms]
+  float* mk;              // [BH, d, d]
+  float* eigval;          // [BH, d]
+  float* kmap;            // [BH, d, rK]
+  float* z32;             // [BH, N, rK]
+  bf16_t* zhi;            // [BH, N, rKpad]
+  bf16_t* zlo;            // [BH, N, rKpad]
+  bf16_t* phi;            // [BH, N, d] raw points split (fp32 inputs only)
+  bf16_t* plo;            // [BH, N, d]
+  double* cmean;          // [BH, Gmax, Dmax] k-means centres (coordinate or raw space)
+  bf16_t* yhi;            // [BH, Gmax, Dmax] centre images (hi part)
+  bf16_t* ylo;            // [BH, Gmax, Dmax] centre images (lo part)
+  float* ybias;           // [BH, Gmax]
+  int* labels;            // [BH, N] working labels
+  int* counts;            // [BH, nchunk, Gmax]
+  int* chunkoff;          // [BH, nchunk, Gmax]
+  int* perm_w;            // [BH, N] working permutation
+  int* off_w;             // [BH, Gmax + 1]
+  int* kv_labels;         // [BH, N]
+  int* q_labels;          // [BH, N]
+  int* perm_k;            // [BH, N]
+  int* off_k;             // [BH, GK + 1]
+  int* perm_q;            // [BH, N]
+  int* off_q;             // [BH, GQ + 1]
+  double* cbar;           // [BH, GK, d] raw key means
+  double* qbar;           // [BH, GQ, d] raw query means
+  float* mq;              // [BH, d, d] query metric s^2 Cbar^T Cbar
+  void* qp;               // [BH, N, d] permuted copies (input dtype)
+  void* kp;
+  void* vp;
+  int* kgroup;            // [BH, N] key-group id of each permuted key position
+  double* mu;             // [BH, GQ, GK]
+  uint64_t* ckey;         // [BH, GQ, GK] orderable descending log-probability
+  int* mand;              // [BH, GQ] best key group per query group (-1 if empty)
+  long long* thr;         // [BH, 4] selection threshold
+  int* csr_ptr;           // [BH, GQ + 1]
+  int* csr_col;           // [BH, GQ * GK]
+  uint32_t* gmask;        // [BH, GQ, gwords] granted bitmask per query group
+  long long* lg;          // [BH, GQ] granted keys per query group
+  int* tiles;             // [BH, max_tiles, 4] (g, row0, nrows, 0)
+  int* ntiles;            // [BH]
+  int* ppos;              // [BH, M] probe positions (permuted order)
+  int* pgroup;            // [BH, M] probe query group
+  double* pw;             // [BH, M] probe weights
+  float* ppart;           // [BH, n_pchunk, 2, M, d + 2] probe partials
+  float* ode;             // [BH, M, d] exact dense probe outputs
+  float* osp;             // [BH, M, d] sparse probe outputs
+  float* fitW;            // [BH, d, R]
+  float* fitV;            // [BH, d, R]
+  float* fitb;            // [BH, d]
+  int* fitrank;           // [BH]
+  double* fitsig;         // [BH, kMaxProbe]
+  double* fitscratch;     // [BH, kFitScratchDoubles]
+  sparsepr_head_stats* stats;  // [BH]
+
+  size_t ws_bytes;
+};
+
+// Validate + fill the shape/settings part.  Returns SPARSEPR_OK or an error.
+sparsepr_status plan_init(Plan* p, const sparsepr_config* cfg, int B, int H, int N, int d,
+                          int dtype);
+// Fill the io views from a tensor description (validated).
+sparsepr_status plan_io(Plan* p, const sparsepr_tensors* io);
+// Carve `base` (may be null to only size).  Sets ws_bytes.
+void plan_carve(Plan* p, char* base);
+
+}  // namespace sp

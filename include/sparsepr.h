@@ -1,0 +1,207 @@
+/*
+ * sparsepr.h -- C ABI of libsparsepr, a gfx950 (MI355X) implementation of one
+ * SparsePR attention call: Response-Coupled Partitioning, block-sparse
+ * attention over the group-permuted layout, and Probe-Fitted Residual
+ * Reconstruction.
+ *
+ * Sources (page title, section):
+ *   [TS] "Resumen Técnico: SparsePR – Atención Dispersa Libre de Entrenamiento
+ *        para Generación de Vídeo y Modelos de Mundo" (gist.science), 2.A-2.C.
+ *   [NE] news explainer reposted from 科技行者 (huashangw.com), sections
+ *        "SparsePR：先把误差聚拢，再用少量“抽查”去纠正" (NE/method) and
+ *        "稀疏执行怎么落地，误差怎么算才公平" (NE/exec).
+ *   [DG] "Partition the Support, Reconstruct the Residual: 无训练稀疏注意力用于
+ *        视频生成与世界模型" (ai-feeds.com digest), 方法 and 行业影响 sections.
+ *
+ * Problem statement ([DG] 方法/输入-输出): given Q, K, V of one attention call,
+ * a target executed-pair density and a probe budget, return the corrected
+ * attention output.  It replaces scaled-dot-product attention without state
+ * kept between calls ([DG] 行业影响/与现有工作流的接口).
+ *
+ * Conventions shared by every call:
+ *   - All tensor pointers are DEVICE pointers owned by the caller.  The
+ *     library never allocates, frees or keeps device memory between calls;
+ *     scratch lives in a caller-provided workspace sized by
+ *     sparsepr_workspace_size().
+ *   - Calls are asynchronous on `stream` (a hipStream_t passed as void*; NULL
+ *     is the legacy default stream).  SPARSEPR_OK means "enqueued".  Argument
+ *     errors are detected on the host before anything is enqueued.  A failed
+ *     kernel launch returns SPARSEPR_ERR_HIP and sparsepr_last_hip_error()
+ *     holds the hipError_t (per thread).  The library never synchronises.
+ *   - Tensors are [B, H, N, d] with element strides given per tensor; the
+ *     d-stride must be 1 and rows must be 16-byte aligned.  Q, K, V and O
+ *     must not alias each other or the workspace.
+ *   - Supported: dtype bf16 or fp32, d in {64, 128}, 2 <= N <= 2^20, B*H >= 1,
+ *     1 <= G_K, G_Q <= 1024 with G_Q*G_K <= 2^20 and G <= N, probe rows
+ *     0..min(256, N), residual rank 0..64, T >= 1 k-means steps.
+ *   - Calls on different streams with different workspaces may run
+ *     concurrently; calls that share a workspace must be ordered.
+ */
+#ifndef SPARSEPR_H
+#define SPARSEPR_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SPARSEPR_OK = 0,
+  SPARSEPR_ERR_INVALID_ARG = -1,
+  SPARSEPR_ERR_UNSUPPORTED = -2,
+  SPARSEPR_ERR_WORKSPACE = -3,
+  SPARSEPR_ERR_HIP = -4,
+  SPARSEPR_ERR_INTERNAL = -5
+} sparsepr_status;
+
+typedef enum { SPARSEPR_BF16 = 0, SPARSEPR_FP32 = 1 } sparsepr_dtype;
+
+typedef enum {
+  /* keys clustered on key-response coordinates, queries on their logits against
+     the K/V-group centres ([TS] 2.A) */
+  SPARSEPR_PART_RESPONSE_COUPLED = 0,
+  /* comparison partition: Q and K clustered separately on raw activations
+     ([NE] NE/method contrasts it with the response-coupled one) */
+  SPARSEPR_PART_INDEPENDENT = 1
+} sparsepr_partition_mode;
+
+/* Method settings.  Every field is a value the pages leave open unless noted;
+   sparsepr_config_default() fills the documented defaults. */
+typedef struct {
+  float density;          /* target executed-pair density rho in (0, 1]; probe
+                             rows count toward it ([TS] 2.C).  >= 1 grants every cell */
+  int probe_rows;         /* M exact rows per (b,h), 64 by default ([NE] NE/method); 0 = no fit */
+  int n_kv_groups;        /* G_K paired K/V groups */
+  int n_q_groups;         /* G_Q query groups */
+  int residual_rank;      /* r: leading residual singular directions kept ([NE] keeps 16) */
+  float ridge_lambda;     /* absolute ridge lambda of the affine fit ([TS] 2.B) */
+  int kmeans_iters;       /* T Lloyd steps, no early stop */
+  int n_sample_q;         /* M_s upper bound of sampled queries (min with N) */
+  int key_coord_rank;     /* r_K upper bound of kept eigenvectors of M_K (min with d, M_s) */
+  float scale;            /* softmax scale; 0 => 1/sqrt(d) rounded to float */
+  float rank_cut;         /* relative singular-value cut of the residual subspace */
+  int partition_mode;     /* sparsepr_partition_mode */
+  unsigned long long seed;/* seed of the query sample (splitmix64) */
+} sparsepr_config;
+
+/* Input/output description.  Strides are in elements, order [b, h, n, d]. */
+typedef struct {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  long long q_strides[4];
+  long long k_strides[4];
+  long long v_strides[4];
+  long long o_strides[4];
+  int B, H, N, d;
+  int dtype;              /* sparsepr_dtype; q, k, v and o share it */
+} sparsepr_tensors;
+
+/* Per-(b,h) statistics written by the device when a stats pointer is given
+   (device memory, B*H entries, row-major over (b,h)). */
+typedef struct {
+  long long routed_pairs;     /* sum over granted cells of |Q_g| * |K_h| */
+  long long budget_pairs;     /* floor(rho N^2) - M N */
+  long long mandatory_pairs;  /* cost of the best cell of every query group */
+  long long probe_pairs;      /* M N */
+  int granted_cells;
+  int nonempty_q_groups;
+  int nonempty_kv_groups;
+  int probe_rows;
+  int residual_rank;          /* r' actually used by the fit */
+  int over_budget;            /* 1 when the mandatory cells alone exceed the budget */
+  int q_tiles;                /* query tiles run by the sparse kernel */
+  int reserved;
+  double rho_route;           /* routed_pairs / N^2 */
+  double rho_exec;            /* (routed_pairs + probe_pairs) / N^2 */
+  double sigma[4];            /* leading singular values of the probe residuals */
+} sparsepr_head_stats;
+
+/* Fill `out` with the defaults for a call of N tokens and head dim d:
+   density 0.25, 64 probe rows, G_K = G_Q = clamp(N/128, 1, 256), r = 32,
+   lambda 1e-3, T = 10, M_s = 256, r_K = 32, scale 0, rank_cut 1e-6,
+   response-coupled partition, seed 0. */
+sparsepr_status sparsepr_config_default(int N, int d, sparsepr_config* out);
+
+/* Check a config against a shape (no device work). */
+sparsepr_status sparsepr_validate(const sparsepr_config* cfg, int B, int H, int N, int d, int dtype);
+
+/* Bytes of workspace every entry point below needs for this shape (256-byte
+   aligned base required). */
+sparsepr_status sparsepr_workspace_size(const sparsepr_config* cfg, int B, int H, int N, int d,
+                                        int dtype, size_t* bytes);
+
+/* The full call ([NE] NE/exec latency chain: partition construction, routing,
+   tensor reorder, sparse attention, exact probe rows, residual fit,
+   correction, output restoration).  Writes o in the original token order.
+   `stats` (device pointer, nullable) receives B*H sparsepr_head_stats. */
+sparsepr_status sparsepr_attention(const sparsepr_config* cfg, const sparsepr_tensors* io,
+                                   void* workspace, size_t workspace_bytes, void* stream,
+                                   sparsepr_head_stats* stats);
+
+/* The full call with the partition given instead of computed: q_labels and
+   kv_labels are device int32 arrays [B*H, N] with values in [0, G_Q) and
+   [0, G_K).  Used to check the stages after partitioning in isolation. */
+sparsepr_status sparsepr_attention_with_partition(const sparsepr_config* cfg,
+                                                  const sparsepr_tensors* io,
+                                                  const int* q_labels, const int* kv_labels,
+                                                  void* workspace, size_t workspace_bytes,
+                                                  void* stream, sparsepr_head_stats* stats);
+
+/* Stage a1-a2 ([TS] 2.A): the sampled query rows (device int32 [B*H, M_s],
+   ascending), M_K = Q_s^T Q_s / M_s (device float [B*H, d, d]) and the
+   eigenvalues of M_K in descending order (device float [B*H, d]).  Any output
+   pointer may be NULL. */
+sparsepr_status sparsepr_key_metric(const sparsepr_config* cfg, const sparsepr_tensors* io,
+                                    void* workspace, size_t workspace_bytes, void* stream,
+                                    int* sample_idx, float* m_k, float* eigvals);
+
+/* Stages a1-a8: response-coupled (or independent) partition.  Writes the
+   labels of the last Lloyd step (device int32 [B*H, N] each). */
+sparsepr_status sparsepr_partition(const sparsepr_config* cfg, const sparsepr_tensors* io,
+                                   void* workspace, size_t workspace_bytes, void* stream,
+                                   int* q_labels, int* kv_labels);
+
+/* Stages a5, a9-a10 from given labels ([TS] 2.C, [NE] NE/exec): stable group
+   permutations perm_q/perm_k (position -> token, int32 [B*H, N]), group
+   offsets off_q [B*H, G_Q+1] and off_k [B*H, G_K+1], and the granted cells as
+   CSR per query group: csr_rowptr [B*H, G_Q+1], csr_cols [B*H, G_Q*G_K]
+   (key-group ids ascending within a row).  NULL outputs are skipped. */
+sparsepr_status sparsepr_route(const sparsepr_config* cfg, const sparsepr_tensors* io,
+                               const int* q_labels, const int* kv_labels,
+                               void* workspace, size_t workspace_bytes, void* stream,
+                               int* perm_q, int* perm_k, int* off_q, int* off_k,
+                               int* csr_rowptr, int* csr_cols, sparsepr_head_stats* stats);
+
+/* Stage a12 alone from given labels: the uncorrected ("hard-drop") sparse
+   output written to io->o in the original token order. */
+sparsepr_status sparsepr_sparse_attention(const sparsepr_config* cfg, const sparsepr_tensors* io,
+                                          const int* q_labels, const int* kv_labels,
+                                          void* workspace, size_t workspace_bytes, void* stream);
+
+/* Stages a11, a13-a14 from given labels ([TS] 2.B, [NE] NE/method): probe
+   positions in permuted order (int32 [B*H, M]), their exact dense outputs and
+   sparse outputs (float [B*H, M, d]), and the fitted correction: W and Vr
+   (float [B*H, d, r], zero beyond the used rank) with B = W Vr^T, the bias
+   b (float [B*H, d]) and the used rank r' (int32 [B*H]).  NULL outputs are
+   skipped. */
+sparsepr_status sparsepr_probe_fit(const sparsepr_config* cfg, const sparsepr_tensors* io,
+                                   const int* q_labels, const int* kv_labels,
+                                   void* workspace, size_t workspace_bytes, void* stream,
+                                   int* probe_pos, float* o_dense, float* o_sparse,
+                                   float* w_mat, float* v_mat, float* bias, int* rank);
+
+/* Dense softmax attention over all keys (the speed baseline), bf16 or fp32,
+   no workspace; scale 0 => 1/sqrt(d). */
+sparsepr_status sparsepr_dense_attention(const sparsepr_tensors* io, float scale, void* stream);
+
+const char* sparsepr_status_string(sparsepr_status s);
+int sparsepr_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPARSEPR_H */

@@ -1,0 +1,104 @@
+"""Shared parity cases: seeded inputs, matching oracle and library configs."""
+
+from __future__ import annotations
+
+import dataclasses
+import functools
+
+import numpy as np
+
+from oracle import OracleConfig, dense_attention, sparsepr_head
+from synth import make_video_qkv, make_workload_inputs, workload
+
+
+@dataclasses.dataclass(frozen=True)
+class Case:
+    name: str
+    frames: int
+    height: int
+    width: int
+    heads: int
+    d: int
+    dtype: str
+    gk: int
+    gq: int
+    density: float
+    probes: int
+    rank: int
+    f90: float = 0.06
+    seed: int = 7
+    mode: str = "response_coupled"
+    workload: str = ""
+
+    @property
+    def n(self):
+        return self.frames * self.height * self.width
+
+    def oracle_cfg(self) -> OracleConfig:
+        return OracleConfig(density=self.density, probe_rows=self.probes, n_kv_groups=self.gk,
+                            n_q_groups=self.gq, residual_rank=self.rank, partition_mode=self.mode)
+
+    def lib_cfg_kwargs(self) -> dict:
+        return dict(density=self.density, probe_rows=self.probes, n_kv_groups=self.gk, n_q_groups=self.gq,
+                    residual_rank=self.rank, partition_mode=0 if self.mode == "response_coupled" else 1)
+
+
+CASES = {
+    # the tiny fp32 call of the workload table (16/16 groups, 64 probes, rank 16)
+    "c1_tiny_fp32": Case("c1_tiny_fp32", 4, 16, 16, 1, 64, "fp32", 16, 16, 0.25, 64, 16,
+                         workload="c1_tiny_fp32"),
+    # bf16, d = 64, ragged groups and a ragged key tail, 2 heads
+    "bf16_d64": Case("bf16_d64", 4, 10, 25, 2, 64, "bf16", 12, 10, 0.3, 32, 8, seed=11),
+    # bf16, d = 128, few large query groups: several query tiles per group
+    "bf16_d128": Case("bf16_d128", 2, 16, 32, 2, 128, "bf16", 16, 4, 0.3, 48, 8, seed=12),
+    # comparison partition (independent Q/K k-means)
+    "bf16_d64_indep": Case("bf16_d64_indep", 4, 10, 25, 1, 64, "bf16", 12, 10, 0.3, 32, 8, seed=13,
+                           mode="independent"),
+    # two heads of the 8k video-DiT call
+    "c2_two_heads": Case("c2_two_heads", 8, 32, 32, 2, 64, "bf16", 64, 64, 0.25, 64, 32,
+                         workload="c2_dit_8k"),
+}
+
+
+@functools.lru_cache(maxsize=None)
+def inputs(name: str):
+    c = CASES[name]
+    if c.workload:
+        return make_workload_inputs(workload(c.workload), heads=c.heads)
+    return make_video_qkv(c.frames, c.height, c.width, c.heads, c.d, c.dtype, c.seed, [c.f90] * c.heads)
+
+
+@functools.lru_cache(maxsize=None)
+def oracle_result(name: str):
+    c = CASES[name]
+    x = inputs(name)
+    cfg = c.oracle_cfg()
+    heads = []
+    for h in range(c.heads):
+        q = x["q"][0, h].double().numpy()
+        k = x["k"][0, h].double().numpy()
+        v = x["v"][0, h].double().numpy()
+        r = sparsepr_head(q, k, v, cfg, bh=h)
+        r["dense"] = dense_attention(q, k, v, r["scale"])
+        heads.append(r)
+    return heads
+
+
+def rel_frob(a, b) -> float:
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300))
+
+
+def max_abs(a, b) -> float:
+    return float(np.abs(np.asarray(a, dtype=np.float64) - np.asarray(b, dtype=np.float64)).max())
+
+
+def tolerances(dtype: str):
+    """(max-abs, relative Frobenius) bounds for attention outputs.
+
+    bf16: the bounds stated for bf16 outputs against the fp64/fp32 oracle.
+    fp32: the kernels accumulate in fp32 over a few thousand terms, so errors
+    stay near 1e-6 relative; the bounds leave two orders of margin.
+    """
+    return (2e-2, 5e-3) if dtype == "bf16" else (1e-4, 1e-5)

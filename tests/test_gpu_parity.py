@@ -1,0 +1,198 @@
+"""GPU path vs the CPU oracle on the same seeded inputs (small sizes).
+
+Every comparison goes through the C ABI of libsparsepr.  Integer stages
+(sample, grouping, permutation, routing) must match bit for bit when the GPU
+is fed the oracle's partition; floating outputs must stay inside the stated
+tolerances; the partition computed on the GPU must agree with the oracle's on
+at least 99% of tokens, with the corrected-output error against dense within
+1.1x the oracle's.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import free_block_sparse_amd as sp
+from parity_cases import CASES, inputs, max_abs, oracle_result, rel_frob, tolerances
+
+pytestmark = pytest.mark.gpu
+
+ALL = list(CASES)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def dev_inputs(name):
+    x = inputs(name)
+    return (x["q"].cuda(), x["k"].cuda(), x["v"].cuda())
+
+
+def lib_cfg(name):
+    c = CASES[name]
+    return sp.make_config(c.n, c.d, **c.lib_cfg_kwargs())
+
+
+def oracle_labels(name):
+    heads = oracle_result(name)
+    ql = torch.tensor(np.stack([h["q_labels"] for h in heads]), dtype=torch.int32).cuda()
+    kl = torch.tensor(np.stack([h["kv_labels"] for h in heads]), dtype=torch.int32).cuda()
+    return ql, kl
+
+
+def banner(name, what):
+    c = CASES[name]
+    print(f"[parity] {what} case={name} N={c.n} H={c.heads} d={c.d} dtype={c.dtype}", flush=True)
+
+
+@pytest.mark.parametrize("name", ALL)
+def test_key_metric_sample_and_spectrum(name):
+    c = CASES[name]
+    if c.mode != "response_coupled":
+        pytest.skip("no key metric in the independent partition")
+    banner(name, "key_metric")
+    q, k, v = dev_inputs(name)
+    smp, mk, ev = sp.sparsepr_key_metric(q, k, v, lib_cfg(name))
+    torch.cuda.synchronize()
+    for h, r in enumerate(oracle_result(name)):
+        assert np.array_equal(smp[h].cpu().numpy(), r["sample"])  # integer spec: bit-exact
+        assert rel_frob(mk[h].cpu().numpy(), r["m_k"]) < 1e-5
+        lam_ref = np.sort(np.linalg.eigvalsh(r["m_k"]))[::-1]
+        lam = ev[h].cpu().double().numpy()
+        assert np.abs(lam - lam_ref).max() <= 2e-5 * lam_ref[0]
+
+
+@pytest.mark.parametrize("name", ALL)
+def test_grouping_and_routing_bit_exact(name):
+    banner(name, "route")
+    q, k, v = dev_inputs(name)
+    ql, kl = oracle_labels(name)
+    res = sp.sparsepr_route(q, k, v, lib_cfg(name), ql, kl)
+    torch.cuda.synchronize()
+    stats = sp.stats_to_dicts(res["stats"])
+    for h, r in enumerate(oracle_result(name)):
+        assert np.array_equal(res["perm_q"][h].cpu().numpy(), r["perm_q"])
+        assert np.array_equal(res["perm_k"][h].cpu().numpy(), r["perm_k"])
+        assert np.array_equal(res["off_q"][h].cpu().numpy(), r["off_q"])
+        assert np.array_equal(res["off_k"][h].cpu().numpy(), r["off_k"])
+        rt = r["route"]
+        rp = res["csr_rowptr"][h].cpu().numpy()
+        assert np.array_equal(rp, rt["csr_rowptr"])
+        assert np.array_equal(res["csr_cols"][h, :rp[-1]].cpu().numpy(), rt["csr_cols"])
+        assert stats[h]["routed_pairs"] == rt["routed_pairs"]
+        assert stats[h]["rho_exec"] == pytest.approx(rt["rho_exec"], abs=0)
+
+
+@pytest.mark.parametrize("name", ALL)
+def test_sparse_attention_matches_oracle(name):
+    banner(name, "sparse_attention")
+    c = CASES[name]
+    q, k, v = dev_inputs(name)
+    ql, kl = oracle_labels(name)
+    out = sp.sparsepr_sparse_attention(q, k, v, lib_cfg(name), ql, kl)
+    torch.cuda.synchronize()
+    ma, rf = tolerances(c.dtype)
+    for h, r in enumerate(oracle_result(name)):
+        got = out[0, h].double().cpu().numpy()
+        assert max_abs(got, r["hard_drop"]) <= ma
+        assert rel_frob(got, r["hard_drop"]) <= rf
+
+
+@pytest.mark.parametrize("name", ALL)
+def test_probe_rows_and_fit_match_oracle(name):
+    banner(name, "probe_fit")
+    c = CASES[name]
+    q, k, v = dev_inputs(name)
+    ql, kl = oracle_labels(name)
+    res = sp.sparsepr_probe_fit(q, k, v, lib_cfg(name), ql, kl)
+    torch.cuda.synchronize()
+    ma, rf = tolerances(c.dtype)
+    for h, r in enumerate(oracle_result(name)):
+        assert np.array_equal(res["probe_pos"][h].cpu().numpy(), r["probes"])
+        od = res["o_dense"][h].double().cpu().numpy()
+        os_ = res["o_sparse"][h].double().cpu().numpy()
+        assert max_abs(od, r["o_dense_probe"]) <= ma and rel_frob(od, r["o_dense_probe"]) <= rf
+        osp_ref = r["o_sparse_perm"][r["probes"]]
+        assert max_abs(os_, osp_ref) <= ma and rel_frob(os_, osp_ref) <= rf
+        assert int(res["rank"][h]) == r["fit"]["rank"]
+
+
+@pytest.mark.parametrize("name", ALL)
+def test_corrected_output_with_oracle_partition(name):
+    banner(name, "attention_with_partition")
+    c = CASES[name]
+    q, k, v = dev_inputs(name)
+    ql, kl = oracle_labels(name)
+    out = sp.sparsepr_attention_with_partition(q, k, v, lib_cfg(name), ql, kl)
+    torch.cuda.synchronize()
+    ma, rf = tolerances(c.dtype)
+    for h, r in enumerate(oracle_result(name)):
+        got = out[0, h].double().cpu().numpy()
+        tok = r["perm_q"][r["probes"]]
+        # probe rows carry their exact dense output
+        assert max_abs(got[tok], r["dense"][tok]) <= ma
+        print(f"  head {h}: corrected max-abs {max_abs(got, r['out']):.3e} rel {rel_frob(got, r['out']):.3e}")
+        assert max_abs(got, r["out"]) <= ma
+        assert rel_frob(got, r["out"]) <= rf
+
+
+@pytest.mark.parametrize("name", ALL)
+def test_end_to_end_partition_agreement_and_error(name):
+    banner(name, "attention")
+    q, k, v = dev_inputs(name)
+    cfg = lib_cfg(name)
+    ql, kl = sp.sparsepr_partition(q, k, v, cfg)
+    out = sp.sparsepr_attention(q, k, v, cfg)
+    torch.cuda.synchronize()
+    for h, r in enumerate(oracle_result(name)):
+        agree_k = (kl[h].cpu().numpy() == r["kv_labels"]).mean()
+        agree_q = (ql[h].cpu().numpy() == r["q_labels"]).mean()
+        err_gpu = rel_frob(out[0, h].double().cpu().numpy(), r["dense"])
+        err_ora = rel_frob(r["out"], r["dense"])
+        print(f"  head {h}: agreement K {agree_k:.4f} Q {agree_q:.4f}; err vs dense gpu {err_gpu:.4f} "
+              f"oracle {err_ora:.4f}")
+        assert agree_k >= 0.99 and agree_q >= 0.99
+        assert err_gpu <= 1.1 * err_ora
+
+
+@pytest.mark.parametrize("name", ["c1_tiny_fp32", "bf16_d64", "bf16_d128"])
+def test_dense_attention_matches_oracle(name):
+    banner(name, "dense_attention")
+    c = CASES[name]
+    q, k, v = dev_inputs(name)
+    out = sp.sparsepr_dense_attention(q, k, v)
+    torch.cuda.synchronize()
+    ma, rf = tolerances(c.dtype)
+    for h, r in enumerate(oracle_result(name)):
+        got = out[0, h].double().cpu().numpy()
+        assert max_abs(got, r["dense"]) <= ma and rel_frob(got, r["dense"]) <= rf
+
+
+@pytest.mark.parametrize("name", ["bf16_d64", "c1_tiny_fp32"])
+def test_two_runs_are_bitwise_identical(name):
+    banner(name, "determinism")
+    q, k, v = dev_inputs(name)
+    cfg = lib_cfg(name)
+    a = sp.sparsepr_attention(q, k, v, cfg)
+    b = sp.sparsepr_attention(q, k, v, cfg)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+def test_full_density_is_dense_attention():
+    name = "bf16_d64"
+    banner(name, "full density")
+    c = CASES[name]
+    q, k, v = dev_inputs(name)
+    cfg = lib_cfg(name)
+    cfg.density = 1.0
+    out = sp.sparsepr_attention(q, k, v, cfg)
+    dense = sp.sparsepr_dense_attention(q, k, v)
+    torch.cuda.synchronize()
+    ma, rf = tolerances(c.dtype)
+    for h, r in enumerate(oracle_result(name)):
+        got = out[0, h].double().cpu().numpy()
+        assert max_abs(got, r["dense"]) <= ma and rel_frob(got, r["dense"]) <= rf
