@@ -38,6 +38,7 @@ struct AttnArgs {
   float scale;
   int correct;
   int dense;
+  const int* vexp;  // V stored as fp16 * 2^-vexp (null: V in the input dtype)
 };
 
 __device__ inline int seg_find(const int* sv, int n, int v) {
@@ -137,7 +138,7 @@ __device__ inline bool setup_item(const AttnArgs& a, int bh, int tile, int* seg_
 // LDS; the contraction order over keys inside a 16-key step follows the S^T
 // register layout (keys 16s + 4h + {0..3} and 16s + 8 + 4h + {0..3}).
 // ============================================================================
-template <int D>
+template <int D, bool VF16>
 __global__ __launch_bounds__(256, 2) void k_sparse_attn_mfma(AttnArgs a) {
   constexpr int KS = D / 16, DB = D / 32;
   constexpr int LDK = D + 8, LDV = 64 + 8;
@@ -231,19 +232,33 @@ __global__ __launch_bounds__(256, 2) void k_sparse_attn_mfma(AttnArgs a) {
 #pragma unroll
       for (int st = 0; st < 4; ++st) {
         const int kt = st >> 1, rb = 8 * (st & 1);
-        uint4 pk;
-        pk.x = (uint32_t)f32_to_bf16(sacc[kt][rb + 0]) | ((uint32_t)f32_to_bf16(sacc[kt][rb + 1]) << 16);
-        pk.y = (uint32_t)f32_to_bf16(sacc[kt][rb + 2]) | ((uint32_t)f32_to_bf16(sacc[kt][rb + 3]) << 16);
-        pk.z = (uint32_t)f32_to_bf16(sacc[kt][rb + 4]) | ((uint32_t)f32_to_bf16(sacc[kt][rb + 5]) << 16);
-        pk.w = (uint32_t)f32_to_bf16(sacc[kt][rb + 6]) | ((uint32_t)f32_to_bf16(sacc[kt][rb + 7]) << 16);
-        const bf16x8 pf = __builtin_bit_cast(bf16x8, pk);
+        if constexpr (VF16) {
+          f16x8 pf;
 #pragma unroll
-        for (int b = 0; b < DB; ++b) {
-          const bf16_t* vrow = Vt + (32 * b + col) * LDV + 16 * st + 4 * half;
-          const uint2 lo = *reinterpret_cast<const uint2*>(vrow);
-          const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 8);
-          const bf16x8 vf = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
-          o[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, o[b], 0, 0, 0);
+          for (int j = 0; j < 8; ++j) pf[j] = (_Float16)sacc[kt][rb + j];
+#pragma unroll
+          for (int b = 0; b < DB; ++b) {
+            const bf16_t* vrow = Vt + (32 * b + col) * LDV + 16 * st + 4 * half;
+            const uint2 lo = *reinterpret_cast<const uint2*>(vrow);
+            const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 8);
+            const f16x8 vf = __builtin_bit_cast(f16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+            o[b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, pf, o[b], 0, 0, 0);
+          }
+        } else {
+          uint4 pk;
+          pk.x = (uint32_t)f32_to_bf16(sacc[kt][rb + 0]) | ((uint32_t)f32_to_bf16(sacc[kt][rb + 1]) << 16);
+          pk.y = (uint32_t)f32_to_bf16(sacc[kt][rb + 2]) | ((uint32_t)f32_to_bf16(sacc[kt][rb + 3]) << 16);
+          pk.z = (uint32_t)f32_to_bf16(sacc[kt][rb + 4]) | ((uint32_t)f32_to_bf16(sacc[kt][rb + 5]) << 16);
+          pk.w = (uint32_t)f32_to_bf16(sacc[kt][rb + 6]) | ((uint32_t)f32_to_bf16(sacc[kt][rb + 7]) << 16);
+          const bf16x8 pf = __builtin_bit_cast(bf16x8, pk);
+#pragma unroll
+          for (int b = 0; b < DB; ++b) {
+            const bf16_t* vrow = Vt + (32 * b + col) * LDV + 16 * st + 4 * half;
+            const uint2 lo = *reinterpret_cast<const uint2*>(vrow);
+            const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 8);
+            const bf16x8 vf = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+            o[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, o[b], 0, 0, 0);
+          }
         }
       }
     }
@@ -252,7 +267,8 @@ __global__ __launch_bounds__(256, 2) void k_sparse_attn_mfma(AttnArgs a) {
 
   // ---- epilogue: normalise, correct (b + x W V^T), restore token order
   const float ltot = l + __shfl_xor(l, 32, 64);
-  const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
+  float inv = ltot > 0.f ? 1.f / ltot : 0.f;
+  if (VF16) inv = ldexpf(inv, a.vexp[bh]);
   float x[DB][16];
 #pragma unroll
   for (int b = 0; b < DB; ++b)
@@ -445,9 +461,10 @@ struct ProbeArgs {
   float* ppart;  // [BH, n_pchunk, 2, M, D + 2]
   float* ode;
   float* osp;
+  const int* vexp;
 };
 
-template <typename T, int D>
+template <typename T, typename VT, int D>
 __global__ __launch_bounds__(256) void k_probe_attn_vec(ProbeArgs a) {
   constexpr int DQ = D / 4;
   __shared__ float Kt[32][D + 1];
@@ -465,7 +482,7 @@ __global__ __launch_bounds__(256) void k_probe_attn_vec(ProbeArgs a) {
   }
   const T* qb = static_cast<const T*>(a.qv.p);
   const T* kb = static_cast<const T*>(a.kv.p);
-  const T* vb = static_cast<const T*>(a.vv.p);
+  const VT* vb = static_cast<const VT*>(a.vv.p);
   float q[DQ], od[DQ], os[DQ];
   const int prow = valid ? a.ppos[(long long)bh * a.M + p] : 0;
 #pragma unroll
@@ -485,7 +502,7 @@ __global__ __launch_bounds__(256) void k_probe_attn_vec(ProbeArgs a) {
       float kx = 0.f, vx = 0.f;
       if (v < k1) {
         kx = Elem<T>::load(kb + a.kv.row_off(bh, v) + cc);
-        vx = Elem<T>::load(vb + a.vv.row_off(bh, v) + cc);
+        vx = Elem<VT>::load(vb + a.vv.row_off(bh, v) + cc);
       }
       Kt[r][cc] = kx;
       Vs[r][cc] = vx;
@@ -538,13 +555,14 @@ __global__ __launch_bounds__(256) void k_probe_attn_vec(ProbeArgs a) {
     ms = mns;
   }
   if (!valid) return;
+  const float vs = a.vexp ? ldexpf(1.0f, a.vexp[bh]) : 1.0f;
   float* base = a.ppart + (((long long)bh * a.n_pchunk + ch) * 2) * a.M * (D + 2);
   float* pd = base + (long long)p * (D + 2);
   float* ps = base + ((long long)a.M + p) * (D + 2);
 #pragma unroll
   for (int i = 0; i < DQ; ++i) {
-    pd[sub + 4 * i] = od[i];
-    ps[sub + 4 * i] = os[i];
+    pd[sub + 4 * i] = od[i] * vs;
+    ps[sub + 4 * i] = os[i] * vs;
   }
   if (sub == 0) {
     pd[D] = md;
@@ -623,14 +641,20 @@ static AttnArgs attn_args(const Plan& p, bool correct) {
   a.scale = p.scale;
   a.correct = correct && p.M > 0 ? 1 : 0;
   a.dense = 0;
+  a.vexp = p.dtype == SPARSEPR_BF16 ? p.vexp : nullptr;
   return a;
 }
 
 static hipError_t launch_attn(const AttnArgs& a, int grid_x, int BH, int d, int dtype, hipStream_t s) {
   dim3 g(grid_x, BH);
   if (dtype == SPARSEPR_BF16) {
-    if (d == 128) hipLaunchKernelGGL(k_sparse_attn_mfma<128>, g, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL(k_sparse_attn_mfma<64>, g, dim3(256), 0, s, a);
+    if (a.vexp) {
+      if (d == 128) hipLaunchKernelGGL((k_sparse_attn_mfma<128, true>), g, dim3(256), 0, s, a);
+      else hipLaunchKernelGGL((k_sparse_attn_mfma<64, true>), g, dim3(256), 0, s, a);
+    } else {
+      if (d == 128) hipLaunchKernelGGL((k_sparse_attn_mfma<128, false>), g, dim3(256), 0, s, a);
+      else hipLaunchKernelGGL((k_sparse_attn_mfma<64, false>), g, dim3(256), 0, s, a);
+    }
   } else {
     if (d == 128) hipLaunchKernelGGL((k_sparse_attn_vec<float, 128>), g, dim3(512), 0, s, a);
     else hipLaunchKernelGGL((k_sparse_attn_vec<float, 64>), g, dim3(512), 0, s, a);
@@ -680,11 +704,13 @@ hipError_t launch_probe_attention(const Plan& p, hipStream_t s) {
   a.osp = p.osp;
   dim3 g(p.n_pchunk, (p.M + 63) / 64, p.BH);
   if (p.dtype == SPARSEPR_BF16) {
-    if (p.d == 128) hipLaunchKernelGGL((k_probe_attn_vec<bf16_t, 128>), g, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((k_probe_attn_vec<bf16_t, 64>), g, dim3(256), 0, s, a);
+    a.vexp = p.vexp;
+    if (p.d == 128) hipLaunchKernelGGL((k_probe_attn_vec<bf16_t, _Float16, 128>), g, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((k_probe_attn_vec<bf16_t, _Float16, 64>), g, dim3(256), 0, s, a);
   } else {
-    if (p.d == 128) hipLaunchKernelGGL((k_probe_attn_vec<float, 128>), g, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((k_probe_attn_vec<float, 64>), g, dim3(256), 0, s, a);
+    a.vexp = nullptr;
+    if (p.d == 128) hipLaunchKernelGGL((k_probe_attn_vec<float, float, 128>), g, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((k_probe_attn_vec<float, float, 64>), g, dim3(256), 0, s, a);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -570,8 +570,44 @@ __global__ __launch_bounds__(1024) void k_query_metric(QMetricArgs a) {
 }
 
 // ============================================================================
-// a9: gather Q, K, V into group-contiguous order; key-group id per position
+// a9: gather Q, K, V into group-contiguous order; key-group id per position.
+// For bf16 inputs V is stored as fp16 scaled by a per-(b,h) power of two 2^-k
+// (k from max |v|, so the largest value lands in [2^14, 2^15)): the P.V
+// product then runs with 11-bit fp16 operands and the scale is undone exactly
+// in the epilogue.
 // ============================================================================
+__global__ __launch_bounds__(256) void k_zero_u32(uint32_t* p, int n) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void k_vmax(View4 v, int N, int d, uint32_t* vmax) {
+  const int bh = blockIdx.y;
+  const int row = blockIdx.x * 256 + threadIdx.x;
+  float m = 0.f;
+  if (row < N) {
+    const T* r = static_cast<const T*>(v.p) + v.row_off(bh, row);
+    for (int c = 0; c < d; ++c) {
+      const float x = fabsf(Elem<T>::load(r + c));
+      m = (x > m || x != x) ? x : m;
+    }
+  }
+  for (int o = 32; o > 0; o >>= 1) {
+    const float t = __shfl_xor(m, o, 64);
+    m = (t > m || t != t) ? t : m;
+  }
+  if ((threadIdx.x & 63) == 0) atomicMax(vmax + bh, __float_as_uint(m));
+}
+
+__device__ inline int v_exponent(uint32_t bits) {
+  const float mx = __uint_as_float(bits);
+  if (!(mx > 0.f) || !(mx < INFINITY)) return 0;
+  int e;
+  frexpf(mx, &e);  // mx = m 2^e, m in [0.5, 1)
+  return e - 15;
+}
+
 template <typename T>
 __global__ __launch_bounds__(256) void k_gather(GatherArgs a) {
   const int bh = blockIdx.y;
@@ -580,6 +616,9 @@ __global__ __launch_bounds__(256) void k_gather(GatherArgs a) {
   const int rows_per_blk = 256 / cpr;
   const int r = threadIdx.x / cpr, c = threadIdx.x - (threadIdx.x / cpr) * cpr;
   const int pos = blockIdx.x * rows_per_blk + r;
+  const bool vf16 = a.vmax != nullptr;
+  const int vk = vf16 ? v_exponent(a.vmax[bh]) : 0;
+  if (vf16 && blockIdx.x == 0 && threadIdx.x == 0) a.vexp[bh] = vk;
   if (pos >= a.N) return;
   const long long dst = ((long long)bh * a.N + pos) * a.d + c * VEC;
   const int tq = a.perm_q[(long long)bh * a.N + pos];
@@ -588,8 +627,17 @@ __global__ __launch_bounds__(256) void k_gather(GatherArgs a) {
       *reinterpret_cast<const uint4*>(static_cast<const T*>(a.q.p) + a.q.row_off(bh, tq) + c * VEC);
   *reinterpret_cast<uint4*>(static_cast<T*>(a.kp) + dst) =
       *reinterpret_cast<const uint4*>(static_cast<const T*>(a.k.p) + a.k.row_off(bh, tk) + c * VEC);
-  *reinterpret_cast<uint4*>(static_cast<T*>(a.vp) + dst) =
-      *reinterpret_cast<const uint4*>(static_cast<const T*>(a.v.p) + a.v.row_off(bh, tk) + c * VEC);
+  const uint4 vv = *reinterpret_cast<const uint4*>(static_cast<const T*>(a.v.p) + a.v.row_off(bh, tk) + c * VEC);
+  if (vf16) {
+    const float sc = ldexpf(1.0f, -vk);
+    const bf16_t* e = reinterpret_cast<const bf16_t*>(&vv);
+    f16x8 h;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) h[j] = (_Float16)(bf16_to_f32(e[j]) * sc);
+    *reinterpret_cast<f16x8*>(static_cast<bf16_t*>(a.vp) + dst) = h;
+  } else {
+    *reinterpret_cast<uint4*>(static_cast<T*>(a.vp) + dst) = vv;
+  }
   if (c == 0) a.kgroup[(long long)bh * a.N + pos] = a.kv_labels[(long long)bh * a.N + tk];
 }
 
@@ -694,8 +742,21 @@ hipError_t launch_query_metric(const Plan& p, hipStream_t s) {
   return hipSuccess;
 }
 
+hipError_t launch_vmax(const Plan& p, hipStream_t s) {
+  if (p.dtype != SPARSEPR_BF16) return hipSuccess;
+  SP_LAUNCH(k_zero_u32, dim3((p.BH + 255) / 256), dim3(256), s, p.vmax, p.BH);
+  SP_LAUNCH(k_vmax<bf16_t>, dim3((p.N + 255) / 256, p.BH), dim3(256), s, p.v, p.N, p.d, p.vmax);
+  return hipSuccess;
+}
+
 hipError_t launch_gather(const Plan& p, hipStream_t s) {
-  GatherArgs a{p.q, p.k, p.v, p.perm_q, p.perm_k, p.kv_labels, p.qp, p.kp, p.vp, p.kgroup, p.N, p.d};
+  const bool vf16 = p.dtype == SPARSEPR_BF16;
+  if (vf16) {
+    hipError_t e = launch_vmax(p, s);
+    if (e != hipSuccess) return e;
+  }
+  GatherArgs a{p.q, p.k, p.v, vf16 ? p.vmax : nullptr, p.vexp, p.perm_q, p.perm_k, p.kv_labels, p.qp, p.kp, p.vp,
+               p.kgroup, p.N, p.d};
   const int vec = 16 / p.esize;
   const int rows_per_blk = 256 / (p.d / vec);
   dim3 g((p.N + rows_per_blk - 1) / rows_per_blk, p.BH);

@@ -12,6 +12,7 @@ typedef uint16_t bf16_t;  // raw bfloat16 bits
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
 constexpr uint64_t kGolden64 = 0x9E3779B97F4A7C15ull;
 
@@ -36,6 +37,10 @@ template <typename T> struct Elem;
 template <> struct Elem<float> {
   __device__ static inline float load(const float* p) { return *p; }
   __device__ static inline void store(float* p, float v) { *p = v; }
+};
+template <> struct Elem<_Float16> {
+  __device__ static inline float load(const _Float16* p) { return (float)*p; }
+  __device__ static inline void store(_Float16* p, float v) { *p = (_Float16)v; }
 };
 template <> struct Elem<bf16_t> {
   __device__ static inline float load(const bf16_t* p) { return bf16_to_f32(*p); }

@@ -104,6 +104,8 @@ struct QMetricArgs {
 
 struct GatherArgs {
   View4 q, k, v;
+  const uint32_t* vmax;   // bf16 inputs: V is stored as fp16 scaled by 2^-vexp
+  int* vexp;
   const int* perm_q;
   const int* perm_k;
   const int* kv_labels;
@@ -124,6 +126,7 @@ hipError_t launch_group_scan(const Plan& p, const ScanArgs& a, hipStream_t s);
 hipError_t launch_group_scatter(const Plan& p, const ScatterArgs& a, hipStream_t s);
 hipError_t launch_centre_update(const Plan& p, const UpdateArgs& a, int pts_type, hipStream_t s);
 hipError_t launch_query_metric(const Plan& p, hipStream_t s);
+hipError_t launch_vmax(const Plan& p, hipStream_t s);
 hipError_t launch_gather(const Plan& p, hipStream_t s);
 
 // router (k_router.hip)

@@ -150,6 +150,8 @@ void plan_carve(Plan* p, char* base) {
   p->kp = c.take<char>(BH * N * d * p->esize);
   p->vp = c.take<char>(BH * N * d * p->esize);
   p->kgroup = c.take<int>(BH * N);
+  p->vmax = c.take<uint32_t>(BH);
+  p->vexp = c.take<int>(BH);
   p->mu = c.take<double>(BH * (long long)p->GQ * p->GK);
   p->ckey = c.take<uint64_t>(BH * (long long)p->GQ * p->GK);
   p->mand = c.take<int>(BH * p->GQ);

@@ -66,6 +66,8 @@ struct Plan {
   void* kp;
   void* vp;
   int* kgroup;            // [BH, N] key-group id of each permuted key position
+  uint32_t* vmax;         // [BH] bit pattern of max |v| (bf16 inputs)
+  int* vexp;              // [BH] power-of-two exponent k: the permuted V holds v * 2^-k in fp16
   double* mu;             // [BH, GQ, GK]
   uint64_t* ckey;         // [BH, GQ, GK] orderable descending log-probability
   int* mand;              // [BH, GQ] best key group per query group (-1 if empty)
