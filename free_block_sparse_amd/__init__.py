@@ -49,6 +49,8 @@ def make_config(n: int, d: int, **kw) -> SparseprConfig:
     for k, v in kw.items():
         if k == "partition_mode" and isinstance(v, str):
             v = {"response_coupled": PART_RESPONSE_COUPLED, "independent": PART_INDEPENDENT}[v]
+        if k == "ridge_mode" and isinstance(v, str):
+            v = {"relative": 0, "absolute": 1}[v]
         if not hasattr(cfg, k):
             raise KeyError(k)
         setattr(cfg, k, v)

@@ -17,6 +17,8 @@ SPARSEPR_BF16 = 0
 SPARSEPR_FP32 = 1
 PART_RESPONSE_COUPLED = 0
 PART_INDEPENDENT = 1
+RIDGE_RELATIVE = 0
+RIDGE_ABSOLUTE = 1
 
 
 class SparseprConfig(ctypes.Structure):
@@ -33,6 +35,7 @@ class SparseprConfig(ctypes.Structure):
         ("scale", ctypes.c_float),
         ("rank_cut", ctypes.c_float),
         ("partition_mode", ctypes.c_int),
+        ("ridge_mode", ctypes.c_int),
         ("seed", ctypes.c_ulonglong),
     ]
 

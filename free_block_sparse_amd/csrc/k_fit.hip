@@ -12,7 +12,8 @@
 //        “抽查”去纠正": ridge regression; the 16 leading singular directions are kept.
 //
 // Computation (readings: unweighted uncentred SVD of R; weighted least squares
-// with an unpenalised intercept; absolute lambda):
+// with an unpenalised intercept; lambda relative to the mean eigenvalue of
+// Xc^T D Xc unless the absolute mode is asked for):
 //   Gram of R (the smaller side) -> Jacobi eigen -> sigma, right singular
 //   vectors V (r' = min(r, M, d, #{sigma > cut sigma_1}));  Y = R V;
 //   weighted means xbar, ybar;  W = (Xc^T D Xc + lambda I)^-1 Xc^T D Yc, solved
@@ -27,6 +28,7 @@ struct FitArgs {
   const float* osp;
   const double* pw;
   int M, d, R, Rcfg;
+  int relative;
   double lambda, cut;
   double* scratch;  // per bh: kFitScratch doubles
   float* W;
@@ -253,9 +255,27 @@ __global__ __launch_bounds__(256) void k_fit(FitArgs a) {
     yb[k] = acc / ws;
   }
   block_sync();
-  // centre Y
+  // centre Y; ridge strength (relative: lambda times the mean eigenvalue of Xc^T D Xc)
   for (int e = tid; e < M * rk; e += nt) Yc[e] -= yb[e % rk];
+  __shared__ double lam_s;
+  if (tid == 0) {
+    double lam = a.lambda;
+    if (a.relative) {
+      double tr = 0.0;
+      for (int mm = 0; mm < M; ++mm) {
+        double s2 = 0.0;
+        for (int dm = 0; dm < d; ++dm) {
+          const double t = (double)osp[mm * d + dm] - xb[dm];
+          s2 += t * t;
+        }
+        tr += w[mm] * s2;
+      }
+      lam *= tr / (double)d;
+    }
+    lam_s = lam;
+  }
   block_sync();
+  const double lam = lam_s;
   bool ok = rk > 0;
   if (rk > 0) {
     if (small) {
@@ -265,7 +285,7 @@ __global__ __launch_bounds__(256) void k_fit(FitArgs a) {
         double acc = 0.0;
         for (int dm = 0; dm < d; ++dm)
           acc += ((double)osp[i * d + dm] - xb[dm]) * ((double)osp[j * d + dm] - xb[dm]);
-        K[e] = sqrt(w[i] * w[j]) * acc + (i == j ? a.lambda : 0.0);
+        K[e] = sqrt(w[i] * w[j]) * acc + (i == j ? lam : 0.0);
       }
       for (int e = tid; e < M * rk; e += nt) Yc[e] *= sqrt(w[e / rk]);
       block_sync();
@@ -300,7 +320,7 @@ __global__ __launch_bounds__(256) void k_fit(FitArgs a) {
         double acc = 0.0;
         for (int mm = 0; mm < M; ++mm)
           acc += w[mm] * ((double)osp[mm * d + i] - xb[i]) * ((double)osp[mm * d + j] - xb[j]);
-        K[e] = acc + (i == j ? a.lambda : 0.0);
+        K[e] = acc + (i == j ? lam : 0.0);
       }
       for (int e = tid; e < d * rk; e += nt) {
         const int i = e / rk, k = e - (e / rk) * rk;
@@ -367,6 +387,7 @@ hipError_t launch_fit(const Plan& p, hipStream_t s) {
   a.d = p.d;
   a.R = p.R > 0 ? p.R : 1;
   a.Rcfg = p.R;
+  a.relative = p.ridge_mode == SPARSEPR_RIDGE_RELATIVE ? 1 : 0;
   a.lambda = (double)p.lambda;
   a.cut = (double)p.rank_cut;
   a.scratch = p.fitscratch;

@@ -215,7 +215,8 @@ sparsepr_status sparsepr_config_default(int N, int d, sparsepr_config* out) {
   out->n_kv_groups = g;
   out->n_q_groups = g;
   out->residual_rank = 32;
-  out->ridge_lambda = 1e-3f;
+  out->ridge_lambda = 1.0f;
+  out->ridge_mode = SPARSEPR_RIDGE_RELATIVE;
   out->kmeans_iters = 10;
   out->n_sample_q = 256;
   out->key_coord_rank = 32;

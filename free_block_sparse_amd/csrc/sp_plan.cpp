@@ -33,6 +33,8 @@ sparsepr_status plan_init(Plan* p, const sparsepr_config* cfg, int B, int H, int
   if (cfg->partition_mode != SPARSEPR_PART_RESPONSE_COUPLED &&
       cfg->partition_mode != SPARSEPR_PART_INDEPENDENT)
     return SPARSEPR_ERR_INVALID_ARG;
+  if (cfg->ridge_mode != SPARSEPR_RIDGE_RELATIVE && cfg->ridge_mode != SPARSEPR_RIDGE_ABSOLUTE)
+    return SPARSEPR_ERR_INVALID_ARG;
 
   p->B = B;
   p->H = H;
@@ -63,6 +65,7 @@ sparsepr_status plan_init(Plan* p, const sparsepr_config* cfg, int B, int H, int
   p->scale = s;
   p->density = cfg->density;
   p->lambda = cfg->ridge_lambda;
+  p->ridge_mode = cfg->ridge_mode;
   p->rank_cut = cfg->rank_cut;
   p->seed = cfg->seed;
   p->dense_route = cfg->density >= 1.0f;

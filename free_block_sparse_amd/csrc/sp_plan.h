@@ -22,6 +22,7 @@ struct Plan {
   int B, H, BH, N, d, dtype, esize;
   int GK, GQ, Gmax, M, R, Ms, rK, rKpad, T, mode;
   int Dk;            // key-side k-means point dimension (padded to 16)
+  int ridge_mode;
   int nchunk;        // ceil(N / kChunk)
   int max_tiles;     // per (b,h) upper bound of query tiles
   int n_pchunk;      // probe key chunks per (b,h)

@@ -66,6 +66,14 @@ typedef enum {
   SPARSEPR_PART_INDEPENDENT = 1
 } sparsepr_partition_mode;
 
+typedef enum {
+  /* lambda is a fraction of the mean eigenvalue of the weighted centred Gram
+     Xc^T D Xc of the probes' sparse outputs (scale free) */
+  SPARSEPR_RIDGE_RELATIVE = 0,
+  /* lambda is used as given */
+  SPARSEPR_RIDGE_ABSOLUTE = 1
+} sparsepr_ridge_mode;
+
 /* Method settings.  Every field is a value the pages leave open unless noted;
    sparsepr_config_default() fills the documented defaults. */
 typedef struct {
@@ -75,13 +83,14 @@ typedef struct {
   int n_kv_groups;        /* G_K paired K/V groups */
   int n_q_groups;         /* G_Q query groups */
   int residual_rank;      /* r: leading residual singular directions kept ([NE] keeps 16) */
-  float ridge_lambda;     /* absolute ridge lambda of the affine fit ([TS] 2.B) */
+  float ridge_lambda;     /* ridge lambda of the affine fit ([TS] 2.B); see ridge_mode */
   int kmeans_iters;       /* T Lloyd steps, no early stop */
   int n_sample_q;         /* M_s upper bound of sampled queries (min with N) */
   int key_coord_rank;     /* r_K upper bound of kept eigenvectors of M_K (min with d, M_s) */
   float scale;            /* softmax scale; 0 => 1/sqrt(d) rounded to float */
   float rank_cut;         /* relative singular-value cut of the residual subspace */
   int partition_mode;     /* sparsepr_partition_mode */
+  int ridge_mode;         /* sparsepr_ridge_mode */
   unsigned long long seed;/* seed of the query sample (splitmix64) */
 } sparsepr_config;
 
@@ -121,8 +130,8 @@ typedef struct {
 
 /* Fill `out` with the defaults for a call of N tokens and head dim d:
    density 0.25, 64 probe rows, G_K = G_Q = clamp(N/128, 1, 256), r = 32,
-   lambda 1e-3, T = 10, M_s = 256, r_K = 32, scale 0, rank_cut 1e-6,
-   response-coupled partition, seed 0. */
+   relative ridge lambda 1.0, T = 10, M_s = 256, r_K = 32, scale 0,
+   rank_cut 1e-6, response-coupled partition, seed 0. */
 sparsepr_status sparsepr_config_default(int N, int d, sparsepr_config* out);
 
 /* Check a config against a shape (no device work). */

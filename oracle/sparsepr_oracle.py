@@ -26,7 +26,9 @@ kept with the design notes; each is a field of ``OracleConfig``):
   U10 probe allocation stratified over non-empty query groups.
   U11 probe rows keep their exact dense output.
   U12 SVD of the unweighted, uncentred probe residuals; rank cut 1e-6 sigma_1.
-  U13 weighted ridge with an unpenalised intercept and absolute lambda.
+  U13 weighted ridge with an unpenalised intercept; lambda is read relative to
+      the mean eigenvalue of the weighted centred Gram of the probes' sparse
+      outputs (scale free, default 1.0); an absolute lambda is a config option.
   U14 softmax scale s = float32(1/sqrt(d)).
 
 Parity pins live in tests/test_oracle_pins.py.  Functions without a pin that
@@ -55,7 +57,8 @@ class OracleConfig:
     n_kv_groups: int = 16          # G_K
     n_q_groups: int = 16           # G_Q
     residual_rank: int = 32        # r
-    ridge_lambda: float = 1e-3     # absolute lambda
+    ridge_lambda: float = 1.0      # ridge strength; see ridge_mode
+    ridge_mode: str = "relative"   # "relative": lambda x mean eigenvalue of Xc^T D Xc; "absolute"
     kmeans_iters: int = 10         # T
     n_sample_q: int = 256          # M_s upper bound
     key_coord_rank: int = 32       # r_K upper bound
@@ -398,7 +401,7 @@ def sparse_attention(qp: np.ndarray, kp: np.ndarray, vp: np.ndarray, granted: np
 # a14: probe-fitted residual reconstruction
 # ----------------------------------------------------------------------------
 def fit_residual(r: np.ndarray, x: np.ndarray, w: np.ndarray, rank: int, lam: float,
-                 cut: float = 1e-6) -> dict:
+                 cut: float = 1e-6, relative: bool = False) -> dict:
     """Fit R ~ b + x B inside the top singular subspace of the probe residuals.
 
     The residual of a probe row is its exact dense output minus its sparse
@@ -411,6 +414,7 @@ def fit_residual(r: np.ndarray, x: np.ndarray, w: np.ndarray, rank: int, lam: fl
     unpenalised intercept:
         W = (Xc^T D Xc + lam I)^-1 Xc^T D Yc,  Y = R V,  b' = ybar - xbar W,
         B = W V^T,  b = b' V^T.
+    With ``relative`` the penalty is lam * trace(Xc^T D Xc) / d.
     """
     m, d = r.shape
     out = {"rank": 0, "sigma": np.zeros(0), "V": np.zeros((d, 0)), "W": np.zeros((d, 0)),
@@ -431,7 +435,9 @@ def fit_residual(r: np.ndarray, x: np.ndarray, w: np.ndarray, rank: int, lam: fl
     ybar = (w[:, None] * y).sum(axis=0) / ws
     xc = x - xbar
     yc = y - ybar
-    a = xc.T @ (w[:, None] * xc) + lam * np.eye(d)
+    gram = xc.T @ (w[:, None] * xc)
+    lam_eff = lam * np.trace(gram) / d if relative else lam
+    a = gram + lam_eff * np.eye(d)
     wmat = np.linalg.solve(a, xc.T @ (w[:, None] * yc))
     bprime = ybar - xbar @ wmat
     out.update(rank=rp, V=v, W=wmat, bprime=bprime, B=wmat @ v.T, b=bprime @ v.T,
@@ -492,7 +498,8 @@ def sparsepr_head(q: np.ndarray, k: np.ndarray, v: np.ndarray, cfg: OracleConfig
     probes, w, mg = select_probes(off_q, m)
     o_de = dense_attention(qp[probes], kp, vp, s) if probes.size else np.zeros((0, d))
     resid = o_de - o_sp[probes]
-    fit = fit_residual(resid, o_sp[probes], w, cfg.residual_rank, cfg.ridge_lambda, cfg.rank_cut)
+    fit = fit_residual(resid, o_sp[probes], w, cfg.residual_rank, cfg.ridge_lambda, cfg.rank_cut,
+                       relative=cfg.ridge_mode == "relative")
 
     corrected = o_sp + fit["b"][None, :] + o_sp @ fit["B"]
     corrected[probes] = o_de

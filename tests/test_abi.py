@@ -31,7 +31,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_struct_sizes_match_header_layout():
-    assert ctypes.sizeof(SparseprConfig) == 56
+    assert ctypes.sizeof(SparseprConfig) == 64
     assert ctypes.sizeof(SparseprTensors) == 4 * 8 + 16 * 8 + 5 * 4 + 4  # padded to 8
     assert ctypes.sizeof(SparseprHeadStats) == 4 * 8 + 8 * 4 + 2 * 8 + 4 * 8
 
@@ -42,7 +42,7 @@ def test_config_defaults():
     assert cfg.n_kv_groups == 255 and cfg.n_q_groups == 255
     assert cfg.residual_rank == 32 and cfg.kmeans_iters == 10
     assert cfg.n_sample_q == 256 and cfg.key_coord_rank == 32
-    assert cfg.ridge_lambda == pytest.approx(1e-3)
+    assert cfg.ridge_lambda == pytest.approx(1.0) and cfg.ridge_mode == 0
     assert sparsepr_config_default(100000, 64).n_kv_groups == 256
 
 
@@ -50,7 +50,7 @@ def test_config_defaults():
     ("density", 0.0), ("density", -1.0), ("probe_rows", -1), ("probe_rows", 300),
     ("n_kv_groups", 0), ("n_q_groups", 2000), ("residual_rank", 65), ("ridge_lambda", -1.0),
     ("kmeans_iters", 0), ("n_sample_q", 0), ("n_sample_q", 257), ("key_coord_rank", 0),
-    ("rank_cut", 1.0), ("partition_mode", 7),
+    ("rank_cut", 1.0), ("partition_mode", 7), ("ridge_mode", 2),
 ])
 def test_validation_rejects_bad_settings(field, value):
     cfg = make_config(4096, 64, n_kv_groups=32, n_q_groups=32)

@@ -63,9 +63,10 @@ def test_key_metric_sample_and_spectrum(name):
         assert rel_frob(mk_gpu, r["m_k"]) < 1e-5
         lam_ref = np.sort(np.linalg.eigvalsh(r["m_k"]))[::-1]
         lam = ev[h].cpu().double().numpy()
-        # Weyl: eigenvalues move by at most ||dM||_2 <= ||dM||_F; plus the fp32
-        # Jacobi stopping accuracy (off-diagonal norm below 3.2e-7 of ||M||_F)
-        bound = np.linalg.norm(mk_gpu - r["m_k"]) + 1e-6 * np.linalg.norm(r["m_k"])
+        # Weyl: eigenvalues move by at most ||dM||_2 <= ||dM||_F; fp32 Jacobi adds a
+        # backward error of order n eps ||M||_F per sweep (at most 10 sweeps here)
+        n = mk_gpu.shape[0]
+        bound = np.linalg.norm(mk_gpu - r["m_k"]) + 10 * n * 6e-8 * np.linalg.norm(r["m_k"])
         assert np.abs(lam - lam_ref).max() <= bound
 
 

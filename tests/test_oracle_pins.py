@@ -391,6 +391,28 @@ def test_fit_recovers_planted_affine_map_in_subspace():
     assert np.allclose(pred, resid[m:], atol=1e-7)
 
 
+def test_relative_ridge_is_scale_free():
+    # scaling the sparse outputs by a leaves the predicted residuals unchanged:
+    # the relative penalty grows with a^2 while W shrinks by 1/a
+    rng = np.random.default_rng(21)
+    m, d = 30, 12
+    x = rng.normal(size=(m + 10, d))
+    r = rng.normal(size=(m, d))
+    w = rng.uniform(0.5, 1.5, size=m)
+    f1 = fit_residual(r, x[:m], w, 4, 0.7, relative=True)
+    f2 = fit_residual(r, 7.0 * x[:m], w, 4, 0.7, relative=True)
+    assert np.allclose(f1["b"] + x[m:] @ f1["B"], f2["b"] + 7.0 * x[m:] @ f2["B"], atol=1e-10)
+    # the absolute penalty is not scale free
+    g1 = fit_residual(r, x[:m], w, 4, 0.7)
+    g2 = fit_residual(r, 7.0 * x[:m], w, 4, 0.7)
+    assert not np.allclose(g1["b"] + x[m:] @ g1["B"], g2["b"] + 7.0 * x[m:] @ g2["B"], atol=1e-6)
+    # the relative penalty equals lam times the mean eigenvalue of Xc^T D Xc
+    xc = x[:m] - (w[:, None] * x[:m]).sum(0) / w.sum()
+    lam_eff = 0.7 * np.linalg.eigvalsh(xc.T @ (w[:, None] * xc)).mean()
+    g3 = fit_residual(r, x[:m], w, 4, lam_eff)
+    assert np.allclose(g3["B"], f1["B"], atol=1e-12) and np.allclose(g3["b"], f1["b"], atol=1e-12)
+
+
 def test_fit_degenerate_cases():
     rng = np.random.default_rng(16)
     x = rng.normal(size=(20, 6))
