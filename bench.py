@@ -1,0 +1,230 @@
+#!/usr/bin/env python3
+"""Benchmark one SparsePR attention call on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c3_dit_32k]
+
+A step is one full call (partitioning, routing, permutation, probes, fit,
+sparse attention with the fused correction, output restoration) over one
+synthetic [1, H, N, d] bf16 input resident in HBM.  Prints ONE JSON line with
+ms/call, executed-pair TFLOP/s, the dense-attention time at the same shape
+(the faster of torch SDPA and the library's own dense kernel), the roofline
+of the dominant kernel (block-sparse attention, timed with HIP events on the
+library's stream) and the CPU oracle timed on a bounded sample.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 / fp16 MFMA
+PEAK_HBM_GBS = 8000.0
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="c3_dit_32k")
+    ap.add_argument("--density", type=float, default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--profile-runs", type=int, default=3)
+    ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic_sparse_attention.json"))
+    return ap.parse_args()
+
+
+def time_fn(fn, reps: int, torch) -> list:
+    """Per-call milliseconds of fn() on the current stream (HIP events)."""
+    out = []
+    for _ in range(reps):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        b.record()
+        b.synchronize()
+        out.append(a.elapsed_time(b))
+    return out
+
+
+def cpu_baseline(x, w, cfg_kw, routed_first_head: int, n: int, d: int, m: int) -> dict:
+    """Time the oracle on head 0 only (a bounded sample of the call)."""
+    try:
+        from threadpoolctl import threadpool_info
+    except Exception:  # pragma: no cover
+        threadpool_info = None
+    from oracle import OracleConfig, sparsepr_head
+
+    cfg = OracleConfig(**cfg_kw)
+    q = x["q"][0, 0].double().numpy()
+    k = x["k"][0, 0].double().numpy()
+    v = x["v"][0, 0].double().numpy()
+    t0 = time.perf_counter()
+    r = sparsepr_head(q, k, v, cfg, bh=0)
+    dt = time.perf_counter() - t0
+    pairs = r["route"]["routed_pairs"] + m * n
+    cores = len(os.sched_getaffinity(0))
+    if threadpool_info is not None:
+        th = [p.get("num_threads", 0) for p in threadpool_info() if p.get("user_api") == "blas"]
+        if th:
+            cores = max(th)
+    return {"value": 4.0 * d * pairs / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"head 0 of {w.heads} of {w.name} (one full per-head call, {dt:.1f} s)",
+            "seconds": round(dt, 3)}
+
+
+def main() -> int:
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build measures one GPU only; run with --gpus 1"}))
+        log("only --gpus 1 is supported: every GPU box here has one GPU")
+        return 2
+    n_threads = len(os.sched_getaffinity(0))
+    for var in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS"):
+        os.environ.setdefault(var, str(n_threads))
+
+    import torch
+    import free_block_sparse_amd as sp
+    from synth import make_workload_inputs, workload
+
+    if not torch.cuda.is_available():
+        log("no GPU visible")
+        return 1
+    w = workload(args.workload)
+    if args.density is not None:
+        w = workload(args.workload, density=args.density)
+    log(f"generating inputs for {w.name}: H={w.heads} N={w.n} d={w.d} {w.dtype}")
+    t0 = time.time()
+    x = make_workload_inputs(w)
+    log(f"inputs ready in {time.time() - t0:.1f}s")
+    q, k, v = (x[t].cuda() for t in ("q", "k", "v"))
+    B, H, N, d = q.shape
+    cfg_kw = dict(density=w.density, probe_rows=w.probe_rows, n_kv_groups=w.n_kv_groups,
+                  n_q_groups=w.n_q_groups, residual_rank=w.residual_rank)
+    cfg = sp.make_config(N, d, **cfg_kw)
+    ws = sp.Workspace()
+    out = torch.empty_like(q)
+
+    def call():
+        sp.sparsepr_attention(q, k, v, cfg, out=out, workspace=ws)
+
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    log(f"warmup done ({args.warmup} calls)")
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(args.steps):
+        call()
+    stop.record()
+    torch.cuda.synchronize()
+    ms_call = start.elapsed_time(stop) / args.steps
+    log(f"timed {args.steps} calls: {ms_call:.3f} ms/call")
+
+    # per-stage times (HIP events on the library's stream) and statistics
+    stage_runs = []
+    stats = None
+    for _ in range(args.profile_runs):
+        _, st_ms, st = sp.sparsepr_attention_profile(q, k, v, cfg, out=out, workspace=ws)
+        stage_runs.append(st_ms)
+        stats = st
+    torch.cuda.synchronize()
+    stage_ms = {s: sum(r[s] for r in stage_runs) / len(stage_runs) for s in stage_runs[0]}
+    heads = sp.stats_to_dicts(stats)
+    routed = sum(h["routed_pairs"] for h in heads)
+    probe_pairs = sum(h["probe_pairs"] for h in heads)
+    rho_exec = (routed + probe_pairs) / (B * H * N * N)
+    kernel_flops = 4.0 * d * routed
+    call_flops = 4.0 * d * (routed + probe_pairs)
+    t_kernel = stage_ms["sparse_attention"]
+    kernel_tflops = kernel_flops / (t_kernel * 1e-3) / 1e12
+    call_tflops = call_flops / (ms_call * 1e-3) / 1e12
+    log(f"stages (ms): " + ", ".join(f"{s}={v:.3f}" for s, v in stage_ms.items()))
+
+    result_extra = {}
+    if not args.no_dense:
+        import torch.nn.functional as F
+        dense_out = torch.empty_like(q)
+        sdpa_ms = time_fn(lambda: F.scaled_dot_product_attention(q, k, v), 3, torch)
+        own_ms = time_fn(lambda: sp.sparsepr_dense_attention(q, k, v, out=dense_out), 3, torch)
+        ref = F.scaled_dot_product_attention(q, k, v).float()
+        err = float((out.float() - ref).norm() / ref.norm())
+        dense_ms = min(min(sdpa_ms), min(own_ms))
+        result_extra.update(dense_ms=round(dense_ms, 4), dense_ms_torch_sdpa=round(min(sdpa_ms), 4),
+                            dense_ms_own_kernel=round(min(own_ms), 4),
+                            speedup_vs_dense=round(dense_ms / ms_call, 4), rel_err_vs_dense=round(err, 5))
+        log(f"dense: sdpa {min(sdpa_ms):.3f} ms, own {min(own_ms):.3f} ms; speedup {dense_ms / ms_call:.3f}; "
+            f"rel err vs dense {err:.4f}")
+        del dense_out, ref
+
+    traffic = None
+    if os.path.exists(args.traffic_json):
+        try:
+            tj = json.load(open(args.traffic_json))
+            if tj.get("workload") == w.name and tj.get("kernel_source_sha") == _kernel_sha():
+                traffic = tj.get("bytes_per_launch")
+        except Exception:
+            traffic = None
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on one head (bounded sample)")
+        cpu = cpu_baseline(x, w, cfg_kw, heads[0]["routed_pairs"], N, d, w.probe_rows)
+        log(f"oracle: {cpu['value']:.4f} TFLOP/s on {cpu['cores']} threads ({cpu['seconds']} s)")
+
+    res = {
+        "metric": "ms/call & executed-pair TFLOP/s (%bf16 MFMA peak) at 25% density; speedup vs dense",
+        "value": round(call_tflops, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_call, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": B, "H": H, "N": N, "d": d, "density": w.density,
+                   "n_kv_groups": w.n_kv_groups, "n_q_groups": w.n_q_groups, "probe_rows": w.probe_rows,
+                   "residual_rank": w.residual_rank, "kmeans_iters": cfg.kmeans_iters, "parallelism": "none"},
+        "roofline": {"bound": "mfma", "achieved": round(kernel_tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(kernel_tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+                     "kernel": "k_sparse_attn_mfma (block-sparse attention, fused correction)",
+                     "kernel_ms": round(t_kernel, 4), "flops_per_launch": kernel_flops},
+        "cpu_baseline": cpu,
+        "call_pct_peak": round(100 * call_tflops / PEAK_BF16_TFLOPS, 2),
+        "rho_exec": round(rho_exec, 5),
+        "rho_route": round(routed / (B * H * N * N), 5),
+        "stage_ms": {s: round(v, 4) for s, v in stage_ms.items()},
+    }
+    res.update(result_extra)
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+def _kernel_sha() -> str:
+    import hashlib
+    h = hashlib.sha1()
+    p = os.path.join(ROOT, "free_block_sparse_amd", "csrc", "k_attn.hip")
+    h.update(open(p, "rb").read())
+    return h.hexdigest()[:12]
+
+
+if __name__ == "__main__":
+    sys.exit(main())

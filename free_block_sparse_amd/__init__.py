@@ -28,7 +28,7 @@ __all__ = [
     "sparsepr_config_default", "sparsepr_workspace_size", "sparsepr_validate", "sparsepr_attention",
     "sparsepr_attention_with_partition", "sparsepr_key_metric", "sparsepr_partition", "sparsepr_route",
     "sparsepr_sparse_attention", "sparsepr_probe_fit", "sparsepr_dense_attention", "make_config",
-    "stats_to_dicts", "SparseprConfig", "SparsePRError",
+    "stats_to_dicts", "SparseprConfig", "SparsePRError", "sparsepr_attention_profile", "Workspace",
 ]
 
 
@@ -155,6 +155,20 @@ def sparsepr_attention(q, k, v, cfg: SparseprConfig, out=None, workspace: Option
     check(lib().sparsepr_attention(ctypes.byref(cfg), ctypes.byref(io), buf.data_ptr(), nbytes,
                                    _stream(stream), _ptr(st)), "sparsepr_attention")
     return (out, st) if with_stats else out
+
+
+def sparsepr_attention_profile(q, k, v, cfg, out=None, workspace: Optional[Workspace] = None, stream=None):
+    """Run one call with per-stage HIP events; returns (out, {stage: ms}, stats tensor)."""
+    from ._lib import STAGES
+    torch = _torch()
+    out = torch.empty_like(q) if out is None else out
+    io = _tensors(q, k, v, out)
+    buf, nbytes = _ws(cfg, q, workspace)
+    st = _stats_buf(q)
+    ms = (ctypes.c_float * len(STAGES))()
+    check(lib().sparsepr_attention_profile(ctypes.byref(cfg), ctypes.byref(io), buf.data_ptr(), nbytes,
+                                           _stream(stream), st.data_ptr(), ms), "sparsepr_attention_profile")
+    return out, dict(zip(STAGES, list(ms))), st
 
 
 def sparsepr_attention_with_partition(q, k, v, cfg, q_labels, kv_labels, out=None, workspace=None,

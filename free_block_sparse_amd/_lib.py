@@ -81,6 +81,9 @@ class SparseprHeadStats(ctypes.Structure):
     ]
 
 
+STAGES = ["sample_metric", "key_eigen", "key_coords", "key_kmeans", "key_centres", "query_kmeans",
+          "query_centres", "route", "gather", "probes", "fit", "sparse_attention", "restore"]
+
 STATUS = {0: "ok", -1: "invalid argument", -2: "unsupported", -3: "workspace too small",
           -4: "HIP error", -5: "internal error"}
 
@@ -106,6 +109,8 @@ _SIGS = {
     "sparsepr_probe_fit": (_I, [ctypes.POINTER(SparseprConfig), ctypes.POINTER(SparseprTensors), _P, _P, _P,
                                 ctypes.c_size_t, _P, _P, _P, _P, _P, _P, _P, _P]),
     "sparsepr_dense_attention": (_I, [ctypes.POINTER(SparseprTensors), ctypes.c_float, _P]),
+    "sparsepr_attention_profile": (_I, [ctypes.POINTER(SparseprConfig), ctypes.POINTER(SparseprTensors), _P,
+                                        ctypes.c_size_t, _P, _P, ctypes.POINTER(ctypes.c_float)]),
     "sparsepr_status_string": (ctypes.c_char_p, [_I]),
     "sparsepr_last_hip_error": (_I, []),
 }

@@ -25,6 +25,23 @@ static thread_local int g_last_hip = 0;
 
 namespace {
 
+// Optional per-stage events (profiling entry point only).
+struct Stager {
+  hipEvent_t ev[SPARSEPR_N_STAGES + 1];
+  int id[SPARSEPR_N_STAGES + 1];
+  int n = 0;
+  hipStream_t s;
+};
+
+inline sparsepr_status mark(Stager* st, int stage) {
+  if (!st) return SPARSEPR_OK;
+  if (st->n > SPARSEPR_N_STAGES) return SPARSEPR_ERR_INTERNAL;
+  HIPCHK(hipEventRecord(st->ev[st->n], st->s));
+  st->id[st->n] = stage;
+  st->n += 1;
+  return SPARSEPR_OK;
+}
+
 sparsepr_status prepare(Plan& p, const sparsepr_config* cfg, const sparsepr_tensors* io, void* ws,
                         size_t ws_bytes) {
   if (!io) return SPARSEPR_ERR_INVALID_ARG;
@@ -145,18 +162,26 @@ sparsepr_status raw_means(Plan& p, const View4& raw, const int* perm, const int*
   return SPARSEPR_OK;
 }
 
-sparsepr_status run_partition(Plan& p, hipStream_t s) {
+sparsepr_status run_partition(Plan& p, hipStream_t s, Stager* st = nullptr) {
   const bool rcp = p.mode == SPARSEPR_PART_RESPONSE_COUPLED;
+  SPCHK(mark(st, -1));
   if (rcp) {
     HIPCHK(launch_sample_metric(p, s));
+    SPCHK(mark(st, SPARSEPR_STAGE_SAMPLE_METRIC));
     HIPCHK(launch_key_eig(p, s));
+    SPCHK(mark(st, SPARSEPR_STAGE_KEY_EIGEN));
     HIPCHK(launch_key_coords(p, s));
+    SPCHK(mark(st, SPARSEPR_STAGE_KEY_COORDS));
   }
   SPCHK(kmeans_side(p, 0, p.GK, p.kv_labels, p.perm_k, p.off_k, s));
+  SPCHK(mark(st, SPARSEPR_STAGE_KEY_KMEANS));
   SPCHK(raw_means(p, p.k, p.perm_k, p.off_k, p.GK, p.cbar, s));
   if (rcp) HIPCHK(launch_query_metric(p, s));
+  SPCHK(mark(st, SPARSEPR_STAGE_KEY_CENTRES));
   SPCHK(kmeans_side(p, 1, p.GQ, p.q_labels, p.perm_q, p.off_q, s));
+  SPCHK(mark(st, SPARSEPR_STAGE_QUERY_KMEANS));
   SPCHK(raw_means(p, p.q, p.perm_q, p.off_q, p.GQ, p.qbar, s));
+  SPCHK(mark(st, SPARSEPR_STAGE_QUERY_CENTRES));
   return SPARSEPR_OK;
 }
 
@@ -180,14 +205,20 @@ sparsepr_status run_given_partition(Plan& p, const int* q_labels, const int* kv_
   return SPARSEPR_OK;
 }
 
-sparsepr_status run_after_partition(Plan& p, hipStream_t s, sparsepr_head_stats* stats) {
+sparsepr_status run_after_partition(Plan& p, hipStream_t s, sparsepr_head_stats* stats, Stager* st = nullptr) {
   HIPCHK(launch_route(p, s));
+  SPCHK(mark(st, SPARSEPR_STAGE_ROUTE));
   HIPCHK(launch_gather(p, s));
+  SPCHK(mark(st, SPARSEPR_STAGE_GATHER));
   HIPCHK(launch_probe_select(p, s));
   HIPCHK(launch_probe_attention(p, s));
+  SPCHK(mark(st, SPARSEPR_STAGE_PROBES));
   HIPCHK(launch_fit(p, s));
+  SPCHK(mark(st, SPARSEPR_STAGE_FIT));
   HIPCHK(launch_sparse_attention(p, true, s));
+  SPCHK(mark(st, SPARSEPR_STAGE_SPARSE_ATTENTION));
   HIPCHK(launch_probe_overwrite(p, s));
+  SPCHK(mark(st, SPARSEPR_STAGE_RESTORE));
   if (stats) HIPCHK(hipMemcpyAsync(stats, p.stats, sizeof(sparsepr_head_stats) * p.BH, hipMemcpyDeviceToDevice, s));
   return SPARSEPR_OK;
 }
@@ -249,6 +280,44 @@ sparsepr_status sparsepr_attention(const sparsepr_config* cfg, const sparsepr_te
   hipStream_t s = static_cast<hipStream_t>(stream);
   SPCHK(run_partition(p, s));
   return run_after_partition(p, s, stats);
+}
+
+sparsepr_status sparsepr_attention_profile(const sparsepr_config* cfg, const sparsepr_tensors* io,
+                                           void* workspace, size_t workspace_bytes, void* stream,
+                                           sparsepr_head_stats* stats, float* stage_ms) {
+  if (!stage_ms) return SPARSEPR_ERR_INVALID_ARG;
+  Plan p;
+  SPCHK(prepare(p, cfg, io, workspace, workspace_bytes));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  Stager st;
+  st.s = s;
+  int made = 0;
+  sparsepr_status rc = SPARSEPR_OK;
+  for (; made <= SPARSEPR_N_STAGES; ++made) {
+    hipError_t e = hipEventCreate(&st.ev[made]);
+    if (e != hipSuccess) {
+      g_last_hip = (int)e;
+      rc = SPARSEPR_ERR_HIP;
+      break;
+    }
+  }
+  if (rc == SPARSEPR_OK) rc = run_partition(p, s, &st);
+  if (rc == SPARSEPR_OK) rc = run_after_partition(p, s, stats, &st);
+  if (rc == SPARSEPR_OK) {
+    for (int i = 0; i < SPARSEPR_N_STAGES; ++i) stage_ms[i] = 0.f;
+    hipError_t e = hipEventSynchronize(st.ev[st.n - 1]);
+    for (int i = 1; i < st.n && e == hipSuccess; ++i) {
+      float ms = 0.f;
+      e = hipEventElapsedTime(&ms, st.ev[i - 1], st.ev[i]);
+      if (st.id[i] >= 0) stage_ms[st.id[i]] += ms;
+    }
+    if (e != hipSuccess) {
+      g_last_hip = (int)e;
+      rc = SPARSEPR_ERR_HIP;
+    }
+  }
+  for (int i = 0; i < made; ++i) (void)hipEventDestroy(st.ev[i]);
+  return rc;
 }
 
 sparsepr_status sparsepr_attention_with_partition(const sparsepr_config* cfg, const sparsepr_tensors* io,

@@ -150,6 +150,32 @@ sparsepr_status sparsepr_attention(const sparsepr_config* cfg, const sparsepr_te
                                    void* workspace, size_t workspace_bytes, void* stream,
                                    sparsepr_head_stats* stats);
 
+/* Stages timed by sparsepr_attention_profile(). */
+enum {
+  SPARSEPR_STAGE_SAMPLE_METRIC = 0,   /* a1 query sample and M_K */
+  SPARSEPR_STAGE_KEY_EIGEN = 1,       /* a2 eigenvectors of M_K */
+  SPARSEPR_STAGE_KEY_COORDS = 2,      /* a3 key-response coordinates */
+  SPARSEPR_STAGE_KEY_KMEANS = 3,      /* a4-a5 key k-means and K/V grouping */
+  SPARSEPR_STAGE_KEY_CENTRES = 4,     /* a6 K/V-group centres and the query metric */
+  SPARSEPR_STAGE_QUERY_KMEANS = 5,    /* a7-a8 query k-means and grouping */
+  SPARSEPR_STAGE_QUERY_CENTRES = 6,   /* query-group centres */
+  SPARSEPR_STAGE_ROUTE = 7,           /* a10 router */
+  SPARSEPR_STAGE_GATHER = 8,          /* a9 permuted Q, K, V */
+  SPARSEPR_STAGE_PROBES = 9,          /* a11, a13 probe selection and exact probe rows */
+  SPARSEPR_STAGE_FIT = 10,            /* a14 residual fit */
+  SPARSEPR_STAGE_SPARSE_ATTENTION = 11, /* a12 + a15 sparse attention with fused correction */
+  SPARSEPR_STAGE_RESTORE = 12,        /* probe rows written back */
+  SPARSEPR_N_STAGES = 13
+};
+
+/* Measurement entry point: the same work as sparsepr_attention, with a HIP
+   event recorded between stages on `stream`; it then waits for the stream
+   and writes each stage's elapsed milliseconds to the HOST array stage_ms
+   [SPARSEPR_N_STAGES] (stages that did not run read 0). */
+sparsepr_status sparsepr_attention_profile(const sparsepr_config* cfg, const sparsepr_tensors* io,
+                                           void* workspace, size_t workspace_bytes, void* stream,
+                                           sparsepr_head_stats* stats, float* stage_ms);
+
 /* The full call with the partition given instead of computed: q_labels and
    kv_labels are device int32 arrays [B*H, N] with values in [0, G_Q) and
    [0, G_K).  Used to check the stages after partitioning in isolation. */
