@@ -138,13 +138,31 @@ __device__ inline bool setup_item(const AttnArgs& a, int bh, int tile, int* seg_
 // LDS; the contraction order over keys inside a 16-key step follows the S^T
 // register layout (keys 16s + 4h + {0..3} and 16s + 8 + 4h + {0..3}).
 // ============================================================================
+// Pack the j-th 16-bit element of KPT 16-byte chunks (one per key) into KPT
+// consecutive key slots of one dim row of the transposed V tile.
+template <int KPT>
+__device__ inline void store_vt_row(bf16_t* dst, const uint4* vr, int j) {
+  uint32_t h[KPT];
+#pragma unroll
+  for (int i = 0; i < KPT; ++i) {
+    const uint32_t w = (j >> 1) == 0 ? vr[i].x : (j >> 1) == 1 ? vr[i].y : (j >> 1) == 2 ? vr[i].z : vr[i].w;
+    h[i] = (j & 1) ? (w >> 16) : (w & 0xffffu);
+  }
+  if constexpr (KPT == 4) {
+    *reinterpret_cast<uint2*>(dst) = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+  } else {
+    *reinterpret_cast<uint32_t*>(dst) = h[0] | (h[1] << 16);
+  }
+}
+
 template <int D, bool VF16>
 __global__ __launch_bounds__(256, 2) void k_sparse_attn_mfma(AttnArgs a) {
   constexpr int KS = D / 16, DB = D / 32;
-  constexpr int LDK = D + 8, LDV = 64 + 8;
-  constexpr int CPR = D / 8;
-  __shared__ __attribute__((aligned(16))) bf16_t Ks[64 * LDK];
-  __shared__ __attribute__((aligned(16))) bf16_t Vt[D * LDV];
+  constexpr int LDK = D + 8, LDV = 64 + 4;
+  constexpr int CPR = D / 8;              // 16-byte chunks per key row
+  constexpr int KPT = (64 * CPR) / 256;   // consecutive keys loaded per thread per tile
+  __shared__ __attribute__((aligned(16))) bf16_t Ks[2][64 * LDK];
+  __shared__ __attribute__((aligned(16))) bf16_t Vt[2][D * LDV];
   __shared__ int seg_v[kMaxGroups + 1], seg_p[kMaxGroups + 1];
   __shared__ int tmp[8];
   const int bh = blockIdx.y, tile = blockIdx.x, tid = threadIdx.x;
@@ -171,25 +189,43 @@ __global__ __launch_bounds__(256, 2) void k_sparse_attn_mfma(AttnArgs a) {
   float m = -INFINITY, l = 0.f;
   const float c = a.scale * 1.4426950408889634f;
 
-  for (int kt0 = 0; kt0 < L; kt0 += 64) {
+  // loader geometry: this thread moves keys KPT*kr .. KPT*kr + KPT-1 of every
+  // tile, 16-byte chunk c8 of each
+  const int c8 = tid % CPR, kr = tid / CPR;
+  int cur = 0;  // segment cursor of this thread's first key (monotone in the tile index)
+  uint4 kreg[KPT], vreg[KPT];
+  auto load_tile = [&](int kt0) {
+    const int v0 = kt0 + KPT * kr;
+    while (cur + 1 < nseg && seg_v[cur + 1] <= v0) ++cur;
+    int s = cur;
 #pragma unroll
-    for (int i = 0; i < (64 * CPR) / 256; ++i) {
-      const int e = tid + 256 * i;
-      const int r = e / CPR, c8 = e - (e / CPR) * CPR;
-      const int v = kt0 + r;
-      uint4 kv4 = make_uint4(0, 0, 0, 0), vv4 = make_uint4(0, 0, 0, 0);
+    for (int i = 0; i < KPT; ++i) {
+      const int v = v0 + i;
+      kreg[i] = make_uint4(0, 0, 0, 0);
+      vreg[i] = make_uint4(0, 0, 0, 0);
       if (v < L) {
-        const int s = seg_find(seg_v, nseg, v);
+        while (s + 1 < nseg && seg_v[s + 1] <= v) ++s;
         const int prow = seg_p[s] + v - seg_v[s];
-        kv4 = *reinterpret_cast<const uint4*>(kb + a.kv.row_off(bh, prow) + 8 * c8);
-        vv4 = *reinterpret_cast<const uint4*>(vb + a.vv.row_off(bh, prow) + 8 * c8);
+        kreg[i] = *reinterpret_cast<const uint4*>(kb + a.kv.row_off(bh, prow) + 8 * c8);
+        vreg[i] = *reinterpret_cast<const uint4*>(vb + a.vv.row_off(bh, prow) + 8 * c8);
       }
-      *reinterpret_cast<uint4*>(Ks + r * LDK + 8 * c8) = kv4;
-      const bf16_t* ve = reinterpret_cast<const bf16_t*>(&vv4);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) Vt[(8 * c8 + j) * LDV + r] = ve[j];
     }
-    __syncthreads();
+  };
+  auto store_tile = [&](int st) {
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) *reinterpret_cast<uint4*>(&Ks[st][(KPT * kr + i) * LDK + 8 * c8]) = kreg[i];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) store_vt_row<KPT>(&Vt[st][(8 * c8 + j) * LDV + KPT * kr], vreg, j);
+  };
+
+  const int ntile = (L + 63) / 64;
+  load_tile(0);
+  store_tile(0);
+  __syncthreads();
+  for (int t = 0; t < ntile; ++t) {
+    const int st = t & 1;
+    const int kt0 = 64 * t;
+    if (t + 1 < ntile) load_tile(kt0 + 64);
     if (wave_active) {
       f32x16 sacc[2];
 #pragma unroll
@@ -197,21 +233,31 @@ __global__ __launch_bounds__(256, 2) void k_sparse_attn_mfma(AttnArgs a) {
         sacc[kt] = f32x16{};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-          const bf16x8 kf = *reinterpret_cast<const bf16x8*>(Ks + (32 * kt + col) * LDK + 16 * ks + 8 * half);
+          const bf16x8 kf = *reinterpret_cast<const bf16x8*>(&Ks[st][(32 * kt + col) * LDK + 16 * ks + 8 * half]);
           sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], sacc[kt], 0, 0, 0);
         }
       }
       float mloc = -INFINITY;
+      if (kt0 + 64 > L) {
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
+        for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = 32 * kt + (r & 3) + 8 * (r >> 2) + 4 * half;
-          float sv = sacc[kt][r] * c;
-          if (kt0 + key >= L) sv = -INFINITY;
-          sacc[kt][r] = sv;
-          mloc = fmaxf(mloc, sv);
-        }
+          for (int r = 0; r < 16; ++r) {
+            const int key = 32 * kt + (r & 3) + 8 * (r >> 2) + 4 * half;
+            const float sv = kt0 + key < L ? sacc[kt][r] * c : -INFINITY;
+            sacc[kt][r] = sv;
+            mloc = fmaxf(mloc, sv);
+          }
+      } else {
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float sv = sacc[kt][r] * c;
+            sacc[kt][r] = sv;
+            mloc = fmaxf(mloc, sv);
+          }
+      }
       mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
       const float mnew = fmaxf(m, mloc);
       const float mb = mnew == -INFINITY ? 0.f : mnew;
@@ -230,15 +276,15 @@ __global__ __launch_bounds__(256, 2) void k_sparse_attn_mfma(AttnArgs a) {
 #pragma unroll
       for (int b = 0; b < DB; ++b) o[b] *= alpha;
 #pragma unroll
-      for (int st = 0; st < 4; ++st) {
-        const int kt = st >> 1, rb = 8 * (st & 1);
+      for (int sp = 0; sp < 4; ++sp) {
+        const int kt = sp >> 1, rb = 8 * (sp & 1);
         if constexpr (VF16) {
           f16x8 pf;
 #pragma unroll
           for (int j = 0; j < 8; ++j) pf[j] = (_Float16)sacc[kt][rb + j];
 #pragma unroll
           for (int b = 0; b < DB; ++b) {
-            const bf16_t* vrow = Vt + (32 * b + col) * LDV + 16 * st + 4 * half;
+            const bf16_t* vrow = &Vt[st][(32 * b + col) * LDV + 16 * sp + 4 * half];
             const uint2 lo = *reinterpret_cast<const uint2*>(vrow);
             const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 8);
             const f16x8 vf = __builtin_bit_cast(f16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
@@ -253,7 +299,7 @@ __global__ __launch_bounds__(256, 2) void k_sparse_attn_mfma(AttnArgs a) {
           const bf16x8 pf = __builtin_bit_cast(bf16x8, pk);
 #pragma unroll
           for (int b = 0; b < DB; ++b) {
-            const bf16_t* vrow = Vt + (32 * b + col) * LDV + 16 * st + 4 * half;
+            const bf16_t* vrow = &Vt[st][(32 * b + col) * LDV + 16 * sp + 4 * half];
             const uint2 lo = *reinterpret_cast<const uint2*>(vrow);
             const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 8);
             const bf16x8 vf = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
@@ -262,6 +308,7 @@ __global__ __launch_bounds__(256, 2) void k_sparse_attn_mfma(AttnArgs a) {
         }
       }
     }
+    if (t + 1 < ntile) store_tile(st ^ 1);
     __syncthreads();
   }
 
@@ -276,8 +323,8 @@ __global__ __launch_bounds__(256, 2) void k_sparse_attn_mfma(AttnArgs a) {
     for (int r = 0; r < 16; ++r) x[b][r] = o[b][r] * inv;
   const int rank = (a.correct && a.fitrank) ? a.fitrank[bh] : 0;
   if (rank > 0) {
-    float* Wl = reinterpret_cast<float*>(Ks);  // D x 33 floats fit in the K tile region
-    float* Vl = reinterpret_cast<float*>(Vt);
+    float* Wl = reinterpret_cast<float*>(&Ks[0][0]);  // D x 33 floats fit in the K tile buffers
+    float* Vl = reinterpret_cast<float*>(&Vt[0][0]);
     float corr[DB][16];
     const float* fb = a.fitb + (long long)bh * D;
 #pragma unroll
@@ -573,31 +620,25 @@ __global__ __launch_bounds__(256) void k_probe_attn_vec(ProbeArgs a) {
 }
 
 template <int D>
-__global__ __launch_bounds__(256) void k_probe_merge(ProbeArgs a) {
-  const int bh = blockIdx.x;
-  for (int e = threadIdx.x; e < 2 * a.M * D; e += 256) {
-    const int which = e / (a.M * D);
-    const int rem = e - which * a.M * D;
-    const int p = rem / D, dm = rem - (rem / D) * D;
-    float mx = -INFINITY;
+__global__ __launch_bounds__(D) void k_probe_merge(ProbeArgs a) {
+  const int bh = blockIdx.z, which = blockIdx.y, p = blockIdx.x, dm = threadIdx.x;
+  const long long stride_ch = 2LL * a.M * (D + 2);
+  const float* pr0 = a.ppart + (((long long)bh * a.n_pchunk) * 2 + which) * a.M * (D + 2) + (long long)p * (D + 2);
+  float mx = -INFINITY;
+  for (int ch = 0; ch < a.n_pchunk; ++ch) mx = fmaxf(mx, pr0[ch * stride_ch + D]);
+  float num = 0.f, den = 0.f;
+  if (mx > -INFINITY) {
     for (int ch = 0; ch < a.n_pchunk; ++ch) {
-      const float* pr = a.ppart + ((((long long)bh * a.n_pchunk + ch) * 2 + which) * a.M + p) * (D + 2);
-      mx = fmaxf(mx, pr[D]);
+      const float* pr = pr0 + ch * stride_ch;
+      const float mc = pr[D];
+      if (mc == -INFINITY) continue;
+      const float f = exp2f(mc - mx);
+      num += f * pr[dm];
+      den += f * pr[D + 1];
     }
-    float num = 0.f, den = 0.f;
-    if (mx > -INFINITY) {
-      for (int ch = 0; ch < a.n_pchunk; ++ch) {
-        const float* pr = a.ppart + ((((long long)bh * a.n_pchunk + ch) * 2 + which) * a.M + p) * (D + 2);
-        if (pr[D] == -INFINITY) continue;
-        const float f = exp2f(pr[D] - mx);
-        num += f * pr[dm];
-        den += f * pr[D + 1];
-      }
-    }
-    const float val = den > 0.f ? num / den : 0.f;
-    float* out = which == 0 ? a.ode : a.osp;
-    out[((long long)bh * a.M + p) * D + dm] = val;
   }
+  float* out = which == 0 ? a.ode : a.osp;
+  out[((long long)bh * a.M + p) * D + dm] = den > 0.f ? num / den : 0.f;
 }
 
 // probe rows keep their exact dense output
@@ -714,8 +755,8 @@ hipError_t launch_probe_attention(const Plan& p, hipStream_t s) {
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (p.d == 128) hipLaunchKernelGGL(k_probe_merge<128>, dim3(p.BH), dim3(256), 0, s, a);
-  else hipLaunchKernelGGL(k_probe_merge<64>, dim3(p.BH), dim3(256), 0, s, a);
+  if (p.d == 128) hipLaunchKernelGGL(k_probe_merge<128>, dim3(p.M, 2, p.BH), dim3(128), 0, s, a);
+  else hipLaunchKernelGGL(k_probe_merge<64>, dim3(p.M, 2, p.BH), dim3(64), 0, s, a);
   return hipGetLastError();
 }
 

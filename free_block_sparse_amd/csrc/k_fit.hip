@@ -149,6 +149,13 @@ __device__ bool cholesky_f64(double* K, int n, int* bad) {
 }
 
 __global__ __launch_bounds__(256) void k_fit(FitArgs a) {
+  // LDS path for M <= 64 (R and Xc staged as fp32, Gram and eigenvectors fp64);
+  // larger probe budgets use the per-(b,h) global scratch slice instead.
+  constexpr int SM = 64;
+  __shared__ float Rl[SM * 128];
+  __shared__ float Xl[SM * 128];
+  __shared__ double Gl[SM * SM];
+  __shared__ double Ul[SM * SM];
   __shared__ double rcs[2 * 64];
   __shared__ int rpq[2 * 64];
   __shared__ double red[8];
@@ -156,33 +163,53 @@ __global__ __launch_bounds__(256) void k_fit(FitArgs a) {
   __shared__ double sig_s[kMaxProbe + 1];
   __shared__ int idx_s[kMaxProbe + 1];
   __shared__ int rk_s;
-  __shared__ double wsum_s;
+  __shared__ double wsum_s, lam_s;
+  __shared__ double xb[128];
+  __shared__ double yb[64];
+  __shared__ double bp[64];
   const int bh = blockIdx.x, tid = threadIdx.x, nt = blockDim.x;
   const int M = a.M, d = a.d, Rmax = a.R;  // Rmax: column stride of the W and V outputs
   double* S = a.scratch + (long long)bh * kFitScratch;
-  double* Rm = S;                    // M x d
-  double* G = S + 256 * 128;         // ne x ne
-  double* U = G + 128 * 128;         // ne x ne
-  double* Vr = U + 128 * 128;        // d x R (fp64)
-  double* K = Vr + 128 * 64;         // ridge system, up to 128 x 128
-  double* Z = K + 128 * 128;         // M x R right-hand sides / solutions (up to 256 x 64)
+  const bool small = M <= d;
+  const int n = small ? M : d;
+  const int ne = n + (n & 1);
+  const bool lds = M <= SM;
+  float* Rf = lds ? Rl : reinterpret_cast<float*>(S);                        // M x d
+  float* Xf = lds ? Xl : reinterpret_cast<float*>(S) + 256 * 128;            // M x d (centred below)
+  double* G = ne <= SM ? Gl : S + 256 * 128;                                 // ne x ne, later the ridge system
+  double* U = ne <= SM ? Ul : S + 256 * 128 + 128 * 128;                     // ne x ne
+  double* Vr = S + 256 * 128 + 2 * 128 * 128;                                // d x Rmax
+  double* Wm = Vr + 128 * 64;                                                // d x rk (also the primal rhs)
+  double* Yc = Wm + 128 * 64;                                                // M x rk
+  double* Kp = Yc + 256 * 64;                                                // primal system d x d (M > d)
   const float* ode = a.ode + (long long)bh * M * d;
   const float* osp = a.osp + (long long)bh * M * d;
   const double* w = a.pw + (long long)bh * M;
 
-  for (int e = tid; e < M * d; e += nt) Rm[e] = (double)ode[e] - (double)osp[e];
-  const bool small = M <= d;
-  const int n = small ? M : d;
-  const int ne = n + (n & 1);
+  for (int e = tid; e < M * d; e += nt) {
+    Rf[e] = ode[e] - osp[e];
+    Xf[e] = osp[e];
+  }
+  if (tid == 0) {
+    double ws = 0.0;
+    for (int i = 0; i < M; ++i) ws += w[i];
+    wsum_s = ws;
+  }
   block_sync();
+  const double ws = wsum_s;
+  for (int dm = tid; dm < d; dm += nt) {
+    double acc = 0.0;
+    for (int mm = 0; mm < M; ++mm) acc += w[mm] * (double)Xf[mm * d + dm];
+    xb[dm] = acc / ws;
+  }
   for (int e = tid; e < ne * ne; e += nt) {
     const int i = e / ne, j = e - (e / ne) * ne;
     double acc = 0.0;
     if (i < n && j < n) {
       if (small)
-        for (int k = 0; k < d; ++k) acc += Rm[i * d + k] * Rm[j * d + k];
+        for (int k = 0; k < d; ++k) acc += (double)Rf[i * d + k] * (double)Rf[j * d + k];
       else
-        for (int mm = 0; mm < M; ++mm) acc += Rm[mm * d + i] * Rm[mm * d + j];
+        for (int mm = 0; mm < M; ++mm) acc += (double)Rf[mm * d + i] * (double)Rf[mm * d + j];
     }
     G[e] = acc;
   }
@@ -210,9 +237,6 @@ __global__ __launch_bounds__(256) void k_fit(FitArgs a) {
     if (d < rk) rk = d;
     if (cnt < rk) rk = cnt;
     rk_s = rk;
-    double ws = 0.0;
-    for (int i = 0; i < M; ++i) ws += w[i];
-    wsum_s = ws;
     for (int i = 0; i < kMaxProbe && i < n; ++i) a.sig[(long long)bh * kMaxProbe + i] = sig_s[i];
   }
   block_sync();
@@ -224,7 +248,7 @@ __global__ __launch_bounds__(256) void k_fit(FitArgs a) {
     double v;
     if (small) {
       double acc = 0.0;
-      for (int mm = 0; mm < M; ++mm) acc += Rm[mm * d + dm] * U[mm * ne + ci];
+      for (int mm = 0; mm < M; ++mm) acc += (double)Rf[mm * d + dm] * U[mm * ne + ci];
       v = acc / sig_s[k];
     } else {
       v = U[dm * ne + ci];
@@ -232,32 +256,23 @@ __global__ __launch_bounds__(256) void k_fit(FitArgs a) {
     Vr[dm * Rmax + k] = v;
   }
   block_sync();
-  // Y = R Vr (M x rk) into Z region first rows; weighted means
-  double* Yc = Z;                      // M x rk
-  __shared__ double xb[128];
-  __shared__ double yb[64];
+  // Y = R Vr (M x rk), weighted means, centring
   for (int e = tid; e < M * rk; e += nt) {
     const int mm = e / rk, k = e - (e / rk) * rk;
     double acc = 0.0;
-    for (int dm = 0; dm < d; ++dm) acc += Rm[mm * d + dm] * Vr[dm * Rmax + k];
+    for (int dm = 0; dm < d; ++dm) acc += (double)Rf[mm * d + dm] * Vr[dm * Rmax + k];
     Yc[mm * rk + k] = acc;
   }
   block_sync();
-  const double ws = wsum_s;
-  for (int dm = tid; dm < d; dm += nt) {
-    double acc = 0.0;
-    for (int mm = 0; mm < M; ++mm) acc += w[mm] * (double)osp[mm * d + dm];
-    xb[dm] = acc / ws;
-  }
   for (int k = tid; k < rk; k += nt) {
     double acc = 0.0;
     for (int mm = 0; mm < M; ++mm) acc += w[mm] * Yc[mm * rk + k];
     yb[k] = acc / ws;
   }
+  for (int e = tid; e < M * d; e += nt) Xf[e] = (float)((double)Xf[e] - xb[e % d]);
   block_sync();
-  // centre Y; ridge strength (relative: lambda times the mean eigenvalue of Xc^T D Xc)
   for (int e = tid; e < M * rk; e += nt) Yc[e] -= yb[e % rk];
-  __shared__ double lam_s;
+  // ridge strength (relative: lambda times the mean eigenvalue of Xc^T D Xc)
   if (tid == 0) {
     double lam = a.lambda;
     if (a.relative) {
@@ -265,7 +280,7 @@ __global__ __launch_bounds__(256) void k_fit(FitArgs a) {
       for (int mm = 0; mm < M; ++mm) {
         double s2 = 0.0;
         for (int dm = 0; dm < d; ++dm) {
-          const double t = (double)osp[mm * d + dm] - xb[dm];
+          const double t = (double)Xf[mm * d + dm];
           s2 += t * t;
         }
         tr += w[mm] * s2;
@@ -279,68 +294,66 @@ __global__ __launch_bounds__(256) void k_fit(FitArgs a) {
   bool ok = rk > 0;
   if (rk > 0) {
     if (small) {
-      // dual: K = D^1/2 Xc Xc^T D^1/2 + lambda I  (M x M), rhs = D^1/2 Yc
+      // dual: K = D^1/2 Xc Xc^T D^1/2 + lambda I  (M x M) in the Gram buffer, rhs = D^1/2 Yc
+      double* K = G;
       for (int e = tid; e < M * M; e += nt) {
         const int i = e / M, j = e - (e / M) * M;
         double acc = 0.0;
-        for (int dm = 0; dm < d; ++dm)
-          acc += ((double)osp[i * d + dm] - xb[dm]) * ((double)osp[j * d + dm] - xb[dm]);
+        for (int dm = 0; dm < d; ++dm) acc += (double)Xf[i * d + dm] * (double)Xf[j * d + dm];
         K[e] = sqrt(w[i] * w[j]) * acc + (i == j ? lam : 0.0);
       }
       for (int e = tid; e < M * rk; e += nt) Yc[e] *= sqrt(w[e / rk]);
       block_sync();
       ok = cholesky_f64(K, M, &bad);
       if (ok) {
-        // solve L L^T z = rhs for every column (one thread per column)
         for (int k = tid; k < rk; k += nt) {
           for (int i = 0; i < M; ++i) {
-            double s = Yc[i * rk + k];
-            for (int j = 0; j < i; ++j) s -= K[i * M + j] * Yc[j * rk + k];
-            Yc[i * rk + k] = s / K[i * M + i];
+            double sacc = Yc[i * rk + k];
+            for (int j = 0; j < i; ++j) sacc -= K[i * M + j] * Yc[j * rk + k];
+            Yc[i * rk + k] = sacc / K[i * M + i];
           }
           for (int i = M - 1; i >= 0; --i) {
-            double s = Yc[i * rk + k];
-            for (int j = i + 1; j < M; ++j) s -= K[j * M + i] * Yc[j * rk + k];
-            Yc[i * rk + k] = s / K[i * M + i];
+            double sacc = Yc[i * rk + k];
+            for (int j = i + 1; j < M; ++j) sacc -= K[j * M + i] * Yc[j * rk + k];
+            Yc[i * rk + k] = sacc / K[i * M + i];
           }
         }
         block_sync();
-        // W = Xc^T D^1/2 Z  (d x rk) -> stored in G region
         for (int e = tid; e < d * rk; e += nt) {
           const int dm = e / rk, k = e - (e / rk) * rk;
           double acc = 0.0;
-          for (int mm = 0; mm < M; ++mm) acc += ((double)osp[mm * d + dm] - xb[dm]) * sqrt(w[mm]) * Yc[mm * rk + k];
-          G[dm * rk + k] = acc;
+          for (int mm = 0; mm < M; ++mm) acc += (double)Xf[mm * d + dm] * sqrt(w[mm]) * Yc[mm * rk + k];
+          Wm[dm * rk + k] = acc;
         }
       }
     } else {
-      // primal: K = Xc^T D Xc + lambda I (d x d), rhs = Xc^T D Yc (d x rk) in G region
+      // primal: K = Xc^T D Xc + lambda I (d x d), rhs = Xc^T D Yc (d x rk)
+      double* K = Kp;
       for (int e = tid; e < d * d; e += nt) {
         const int i = e / d, j = e - (e / d) * d;
         double acc = 0.0;
-        for (int mm = 0; mm < M; ++mm)
-          acc += w[mm] * ((double)osp[mm * d + i] - xb[i]) * ((double)osp[mm * d + j] - xb[j]);
+        for (int mm = 0; mm < M; ++mm) acc += w[mm] * (double)Xf[mm * d + i] * (double)Xf[mm * d + j];
         K[e] = acc + (i == j ? lam : 0.0);
       }
       for (int e = tid; e < d * rk; e += nt) {
         const int i = e / rk, k = e - (e / rk) * rk;
         double acc = 0.0;
-        for (int mm = 0; mm < M; ++mm) acc += w[mm] * ((double)osp[mm * d + i] - xb[i]) * Yc[mm * rk + k];
-        G[e] = acc;
+        for (int mm = 0; mm < M; ++mm) acc += w[mm] * (double)Xf[mm * d + i] * Yc[mm * rk + k];
+        Wm[e] = acc;
       }
       block_sync();
       ok = cholesky_f64(K, d, &bad);
       if (ok) {
         for (int k = tid; k < rk; k += nt) {
           for (int i = 0; i < d; ++i) {
-            double s = G[i * rk + k];
-            for (int j = 0; j < i; ++j) s -= K[i * d + j] * G[j * rk + k];
-            G[i * rk + k] = s / K[i * d + i];
+            double sacc = Wm[i * rk + k];
+            for (int j = 0; j < i; ++j) sacc -= K[i * d + j] * Wm[j * rk + k];
+            Wm[i * rk + k] = sacc / K[i * d + i];
           }
           for (int i = d - 1; i >= 0; --i) {
-            double s = G[i * rk + k];
-            for (int j = i + 1; j < d; ++j) s -= K[j * d + i] * G[j * rk + k];
-            G[i * rk + k] = s / K[i * d + i];
+            double sacc = Wm[i * rk + k];
+            for (int j = i + 1; j < d; ++j) sacc -= K[j * d + i] * Wm[j * rk + k];
+            Wm[i * rk + k] = sacc / K[i * d + i];
           }
         }
       }
@@ -349,10 +362,9 @@ __global__ __launch_bounds__(256) void k_fit(FitArgs a) {
   }
   if (!ok) rk = 0;
   // outputs: W (d x R) and V (d x R) zero beyond rk, b = (ybar - xbar W) V^T
-  __shared__ double bp[64];
   for (int k = tid; k < rk; k += nt) {
     double acc = yb[k];
-    for (int dm = 0; dm < d; ++dm) acc -= xb[dm] * G[dm * rk + k];
+    for (int dm = 0; dm < d; ++dm) acc -= xb[dm] * Wm[dm * rk + k];
     bp[k] = acc;
   }
   block_sync();
@@ -360,7 +372,7 @@ __global__ __launch_bounds__(256) void k_fit(FitArgs a) {
   float* Vo = a.V + (long long)bh * d * Rmax;
   for (int e = tid; e < d * Rmax; e += nt) {
     const int dm = e / Rmax, k = e - (e / Rmax) * Rmax;
-    Wo[e] = k < rk ? (float)G[dm * rk + k] : 0.f;
+    Wo[e] = k < rk ? (float)Wm[dm * rk + k] : 0.f;
     Vo[e] = k < rk ? (float)Vr[dm * Rmax + k] : 0.f;
   }
   for (int dm = tid; dm < d; dm += nt) {

@@ -161,17 +161,21 @@ __global__ __launch_bounds__(1024) void k_key_eig(EigArgs a) {
   __shared__ int rp[HP], rq[HP];
   __shared__ float red[2][32];
   __shared__ int stop;
-  const int bh = blockIdx.x, tid = threadIdx.x, nt = blockDim.x;
+  const int bh = blockIdx.x, tid = threadIdx.x;
+  constexpr int NT = 1024;
   const float* mk = a.mk + (long long)bh * D * D;
-  for (int e = tid; e < D * D; e += nt) {
+  for (int e = tid; e < D * D; e += NT) {
     const int i = e / D, j = e - (e / D) * D;
     A[i * LD + j] = mk[e];
     V[i * LD + j] = i == j ? 1.f : 0.f;
   }
   __syncthreads();
-  for (int sweep = 0; sweep < 40; ++sweep) {
+  // thread -> (column pair ib, first row pair / row) for the block updates
+  const int ib = tid % HP, i0 = tid / HP;
+  constexpr int RSTEP = NT / HP;  // 16 (D=128) or 32 (D=64)
+  for (int sweep = 0; sweep < 16; ++sweep) {
     float off = 0.f, tot = 0.f;
-    for (int e = tid; e < D * D; e += nt) {
+    for (int e = tid; e < D * D; e += NT) {
       const int i = e / D, j = e - (e / D) * D;
       const float x = A[i * LD + j];
       tot += x * x;
@@ -186,11 +190,13 @@ __global__ __launch_bounds__(1024) void k_key_eig(EigArgs a) {
     __syncthreads();
     if (tid == 0) {
       float o = 0.f, t = 0.f;
-      for (int w = 0; w < nt / 64; ++w) {
+      for (int w = 0; w < NT / 64; ++w) {
         o += red[0][w];
         t += red[1][w];
       }
-      stop = !(o > 1e-13f * t);
+      // relative off-diagonal norm below ~3e-6: far below what the k-means
+      // coordinates resolve, and reachable in fp32
+      stop = !(o > 1e-11f * t);
     }
     __syncthreads();
     if (stop) break;
@@ -214,13 +220,14 @@ __global__ __launch_bounds__(1024) void k_key_eig(EigArgs a) {
         rq[tid] = q;
       }
       __syncthreads();
-      for (int blk = tid; blk < HP * HP; blk += nt) {
-        const int ia = blk / HP, ib = blk - (blk / HP) * HP;
-        const int pa = rp[ia], qa = rq[ia], pb = rp[ib], qb = rq[ib];
-        const float ca = rc[ia], sa = rs[ia], cb = rc[ib], sb = rs[ib];
+      const int pb = rp[ib], qb = rq[ib];
+      const float cb = rc[ib], sb = rs[ib];
+      // A <- Ja^T A Jb on the 2x2 blocks (row pair ia, column pair ib)
+      for (int ia = i0; ia < HP; ia += RSTEP) {
+        const int pa = rp[ia], qa = rq[ia];
+        const float ca = rc[ia], sa = rs[ia];
         const float x00 = A[pa * LD + pb], x01 = A[pa * LD + qb];
         const float x10 = A[qa * LD + pb], x11 = A[qa * LD + qb];
-        // T = Ja^T X, X' = T Jb with J = [[c, s], [-s, c]]
         const float t00 = ca * x00 - sa * x10, t01 = ca * x01 - sa * x11;
         const float t10 = sa * x00 + ca * x10, t11 = sa * x01 + ca * x11;
         A[pa * LD + pb] = cb * t00 - sb * t01;
@@ -228,10 +235,8 @@ __global__ __launch_bounds__(1024) void k_key_eig(EigArgs a) {
         A[qa * LD + pb] = cb * t10 - sb * t11;
         A[qa * LD + qb] = sb * t10 + cb * t11;
       }
-      for (int task = tid; task < D * HP; task += nt) {
-        const int i = task / HP, ib = task - (task / HP) * HP;
-        const int pb = rp[ib], qb = rq[ib];
-        const float cb = rc[ib], sb = rs[ib];
+      // V <- V Jb on columns (pb, qb)
+      for (int i = i0; i < D; i += RSTEP) {
         const float v1 = V[i * LD + pb], v2 = V[i * LD + qb];
         V[i * LD + pb] = cb * v1 - sb * v2;
         V[i * LD + qb] = sb * v1 + cb * v2;
@@ -240,7 +245,7 @@ __global__ __launch_bounds__(1024) void k_key_eig(EigArgs a) {
     }
   }
   // rank eigenvalues (descending, ties by index) and emit the coordinate map
-  for (int i = tid; i < D; i += nt) {
+  for (int i = tid; i < D; i += NT) {
     const float li = A[i * LD + i];
     int rank = 0;
     for (int j = 0; j < D; ++j) {
@@ -269,10 +274,15 @@ __global__ __launch_bounds__(256) void k_key_coords(CoordArgs a) {
   const float* kmap = a.kmap + (long long)bh * D * rK;
   for (int e = tid; e < D * rK; e += 256) km[e / rK][e % rK] = kmap[e];
   const T* kb = static_cast<const T*>(a.k.p);
-  for (int e = tid; e < 64 * D; e += 256) {
-    const int r = e / D, c = e - (e / D) * D;
+  constexpr int VEC = 16 / sizeof(T);
+  for (int e = tid; e < 64 * (D / VEC); e += 256) {
+    const int r = e / (D / VEC), c = (e - (e / (D / VEC)) * (D / VEC)) * VEC;
     const int n = n0 + r;
-    kr[r][c] = n < N ? Elem<T>::load(kb + a.k.row_off(bh, n) + c) : 0.f;
+    uint4 u = make_uint4(0, 0, 0, 0);
+    if (n < N) u = *reinterpret_cast<const uint4*>(kb + a.k.row_off(bh, n) + c);
+    const T* ev = reinterpret_cast<const T*>(&u);
+#pragma unroll
+    for (int j = 0; j < VEC; ++j) kr[r][c + j] = n < N ? Elem<T>::load(ev + j) : 0.f;
   }
   __syncthreads();
   const int r = tid >> 2;
@@ -281,10 +291,9 @@ __global__ __launch_bounds__(256) void k_key_coords(CoordArgs a) {
   const long long zrow = (long long)bh * N + n;
   for (int j = tid & 3; j < rKpad; j += 4) {
     float acc = 0.f;
-    if (j < rK) {
+    if (j < rK)
       for (int c = 0; c < D; ++c) acc += kr[r][c] * km[c][j];
-      a.z32[zrow * rK + j] = acc;
-    }
+    a.z32[zrow * rKpad + j] = acc;
     const bf16_t hi = f32_to_bf16(acc);
     a.zhi[zrow * rKpad + j] = hi;
     a.zlo[zrow * rKpad + j] = f32_to_bf16(acc - bf16_to_f32(hi));
@@ -483,90 +492,147 @@ __global__ __launch_bounds__(256) void k_group_scatter(ScatterArgs a) {
 }
 
 // ============================================================================
-// centre update: fp64 mean of each group's point rows summed in ascending token
-// order; then centre image y = M mean (or the mean itself) and bias mean . y
+// centre update, step 1: fp64 mean of each group's point rows, summed one row
+// after another in ascending token order (member rows are staged through LDS
+// 64 at a time; each thread owns one dimension).  Empty groups keep their
+// previous centre.
 // ============================================================================
 template <typename TP>
-__global__ __launch_bounds__(256) void k_centre_update(UpdateArgs a) {
-  __shared__ double smean[8][128];
-  __shared__ double sprod[8][128];
-  const int bh = blockIdx.y, tid = threadIdx.x;
-  const int Dimg = a.Dimg, Dp = a.Dp;
-  const int gpb = min(8, 256 / Dimg);
-  const int gl = tid / Dimg, j = tid - (tid / Dimg) * Dimg;
-  const int g = blockIdx.x * gpb + gl;
-  const bool gval = gl < gpb && g < a.G;
+__global__ __launch_bounds__(128) void k_group_mean(UpdateArgs a) {
+  constexpr int CH = 64;
+  __shared__ float rows[CH][129];
+  __shared__ int idx[CH];
+  const int bh = blockIdx.y, g = blockIdx.x, tid = threadIdx.x;
+  const int Dp = a.Dp;
   const TP* xb = static_cast<const TP*>(a.pts.p);
-  double mean = 0.0;
-  bool keep_old = false;
-  int n_g = 0;
-  if (gval && j < Dp) {
-    if (a.init) {
-      const long long idx = ((2LL * g + 1) * a.N) / (2LL * a.G);
-      mean = (double)Elem<TP>::load(xb + a.pts.row_off(bh, idx) + j);
-      n_g = 1;
-    } else {
-      const int* off = a.off + (long long)bh * a.offstride;
-      const int* perm = a.perm + (long long)bh * a.N;
-      const int a0 = off[g], a1 = off[g + 1];
-      n_g = a1 - a0;
-      if (n_g > 0) {
-        double s = 0.0;
-        for (int m = a0; m < a1; ++m) s = __dadd_rn(s, (double)Elem<TP>::load(xb + a.pts.row_off(bh, perm[m]) + j));
-        mean = s / (double)n_g;
+  double* cm = a.cmean ? a.cmean + ((long long)bh * a.gstride + g) * a.cstride : nullptr;
+  if (a.init) {
+    const long long sidx = ((2LL * g + 1) * a.N) / (2LL * a.G);
+    for (int j = tid; j < Dp; j += 128) cm[j] = (double)Elem<TP>::load(xb + a.pts.row_off(bh, sidx) + j);
+    return;
+  }
+  const int* off = a.off + (long long)bh * a.offstride;
+  const int* perm = a.perm + (long long)bh * a.N;
+  const int a0 = off[g], a1 = off[g + 1];
+  const int n_g = a1 - a0;
+  double s = 0.0;
+  constexpr int VEC = 16 / sizeof(TP);
+  const int cpr = (Dp + VEC - 1) / VEC;  // rows are padded to a 16-byte multiple
+  for (int m0 = a0; m0 < a1; m0 += CH) {
+    const int nr = min(CH, a1 - m0);
+    __syncthreads();
+    if (tid < nr) idx[tid] = perm[m0 + tid];
+    __syncthreads();
+    for (int e = tid; e < nr * cpr; e += 128) {
+      const int r = e / cpr, c = (e - (e / cpr) * cpr) * VEC;
+      const uint4 u = *reinterpret_cast<const uint4*>(xb + a.pts.row_off(bh, idx[r]) + c);
+      const TP* ev = reinterpret_cast<const TP*>(&u);
+#pragma unroll
+      for (int j = 0; j < VEC; ++j) rows[r][c + j] = Elem<TP>::load(ev + j);
+    }
+    __syncthreads();
+    if (tid < Dp)
+      for (int r = 0; r < nr; ++r) s = __dadd_rn(s, (double)rows[r][tid]);
+  }
+  if (tid >= Dp) return;
+  double mean;
+  if (n_g > 0) {
+    mean = s / (double)n_g;
+    if (cm) cm[tid] = mean;
+  } else {
+    mean = cm ? cm[tid] : 0.0;
+  }
+  if (a.means_out)
+    a.means_out[((long long)bh * a.mo_gstride + g) * Dp + tid] = n_g > 0 ? mean : __builtin_nan("");
+}
+
+// centre update, step 2: image y = M mean (or the mean itself), stored as a
+// hi/lo bf16 pair, and bias mean . y; 16 groups per workgroup share M.
+__global__ __launch_bounds__(256) void k_centre_images(UpdateArgs a) {
+  constexpr int GB = 16;
+  __shared__ double smean[GB][128];
+  __shared__ double sprod[GB][128];
+  const int bh = blockIdx.y, g0 = blockIdx.x * GB, tid = threadIdx.x;
+  const int Dp = a.Dp, Dimg = a.Dimg;
+  const int ng = min(GB, a.G - g0);
+  for (int e = tid; e < GB * 128; e += 256) {
+    const int gl = e >> 7, j = e & 127;
+    smean[gl][j] = (gl < ng && j < Dp) ? a.cmean[((long long)bh * a.gstride + g0 + gl) * a.cstride + j] : 0.0;
+  }
+  __syncthreads();
+  const float* M = a.metric ? a.metric + (long long)bh * Dp * Dp : nullptr;
+  for (int e = tid; e < GB * Dimg; e += 256) {
+    const int gl = e / Dimg, j = e - (e / Dimg) * Dimg;
+    double y = 0.0;
+    if (gl < ng && j < Dp) {
+      if (M) {
+        for (int k = 0; k < Dp; ++k) y += (double)M[k * Dp + j] * smean[gl][k];
       } else {
-        keep_old = true;
+        y = smean[gl][j];
       }
     }
-    if (a.means_out) {
-      a.means_out[((long long)bh * a.mo_gstride + g) * Dp + j] = n_g > 0 ? mean : __builtin_nan("");
+    if (j < 128) sprod[gl][j] = (j < Dp) ? y * smean[gl][j] : 0.0;
+    if (gl < ng) {
+      const long long yo = ((long long)bh * a.gstride + g0 + gl) * a.ystride + j;
+      const float yf = (float)y;
+      const bf16_t hi = f32_to_bf16(yf);
+      a.yhi[yo] = hi;
+      a.ylo[yo] = f32_to_bf16(yf - bf16_to_f32(hi));
     }
   }
-  if (a.means_only) return;
-  double* cm = a.cmean + ((long long)bh * a.gstride + (gval ? g : 0)) * a.cstride;
-  if (gval && j < Dp) {
-    if (keep_old) mean = cm[j];
-    cm[j] = mean;
-  }
-  if (gl < 8) smean[gl][j] = (gval && j < Dp) ? mean : 0.0;
   __syncthreads();
-  double y = 0.0;
-  if (gval && j < Dp) {
-    if (a.metric) {
-      const float* M = a.metric + (long long)bh * Dp * Dp;
-      for (int k = 0; k < Dp; ++k) y += (double)M[k * Dp + j] * smean[gl][k];
-    } else {
-      y = mean;
-    }
-  }
-  if (gl < 8) sprod[gl][j] = (gval && j < Dp) ? y * smean[gl][j] : 0.0;
-  __syncthreads();
-  if (!gval) return;
-  const long long yo = ((long long)bh * a.gstride + g) * a.ystride + j;
-  const float yf = (float)y;
-  const bf16_t hi = f32_to_bf16(yf);
-  a.yhi[yo] = hi;
-  a.ylo[yo] = f32_to_bf16(yf - bf16_to_f32(hi));
-  if (j == 0) {
+  if (tid < ng) {
     double b = 0.0;
-    for (int k = 0; k < Dp; ++k) b += sprod[gl][k];
-    a.ybias[(long long)bh * a.gstride + g] = (float)b;
+    for (int k = 0; k < Dp; ++k) b += sprod[tid][k];
+    a.ybias[(long long)bh * a.gstride + g0 + tid] = (float)b;
   }
 }
 
-// M_Q = s^2 sum over non-empty key groups of cbar_h cbar_h^T
+// M_Q = s^2 sum over non-empty key groups of cbar_h cbar_h^T (d x d per (b,h));
+// 16 key groups at a time are staged in LDS, each thread owns a 4x4 block
 __global__ __launch_bounds__(1024) void k_query_metric(QMetricArgs a) {
-  const int bh = blockIdx.x, d = a.d;
+  constexpr int HB = 16;
+  __shared__ double cs[HB][128];
+  const int bh = blockIdx.x, d = a.d, tid = threadIdx.x;
   const double* cb = a.cbar + (long long)bh * a.GK * d;
   const int* off = a.off_k + (long long)bh * (a.GK + 1);
-  const double s2 = (double)a.scale * (double)a.scale;
-  for (int e = threadIdx.x; e < d * d; e += blockDim.x) {
-    const int i = e / d, j = e - (e / d) * d;
-    double acc = 0.0;
-    for (int h = 0; h < a.GK; ++h)
-      if (off[h + 1] > off[h]) acc += cb[(long long)h * d + i] * cb[(long long)h * d + j];
-    a.mq[(long long)bh * d * d + e] = (float)(s2 * acc);
+  const int nb = d / 4;  // 4x4 blocks per row of blocks
+  const int bi = tid / nb, bj = tid - (tid / nb) * nb;
+  const bool act = bi < nb;
+  double acc[4][4];
+#pragma unroll
+  for (int x = 0; x < 4; ++x)
+#pragma unroll
+    for (int y = 0; y < 4; ++y) acc[x][y] = 0.0;
+  for (int h0 = 0; h0 < a.GK; h0 += HB) {
+    __syncthreads();
+    for (int e = tid; e < HB * d; e += 1024) {
+      const int hl = e / d, j = e - (e / d) * d;
+      const int h = h0 + hl;
+      cs[hl][j] = (h < a.GK && off[h + 1] > off[h]) ? cb[(long long)h * d + j] : 0.0;
+    }
+    __syncthreads();
+    if (act) {
+      for (int hl = 0; hl < HB; ++hl) {
+        double u[4], v[4];
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          u[x] = cs[hl][4 * bi + x];
+          v[x] = cs[hl][4 * bj + x];
+        }
+#pragma unroll
+        for (int x = 0; x < 4; ++x)
+#pragma unroll
+          for (int y = 0; y < 4; ++y) acc[x][y] += u[x] * v[y];
+      }
+    }
   }
+  if (!act) return;
+  const double s2 = (double)a.scale * (double)a.scale;
+#pragma unroll
+  for (int x = 0; x < 4; ++x)
+#pragma unroll
+    for (int y = 0; y < 4; ++y) a.mq[(long long)bh * d * d + (4 * bi + x) * d + 4 * bj + y] = (float)(s2 * acc[x][y]);
 }
 
 // ============================================================================
@@ -584,12 +650,17 @@ __global__ __launch_bounds__(256) void k_zero_u32(uint32_t* p, int n) {
 template <typename T>
 __global__ __launch_bounds__(256) void k_vmax(View4 v, int N, int d, uint32_t* vmax) {
   const int bh = blockIdx.y;
-  const int row = blockIdx.x * 256 + threadIdx.x;
+  constexpr int VEC = 16 / sizeof(T);
+  const int cpr = d / VEC;
+  const long long e = (long long)blockIdx.x * 256 + threadIdx.x;  // one 16-byte chunk
   float m = 0.f;
-  if (row < N) {
-    const T* r = static_cast<const T*>(v.p) + v.row_off(bh, row);
-    for (int c = 0; c < d; ++c) {
-      const float x = fabsf(Elem<T>::load(r + c));
+  if (e < (long long)N * cpr) {
+    const int row = (int)(e / cpr), c = (int)(e - (e / cpr) * cpr) * VEC;
+    const uint4 u = *reinterpret_cast<const uint4*>(static_cast<const T*>(v.p) + v.row_off(bh, row) + c);
+    const T* ev = reinterpret_cast<const T*>(&u);
+#pragma unroll
+    for (int j = 0; j < VEC; ++j) {
+      const float x = fabsf(Elem<T>::load(ev + j));
       m = (x > m || x != x) ? x : m;
     }
   }
@@ -729,10 +800,11 @@ hipError_t launch_group_scatter(const Plan& p, const ScatterArgs& a, hipStream_t
 }
 
 hipError_t launch_centre_update(const Plan& p, const UpdateArgs& a, int pts_type, hipStream_t s) {
-  const int gpb = (256 / a.Dimg) < 8 ? (256 / a.Dimg) : 8;
-  dim3 g((a.G + gpb - 1) / gpb, p.BH);
-  if (pts_type == 0) SP_LAUNCH(k_centre_update<bf16_t>, g, dim3(256), s, a);
-  else SP_LAUNCH(k_centre_update<float>, g, dim3(256), s, a);
+  dim3 g(a.G, p.BH);
+  if (pts_type == 0) SP_LAUNCH(k_group_mean<bf16_t>, g, dim3(128), s, a);
+  else SP_LAUNCH(k_group_mean<float>, g, dim3(128), s, a);
+  if (a.means_only) return hipSuccess;
+  SP_LAUNCH(k_centre_images, dim3((a.G + 15) / 16, p.BH), dim3(256), s, a);
   return hipSuccess;
 }
 
@@ -745,7 +817,8 @@ hipError_t launch_query_metric(const Plan& p, hipStream_t s) {
 hipError_t launch_vmax(const Plan& p, hipStream_t s) {
   if (p.dtype != SPARSEPR_BF16) return hipSuccess;
   SP_LAUNCH(k_zero_u32, dim3((p.BH + 255) / 256), dim3(256), s, p.vmax, p.BH);
-  SP_LAUNCH(k_vmax<bf16_t>, dim3((p.N + 255) / 256, p.BH), dim3(256), s, p.v, p.N, p.d, p.vmax);
+  const long long chunks = (long long)p.N * (p.d / 8);
+  SP_LAUNCH(k_vmax<bf16_t>, dim3((unsigned)((chunks + 255) / 256), p.BH), dim3(256), s, p.v, p.N, p.d, p.vmax);
   return hipSuccess;
 }
 

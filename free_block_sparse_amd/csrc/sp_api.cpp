@@ -79,7 +79,7 @@ sparsepr_status kmeans_side(Plan& p, int side, int G, int* labels_out, int* perm
     lo = true;
     aa.pts = contig(p.zhi, p, D);
     aa.pts_lo = p.zlo;
-    ua.pts = contig(p.z32, p, p.rK);
+    ua.pts = contig(p.z32, p, p.rKpad);
     ua.Dp = p.rK;
     ua.Dimg = p.rKpad;
     ua.metric = nullptr;

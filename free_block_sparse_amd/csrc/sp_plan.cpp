@@ -125,7 +125,7 @@ void plan_carve(Plan* p, char* base) {
   p->eigval = c.take<float>(BH * d);
   p->kmap = c.take<float>(BH * d * p->rK);
   const bool rcp = p->mode == SPARSEPR_PART_RESPONSE_COUPLED;
-  p->z32 = rcp ? c.take<float>(BH * N * p->rK) : nullptr;
+  p->z32 = rcp ? c.take<float>(BH * N * p->rKpad) : nullptr;
   p->zhi = rcp ? c.take<bf16_t>(BH * N * p->rKpad) : nullptr;
   p->zlo = rcp ? c.take<bf16_t>(BH * N * p->rKpad) : nullptr;
   const bool f32 = p->dtype == SPARSEPR_FP32;

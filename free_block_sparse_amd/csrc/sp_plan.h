@@ -40,7 +40,7 @@ struct Plan {
   float* mk;              // [BH, d, d]
   float* eigval;          // [BH, d]
   float* kmap;            // [BH, d, rK]
-  float* z32;             // [BH, N, rK]
+  float* z32;             // [BH, N, rKpad] (zero beyond rK)
   bf16_t* zhi;            // [BH, N, rKpad]
   bf16_t* zlo;            // [BH, N, rKpad]
   bf16_t* phi;            // [BH, N, d] raw points split (fp32 inputs only)
