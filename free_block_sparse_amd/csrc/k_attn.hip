@@ -15,6 +15,8 @@
 // not every granted cell.
 #include <string.h>
 
+#include <type_traits>
+
 #include "sp_kernels.h"
 
 namespace sp {
@@ -218,15 +220,8 @@ __global__ __launch_bounds__(256, 2) void k_sparse_attn_mfma(AttnArgs a) {
     for (int j = 0; j < 8; ++j) store_vt_row<KPT>(&Vt[st][(8 * c8 + j) * LDV + KPT * kr], vreg, j);
   };
 
-  const int ntile = (L + 63) / 64;
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
-  for (int t = 0; t < ntile; ++t) {
-    const int st = t & 1;
-    const int kt0 = 64 * t;
-    if (t + 1 < ntile) load_tile(kt0 + 64);
-    if (wave_active) {
+  auto compute_tile = [&](auto mask_tag, int st, int kt0) {
+    constexpr bool MASK = decltype(mask_tag)::value;
       f32x16 sacc[2];
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
@@ -237,44 +232,44 @@ __global__ __launch_bounds__(256, 2) void k_sparse_attn_mfma(AttnArgs a) {
           sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], sacc[kt], 0, 0, 0);
         }
       }
+      // row max of the raw scores (masking the ragged end of the sequence)
       float mloc = -INFINITY;
-      if (kt0 + 64 > L) {
+      if constexpr (MASK) {
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int key = 32 * kt + (r & 3) + 8 * (r >> 2) + 4 * half;
-            const float sv = kt0 + key < L ? sacc[kt][r] * c : -INFINITY;
-            sacc[kt][r] = sv;
-            mloc = fmaxf(mloc, sv);
-          }
-      } else {
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const float sv = sacc[kt][r] * c;
-            sacc[kt][r] = sv;
-            mloc = fmaxf(mloc, sv);
+            if (kt0 + key >= L) sacc[kt][r] = -INFINITY;
           }
       }
-      mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
-      const float mnew = fmaxf(m, mloc);
-      const float mb = mnew == -INFINITY ? 0.f : mnew;
-      const float alpha = exp2f(m - mb);
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mloc = fmaxf(mloc, sacc[kt][r]);
+      mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64)) * c;
+      // Lazy rescaling: the reference max only moves when a row's max grows by
+      // more than 8 (log2 units), so p <= 2^8 stays exact in fp16 and fp32 sums;
+      // the softmax is invariant to the reference.
+      if (__builtin_amdgcn_ballot_w64(mloc > m + 8.f)) {
+        const float mnew = fmaxf(m, mloc);
+        const float alpha = __builtin_amdgcn_exp2f(m - mnew);
+        l *= alpha;
+#pragma unroll
+        for (int b = 0; b < DB; ++b) o[b] *= alpha;
+        m = mnew;
+      }
+      const float mb = m;
       float psum = 0.f;
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float pv = exp2f(sacc[kt][r] - mb);
+          const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kt][r], c, -mb));
           sacc[kt][r] = pv;
           psum += pv;
         }
-      l = l * alpha + psum;
-      m = mnew;
-#pragma unroll
-      for (int b = 0; b < DB; ++b) o[b] *= alpha;
+      l += psum;
 #pragma unroll
       for (int sp = 0; sp < 4; ++sp) {
         const int kt = sp >> 1, rb = 8 * (sp & 1);
@@ -307,6 +302,20 @@ __global__ __launch_bounds__(256, 2) void k_sparse_attn_mfma(AttnArgs a) {
           }
         }
       }
+  };
+
+  const int ntile = (L + 63) / 64;
+  const int nfull = L / 64;  // tiles without a ragged end
+  load_tile(0);
+  store_tile(0);
+  __syncthreads();
+  for (int t = 0; t < ntile; ++t) {
+    const int st = t & 1;
+    const int kt0 = 64 * t;
+    if (t + 1 < ntile) load_tile(kt0 + 64);
+    if (wave_active) {
+      if (t < nfull) compute_tile(std::false_type{}, st, kt0);
+      else compute_tile(std::true_type{}, st, kt0);
     }
     if (t + 1 < ntile) store_tile(st ^ 1);
     __syncthreads();

@@ -50,7 +50,7 @@ __device__ void jacobi_sym_f64(double* A, double* V, int n, double* rcs, int* rp
   const int hp = n / 2;
   for (int e = tid; e < n * n; e += nt) V[e] = (e / n == e % n) ? 1.0 : 0.0;
   block_sync();
-  for (int sweep = 0; sweep < 60; ++sweep) {
+  for (int sweep = 0; sweep < 30; ++sweep) {
     double off = 0.0, tot = 0.0;
     for (int e = tid; e < n * n; e += nt) {
       const double x = A[e];
@@ -70,7 +70,7 @@ __device__ void jacobi_sym_f64(double* A, double* V, int n, double* rcs, int* rp
         o += red[2 * w];
         t += red[2 * w + 1];
       }
-      *stop = !(o > 1e-26 * t);
+      *stop = !(o > 1e-24 * t);
     }
     block_sync();
     if (*stop) break;

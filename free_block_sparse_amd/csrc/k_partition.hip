@@ -170,9 +170,12 @@ __global__ __launch_bounds__(1024) void k_key_eig(EigArgs a) {
     V[i * LD + j] = i == j ? 1.f : 0.f;
   }
   __syncthreads();
-  // thread -> (column pair ib, first row pair / row) for the block updates
-  const int ib = tid % HP, i0 = tid / HP;
-  constexpr int RSTEP = NT / HP;  // 16 (D=128) or 32 (D=64)
+  // lanes own row pairs / rows (row stride D + 1 keeps them on distinct banks);
+  // waves step through column pairs
+  const int lane = tid & 63, wv = tid >> 6;
+  constexpr int WPR = 64 / HP;     // column-pair offsets per wave (1 for D=128, 2 for D=64)
+  const int ia = lane % HP, ib0 = wv * WPR + lane / HP;
+  constexpr int CSTEP = (NT / 64) * WPR;
   for (int sweep = 0; sweep < 16; ++sweep) {
     float off = 0.f, tot = 0.f;
     for (int e = tid; e < D * D; e += NT) {
@@ -220,12 +223,12 @@ __global__ __launch_bounds__(1024) void k_key_eig(EigArgs a) {
         rq[tid] = q;
       }
       __syncthreads();
-      const int pb = rp[ib], qb = rq[ib];
-      const float cb = rc[ib], sb = rs[ib];
-      // A <- Ja^T A Jb on the 2x2 blocks (row pair ia, column pair ib)
-      for (int ia = i0; ia < HP; ia += RSTEP) {
-        const int pa = rp[ia], qa = rq[ia];
-        const float ca = rc[ia], sa = rs[ia];
+      const int pa = rp[ia], qa = rq[ia];
+      const float ca = rc[ia], sa = rs[ia];
+      for (int ib = ib0; ib < HP; ib += CSTEP) {
+        const int pb = rp[ib], qb = rq[ib];
+        const float cb = rc[ib], sb = rs[ib];
+        // A <- Ja^T A Jb on the 2x2 block (row pair ia, column pair ib)
         const float x00 = A[pa * LD + pb], x01 = A[pa * LD + qb];
         const float x10 = A[qa * LD + pb], x11 = A[qa * LD + qb];
         const float t00 = ca * x00 - sa * x10, t01 = ca * x01 - sa * x11;
@@ -235,11 +238,15 @@ __global__ __launch_bounds__(1024) void k_key_eig(EigArgs a) {
         A[qa * LD + pb] = cb * t10 - sb * t11;
         A[qa * LD + qb] = sb * t10 + cb * t11;
       }
-      // V <- V Jb on columns (pb, qb)
-      for (int i = i0; i < D; i += RSTEP) {
-        const float v1 = V[i * LD + pb], v2 = V[i * LD + qb];
-        V[i * LD + pb] = cb * v1 - sb * v2;
-        V[i * LD + qb] = sb * v1 + cb * v2;
+      // V <- V J: lanes own rows, waves step through column pairs
+      for (int ib = wv; ib < HP; ib += NT / 64) {
+        const int pb = rp[ib], qb = rq[ib];
+        const float cb = rc[ib], sb = rs[ib];
+        for (int i = lane; i < D; i += 64) {
+          const float v1 = V[i * LD + pb], v2 = V[i * LD + qb];
+          V[i * LD + pb] = cb * v1 - sb * v2;
+          V[i * LD + qb] = sb * v1 + cb * v2;
+        }
       }
       __syncthreads();
     }
@@ -649,12 +656,13 @@ __global__ __launch_bounds__(256) void k_zero_u32(uint32_t* p, int n) {
 
 template <typename T>
 __global__ __launch_bounds__(256) void k_vmax(View4 v, int N, int d, uint32_t* vmax) {
+  __shared__ float red[4];
   const int bh = blockIdx.y;
   constexpr int VEC = 16 / sizeof(T);
   const int cpr = d / VEC;
-  const long long e = (long long)blockIdx.x * 256 + threadIdx.x;  // one 16-byte chunk
+  const long long total = (long long)N * cpr;
   float m = 0.f;
-  if (e < (long long)N * cpr) {
+  for (long long e = (long long)blockIdx.x * 256 + threadIdx.x; e < total; e += (long long)gridDim.x * 256) {
     const int row = (int)(e / cpr), c = (int)(e - (e / cpr) * cpr) * VEC;
     const uint4 u = *reinterpret_cast<const uint4*>(static_cast<const T*>(v.p) + v.row_off(bh, row) + c);
     const T* ev = reinterpret_cast<const T*>(&u);
@@ -668,7 +676,12 @@ __global__ __launch_bounds__(256) void k_vmax(View4 v, int N, int d, uint32_t* v
     const float t = __shfl_xor(m, o, 64);
     m = (t > m || t != t) ? t : m;
   }
-  if ((threadIdx.x & 63) == 0) atomicMax(vmax + bh, __float_as_uint(m));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int w = 1; w < 4; ++w) m = (red[w] > m || red[w] != red[w]) ? red[w] : m;
+    atomicMax(vmax + bh, __float_as_uint(m));
+  }
 }
 
 __device__ inline int v_exponent(uint32_t bits) {
@@ -817,8 +830,7 @@ hipError_t launch_query_metric(const Plan& p, hipStream_t s) {
 hipError_t launch_vmax(const Plan& p, hipStream_t s) {
   if (p.dtype != SPARSEPR_BF16) return hipSuccess;
   SP_LAUNCH(k_zero_u32, dim3((p.BH + 255) / 256), dim3(256), s, p.vmax, p.BH);
-  const long long chunks = (long long)p.N * (p.d / 8);
-  SP_LAUNCH(k_vmax<bf16_t>, dim3((unsigned)((chunks + 255) / 256), p.BH), dim3(256), s, p.v, p.N, p.d, p.vmax);
+  SP_LAUNCH(k_vmax<bf16_t>, dim3(64, p.BH), dim3(256), s, p.v, p.N, p.d, p.vmax);
   return hipSuccess;
 }
 
