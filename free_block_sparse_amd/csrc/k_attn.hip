@@ -253,7 +253,10 @@ __global__ __launch_bounds__(256, 2) void k_sparse_attn_mfma(AttnArgs a) {
       // the softmax is invariant to the reference.
       if (__builtin_amdgcn_ballot_w64(mloc > m + 8.f)) {
         const float mnew = fmaxf(m, mloc);
-        const float alpha = __builtin_amdgcn_exp2f(m - mnew);
+        float alpha = __builtin_amdgcn_exp2f(m - mnew);
+        // alpha is opaque past this point, so the rescale below cannot be
+        // speculated out of the (rarely taken) branch
+        asm volatile("" : "+v"(alpha));
         l *= alpha;
 #pragma unroll
         for (int b = 0; b < DB; ++b) o[b] *= alpha;
@@ -309,17 +312,14 @@ __global__ __launch_bounds__(256, 2) void k_sparse_attn_mfma(AttnArgs a) {
   load_tile(0);
   store_tile(0);
   __syncthreads();
-  for (int t = 0; t < ntile; ++t) {
+  for (int t = 0; t < nfull; ++t) {
     const int st = t & 1;
-    const int kt0 = 64 * t;
-    if (t + 1 < ntile) load_tile(kt0 + 64);
-    if (wave_active) {
-      if (t < nfull) compute_tile(std::false_type{}, st, kt0);
-      else compute_tile(std::true_type{}, st, kt0);
-    }
+    if (t + 1 < ntile) load_tile(64 * t + 64);
+    if (wave_active) compute_tile(std::false_type{}, st, 64 * t);
     if (t + 1 < ntile) store_tile(st ^ 1);
     __syncthreads();
   }
+  if (nfull < ntile && wave_active) compute_tile(std::true_type{}, nfull & 1, 64 * nfull);
 
   // ---- epilogue: normalise, correct (b + x W V^T), restore token order
   const float ltot = l + __shfl_xor(l, 32, 64);
