@@ -140,31 +140,32 @@ __device__ inline bool setup_item(const AttnArgs& a, int bh, int tile, int* seg_
 // LDS; the contraction order over keys inside a 16-key step follows the S^T
 // register layout (keys 16s + 4h + {0..3} and 16s + 8 + 4h + {0..3}).
 // ============================================================================
-// Pack the j-th 16-bit element of KPT 16-byte chunks (one per key) into KPT
-// consecutive key slots of one dim row of the transposed V tile.
-template <int KPT>
-__device__ inline void store_vt_row(bf16_t* dst, const uint4* vr, int j) {
-  uint32_t h[KPT];
-#pragma unroll
-  for (int i = 0; i < KPT; ++i) {
-    const uint32_t w = (j >> 1) == 0 ? vr[i].x : (j >> 1) == 1 ? vr[i].y : (j >> 1) == 2 ? vr[i].z : vr[i].w;
-    h[i] = (j & 1) ? (w >> 16) : (w & 0xffffu);
-  }
-  if constexpr (KPT == 4) {
-    *reinterpret_cast<uint2*>(dst) = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
-  } else {
-    *reinterpret_cast<uint32_t*>(dst) = h[0] | (h[1] << 16);
-  }
-}
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+#define SP_LDS(p) ((__attribute__((address_space(3))) void*)(p))
+#define SP_GLB(p) ((__attribute__((address_space(1))) void*)(p))
+
+// LDS tile layout: rows of D 16-bit values, no padding; the 16-byte chunks of
+// a row are permuted by an XOR swizzle so that
+//   K fragment reads (16 lanes = 16 keys, one chunk)          -> distinct banks,
+//   V transposing reads (ds_read_b64_tr_b16, 4 keys x 4 dims) -> distinct banks.
+template <int CPR> __device__ inline int swz_k(int key) { return key & (CPR - 1); }
+template <int CPR> __device__ inline int swz_v(int key) { return (4 * key) & (CPR - 1); }
 
 template <int D, bool VF16>
 __global__ __launch_bounds__(256, 2) void k_sparse_attn_mfma(AttnArgs a) {
   constexpr int KS = D / 16, DB = D / 32;
-  constexpr int LDK = D + 8, LDV = 64 + 4;
   constexpr int CPR = D / 8;              // 16-byte chunks per key row
-  constexpr int KPT = (64 * CPR) / 256;   // consecutive keys loaded per thread per tile
-  __shared__ __attribute__((aligned(16))) bf16_t Ks[2][64 * LDK];
-  __shared__ __attribute__((aligned(16))) bf16_t Vt[2][D * LDV];
+  constexpr int RPI = 64 / CPR;           // rows moved by one wave-wide 16-byte LDS-DMA load
+  constexpr int IPW = 64 / RPI / 4;       // such loads per wave per tile (K and V each)
+  // Two pipeline stages, each [K | V][64 keys][D] (V sits VOFF bytes past K).
+  // They are distinct objects so that reads of one stage provably do not
+  // alias the LDS-DMA writes in flight into the other: with that (and the
+  // restrict-qualified tile bases below) no wait on the loads of the next
+  // tile is placed in front of the current tile's LDS reads.
+  constexpr int VOFF = 64 * D * 2;
+  __shared__ __attribute__((aligned(1024))) bf16_t KV0[2 * 64 * D];
+  __shared__ __attribute__((aligned(1024))) bf16_t KV1[2 * 64 * D];
+  __shared__ long long offs0[128], offs1[128];  // element offsets of the K rows, then the V rows
   __shared__ int seg_v[kMaxGroups + 1], seg_p[kMaxGroups + 1];
   __shared__ int tmp[8];
   const int bh = blockIdx.y, tile = blockIdx.x, tid = threadIdx.x;
@@ -191,135 +192,192 @@ __global__ __launch_bounds__(256, 2) void k_sparse_attn_mfma(AttnArgs a) {
   float m = -INFINITY, l = 0.f;
   const float c = a.scale * 1.4426950408889634f;
 
-  // loader geometry: this thread moves keys KPT*kr .. KPT*kr + KPT-1 of every
-  // tile, 16-byte chunk c8 of each
-  const int c8 = tid % CPR, kr = tid / CPR;
-  int cur = 0;  // segment cursor of this thread's first key (monotone in the tile index)
-  uint4 kreg[KPT], vreg[KPT];
-  auto load_tile = [&](int kt0) {
-    const int v0 = kt0 + KPT * kr;
-    while (cur + 1 < nseg && seg_v[cur + 1] <= v0) ++cur;
-    int s = cur;
+  // Wave 0 resolves the physical rows of one tile (virtual key -> segment);
+  // lane j owns key j of every tile, so its segment cursor only moves forward.
+  int cur = 0;
+  auto rows = [&](long long* __restrict__ ofs, const int* __restrict__ sv, const int* __restrict__ sp, int tt) {
+    const int v = 64 * tt + lane;
+    int prow = sp[0];  // rows past the end read a valid row; they are masked
+    if (v < L) {
+      while (cur + 1 < nseg && sv[cur + 1] <= v) ++cur;
+      prow = sp[cur] + v - sv[cur];
+    }
+    ofs[lane] = a.kv.row_off(bh, prow);
+    ofs[64 + lane] = a.vv.row_off(bh, prow);
+  };
+  // Every wave moves its share of the K and V tiles straight into LDS.
+  typedef __attribute__((address_space(3))) char lds_char;
+  auto issue = [&](lds_char* __restrict__ dst, const long long* __restrict__ ofs, const bf16_t* __restrict__ gk0,
+                   const bf16_t* __restrict__ gv0) {
 #pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-      const int v = v0 + i;
-      kreg[i] = make_uint4(0, 0, 0, 0);
-      vreg[i] = make_uint4(0, 0, 0, 0);
-      if (v < L) {
-        while (s + 1 < nseg && seg_v[s + 1] <= v) ++s;
-        const int prow = seg_p[s] + v - seg_v[s];
-        kreg[i] = *reinterpret_cast<const uint4*>(kb + a.kv.row_off(bh, prow) + 8 * c8);
-        vreg[i] = *reinterpret_cast<const uint4*>(vb + a.vv.row_off(bh, prow) + 8 * c8);
-      }
+    for (int i = 0; i < IPW; ++i) {
+      const int rb = (w * IPW + i) * RPI;
+      const int r = rb + lane / CPR, sl = lane % CPR;
+      const bf16_t* gk = gk0 + ofs[r] + 8 * (sl ^ swz_k<CPR>(r));
+      const bf16_t* gv = gv0 + ofs[64 + r] + 8 * (sl ^ swz_v<CPR>(r));
+      __builtin_amdgcn_global_load_lds(SP_GLB(gk), dst + rb * 2 * D, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(SP_GLB(gv), dst + VOFF + rb * 2 * D, 16, 0, 0);
     }
   };
-  auto store_tile = [&](int st) {
-#pragma unroll
-    for (int i = 0; i < KPT; ++i) *reinterpret_cast<uint4*>(&Ks[st][(KPT * kr + i) * LDK + 8 * c8]) = kreg[i];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) store_vt_row<KPT>(&Vt[st][(8 * c8 + j) * LDV + KPT * kr], vreg, j);
-  };
 
-  auto compute_tile = [&](auto mask_tag, int st, int kt0) {
+  // Per-lane LDS byte bases of the fragment reads.  The chunk swizzle only
+  // flips address bits below the row bits, so every fragment address is
+  // (base ^ small constant) + immediate offset.
+  const int gi = lane >> 4, li = lane & 15, rr = li >> 2, qq = li & 3;
+  const uint32_t kbase0 = col * 2 * D + 16 * (half ^ swz_k<CPR>(col));
+  const uint32_t vbase0 = VOFF + (4 * (gi >> 1) + rr) * 2 * D + 64 * (swz_v<CPR>(rr) >> 2) +
+                          16 * (2 * (gi & 1) + (qq >> 1)) + 8 * (qq & 1);
+
+  auto compute_tile = [&](auto mask_tag, const lds_char* __restrict__ lds, int kt0) {
     constexpr bool MASK = decltype(mask_tag)::value;
-      f32x16 sacc[2];
+    // opaque per tile: keeps the derived addresses from being hoisted into
+    // registers for the whole loop
+    uint32_t kb0 = kbase0, vb0 = vbase0;
+    asm volatile("" : "+v"(kb0), "+v"(vb0));
+    f32x16 sacc[2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) sacc[kt] = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const uint32_t ka = kb0 ^ (32u * ks);
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
-        sacc[kt] = f32x16{};
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          const bf16x8 kf = *reinterpret_cast<const bf16x8*>(&Ks[st][(32 * kt + col) * LDK + 16 * ks + 8 * half]);
-          sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], sacc[kt], 0, 0, 0);
-        }
+        const bf16x8 kf = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(lds + ka + kt * 32 * 2 * D);  // keys 32kt + col
+        sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], sacc[kt], 0, 0, 0);
       }
-      // row max of the raw scores (masking the ragged end of the sequence)
-      float mloc = -INFINITY;
-      if constexpr (MASK) {
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = 32 * kt + (r & 3) + 8 * (r >> 2) + 4 * half;
-            if (kt0 + key >= L) sacc[kt][r] = -INFINITY;
-          }
-      }
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mloc = fmaxf(mloc, sacc[kt][r]);
-      mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64)) * c;
-      // Lazy rescaling: the reference max only moves when a row's max grows by
-      // more than 8 (log2 units), so p <= 2^8 stays exact in fp16 and fp32 sums;
-      // the softmax is invariant to the reference.
-      if (__builtin_amdgcn_ballot_w64(mloc > m + 8.f)) {
-        const float mnew = fmaxf(m, mloc);
-        float alpha = __builtin_amdgcn_exp2f(m - mnew);
-        // alpha is opaque past this point, so the rescale below cannot be
-        // speculated out of the (rarely taken) branch
-        asm volatile("" : "+v"(alpha));
-        l *= alpha;
-#pragma unroll
-        for (int b = 0; b < DB; ++b) o[b] *= alpha;
-        m = mnew;
-      }
-      const float mb = m;
-      float psum = 0.f;
+    }
+    // row max of the raw scores (masking the ragged end of the sequence)
+    float mloc = -INFINITY;
+    if constexpr (MASK) {
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kt][r], c, -mb));
-          sacc[kt][r] = pv;
-          psum += pv;
+          const int key = 32 * kt + (r & 3) + 8 * (r >> 2) + 4 * half;
+          if (kt0 + key >= L) sacc[kt][r] = -INFINITY;
         }
-      l += psum;
+    }
 #pragma unroll
-      for (int sp = 0; sp < 4; ++sp) {
-        const int kt = sp >> 1, rb = 8 * (sp & 1);
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mloc = fmaxf(mloc, sacc[kt][r]);
+    mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64)) * c;
+    // Lazy rescaling: the reference max only moves when a row's max grows by
+    // more than 8 (log2 units), so p <= 2^8 stays exact in fp16 and fp32 sums;
+    // the softmax is invariant to the reference.
+    if (__builtin_amdgcn_ballot_w64(mloc > m + 8.f)) {
+      const float mnew = fmaxf(m, mloc);
+      float alpha = __builtin_amdgcn_exp2f(m - mnew);
+      // alpha is opaque past this point, so the rescale below cannot be
+      // speculated out of the (rarely taken) branch
+      asm volatile("" : "+v"(alpha));
+      l *= alpha;
+      // in place, so the accumulators keep their registers across the branch
+#pragma unroll
+      for (int b = 0; b < DB; ++b)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) asm volatile("v_mul_f32 %0, %1, %0" : "+v"(o[b][i]) : "v"(alpha));
+      m = mnew;
+    }
+    const float mb = m;
+    float psum = 0.f;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kt][r], c, -mb));
+        sacc[kt][r] = pv;
+        if constexpr (!VF16) psum += pv;
+      }
+    // P.V: A = V^T fragment read transposed from the row-major V tile.  In a
+    // 16-lane group (index gi = lane>>4, i = lane&15) lane i supplies the
+    // address of key kb + (i>>2), dims 4(i&3)..+3; it receives dim (i) of keys
+    // kb..kb+3 -- the keys its P values (S^T register layout) belong to.
+    uint32_t va[DB];
+#pragma unroll
+    for (int b = 0; b < DB; ++b) va[b] = vb0 ^ (64u * b);
+#pragma unroll
+    for (int sp = 0; sp < 4; ++sp) {
+      const int kt = sp >> 1, rb = 8 * (sp & 1);
+      uint32_t pw[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
         if constexpr (VF16) {
-          f16x8 pf;
-#pragma unroll
-          for (int j = 0; j < 8; ++j) pf[j] = (_Float16)sacc[kt][rb + j];
-#pragma unroll
-          for (int b = 0; b < DB; ++b) {
-            const bf16_t* vrow = &Vt[st][(32 * b + col) * LDV + 16 * sp + 4 * half];
-            const uint2 lo = *reinterpret_cast<const uint2*>(vrow);
-            const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 8);
-            const f16x8 vf = __builtin_bit_cast(f16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
-            o[b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, pf, o[b], 0, 0, 0);
-          }
+          typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+          const h2 hv = {(_Float16)sacc[kt][rb + 2 * j], (_Float16)sacc[kt][rb + 2 * j + 1]};
+          pw[j] = __builtin_bit_cast(uint32_t, hv);
         } else {
-          uint4 pk;
-          pk.x = (uint32_t)f32_to_bf16(sacc[kt][rb + 0]) | ((uint32_t)f32_to_bf16(sacc[kt][rb + 1]) << 16);
-          pk.y = (uint32_t)f32_to_bf16(sacc[kt][rb + 2]) | ((uint32_t)f32_to_bf16(sacc[kt][rb + 3]) << 16);
-          pk.z = (uint32_t)f32_to_bf16(sacc[kt][rb + 4]) | ((uint32_t)f32_to_bf16(sacc[kt][rb + 5]) << 16);
-          pk.w = (uint32_t)f32_to_bf16(sacc[kt][rb + 6]) | ((uint32_t)f32_to_bf16(sacc[kt][rb + 7]) << 16);
-          const bf16x8 pf = __builtin_bit_cast(bf16x8, pk);
-#pragma unroll
-          for (int b = 0; b < DB; ++b) {
-            const bf16_t* vrow = &Vt[st][(32 * b + col) * LDV + 16 * sp + 4 * half];
-            const uint2 lo = *reinterpret_cast<const uint2*>(vrow);
-            const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 8);
-            const bf16x8 vf = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
-            o[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, o[b], 0, 0, 0);
-          }
+          pw[j] = (uint32_t)f32_to_bf16(sacc[kt][rb + 2 * j]) | ((uint32_t)f32_to_bf16(sacc[kt][rb + 2 * j + 1]) << 16);
         }
       }
+      const uint4 pk = make_uint4(pw[0], pw[1], pw[2], pw[3]);
+      if constexpr (VF16) {
+        // row sum of the fp16 probabilities the product below uses (fp32 accumulation)
+        typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+        const h2 one2 = {(_Float16)1.f, (_Float16)1.f};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) psum = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, pw[j]), one2, psum, false);
+      }
+#pragma unroll
+      for (int b = 0; b < DB; ++b) {
+        // keys 16sp + 4(gi>>1) + (0..3) and the same + 8, dims 32b + 16(gi&1) + (0..15)
+        const v4i16 t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            reinterpret_cast<__attribute__((address_space(3))) v4i16*>(const_cast<lds_char*>(lds) + va[b] + sp * 32 * D));
+        const v4i16 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            reinterpret_cast<__attribute__((address_space(3))) v4i16*>(const_cast<lds_char*>(lds) + va[b] + sp * 32 * D + 16 * D));
+        const uint2 u0 = __builtin_bit_cast(uint2, t0), u1 = __builtin_bit_cast(uint2, t1);
+        const uint4 vv = make_uint4(u0.x, u0.y, u1.x, u1.y);
+        if constexpr (VF16) {
+          o[b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, vv), __builtin_bit_cast(f16x8, pk),
+                                                        o[b], 0, 0, 0);
+        } else {
+          o[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vv),
+                                                         __builtin_bit_cast(bf16x8, pk), o[b], 0, 0, 0);
+        }
+      }
+    }
+    l += psum;
   };
 
   const int ntile = (L + 63) / 64;
   const int nfull = L / 64;  // tiles without a ragged end
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
-  for (int t = 0; t < nfull; ++t) {
-    const int st = t & 1;
-    if (t + 1 < ntile) load_tile(64 * t + 64);
-    if (wave_active) compute_tile(std::false_type{}, st, 64 * t);
-    if (t + 1 < ntile) store_tile(st ^ 1);
+  lds_char* const s0 = (lds_char*)KV0;
+  lds_char* const s1 = (lds_char*)KV1;
+  const bf16_t* const gk0 = kb;
+  const bf16_t* const gv0 = vb;
+  // One pipeline step: start the DMA of tile t+1 into the other stage,
+  // resolve the rows of tile t+2, compute tile t, then wait for the DMA and
+  // meet at the barrier.  Tile t uses offsets buffer t&1 and stage t&1.
+  auto step = [&](auto mask_tag, lds_char* cur_st, lds_char* nxt_st, long long* nxt_ofs, long long* cur_ofs, int t) {
+    if (t + 1 < ntile) issue(nxt_st, nxt_ofs, gk0, gv0);
+    if (w == 0 && t + 2 < ntile) rows(cur_ofs, seg_v, seg_p, t + 2);
+    if (wave_active) compute_tile(mask_tag, cur_st, 64 * t);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
+  };
+  if (w == 0) rows(offs0, seg_v, seg_p, 0);
+  __syncthreads();
+  issue(s0, offs0, gk0, gv0);
+  if (w == 0 && ntile > 1) rows(offs1, seg_v, seg_p, 1);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  // full tiles in pairs (stages fixed at compile time), then the odd one and
+  // the ragged end, so the hot loop carries no masking and no path merges
+  constexpr std::false_type full{};
+  constexpr std::true_type ragged{};
+  int t = 0;
+  for (; t + 1 < nfull; t += 2) {
+    step(full, s0, s1, offs1, offs0, t);
+    step(full, s1, s0, offs0, offs1, t + 1);
   }
-  if (nfull < ntile && wave_active) compute_tile(std::true_type{}, nfull & 1, 64 * nfull);
+  if (t < nfull) {
+    step(full, s0, s1, offs1, offs0, t);
+    ++t;
+  }
+  if (t < ntile) {
+    if (t & 1) step(ragged, s1, s0, offs0, offs1, t);
+    else step(ragged, s0, s1, offs1, offs0, t);
+  }
 
   // ---- epilogue: normalise, correct (b + x W V^T), restore token order
   const float ltot = l + __shfl_xor(l, 32, 64);
@@ -332,8 +390,8 @@ __global__ __launch_bounds__(256, 2) void k_sparse_attn_mfma(AttnArgs a) {
     for (int r = 0; r < 16; ++r) x[b][r] = o[b][r] * inv;
   const int rank = (a.correct && a.fitrank) ? a.fitrank[bh] : 0;
   if (rank > 0) {
-    float* Wl = reinterpret_cast<float*>(&Ks[0][0]);  // D x 33 floats fit in the K tile buffers
-    float* Vl = reinterpret_cast<float*>(&Vt[0][0]);
+    float* Wl = reinterpret_cast<float*>(KV0);  // D x 33 floats fit in one stage's K tile
+    float* Vl = reinterpret_cast<float*>(KV1);
     float corr[DB][16];
     const float* fb = a.fitb + (long long)bh * D;
 #pragma unroll
