@@ -41,7 +41,9 @@ def parse():
     ap.add_argument("--density", type=float, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
-    ap.add_argument("--profile-runs", type=int, default=3)
+    ap.add_argument("--profile-runs", type=int, default=3, help="calls timed per stage (at least 1)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB three times (counter calibration) and exit")
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic_sparse_attention.json"))
     return ap.parse_args()
 
@@ -89,8 +91,8 @@ def cpu_baseline(x, w, cfg_kw, routed_first_head: int, n: int, d: int, m: int) -
 def main() -> int:
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build measures one GPU only; run with --gpus 1"}))
-        log("only --gpus 1 is supported: every GPU box here has one GPU")
+        print(json.dumps({"error": "the benchmark measures one GPU; multi-GPU runs are not supported (use --gpus 1)"}))
+        log("only --gpus 1 is supported: the call runs on one GPU (heads would shard across GPUs without exchange)")
         return 2
     n_threads = len(os.sched_getaffinity(0))
     for var in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS"):
@@ -103,6 +105,15 @@ def main() -> int:
     if not torch.cuda.is_available():
         log("no GPU visible")
         return 1
+    if args.copy_calibration:
+        nbytes = args.copy_calibration << 20
+        src = torch.ones(nbytes // 2, dtype=torch.bfloat16, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": nbytes, "copies": 3}), flush=True)
+        return 0
     w = workload(args.workload)
     if args.density is not None:
         w = workload(args.workload, density=args.density)
@@ -139,7 +150,7 @@ def main() -> int:
     # per-stage times (HIP events on the library's stream) and statistics
     stage_runs = []
     stats = None
-    for _ in range(args.profile_runs):
+    for _ in range(max(1, args.profile_runs)):
         _, st_ms, st = sp.sparsepr_attention_profile(q, k, v, cfg, out=out, workspace=ws)
         stage_runs.append(st_ms)
         stats = st
