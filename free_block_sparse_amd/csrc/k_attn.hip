@@ -41,7 +41,23 @@ struct AttnArgs {
   int correct;
   int dense;
   const int* vexp;  // V stored as fp16 * 2^-vexp (null: V in the input dtype)
+  int grid_tiles;   // tile slots per head in the launch grid
+  int BH;
 };
+
+// Workgroups are handed to the 8 XCDs round-robin (workgroup i runs on XCD
+// i % 8), and each XCD has its own L2.  Give every XCD one contiguous range of
+// (head, tile) slots so that the workgroups resident on an XCD work on the same
+// head and on neighbouring query groups, whose key ranges overlap.
+constexpr int kXcds = 8;
+__device__ inline void xcd_item(const AttnArgs& a, int* bh, int* tile) {
+  const int total = a.grid_tiles * a.BH;
+  const int per = (total + kXcds - 1) / kXcds;
+  const int i = blockIdx.x;
+  const int logical = (i % kXcds) * per + i / kXcds;
+  *bh = logical / a.grid_tiles;
+  *tile = logical % a.grid_tiles;
+}
 
 __device__ inline int seg_find(const int* sv, int n, int v) {
   int lo = 0, hi = n - 1;
@@ -168,7 +184,10 @@ __global__ __launch_bounds__(256, 2) void k_sparse_attn_mfma(AttnArgs a) {
   __shared__ long long offs0[128], offs1[128];  // element offsets of the K rows, then the V rows
   __shared__ int seg_v[kMaxGroups + 1], seg_p[kMaxGroups + 1];
   __shared__ int tmp[8];
-  const int bh = blockIdx.y, tile = blockIdx.x, tid = threadIdx.x;
+  int bh, tile;
+  xcd_item(a, &bh, &tile);
+  if (bh >= a.BH) return;
+  const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63, half = lane >> 5, col = lane & 31;
   int g, row0, nrows, nseg, L;
   if (!setup_item<4>(a, bh, tile, seg_v, seg_p, tmp, &g, &row0, &nrows, &nseg, &L)) return;
@@ -686,6 +705,235 @@ __global__ __launch_bounds__(256) void k_probe_attn_vec(ProbeArgs a) {
   }
 }
 
+// Probe rows on the matrix cores (bf16 Q/K, fp16-scaled V).  One workgroup
+// of two waves takes 64 probe rows against one chunk of kProbeChunk keys;
+// wave w owns probes 32w..32w+31, one per lane column, and keeps two online
+// softmaxes: dense over every key, and sparse over the keys whose K/V group
+// is granted to the probe's query group.  Both products share each V
+// fragment.  Partials (unnormalised o, reference max in log2 units, sum) are
+// combined across chunks by k_probe_merge.
+template <int D>
+__global__ __launch_bounds__(128, 2) void k_probe_attn_mfma(ProbeArgs a) {
+  constexpr int KS = D / 16, DB = D / 32;
+  constexpr int CPR = D / 8, RPI = 64 / CPR, IPW = 64 / RPI / 2;
+  constexpr int VOFF = 64 * D * 2;
+  constexpr int MW = kMaxGroups / 32;
+  __shared__ __attribute__((aligned(1024))) bf16_t KV0[2 * 64 * D];
+  __shared__ __attribute__((aligned(1024))) bf16_t KV1[2 * 64 * D];
+  __shared__ int kg0[64], kg1[64];
+  __shared__ uint32_t msk[64 * MW];
+  const int bh = blockIdx.z, pb = blockIdx.y, ch = blockIdx.x, tid = threadIdx.x;
+  const int w = tid >> 6, lane = tid & 63, half = lane >> 5, col = lane & 31;
+  const int k0 = ch * kProbeChunk, k1 = min(a.N, k0 + kProbeChunk);
+  const int L = k1 - k0;
+  if (L <= 0) return;
+  // grant masks of the probes' query groups
+  for (int e = tid; e < 64 * a.gwords; e += 128) {
+    const int r = e / a.gwords, wd = e - r * a.gwords;
+    const int pp = pb * 64 + r;
+    msk[r * MW + wd] =
+        pp < a.M ? a.gmask[((long long)bh * a.GQ + a.pgroup[(long long)bh * a.M + pp]) * a.gwords + wd] : 0u;
+  }
+  const int pl = 32 * w + col;
+  const int p = pb * 64 + pl;
+  const bool valid = p < a.M;
+  const bf16_t* qb = static_cast<const bf16_t*>(a.qv.p);
+  const bf16_t* kb = static_cast<const bf16_t*>(a.kv.p);
+  const bf16_t* vb = static_cast<const bf16_t*>(a.vv.p);
+  const int prow = valid ? a.ppos[(long long)bh * a.M + p] : 0;
+  bf16x8 qf[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    uint4 u = make_uint4(0, 0, 0, 0);
+    if (valid) u = *reinterpret_cast<const uint4*>(qb + a.qv.row_off(bh, prow) + 16 * ks + 8 * half);
+    qf[ks] = __builtin_bit_cast(bf16x8, u);
+  }
+  f32x16 od[DB], os[DB];
+#pragma unroll
+  for (int b = 0; b < DB; ++b) {
+    od[b] = f32x16{};
+    os[b] = f32x16{};
+  }
+  float md = -INFINITY, ld = 0.f, ms = -INFINITY, ls = 0.f;
+  const float c = a.scale * 1.4426950408889634f;
+  const int* kgrp = a.kgroup + (long long)bh * a.N;
+
+  typedef __attribute__((address_space(3))) char lds_char;
+  // the keys of a chunk are consecutive rows of the permuted K/V
+  auto issue = [&](lds_char* __restrict__ dst, int tt) {
+#pragma unroll
+    for (int i = 0; i < IPW; ++i) {
+      const int rb = (w * IPW + i) * RPI;
+      const int r = rb + lane / CPR, sl = lane % CPR;
+      const int v = k0 + min(64 * tt + r, L - 1);  // rows past the end are masked
+      const bf16_t* gk = kb + a.kv.row_off(bh, v) + 8 * (sl ^ swz_k<CPR>(r));
+      const bf16_t* gv = vb + a.vv.row_off(bh, v) + 8 * (sl ^ swz_v<CPR>(r));
+      __builtin_amdgcn_global_load_lds(SP_GLB(gk), dst + rb * 2 * D, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(SP_GLB(gv), dst + VOFF + rb * 2 * D, 16, 0, 0);
+    }
+  };
+  const int gi = lane >> 4, li = lane & 15, rr = li >> 2, qq = li & 3;
+  const uint32_t kbase0 = col * 2 * D + 16 * (half ^ swz_k<CPR>(col));
+  const uint32_t vbase0 = VOFF + (4 * (gi >> 1) + rr) * 2 * D + 64 * (swz_v<CPR>(rr) >> 2) +
+                          16 * (2 * (gi & 1) + (qq >> 1)) + 8 * (qq & 1);
+  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+  const h2 one2 = {(_Float16)1.f, (_Float16)1.f};
+
+  auto compute = [&](const lds_char* __restrict__ lds, const int* __restrict__ kgt,
+                     const uint32_t* __restrict__ mrow, int kt0) {
+    uint32_t kb0 = kbase0, vb0 = vbase0;
+    asm volatile("" : "+v"(kb0), "+v"(vb0));
+    f32x16 sacc[2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) sacc[kt] = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const uint32_t ka = kb0 ^ (32u * ks);
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        const bf16x8 kf = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(lds + ka + kt * 32 * 2 * D);
+        sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], sacc[kt], 0, 0, 0);
+      }
+    }
+    // which of this lane's 32 keys are granted to its probe's query group
+    uint32_t amask = 0;
+    const int h0 = kgt[0];
+    if (h0 == kgt[63]) {
+      amask = ((mrow[h0 >> 5] >> (h0 & 31)) & 1u) ? 0xffffffffu : 0u;
+    } else {
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int h = kgt[32 * kt + (r & 3) + 8 * (r >> 2) + 4 * half];
+          amask |= ((mrow[h >> 5] >> (h & 31)) & 1u) << (16 * kt + r);
+        }
+    }
+    float mld = -INFINITY, mls = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = 32 * kt + (r & 3) + 8 * (r >> 2) + 4 * half;
+        float sv = sacc[kt][r];
+        if (kt0 + key >= L) sv = -INFINITY;
+        sacc[kt][r] = sv;
+        mld = fmaxf(mld, sv);
+        if ((amask >> (16 * kt + r)) & 1u) mls = fmaxf(mls, sv);
+      }
+    mld = fmaxf(mld, __shfl_xor(mld, 32, 64)) * c;
+    mls = fmaxf(mls, __shfl_xor(mls, 32, 64)) * c;
+    // lazy rescaling of either reference max (p <= 2^8 stays exact in fp16)
+    if (__builtin_amdgcn_ballot_w64(mld > md + 8.f)) {
+      const float mn = fmaxf(md, mld);
+      const float al = md == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(md - mn);
+      ld *= al;
+#pragma unroll
+      for (int b = 0; b < DB; ++b) od[b] *= al;
+      md = mn;
+    }
+    if (__builtin_amdgcn_ballot_w64(mls > ms + 8.f)) {
+      const float mn = fmaxf(ms, mls);
+      const float al = ms == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ms - mn);
+      ls *= al;
+#pragma unroll
+      for (int b = 0; b < DB; ++b) os[b] *= al;
+      ms = mn;
+    }
+    const float mbd = md == -INFINITY ? 0.f : md;
+    const float mbs = ms == -INFINITY ? 0.f : ms;
+    uint32_t va[DB];
+#pragma unroll
+    for (int b = 0; b < DB; ++b) va[b] = vb0 ^ (64u * b);
+#pragma unroll
+    for (int sp = 0; sp < 4; ++sp) {
+      const int kt = sp >> 1, rb = 8 * (sp & 1);
+      uint32_t pwd[4], pws[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int r0 = rb + 2 * j, r1 = r0 + 1;
+        const float s0 = sacc[kt][r0], s1 = sacc[kt][r1];
+        const float d0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s0, c, -mbd));
+        const float d1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s1, c, -mbd));
+        // ungranted keys get exponent -inf, i.e. probability 0
+        const float x0 = ((amask >> (16 * kt + r0)) & 1u) ? __builtin_fmaf(s0, c, -mbs) : -INFINITY;
+        const float x1 = ((amask >> (16 * kt + r1)) & 1u) ? __builtin_fmaf(s1, c, -mbs) : -INFINITY;
+        const float e0 = __builtin_amdgcn_exp2f(x0);
+        const float e1 = __builtin_amdgcn_exp2f(x1);
+        const h2 hd = {(_Float16)d0, (_Float16)d1};
+        const h2 hs = {(_Float16)e0, (_Float16)e1};
+        pwd[j] = __builtin_bit_cast(uint32_t, hd);
+        pws[j] = __builtin_bit_cast(uint32_t, hs);
+        ld = __builtin_amdgcn_fdot2(hd, one2, ld, false);
+        ls = __builtin_amdgcn_fdot2(hs, one2, ls, false);
+      }
+      const f16x8 pkd = __builtin_bit_cast(f16x8, make_uint4(pwd[0], pwd[1], pwd[2], pwd[3]));
+      const f16x8 pks = __builtin_bit_cast(f16x8, make_uint4(pws[0], pws[1], pws[2], pws[3]));
+#pragma unroll
+      for (int b = 0; b < DB; ++b) {
+        const v4i16 t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            reinterpret_cast<__attribute__((address_space(3))) v4i16*>(const_cast<lds_char*>(lds) + va[b] + sp * 32 * D));
+        const v4i16 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            reinterpret_cast<__attribute__((address_space(3))) v4i16*>(const_cast<lds_char*>(lds) + va[b] + sp * 32 * D + 16 * D));
+        const uint2 u0 = __builtin_bit_cast(uint2, t0), u1 = __builtin_bit_cast(uint2, t1);
+        const f16x8 vv = __builtin_bit_cast(f16x8, make_uint4(u0.x, u0.y, u1.x, u1.y));
+        od[b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vv, pkd, od[b], 0, 0, 0);
+        os[b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vv, pks, os[b], 0, 0, 0);
+      }
+    }
+  };
+
+  lds_char* const s0 = (lds_char*)KV0;
+  lds_char* const s1 = (lds_char*)KV1;
+  const int ntile = (L + 63) / 64;
+  const uint32_t* mrow = msk + pl * MW;
+  // one pipeline step: DMA of tile t+1 and its group ids, compute tile t
+  // the tile's 64 group ids travel by LDS-DMA too (wave 0, 4 bytes a lane)
+  auto issue_groups = [&](int* kgn, int tt) {
+    if (w == 0)
+      __builtin_amdgcn_global_load_lds(SP_GLB(kgrp + k0 + min(64 * tt + lane, L - 1)), SP_LDS(kgn), 4, 0, 0);
+  };
+  auto step = [&](lds_char* cur, lds_char* nxt, const int* kgc, int* kgn, int t) {
+    if (t + 1 < ntile) {
+      issue(nxt, t + 1);
+      issue_groups(kgn, t + 1);
+    }
+    compute(cur, kgc, mrow, 64 * t);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+  };
+  issue_groups(kg0, 0);
+  issue(s0, 0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  for (int t = 0; t < ntile; t += 2) {
+    step(s0, s1, kg0, kg1, t);
+    if (t + 1 < ntile) step(s1, s0, kg1, kg0, t + 1);
+  }
+
+  ld += __shfl_xor(ld, 32, 64);
+  ls += __shfl_xor(ls, 32, 64);
+  if (!valid) return;
+  const float vs = ldexpf(1.0f, a.vexp[bh]);
+  float* base = a.ppart + (((long long)bh * a.n_pchunk + ch) * 2) * a.M * (D + 2);
+  float* pd = base + (long long)p * (D + 2);
+  float* ps = base + ((long long)a.M + p) * (D + 2);
+#pragma unroll
+  for (int b = 0; b < DB; ++b)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int dim = 32 * b + (r & 3) + 8 * (r >> 2) + 4 * half;
+      pd[dim] = od[b][r] * vs;
+      ps[dim] = os[b][r] * vs;
+    }
+  if (half == 0) {
+    pd[D] = md;
+    pd[D + 1] = ld;
+    ps[D] = ms;
+    ps[D + 1] = ls;
+  }
+}
+
 template <int D>
 __global__ __launch_bounds__(D) void k_probe_merge(ProbeArgs a) {
   const int bh = blockIdx.z, which = blockIdx.y, p = blockIdx.x, dm = threadIdx.x;
@@ -753,15 +1001,19 @@ static AttnArgs attn_args(const Plan& p, bool correct) {
   return a;
 }
 
-static hipError_t launch_attn(const AttnArgs& a, int grid_x, int BH, int d, int dtype, hipStream_t s) {
+static hipError_t launch_attn(AttnArgs a, int grid_x, int BH, int d, int dtype, hipStream_t s) {
   dim3 g(grid_x, BH);
   if (dtype == SPARSEPR_BF16) {
+    a.grid_tiles = grid_x;
+    a.BH = BH;
+    const long long total = (long long)grid_x * BH;
+    const dim3 g1((unsigned)((total + kXcds - 1) / kXcds * kXcds));
     if (a.vexp) {
-      if (d == 128) hipLaunchKernelGGL((k_sparse_attn_mfma<128, true>), g, dim3(256), 0, s, a);
-      else hipLaunchKernelGGL((k_sparse_attn_mfma<64, true>), g, dim3(256), 0, s, a);
+      if (d == 128) hipLaunchKernelGGL((k_sparse_attn_mfma<128, true>), g1, dim3(256), 0, s, a);
+      else hipLaunchKernelGGL((k_sparse_attn_mfma<64, true>), g1, dim3(256), 0, s, a);
     } else {
-      if (d == 128) hipLaunchKernelGGL((k_sparse_attn_mfma<128, false>), g, dim3(256), 0, s, a);
-      else hipLaunchKernelGGL((k_sparse_attn_mfma<64, false>), g, dim3(256), 0, s, a);
+      if (d == 128) hipLaunchKernelGGL((k_sparse_attn_mfma<128, false>), g1, dim3(256), 0, s, a);
+      else hipLaunchKernelGGL((k_sparse_attn_mfma<64, false>), g1, dim3(256), 0, s, a);
     }
   } else {
     if (d == 128) hipLaunchKernelGGL((k_sparse_attn_vec<float, 128>), g, dim3(512), 0, s, a);
@@ -813,8 +1065,8 @@ hipError_t launch_probe_attention(const Plan& p, hipStream_t s) {
   dim3 g(p.n_pchunk, (p.M + 63) / 64, p.BH);
   if (p.dtype == SPARSEPR_BF16) {
     a.vexp = p.vexp;
-    if (p.d == 128) hipLaunchKernelGGL((k_probe_attn_vec<bf16_t, _Float16, 128>), g, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((k_probe_attn_vec<bf16_t, _Float16, 64>), g, dim3(256), 0, s, a);
+    if (p.d == 128) hipLaunchKernelGGL((k_probe_attn_mfma<128>), g, dim3(128), 0, s, a);
+    else hipLaunchKernelGGL((k_probe_attn_mfma<64>), g, dim3(128), 0, s, a);
   } else {
     a.vexp = nullptr;
     if (p.d == 128) hipLaunchKernelGGL((k_probe_attn_vec<float, float, 128>), g, dim3(256), 0, s, a);

@@ -11,7 +11,7 @@ namespace sp {
 
 constexpr int kChunk = 256;      // points per k-means assignment workgroup
 constexpr int kTileRows = 128;   // query rows per sparse-attention workgroup
-constexpr int kProbeChunk = 2048;  // keys per probe-attention workgroup
+constexpr int kProbeChunk = 1024;  // keys per probe-attention workgroup
 constexpr int kMaxProbe = 256;
 constexpr int kMaxRank = 64;
 constexpr int kMaxGroups = 1024;
