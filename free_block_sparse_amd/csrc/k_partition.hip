@@ -307,6 +307,81 @@ __global__ __launch_bounds__(256) void k_key_coords(CoordArgs a) {
   }
 }
 
+// bf16 keys on the matrix cores: z^T = kmap^T K^T with kmap split into three
+// bf16 pieces (24 significant bits, like fp32); products with bf16 keys are
+// exact and accumulate in fp32.  Each wave takes 32-token blocks; lanes hold
+// the map as the A operand for up to two blocks of 32 coordinates.
+template <int D>
+__global__ __launch_bounds__(256) void k_key_coords_mfma(CoordArgs a) {
+  constexpr int KS = D / 16;
+  const int bh = blockIdx.y, tid = threadIdx.x;
+  const int w = tid >> 6, lane = tid & 63, half = lane >> 5, col = lane & 31;
+  const int rK = a.rK, rKpad = a.rKpad, N = a.N;
+  const int ncb = (rK + 31) / 32;
+  const float* kmap = a.kmap + (long long)bh * D * rK;
+  bf16x8 mp[3][2][KS];
+#pragma unroll
+  for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      bf16_t pv[3][8];
+      const int cc = 32 * cb + col;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        float x = (cb < ncb && cc < rK) ? kmap[(16 * ks + 8 * half + j) * rK + cc] : 0.f;
+#pragma unroll
+        for (int q = 0; q < 3; ++q) {
+          pv[q][j] = f32_to_bf16(x);
+          x -= bf16_to_f32(pv[q][j]);
+        }
+      }
+#pragma unroll
+      for (int q = 0; q < 3; ++q) mp[q][cb][ks] = *reinterpret_cast<const bf16x8*>(pv[q]);
+    }
+  const bf16_t* kb = static_cast<const bf16_t*>(a.k.p);
+  for (int blk = 0; blk < 2; ++blk) {
+    const int n0 = blockIdx.x * 256 + 64 * w + 32 * blk;
+    if (n0 >= N) break;
+    const int n = n0 + col;
+    bf16x8 kf[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      uint4 u = make_uint4(0, 0, 0, 0);
+      if (n < N) u = *reinterpret_cast<const uint4*>(kb + a.k.row_off(bh, n) + 16 * ks + 8 * half);
+      kf[ks] = __builtin_bit_cast(bf16x8, u);
+    }
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) {
+      if (cb >= ncb) break;
+      f32x16 acc = {};
+      // smallest pieces first
+#pragma unroll
+      for (int q = 2; q >= 0; --q)
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(mp[q][cb][ks], kf[ks], acc, 0, 0, 0);
+      if (n >= N) continue;
+      const long long zrow = ((long long)bh * N + n) * rKpad;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int c = 32 * cb + 8 * q + 4 * half;  // coordinates c..c+3 of token n
+        if (c >= rKpad) continue;
+        float4 zf;
+        bf16_t hv[4], lv[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float x = acc[4 * q + i];
+          (&zf.x)[i] = x;
+          hv[i] = f32_to_bf16(x);
+          lv[i] = f32_to_bf16(x - bf16_to_f32(hv[i]));
+        }
+        *reinterpret_cast<float4*>(a.z32 + zrow + c) = zf;
+        *reinterpret_cast<uint2*>(a.zhi + zrow + c) = *reinterpret_cast<const uint2*>(hv);
+        *reinterpret_cast<uint2*>(a.zlo + zrow + c) = *reinterpret_cast<const uint2*>(lv);
+      }
+    }
+  }
+}
+
 // fp32 raw rows -> hi/lo bf16 pair (fp32 inputs only)
 __global__ __launch_bounds__(256) void k_split_rows(SplitArgs a) {
   const int bh = blockIdx.y;
@@ -452,17 +527,28 @@ __global__ __launch_bounds__(256) void k_count_labels(CountArgs a) {
 // a5: counting sort -- chunk offsets (group-major, chunk-minor) and stable scatter
 // ============================================================================
 __global__ __launch_bounds__(1024) void k_group_scan(ScanArgs a) {
+  __shared__ int part[1024];
   __shared__ int tot[kMaxGroups];
   const int bh = blockIdx.x, tid = threadIdx.x;
   const int G = a.G, nch = a.nchunk;
+  // P threads per group, each over a contiguous range of chunks
+  const int P = 1024 / G;  // G <= kMaxGroups = 1024
+  const int g = tid % G, pt = tid / G;
+  const bool act = pt < P;
+  const int c0 = act ? (int)((long long)pt * nch / P) : 0;
+  const int c1 = act ? (int)((long long)(pt + 1) * nch / P) : 0;
   const int* cnt = a.counts + (long long)bh * nch * a.gstride;
-  for (int g = tid; g < G; g += 1024) {
-    int s = 0;
-    for (int c = 0; c < nch; ++c) s += cnt[(long long)c * a.gstride + g];
-    tot[g] = s;
+  int sum = 0;
+  for (int c = c0; c < c1; ++c) sum += cnt[(long long)c * a.gstride + g];
+  if (act) part[pt * G + g] = sum;
+  __syncthreads();
+  if (tid < G) {
+    int t = 0;
+    for (int q = 0; q < P; ++q) t += part[q * G + tid];
+    tot[tid] = t;
   }
   __syncthreads();
-  // inclusive Hillis-Steele scan over G <= 1024 entries
+  // inclusive Hillis-Steele scan over the G group totals
   for (int o = 1; o < G; o <<= 1) {
     int v = 0;
     if (tid < G && tid >= o) v = tot[tid - o];
@@ -470,29 +556,47 @@ __global__ __launch_bounds__(1024) void k_group_scan(ScanArgs a) {
     if (tid < G) tot[tid] += v;
     __syncthreads();
   }
+  if (!act) return;
+  int base = g == 0 ? 0 : tot[g - 1];
   int* off = a.off + (long long)bh * a.offstride;
-  int* co = a.chunkoff + (long long)bh * nch * a.gstride;
-  for (int g = tid; g < G; g += 1024) {
-    int base = g == 0 ? 0 : tot[g - 1];
-    off[g] = base;
-    for (int c = 0; c < nch; ++c) {
-      co[(long long)c * a.gstride + g] = base;
-      base += cnt[(long long)c * a.gstride + g];
-    }
-  }
+  if (pt == 0) off[g] = base;
   if (tid == 0) off[G] = a.N;
+  for (int q = 0; q < pt; ++q) base += part[q * G + g];
+  int* co = a.chunkoff + (long long)bh * nch * a.gstride;
+  for (int c = c0; c < c1; ++c) {
+    co[(long long)c * a.gstride + g] = base;
+    base += cnt[(long long)c * a.gstride + g];
+  }
 }
 
+// Stable scatter of one chunk: the rank of a point among the earlier points
+// of its chunk with the same label.  Inside a wave, lanes with equal labels
+// are matched with one ballot per distinct label; earlier waves contribute
+// their per-label counts.
 __global__ __launch_bounds__(256) void k_group_scatter(ScatterArgs a) {
-  __shared__ int lab[kChunk];
+  __shared__ int hist[4][kMaxGroups];
   const int bh = blockIdx.y, chunk = blockIdx.x, tid = threadIdx.x;
-  const int n = chunk * kChunk + tid;
-  lab[tid] = n < a.N ? a.labels[(long long)bh * a.N + n] : -1;
+  const int w = tid >> 6, lane = tid & 63;
+  for (int e = tid; e < 4 * a.gstride; e += 256) hist[e / a.gstride][e % a.gstride] = 0;
   __syncthreads();
-  if (n >= a.N) return;
-  const int my = lab[tid];
+  const int n = chunk * kChunk + tid;
+  const int my = n < a.N ? a.labels[(long long)bh * a.N + n] : -1;
+  const unsigned long long lt = (1ull << lane) - 1ull;
+  unsigned long long todo = __builtin_amdgcn_ballot_w64(my >= 0);
   int rank = 0;
-  for (int j = 0; j < tid; ++j) rank += lab[j] == my;
+  while (todo) {
+    const int leader = __builtin_ctzll(todo);
+    const int lab = __builtin_amdgcn_readlane(my, leader);
+    const unsigned long long m = __builtin_amdgcn_ballot_w64(my == lab);
+    if (my == lab) {
+      rank = __builtin_popcountll(m & lt);
+      if (lane == leader) hist[w][lab] = __builtin_popcountll(m);
+    }
+    todo &= ~m;
+  }
+  __syncthreads();
+  if (my < 0) return;
+  for (int q = 0; q < w; ++q) rank += hist[q][my];
   const int pos = a.chunkoff[((long long)bh * a.nchunk + chunk) * a.gstride + my] + rank;
   a.perm[(long long)bh * a.N + pos] = n;
   if (a.out_labels) a.out_labels[(long long)bh * a.N + n] = my;
@@ -505,43 +609,46 @@ __global__ __launch_bounds__(256) void k_group_scatter(ScatterArgs a) {
 // previous centre.
 // ============================================================================
 template <typename TP>
-__global__ __launch_bounds__(128) void k_group_mean(UpdateArgs a) {
-  constexpr int CH = 64;
-  __shared__ float rows[CH][129];
-  __shared__ int idx[CH];
+__global__ __launch_bounds__(256) void k_group_mean(UpdateArgs a) {
+  constexpr int NT = 256;
+  __shared__ double part[NT];
   const int bh = blockIdx.y, g = blockIdx.x, tid = threadIdx.x;
   const int Dp = a.Dp;
   const TP* xb = static_cast<const TP*>(a.pts.p);
   double* cm = a.cmean ? a.cmean + ((long long)bh * a.gstride + g) * a.cstride : nullptr;
   if (a.init) {
     const long long sidx = ((2LL * g + 1) * a.N) / (2LL * a.G);
-    for (int j = tid; j < Dp; j += 128) cm[j] = (double)Elem<TP>::load(xb + a.pts.row_off(bh, sidx) + j);
+    for (int j = tid; j < Dp; j += NT) cm[j] = (double)Elem<TP>::load(xb + a.pts.row_off(bh, sidx) + j);
     return;
   }
   const int* off = a.off + (long long)bh * a.offstride;
   const int* perm = a.perm + (long long)bh * a.N;
   const int a0 = off[g], a1 = off[g + 1];
   const int n_g = a1 - a0;
+  // The means handed to the router (means_out) are summed one row after
+  // another in ascending token order, as the reference computation does.
+  // Inside the Lloyd iterations each dimension is split over P fixed,
+  // interleaved row subsets whose sums are added in a fixed order, so the
+  // result is still deterministic.  Each thread reads its own dimension of
+  // the member rows directly, eight rows in flight.
+  const int P = a.means_out ? 1 : max(1, NT / Dp);
+  const int j = tid % Dp, pt = tid / Dp;
   double s = 0.0;
-  constexpr int VEC = 16 / sizeof(TP);
-  const int cpr = (Dp + VEC - 1) / VEC;  // rows are padded to a 16-byte multiple
-  for (int m0 = a0; m0 < a1; m0 += CH) {
-    const int nr = min(CH, a1 - m0);
-    __syncthreads();
-    if (tid < nr) idx[tid] = perm[m0 + tid];
-    __syncthreads();
-    for (int e = tid; e < nr * cpr; e += 128) {
-      const int r = e / cpr, c = (e - (e / cpr) * cpr) * VEC;
-      const uint4 u = *reinterpret_cast<const uint4*>(xb + a.pts.row_off(bh, idx[r]) + c);
-      const TP* ev = reinterpret_cast<const TP*>(&u);
+  if (pt < P) {
+    int r = a0 + pt;
+    for (; r + 7 * P < a1; r += 8 * P) {
+      float v[8];
 #pragma unroll
-      for (int j = 0; j < VEC; ++j) rows[r][c + j] = Elem<TP>::load(ev + j);
+      for (int u = 0; u < 8; ++u) v[u] = Elem<TP>::load(xb + a.pts.row_off(bh, perm[r + u * P]) + j);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) s = __dadd_rn(s, (double)v[u]);
     }
-    __syncthreads();
-    if (tid < Dp)
-      for (int r = 0; r < nr; ++r) s = __dadd_rn(s, (double)rows[r][tid]);
+    for (; r < a1; r += P) s = __dadd_rn(s, (double)Elem<TP>::load(xb + a.pts.row_off(bh, perm[r]) + j));
   }
+  part[tid] = s;
+  __syncthreads();
   if (tid >= Dp) return;
+  for (int q = 1; q < P; ++q) s = __dadd_rn(s, part[q * Dp + tid]);
   double mean;
   if (n_g > 0) {
     mean = s / (double)n_g;
@@ -554,11 +661,13 @@ __global__ __launch_bounds__(128) void k_group_mean(UpdateArgs a) {
 }
 
 // centre update, step 2: image y = M mean (or the mean itself), stored as a
-// hi/lo bf16 pair, and bias mean . y; 16 groups per workgroup share M.
+// hi/lo bf16 pair, and bias mean . y (fp64 accumulation).
+// 16 groups per workgroup; 16 threads per group, each owning every 16th
+// dimension; M is staged through LDS 32 rows at a time.
 __global__ __launch_bounds__(256) void k_centre_images(UpdateArgs a) {
-  constexpr int GB = 16;
-  __shared__ double smean[GB][128];
-  __shared__ double sprod[GB][128];
+  constexpr int GB = 16, MR = 32;
+  __shared__ double smean[GB][129];
+  __shared__ float sm[MR][129];
   const int bh = blockIdx.y, g0 = blockIdx.x * GB, tid = threadIdx.x;
   const int Dp = a.Dp, Dimg = a.Dimg;
   const int ng = min(GB, a.G - g0);
@@ -566,33 +675,57 @@ __global__ __launch_bounds__(256) void k_centre_images(UpdateArgs a) {
     const int gl = e >> 7, j = e & 127;
     smean[gl][j] = (gl < ng && j < Dp) ? a.cmean[((long long)bh * a.gstride + g0 + gl) * a.cstride + j] : 0.0;
   }
-  __syncthreads();
+  const int gl = tid >> 4, jj = tid & 15;
   const float* M = a.metric ? a.metric + (long long)bh * Dp * Dp : nullptr;
-  for (int e = tid; e < GB * Dimg; e += 256) {
-    const int gl = e / Dimg, j = e - (e / Dimg) * Dimg;
-    double y = 0.0;
-    if (gl < ng && j < Dp) {
-      if (M) {
-        for (int k = 0; k < Dp; ++k) y += (double)M[k * Dp + j] * smean[gl][k];
-      } else {
-        y = smean[gl][j];
+  double y[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) y[k] = 0.0;
+  __syncthreads();
+  if (M) {
+    for (int i0 = 0; i0 < Dp; i0 += MR) {
+      const int nr = min(MR, Dp - i0);
+      __syncthreads();
+      for (int e = tid; e < nr * Dp; e += 256) {
+        const int r = e / Dp, c = e - (e / Dp) * Dp;
+        sm[r][c] = M[(long long)(i0 + r) * Dp + c];
+      }
+      __syncthreads();
+      for (int r = 0; r < nr; ++r) {
+        const double mv = smean[gl][i0 + r];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const int j = jj + 16 * k;
+          if (j < Dp) y[k] = __builtin_fma((double)sm[r][j], mv, y[k]);
+        }
       }
     }
-    if (j < 128) sprod[gl][j] = (j < Dp) ? y * smean[gl][j] : 0.0;
-    if (gl < ng) {
-      const long long yo = ((long long)bh * a.gstride + g0 + gl) * a.ystride + j;
-      const float yf = (float)y;
-      const bf16_t hi = f32_to_bf16(yf);
-      a.yhi[yo] = hi;
-      a.ylo[yo] = f32_to_bf16(yf - bf16_to_f32(hi));
+  } else {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int j = jj + 16 * k;
+      y[k] = j < Dp ? smean[gl][j] : 0.0;
     }
   }
-  __syncthreads();
-  if (tid < ng) {
-    double b = 0.0;
-    for (int k = 0; k < Dp; ++k) b += sprod[tid][k];
-    a.ybias[(long long)bh * a.gstride + g0 + tid] = (float)b;
+  double b = 0.0;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const int j = jj + 16 * k;
+    if (j < Dp) b = __builtin_fma(y[k], smean[gl][j], b);
   }
+  for (int o = 8; o > 0; o >>= 1) b += __shfl_xor(b, o, 16);
+  if (gl >= ng) return;
+  const long long yo = ((long long)bh * a.gstride + g0 + gl) * a.ystride;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const int j = jj + 16 * k;
+    if (j < Dimg) {
+      const float yf = j < Dp ? (float)y[k] : 0.f;
+      const bf16_t hi = f32_to_bf16(yf);
+      a.yhi[yo + j] = hi;
+      a.ylo[yo + j] = f32_to_bf16(yf - bf16_to_f32(hi));
+    }
+  }
+  if (jj == 0) a.ybias[(long long)bh * a.gstride + g0 + gl] = (float)b;
 }
 
 // M_Q = s^2 sum over non-empty key groups of cbar_h cbar_h^T (d x d per (b,h));
@@ -758,8 +891,9 @@ hipError_t launch_key_coords(const Plan& p, hipStream_t s) {
   CoordArgs a{p.k, p.kmap, p.N, p.rK, p.rKpad, p.z32, p.zhi, p.zlo};
   dim3 g((p.N + 63) / 64, p.BH);
   if (p.dtype == SPARSEPR_BF16) {
-    if (p.d == 128) SP_LAUNCH((k_key_coords<bf16_t, 128>), g, dim3(256), s, a);
-    else SP_LAUNCH((k_key_coords<bf16_t, 64>), g, dim3(256), s, a);
+    const dim3 gm((p.N + 255) / 256, p.BH);
+    if (p.d == 128) SP_LAUNCH((k_key_coords_mfma<128>), gm, dim3(256), s, a);
+    else SP_LAUNCH((k_key_coords_mfma<64>), gm, dim3(256), s, a);
   } else {
     if (p.d == 128) SP_LAUNCH((k_key_coords<float, 128>), g, dim3(256), s, a);
     else SP_LAUNCH((k_key_coords<float, 64>), g, dim3(256), s, a);
@@ -814,8 +948,8 @@ hipError_t launch_group_scatter(const Plan& p, const ScatterArgs& a, hipStream_t
 
 hipError_t launch_centre_update(const Plan& p, const UpdateArgs& a, int pts_type, hipStream_t s) {
   dim3 g(a.G, p.BH);
-  if (pts_type == 0) SP_LAUNCH(k_group_mean<bf16_t>, g, dim3(128), s, a);
-  else SP_LAUNCH(k_group_mean<float>, g, dim3(128), s, a);
+  if (pts_type == 0) SP_LAUNCH(k_group_mean<bf16_t>, g, dim3(256), s, a);
+  else SP_LAUNCH(k_group_mean<float>, g, dim3(256), s, a);
   if (a.means_only) return hipSuccess;
   SP_LAUNCH(k_centre_images, dim3((a.G + 15) / 16, p.BH), dim3(256), s, a);
   return hipSuccess;
