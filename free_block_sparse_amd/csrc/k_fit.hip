@@ -14,12 +14,13 @@
 // Computation (readings: unweighted uncentred SVD of R; weighted least squares
 // with an unpenalised intercept; lambda relative to the mean eigenvalue of
 // Xc^T D Xc unless the absolute mode is asked for):
-//   Gram of R (the smaller side) -> Jacobi eigen -> sigma, right singular
+//   Gram of R (the smaller side) -> symmetric eigensolver -> sigma, right singular
 //   vectors V (r' = min(r, M, d, #{sigma > cut sigma_1}));  Y = R V;
 //   weighted means xbar, ybar;  W = (Xc^T D Xc + lambda I)^-1 Xc^T D Yc, solved
 //   in the M x M dual form when M <= d;  b = (ybar - xbar W) V^T.
 // All matrices live in a per-(b,h) global scratch slice (L2 resident).
 #include "sp_kernels.h"
+#include "sp_eig.h"
 
 namespace sp {
 
@@ -124,49 +125,92 @@ __device__ void jacobi_sym_f64(double* A, double* V, int n, double* rcs, int* rp
 
 // In-place Cholesky (lower) of an SPD n x n matrix; returns false on a
 // non-positive pivot.  All threads call it.
-__device__ bool cholesky_f64(double* K, int n, int* bad) {
+__device__ bool cholesky_f64(double* K, int n, int ld, int* bad) {
   const int tid = threadIdx.x, nt = blockDim.x;
   if (tid == 0) *bad = 0;
   block_sync();
   for (int k = 0; k < n; ++k) {
     if (tid == 0) {
-      const double piv = K[k * n + k];
+      const double piv = K[k * ld + k];
       if (!(piv > 0.0)) *bad = 1;
-      K[k * n + k] = sqrt(piv > 0.0 ? piv : 1.0);
+      K[k * ld + k] = sqrt(piv > 0.0 ? piv : 1.0);
     }
     block_sync();
-    const double lkk = K[k * n + k];
-    for (int i = k + 1 + tid; i < n; i += nt) K[i * n + k] /= lkk;
+    const double lkk = K[k * ld + k];
+    for (int i = k + 1 + tid; i < n; i += nt) K[i * ld + k] /= lkk;
     block_sync();
     const int m = n - k - 1;
     for (int e = tid; e < m * m; e += nt) {
       const int i = k + 1 + e / m, j = k + 1 + e % m;
-      if (j <= i) K[i * n + j] -= K[i * n + k] * K[j * n + k];
+      if (j <= i) K[i * ld + j] -= K[i * ld + k] * K[j * ld + k];
     }
     block_sync();
   }
   return *bad == 0;
 }
 
-__global__ __launch_bounds__(256) void k_fit(FitArgs a) {
-  // LDS path for M <= 64 (R and Xc staged as fp32, Gram and eigenvectors fp64);
-  // larger probe budgets use the per-(b,h) global scratch slice instead.
-  constexpr int SM = 64;
-  __shared__ float Rl[SM * 128];
-  __shared__ float Xl[SM * 128];
-  __shared__ double Gl[SM * SM];
-  __shared__ double Ul[SM * SM];
+// Solve L L^T Y = Y in place for the nc columns of Y (row stride ldy), with
+// the lower Cholesky factor L (row stride ld).  Column-parallel: one pivot
+// at a time, its row scaled, then eliminated from the remaining rows.
+__device__ void chol_solve_f64(const double* L, int n, int ld, double* Y, int nc, int ldy) {
+  const int tid = threadIdx.x, nt = blockDim.x;
+  for (int j = 0; j < n; ++j) {
+    for (int c = tid; c < nc; c += nt) Y[j * ldy + c] /= L[j * ld + j];
+    block_sync();
+    for (int e = tid; e < (n - 1 - j) * nc; e += nt) {
+      const int i = j + 1 + e / nc, c = e - (e / nc) * nc;
+      Y[i * ldy + c] -= L[i * ld + j] * Y[j * ldy + c];
+    }
+    block_sync();
+  }
+  for (int i = n - 1; i >= 0; --i) {
+    for (int c = tid; c < nc; c += nt) Y[i * ldy + c] /= L[i * ld + i];
+    block_sync();
+    for (int e = tid; e < i * nc; e += nt) {
+      const int j = e / nc, c = e - (e / nc) * nc;
+      Y[j * ldy + c] -= L[i * ld + j] * Y[i * ldy + c];
+    }
+    block_sync();
+  }
+}
+
+// Sum over the workgroup (every thread gets the result); red holds one
+// double per wave.
+__device__ double block_sum_d(double v, double* red) {
+  const int tid = threadIdx.x, nw = blockDim.x >> 6;
+  v = wave_sum_d(v);
+  block_sync();
+  if ((tid & 63) == 0) red[tid >> 6] = v;
+  block_sync();
+  double t = 0.0;
+  for (int w = 0; w < nw; ++w) t += red[w];
+  return t;
+}
+
+constexpr int kFitThreads = 1024;
+
+__global__ __launch_bounds__(1024) void k_fit(FitArgs a) {
+  // LDS path for M <= 64: R and X as fp32 rows of stride d + 1, the Gram /
+  // ridge system and eigenvectors as fp64 rows of stride 65 (odd strides keep
+  // column walks on distinct banks).  Larger probe budgets use the
+  // per-(b,h) global scratch slice with unpadded strides.
+  constexpr int SM = 64, SLX = 129, SLG = SM + 1;
+  __shared__ float Rl[SM * SLX];
+  __shared__ float Xl[SM * SLX];
+  __shared__ double Gl[SM * SLG];
+  __shared__ double Ul[SM * SLG];
   __shared__ double rcs[2 * 64];
   __shared__ int rpq[2 * 64];
-  __shared__ double red[8];
+  __shared__ double red[32];
   __shared__ int stop, bad;
   __shared__ double sig_s[kMaxProbe + 1];
   __shared__ int idx_s[kMaxProbe + 1];
   __shared__ int rk_s;
-  __shared__ double wsum_s, lam_s;
   __shared__ double xb[128];
   __shared__ double yb[64];
   __shared__ double bp[64];
+  __shared__ double edg[128 + 2], eeo[64 + 2], etau[64], evb[64], epb[64], erot[4 * 64];
+  __shared__ int ectl[8];
   const int bh = blockIdx.x, tid = threadIdx.x, nt = blockDim.x;
   const int M = a.M, d = a.d, Rmax = a.R;  // Rmax: column stride of the W and V outputs
   double* S = a.scratch + (long long)bh * kFitScratch;
@@ -174,10 +218,13 @@ __global__ __launch_bounds__(256) void k_fit(FitArgs a) {
   const int n = small ? M : d;
   const int ne = n + (n & 1);
   const bool lds = M <= SM;
+  const int ldx = lds ? SLX : d;
+  const bool glds = ne <= SM;
+  const int ldg = glds ? SLG : ne;
   float* Rf = lds ? Rl : reinterpret_cast<float*>(S);                        // M x d
   float* Xf = lds ? Xl : reinterpret_cast<float*>(S) + 256 * 128;            // M x d (centred below)
-  double* G = ne <= SM ? Gl : S + 256 * 128;                                 // ne x ne, later the ridge system
-  double* U = ne <= SM ? Ul : S + 256 * 128 + 128 * 128;                     // ne x ne
+  double* G = glds ? Gl : S + 256 * 128;                                     // ne x ne, later the ridge system
+  double* U = glds ? Ul : S + 256 * 128 + 128 * 128;                         // ne x ne
   double* Vr = S + 256 * 128 + 2 * 128 * 128;                                // d x Rmax
   double* Wm = Vr + 128 * 64;                                                // d x rk (also the primal rhs)
   double* Yc = Wm + 128 * 64;                                                // M x rk
@@ -187,40 +234,48 @@ __global__ __launch_bounds__(256) void k_fit(FitArgs a) {
   const double* w = a.pw + (long long)bh * M;
 
   for (int e = tid; e < M * d; e += nt) {
-    Rf[e] = ode[e] - osp[e];
-    Xf[e] = osp[e];
+    const int mm = e / d, dm = e - (e / d) * d;
+    Rf[mm * ldx + dm] = ode[e] - osp[e];
+    Xf[mm * ldx + dm] = osp[e];
   }
-  if (tid == 0) {
-    double ws = 0.0;
-    for (int i = 0; i < M; ++i) ws += w[i];
-    wsum_s = ws;
-  }
-  block_sync();
-  const double ws = wsum_s;
+  double wpart = 0.0;
+  for (int i = tid; i < M; i += nt) wpart += w[i];
+  const double ws = block_sum_d(wpart, red);
   for (int dm = tid; dm < d; dm += nt) {
     double acc = 0.0;
-    for (int mm = 0; mm < M; ++mm) acc += w[mm] * (double)Xf[mm * d + dm];
+    for (int mm = 0; mm < M; ++mm) acc += w[mm] * (double)Xf[mm * ldx + dm];
     xb[dm] = acc / ws;
   }
+  // Gram of the smaller side of R
   for (int e = tid; e < ne * ne; e += nt) {
     const int i = e / ne, j = e - (e / ne) * ne;
     double acc = 0.0;
     if (i < n && j < n) {
       if (small)
-        for (int k = 0; k < d; ++k) acc += (double)Rf[i * d + k] * (double)Rf[j * d + k];
+        for (int k = 0; k < d; ++k) acc += (double)Rf[i * ldx + k] * (double)Rf[j * ldx + k];
       else
-        for (int mm = 0; mm < M; ++mm) acc += (double)Rf[mm * d + i] * (double)Rf[mm * d + j];
+        for (int mm = 0; mm < M; ++mm) acc += (double)Rf[mm * ldx + i] * (double)Rf[mm * ldx + j];
     }
-    G[e] = acc;
+    G[i * ldg + j] = acc;
   }
   block_sync();
-  jacobi_sym_f64(G, U, ne, rcs, rpq, &stop, red);
+  if (glds) {
+    // Householder tridiagonalisation + shifted QR, everything in LDS
+    const EigWork<double> ew{G, ldg, U, ldg, edg, eeo, etau, evb, epb, erot, ectl};
+    eig_tridiagonalize<double, kFitThreads>(ew, ne);
+    eig_tridiagonal_qr<double, kFitThreads>(ew, ne);
+    eig_back_transform<double, kFitThreads, 16>(ew, ne, nullptr, ne);
+  } else {
+    jacobi_sym_f64(G, U, ne, rcs, rpq, &stop, red);
+    for (int i = tid; i < ne; i += nt) edg[i] = G[i * ne + i];
+    block_sync();
+  }
   // eigenvalues, descending with ties by index
   for (int i = tid; i < ne; i += nt) {
-    const double li = G[i * ne + i];
+    const double li = edg[i];
     int r = 0;
     for (int j = 0; j < ne; ++j) {
-      const double lj = G[j * ne + j];
+      const double lj = edg[j];
       r += (lj > li) || (lj == li && j < i);
     }
     sig_s[r] = sqrt(li > 0.0 ? li : 0.0);
@@ -248,10 +303,10 @@ __global__ __launch_bounds__(256) void k_fit(FitArgs a) {
     double v;
     if (small) {
       double acc = 0.0;
-      for (int mm = 0; mm < M; ++mm) acc += (double)Rf[mm * d + dm] * U[mm * ne + ci];
+      for (int mm = 0; mm < M; ++mm) acc += (double)Rf[mm * ldx + dm] * U[mm * ldg + ci];
       v = acc / sig_s[k];
     } else {
-      v = U[dm * ne + ci];
+      v = U[dm * ldg + ci];
     }
     Vr[dm * Rmax + k] = v;
   }
@@ -260,7 +315,7 @@ __global__ __launch_bounds__(256) void k_fit(FitArgs a) {
   for (int e = tid; e < M * rk; e += nt) {
     const int mm = e / rk, k = e - (e / rk) * rk;
     double acc = 0.0;
-    for (int dm = 0; dm < d; ++dm) acc += (double)Rf[mm * d + dm] * Vr[dm * Rmax + k];
+    for (int dm = 0; dm < d; ++dm) acc += (double)Rf[mm * ldx + dm] * Vr[dm * Rmax + k];
     Yc[mm * rk + k] = acc;
   }
   block_sync();
@@ -269,28 +324,24 @@ __global__ __launch_bounds__(256) void k_fit(FitArgs a) {
     for (int mm = 0; mm < M; ++mm) acc += w[mm] * Yc[mm * rk + k];
     yb[k] = acc / ws;
   }
-  for (int e = tid; e < M * d; e += nt) Xf[e] = (float)((double)Xf[e] - xb[e % d]);
+  for (int e = tid; e < M * d; e += nt) {
+    const int mm = e / d, dm = e - (e / d) * d;
+    Xf[mm * ldx + dm] = (float)((double)Xf[mm * ldx + dm] - xb[dm]);
+  }
   block_sync();
   for (int e = tid; e < M * rk; e += nt) Yc[e] -= yb[e % rk];
   // ridge strength (relative: lambda times the mean eigenvalue of Xc^T D Xc)
-  if (tid == 0) {
-    double lam = a.lambda;
-    if (a.relative) {
-      double tr = 0.0;
-      for (int mm = 0; mm < M; ++mm) {
-        double s2 = 0.0;
-        for (int dm = 0; dm < d; ++dm) {
-          const double t = (double)Xf[mm * d + dm];
-          s2 += t * t;
-        }
-        tr += w[mm] * s2;
-      }
-      lam *= tr / (double)d;
+  double lam = a.lambda;
+  if (a.relative) {
+    double tpart = 0.0;
+    for (int e = tid; e < M * d; e += nt) {
+      const int mm = e / d, dm = e - (e / d) * d;
+      const double t = (double)Xf[mm * ldx + dm];
+      tpart += w[mm] * t * t;
     }
-    lam_s = lam;
+    lam *= block_sum_d(tpart, red) / (double)d;
   }
   block_sync();
-  const double lam = lam_s;
   bool ok = rk > 0;
   if (rk > 0) {
     if (small) {
@@ -299,30 +350,18 @@ __global__ __launch_bounds__(256) void k_fit(FitArgs a) {
       for (int e = tid; e < M * M; e += nt) {
         const int i = e / M, j = e - (e / M) * M;
         double acc = 0.0;
-        for (int dm = 0; dm < d; ++dm) acc += (double)Xf[i * d + dm] * (double)Xf[j * d + dm];
-        K[e] = sqrt(w[i] * w[j]) * acc + (i == j ? lam : 0.0);
+        for (int dm = 0; dm < d; ++dm) acc += (double)Xf[i * ldx + dm] * (double)Xf[j * ldx + dm];
+        K[i * ldg + j] = sqrt(w[i] * w[j]) * acc + (i == j ? lam : 0.0);
       }
       for (int e = tid; e < M * rk; e += nt) Yc[e] *= sqrt(w[e / rk]);
       block_sync();
-      ok = cholesky_f64(K, M, &bad);
+      ok = cholesky_f64(K, M, ldg, &bad);
       if (ok) {
-        for (int k = tid; k < rk; k += nt) {
-          for (int i = 0; i < M; ++i) {
-            double sacc = Yc[i * rk + k];
-            for (int j = 0; j < i; ++j) sacc -= K[i * M + j] * Yc[j * rk + k];
-            Yc[i * rk + k] = sacc / K[i * M + i];
-          }
-          for (int i = M - 1; i >= 0; --i) {
-            double sacc = Yc[i * rk + k];
-            for (int j = i + 1; j < M; ++j) sacc -= K[j * M + i] * Yc[j * rk + k];
-            Yc[i * rk + k] = sacc / K[i * M + i];
-          }
-        }
-        block_sync();
+        chol_solve_f64(K, M, ldg, Yc, rk, rk);
         for (int e = tid; e < d * rk; e += nt) {
           const int dm = e / rk, k = e - (e / rk) * rk;
           double acc = 0.0;
-          for (int mm = 0; mm < M; ++mm) acc += (double)Xf[mm * d + dm] * sqrt(w[mm]) * Yc[mm * rk + k];
+          for (int mm = 0; mm < M; ++mm) acc += (double)Xf[mm * ldx + dm] * sqrt(w[mm]) * Yc[mm * rk + k];
           Wm[dm * rk + k] = acc;
         }
       }
@@ -332,31 +371,18 @@ __global__ __launch_bounds__(256) void k_fit(FitArgs a) {
       for (int e = tid; e < d * d; e += nt) {
         const int i = e / d, j = e - (e / d) * d;
         double acc = 0.0;
-        for (int mm = 0; mm < M; ++mm) acc += w[mm] * (double)Xf[mm * d + i] * (double)Xf[mm * d + j];
+        for (int mm = 0; mm < M; ++mm) acc += w[mm] * (double)Xf[mm * ldx + i] * (double)Xf[mm * ldx + j];
         K[e] = acc + (i == j ? lam : 0.0);
       }
       for (int e = tid; e < d * rk; e += nt) {
         const int i = e / rk, k = e - (e / rk) * rk;
         double acc = 0.0;
-        for (int mm = 0; mm < M; ++mm) acc += w[mm] * (double)Xf[mm * d + i] * Yc[mm * rk + k];
+        for (int mm = 0; mm < M; ++mm) acc += w[mm] * (double)Xf[mm * ldx + i] * Yc[mm * rk + k];
         Wm[e] = acc;
       }
       block_sync();
-      ok = cholesky_f64(K, d, &bad);
-      if (ok) {
-        for (int k = tid; k < rk; k += nt) {
-          for (int i = 0; i < d; ++i) {
-            double sacc = Wm[i * rk + k];
-            for (int j = 0; j < i; ++j) sacc -= K[i * d + j] * Wm[j * rk + k];
-            Wm[i * rk + k] = sacc / K[i * d + i];
-          }
-          for (int i = d - 1; i >= 0; --i) {
-            double sacc = Wm[i * rk + k];
-            for (int j = i + 1; j < d; ++j) sacc -= K[j * d + i] * Wm[j * rk + k];
-            Wm[i * rk + k] = sacc / K[i * d + i];
-          }
-        }
-      }
+      ok = cholesky_f64(K, d, d, &bad);
+      if (ok) chol_solve_f64(K, d, d, Wm, rk, rk);
     }
     block_sync();
   }
@@ -409,7 +435,7 @@ hipError_t launch_fit(const Plan& p, hipStream_t s) {
   a.rank = p.fitrank;
   a.sig = p.fitsig;
   a.stats = p.stats;
-  hipLaunchKernelGGL(k_fit, dim3(p.BH), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(k_fit, dim3(p.BH), dim3(kFitThreads), 0, s, a);
   return hipGetLastError();
 }
 

@@ -18,6 +18,7 @@
 // bf16 MFMA product with a fused argmin does the assignment.  Centre images
 // are kept as hi + lo bf16 pairs (16 significant bits).
 #include "sp_kernels.h"
+#include "sp_eig.h"
 
 namespace sp {
 
@@ -153,118 +154,44 @@ __device__ inline void rr_pair(int k, int r, int n, int* p, int* q) {
 
 template <int D>
 __global__ __launch_bounds__(1024) void k_key_eig(EigArgs a) {
-  constexpr int LD = D + 1;
-  constexpr int HP = D / 2;
-  __shared__ float A[D * LD];
-  __shared__ float V[D * LD];
-  __shared__ float rc[HP], rs[HP];
-  __shared__ int rp[HP], rq[HP];
-  __shared__ float red[2][32];
-  __shared__ int stop;
-  const int bh = blockIdx.x, tid = threadIdx.x;
+  constexpr int LD = D + 1;  // odd row stride: column walks hit distinct banks
   constexpr int NT = 1024;
+  __shared__ float A[D * LD];
+  __shared__ float Z[D * LD];
+  __shared__ float dg[D + 2], eo[D + 2], tau[D], vb[D], pb[D];
+  __shared__ float rot[4 * D];
+  __shared__ int ctl[8];
+  __shared__ int top[D];
+  const int bh = blockIdx.x, tid = threadIdx.x;
   const float* mk = a.mk + (long long)bh * D * D;
   for (int e = tid; e < D * D; e += NT) {
     const int i = e / D, j = e - (e / D) * D;
     A[i * LD + j] = mk[e];
-    V[i * LD + j] = i == j ? 1.f : 0.f;
   }
   __syncthreads();
-  // lanes own row pairs / rows (row stride D + 1 keeps them on distinct banks);
-  // waves step through column pairs
-  const int lane = tid & 63, wv = tid >> 6;
-  constexpr int WPR = 64 / HP;     // column-pair offsets per wave (1 for D=128, 2 for D=64)
-  const int ia = lane % HP, ib0 = wv * WPR + lane / HP;
-  constexpr int CSTEP = (NT / 64) * WPR;
-  for (int sweep = 0; sweep < 16; ++sweep) {
-    float off = 0.f, tot = 0.f;
-    for (int e = tid; e < D * D; e += NT) {
-      const int i = e / D, j = e - (e / D) * D;
-      const float x = A[i * LD + j];
-      tot += x * x;
-      if (i != j) off += x * x;
-    }
-    off = wave_sum(off);
-    tot = wave_sum(tot);
-    if ((tid & 63) == 0) {
-      red[0][tid >> 6] = off;
-      red[1][tid >> 6] = tot;
-    }
-    __syncthreads();
-    if (tid == 0) {
-      float o = 0.f, t = 0.f;
-      for (int w = 0; w < NT / 64; ++w) {
-        o += red[0][w];
-        t += red[1][w];
-      }
-      // relative off-diagonal norm below ~3e-6: far below what the k-means
-      // coordinates resolve, and reachable in fp32
-      stop = !(o > 1e-11f * t);
-    }
-    __syncthreads();
-    if (stop) break;
-    for (int r = 0; r < D - 1; ++r) {
-      if (tid < HP) {
-        int p, q;
-        rr_pair(tid, r, D, &p, &q);
-        const float app = A[p * LD + p], aqq = A[q * LD + q], apq = A[p * LD + q];
-        float c = 1.f, s = 0.f;
-        if (apq != 0.f) {
-          const float th = (aqq - app) / (2.f * apq);
-          float t;
-          if (fabsf(th) > 1e18f) t = 0.5f / th;
-          else t = (th >= 0.f ? 1.f : -1.f) / (fabsf(th) + sqrtf(1.f + th * th));
-          c = 1.f / sqrtf(1.f + t * t);
-          s = t * c;
-        }
-        rc[tid] = c;
-        rs[tid] = s;
-        rp[tid] = p;
-        rq[tid] = q;
-      }
-      __syncthreads();
-      const int pa = rp[ia], qa = rq[ia];
-      const float ca = rc[ia], sa = rs[ia];
-      for (int ib = ib0; ib < HP; ib += CSTEP) {
-        const int pb = rp[ib], qb = rq[ib];
-        const float cb = rc[ib], sb = rs[ib];
-        // A <- Ja^T A Jb on the 2x2 block (row pair ia, column pair ib)
-        const float x00 = A[pa * LD + pb], x01 = A[pa * LD + qb];
-        const float x10 = A[qa * LD + pb], x11 = A[qa * LD + qb];
-        const float t00 = ca * x00 - sa * x10, t01 = ca * x01 - sa * x11;
-        const float t10 = sa * x00 + ca * x10, t11 = sa * x01 + ca * x11;
-        A[pa * LD + pb] = cb * t00 - sb * t01;
-        A[pa * LD + qb] = sb * t00 + cb * t01;
-        A[qa * LD + pb] = cb * t10 - sb * t11;
-        A[qa * LD + qb] = sb * t10 + cb * t11;
-      }
-      // V <- V J: lanes own rows, waves step through column pairs
-      for (int ib = wv; ib < HP; ib += NT / 64) {
-        const int pb = rp[ib], qb = rq[ib];
-        const float cb = rc[ib], sb = rs[ib];
-        for (int i = lane; i < D; i += 64) {
-          const float v1 = V[i * LD + pb], v2 = V[i * LD + qb];
-          V[i * LD + pb] = cb * v1 - sb * v2;
-          V[i * LD + qb] = sb * v1 + cb * v2;
-        }
-      }
-      __syncthreads();
-    }
-  }
-  // rank eigenvalues (descending, ties by index) and emit the coordinate map
+  const EigWork<float> w{A, LD, Z, LD, dg, eo, tau, vb, pb, rot, ctl};
+  eig_tridiagonalize<float, NT>(w, D);
+  eig_tridiagonal_qr<float, NT>(w, D);
+  // rank eigenvalues (descending, ties by index)
   for (int i = tid; i < D; i += NT) {
-    const float li = A[i * LD + i];
+    const float li = dg[i];
     int rank = 0;
     for (int j = 0; j < D; ++j) {
-      const float lj = A[j * LD + j];
+      const float lj = dg[j];
       rank += (lj > li) || (lj == li && j < i);
     }
     if (a.eigval) a.eigval[(long long)bh * D + rank] = li;
-    if (rank < a.rK) {
-      const float f = a.scale * sqrtf(fmaxf(li, 0.f));
-      float* km = a.kmap + (long long)bh * D * a.rK;
-      for (int k = 0; k < D; ++k) km[k * a.rK + rank] = f * V[k * LD + i];
-    }
+    if (rank < a.rK) top[rank] = i;
+  }
+  __syncthreads();
+  eig_back_transform<float, NT, 32>(w, D, top, a.rK);
+  // coordinate map: column k of kmap = s sqrt(lambda_k) u_k
+  float* km = a.kmap + (long long)bh * D * a.rK;
+  for (int e = tid; e < D * a.rK; e += NT) {
+    const int r = e / D, k = e - (e / D) * D;
+    const int i = top[r];
+    const float f = a.scale * sqrtf(fmaxf(dg[i], 0.f));
+    km[k * a.rK + r] = f * Z[k * LD + i];
   }
 }
 

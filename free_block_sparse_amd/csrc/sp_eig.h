@@ -1,0 +1,314 @@
+// Symmetric eigensolver for one small matrix (n <= 128) held by one workgroup.
+//
+//   1. Householder reduction to tridiagonal form, A = Q T Q^T.  Each step
+//      reflects the column below the diagonal onto its first entry; the
+//      product with the trailing block and the rank-2 update are spread over
+//      the workgroup.  The reflectors stay in the strictly lower part of A.
+//   2. Implicit symmetric QR on T with Wilkinson shifts from the trailing 2x2
+//      block and deflation of negligible off-diagonal entries.  One lane
+//      chases the bulge of step t while the other waves apply the rotations
+//      of step t-1 to the rows of Z, so the eigenvector update runs beside
+//      the scalar chase.
+//   3. Back-transformation of the requested columns of Z by the reflectors.
+//
+// Standard dense symmetric eigenvalue algorithms (reduction to tridiagonal
+// form, shifted QR); written for a single GPU workgroup.
+
+#pragma once
+
+#include "sp_common.h"
+
+namespace sp {
+
+template <typename T>
+struct EigEps;
+template <>
+struct EigEps<float> {
+  static constexpr float v = 1.1920929e-7f;
+};
+template <>
+struct EigEps<double> {
+  static constexpr double v = 2.220446049250313e-16;
+};
+
+// 1 / sqrt(q) for q > 0: the hardware estimate, refined by one Newton step in
+// fp64 (the fp32 estimate is already within about an ulp).
+__device__ inline float eig_rsqrt(float q) { return __builtin_amdgcn_rsqf(q); }
+__device__ inline double eig_rsqrt(double q) {
+  const double y = __builtin_amdgcn_rsq(q);
+  return y * (1.5 - 0.5 * q * y * y);
+}
+
+template <typename T>
+__device__ inline T eig_sum(T v, int width) {
+  for (int o = width >> 1; o > 0; o >>= 1) v += __shfl_xor(v, o, width);
+  return v;
+}
+
+template <typename T>
+struct EigWork {
+  T* A;
+  int lda;   // n x n symmetric matrix in; reflectors out (below the subdiagonal)
+  T* Z;
+  int ldz;   // n x n eigenvectors out (column j belongs to dg[j])
+  T* dg;     // [n + 2] eigenvalues out (unsorted)
+  T* eo;     // [n + 2] off-diagonal of T
+  T* tau;    // [n] reflector scales
+  T* vb;     // [n] current reflector
+  T* pb;     // [max(n, 2)] A22 v
+  T* rot;    // [2][2n] rotation pairs (c, s), double-buffered
+  int* ctl;  // [8]
+};
+
+// Step 1.  NT threads; every thread calls it.
+template <typename T, int NT>
+__device__ void eig_tridiagonalize(const EigWork<T>& w, int n) {
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  T* A = w.A;
+  const int lda = w.lda;
+  constexpr int TPR = NT >= 256 ? NT / 128 : 1;  // threads per row of the product
+  for (int k = 0; k + 2 < n; ++k) {
+    const int m = n - k - 1;
+    T* x = A + (k + 1) * lda + k;  // x[i * lda], i < m
+    if (wv == 0) {
+      T sig = 0;
+      for (int i = 1 + lane; i < m; i += 64) sig += x[i * lda] * x[i * lda];
+      sig = eig_sum(sig, 64);
+      const T x0 = x[0];
+      T tau = 0, beta = x0, scale = 0;
+      if (sig != T(0)) {
+        const T nrm = sqrt(x0 * x0 + sig);
+        beta = x0 >= T(0) ? -nrm : nrm;
+        tau = (beta - x0) / beta;
+        scale = T(1) / (x0 - beta);
+      }
+      for (int i = lane; i < m; i += 64) {
+        const T vi = i == 0 ? T(1) : x[i * lda] * scale;
+        w.vb[i] = vi;
+        x[i * lda] = vi;
+      }
+      if (lane == 0) {
+        w.tau[k] = tau;
+        w.eo[k] = beta;
+        w.dg[k] = A[k * lda + k];
+      }
+    }
+    __syncthreads();
+    const T tau = w.tau[k];
+    if (tau == T(0)) continue;
+    {
+      const int row = tid / TPR, sub = tid - row * TPR;
+      T acc = 0;
+      if (row < m) {
+        const T* ar = A + (k + 1 + row) * lda + (k + 1);
+        for (int j = sub; j < m; j += TPR) acc += ar[j] * w.vb[j];
+      }
+      if (TPR > 1) acc = eig_sum(acc, TPR);
+      if (row < m && sub == 0) w.pb[row] = tau * acc;
+    }
+    __syncthreads();
+    T kk = 0;
+    for (int i = lane; i < m; i += 64) kk += w.vb[i] * w.pb[i];
+    kk = eig_sum(kk, 64) * (tau * T(0.5));
+    for (int e = tid; e < m * m; e += NT) {
+      const int i = e / m, j = e - (e / m) * m;
+      const T vi = w.vb[i], vj = w.vb[j];
+      const T wi = w.pb[i] - kk * vi, wj = w.pb[j] - kk * vj;
+      A[(k + 1 + i) * lda + (k + 1 + j)] -= vi * wj + wi * vj;
+    }
+    __syncthreads();
+  }
+  if (tid == 0) {
+    if (n >= 2) {
+      w.dg[n - 2] = A[(n - 2) * lda + (n - 2)];
+      w.dg[n - 1] = A[(n - 1) * lda + (n - 1)];
+      w.eo[n - 2] = A[(n - 1) * lda + (n - 2)];
+    } else {
+      w.dg[0] = A[0];
+    }
+  }
+  __syncthreads();
+}
+
+// Step 2.  Needs NT >= 64 + n (waves 1.. apply the rotations).
+template <typename T, int NT>
+__device__ void eig_tridiagonal_qr(const EigWork<T>& w, int n) {
+  const int tid = threadIdx.x;
+  T* Z = w.Z;
+  const int ldz = w.ldz;
+  for (int e = tid; e < n * n; e += NT) {
+    const int i = e / n, j = e - (e / n) * n;
+    Z[i * ldz + j] = i == j ? T(1) : T(0);
+  }
+  if (tid == 0) {
+    w.ctl[0] = n - 1;  // bottom of the unreduced part
+    w.ctl[1] = 0;      // steps taken
+    // Gershgorin bound of T: off-diagonal entries below eps * ||T|| are at
+    // the rounding level of the whole matrix and are dropped as well, so an
+    // eigenvalue far below ||T|| cannot hold up convergence
+    T tn = 0;
+    for (int i = 0; i < n; ++i) {
+      T r = fabs(w.dg[i]);
+      if (i > 0) r += fabs(w.eo[i - 1]);
+      if (i + 1 < n) r += fabs(w.eo[i]);
+      tn = r > tn ? r : tn;
+    }
+    w.pb[0] = tn;
+  }
+  __syncthreads();
+  const T eps = EigEps<T>::v;
+  const T tiny = eps * w.pb[0];
+  for (int t = 0;; ++t) {
+    const int b = t & 1;
+    if (tid < 64) {
+      // Wave 0.  Negligible off-diagonal entries (relative to their diagonal
+      // neighbours, or to ||T||) are found with one ballot per 64 entries:
+      // the unreduced block [l, mm] ends at the last non-negligible entry
+      // and starts after the negligible entry before it.
+      const int lane = tid;
+      T* d = w.dg;
+      T* e = w.eo;
+      const int mm0 = w.ctl[0];
+      const int steps = w.ctl[1];
+      unsigned long long neg[2] = {0ull, 0ull};
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int i = lane + 64 * h;
+        bool ng = false;
+        if (i < mm0) {
+          const T ei = fabs(e[i]);
+          ng = ei <= eps * (fabs(d[i]) + fabs(d[i + 1])) || ei <= tiny;
+          if (ng) e[i] = T(0);
+        }
+        neg[h] = __builtin_amdgcn_ballot_w64(ng);
+      }
+      // bit i of the mask (i < mm0) is set where e[i] is negligible
+      int mm = 0;
+      for (int h = 1; h >= 0 && mm == 0; --h) {
+        const unsigned long long keep = ~neg[h] & (mm0 - 64 * h >= 64 ? ~0ull : (mm0 - 64 * h > 0 ? ((1ull << (mm0 - 64 * h)) - 1ull) : 0ull));
+        if (keep) mm = 64 * h + 63 - __builtin_clzll(keep) + 1;
+      }
+      if (mm == 0 || steps >= 30 * n) {
+        if (lane == 0) {
+          w.ctl[2 + 2 * b] = -1;
+          w.ctl[3 + 2 * b] = -1;
+          w.ctl[0] = mm;
+        }
+      } else {
+        int l = 0;
+        for (int h = 1; h >= 0; --h) {
+          const int lim = mm - 1 - 64 * h;  // entries below mm - 1 in this half
+          if (lim <= 0) continue;
+          const unsigned long long below = neg[h] & (lim >= 64 ? ~0ull : ((1ull << lim) - 1ull));
+          if (below) {
+            l = 64 * h + 63 - __builtin_clzll(below) + 1;
+            break;
+          }
+        }
+        if (lane == 0) {
+          // Wilkinson shift: the eigenvalue of the trailing 2x2 block nearer d[mm]
+          const T a0 = d[mm - 1], bb = e[mm - 1], c0 = d[mm];
+          const T del = (a0 - c0) * T(0.5);
+          const T hyp = sqrt(del * del + bb * bb);
+          const T mu = c0 - bb * bb / (del + (del >= T(0) ? hyp : -hyp));
+          // The chase keeps the entries it is rotating in registers: a = d[k]
+          // and bq = e[k] as updated by the previous rotation; d[k+1] and
+          // e[k+1] are still untouched and are read one step ahead.
+          T x = d[l] - mu, z = e[l];
+          T a = d[l], bq = e[l];
+          T dn = d[l + 1], en = e[l + 1];
+          T* rot = w.rot + b * 2 * n;
+          // Branch-free body: d and e are padded by two entries, so the
+          // read-ahead never leaves the arrays; the first step's "previous
+          // off-diagonal" goes to a dummy slot; the block's last d and e
+          // entries are written after the loop.
+          T* eprev = w.pb + 1;
+          for (int k = l; k < mm; ++k) {
+            const T dd = dn, ek1 = en;
+            dn = d[k + 2];
+            en = e[k + 2];
+            // rotation in the (k, k+1) plane that zeroes z against x
+            const T q = x * x + z * z;
+            const bool pos = q > T(0);
+            const T ir = eig_rsqrt(pos ? q : T(1));
+            const T c = pos ? x * ir : T(1);
+            const T s = pos ? -z * ir : T(0);
+            *eprev = q * ir;
+            eprev = e + k;
+            const T cc = c * c, ss = s * s, cs = c * s;
+            const T dk = a * cc - T(2) * bq * cs + dd * ss;
+            const T dk1 = a * ss + T(2) * bq * cs + dd * cc;
+            const T ek = (a - dd) * cs + bq * (cc - ss);
+            d[k] = dk;
+            rot[2 * k] = c;
+            rot[2 * k + 1] = s;
+            x = ek;
+            z = -s * ek1;
+            bq = c * ek1;
+            a = dk1;
+          }
+          e[mm - 1] = x;
+          d[mm] = a;
+          w.ctl[2 + 2 * b] = l;
+          w.ctl[3 + 2 * b] = mm;
+          w.ctl[1] = steps + 1;
+          w.ctl[0] = mm;
+        }
+      }
+    } else if (t > 0 && tid >= 64) {
+      // rotations of the previous step, applied to the rows of Z
+      const int pbuf = b ^ 1;
+      const int l = w.ctl[2 + 2 * pbuf], mm = w.ctl[3 + 2 * pbuf];
+      if (l >= 0) {
+        const T* rot = w.rot + pbuf * 2 * n;
+        for (int i = tid - 64; i < n; i += NT - 64) {
+          T* zr = Z + i * ldz;
+          T xk = zr[l];
+          for (int k0 = l; k0 < mm; k0 += 8) {
+            const int nk = mm - k0 < 8 ? mm - k0 : 8;
+            T y[8], c[8], sn[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+              if (u < nk) {
+                y[u] = zr[k0 + u + 1];
+                c[u] = rot[2 * (k0 + u)];
+                sn[u] = rot[2 * (k0 + u) + 1];
+              }
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+              if (u < nk) {
+                zr[k0 + u] = c[u] * xk - sn[u] * y[u];
+                xk = sn[u] * xk + c[u] * y[u];
+              }
+          }
+          zr[mm] = xk;
+        }
+      }
+    }
+    __syncthreads();
+    if (w.ctl[2 + 2 * b] < 0) break;  // converged; step t-1 was applied above
+  }
+}
+
+// Step 3: Z[:, cols[c]] <- Q Z[:, cols[c]] for c < ncol (cols == nullptr: c).
+// GW consecutive threads (one wave or part of one) take a column.
+template <typename T, int NT, int GW>
+__device__ void eig_back_transform(const EigWork<T>& w, int n, const int* cols, int ncol) {
+  const int tid = threadIdx.x, g = tid / GW, sub = tid - (tid / GW) * GW;
+  constexpr int NG = NT / GW;
+  for (int c = g; c < ncol; c += NG) {
+    const int j = cols ? cols[c] : c;
+    for (int k = n - 3; k >= 0; --k) {
+      const T tau = w.tau[k];
+      if (tau == T(0)) continue;
+      const int m = n - k - 1;
+      T s = 0;
+      for (int i = sub; i < m; i += GW) s += w.A[(k + 1 + i) * w.lda + k] * w.Z[(k + 1 + i) * w.ldz + j];
+      s = eig_sum(s, GW) * tau;
+      for (int i = sub; i < m; i += GW) w.Z[(k + 1 + i) * w.ldz + j] -= s * w.A[(k + 1 + i) * w.lda + k];
+    }
+  }
+  __syncthreads();
+}
+
+}  // namespace sp

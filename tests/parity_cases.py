@@ -7,7 +7,8 @@ import functools
 
 import numpy as np
 
-from oracle import OracleConfig, dense_attention, sparsepr_head
+from oracle import (OracleConfig, dense_attention, group_by_labels, group_means, key_coordinates, kmeans,
+                    query_coordinates, softmax_scale, sparsepr_head)
 from synth import make_video_qkv, make_workload_inputs, workload
 
 
@@ -102,3 +103,32 @@ def tolerances(dtype: str):
     stay near 1e-6 relative; the bounds leave two orders of margin.
     """
     return (2e-2, 5e-3) if dtype == "bf16" else (1e-4, 1e-5)
+
+
+def oracle_key_labels_from_metric(name: str, h: int, m_k) -> np.ndarray:
+    """The oracle's key k-means run on coordinates built from a given M_K."""
+    c = CASES[name]
+    cfg = c.oracle_cfg()
+    k64 = inputs(name)["k"][0, h].double().numpy()
+    n, d = k64.shape
+    s = softmax_scale(cfg, d)
+    r_k = min(cfg.key_coord_rank, d, min(cfg.n_sample_q, n))
+    z, _, _ = key_coordinates(k64, np.asarray(m_k, dtype=np.float64), r_k, s)
+    labels, _ = kmeans(z, c.gk, cfg.kmeans_iters)
+    return labels
+
+
+def oracle_query_labels_given_keys(name: str, h: int, kv_labels) -> np.ndarray:
+    """The oracle's query k-means run on the query coordinates that a given
+    key partition defines."""
+    c = CASES[name]
+    cfg = c.oracle_cfg()
+    x = inputs(name)
+    q64 = x["q"][0, h].double().numpy()
+    k64 = x["k"][0, h].double().numpy()
+    s = softmax_scale(cfg, q64.shape[1])
+    perm_k, nk, off_k = group_by_labels(np.asarray(kv_labels, dtype=np.int64), c.gk)
+    cbar = group_means(k64, perm_k, off_k)
+    u = query_coordinates(q64, cbar[nk > 0], s)
+    labels, _ = kmeans(u, c.gq, cfg.kmeans_iters)
+    return labels
