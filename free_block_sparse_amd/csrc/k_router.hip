@@ -314,6 +314,7 @@ __global__ __launch_bounds__(1024) void k_route_select(RouteArgs a) {
 // ---------------------------------------------------------------- CSR, masks, tiles, stats
 __global__ __launch_bounds__(256) void k_route_emit(RouteArgs a) {
   __shared__ int nq[kMaxGroups], nk[kMaxGroups], cnt[kMaxGroups], tcnt[kMaxGroups];
+  __shared__ int bucket[kMaxGroups + 1], order[kMaxGroups], mands[kMaxGroups];
   __shared__ long long lsh[kMaxGroups];
   __shared__ long long thr[4];
   const int bh = blockIdx.x, tid = threadIdx.x;
@@ -322,7 +323,11 @@ __global__ __launch_bounds__(256) void k_route_emit(RouteArgs a) {
   const int* offk = a.off_k + (long long)bh * (GK + 1);
   const uint64_t* ck = a.ckey + (long long)bh * GQ * GK;
   const int* mand = a.mand + (long long)bh * GQ;
-  for (int g = tid; g < GQ; g += 256) nq[g] = offq[g + 1] - offq[g];
+  for (int g = tid; g < GQ; g += 256) {
+    nq[g] = offq[g + 1] - offq[g];
+    const int mg = mand[g];
+    mands[g] = mg >= 0 && mg < GK ? mg : -1;
+  }
   for (int h = tid; h < GK; h += 256) nk[h] = offk[h + 1] - offk[h];
   if (tid < 4) thr[tid] = a.thr[(long long)bh * 4 + tid];
   __syncthreads();
@@ -338,7 +343,7 @@ __global__ __launch_bounds__(256) void k_route_emit(RouteArgs a) {
         bool gr = false;
         if (nq[g] > 0 && nk[h] > 0) {
           const uint32_t cell = (uint32_t)(g * GK + h);
-          gr = (h == mand[g]) || (ck[cell] != kExcluded && thr_grants(thr, ck[cell], cell));
+          gr = (h == mands[g]) || (ck[cell] != kExcluded && thr_grants(thr, ck[cell], cell));
         }
         if (gr) {
           bits |= 1u << b;
@@ -360,18 +365,30 @@ __global__ __launch_bounds__(256) void k_route_emit(RouteArgs a) {
     int acc = 0, tacc = 0;
     long long routed = 0, mandc = 0;
     int neq = 0, nek = 0;
+    // Tiles are listed by the mandatory (best) key group of their query
+    // group, then by group: query groups that attend to the same keys come
+    // next to each other, and the attention kernel runs neighbouring tiles
+    // on one XCD, where they share the L2.  (Stable counting sort; the order
+    // only decides which tiles run together, never a result.)
+    for (int h = 0; h <= GK; ++h) bucket[h] = 0;
+    for (int g = 0; g < GQ; ++g) ++bucket[(mands[g] >= 0 ? mands[g] : 0) + 1];
+    for (int h = 0; h < GK; ++h) bucket[h + 1] += bucket[h];
+    for (int g = 0; g < GQ; ++g) order[bucket[mands[g] >= 0 ? mands[g] : 0]++] = g;
+    for (int i = 0; i < GQ; ++i) {
+      const int g = order[i];
+      const int tc = tcnt[g];
+      tcnt[g] = tacc;
+      tacc += tc;
+    }
     for (int g = 0; g < GQ; ++g) {
       rp[g] = acc;
       const int c = cnt[g];
       cnt[g] = acc;
       acc += c;
-      const int tc = tcnt[g];
-      tcnt[g] = tacc;
-      tacc += tc;
       routed += (long long)nq[g] * lsh[g];
       if (nq[g] > 0) {
         ++neq;
-        if (mand[g] >= 0) mandc += (long long)nq[g] * nk[mand[g]];
+        if (mands[g] >= 0) mandc += (long long)nq[g] * nk[mands[g]];
       }
     }
     rp[GQ] = acc;
