@@ -330,48 +330,74 @@ __global__ __launch_bounds__(256) void k_split_rows(SplitArgs a) {
 // B[k][n]: k = 8*(lane/32)+j, n = lane%32; D[i][j]: j = lane%32,
 // i = (r%4) + 8*(r/4) + 4*(lane/32) for accumulator register r.
 // ============================================================================
-template <int D, bool LO>
-__global__ __launch_bounds__(256) void k_kmeans_assign(AssignArgs a) {
+// Smallest of the 16 distances c - 2 x.y held by one lane for a 32-centre
+// block (register r belongs to centre (r&3) + 8(r>>2) + 4*half, increasing
+// in r).  Pairwise tree (depth 4); on ties the lower register, i.e. the
+// lower centre index, is kept.  Returns the distance and writes the
+// register index.
+__device__ inline float block_argmin16(const f32x16& acc, const float* sb, int* ridx) {
+  float v[16];
+  int id[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    v[r] = __builtin_fmaf(-2.0f, acc[r], sb[r]);
+    id[r] = r;
+  }
+#pragma unroll
+  for (int w = 1; w < 16; w <<= 1)
+#pragma unroll
+    for (int r = 0; r < 16; r += 2 * w) {
+      const bool right = v[r + w] < v[r];
+      v[r] = right ? v[r + w] : v[r];
+      id[r] = right ? id[r + w] : id[r];
+    }
+  *ridx = id[0];
+  return v[0];
+}
+
+template <int D, bool LO, int CG>
+__global__ __launch_bounds__(512, 4) void k_kmeans_assign(AssignArgs a) {
+  // One 256-point histogram chunk per workgroup (8 waves x one 32-point MFMA
+  // column, points held as B operands in registers), two workgroups per CU;
+  // the centre images are staged through LDS CG at a time (two barriers per
+  // CG centres) and read as A operands, two 32-centre blocks at a time.
   constexpr int KS = D / 16;
   constexpr int LDI = D + 8;  // padded LDS row (bank spread)
-  __shared__ __attribute__((aligned(16))) bf16_t sh[32 * LDI];
-  __shared__ __attribute__((aligned(16))) bf16_t sl[32 * LDI];
-  __shared__ float sbias[32];
+  constexpr int NT = 512;
+  __shared__ __attribute__((aligned(16))) bf16_t sh[CG * LDI];
+  __shared__ __attribute__((aligned(16))) bf16_t sl[CG * LDI];
+  __shared__ __attribute__((aligned(16))) float sbias[CG];
   __shared__ int hist[kMaxGroups];
-  const int bh = blockIdx.y, chunk = blockIdx.x;
+  const int bh = blockIdx.y, blk = blockIdx.x;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int N = a.N, G = a.G;
   const int half = lane >> 5, col = lane & 31;
-  const int nb = chunk * kChunk + wave * 64;
+  const int n = blk * kChunk + wave * 32 + col;
 
-  for (int g = tid; g < G; g += 256) hist[g] = 0;
+  for (int g = tid; g < G; g += NT) hist[g] = 0;
 
-  bf16x8 ph[2][KS];
-  bf16x8 pl[2][LO ? KS : 1];
+  bf16x8 ph[KS];
+  bf16x8 pl[LO ? KS : 1];
   const bf16_t* hib = static_cast<const bf16_t*>(a.pts.p);
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    const int n = nb + 32 * t + col;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      uint4 v = make_uint4(0, 0, 0, 0);
-      uint4 w = make_uint4(0, 0, 0, 0);
-      if (n < N) {
-        v = *reinterpret_cast<const uint4*>(hib + a.pts.row_off(bh, n) + 16 * ks + 8 * half);
-        if (LO) w = *reinterpret_cast<const uint4*>(a.pts_lo + ((long long)bh * N + n) * D + 16 * ks + 8 * half);
-      }
-      ph[t][ks] = __builtin_bit_cast(bf16x8, v);
-      if (LO) pl[t][LO ? ks : 0] = __builtin_bit_cast(bf16x8, w);
+  for (int ks = 0; ks < KS; ++ks) {
+    uint4 v = make_uint4(0, 0, 0, 0);
+    uint4 w = make_uint4(0, 0, 0, 0);
+    if (n < N) {
+      v = *reinterpret_cast<const uint4*>(hib + a.pts.row_off(bh, n) + 16 * ks + 8 * half);
+      if (LO) w = *reinterpret_cast<const uint4*>(a.pts_lo + ((long long)bh * N + n) * D + 16 * ks + 8 * half);
     }
+    ph[ks] = __builtin_bit_cast(bf16x8, v);
+    if (LO) pl[LO ? ks : 0] = __builtin_bit_cast(bf16x8, w);
   }
-  float best[2] = {INFINITY, INFINITY};
-  int bidx[2] = {0, 0};
+  float best = INFINITY;
+  int bidx = 0;
   const bf16_t* yh = a.yhi + (long long)bh * a.gstride * a.ystride;
   const bf16_t* yl = a.ylo + (long long)bh * a.gstride * a.ystride;
   const float* yb = a.ybias + (long long)bh * a.gstride;
-  for (int c0 = 0; c0 < G; c0 += 32) {
+  for (int c0 = 0; c0 < G; c0 += CG) {
     __syncthreads();
-    for (int e = tid; e < 32 * (D / 8); e += 256) {
+    for (int e = tid; e < CG * (D / 8); e += NT) {
       const int r = e / (D / 8), cc = e - (e / (D / 8)) * (D / 8);
       const int c = c0 + r;
       uint4 vh = make_uint4(0, 0, 0, 0), vl = make_uint4(0, 0, 0, 0);
@@ -382,53 +408,79 @@ __global__ __launch_bounds__(256) void k_kmeans_assign(AssignArgs a) {
       *reinterpret_cast<uint4*>(sh + r * LDI + cc * 8) = vh;
       *reinterpret_cast<uint4*>(sl + r * LDI + cc * 8) = vl;
     }
-    if (tid < 32) sbias[tid] = (c0 + tid < G) ? yb[c0 + tid] : INFINITY;
+    for (int e = tid; e < CG; e += NT) sbias[e] = (c0 + e < G) ? yb[c0 + e] : INFINITY;
     __syncthreads();
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      f32x16 acc = {};
+    const int nblk = min(CG, G - c0);
+    // two 32-centre blocks at a time: independent accumulator chains
+    for (int cb = 0; cb < nblk; cb += 64) {
+      const bool two = cb + 32 < nblk;
+      f32x16 acc0 = {}, acc1 = {};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8 ah = *reinterpret_cast<const bf16x8*>(sh + col * LDI + 16 * ks + 8 * half);
-        const bf16x8 al = *reinterpret_cast<const bf16x8*>(sl + col * LDI + 16 * ks + 8 * half);
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, ph[t][ks], acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, ph[t][ks], acc, 0, 0, 0);
-        if (LO) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, pl[t][LO ? ks : 0], acc, 0, 0, 0);
+        const bf16_t* r0 = sh + (cb + col) * LDI + 16 * ks + 8 * half;
+        const bf16_t* q0 = sl + (cb + col) * LDI + 16 * ks + 8 * half;
+        const bf16x8 ah0 = *reinterpret_cast<const bf16x8*>(r0);
+        const bf16x8 al0 = *reinterpret_cast<const bf16x8*>(q0);
+        const bf16x8 ah1 = *reinterpret_cast<const bf16x8*>(r0 + 32 * LDI);
+        const bf16x8 al1 = *reinterpret_cast<const bf16x8*>(q0 + 32 * LDI);
+        acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah0, ph[ks], acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah1, ph[ks], acc1, 0, 0, 0);
+        acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al0, ph[ks], acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al1, ph[ks], acc1, 0, 0, 0);
+        if (LO) {
+          acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah0, pl[LO ? ks : 0], acc0, 0, 0, 0);
+          acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah1, pl[LO ? ks : 0], acc1, 0, 0, 0);
+        }
       }
+      // biases of this lane's centres: four runs of four consecutive centres
+      float sb[16];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int i = (r & 3) + 8 * (r >> 2) + 4 * half;
-        const float dist = sbias[i] - 2.0f * acc[r];
-        if (dist < best[t]) {
-          best[t] = dist;
-          bidx[t] = c0 + i;
+      for (int q = 0; q < 4; ++q) {
+        const float4 f = *reinterpret_cast<const float4*>(sbias + cb + 8 * q + 4 * half);
+        sb[4 * q] = f.x;
+        sb[4 * q + 1] = f.y;
+        sb[4 * q + 2] = f.z;
+        sb[4 * q + 3] = f.w;
+      }
+      int rr;
+      float dist = block_argmin16(acc0, sb, &rr);
+      if (dist < best) {
+        best = dist;
+        bidx = c0 + cb + (rr & 3) + 8 * (rr >> 2) + 4 * half;
+      }
+      if (two) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float4 f = *reinterpret_cast<const float4*>(sbias + cb + 32 + 8 * q + 4 * half);
+          sb[4 * q] = f.x;
+          sb[4 * q + 1] = f.y;
+          sb[4 * q + 2] = f.z;
+          sb[4 * q + 3] = f.w;
+        }
+        dist = block_argmin16(acc1, sb, &rr);
+        if (dist < best) {
+          best = dist;
+          bidx = c0 + cb + 32 + (rr & 3) + 8 * (rr >> 2) + 4 * half;
         }
       }
     }
   }
-#pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    const float ob = __shfl_xor(best[t], 32, 64);
-    const int oi = __shfl_xor(bidx[t], 32, 64);
-    if (ob < best[t] || (ob == best[t] && oi < bidx[t])) {
-      best[t] = ob;
-      bidx[t] = oi;
+  {
+    const float ob = __shfl_xor(best, 32, 64);
+    const int oi = __shfl_xor(bidx, 32, 64);
+    if (ob < best || (ob == best && oi < bidx)) {
+      best = ob;
+      bidx = oi;
     }
   }
   __syncthreads();
-  if (half == 0) {
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const int n = nb + 32 * t + col;
-      if (n < N) {
-        a.labels[(long long)bh * N + n] = bidx[t];
-        atomicAdd(&hist[bidx[t]], 1);
-      }
-    }
+  if (half == 0 && n < N) {
+    a.labels[(long long)bh * N + n] = bidx;
+    atomicAdd(&hist[bidx], 1);
   }
   __syncthreads();
-  int* cnt = a.counts + ((long long)bh * a.nchunk + chunk) * a.gstride;
-  for (int g = tid; g < G; g += 256) cnt[g] = hist[g];
+  int* cnt = a.counts + ((long long)bh * a.nchunk + blk) * a.gstride;
+  for (int g = tid; g < G; g += NT) cnt[g] = hist[g];
 }
 
 // histogram of given labels (partition supplied by the caller); labels outside
@@ -538,7 +590,7 @@ __global__ __launch_bounds__(256) void k_group_scatter(ScatterArgs a) {
 template <typename TP>
 __global__ __launch_bounds__(256) void k_group_mean(UpdateArgs a) {
   constexpr int NT = 256;
-  __shared__ double part[NT];
+  __shared__ double part[NT * 8];  // P subsets x (padded) dims
   const int bh = blockIdx.y, g = blockIdx.x, tid = threadIdx.x;
   const int Dp = a.Dp;
   const TP* xb = static_cast<const TP*>(a.pts.p);
@@ -552,30 +604,60 @@ __global__ __launch_bounds__(256) void k_group_mean(UpdateArgs a) {
   const int* perm = a.perm + (long long)bh * a.N;
   const int a0 = off[g], a1 = off[g + 1];
   const int n_g = a1 - a0;
-  // The means handed to the router (means_out) are summed one row after
-  // another in ascending token order, as the reference computation does.
-  // Inside the Lloyd iterations each dimension is split over P fixed,
-  // interleaved row subsets whose sums are added in a fixed order, so the
-  // result is still deterministic.  Each thread reads its own dimension of
-  // the member rows directly, eight rows in flight.
-  const int P = a.means_out ? 1 : max(1, NT / Dp);
-  const int j = tid % Dp, pt = tid / Dp;
   double s = 0.0;
-  if (pt < P) {
-    int r = a0 + pt;
-    for (; r + 7 * P < a1; r += 8 * P) {
-      float v[8];
+  if (a.means_out) {
+    // Means handed to the router: rows summed one after another in ascending
+    // token order, as the reference computation does (one thread per dim).
+    if (tid < Dp) {
+      int r = a0;
+      for (; r + 7 < a1; r += 8) {
+        float v[8];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] = Elem<TP>::load(xb + a.pts.row_off(bh, perm[r + u * P]) + j);
+        for (int u = 0; u < 8; ++u) v[u] = Elem<TP>::load(xb + a.pts.row_off(bh, perm[r + u]) + tid);
 #pragma unroll
-      for (int u = 0; u < 8; ++u) s = __dadd_rn(s, (double)v[u]);
+        for (int u = 0; u < 8; ++u) s = __dadd_rn(s, (double)v[u]);
+      }
+      for (; r < a1; ++r) s = __dadd_rn(s, (double)Elem<TP>::load(xb + a.pts.row_off(bh, perm[r]) + tid));
     }
-    for (; r < a1; r += P) s = __dadd_rn(s, (double)Elem<TP>::load(xb + a.pts.row_off(bh, perm[r]) + j));
+  } else {
+    // Lloyd updates: 16-byte row pieces; thread (piece c, subset pt) sums the
+    // rows r = a0 + pt (mod P) of its VEC dims; the P subset sums are added
+    // in a fixed order, so the result is deterministic.
+    constexpr int VEC = 16 / sizeof(TP);
+    const int cpr = (Dp + VEC - 1) / VEC;  // rows are padded to a 16-byte multiple
+    const int P = NT / cpr;
+    const int c = tid % cpr, pt = tid / cpr;
+    double acc[VEC];
+#pragma unroll
+    for (int q = 0; q < VEC; ++q) acc[q] = 0.0;
+    if (pt < P) {
+      int r = a0 + pt;
+      for (; r + 3 * P < a1; r += 4 * P) {
+        uint4 u[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          u[k] = *reinterpret_cast<const uint4*>(xb + a.pts.row_off(bh, perm[r + k * P]) + c * VEC);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const TP* ev = reinterpret_cast<const TP*>(&u[k]);
+#pragma unroll
+          for (int q = 0; q < VEC; ++q) acc[q] = __dadd_rn(acc[q], (double)Elem<TP>::load(ev + q));
+        }
+      }
+      for (; r < a1; r += P) {
+        const uint4 u = *reinterpret_cast<const uint4*>(xb + a.pts.row_off(bh, perm[r]) + c * VEC);
+        const TP* ev = reinterpret_cast<const TP*>(&u);
+#pragma unroll
+        for (int q = 0; q < VEC; ++q) acc[q] = __dadd_rn(acc[q], (double)Elem<TP>::load(ev + q));
+      }
+#pragma unroll
+      for (int q = 0; q < VEC; ++q) part[pt * (cpr * VEC) + c * VEC + q] = acc[q];
+    }
+    __syncthreads();
+    if (tid < Dp)
+      for (int q = 0; q < P; ++q) s = __dadd_rn(s, part[q * (cpr * VEC) + tid]);
   }
-  part[tid] = s;
-  __syncthreads();
   if (tid >= Dp) return;
-  for (int q = 1; q < P; ++q) s = __dadd_rn(s, part[q * Dp + tid]);
   double mean;
   if (n_g > 0) {
     mean = s / (double)n_g;
@@ -589,12 +671,12 @@ __global__ __launch_bounds__(256) void k_group_mean(UpdateArgs a) {
 
 // centre update, step 2: image y = M mean (or the mean itself), stored as a
 // hi/lo bf16 pair, and bias mean . y (fp64 accumulation).
-// 16 groups per workgroup; 16 threads per group, each owning every 16th
-// dimension; M is staged through LDS 32 rows at a time.
+// 16 groups per workgroup; 16 threads per group, each owning 8 consecutive
+// dimensions; M is staged through LDS 32 rows at a time.
 __global__ __launch_bounds__(256) void k_centre_images(UpdateArgs a) {
   constexpr int GB = 16, MR = 32;
   __shared__ double smean[GB][129];
-  __shared__ float sm[MR][129];
+  __shared__ __attribute__((aligned(16))) float sm[MR][132];
   const int bh = blockIdx.y, g0 = blockIdx.x * GB, tid = threadIdx.x;
   const int Dp = a.Dp, Dimg = a.Dimg;
   const int ng = min(GB, a.G - g0);
@@ -602,6 +684,7 @@ __global__ __launch_bounds__(256) void k_centre_images(UpdateArgs a) {
     const int gl = e >> 7, j = e & 127;
     smean[gl][j] = (gl < ng && j < Dp) ? a.cmean[((long long)bh * a.gstride + g0 + gl) * a.cstride + j] : 0.0;
   }
+  // thread (group gl, piece jj) owns dims 8 jj .. 8 jj + 7
   const int gl = tid >> 4, jj = tid & 15;
   const float* M = a.metric ? a.metric + (long long)bh * Dp * Dp : nullptr;
   double y[8];
@@ -617,40 +700,44 @@ __global__ __launch_bounds__(256) void k_centre_images(UpdateArgs a) {
         sm[r][c] = M[(long long)(i0 + r) * Dp + c];
       }
       __syncthreads();
-      for (int r = 0; r < nr; ++r) {
-        const double mv = smean[gl][i0 + r];
+      if (8 * jj < Dp) {
+        for (int r = 0; r < nr; ++r) {
+          const double mv = smean[gl][i0 + r];
+          const float4 m0 = *reinterpret_cast<const float4*>(&sm[r][8 * jj]);
+          const float4 m1 = *reinterpret_cast<const float4*>(&sm[r][8 * jj + 4]);
+          const float mm[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          const int j = jj + 16 * k;
-          if (j < Dp) y[k] = __builtin_fma((double)sm[r][j], mv, y[k]);
+          for (int k = 0; k < 8; ++k) y[k] = __builtin_fma((double)mm[k], mv, y[k]);
         }
       }
     }
   } else {
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-      const int j = jj + 16 * k;
+      const int j = 8 * jj + k;
       y[k] = j < Dp ? smean[gl][j] : 0.0;
     }
   }
   double b = 0.0;
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
-    const int j = jj + 16 * k;
+    const int j = 8 * jj + k;
     if (j < Dp) b = __builtin_fma(y[k], smean[gl][j], b);
   }
   for (int o = 8; o > 0; o >>= 1) b += __shfl_xor(b, o, 16);
   if (gl >= ng) return;
   const long long yo = ((long long)bh * a.gstride + g0 + gl) * a.ystride;
+  if (8 * jj < Dimg) {
+    bf16_t hv[8], lv[8];
 #pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    const int j = jj + 16 * k;
-    if (j < Dimg) {
+    for (int k = 0; k < 8; ++k) {
+      const int j = 8 * jj + k;
       const float yf = j < Dp ? (float)y[k] : 0.f;
-      const bf16_t hi = f32_to_bf16(yf);
-      a.yhi[yo + j] = hi;
-      a.ylo[yo + j] = f32_to_bf16(yf - bf16_to_f32(hi));
+      hv[k] = f32_to_bf16(yf);
+      lv[k] = f32_to_bf16(yf - bf16_to_f32(hv[k]));
     }
+    *reinterpret_cast<uint4*>(a.yhi + yo + 8 * jj) = *reinterpret_cast<const uint4*>(hv);
+    *reinterpret_cast<uint4*>(a.ylo + yo + 8 * jj) = *reinterpret_cast<const uint4*>(lv);
   }
   if (jj == 0) a.ybias[(long long)bh * a.gstride + g0 + gl] = (float)b;
 }
@@ -836,22 +923,24 @@ hipError_t launch_split_rows(const Plan& p, const View4& x, hipStream_t s) {
 }
 
 hipError_t launch_assign(const Plan& p, const AssignArgs& a, int D, bool lo, hipStream_t s) {
+  static_assert(kChunk == 256, "one assign workgroup covers one histogram chunk");
   dim3 g(p.nchunk, p.BH);
+  const dim3 b(512);
   if (D == 16) {
-    if (lo) SP_LAUNCH((k_kmeans_assign<16, true>), g, dim3(256), s, a);
-    else SP_LAUNCH((k_kmeans_assign<16, false>), g, dim3(256), s, a);
+    if (lo) SP_LAUNCH((k_kmeans_assign<16, true, 256>), g, b, s, a);
+    else SP_LAUNCH((k_kmeans_assign<16, false, 256>), g, b, s, a);
   } else if (D == 32) {
-    if (lo) SP_LAUNCH((k_kmeans_assign<32, true>), g, dim3(256), s, a);
-    else SP_LAUNCH((k_kmeans_assign<32, false>), g, dim3(256), s, a);
+    if (lo) SP_LAUNCH((k_kmeans_assign<32, true, 256>), g, b, s, a);
+    else SP_LAUNCH((k_kmeans_assign<32, false, 256>), g, b, s, a);
   } else if (D == 48) {
-    if (lo) SP_LAUNCH((k_kmeans_assign<48, true>), g, dim3(256), s, a);
-    else SP_LAUNCH((k_kmeans_assign<48, false>), g, dim3(256), s, a);
+    if (lo) SP_LAUNCH((k_kmeans_assign<48, true, 256>), g, b, s, a);
+    else SP_LAUNCH((k_kmeans_assign<48, false, 256>), g, b, s, a);
   } else if (D == 64) {
-    if (lo) SP_LAUNCH((k_kmeans_assign<64, true>), g, dim3(256), s, a);
-    else SP_LAUNCH((k_kmeans_assign<64, false>), g, dim3(256), s, a);
+    if (lo) SP_LAUNCH((k_kmeans_assign<64, true, 128>), g, b, s, a);
+    else SP_LAUNCH((k_kmeans_assign<64, false, 128>), g, b, s, a);
   } else if (D == 128) {
-    if (lo) SP_LAUNCH((k_kmeans_assign<128, true>), g, dim3(256), s, a);
-    else SP_LAUNCH((k_kmeans_assign<128, false>), g, dim3(256), s, a);
+    if (lo) SP_LAUNCH((k_kmeans_assign<128, true, 128>), g, b, s, a);
+    else SP_LAUNCH((k_kmeans_assign<128, false, 128>), g, b, s, a);
   } else {
     return hipErrorInvalidValue;
   }
