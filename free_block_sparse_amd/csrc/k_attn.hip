@@ -212,14 +212,22 @@ __global__ __launch_bounds__(256, 2) void k_sparse_attn_mfma(AttnArgs a) {
   const float c = a.scale * 1.4426950408889634f;
 
   // Wave 0 resolves the physical rows of one tile (virtual key -> segment);
-  // lane j owns key j of every tile, so its segment cursor only moves forward.
-  int cur = 0;
+  // lane j owns key j of every tile, so its segment cursor only moves
+  // forward.  The current segment's virtual start, physical start and the
+  // next segment's virtual start stay in registers: LDS is read only when a
+  // key crosses into the next segment.
+  int cur = 0, cv = seg_v[0], cp = seg_p[0], nv = nseg > 1 ? seg_v[1] : 0x7fffffff;
   auto rows = [&](long long* __restrict__ ofs, const int* __restrict__ sv, const int* __restrict__ sp, int tt) {
     const int v = 64 * tt + lane;
-    int prow = sp[0];  // rows past the end read a valid row; they are masked
+    int prow = cp;  // rows past the end read a valid row; they are masked
     if (v < L) {
-      while (cur + 1 < nseg && sv[cur + 1] <= v) ++cur;
-      prow = sp[cur] + v - sv[cur];
+      while (v >= nv) {
+        ++cur;
+        cv = nv;
+        cp = sp[cur];
+        nv = cur + 1 < nseg ? sv[cur + 1] : 0x7fffffff;
+      }
+      prow = cp + v - cv;
     }
     ofs[lane] = a.kv.row_off(bh, prow);
     ofs[64 + lane] = a.vv.row_off(bh, prow);

@@ -266,8 +266,10 @@ __global__ __launch_bounds__(256) void k_key_coords_mfma(CoordArgs a) {
       for (int q = 0; q < 3; ++q) mp[q][cb][ks] = *reinterpret_cast<const bf16x8*>(pv[q]);
     }
   const bf16_t* kb = static_cast<const bf16_t*>(a.k.p);
-  for (int blk = 0; blk < 2; ++blk) {
-    const int n0 = blockIdx.x * 256 + 64 * w + 32 * blk;
+  // each wave covers 8 consecutive 32-token blocks (the map fragments above
+  // are built once per wave)
+  for (int blk = 0; blk < 8; ++blk) {
+    const int n0 = blockIdx.x * 1024 + 256 * w + 32 * blk;
     if (n0 >= N) break;
     const int n = n0 + col;
     bf16x8 kf[KS];
@@ -905,7 +907,7 @@ hipError_t launch_key_coords(const Plan& p, hipStream_t s) {
   CoordArgs a{p.k, p.kmap, p.N, p.rK, p.rKpad, p.z32, p.zhi, p.zlo};
   dim3 g((p.N + 63) / 64, p.BH);
   if (p.dtype == SPARSEPR_BF16) {
-    const dim3 gm((p.N + 255) / 256, p.BH);
+    const dim3 gm((p.N + 1023) / 1024, p.BH);
     if (p.d == 128) SP_LAUNCH((k_key_coords_mfma<128>), gm, dim3(256), s, a);
     else SP_LAUNCH((k_key_coords_mfma<64>), gm, dim3(256), s, a);
   } else {
