@@ -210,6 +210,7 @@ __global__ __launch_bounds__(1024) void k_fit(FitArgs a) {
   __shared__ double yb[64];
   __shared__ double bp[64];
   __shared__ double edg[128 + 2], eeo[64 + 2], etau[64], evb[64], epb[64], erot[4 * 64];
+  __shared__ double Ycl[SM * 32];  // Y (M x rk) when M <= 64 and rk <= 32
   __shared__ int ectl[8];
   const int bh = blockIdx.x, tid = threadIdx.x, nt = blockDim.x;
   const int M = a.M, d = a.d, Rmax = a.R;  // Rmax: column stride of the W and V outputs
@@ -227,8 +228,8 @@ __global__ __launch_bounds__(1024) void k_fit(FitArgs a) {
   double* U = glds ? Ul : S + 256 * 128 + 128 * 128;                         // ne x ne
   double* Vr = S + 256 * 128 + 2 * 128 * 128;                                // d x Rmax
   double* Wm = Vr + 128 * 64;                                                // d x rk (also the primal rhs)
-  double* Yc = Wm + 128 * 64;                                                // M x rk
-  double* Kp = Yc + 256 * 64;                                                // primal system d x d (M > d)
+  double* Yc = (lds && a.Rcfg <= 32) ? Ycl : Wm + 128 * 64;                 // M x rk
+  double* Kp = Wm + 128 * 64 + 256 * 64;                                     // primal system d x d (M > d)
   const float* ode = a.ode + (long long)bh * M * d;
   const float* osp = a.osp + (long long)bh * M * d;
   const double* w = a.pw + (long long)bh * M;
@@ -311,11 +312,15 @@ __global__ __launch_bounds__(1024) void k_fit(FitArgs a) {
     Vr[dm * Rmax + k] = v;
   }
   block_sync();
-  // Y = R Vr (M x rk), weighted means, centring
+  // Y = R Vr (M x rk); in the dual form R Vr = R R^T U_r / sigma = U_r sigma
   for (int e = tid; e < M * rk; e += nt) {
     const int mm = e / rk, k = e - (e / rk) * rk;
     double acc = 0.0;
-    for (int dm = 0; dm < d; ++dm) acc += (double)Rf[mm * ldx + dm] * Vr[dm * Rmax + k];
+    if (small) {
+      acc = U[mm * ldg + idx_s[k]] * sig_s[k];
+    } else {
+      for (int dm = 0; dm < d; ++dm) acc += (double)Rf[mm * ldx + dm] * Vr[dm * Rmax + k];
+    }
     Yc[mm * rk + k] = acc;
   }
   block_sync();
@@ -355,9 +360,51 @@ __global__ __launch_bounds__(1024) void k_fit(FitArgs a) {
       }
       for (int e = tid; e < M * rk; e += nt) Yc[e] *= sqrt(w[e / rk]);
       block_sync();
-      ok = cholesky_f64(K, M, ldg, &bad);
+      if (M <= 64) {
+        // one wave factors K column by column (lane i owns row i of L, left-
+        // looking dot products), then every wave solves its columns of Y with
+        // lanes as rows: no workgroup barrier inside either
+        const int wv = tid >> 6, ln = tid & 63;
+        if (wv == 0) {
+          bool badl = false;
+          for (int k = 0; k < M; ++k) {
+            const int rl = ln < M ? ln : k;  // idle lanes shadow the pivot row
+            double acc = K[rl * ldg + k];
+            for (int j = 0; j < k; ++j) acc -= K[rl * ldg + j] * K[k * ldg + j];
+            const double piv = __shfl(acc, k, 64);
+            badl |= !(piv > 0.0);
+            const double lkk = sqrt(piv > 0.0 ? piv : 1.0);
+            if (ln == k) K[k * ldg + k] = lkk;
+            else if (ln > k && ln < M) K[ln * ldg + k] = acc / lkk;
+            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+          }
+          if (ln == 0) bad = badl ? 1 : 0;
+        }
+        block_sync();
+        ok = bad == 0;
+        if (ok) {
+          const double dinv = ln < M ? 1.0 / K[ln * ldg + ln] : 0.0;
+          for (int cidx = wv; cidx < rk; cidx += nt >> 6) {
+            double y = ln < M ? Yc[ln * rk + cidx] : 0.0;
+            for (int j = 0; j < M; ++j) {  // L z = y
+              const double zj = __shfl(y * dinv, j, 64);
+              if (ln == j) y = zj;
+              else if (ln > j && ln < M) y -= K[ln * ldg + j] * zj;
+            }
+            for (int i = M - 1; i >= 0; --i) {  // L^T x = z
+              const double xi = __shfl(y * dinv, i, 64);
+              if (ln == i) y = xi;
+              else if (ln < i) y -= K[i * ldg + ln] * xi;
+            }
+            if (ln < M) Yc[ln * rk + cidx] = y;
+          }
+        }
+        block_sync();
+      } else {
+        ok = cholesky_f64(K, M, ldg, &bad);
+        if (ok) chol_solve_f64(K, M, ldg, Yc, rk, rk);
+      }
       if (ok) {
-        chol_solve_f64(K, M, ldg, Yc, rk, rk);
         for (int e = tid; e < d * rk; e += nt) {
           const int dm = e / rk, k = e - (e / rk) * rk;
           double acc = 0.0;
