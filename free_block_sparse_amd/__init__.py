@@ -187,7 +187,8 @@ def sparsepr_attention_with_partition(q, k, v, cfg, q_labels, kv_labels, out=Non
 
 
 def sparsepr_key_metric(q, k, v, cfg, workspace=None, stream=None):
-    """Returns (sample [B*H, M_s] int32, M_K [B*H, d, d], eigenvalues [B*H, d])."""
+    """Returns (sample [B*H, M_s] int32, M_K [B*H, d, d], eigenvalues [B*H, d],
+    key coordinate map [B*H, d, r_K])."""
     torch = _torch()
     B, H, N, d = q.shape
     ms = min(cfg.n_sample_q, N)
@@ -197,10 +198,13 @@ def sparsepr_key_metric(q, k, v, cfg, workspace=None, stream=None):
     smp = torch.empty(B * H, ms, dtype=torch.int32, device=q.device)
     mk = torch.empty(B * H, d, d, dtype=torch.float32, device=q.device)
     ev = torch.empty(B * H, d, dtype=torch.float32, device=q.device)
+    rk = min(cfg.key_coord_rank, d, ms)
+    km = torch.empty(B * H, d, rk, dtype=torch.float32, device=q.device)
     check(lib().sparsepr_key_metric(ctypes.byref(cfg), ctypes.byref(io), buf.data_ptr(), nbytes,
-                                    _stream(stream), smp.data_ptr(), mk.data_ptr(), ev.data_ptr()),
+                                    _stream(stream), smp.data_ptr(), mk.data_ptr(), ev.data_ptr(),
+                                    km.data_ptr()),
           "sparsepr_key_metric")
-    return smp, mk, ev
+    return smp, mk, ev, km
 
 
 def sparsepr_partition(q, k, v, cfg, workspace=None, stream=None):

@@ -99,7 +99,7 @@ _SIGS = {
     "sparsepr_attention_with_partition": (_I, [ctypes.POINTER(SparseprConfig), ctypes.POINTER(SparseprTensors),
                                                _P, _P, _P, ctypes.c_size_t, _P, _P]),
     "sparsepr_key_metric": (_I, [ctypes.POINTER(SparseprConfig), ctypes.POINTER(SparseprTensors), _P,
-                                 ctypes.c_size_t, _P, _P, _P, _P]),
+                                 ctypes.c_size_t, _P, _P, _P, _P, _P]),
     "sparsepr_partition": (_I, [ctypes.POINTER(SparseprConfig), ctypes.POINTER(SparseprTensors), _P,
                                 ctypes.c_size_t, _P, _P, _P]),
     "sparsepr_route": (_I, [ctypes.POINTER(SparseprConfig), ctypes.POINTER(SparseprTensors), _P, _P, _P,

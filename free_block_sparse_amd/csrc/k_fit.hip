@@ -36,7 +36,6 @@ struct FitArgs {
   float* V;
   float* b;
   int* rank;
-  double* sig;
   sparsepr_head_stats* stats;
 };
 
@@ -260,40 +259,70 @@ __global__ __launch_bounds__(1024) void k_fit(FitArgs a) {
     G[i * ldg + j] = acc;
   }
   block_sync();
+  bool fast = false;  // leading eigenpairs by multisection + twisted factorisations
   if (glds) {
-    // Householder tridiagonalisation + shifted QR, everything in LDS
+    // Householder tridiagonalisation, then the leading eigenvalues by
+    // multisection (the rank follows from them) and their vectors by twisted
+    // factorisations; shifted QR on all of them when two leading eigenvalues
+    // cannot be told apart.  Everything in LDS.
     const EigWork<double> ew{G, ldg, U, ldg, edg, eeo, etau, evb, epb, erot, ectl};
     eig_tridiagonalize<double, kFitThreads>(ew, ne);
-    eig_tridiagonal_qr<double, kFitThreads>(ew, ne);
-    eig_back_transform<double, kFitThreads, 16>(ew, ne, nullptr, ne);
+    int nval = a.Rcfg > 4 ? a.Rcfg : 4;
+    if (nval > ne) nval = ne;
+    eig_bisect<double, kFitThreads>(ew, ne, nval);
+    if (tid == 0) {
+      const double* lam = erot + ne;
+      for (int r = 0; r < nval; ++r) {
+        sig_s[r] = sqrt(lam[r] > 0.0 ? lam[r] : 0.0);
+        idx_s[r] = r;
+      }
+      const double s1 = sig_s[0];
+      int cnt = 0;
+      if (s1 > 0.0 && s1 < INFINITY)
+        for (int r = 0; r < nval && r < n; ++r) cnt += sig_s[r] > a.cut * s1;
+      int rk = a.Rcfg;
+      if (M < rk) rk = M;
+      if (d < rk) rk = d;
+      if (cnt < rk) rk = cnt;
+      rk_s = rk;
+    }
+    block_sync();
+    fast = eig_twisted<double, kFitThreads>(ew, ne, rk_s);
+    if (fast) {
+      eig_back_transform<double, kFitThreads, 16>(ew, ne, nullptr, rk_s);
+    } else {
+      eig_tridiagonal_qr<double, kFitThreads>(ew, ne);
+      eig_back_transform<double, kFitThreads, 16>(ew, ne, nullptr, ne);
+    }
   } else {
     jacobi_sym_f64(G, U, ne, rcs, rpq, &stop, red);
     for (int i = tid; i < ne; i += nt) edg[i] = G[i * ne + i];
     block_sync();
   }
-  // eigenvalues, descending with ties by index
-  for (int i = tid; i < ne; i += nt) {
-    const double li = edg[i];
-    int r = 0;
-    for (int j = 0; j < ne; ++j) {
-      const double lj = edg[j];
-      r += (lj > li) || (lj == li && j < i);
+  if (!fast) {
+    // eigenvalues, descending with ties by index
+    for (int i = tid; i < ne; i += nt) {
+      const double li = edg[i];
+      int r = 0;
+      for (int j = 0; j < ne; ++j) {
+        const double lj = edg[j];
+        r += (lj > li) || (lj == li && j < i);
+      }
+      sig_s[r] = sqrt(li > 0.0 ? li : 0.0);
+      idx_s[r] = i;
     }
-    sig_s[r] = sqrt(li > 0.0 ? li : 0.0);
-    idx_s[r] = i;
-  }
-  block_sync();
-  if (tid == 0) {
-    const double s1 = sig_s[0];
-    int cnt = 0;
-    if (s1 > 0.0 && s1 < INFINITY)
-      for (int i = 0; i < n; ++i) cnt += sig_s[i] > a.cut * s1;
-    int rk = a.Rcfg;
-    if (M < rk) rk = M;
-    if (d < rk) rk = d;
-    if (cnt < rk) rk = cnt;
-    rk_s = rk;
-    for (int i = 0; i < kMaxProbe && i < n; ++i) a.sig[(long long)bh * kMaxProbe + i] = sig_s[i];
+    block_sync();
+    if (tid == 0) {
+      const double s1 = sig_s[0];
+      int cnt = 0;
+      if (s1 > 0.0 && s1 < INFINITY)
+        for (int i = 0; i < n; ++i) cnt += sig_s[i] > a.cut * s1;
+      int rk = a.Rcfg;
+      if (M < rk) rk = M;
+      if (d < rk) rk = d;
+      if (cnt < rk) rk = cnt;
+      rk_s = rk;
+    }
   }
   block_sync();
   int rk = rk_s;
@@ -480,7 +509,6 @@ hipError_t launch_fit(const Plan& p, hipStream_t s) {
   a.V = p.fitV;
   a.b = p.fitb;
   a.rank = p.fitrank;
-  a.sig = p.fitsig;
   a.stats = p.stats;
   hipLaunchKernelGGL(k_fit, dim3(p.BH), dim3(kFitThreads), 0, s, a);
   return hipGetLastError();

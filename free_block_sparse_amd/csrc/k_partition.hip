@@ -162,6 +162,7 @@ __global__ __launch_bounds__(1024) void k_key_eig(EigArgs a) {
   __shared__ float rot[4 * D];
   __shared__ int ctl[8];
   __shared__ int top[D];
+  __shared__ float lamv[D];  // eigenvalue of column i of Z
   const int bh = blockIdx.x, tid = threadIdx.x;
   const float* mk = a.mk + (long long)bh * D * D;
   for (int e = tid; e < D * D; e += NT) {
@@ -171,17 +172,31 @@ __global__ __launch_bounds__(1024) void k_key_eig(EigArgs a) {
   __syncthreads();
   const EigWork<float> w{A, LD, Z, LD, dg, eo, tau, vb, pb, rot, ctl};
   eig_tridiagonalize<float, NT>(w, D);
-  eig_tridiagonal_qr<float, NT>(w, D);
-  // rank eigenvalues (descending, ties by index)
-  for (int i = tid; i < D; i += NT) {
-    const float li = dg[i];
-    int rank = 0;
-    for (int j = 0; j < D; ++j) {
-      const float lj = dg[j];
-      rank += (lj > li) || (lj == li && j < i);
+  // every eigenvalue by multisection (all of them are reported), vectors
+  // of the leading rK by twisted factorisations; shifted QR when two of the
+  // leading eigenvalues cannot be told apart
+  eig_bisect<float, NT>(w, D, D);
+  for (int i = tid; i < D; i += NT) lamv[i] = rot[D + i];
+  __syncthreads();
+  if (eig_twisted<float, NT>(w, D, a.rK)) {
+    for (int i = tid; i < D; i += NT) {
+      if (a.eigval) a.eigval[(long long)bh * D + i] = lamv[i];
+      if (i < a.rK) top[i] = i;
     }
-    if (a.eigval) a.eigval[(long long)bh * D + rank] = li;
-    if (rank < a.rK) top[rank] = i;
+  } else {
+    eig_tridiagonal_qr<float, NT>(w, D);
+    // rank eigenvalues (descending, ties by index)
+    for (int i = tid; i < D; i += NT) {
+      const float li = dg[i];
+      int rank = 0;
+      for (int j = 0; j < D; ++j) {
+        const float lj = dg[j];
+        rank += (lj > li) || (lj == li && j < i);
+      }
+      if (a.eigval) a.eigval[(long long)bh * D + rank] = li;
+      if (rank < a.rK) top[rank] = i;
+      lamv[i] = li;
+    }
   }
   __syncthreads();
   eig_back_transform<float, NT, 32>(w, D, top, a.rK);
@@ -190,7 +205,7 @@ __global__ __launch_bounds__(1024) void k_key_eig(EigArgs a) {
   for (int e = tid; e < D * a.rK; e += NT) {
     const int r = e / D, k = e - (e / D) * D;
     const int i = top[r];
-    const float f = a.scale * sqrtf(fmaxf(dg[i], 0.f));
+    const float f = a.scale * sqrtf(fmaxf(lamv[i], 0.f));
     km[k * a.rK + r] = f * Z[k * LD + i];
   }
 }

@@ -333,7 +333,7 @@ sparsepr_status sparsepr_attention_with_partition(const sparsepr_config* cfg, co
 
 sparsepr_status sparsepr_key_metric(const sparsepr_config* cfg, const sparsepr_tensors* io, void* workspace,
                                     size_t workspace_bytes, void* stream, int* sample_idx, float* m_k,
-                                    float* eigvals) {
+                                    float* eigvals, float* key_map) {
   Plan p;
   SPCHK(prepare(p, cfg, io, workspace, workspace_bytes));
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -342,6 +342,7 @@ sparsepr_status sparsepr_key_metric(const sparsepr_config* cfg, const sparsepr_t
   SPCHK(copy_out(sample_idx, p.sample, (long long)p.BH * p.Ms, s));
   SPCHK(copy_out(m_k, p.mk, (long long)p.BH * p.d * p.d, s));
   SPCHK(copy_out(eigvals, p.eigval, (long long)p.BH * p.d, s));
+  SPCHK(copy_out(key_map, p.kmap, (long long)p.BH * p.d * p.rK, s));
   return SPARSEPR_OK;
 }
 

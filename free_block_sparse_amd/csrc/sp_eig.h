@@ -11,8 +11,19 @@
 //      the scalar chase.
 //   3. Back-transformation of the requested columns of Z by the reflectors.
 //
+// When only some eigenpairs are wanted, step 2 is replaced by
+//   2'. eigenvalues by multisection on Sturm counts (every eigenvalue gets a
+//       group of threads that split its bracket into P+1 parts per round),
+//       eigenvectors of T by one twisted factorisation each (the forward and
+//       backward LDL^T pivots of T - lambda I meet at the index where the
+//       twisted pivot is smallest; the vector follows from that index
+//       outwards), Gram-Schmidt inside clusters of close eigenvalues, and the
+//       shifted QR of step 2 as the fallback when two wanted eigenvalues are
+//       too close to tell apart.
+//
 // Standard dense symmetric eigenvalue algorithms (reduction to tridiagonal
-// form, shifted QR); written for a single GPU workgroup.
+// form, shifted QR, Sturm-sequence bisection, inverse iteration by twisted
+// factorisations); written for a single GPU workgroup.
 
 #pragma once
 
@@ -30,6 +41,17 @@ template <>
 struct EigEps<double> {
   static constexpr double v = 2.220446049250313e-16;
 };
+// smallest normal number
+template <typename T>
+struct EigTiny;
+template <>
+struct EigTiny<float> {
+  static constexpr float v = 1.1754944e-38f;
+};
+template <>
+struct EigTiny<double> {
+  static constexpr double v = 2.2250738585072014e-308;
+};
 
 // 1 / sqrt(q) for q > 0: the hardware estimate, refined by one Newton step in
 // fp64 (the fp32 estimate is already within about an ulp).
@@ -37,6 +59,17 @@ __device__ inline float eig_rsqrt(float q) { return __builtin_amdgcn_rsqf(q); }
 __device__ inline double eig_rsqrt(double q) {
   const double y = __builtin_amdgcn_rsq(q);
   return y * (1.5 - 0.5 * q * y * y);
+}
+
+// 1 / x for the Sturm and twisted-factorisation recurrences: the hardware
+// estimate (fp32, about an ulp) or the fp64 estimate refined by two Newton
+// steps.  A relative error of a few ulps in a pivot is absorbed in the
+// backward error of both recurrences.
+__device__ inline float eig_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
+__device__ inline double eig_rcp(double x) {
+  double y = __builtin_amdgcn_rcp(x);
+  y = fma(y, fma(-x, y, 1.0), y);
+  return fma(y, fma(-x, y, 1.0), y);
 }
 
 template <typename T>
@@ -288,6 +321,178 @@ __device__ void eig_tridiagonal_qr(const EigWork<T>& w, int n) {
     __syncthreads();
     if (w.ctl[2 + 2 * b] < 0) break;  // converged; step t-1 was applied above
   }
+}
+
+// Number of eigenvalues of T below x (negative pivots of T - x I), with
+// pivots smaller than pivmin pushed to -pivmin.  e2 holds the squared
+// off-diagonal.
+template <typename T>
+__device__ inline int eig_sturm(const T* d, const T* e2, int n, T x, T pivmin) {
+  T q = d[0] - x;
+  int c = q <= pivmin;
+  q = q <= pivmin ? fmin(q, -pivmin) : q;
+  for (int i = 1; i < n; ++i) {
+    q = (d[i] - x) - e2[i - 1] * eig_rcp(q);
+    c += q <= pivmin;
+    q = q <= pivmin ? fmin(q, -pivmin) : q;
+  }
+  return c;
+}
+
+// Step 2', eigenvalues: the nval largest eigenvalues of T (w.dg, w.eo),
+// descending, into w.rot[n + r].  Leaves the squared off-diagonal in
+// w.rot[0, n) and ||T|| (Gershgorin), pivmin in w.rot[2n], w.rot[2n + 1].
+// Brackets shrink until they are below eps * ||T|| or two ulps of the
+// eigenvalue.  Every thread calls it.
+template <typename T, int NT>
+__device__ void eig_bisect(const EigWork<T>& w, int n, int nval) {
+  const int tid = threadIdx.x;
+  T* e2 = w.rot;
+  T* lam = w.rot + n;
+  T* sc = w.rot + 2 * n;
+  const T* d = w.dg;
+  const T eps = EigEps<T>::v;
+  if (tid < 64) {
+    T lo = T(3.0e38), hi = T(-3.0e38), em = 0;
+    for (int i = tid; i < n; i += 64) {
+      const T ea = i + 1 < n ? fabs(w.eo[i]) : T(0);
+      const T eb = i > 0 ? fabs(w.eo[i - 1]) : T(0);
+      if (i + 1 < n) e2[i] = w.eo[i] * w.eo[i];
+      lo = fmin(lo, d[i] - ea - eb);
+      hi = fmax(hi, d[i] + ea + eb);
+      em = fmax(em, ea * ea);
+    }
+    for (int o = 32; o > 0; o >>= 1) {
+      lo = fmin(lo, __shfl_xor(lo, o, 64));
+      hi = fmax(hi, __shfl_xor(hi, o, 64));
+      em = fmax(em, __shfl_xor(em, o, 64));
+    }
+    if (tid == 0) {
+      const T tn = fmax(fabs(lo), fabs(hi));
+      const T pivmin = T(EigTiny<T>::v) * fmax(T(1), em);
+      const T pad = T(2) * tn * eps * T(n) + T(2) * pivmin;
+      sc[0] = tn;
+      sc[1] = pivmin;
+      sc[2] = lo - pad;
+      sc[3] = hi + pad;
+    }
+  }
+  __syncthreads();
+  // group of P threads per eigenvalue (P a power of two, within one wave)
+  int P = 64;
+  while (P > 1 && P * nval > NT) P >>= 1;
+  const int r = tid / P, sub = tid - (tid / P) * P;
+  if (r < nval) {
+    const T tn = sc[0], pivmin = sc[1];
+    const T atol = eps * tn;
+    const int idx = n - 1 - r;  // ascending index of the r-th largest
+    T lo = sc[2], hi = sc[3];
+    const int gbase = (tid & 63) - sub;
+    const unsigned long long gmask = (P == 64 ? ~0ull : ((1ull << P) - 1ull)) << gbase;
+    for (int it = 0; it < 256; ++it) {
+      const T wd = hi - lo;
+      if (!(wd > fmax(atol, T(2) * eps * fmax(fabs(lo), fabs(hi))))) break;
+      const T step = wd / T(P + 1);
+      const T x = lo + T(sub + 1) * step;
+      const bool above = eig_sturm(d, e2, n, x, pivmin) > idx;
+      const unsigned long long m = __builtin_amdgcn_ballot_w64(above) & gmask;
+      const int t = m ? __builtin_ctzll(m) - gbase : P;  // first point above the eigenvalue
+      const T nhi = t < P ? lo + T(t + 1) * step : hi;
+      const T nlo = t > 0 ? lo + T(t) * step : lo;
+      if (nhi == hi && nlo == lo) break;
+      lo = nlo;
+      hi = nhi;
+    }
+    if (sub == 0) lam[r] = (lo + hi) * T(0.5);
+  }
+  __syncthreads();
+}
+
+// Step 2', eigenvectors: for r < nvec, column r of Z gets the unit
+// eigenvector of T for lam[r] = w.rot[n + r] (as left by eig_bisect).
+// Columns [nvec, 2 nvec) of Z are scratch, so 2 nvec <= n is required.
+// Returns false (all threads) when two of the wanted eigenvalues are closer
+// than a few ulps of ||T|| or 2 nvec > n; Z then holds nothing useful.
+template <typename T, int NT>
+__device__ bool eig_twisted(const EigWork<T>& w, int n, int nvec) {
+  const int tid = threadIdx.x;
+  const T* e = w.eo;
+  const T* d = w.dg;
+  const T* lam = w.rot + n;
+  const T tn = w.rot[2 * n], pivmin = w.rot[2 * n + 1];
+  const T eps = EigEps<T>::v;
+  T* Z = w.Z;
+  const int ldz = w.ldz;
+  if (2 * nvec > n) return false;
+  for (int r = 1; r < nvec; ++r)
+    if (lam[r - 1] - lam[r] <= T(8) * eps * tn) return false;
+  if (tid < nvec) {
+    const int r = tid;
+    const T l = lam[r];
+    T* zc = Z + r;          // l_i, later x_i
+    T* uc = Z + nvec + r;   // dplus_i, later u_{i-1}
+    T dp = d[0] - l;
+    for (int i = 0; i + 1 < n; ++i) {
+      if (fabs(dp) < pivmin) dp = dp < T(0) ? -pivmin : pivmin;
+      const T li = e[i] * eig_rcp(dp);
+      uc[i * ldz] = dp;
+      zc[i * ldz] = li;
+      dp = (d[i + 1] - l) - li * e[i];
+    }
+    if (fabs(dp) < pivmin) dp = dp < T(0) ? -pivmin : pivmin;
+    T dm = d[n - 1] - l;
+    // twisted pivot gamma_k = dplus_k + dminus_k - (d_k - lambda)
+    T best = fabs(dp);
+    int tw = n - 1;
+    for (int i = n - 2; i >= 0; --i) {
+      if (fabs(dm) < pivmin) dm = dm < T(0) ? -pivmin : pivmin;
+      const T ui = e[i] * eig_rcp(dm);
+      const T dpi = uc[i * ldz];
+      uc[(i + 1) * ldz] = ui;
+      const T g = fabs(dpi - ui * e[i]);
+      if (g < best) {
+        best = g;
+        tw = i;
+      }
+      dm = (d[i] - l) - ui * e[i];
+    }
+    T x = T(1), ss = T(1);
+    zc[tw * ldz] = x;
+    for (int i = tw - 1; i >= 0; --i) {
+      x = -zc[i * ldz] * x;
+      zc[i * ldz] = x;
+      ss += x * x;
+    }
+    x = T(1);
+    for (int i = tw; i + 1 < n; ++i) {
+      x = -uc[(i + 1) * ldz] * x;
+      zc[(i + 1) * ldz] = x;
+      ss += x * x;
+    }
+    const T inv = eig_rsqrt(ss);
+    for (int i = 0; i < n; ++i) zc[i * ldz] *= inv;
+  }
+  __syncthreads();
+  // Gram-Schmidt against the earlier members of a cluster (gap below
+  // 1e-3 ||T||), one wave, columns in order
+  if (tid < 64) {
+    const T ctol = T(1e-3) * tn;
+    for (int r = 1; r < nvec; ++r) {
+      if (lam[r - 1] - lam[r] >= ctol) continue;
+      for (int q = r - 1; q >= 0 && lam[q] - lam[r] < ctol; --q) {
+        T dt = 0;
+        for (int i = tid; i < n; i += 64) dt += Z[i * ldz + q] * Z[i * ldz + r];
+        dt = eig_sum(dt, 64);
+        for (int i = tid; i < n; i += 64) Z[i * ldz + r] -= dt * Z[i * ldz + q];
+      }
+      T nr = 0;
+      for (int i = tid; i < n; i += 64) nr += Z[i * ldz + r] * Z[i * ldz + r];
+      const T inv = eig_rsqrt(eig_sum(nr, 64));
+      for (int i = tid; i < n; i += 64) Z[i * ldz + r] *= inv;
+    }
+  }
+  __syncthreads();
+  return true;
 }
 
 // Step 3: Z[:, cols[c]] <- Q Z[:, cols[c]] for c < ncol (cols == nullptr: c).

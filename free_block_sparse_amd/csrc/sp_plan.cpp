@@ -177,7 +177,6 @@ void plan_carve(Plan* p, char* base) {
   p->fitV = c.take<float>(BH * d * R);
   p->fitb = c.take<float>(BH * d);
   p->fitrank = c.take<int>(BH);
-  p->fitsig = c.take<double>(BH * kMaxProbe);
   p->fitscratch = c.take<double>(BH * kFitScratchDoubles);
   p->stats = c.take<sparsepr_head_stats>(BH);
   p->ws_bytes = (c.off + 255) & ~(size_t)255;

@@ -89,7 +89,6 @@ struct Plan {
   float* fitV;            // [BH, d, R]
   float* fitb;            // [BH, d]
   int* fitrank;           // [BH]
-  double* fitsig;         // [BH, kMaxProbe]
   double* fitscratch;     // [BH, kFitScratchDoubles]
   sparsepr_head_stats* stats;  // [BH]
 

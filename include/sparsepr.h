@@ -185,13 +185,16 @@ sparsepr_status sparsepr_attention_with_partition(const sparsepr_config* cfg,
                                                   void* workspace, size_t workspace_bytes,
                                                   void* stream, sparsepr_head_stats* stats);
 
-/* Stage a1-a2 ([TS] 2.A): the sampled query rows (device int32 [B*H, M_s],
-   ascending), M_K = Q_s^T Q_s / M_s (device float [B*H, d, d]) and the
-   eigenvalues of M_K in descending order (device float [B*H, d]).  Any output
-   pointer may be NULL. */
+/* Stages a1-a2 ([TS] 2.A): the sampled query rows (device int32 [B*H, M_s],
+   ascending), M_K = Q_s^T Q_s / M_s (device float [B*H, d, d]), the
+   eigenvalues of M_K in descending order (device float [B*H, d]) and the key
+   coordinate map (device float [B*H, d, r_K], row-major: column r is
+   s sqrt(lambda_r) u_r for the r-th largest eigenpair, r_K =
+   min(key_coord_rank, d, M_s); the sign of each column is unspecified).  Any
+   output pointer may be NULL. */
 sparsepr_status sparsepr_key_metric(const sparsepr_config* cfg, const sparsepr_tensors* io,
                                     void* workspace, size_t workspace_bytes, void* stream,
-                                    int* sample_idx, float* m_k, float* eigvals);
+                                    int* sample_idx, float* m_k, float* eigvals, float* key_map);
 
 /* Stages a1-a8: response-coupled (or independent) partition.  Writes the
    labels of the last Lloyd step (device int32 [B*H, N] each). */

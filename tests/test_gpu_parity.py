@@ -56,7 +56,7 @@ def test_key_metric_sample_and_spectrum(name):
         pytest.skip("no key metric in the independent partition")
     banner(name, "key_metric")
     q, k, v = dev_inputs(name)
-    smp, mk, ev = sp.sparsepr_key_metric(q, k, v, lib_cfg(name))
+    smp, mk, ev, km = sp.sparsepr_key_metric(q, k, v, lib_cfg(name))
     torch.cuda.synchronize()
     for h, r in enumerate(oracle_result(name)):
         assert np.array_equal(smp[h].cpu().numpy(), r["sample"])  # integer spec: bit-exact
@@ -64,11 +64,60 @@ def test_key_metric_sample_and_spectrum(name):
         assert rel_frob(mk_gpu, r["m_k"]) < 1e-5
         lam_ref = np.sort(np.linalg.eigvalsh(r["m_k"]))[::-1]
         lam = ev[h].cpu().double().numpy()
-        # Weyl: eigenvalues move by at most ||dM||_2 <= ||dM||_F; fp32 Jacobi adds a
-        # backward error of order n eps ||M||_F per sweep (at most 10 sweeps here)
+        # Weyl: eigenvalues move by at most ||dM||_2 <= ||dM||_F; the fp32
+        # reduction and bisection add a backward error of order n eps ||M||_F
         n = mk_gpu.shape[0]
         bound = np.linalg.norm(mk_gpu - r["m_k"]) + 10 * n * 6e-8 * np.linalg.norm(r["m_k"])
         assert np.abs(lam - lam_ref).max() <= bound
+        check_key_map(km[h].cpu().double().numpy(), mk_gpu, r["scale"])
+
+
+def check_key_map(km, mk, s):
+    """km km^T must equal s^2 U_r Lambda_r U_r^T for the leading r eigenpairs of
+    the metric the library computed (sign- and rotation-free within clusters)."""
+    r = km.shape[1]
+    lam, vec = np.linalg.eigh(mk)
+    lam, vec = lam[::-1], vec[:, ::-1]
+    ref = (s * s) * (vec[:, :r] * np.clip(lam[:r], 0, None)) @ vec[:, :r].T
+    got = km @ km.T
+    gap = lam[r - 1] - lam[r] if r < len(lam) else lam[0]
+    tol = 50 * 1.2e-7 * (1.0 + lam[0] / max(gap, 1e-30))
+    err = np.linalg.norm(got - ref) / np.linalg.norm(ref)
+    print(f"[parity] key map rel err {err:.2e} (tol {tol:.2e}, boundary gap {gap / lam[0]:.2e} of lambda_1)",
+          flush=True)
+    assert err <= tol
+
+
+@pytest.mark.parametrize("kind", ["close_pairs", "repeated_top"])
+def test_key_map_with_clustered_spectrum(kind):
+    """Metrics whose leading eigenvalues sit in tight clusters (relative gaps
+    1e-4 and 1e-3, or exactly repeated): the eigenvectors of the clusters are
+    orthogonalised against each other, and exact repeats take the shifted-QR
+    path; both must reproduce the leading eigenspaces."""
+    n, d, rk = 256, 64, 16
+    print(f"[parity] key_map clustered spectrum kind={kind} N={n} d={d} r_K={rk} fp32", flush=True)
+    rng = np.random.default_rng(7)
+    lam = np.geomspace(1.0, 0.02, d)
+    if kind == "close_pairs":
+        lam[3] = lam[2] * (1 - 1e-4)
+        lam[7] = lam[6] * (1 - 1e-3)
+        lam[8] = lam[7] * (1 - 1e-4)
+    else:
+        lam[1:4] = lam[1]
+        lam[9:11] = lam[9]
+    u, _ = np.linalg.qr(rng.standard_normal((n, d)))
+    v, _ = np.linalg.qr(rng.standard_normal((d, d)))
+    q = (np.sqrt(n) * (u * np.sqrt(lam)) @ v.T).astype(np.float32)
+    qt = torch.from_numpy(q).reshape(1, 1, n, d).cuda()
+    cfg = sp.make_config(n, d, n_sample_q=256, key_coord_rank=rk, n_kv_groups=4, n_q_groups=4,
+                         probe_rows=8, residual_rank=4)
+    smp, mk, ev, km = sp.sparsepr_key_metric(qt, qt.clone(), qt.clone(), cfg)
+    torch.cuda.synchronize()
+    assert np.array_equal(np.sort(smp[0].cpu().numpy()), np.arange(n))
+    mk64 = mk[0].cpu().double().numpy()
+    lam_ref = np.sort(np.linalg.eigvalsh(mk64))[::-1]
+    assert np.abs(ev[0].cpu().double().numpy() - lam_ref).max() <= 10 * d * 6e-8 * np.linalg.norm(mk64)
+    check_key_map(km[0].cpu().double().numpy(), mk64, float(np.float32(1.0 / np.sqrt(d))))
 
 
 @pytest.mark.parametrize("name", ALL)
@@ -172,7 +221,7 @@ def test_end_to_end_partition_agreement_and_error(name):
     out = sp.sparsepr_attention(q, k, v, cfg)
     mk = None
     if c.mode == "response_coupled":
-        _, mk, _ = sp.sparsepr_key_metric(q, k, v, cfg)
+        _, mk, _, _ = sp.sparsepr_key_metric(q, k, v, cfg)
     torch.cuda.synchronize()
     for h, r in enumerate(oracle_result(name)):
         kl_h, ql_h = kl[h].cpu().numpy(), ql[h].cpu().numpy()
