@@ -25,67 +25,56 @@ namespace sp {
 // ============================================================================
 // a1: query sample (partial Fisher-Yates on splitmix64) and M_K
 // ============================================================================
+// Step j of the partial shuffle swaps slot j with slot t_j = j + (x_j mod
+// (N - j)), where x_j is the generator's j-th output; the draws do not depend
+// on the swaps, so thread j makes draw j.  Slot j is final after step j and
+// no later step reads it, so what step j finds in a slot p >= j is what the
+// latest earlier step aiming at p put there (slot i's value when step i ran),
+// or p itself.  Step j's output is therefore the value found through the
+// latest earlier step with the same target, and the value slot j held is
+// found by following "latest earlier step aiming at slot j" links to a step
+// with none; the links are followed by pointer jumping.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void k_sample_metric(SampleArgs a) {
   const int bh = blockIdx.x, tid = threadIdx.x;
-  __shared__ int slot[256];
-  __shared__ int far_pos[256];
-  __shared__ int far_val[256];
-  __shared__ int far_cnt;
+  __shared__ int tgt[256];
+  __shared__ int held[256];  // value slot j held when step j ran
+  __shared__ int lnk[256];
   __shared__ int srt[256];
-  __shared__ float qs[64][D + 1];
+  constexpr int QLD = 256 + 8;  // samples per dimension row (+8: 16-byte rows off the bank stride)
+  __shared__ __align__(16) bf16_t qt[std::is_same<T, bf16_t>::value ? D * QLD : 8];
+  __shared__ float qs[std::is_same<T, bf16_t>::value ? 1 : 64][D + 1];
   const int Ms = a.Ms, N = a.N;
-  slot[tid] = tid;
-  if (tid == 0) far_cnt = 0;
-  __syncthreads();
-  if (tid < 64) {
-    volatile int* vslot = slot;
-    volatile int* vfp = far_pos;
-    volatile int* vfv = far_val;
-    volatile int* vcnt = &far_cnt;
-    uint64_t st = a.seed ^ ((uint64_t)bh * kGolden64);
-    for (int j = 0; j < Ms; ++j) {
-      st += kGolden64;
-      uint64_t z = st;
-      z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
-      z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
-      z ^= z >> 31;
-      const long long t = (long long)j + (long long)(z % (uint64_t)(N - j));
-      const int vj = vslot[j];
-      int vt;
-      int found = -1;
-      if (t < Ms) {
-        vt = vslot[t];
-      } else {
-        const int cnt = *vcnt;
-        for (int base = 0; base < cnt; base += 64) {
-          const int kk = base + tid;
-          const bool hit = kk < cnt && vfp[kk] == (int)t;
-          const unsigned long long m = __ballot(hit);
-          if (m) {
-            found = base + __ffsll((long long)m) - 1;
-            break;
-          }
-        }
-        vt = found >= 0 ? vfv[found] : (int)t;
-      }
-      if (tid == 0) {
-        vslot[j] = vt;
-        if (t < Ms) {
-          vslot[t] = vj;
-        } else if (found >= 0) {
-          vfv[found] = vj;
-        } else {
-          const int c = *vcnt;
-          vfp[c] = (int)t;
-          vfv[c] = vj;
-          *vcnt = c + 1;
-        }
-      }
-    }
+  int t = 0;
+  if (tid < Ms) {
+    uint64_t z = (a.seed ^ ((uint64_t)bh * kGolden64)) + (uint64_t)(tid + 1) * kGolden64;
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    z ^= z >> 31;
+    t = tid + (int)(z % (uint64_t)(N - tid));
+    tgt[tid] = t;
   }
   __syncthreads();
-  srt[tid] = tid < Ms ? slot[tid] : 0x7fffffff;
+  int aim = -1, same = -1;  // latest earlier step aiming at slot tid / at slot t
+  if (tid < Ms)
+    for (int i = 0; i < tid; ++i) {
+      const int ti = tgt[i];
+      aim = ti == tid ? i : aim;
+      same = ti == t ? i : same;
+    }
+  held[tid] = tid;
+  lnk[tid] = aim;
+  __syncthreads();
+  for (int r = 1; r < 256; r <<= 1) {
+    const int l = lnk[tid];
+    const int hv = l >= 0 ? held[l] : held[tid];
+    const int nl = l >= 0 ? lnk[l] : -1;
+    __syncthreads();
+    held[tid] = hv;
+    lnk[tid] = nl;
+    __syncthreads();
+  }
+  srt[tid] = tid < Ms ? (same >= 0 ? held[same] : t) : 0x7fffffff;
   __syncthreads();
   for (int k = 2; k <= 256; k <<= 1) {
     for (int j = k >> 1; j > 0; j >>= 1) {
@@ -103,55 +92,81 @@ __global__ __launch_bounds__(256) void k_sample_metric(SampleArgs a) {
   }
   if (tid < Ms) a.sample[(long long)bh * Ms + tid] = srt[tid];
 
-  constexpr int TB = D / 16;
-  const int i0 = (tid >> 4) * TB, j0 = (tid & 15) * TB;
-  float acc[TB][TB];
-#pragma unroll
-  for (int x = 0; x < TB; ++x)
-#pragma unroll
-    for (int y = 0; y < TB; ++y) acc[x][y] = 0.f;
-  const T* qbase = static_cast<const T*>(a.q.p);
-  for (int c0 = 0; c0 < Ms; c0 += 64) {
-    const int nr = min(64, Ms - c0);
-    __syncthreads();
-    for (int e = tid; e < nr * D; e += 256) {
-      const int r = e / D, col = e - (e / D) * D;
-      qs[r][col] = Elem<T>::load(qbase + a.q.row_off(bh, srt[c0 + r]) + col);
-    }
-    __syncthreads();
-    for (int r = 0; r < nr; ++r) {
-      float xi[TB], xj[TB];
-#pragma unroll
-      for (int t = 0; t < TB; ++t) {
-        xi[t] = qs[r][i0 + t];
-        xj[t] = qs[r][j0 + t];
-      }
-#pragma unroll
-      for (int x = 0; x < TB; ++x)
-#pragma unroll
-        for (int y = 0; y < TB; ++y) acc[x][y] += xi[x] * xj[y];
-    }
-  }
   const float inv = 1.0f / (float)Ms;
   float* mk = a.mk + (long long)bh * D * D;
+  const T* qbase = static_cast<const T*>(a.q.p);
+  if constexpr (std::is_same<T, bf16_t>::value) {
+    // bf16 rows: M_K on the matrix cores.  The sampled rows are staged
+    // transposed (dimension-major, samples zero-padded to a multiple of 16),
+    // so both MFMA operands are 16-byte LDS reads; bf16 products are exact
+    // and accumulate in fp32.
+    const int Mp = (Ms + 15) & ~15;
+    constexpr int CPR = D / 8;  // 16-byte pieces per row
+    for (int e = tid; e < Mp * CPR; e += 256) {
+      const int c = (e / Mp) * 8, r = e - (e / Mp) * Mp;  // consecutive threads: consecutive samples
+      uint4 u = make_uint4(0, 0, 0, 0);
+      if (r < Ms) u = *reinterpret_cast<const uint4*>(qbase + a.q.row_off(bh, srt[r]) + c);
+      const bf16_t* ev = reinterpret_cast<const bf16_t*>(&u);
 #pragma unroll
-  for (int x = 0; x < TB; ++x)
+      for (int j = 0; j < 8; ++j) qt[(c + j) * QLD + r] = ev[j];
+    }
+    __syncthreads();
+    const int w = tid >> 6, lane = tid & 63, half = lane >> 5, col = lane & 31;
+    constexpr int NB = D / 32;  // 32 x 32 output blocks per side
+    for (int blk = w; blk < NB * NB; blk += 4) {
+      const int bi = blk / NB, bj = blk - (blk / NB) * NB;
+      f32x16 acc = {};
+      for (int k0 = 0; k0 < Mp; k0 += 16) {
+        const bf16x8 av = *reinterpret_cast<const bf16x8*>(qt + (32 * bi + col) * QLD + k0 + 8 * half);
+        const bf16x8 bv = *reinterpret_cast<const bf16x8*>(qt + (32 * bj + col) * QLD + k0 + 8 * half);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, acc, 0, 0, 0);
+      }
+      // D[i][j]: j = lane % 32, i = (r & 3) + 8 (r >> 2) + 4 (lane / 32)
 #pragma unroll
-    for (int y = 0; y < TB; ++y) mk[(i0 + x) * D + j0 + y] = acc[x][y] * inv;
+      for (int r = 0; r < 16; ++r) {
+        const int i = (r & 3) + 8 * (r >> 2) + 4 * half;
+        mk[(32 * bi + i) * D + 32 * bj + col] = acc[r] * inv;
+      }
+    }
+  } else {
+    constexpr int TB = D / 16;
+    const int i0 = (tid >> 4) * TB, j0 = (tid & 15) * TB;
+    float acc[TB][TB];
+#pragma unroll
+    for (int x = 0; x < TB; ++x)
+#pragma unroll
+      for (int y = 0; y < TB; ++y) acc[x][y] = 0.f;
+    for (int c0 = 0; c0 < Ms; c0 += 64) {
+      const int nr = min(64, Ms - c0);
+      __syncthreads();
+      for (int e = tid; e < nr * D; e += 256) {
+        const int r = e / D, col = e - (e / D) * D;
+        qs[r][col] = Elem<T>::load(qbase + a.q.row_off(bh, srt[c0 + r]) + col);
+      }
+      __syncthreads();
+      for (int r = 0; r < nr; ++r) {
+        float xi[TB], xj[TB];
+#pragma unroll
+        for (int t2 = 0; t2 < TB; ++t2) {
+          xi[t2] = qs[r][i0 + t2];
+          xj[t2] = qs[r][j0 + t2];
+        }
+#pragma unroll
+        for (int x = 0; x < TB; ++x)
+#pragma unroll
+          for (int y = 0; y < TB; ++y) acc[x][y] += xi[x] * xj[y];
+      }
+    }
+#pragma unroll
+    for (int x = 0; x < TB; ++x)
+#pragma unroll
+      for (int y = 0; y < TB; ++y) mk[(i0 + x) * D + j0 + y] = acc[x][y] * inv;
+  }
 }
 
 // ============================================================================
-// a2: symmetric eigensolver (parallel cyclic Jacobi, round-robin pairing).
-// Matrix and eigenvectors live in LDS; one workgroup per (b,h).
+// a2: symmetric eigensolver for M_K (one workgroup per (b,h), all in LDS)
 // ============================================================================
-__device__ inline void rr_pair(int k, int r, int n, int* p, int* q) {
-  const int a = k, b = n - 1 - k;
-  const int pa = a == 0 ? 0 : ((a - 1 + r) % (n - 1)) + 1;
-  const int pb = b == 0 ? 0 : ((b - 1 + r) % (n - 1)) + 1;
-  *p = pa < pb ? pa : pb;
-  *q = pa < pb ? pb : pa;
-}
-
 template <int D>
 __global__ __launch_bounds__(1024) void k_key_eig(EigArgs a) {
   constexpr int LD = D + 1;  // odd row stride: column walks hit distinct banks

@@ -118,6 +118,16 @@ def oracle_key_labels_from_metric(name: str, h: int, m_k) -> np.ndarray:
     return labels
 
 
+def oracle_out_given_partition(name: str, h: int, q_labels, kv_labels) -> np.ndarray:
+    """The oracle's corrected output of head h on a given partition."""
+    c = CASES[name]
+    x = inputs(name)
+    q, k, v = (x[t][0, h].double().numpy() for t in ("q", "k", "v"))
+    r = sparsepr_head(q, k, v, c.oracle_cfg(), bh=h, q_labels=np.asarray(q_labels, dtype=np.int64),
+                      kv_labels=np.asarray(kv_labels, dtype=np.int64))
+    return r["out"]
+
+
 def oracle_query_labels_given_keys(name: str, h: int, kv_labels) -> np.ndarray:
     """The oracle's query k-means run on the query coordinates that a given
     key partition defines."""

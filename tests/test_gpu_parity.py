@@ -13,8 +13,8 @@ import pytest
 import torch
 
 import free_block_sparse_amd as sp
-from parity_cases import (CASES, inputs, max_abs, oracle_key_labels_from_metric, oracle_query_labels_given_keys,
-                          oracle_result, rel_frob, tolerances)
+from parity_cases import (CASES, inputs, max_abs, oracle_key_labels_from_metric, oracle_out_given_partition,
+                          oracle_query_labels_given_keys, oracle_result, rel_frob, tolerances)
 
 pytestmark = pytest.mark.gpu
 
@@ -211,7 +211,9 @@ def test_end_to_end_partition_agreement_and_error(name):
     M_K by 1e-7 (relative, below fp32 rounding of M_K) moves the oracle's own
     query partition to ~91% agreement in half the trials, so no fp32
     computation of M_K can promise the unconditional figure there (it is
-    printed).
+    printed).  The error bar follows the same reading: the GPU's error is held
+    to 1.1x the oracle's error on the GPU's partition, and also to 1.1x the
+    oracle's own error wherever the two partitions agree unconditionally.
     """
     banner(name, "attention")
     c = CASES[name]
@@ -236,10 +238,13 @@ def test_end_to_end_partition_agreement_and_error(name):
         raw_q = (ql_h == r["q_labels"]).mean()
         err_gpu = rel_frob(out[0, h].double().cpu().numpy(), r["dense"])
         err_ora = rel_frob(r["out"], r["dense"])
+        err_cond = rel_frob(oracle_out_given_partition(name, h, ql_h, kl_h), r["dense"])
         print(f"  head {h}: agreement K {agree_k:.4f} Q {agree_q:.4f} (unconditional K {raw_k:.4f} Q {raw_q:.4f}); "
-              f"err vs dense gpu {err_gpu:.4f} oracle {err_ora:.4f}")
+              f"err vs dense gpu {err_gpu:.4f} oracle {err_ora:.4f} oracle on the GPU partition {err_cond:.4f}")
         assert agree_k >= 0.99 and agree_q >= 0.99
-        assert err_gpu <= 1.1 * err_ora
+        assert err_gpu <= 1.1 * err_cond
+        if raw_k >= 0.99 and raw_q >= 0.99:
+            assert err_gpu <= 1.1 * err_ora
 
 
 @pytest.mark.parametrize("name", ["c1_tiny_fp32", "bf16_d64", "bf16_d128"])
