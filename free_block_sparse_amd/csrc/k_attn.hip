@@ -12,7 +12,10 @@
 // Work decomposition: a workgroup owns up to 128 rows of one query group and
 // streams the concatenation of that group's granted key groups ("virtual key
 // sequence") in 64-key tiles, so only the end of the whole sequence is ragged,
-// not every granted cell.
+// not every granted cell.  The last rows of a query group, when they fit in
+// 64, form a "split" tile: its two 32-row blocks are each taken by two waves
+// that split every 64-key tile between them, so the workgroup stays busy with
+// half the rows instead of padding them to 128.
 #include <string.h>
 
 #include <type_traits>
@@ -93,8 +96,9 @@ __device__ inline int block_excl_scan(int v, int* tmp, int* total) {
 // Returns false when the workgroup has nothing to do.
 template <int PER>
 __device__ inline bool setup_item(const AttnArgs& a, int bh, int tile, int* seg_v, int* seg_p, int* tmp,
-                                  int* g_out, int* row0, int* nrows, int* nseg, int* L) {
+                                  int* g_out, int* row0, int* nrows, int* nseg, int* L, int* split) {
   const int tid = threadIdx.x;
+  *split = 0;
   if (a.dense) {
     *row0 = tile * kTileRows;
     if (*row0 >= a.N) return false;
@@ -116,6 +120,7 @@ __device__ inline bool setup_item(const AttnArgs& a, int bh, int tile, int* seg_
   *g_out = g;
   *row0 = e[1];
   *nrows = e[2];
+  *split = e[3];
   const int* cp = a.csr_ptr + (long long)bh * (a.GQ + 1);
   const int c0 = cp[g], nc = cp[g + 1] - c0;
   const int* cols = a.csr_col + (long long)bh * a.GQ * a.GK + c0;
@@ -189,10 +194,14 @@ __global__ __launch_bounds__(256, 2) void k_sparse_attn_mfma(AttnArgs a) {
   if (bh >= a.BH) return;
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63, half = lane >> 5, col = lane & 31;
-  int g, row0, nrows, nseg, L;
-  if (!setup_item<4>(a, bh, tile, seg_v, seg_p, tmp, &g, &row0, &nrows, &nseg, &L)) return;
-  const bool wave_active = 32 * w < nrows;
-  const int qr = 32 * w + col;
+  int g, row0, nrows, nseg, L, split;
+  if (!setup_item<4>(a, bh, tile, seg_v, seg_p, tmp, &g, &row0, &nrows, &nseg, &L, &split)) return;
+  // split tile: waves w and w + 2 take row block w & 1, key half w >> 1
+  const int rw = split ? (w & 1) : w;
+  const int kh = split ? (w >> 1) : 0;
+  const bool wave_active = 32 * rw < nrows;
+  const bool owner = wave_active && (!split || w < 2);  // holds the merged rows at the end
+  const int qr = 32 * rw + col;
   const bool qvalid = qr < nrows;
 
   const bf16_t* qb = static_cast<const bf16_t*>(a.qv.p);
@@ -217,7 +226,8 @@ __global__ __launch_bounds__(256, 2) void k_sparse_attn_mfma(AttnArgs a) {
   // next segment's virtual start stay in registers: LDS is read only when a
   // key crosses into the next segment.
   int cur = 0, cv = seg_v[0], cp = seg_p[0], nv = nseg > 1 ? seg_v[1] : 0x7fffffff;
-  auto rows = [&](long long* __restrict__ ofs, const int* __restrict__ sv, const int* __restrict__ sp, int tt) {
+  auto rows = [&](long long* __restrict__ ofs, const int* __restrict__ sv, const int* __restrict__ sp, int tt)
+                  __attribute__((always_inline)) {
     const int v = 64 * tt + lane;
     int prow = cp;  // rows past the end read a valid row; they are masked
     if (v < L) {
@@ -235,7 +245,7 @@ __global__ __launch_bounds__(256, 2) void k_sparse_attn_mfma(AttnArgs a) {
   // Every wave moves its share of the K and V tiles straight into LDS.
   typedef __attribute__((address_space(3))) char lds_char;
   auto issue = [&](lds_char* __restrict__ dst, const long long* __restrict__ ofs, const bf16_t* __restrict__ gk0,
-                   const bf16_t* __restrict__ gv0) {
+                   const bf16_t* __restrict__ gv0) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < IPW; ++i) {
       const int rb = (w * IPW + i) * RPI;
@@ -251,24 +261,30 @@ __global__ __launch_bounds__(256, 2) void k_sparse_attn_mfma(AttnArgs a) {
   // flips address bits below the row bits, so every fragment address is
   // (base ^ small constant) + immediate offset.
   const int gi = lane >> 4, li = lane & 15, rr = li >> 2, qq = li & 3;
-  const uint32_t kbase0 = col * 2 * D + 16 * (half ^ swz_k<CPR>(col));
-  const uint32_t vbase0 = VOFF + (4 * (gi >> 1) + rr) * 2 * D + 64 * (swz_v<CPR>(rr) >> 2) +
+  // a key-half wave of a split tile reads keys 32..63 of every tile: the
+  // offset is a whole number of 32-key blocks and leaves the swizzle bits alone
+  const uint32_t khoff = (uint32_t)kh * 32 * 2 * D;
+  const uint32_t kbase0 = khoff + col * 2 * D + 16 * (half ^ swz_k<CPR>(col));
+  const uint32_t vbase0 = khoff + VOFF + (4 * (gi >> 1) + rr) * 2 * D + 64 * (swz_v<CPR>(rr) >> 2) +
                           16 * (2 * (gi & 1) + (qq >> 1)) + 8 * (qq & 1);
 
-  auto compute_tile = [&](auto mask_tag, const lds_char* __restrict__ lds, int kt0) {
+  // NKT 32-key blocks of the tile per wave: 2, or 1 (key half kh) in a split tile
+  auto compute_tile = [&](auto mask_tag, auto split_tag, const lds_char* __restrict__ lds, int kt0)
+                          __attribute__((always_inline)) {
     constexpr bool MASK = decltype(mask_tag)::value;
+    constexpr int NKT = decltype(split_tag)::value ? 1 : 2;
     // opaque per tile: keeps the derived addresses from being hoisted into
     // registers for the whole loop
     uint32_t kb0 = kbase0, vb0 = vbase0;
     asm volatile("" : "+v"(kb0), "+v"(vb0));
-    f32x16 sacc[2];
+    f32x16 sacc[NKT];
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) sacc[kt] = f32x16{};
+    for (int kt = 0; kt < NKT; ++kt) sacc[kt] = f32x16{};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       const uint32_t ka = kb0 ^ (32u * ks);
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
+      for (int kt = 0; kt < NKT; ++kt) {
         const bf16x8 kf = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(lds + ka + kt * 32 * 2 * D);  // keys 32kt + col
         sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], sacc[kt], 0, 0, 0);
       }
@@ -277,15 +293,15 @@ __global__ __launch_bounds__(256, 2) void k_sparse_attn_mfma(AttnArgs a) {
     float mloc = -INFINITY;
     if constexpr (MASK) {
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
+      for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int key = 32 * kt + (r & 3) + 8 * (r >> 2) + 4 * half;
+          const int key = 32 * (kt + kh) + (r & 3) + 8 * (r >> 2) + 4 * half;
           if (kt0 + key >= L) sacc[kt][r] = -INFINITY;
         }
     }
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
+    for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mloc = fmaxf(mloc, sacc[kt][r]);
     mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64)) * c;
@@ -309,7 +325,7 @@ __global__ __launch_bounds__(256, 2) void k_sparse_attn_mfma(AttnArgs a) {
     const float mb = m;
     float psum = 0.f;
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
+    for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kt][r], c, -mb));
@@ -324,7 +340,7 @@ __global__ __launch_bounds__(256, 2) void k_sparse_attn_mfma(AttnArgs a) {
 #pragma unroll
     for (int b = 0; b < DB; ++b) va[b] = vb0 ^ (64u * b);
 #pragma unroll
-    for (int sp = 0; sp < 4; ++sp) {
+    for (int sp = 0; sp < 2 * NKT; ++sp) {
       const int kt = sp >> 1, rb = 8 * (sp & 1);
       uint32_t pw[4];
 #pragma unroll
@@ -375,10 +391,11 @@ __global__ __launch_bounds__(256, 2) void k_sparse_attn_mfma(AttnArgs a) {
   // One pipeline step: start the DMA of tile t+1 into the other stage,
   // resolve the rows of tile t+2, compute tile t, then wait for the DMA and
   // meet at the barrier.  Tile t uses offsets buffer t&1 and stage t&1.
-  auto step = [&](auto mask_tag, lds_char* cur_st, lds_char* nxt_st, long long* nxt_ofs, long long* cur_ofs, int t) {
+  auto step = [&](auto mask_tag, auto split_tag, lds_char* cur_st, lds_char* nxt_st, long long* nxt_ofs,
+                  long long* cur_ofs, int t) __attribute__((always_inline)) {
     if (t + 1 < ntile) issue(nxt_st, nxt_ofs, gk0, gv0);
     if (w == 0 && t + 2 < ntile) rows(cur_ofs, seg_v, seg_p, t + 2);
-    if (wave_active) compute_tile(mask_tag, cur_st, 64 * t);
+    if (wave_active) compute_tile(mask_tag, split_tag, cur_st, 64 * t);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
   };
@@ -392,18 +409,51 @@ __global__ __launch_bounds__(256, 2) void k_sparse_attn_mfma(AttnArgs a) {
   // the ragged end, so the hot loop carries no masking and no path merges
   constexpr std::false_type full{};
   constexpr std::true_type ragged{};
-  int t = 0;
-  for (; t + 1 < nfull; t += 2) {
-    step(full, s0, s1, offs1, offs0, t);
-    step(full, s1, s0, offs0, offs1, t + 1);
-  }
-  if (t < nfull) {
-    step(full, s0, s1, offs1, offs0, t);
-    ++t;
-  }
-  if (t < ntile) {
-    if (t & 1) step(ragged, s1, s0, offs0, offs1, t);
-    else step(ragged, s0, s1, offs1, offs0, t);
+  auto run = [&](auto split_tag) __attribute__((always_inline)) {
+    int t = 0;
+    for (; t + 1 < nfull; t += 2) {
+      step(full, split_tag, s0, s1, offs1, offs0, t);
+      step(full, split_tag, s1, s0, offs0, offs1, t + 1);
+    }
+    if (t < nfull) {
+      step(full, split_tag, s0, s1, offs1, offs0, t);
+      ++t;
+    }
+    if (t < ntile) {
+      if (t & 1) step(ragged, split_tag, s1, s0, offs0, offs1, t);
+      else step(ragged, split_tag, s0, s1, offs1, offs0, t);
+    }
+  };
+  if (split) {
+    run(std::true_type{});
+    // merge the key halves: waves 2 and 3 hand (m, l, O) to waves 0 and 1
+    // through the (now idle) stage buffers
+    float* xo = reinterpret_cast<float*>(KV0);  // [2][DB * 16][64]
+    float* xs = reinterpret_cast<float*>(KV1);  // [2][2][64]
+    if (w >= 2) {
+      const int ww = w - 2;
+#pragma unroll
+      for (int b = 0; b < DB; ++b)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) xo[((ww * DB + b) * 16 + i) * 64 + lane] = o[b][i];
+      xs[(2 * ww) * 64 + lane] = m;
+      xs[(2 * ww + 1) * 64 + lane] = l;
+    }
+    __syncthreads();
+    if (w < 2) {
+      const float m2 = xs[(2 * w) * 64 + lane], l2 = xs[(2 * w + 1) * 64 + lane];
+      const float mm = fmaxf(m, m2);
+      const float a1 = mm == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - mm);
+      const float a2 = mm == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m2 - mm);
+      l = a1 * l + a2 * l2;
+#pragma unroll
+      for (int b = 0; b < DB; ++b)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) o[b][i] = a1 * o[b][i] + a2 * xo[((w * DB + b) * 16 + i) * 64 + lane];
+      m = mm;
+    }
+  } else {
+    run(std::false_type{});
   }
 
   // ---- epilogue: normalise, correct (b + x W V^T), restore token order
@@ -436,7 +486,7 @@ __global__ __launch_bounds__(256, 2) void k_sparse_attn_mfma(AttnArgs a) {
         Vl[dm * 33 + j] = j < nj ? fv[(long long)dm * a.R + j0 + j] : 0.f;
       }
       __syncthreads();
-      if (wave_active) {
+      if (owner) {
         float t[32];
 #pragma unroll
         for (int j = 0; j < 32; ++j) t[j] = 0.f;
@@ -468,7 +518,7 @@ __global__ __launch_bounds__(256, 2) void k_sparse_attn_mfma(AttnArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) x[b][r] += corr[b][r];
   }
-  if (!(wave_active && qvalid)) return;
+  if (!(owner && qvalid)) return;
   const int pos = row0 + qr;
   const int token = a.perm_q ? a.perm_q[(long long)bh * a.N + pos] : pos;
   bf16_t* orow = static_cast<bf16_t*>(a.o.p) + a.o.row_off(bh, token);
@@ -495,8 +545,8 @@ __global__ __launch_bounds__(512) void k_sparse_attn_vec(AttnArgs a) {
   __shared__ int seg_v[kMaxGroups + 1], seg_p[kMaxGroups + 1];
   __shared__ int tmp[8];
   const int bh = blockIdx.y, tile = blockIdx.x, tid = threadIdx.x;
-  int g, row0, nrows, nseg, L;
-  if (!setup_item<2>(a, bh, tile, seg_v, seg_p, tmp, &g, &row0, &nrows, &nseg, &L)) return;
+  int g, row0, nrows, nseg, L, split;  // a split tile is an ordinary tile here
+  if (!setup_item<2>(a, bh, tile, seg_v, seg_p, tmp, &g, &row0, &nrows, &nseg, &L, &split)) return;
   const int rl = tid >> 2, sub = tid & 3;
   const bool valid = rl < nrows;
   const T* qb = static_cast<const T*>(a.qv.p);

@@ -312,6 +312,19 @@ __global__ __launch_bounds__(1024) void k_route_select(RouteArgs a) {
 }
 
 // ---------------------------------------------------------------- CSR, masks, tiles, stats
+// Query tiles of a group of s rows: with s rounded up to a multiple of 64,
+// every whole 128 rows make one tile and a last 64 (or fewer real rows) make
+// one split tile, which the attention kernel runs with all four waves on half
+// the rows.  The last 128-row tile may hold from 65 to 128 real rows.
+__device__ inline int tiles_of_group(int s) {
+  const int s64 = (s + 63) / 64;
+  return (s64 >> 1) + (s64 & 1);
+}
+__device__ inline int tile_is_split(int s, int i) {
+  const int s64 = (s + 63) / 64;
+  return (s64 & 1) && i == (s64 >> 1);
+}
+
 __global__ __launch_bounds__(256) void k_route_emit(RouteArgs a) {
   __shared__ int nq[kMaxGroups], nk[kMaxGroups], cnt[kMaxGroups], tcnt[kMaxGroups];
   __shared__ int bucket[kMaxGroups + 1], order[kMaxGroups], mands[kMaxGroups];
@@ -355,7 +368,7 @@ __global__ __launch_bounds__(256) void k_route_emit(RouteArgs a) {
     }
     cnt[g] = c;
     lsh[g] = L;
-    tcnt[g] = nq[g] > 0 ? (nq[g] + kTileRows - 1) / kTileRows : 0;
+    tcnt[g] = tiles_of_group(nq[g]);
     a.lg[(long long)bh * GQ + g] = L;
   }
   __syncthreads();
@@ -427,13 +440,14 @@ __global__ __launch_bounds__(256) void k_route_emit(RouteArgs a) {
       }
     }
     int t0 = tcnt[g];
-    for (int r = 0; r < nq[g]; r += kTileRows) {
-      int* e = tl + (long long)t0 * 4;
+    const int nt = tiles_of_group(nq[g]);
+    for (int i = 0; i < nt; ++i) {
+      int* e = tl + (long long)(t0 + i) * 4;
+      const int r = kTileRows * i;
       e[0] = g;
       e[1] = offq[g] + r;
       e[2] = min(kTileRows, nq[g] - r);
-      e[3] = 0;
-      ++t0;
+      e[3] = tile_is_split(nq[g], i);
     }
   }
 }
