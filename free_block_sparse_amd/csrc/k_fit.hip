@@ -188,6 +188,27 @@ __device__ double block_sum_d(double v, double* red) {
 
 constexpr int kFitThreads = 1024;
 
+// fp64 dot product of two strided sequences with four accumulators: in these
+// small products the chain of dependent additions, not the arithmetic, sets
+// the time.
+template <typename TA, typename TB>
+__device__ inline double dot4(const TA* x, int sx, const TB* y, int sy, int n) {
+  double a0 = 0.0, a1 = 0.0, a2 = 0.0, a3 = 0.0;
+  int k = 0;
+  for (; k + 3 < n; k += 4) {
+    a0 += (double)x[k * sx] * (double)y[k * sy];
+    a1 += (double)x[(k + 1) * sx] * (double)y[(k + 1) * sy];
+    a2 += (double)x[(k + 2) * sx] * (double)y[(k + 2) * sy];
+    a3 += (double)x[(k + 3) * sx] * (double)y[(k + 3) * sy];
+  }
+  for (; k < n; ++k) a0 += (double)x[k * sx] * (double)y[k * sy];
+  return (a0 + a1) + (a2 + a3);
+}
+
+// ALL_LDS: M <= 64 probes and r <= 32, so every matrix lives in LDS; the
+// pointers below are then known to be LDS pointers and compile to LDS
+// accesses instead of generic ones.
+template <bool ALL_LDS>
 __global__ __launch_bounds__(1024) void k_fit(FitArgs a) {
   // LDS path for M <= 64: R and X as fp32 rows of stride d + 1, the Gram /
   // ridge system and eigenvectors as fp64 rows of stride 65 (odd strides keep
@@ -210,6 +231,7 @@ __global__ __launch_bounds__(1024) void k_fit(FitArgs a) {
   __shared__ double bp[64];
   __shared__ double edg[128 + 2], eeo[64 + 2], etau[64], evb[64], epb[64], erot[4 * 64];
   __shared__ double Ycl[SM * 32];  // Y (M x rk) when M <= 64 and rk <= 32
+  __shared__ double sws[kMaxProbe];  // sqrt of the probe weights
   __shared__ int ectl[8];
   const int bh = blockIdx.x, tid = threadIdx.x, nt = blockDim.x;
   const int M = a.M, d = a.d, Rmax = a.R;  // Rmax: column stride of the W and V outputs
@@ -217,9 +239,9 @@ __global__ __launch_bounds__(1024) void k_fit(FitArgs a) {
   const bool small = M <= d;
   const int n = small ? M : d;
   const int ne = n + (n & 1);
-  const bool lds = M <= SM;
+  const bool lds = ALL_LDS || M <= SM;
   const int ldx = lds ? SLX : d;
-  const bool glds = ne <= SM;
+  const bool glds = ALL_LDS || ne <= SM;
   const int ldg = glds ? SLG : ne;
   float* Rf = lds ? Rl : reinterpret_cast<float*>(S);                        // M x d
   float* Xf = lds ? Xl : reinterpret_cast<float*>(S) + 256 * 128;            // M x d (centred below)
@@ -227,7 +249,7 @@ __global__ __launch_bounds__(1024) void k_fit(FitArgs a) {
   double* U = glds ? Ul : S + 256 * 128 + 128 * 128;                         // ne x ne
   double* Vr = S + 256 * 128 + 2 * 128 * 128;                                // d x Rmax
   double* Wm = Vr + 128 * 64;                                                // d x rk (also the primal rhs)
-  double* Yc = (lds && a.Rcfg <= 32) ? Ycl : Wm + 128 * 64;                 // M x rk
+  double* Yc = (ALL_LDS || (lds && a.Rcfg <= 32)) ? Ycl : Wm + 128 * 64;    // M x rk
   double* Kp = Wm + 128 * 64 + 256 * 64;                                     // primal system d x d (M > d)
   const float* ode = a.ode + (long long)bh * M * d;
   const float* osp = a.osp + (long long)bh * M * d;
@@ -239,12 +261,13 @@ __global__ __launch_bounds__(1024) void k_fit(FitArgs a) {
     Xf[mm * ldx + dm] = osp[e];
   }
   double wpart = 0.0;
-  for (int i = tid; i < M; i += nt) wpart += w[i];
+  for (int i = tid; i < M; i += nt) {
+    wpart += w[i];
+    sws[i] = sqrt(w[i]);
+  }
   const double ws = block_sum_d(wpart, red);
   for (int dm = tid; dm < d; dm += nt) {
-    double acc = 0.0;
-    for (int mm = 0; mm < M; ++mm) acc += w[mm] * (double)Xf[mm * ldx + dm];
-    xb[dm] = acc / ws;
+    xb[dm] = dot4(w, 1, Xf + dm, ldx, M) / ws;
   }
   // Gram of the smaller side of R
   for (int e = tid; e < ne * ne; e += nt) {
@@ -332,9 +355,7 @@ __global__ __launch_bounds__(1024) void k_fit(FitArgs a) {
     const int ci = idx_s[k];
     double v;
     if (small) {
-      double acc = 0.0;
-      for (int mm = 0; mm < M; ++mm) acc += (double)Rf[mm * ldx + dm] * U[mm * ldg + ci];
-      v = acc / sig_s[k];
+      v = dot4(Rf + dm, ldx, U + ci, ldg, M) / sig_s[k];
     } else {
       v = U[dm * ldg + ci];
     }
@@ -385,9 +406,9 @@ __global__ __launch_bounds__(1024) void k_fit(FitArgs a) {
         const int i = e / M, j = e - (e / M) * M;
         double acc = 0.0;
         for (int dm = 0; dm < d; ++dm) acc += (double)Xf[i * ldx + dm] * (double)Xf[j * ldx + dm];
-        K[i * ldg + j] = sqrt(w[i] * w[j]) * acc + (i == j ? lam : 0.0);
+        K[i * ldg + j] = sws[i] * sws[j] * acc + (i == j ? lam : 0.0);
       }
-      for (int e = tid; e < M * rk; e += nt) Yc[e] *= sqrt(w[e / rk]);
+      for (int e = tid; e < M * rk; e += nt) Yc[e] *= sws[e / rk];
       block_sync();
       if (M <= 64) {
         // one wave factors K column by column (lane i owns row i of L, left-
@@ -398,14 +419,14 @@ __global__ __launch_bounds__(1024) void k_fit(FitArgs a) {
           bool badl = false;
           for (int k = 0; k < M; ++k) {
             const int rl = ln < M ? ln : k;  // idle lanes shadow the pivot row
-            double acc = K[rl * ldg + k];
-            for (int j = 0; j < k; ++j) acc -= K[rl * ldg + j] * K[k * ldg + j];
+            const double acc = K[rl * ldg + k] - dot4(K + rl * ldg, 1, K + k * ldg, 1, k);
             const double piv = __shfl(acc, k, 64);
             badl |= !(piv > 0.0);
             const double lkk = sqrt(piv > 0.0 ? piv : 1.0);
+            // a wave's LDS accesses complete in order, and the next column's
+            // reads may alias these writes, so they are not moved above them
             if (ln == k) K[k * ldg + k] = lkk;
             else if (ln > k && ln < M) K[ln * ldg + k] = acc / lkk;
-            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
           }
           if (ln == 0) bad = badl ? 1 : 0;
         }
@@ -413,19 +434,31 @@ __global__ __launch_bounds__(1024) void k_fit(FitArgs a) {
         ok = bad == 0;
         if (ok) {
           const double dinv = ln < M ? 1.0 / K[ln * ldg + ln] : 0.0;
-          for (int cidx = wv; cidx < rk; cidx += nt >> 6) {
-            double y = ln < M ? Yc[ln * rk + cidx] : 0.0;
+          // two right-hand sides per pass: independent chains
+          const int nw = nt >> 6;
+          for (int c0 = wv; c0 < rk; c0 += 2 * nw) {
+            const int c1 = c0 + nw;
+            const bool two = c1 < rk;
+            double y0 = ln < M ? Yc[ln * rk + c0] : 0.0;
+            double y1 = (two && ln < M) ? Yc[ln * rk + c1] : 0.0;
             for (int j = 0; j < M; ++j) {  // L z = y
-              const double zj = __shfl(y * dinv, j, 64);
-              if (ln == j) y = zj;
-              else if (ln > j && ln < M) y -= K[ln * ldg + j] * zj;
+              const double lj = (ln > j && ln < M) ? K[ln * ldg + j] : 0.0;
+              const double z0 = __shfl(y0 * dinv, j, 64);
+              const double z1 = __shfl(y1 * dinv, j, 64);
+              y0 = ln == j ? z0 : y0 - lj * z0;
+              y1 = ln == j ? z1 : y1 - lj * z1;
             }
             for (int i = M - 1; i >= 0; --i) {  // L^T x = z
-              const double xi = __shfl(y * dinv, i, 64);
-              if (ln == i) y = xi;
-              else if (ln < i) y -= K[i * ldg + ln] * xi;
+              const double li = ln < i ? K[i * ldg + ln] : 0.0;
+              const double x0 = __shfl(y0 * dinv, i, 64);
+              const double x1 = __shfl(y1 * dinv, i, 64);
+              y0 = ln == i ? x0 : y0 - li * x0;
+              y1 = ln == i ? x1 : y1 - li * x1;
             }
-            if (ln < M) Yc[ln * rk + cidx] = y;
+            if (ln < M) {
+              Yc[ln * rk + c0] = y0;
+              if (two) Yc[ln * rk + c1] = y1;
+            }
           }
         }
         block_sync();
@@ -434,11 +467,12 @@ __global__ __launch_bounds__(1024) void k_fit(FitArgs a) {
         if (ok) chol_solve_f64(K, M, ldg, Yc, rk, rk);
       }
       if (ok) {
+        // W = Xc^T D^1/2 Y
+        for (int e = tid; e < M * rk; e += nt) Yc[e] *= sws[e / rk];
+        block_sync();
         for (int e = tid; e < d * rk; e += nt) {
           const int dm = e / rk, k = e - (e / rk) * rk;
-          double acc = 0.0;
-          for (int mm = 0; mm < M; ++mm) acc += (double)Xf[mm * ldx + dm] * sqrt(w[mm]) * Yc[mm * rk + k];
-          Wm[dm * rk + k] = acc;
+          Wm[dm * rk + k] = dot4(Xf + dm, ldx, Yc + k, rk, M);
         }
       }
     } else {
@@ -510,7 +544,8 @@ hipError_t launch_fit(const Plan& p, hipStream_t s) {
   a.b = p.fitb;
   a.rank = p.fitrank;
   a.stats = p.stats;
-  hipLaunchKernelGGL(k_fit, dim3(p.BH), dim3(kFitThreads), 0, s, a);
+  if (a.M <= 64 && a.Rcfg <= 32) hipLaunchKernelGGL(k_fit<true>, dim3(p.BH), dim3(kFitThreads), 0, s, a);
+  else hipLaunchKernelGGL(k_fit<false>, dim3(p.BH), dim3(kFitThreads), 0, s, a);
   return hipGetLastError();
 }
 

@@ -41,6 +41,16 @@ template <>
 struct EigEps<double> {
   static constexpr double v = 2.220446049250313e-16;
 };
+template <typename T>
+struct EigSqrtEps;
+template <>
+struct EigSqrtEps<float> {
+  static constexpr float v = 3.4526698e-4f;
+};
+template <>
+struct EigSqrtEps<double> {
+  static constexpr double v = 1.4901161193847656e-8;
+};
 // smallest normal number
 template <typename T>
 struct EigTiny;
@@ -143,11 +153,16 @@ __device__ void eig_tridiagonalize(const EigWork<T>& w, int n) {
     T kk = 0;
     for (int i = lane; i < m; i += 64) kk += w.vb[i] * w.pb[i];
     kk = eig_sum(kk, 64) * (tau * T(0.5));
-    for (int e = tid; e < m * m; e += NT) {
-      const int i = e / m, j = e - (e / m) * m;
-      const T vi = w.vb[i], vj = w.vb[j];
-      const T wi = w.pb[i] - kk * vi, wj = w.pb[j] - kk * vj;
-      A[(k + 1 + i) * lda + (k + 1 + j)] -= vi * wj + wi * vj;
+    // rank-2 update, row by row with the same thread layout as the product
+    // above: A22 -= v w^T + w v^T with w = p - kk v
+    for (int row = tid / TPR; row < m; row += NT / TPR) {
+      const int sub = tid - (tid / TPR) * TPR;
+      const T vi = w.vb[row], wi = w.pb[row] - kk * vi;
+      T* ar = A + (k + 1 + row) * lda + (k + 1);
+      for (int j = sub; j < m; j += TPR) {
+        const T vj = w.vb[j], wj = w.pb[j] - kk * vj;
+        ar[j] -= vi * wj + wi * vj;
+      }
     }
     __syncthreads();
   }
@@ -473,10 +488,12 @@ __device__ bool eig_twisted(const EigWork<T>& w, int n, int nvec) {
     for (int i = 0; i < n; ++i) zc[i * ldz] *= inv;
   }
   __syncthreads();
-  // Gram-Schmidt against the earlier members of a cluster (gap below
-  // 1e-3 ||T||), one wave, columns in order
+  // Gram-Schmidt against the earlier members of a cluster, one wave, columns
+  // in order.  A twisted-factorisation vector loses orthogonality to a
+  // neighbour in proportion to eps ||T|| / gap, so clusters are gaps below
+  // sqrt(eps) ||T||: the loss stays near sqrt(eps) without them.
   if (tid < 64) {
-    const T ctol = T(1e-3) * tn;
+    const T ctol = T(EigSqrtEps<T>::v) * tn;
     for (int r = 1; r < nvec; ++r) {
       if (lam[r - 1] - lam[r] >= ctol) continue;
       for (int q = r - 1; q >= 0 && lam[q] - lam[r] < ctol; --q) {
