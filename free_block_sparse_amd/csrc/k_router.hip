@@ -85,30 +85,29 @@ __global__ __launch_bounds__(256) void k_route_mu(RouteArgs a) {
 }
 
 // ---------------------------------------------------------------- keys
+// One wave per query group (four per workgroup); no workgroup barriers.
 __global__ __launch_bounds__(256) void k_route_keys(RouteArgs a) {
-  __shared__ double term[kMaxGroups];
-  __shared__ double rmax[4];
-  __shared__ int rarg[4];
-  __shared__ double ell_s;
-  __shared__ int best_s;
-  const int bh = blockIdx.y, g = blockIdx.x, tid = threadIdx.x;
+  __shared__ double term[4][kMaxGroups];
+  const int bh = blockIdx.y, wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int g = blockIdx.x * 4 + wv;
+  if (g >= a.GQ) return;
   const int GK = a.GK;
   const int* offq = a.off_q + (long long)bh * (a.GQ + 1);
   const int* offk = a.off_k + (long long)bh * (a.GK + 1);
   const long long row = ((long long)bh * a.GQ + g) * GK;
   const int nq = offq[g + 1] - offq[g];
   if (nq <= 0) {
-    for (int h = tid; h < GK; h += 256) a.ckey[row + h] = kExcluded;
-    if (tid == 0) a.mand[(long long)bh * a.GQ + g] = -1;
+    for (int h = lane; h < GK; h += 64) a.ckey[row + h] = kExcluded;
+    if (lane == 0) a.mand[(long long)bh * a.GQ + g] = -1;
     return;
   }
   // first maximum of mu over non-empty key groups
   double bm = -INFINITY;
   int bi = 0x7fffffff;
-  for (int h = tid; h < GK; h += 256) {
+  for (int h = lane; h < GK; h += 64) {
     if (offk[h + 1] <= offk[h]) continue;
     const double m = a.mu[row + h];
-    if (bi == 0x7fffffff || m > bm) {  // strided per-thread scan keeps the first maximum
+    if (bi == 0x7fffffff || m > bm) {  // strided per-lane scan keeps the first maximum
       bm = m;
       bi = h;
     }
@@ -122,45 +121,27 @@ __global__ __launch_bounds__(256) void k_route_keys(RouteArgs a) {
       bi = oi;
     }
   }
-  if ((tid & 63) == 0) {
-    rmax[tid >> 6] = bm;
-    rarg[tid >> 6] = bi;
-  }
-  __syncthreads();
-  if (tid == 0) {
-    double m = rmax[0];
-    int i = rarg[0];
-    for (int w = 1; w < 4; ++w) {
-      const int oi = rarg[w];
-      const double om = rmax[w];
-      if (oi != 0x7fffffff && (i == 0x7fffffff || om > m || (om == m && oi < i))) {
-        m = om;
-        i = oi;
-      }
-    }
-    best_s = i;
-    rmax[0] = m;
-  }
-  __syncthreads();
-  const int best = best_s;
-  const double mx = rmax[0];
+  const int best = bi;
+  const double mx = bm;
   const bool finite = best != 0x7fffffff && mx > -INFINITY && mx < INFINITY;
-  for (int h = tid; h < GK; h += 256) {
+  double* tm = term[wv];
+  for (int h = lane; h < GK; h += 64) {
     double t = 0.0;
     if (finite && offk[h + 1] > offk[h]) t = __dmul_rn((double)(offk[h + 1] - offk[h]), exp(__dsub_rn(a.mu[row + h], mx)));
-    term[h] = t;
+    tm[h] = t;
   }
-  __syncthreads();
-  if (tid == 0) {
+  // sequential sum in ascending h (lane 0); this wave's LDS writes above are
+  // complete before its reads below, which may alias them
+  double ell = 0.0;
+  if (lane == 0) {
     double tot = 0.0;
     for (int h = 0; h < GK; ++h)
-      if (offk[h + 1] > offk[h]) tot = __dadd_rn(tot, term[h]);
-    ell_s = finite ? __dadd_rn(mx, log(tot)) : 0.0;
+      if (offk[h + 1] > offk[h]) tot = __dadd_rn(tot, tm[h]);
+    ell = finite ? __dadd_rn(mx, log(tot)) : 0.0;
     a.mand[(long long)bh * a.GQ + g] = best == 0x7fffffff ? -1 : best;
   }
-  __syncthreads();
-  const double ell = ell_s;
-  for (int h = tid; h < GK; h += 256) {
+  ell = __shfl(ell, 0, 64);
+  for (int h = lane; h < GK; h += 64) {
     uint64_t ck = kExcluded;
     if (offk[h + 1] > offk[h] && h != best) {
       double key = finite ? __dsub_rn(a.mu[row + h], ell) : -INFINITY;
@@ -213,14 +194,22 @@ __device__ inline bool thr_grants(const long long* thr, uint64_t ck, uint32_t ce
   return c < 0 || (mode == 3 && c == 0);
 }
 
+// Once the cells sharing the selected prefix number at most kSelCap, they are
+// gathered, sorted and scanned instead of being narrowed a byte at a time.
+constexpr int kSelCap = 1024;
+
 __global__ __launch_bounds__(1024) void k_route_select(RouteArgs a) {
   __shared__ int nq[kMaxGroups], nk[kMaxGroups];
   __shared__ unsigned long long hist[16][256];
+  __shared__ int cnth[256];
   __shared__ long long red[16];
   __shared__ long long rem_s;
   __shared__ unsigned long long ph_s;
   __shared__ unsigned pl_s;
-  __shared__ int nbits_s, done_s, mode_s;
+  __shared__ int nbits_s, done_s, mode_s, finish_s, ncand_s, found_s;
+  __shared__ unsigned long long sk[kSelCap];
+  __shared__ unsigned scell[kSelCap];
+  __shared__ long long scost[kSelCap];
   const int bh = blockIdx.x, tid = threadIdx.x, wave = tid >> 6;
   const int GQ = a.GQ, GK = a.GK;
   const int* offq = a.off_q + (long long)bh * (GQ + 1);
@@ -258,20 +247,46 @@ __global__ __launch_bounds__(1024) void k_route_select(RouteArgs a) {
   __syncthreads();
   const uint64_t* ck = a.ckey + (long long)bh * GQ * GK;
   const int ncell = GQ * GK;
+  if (tid == 0) finish_s = 0;
   for (int pass = 0; pass < 11 && !done_s; ++pass) {
     for (int e = tid; e < 16 * 256; e += 1024) (&hist[0][0])[e] = 0ull;
+    if (tid < 256) cnth[tid] = 0;
     __syncthreads();
     const int nbits = nbits_s;
     const uint64_t ph = ph_s;
     const uint32_t pl = pl_s;
-    for (int c = tid; c < ncell; c += 1024) {
-      const uint64_t k = ck[c];
-      if (k == kExcluded) continue;
-      if (!comp_prefix_eq(k, (uint32_t)c, nbits, ph, pl)) continue;
-      int dig;
-      comp_digits(k, (uint32_t)c, pass, &dig);
-      const int g = c / GK, h = c - (c / GK) * GK;
-      atomicAdd(&hist[wave][dig], (unsigned long long)((long long)nq[g] * nk[h]));
+    const int lane = tid & 63;
+    for (int c0 = 0; c0 < ncell; c0 += 1024) {
+      const int c = c0 + tid;
+      bool take = false;
+      int dig = 0;
+      unsigned long long cost = 0;
+      if (c < ncell) {
+        const uint64_t k = ck[c];
+        if (k != kExcluded && comp_prefix_eq(k, (uint32_t)c, nbits, ph, pl)) {
+          take = true;
+          comp_digits(k, (uint32_t)c, pass, &dig);
+          const int g = c / GK, h = c - (c / GK) * GK;
+          cost = (unsigned long long)((long long)nq[g] * nk[h]);
+        }
+      }
+      // early passes put almost every cell in one bin: when all the wave's
+      // cells share a digit, one lane adds the wave's total
+      const unsigned long long act = __builtin_amdgcn_ballot_w64(take);
+      if (act == 0ull) continue;
+      const int first = __builtin_ctzll(act);
+      const int d0 = __shfl(dig, first, 64);
+      if (__builtin_amdgcn_ballot_w64(take && dig == d0) == act) {
+        unsigned long long t = cost;
+        for (int o = 32; o > 0; o >>= 1) t += __shfl_xor(t, o, 64);
+        if (lane == first) {
+          atomicAdd(&hist[wave][d0], t);
+          atomicAdd(&cnth[d0], __builtin_popcountll(act));
+        }
+      } else if (take) {
+        atomicAdd(&hist[wave][dig], cost);
+        atomicAdd(&cnth[dig], 1);
+      }
     }
     __syncthreads();
     if (tid < 256) {
@@ -299,9 +314,86 @@ __global__ __launch_bounds__(1024) void k_route_select(RouteArgs a) {
         if (pass < 8) ph_s |= (uint64_t)chosen << (56 - 8 * pass);
         else pl_s |= (uint32_t)chosen << (16 - 8 * (pass - 8));
         nbits_s = nbits + 8;
+        if (cnth[chosen] <= kSelCap) {
+          finish_s = 1;
+          done_s = 1;
+        }
       }
     }
     __syncthreads();
+  }
+  if (finish_s) {
+    // the cells with the selected prefix, in grant order: the first whose
+    // cumulative cost exceeds what is left of the budget is the threshold
+    const int nbits = nbits_s;
+    const uint64_t ph = ph_s;
+    const uint32_t pl = pl_s;
+    if (tid == 0) {
+      ncand_s = 0;
+      found_s = 0;
+    }
+    __syncthreads();
+    for (int c = tid; c < ncell; c += 1024) {
+      const uint64_t k = ck[c];
+      if (k == kExcluded || !comp_prefix_eq(k, (uint32_t)c, nbits, ph, pl)) continue;
+      const int slot = atomicAdd(&ncand_s, 1);
+      const int g = c / GK, h = c - (c / GK) * GK;
+      sk[slot] = k;
+      scell[slot] = (unsigned)c;
+      scost[slot] = (long long)nq[g] * nk[h];
+    }
+    __syncthreads();
+    const int nc = ncand_s;
+    if (tid >= nc) {
+      sk[tid] = ~0ull;
+      scell[tid] = ~0u;
+      scost[tid] = 0;
+    }
+    __syncthreads();
+    // bitonic sort of (key, cell) ascending
+    for (int kk = 2; kk <= kSelCap; kk <<= 1) {
+      for (int j = kk >> 1; j > 0; j >>= 1) {
+        const int ixj = tid ^ j;
+        if (ixj > tid) {
+          const bool up = (tid & kk) == 0;
+          const bool gt = sk[tid] > sk[ixj] || (sk[tid] == sk[ixj] && scell[tid] > scell[ixj]);
+          if (gt == up) {
+            const unsigned long long t0 = sk[tid];
+            sk[tid] = sk[ixj];
+            sk[ixj] = t0;
+            const unsigned t1 = scell[tid];
+            scell[tid] = scell[ixj];
+            scell[ixj] = t1;
+            const long long t2 = scost[tid];
+            scost[tid] = scost[ixj];
+            scost[ixj] = t2;
+          }
+        }
+        __syncthreads();
+      }
+    }
+    // inclusive prefix of the costs in that order
+    long long inc = scost[tid];
+    for (int o = 1; o < 64; o <<= 1) {
+      const long long t = __shfl_up(inc, o, 64);
+      if ((tid & 63) >= o) inc += t;
+    }
+    if ((tid & 63) == 63) red[wave] = inc;
+    __syncthreads();
+    for (int w = 0; w < wave; ++w) inc += red[w];
+    const long long rem = rem_s;
+    // first position past the budget (positions past nc never qualify: their cost is 0
+    // and their prefix equals the total of the candidates)
+    const bool over = tid < nc && inc > rem && (tid == 0 || inc - scost[tid] <= rem);
+    if (over) {
+      found_s = 1;
+      ph_s = sk[tid];
+      pl_s = scell[tid];
+      nbits_s = 88;
+    }
+    __syncthreads();
+    // a threshold cell: grant everything before it; otherwise every candidate fits
+    if (tid == 0) mode_s = found_s ? 2 : 3;
   }
   if (tid == 0) {
     thr[0] = (long long)ph_s;
@@ -325,11 +417,57 @@ __device__ inline int tile_is_split(int s, int i) {
   return (s64 & 1) && i == (s64 >> 1);
 }
 
+// Exclusive scan over the block of up to 4 * 256 ints held in v[0..n) (in
+// place; 4 consecutive entries per thread).  Returns the total.
+__device__ inline int block_scan4(int* v, int n, int* tmp) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  int loc[4], sum = 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int i = 4 * tid + q;
+    loc[q] = i < n ? v[i] : 0;
+    sum += loc[q];
+  }
+  int inc = sum;
+  for (int o = 1; o < 64; o <<= 1) {
+    const int t = __shfl_up(inc, o, 64);
+    if (lane >= o) inc += t;
+  }
+  __syncthreads();
+  if (lane == 63) tmp[w] = inc;
+  __syncthreads();
+  int base = 0, tot = 0;
+  for (int q = 0; q < 4; ++q) {
+    if (q < w) base += tmp[q];
+    tot += tmp[q];
+  }
+  int run = base + inc - sum;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int i = 4 * tid + q;
+    if (i < n) v[i] = run;
+    run += loc[q];
+  }
+  __syncthreads();
+  return tot;
+}
+
+template <typename T>
+__device__ inline T block_sum256(T v, T* tmp) {
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) tmp[threadIdx.x >> 6] = v;
+  __syncthreads();
+  return tmp[0] + tmp[1] + tmp[2] + tmp[3];
+}
+
 __global__ __launch_bounds__(256) void k_route_emit(RouteArgs a) {
   __shared__ int nq[kMaxGroups], nk[kMaxGroups], cnt[kMaxGroups], tcnt[kMaxGroups];
-  __shared__ int bucket[kMaxGroups + 1], order[kMaxGroups], mands[kMaxGroups];
+  __shared__ int ord[kMaxGroups], mands[kMaxGroups];
   __shared__ long long lsh[kMaxGroups];
   __shared__ long long thr[4];
+  __shared__ int tmpi[4];
+  __shared__ long long tmpl[4];
   const int bh = blockIdx.x, tid = threadIdx.x;
   const int GQ = a.GQ, GK = a.GK;
   const int* offq = a.off_q + (long long)bh * (GQ + 1);
@@ -344,19 +482,24 @@ __global__ __launch_bounds__(256) void k_route_emit(RouteArgs a) {
   for (int h = tid; h < GK; h += 256) nk[h] = offk[h + 1] - offk[h];
   if (tid < 4) thr[tid] = a.thr[(long long)bh * 4 + tid];
   __syncthreads();
+  // grants of every cell of group g: one bit per key group
   uint32_t* gm = a.gmask + (long long)bh * GQ * a.gwords;
   for (int g = tid; g < GQ; g += 256) {
     int c = 0;
     long long L = 0;
+    const uint64_t* row = ck + (long long)g * GK;
     for (int w = 0; w < a.gwords; ++w) {
+      uint64_t kv[32];
+#pragma unroll
+      for (int b = 0; b < 32; ++b) kv[b] = 32 * w + b < GK ? row[32 * w + b] : kExcluded;
       uint32_t bits = 0;
+#pragma unroll
       for (int b = 0; b < 32; ++b) {
         const int h = 32 * w + b;
-        if (h >= GK) break;
         bool gr = false;
-        if (nq[g] > 0 && nk[h] > 0) {
+        if (h < GK && nq[g] > 0 && nk[h] > 0) {
           const uint32_t cell = (uint32_t)(g * GK + h);
-          gr = (h == mands[g]) || (ck[cell] != kExcluded && thr_grants(thr, ck[cell], cell));
+          gr = (h == mands[g]) || (kv[b] != kExcluded && thr_grants(thr, kv[b], cell));
         }
         if (gr) {
           bits |= 1u << b;
@@ -371,41 +514,47 @@ __global__ __launch_bounds__(256) void k_route_emit(RouteArgs a) {
     tcnt[g] = tiles_of_group(nq[g]);
     a.lg[(long long)bh * GQ + g] = L;
   }
+  // Tiles are listed by the mandatory (best) key group of their query group,
+  // then by group: query groups that attend to the same keys come next to
+  // each other, and the attention kernel runs neighbouring tiles on one XCD,
+  // where they share the L2.  (A stable order by that key; it only decides
+  // which tiles run together, never a result.)
   __syncthreads();
+  for (int g = tid; g < GQ; g += 256) {
+    const int mg = mands[g] >= 0 ? mands[g] : 0;
+    int pos = 0;
+    for (int q = 0; q < GQ; ++q) {
+      const int mq = mands[q] >= 0 ? mands[q] : 0;
+      pos += mq < mg || (mq == mg && q < g);
+    }
+    ord[pos] = g;
+  }
+  // per-group figures for the statistics (before the scans reuse the arrays)
+  long long routed = 0, mandc = 0;
+  int neq = 0, nek = 0;
+  for (int g = tid; g < GQ; g += 256) {
+    routed += (long long)nq[g] * lsh[g];
+    if (nq[g] > 0) {
+      ++neq;
+      if (mands[g] >= 0) mandc += (long long)nq[g] * nk[mands[g]];
+    }
+  }
+  for (int h = tid; h < GK; h += 256) nek += nk[h] > 0;
+  routed = block_sum256(routed, tmpl);
+  mandc = block_sum256(mandc, tmpl);
+  neq = block_sum256(neq, tmpi);
+  nek = block_sum256(nek, tmpi);
+  // tile offsets in that order, CSR row offsets in group order
+  __shared__ int tord[kMaxGroups];
+  for (int i = tid; i < GQ; i += 256) tord[i] = tcnt[ord[i]];
+  __syncthreads();
+  const int tacc = block_scan4(tord, GQ, tmpi);
+  for (int i = tid; i < GQ; i += 256) tcnt[ord[i]] = tord[i];
+  const int acc = block_scan4(cnt, GQ, tmpi);
+  int* rp = a.csr_ptr + (long long)bh * (GQ + 1);
+  for (int g = tid; g < GQ; g += 256) rp[g] = cnt[g];
   if (tid == 0) {
-    // exclusive scans (sequential; G <= 1024)
-    int* rp = a.csr_ptr + (long long)bh * (GQ + 1);
-    int acc = 0, tacc = 0;
-    long long routed = 0, mandc = 0;
-    int neq = 0, nek = 0;
-    // Tiles are listed by the mandatory (best) key group of their query
-    // group, then by group: query groups that attend to the same keys come
-    // next to each other, and the attention kernel runs neighbouring tiles
-    // on one XCD, where they share the L2.  (Stable counting sort; the order
-    // only decides which tiles run together, never a result.)
-    for (int h = 0; h <= GK; ++h) bucket[h] = 0;
-    for (int g = 0; g < GQ; ++g) ++bucket[(mands[g] >= 0 ? mands[g] : 0) + 1];
-    for (int h = 0; h < GK; ++h) bucket[h + 1] += bucket[h];
-    for (int g = 0; g < GQ; ++g) order[bucket[mands[g] >= 0 ? mands[g] : 0]++] = g;
-    for (int i = 0; i < GQ; ++i) {
-      const int g = order[i];
-      const int tc = tcnt[g];
-      tcnt[g] = tacc;
-      tacc += tc;
-    }
-    for (int g = 0; g < GQ; ++g) {
-      rp[g] = acc;
-      const int c = cnt[g];
-      cnt[g] = acc;
-      acc += c;
-      routed += (long long)nq[g] * lsh[g];
-      if (nq[g] > 0) {
-        ++neq;
-        if (mands[g] >= 0) mandc += (long long)nq[g] * nk[mands[g]];
-      }
-    }
     rp[GQ] = acc;
-    for (int h = 0; h < GK; ++h) nek += nk[h] > 0;
     a.ntiles[bh] = tacc;
     sparsepr_head_stats st;
     const double nn = (double)a.N * (double)a.N;
@@ -480,7 +629,7 @@ hipError_t launch_route(const Plan& p, hipStream_t s) {
   a.max_tiles = p.max_tiles;
   a.stats = p.stats;
   hipLaunchKernelGGL(k_route_mu, dim3((p.GQ + 15) / 16, p.BH), dim3(256), 0, s, a);
-  hipLaunchKernelGGL(k_route_keys, dim3(p.GQ, p.BH), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(k_route_keys, dim3((p.GQ + 3) / 4, p.BH), dim3(256), 0, s, a);
   hipLaunchKernelGGL(k_route_select, dim3(p.BH), dim3(1024), 0, s, a);
   hipLaunchKernelGGL(k_route_emit, dim3(p.BH), dim3(256), 0, s, a);
   return hipGetLastError();
