@@ -25,9 +25,9 @@
 namespace sp {
 
 struct AttnArgs {
-  View4 qv, kv, vv;       // row addressing of the (permuted or original) inputs
+  View4 qv, kv, vv;       // row addressing: Q in token order, K and V permuted (or all original)
   MutView4 o;
-  const int* perm_q;      // position -> token (null: identity)
+  const int* perm_q;      // position -> token (null: identity); also addresses the Q rows
   const int* off_k;
   const int* csr_ptr;
   const int* csr_col;
@@ -207,11 +207,12 @@ __global__ __launch_bounds__(256, 2) void k_sparse_attn_mfma(AttnArgs a) {
   const bf16_t* qb = static_cast<const bf16_t*>(a.qv.p);
   const bf16_t* kb = static_cast<const bf16_t*>(a.kv.p);
   const bf16_t* vb = static_cast<const bf16_t*>(a.vv.p);
+  const int qtok = !qvalid ? 0 : (a.perm_q ? a.perm_q[(long long)bh * a.N + row0 + qr] : row0 + qr);
   bf16x8 qf[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
     uint4 u = make_uint4(0, 0, 0, 0);
-    if (qvalid) u = *reinterpret_cast<const uint4*>(qb + a.qv.row_off(bh, row0 + qr) + 16 * ks + 8 * half);
+    if (qvalid) u = *reinterpret_cast<const uint4*>(qb + a.qv.row_off(bh, qtok) + 16 * ks + 8 * half);
     qf[ks] = __builtin_bit_cast(bf16x8, u);
   }
   f32x16 o[DB];
@@ -552,10 +553,11 @@ __global__ __launch_bounds__(512) void k_sparse_attn_vec(AttnArgs a) {
   const T* qb = static_cast<const T*>(a.qv.p);
   const T* kb = static_cast<const T*>(a.kv.p);
   const T* vb = static_cast<const T*>(a.vv.p);
+  const int qtok = !valid ? 0 : (a.perm_q ? a.perm_q[(long long)bh * a.N + row0 + rl] : row0 + rl);
   float q[DQ], o[DQ];
 #pragma unroll
   for (int i = 0; i < DQ; ++i) {
-    q[i] = valid ? Elem<T>::load(qb + a.qv.row_off(bh, row0 + rl) + sub + 4 * i) : 0.f;
+    q[i] = valid ? Elem<T>::load(qb + a.qv.row_off(bh, qtok) + sub + 4 * i) : 0.f;
     o[i] = 0.f;
   }
   float m = -INFINITY, l = 0.f;
@@ -641,7 +643,8 @@ __global__ __launch_bounds__(512) void k_sparse_attn_vec(AttnArgs a) {
 // granted cells, from one pass over a key chunk (split-K), then a merge.
 // ============================================================================
 struct ProbeArgs {
-  View4 qv, kv, vv;  // permuted arrays
+  View4 qv, kv, vv;  // Q in token order, K and V permuted
+  const int* perm_q; // position -> token, addresses the probe rows of Q
   const int* ppos;
   const int* pgroup;
   const int* kgroup;
@@ -676,9 +679,10 @@ __global__ __launch_bounds__(256) void k_probe_attn_vec(ProbeArgs a) {
   const VT* vb = static_cast<const VT*>(a.vv.p);
   float q[DQ], od[DQ], os[DQ];
   const int prow = valid ? a.ppos[(long long)bh * a.M + p] : 0;
+  const int ptok = valid ? a.perm_q[(long long)bh * a.N + prow] : 0;
 #pragma unroll
   for (int i = 0; i < DQ; ++i) {
-    q[i] = valid ? Elem<T>::load(qb + a.qv.row_off(bh, prow) + sub + 4 * i) : 0.f;
+    q[i] = valid ? Elem<T>::load(qb + a.qv.row_off(bh, ptok) + sub + 4 * i) : 0.f;
     od[i] = 0.f;
     os[i] = 0.f;
   }
@@ -799,11 +803,12 @@ __global__ __launch_bounds__(128, 2) void k_probe_attn_mfma(ProbeArgs a) {
   const bf16_t* kb = static_cast<const bf16_t*>(a.kv.p);
   const bf16_t* vb = static_cast<const bf16_t*>(a.vv.p);
   const int prow = valid ? a.ppos[(long long)bh * a.M + p] : 0;
+  const int ptok = valid ? a.perm_q[(long long)bh * a.N + prow] : 0;
   bf16x8 qf[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
     uint4 u = make_uint4(0, 0, 0, 0);
-    if (valid) u = *reinterpret_cast<const uint4*>(qb + a.qv.row_off(bh, prow) + 16 * ks + 8 * half);
+    if (valid) u = *reinterpret_cast<const uint4*>(qb + a.qv.row_off(bh, ptok) + 16 * ks + 8 * half);
     qf[ks] = __builtin_bit_cast(bf16x8, u);
   }
   f32x16 od[DB], os[DB];
@@ -1033,7 +1038,7 @@ __global__ __launch_bounds__(256) void k_probe_overwrite(MutView4 o, const int* 
 static AttnArgs attn_args(const Plan& p, bool correct) {
   AttnArgs a;
   const long long nd = (long long)p.N * p.d;
-  a.qv = View4{p.qp, (long long)p.H * nd, nd, p.d, p.H};
+  a.qv = p.q;
   a.kv = View4{p.kp, (long long)p.H * nd, nd, p.d, p.H};
   a.vv = View4{p.vp, (long long)p.H * nd, nd, p.d, p.H};
   a.o = p.o;
@@ -1104,7 +1109,8 @@ hipError_t launch_probe_attention(const Plan& p, hipStream_t s) {
   if (p.M <= 0) return hipSuccess;
   ProbeArgs a;
   const long long nd = (long long)p.N * p.d;
-  a.qv = View4{p.qp, (long long)p.H * nd, nd, p.d, p.H};
+  a.qv = p.q;
+  a.perm_q = p.perm_q;
   a.kv = View4{p.kp, (long long)p.H * nd, nd, p.d, p.H};
   a.vv = View4{p.vp, (long long)p.H * nd, nd, p.d, p.H};
   a.ppos = p.ppos;

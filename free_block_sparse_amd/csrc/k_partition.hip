@@ -884,10 +884,7 @@ __global__ __launch_bounds__(256) void k_gather(GatherArgs a) {
   if (vf16 && blockIdx.x == 0 && threadIdx.x == 0) a.vexp[bh] = vk;
   if (pos >= a.N) return;
   const long long dst = ((long long)bh * a.N + pos) * a.d + c * VEC;
-  const int tq = a.perm_q[(long long)bh * a.N + pos];
   const int tk = a.perm_k[(long long)bh * a.N + pos];
-  *reinterpret_cast<uint4*>(static_cast<T*>(a.qp) + dst) =
-      *reinterpret_cast<const uint4*>(static_cast<const T*>(a.q.p) + a.q.row_off(bh, tq) + c * VEC);
   *reinterpret_cast<uint4*>(static_cast<T*>(a.kp) + dst) =
       *reinterpret_cast<const uint4*>(static_cast<const T*>(a.k.p) + a.k.row_off(bh, tk) + c * VEC);
   const uint4 vv = *reinterpret_cast<const uint4*>(static_cast<const T*>(a.v.p) + a.v.row_off(bh, tk) + c * VEC);
@@ -1022,7 +1019,7 @@ hipError_t launch_gather(const Plan& p, hipStream_t s) {
     hipError_t e = launch_vmax(p, s);
     if (e != hipSuccess) return e;
   }
-  GatherArgs a{p.q, p.k, p.v, vf16 ? p.vmax : nullptr, p.vexp, p.perm_q, p.perm_k, p.kv_labels, p.qp, p.kp, p.vp,
+  GatherArgs a{p.k, p.v, vf16 ? p.vmax : nullptr, p.vexp, p.perm_k, p.kv_labels, p.kp, p.vp,
                p.kgroup, p.N, p.d};
   const int vec = 16 / p.esize;
   const int rows_per_blk = 256 / (p.d / vec);

@@ -647,9 +647,13 @@ struct ProbeSelArgs {
 __global__ __launch_bounds__(64) void k_probe_select(ProbeSelArgs a) {
   __shared__ int ne[kMaxGroups];
   __shared__ int mg[kMaxGroups];
+  __shared__ int off[kMaxGroups + 1];
   const int bh = blockIdx.x;
-  if (threadIdx.x != 0 || a.M <= 0) return;
-  const int* off = a.off_q + (long long)bh * (a.GQ + 1);
+  if (a.M <= 0) return;
+  // the group offsets are staged in LDS; one lane then allocates in order
+  for (int g = threadIdx.x; g <= a.GQ; g += 64) off[g] = a.off_q[(long long)bh * (a.GQ + 1) + g];
+  __syncthreads();
+  if (threadIdx.x != 0) return;
   int gp = 0;
   for (int g = 0; g < a.GQ; ++g) {
     mg[g] = 0;

@@ -103,13 +103,11 @@ struct QMetricArgs {
 };
 
 struct GatherArgs {
-  View4 q, k, v;
+  View4 k, v;
   const uint32_t* vmax;   // bf16 inputs: V is stored as fp16 scaled by 2^-vexp
   int* vexp;
-  const int* perm_q;
   const int* perm_k;
   const int* kv_labels;
-  void* qp;
   void* kp;
   void* vp;
   int* kgroup;

@@ -149,7 +149,6 @@ void plan_carve(Plan* p, char* base) {
   p->cbar = c.take<double>(BH * p->GK * d);
   p->qbar = c.take<double>(BH * p->GQ * d);
   p->mq = c.take<float>(BH * d * d);
-  p->qp = c.take<char>(BH * N * d * p->esize);
   p->kp = c.take<char>(BH * N * d * p->esize);
   p->vp = c.take<char>(BH * N * d * p->esize);
   p->kgroup = c.take<int>(BH * N);

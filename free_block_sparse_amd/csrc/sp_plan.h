@@ -63,8 +63,7 @@ struct Plan {
   double* cbar;           // [BH, GK, d] raw key means
   double* qbar;           // [BH, GQ, d] raw query means
   float* mq;              // [BH, d, d] query metric s^2 Cbar^T Cbar
-  void* qp;               // [BH, N, d] permuted copies (input dtype)
-  void* kp;
+  void* kp;               // [BH, N, d] permuted copies of K (input dtype) and V
   void* vp;
   int* kgroup;            // [BH, N] key-group id of each permuted key position
   uint32_t* vmax;         // [BH] bit pattern of max |v| (bf16 inputs)
