@@ -231,7 +231,7 @@ __global__ __launch_bounds__(1024) void k_fit(FitArgs a) {
   __shared__ double bp[64];
   __shared__ double edg[128 + 2], eeo[64 + 2], etau[64], evb[64], epb[64], erot[4 * 64];
   __shared__ double Ycl[SM * 32];  // Y (M x rk) when M <= 64 and rk <= 32
-  __shared__ double sws[kMaxProbe];  // sqrt of the probe weights
+  __shared__ double wl[kMaxProbe];  // the probe weights
   __shared__ int ectl[8];
   const int bh = blockIdx.x, tid = threadIdx.x, nt = blockDim.x;
   const int M = a.M, d = a.d, Rmax = a.R;  // Rmax: column stride of the W and V outputs
@@ -253,17 +253,33 @@ __global__ __launch_bounds__(1024) void k_fit(FitArgs a) {
   double* Kp = Wm + 128 * 64 + 256 * 64;                                     // primal system d x d (M > d)
   const float* ode = a.ode + (long long)bh * M * d;
   const float* osp = a.osp + (long long)bh * M * d;
-  const double* w = a.pw + (long long)bh * M;
+  const double* wg = a.pw + (long long)bh * M;
+  const double* w = wl;
 
-  for (int e = tid; e < M * d; e += nt) {
-    const int mm = e / d, dm = e - (e / d) * d;
-    Rf[mm * ldx + dm] = ode[e] - osp[e];
-    Xf[mm * ldx + dm] = osp[e];
+  // staged eight elements per thread at a time, the loads in flight together
+  for (int e0 = 0; e0 < M * d; e0 += 8 * nt) {
+    float od[8], op[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int e = e0 + tid + u * nt;
+      od[u] = e < M * d ? ode[e] : 0.f;
+      op[u] = e < M * d ? osp[e] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int e = e0 + tid + u * nt;
+      if (e < M * d) {
+        const int mm = e / d, dm = e - (e / d) * d;
+        Rf[mm * ldx + dm] = od[u] - op[u];
+        Xf[mm * ldx + dm] = op[u];
+      }
+    }
   }
   double wpart = 0.0;
   for (int i = tid; i < M; i += nt) {
-    wpart += w[i];
-    sws[i] = sqrt(w[i]);
+    const double wi = wg[i];
+    wpart += wi;
+    wl[i] = wi;
   }
   const double ws = block_sum_d(wpart, red);
   for (int dm = tid; dm < d; dm += nt) {
@@ -406,9 +422,9 @@ __global__ __launch_bounds__(1024) void k_fit(FitArgs a) {
         const int i = e / M, j = e - (e / M) * M;
         double acc = 0.0;
         for (int dm = 0; dm < d; ++dm) acc += (double)Xf[i * ldx + dm] * (double)Xf[j * ldx + dm];
-        K[i * ldg + j] = sws[i] * sws[j] * acc + (i == j ? lam : 0.0);
+        K[i * ldg + j] = sqrt(w[i] * w[j]) * acc + (i == j ? lam : 0.0);
       }
-      for (int e = tid; e < M * rk; e += nt) Yc[e] *= sws[e / rk];
+      for (int e = tid; e < M * rk; e += nt) Yc[e] *= sqrt(w[e / rk]);
       block_sync();
       if (M <= 64) {
         // one wave factors K column by column (lane i owns row i of L, left-
@@ -468,7 +484,7 @@ __global__ __launch_bounds__(1024) void k_fit(FitArgs a) {
       }
       if (ok) {
         // W = Xc^T D^1/2 Y
-        for (int e = tid; e < M * rk; e += nt) Yc[e] *= sws[e / rk];
+        for (int e = tid; e < M * rk; e += nt) Yc[e] *= sqrt(w[e / rk]);
         block_sync();
         for (int e = tid; e < d * rk; e += nt) {
           const int dm = e / rk, k = e - (e / rk) * rk;

@@ -180,9 +180,15 @@ __global__ __launch_bounds__(1024) void k_key_eig(EigArgs a) {
   __shared__ float lamv[D];  // eigenvalue of column i of Z
   const int bh = blockIdx.x, tid = threadIdx.x;
   const float* mk = a.mk + (long long)bh * D * D;
-  for (int e = tid; e < D * D; e += NT) {
-    const int i = e / D, j = e - (e / D) * D;
-    A[i * LD + j] = mk[e];
+  {
+    float t[D * D / NT];
+#pragma unroll
+    for (int u = 0; u < D * D / NT; ++u) t[u] = mk[tid + NT * u];
+#pragma unroll
+    for (int u = 0; u < D * D / NT; ++u) {
+      const int e = tid + NT * u, i = e / D, j = e - (e / D) * D;
+      A[i * LD + j] = t[u];
+    }
   }
   __syncthreads();
   const EigWork<float> w{A, LD, Z, LD, dg, eo, tau, vb, pb, rot, ctl};
@@ -549,8 +555,17 @@ __global__ __launch_bounds__(1024) void k_group_scan(ScanArgs a) {
   const int c0 = act ? (int)((long long)pt * nch / P) : 0;
   const int c1 = act ? (int)((long long)(pt + 1) * nch / P) : 0;
   const int* cnt = a.counts + (long long)bh * nch * a.gstride;
+  // loads eight at a time, so they are in flight together
   int sum = 0;
-  for (int c = c0; c < c1; ++c) sum += cnt[(long long)c * a.gstride + g];
+  int c = c0;
+  for (; c + 8 <= c1; c += 8) {
+    int v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = cnt[(long long)(c + u) * a.gstride + g];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) sum += v[u];
+  }
+  for (; c < c1; ++c) sum += cnt[(long long)c * a.gstride + g];
   if (act) part[pt * G + g] = sum;
   __syncthreads();
   if (tid < G) {
@@ -574,9 +589,20 @@ __global__ __launch_bounds__(1024) void k_group_scan(ScanArgs a) {
   if (tid == 0) off[G] = a.N;
   for (int q = 0; q < pt; ++q) base += part[q * G + g];
   int* co = a.chunkoff + (long long)bh * nch * a.gstride;
-  for (int c = c0; c < c1; ++c) {
-    co[(long long)c * a.gstride + g] = base;
-    base += cnt[(long long)c * a.gstride + g];
+  int c2 = c0;
+  for (; c2 + 8 <= c1; c2 += 8) {
+    int v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = cnt[(long long)(c2 + u) * a.gstride + g];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      co[(long long)(c2 + u) * a.gstride + g] = base;
+      base += v[u];
+    }
+  }
+  for (; c2 < c1; ++c2) {
+    co[(long long)c2 * a.gstride + g] = base;
+    base += cnt[(long long)c2 * a.gstride + g];
   }
 }
 
@@ -712,9 +738,19 @@ __global__ __launch_bounds__(256) void k_centre_images(UpdateArgs a) {
   const int bh = blockIdx.y, g0 = blockIdx.x * GB, tid = threadIdx.x;
   const int Dp = a.Dp, Dimg = a.Dimg;
   const int ng = min(GB, a.G - g0);
-  for (int e = tid; e < GB * 128; e += 256) {
-    const int gl = e >> 7, j = e & 127;
-    smean[gl][j] = (gl < ng && j < Dp) ? a.cmean[((long long)bh * a.gstride + g0 + gl) * a.cstride + j] : 0.0;
+  {
+    // all eight loads of a thread in flight before the stores
+    double t[GB * 128 / 256];
+#pragma unroll
+    for (int u = 0; u < GB * 128 / 256; ++u) {
+      const int e = tid + 256 * u, gl = e >> 7, j = e & 127;
+      t[u] = (gl < ng && j < Dp) ? a.cmean[((long long)bh * a.gstride + g0 + gl) * a.cstride + j] : 0.0;
+    }
+#pragma unroll
+    for (int u = 0; u < GB * 128 / 256; ++u) {
+      const int e = tid + 256 * u;
+      smean[e >> 7][e & 127] = t[u];
+    }
   }
   // thread (group gl, piece jj) owns dims 8 jj .. 8 jj + 7
   const int gl = tid >> 4, jj = tid & 15;
@@ -727,9 +763,28 @@ __global__ __launch_bounds__(256) void k_centre_images(UpdateArgs a) {
     for (int i0 = 0; i0 < Dp; i0 += MR) {
       const int nr = min(MR, Dp - i0);
       __syncthreads();
-      for (int e = tid; e < nr * Dp; e += 256) {
-        const int r = e / Dp, c = e - (e / Dp) * Dp;
-        sm[r][c] = M[(long long)(i0 + r) * Dp + c];
+      if ((Dp & 3) == 0) {
+        // float4 pieces, up to four per thread in flight together
+        const int np = nr * Dp / 4;
+        float4 t[MR * 128 / 4 / 256];
+#pragma unroll
+        for (int u = 0; u < MR * 128 / 4 / 256; ++u) {
+          const int e = tid + 256 * u;
+          if (e < np) t[u] = *reinterpret_cast<const float4*>(M + (long long)i0 * Dp + 4 * e);
+        }
+#pragma unroll
+        for (int u = 0; u < MR * 128 / 4 / 256; ++u) {
+          const int e = tid + 256 * u;
+          if (e < np) {
+            const int r = (4 * e) / Dp, c = 4 * e - r * Dp;
+            *reinterpret_cast<float4*>(&sm[r][c]) = t[u];
+          }
+        }
+      } else {
+        for (int e = tid; e < nr * Dp; e += 256) {
+          const int r = e / Dp, c = e - (e / Dp) * Dp;
+          sm[r][c] = M[(long long)(i0 + r) * Dp + c];
+        }
       }
       __syncthreads();
       if (8 * jj < Dp) {

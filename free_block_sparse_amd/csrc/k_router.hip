@@ -691,14 +691,19 @@ __global__ __launch_bounds__(64) void k_probe_select(ProbeSelArgs a) {
     for (int t = 0; t < mg[g]; ++t) {
       a.ppos[(long long)bh * M + k] = off[g] + (int)(((2LL * t + 1) * sz) / (2LL * mg[g]));
       a.pgroup[(long long)bh * M + k] = g;
-      const double w = (double)sz / (double)mg[g];
-      a.pw[(long long)bh * M + k] = w;
-      tot += w;
+      tot += (double)sz / (double)mg[g];
       ++k;
     }
   }
+  // the weights again, scaled (stores only: no load waits on them)
   const double f = (double)M / tot;
-  for (int i = 0; i < M; ++i) a.pw[(long long)bh * M + i] *= f;
+  k = 0;
+  for (int r = 0; r < gp; ++r) {
+    const int g = ne[r];
+    const long long sz = off[g + 1] - off[g];
+    const double wv = ((double)sz / (double)mg[g]) * f;
+    for (int t = 0; t < mg[g]; ++t) a.pw[(long long)bh * M + k++] = wv;
+  }
 }
 
 hipError_t launch_probe_select(const Plan& p, hipStream_t s) {
