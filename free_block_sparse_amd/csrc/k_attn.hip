@@ -1002,17 +1002,34 @@ __global__ __launch_bounds__(D) void k_probe_merge(ProbeArgs a) {
   const int bh = blockIdx.z, which = blockIdx.y, p = blockIdx.x, dm = threadIdx.x;
   const long long stride_ch = 2LL * a.M * (D + 2);
   const float* pr0 = a.ppart + (((long long)bh * a.n_pchunk) * 2 + which) * a.M * (D + 2) + (long long)p * (D + 2);
+  // chunk partials eight at a time, so their loads are in flight together
   float mx = -INFINITY;
-  for (int ch = 0; ch < a.n_pchunk; ++ch) mx = fmaxf(mx, pr0[ch * stride_ch + D]);
+  for (int c0 = 0; c0 < a.n_pchunk; c0 += 8) {
+    float m8[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) m8[u] = c0 + u < a.n_pchunk ? pr0[(c0 + u) * stride_ch + D] : -INFINITY;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) mx = fmaxf(mx, m8[u]);
+  }
   float num = 0.f, den = 0.f;
   if (mx > -INFINITY) {
-    for (int ch = 0; ch < a.n_pchunk; ++ch) {
-      const float* pr = pr0 + ch * stride_ch;
-      const float mc = pr[D];
-      if (mc == -INFINITY) continue;
-      const float f = exp2f(mc - mx);
-      num += f * pr[dm];
-      den += f * pr[D + 1];
+    for (int c0 = 0; c0 < a.n_pchunk; c0 += 8) {
+      float mc[8], xv[8], lv[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const bool in = c0 + u < a.n_pchunk;
+        const float* pr = pr0 + (c0 + u) * stride_ch;
+        mc[u] = in ? pr[D] : -INFINITY;
+        xv[u] = in ? pr[dm] : 0.f;
+        lv[u] = in ? pr[D + 1] : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (mc[u] == -INFINITY) continue;
+        const float f = exp2f(mc[u] - mx);
+        num += f * xv[u];
+        den += f * lv[u];
+      }
     }
   }
   float* out = which == 0 ? a.ode : a.osp;

@@ -644,66 +644,92 @@ struct ProbeSelArgs {
   double* pw;
 };
 
+// One wave per (b, h).  The non-empty groups are compacted in order with
+// ballots, the strided allocation (M < groups) counts with LDS atomics, and
+// every probe finds its group by a binary search over the allocation prefix.
 __global__ __launch_bounds__(64) void k_probe_select(ProbeSelArgs a) {
   __shared__ int ne[kMaxGroups];
   __shared__ int mg[kMaxGroups];
   __shared__ int off[kMaxGroups + 1];
-  const int bh = blockIdx.x;
-  if (a.M <= 0) return;
-  // the group offsets are staged in LDS; one lane then allocates in order
-  for (int g = threadIdx.x; g <= a.GQ; g += 64) off[g] = a.off_q[(long long)bh * (a.GQ + 1) + g];
+  __shared__ int cum[kMaxGroups + 1];
+  __shared__ double wl[kMaxProbe];
+  const int bh = blockIdx.x, lane = threadIdx.x;
+  const int M = a.M, GQ = a.GQ;
+  if (M <= 0) return;
+  for (int g = lane; g <= GQ; g += 64) off[g] = a.off_q[(long long)bh * (GQ + 1) + g];
+  for (int g = lane; g < GQ; g += 64) mg[g] = 0;
   __syncthreads();
-  if (threadIdx.x != 0) return;
+  const unsigned long long below = (1ull << lane) - 1ull;
   int gp = 0;
-  for (int g = 0; g < a.GQ; ++g) {
-    mg[g] = 0;
-    if (off[g + 1] > off[g]) ne[gp++] = g;
+  for (int g0 = 0; g0 < GQ; g0 += 64) {
+    const int g = g0 + lane;
+    const bool nz = g < GQ && off[g + 1] > off[g];
+    const unsigned long long m = __builtin_amdgcn_ballot_w64(nz);
+    if (nz) ne[gp + __builtin_popcountll(m & below)] = g;
+    gp += __builtin_popcountll(m);
   }
-  const int M = a.M;
+  __syncthreads();
+  if (gp == 0) return;
   if (M >= gp) {
-    const int base = M / gp, rem = M - (M / gp) * gp;
-    long long carry = 0;
-    for (int r = 0; r < gp; ++r) {
-      const int g = ne[r];
-      const long long want = base + (r < rem ? 1 : 0) + carry;
-      const long long sz = off[g + 1] - off[g];
-      const long long m = want < sz ? want : sz;
-      mg[g] = (int)m;
-      carry = want - m;
-    }
-    while (carry > 0) {
-      for (int r = 0; r < gp && carry > 0; ++r) {
+    if (lane == 0) {
+      const int base = M / gp, rem = M - (M / gp) * gp;
+      long long carry = 0;
+      for (int r = 0; r < gp; ++r) {
         const int g = ne[r];
-        const long long room = (long long)(off[g + 1] - off[g]) - mg[g];
-        const long long add = carry < room ? carry : room;
-        mg[g] += (int)add;
-        carry -= add;
+        const long long want = base + (r < rem ? 1 : 0) + carry;
+        const long long sz = off[g + 1] - off[g];
+        const long long m = want < sz ? want : sz;
+        mg[g] = (int)m;
+        carry = want - m;
+      }
+      while (carry > 0) {
+        for (int r = 0; r < gp && carry > 0; ++r) {
+          const int g = ne[r];
+          const long long room = (long long)(off[g + 1] - off[g]) - mg[g];
+          const long long add = carry < room ? carry : room;
+          mg[g] += (int)add;
+          carry -= add;
+        }
       }
     }
   } else {
-    for (int j = 0; j < M; ++j) mg[ne[((2LL * j + 1) * gp) / (2LL * M)]] += 1;
+    for (int j = lane; j < M; j += 64) atomicAdd(&mg[ne[(int)(((2LL * j + 1) * gp) / (2LL * M))]], 1);
   }
-  int k = 0;
-  double tot = 0.0;
-  for (int r = 0; r < gp; ++r) {
-    const int g = ne[r];
-    const long long sz = off[g + 1] - off[g];
-    for (int t = 0; t < mg[g]; ++t) {
-      a.ppos[(long long)bh * M + k] = off[g] + (int)(((2LL * t + 1) * sz) / (2LL * mg[g]));
-      a.pgroup[(long long)bh * M + k] = g;
-      tot += (double)sz / (double)mg[g];
-      ++k;
+  __syncthreads();
+  // cum[r]: probes of the groups ranked before r
+  int run = 0;
+  for (int r0 = 0; r0 < gp; r0 += 64) {
+    const int r = r0 + lane;
+    const int v = r < gp ? mg[ne[r]] : 0;
+    int inc = v;
+    for (int o = 1; o < 64; o <<= 1) {
+      const int t = __shfl_up(inc, o, 64);
+      if (lane >= o) inc += t;
     }
+    if (r < gp) cum[r] = run + inc - v;
+    run += __shfl(inc, 63, 64);
   }
-  // the weights again, scaled (stores only: no load waits on them)
-  const double f = (double)M / tot;
-  k = 0;
-  for (int r = 0; r < gp; ++r) {
-    const int g = ne[r];
+  if (lane == 0) cum[gp] = run;
+  __syncthreads();
+  double part = 0.0;
+  for (int k = lane; k < M; k += 64) {
+    int lo = 0, hi = gp - 1;  // last rank with cum[r] <= k
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (cum[mid] <= k) lo = mid;
+      else hi = mid - 1;
+    }
+    const int g = ne[lo], t = k - cum[lo];
     const long long sz = off[g + 1] - off[g];
-    const double wv = ((double)sz / (double)mg[g]) * f;
-    for (int t = 0; t < mg[g]; ++t) a.pw[(long long)bh * M + k++] = wv;
+    a.ppos[(long long)bh * M + k] = off[g] + (int)(((2LL * t + 1) * sz) / (2LL * mg[g]));
+    a.pgroup[(long long)bh * M + k] = g;
+    const double w = (double)sz / (double)mg[g];
+    wl[k] = w;
+    part += w;
   }
+  for (int o = 32; o > 0; o >>= 1) part += __shfl_xor(part, o, 64);
+  const double f = (double)M / part;
+  for (int k = lane; k < M; k += 64) a.pw[(long long)bh * M + k] = wl[k] * f;
 }
 
 hipError_t launch_probe_select(const Plan& p, hipStream_t s) {
