@@ -17,6 +17,10 @@
 // argmin_g (c_g - 2 x . y_g) with y_g = M xbar_g and c_g = xbar_g . y_g, so one
 // bf16 MFMA product with a fused argmin does the assignment.  Centre images
 // are kept as hi + lo bf16 pairs (16 significant bits).
+#include <algorithm>
+#include <map>
+#include <mutex>
+
 #include "sp_kernels.h"
 #include "sp_eig.h"
 
@@ -274,7 +278,7 @@ __global__ __launch_bounds__(256) void k_key_coords(CoordArgs a) {
 // bf16 pieces (24 significant bits, like fp32); products with bf16 keys are
 // exact and accumulate in fp32.  Each wave takes 32-token blocks; lanes hold
 // the map as the A operand for up to two blocks of 32 coordinates.
-template <int D>
+template <int D, int NCB>
 __global__ __launch_bounds__(256) void k_key_coords_mfma(CoordArgs a) {
   constexpr int KS = D / 16;
   const int bh = blockIdx.y, tid = threadIdx.x;
@@ -282,9 +286,9 @@ __global__ __launch_bounds__(256) void k_key_coords_mfma(CoordArgs a) {
   const int rK = a.rK, rKpad = a.rKpad, N = a.N;
   const int ncb = (rK + 31) / 32;
   const float* kmap = a.kmap + (long long)bh * D * rK;
-  bf16x8 mp[3][2][KS];
+  bf16x8 mp[3][NCB][KS];  // NCB 32-coordinate blocks (r_K <= 32 NCB)
 #pragma unroll
-  for (int cb = 0; cb < 2; ++cb)
+  for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       bf16_t pv[3][8];
@@ -316,7 +320,7 @@ __global__ __launch_bounds__(256) void k_key_coords_mfma(CoordArgs a) {
       kf[ks] = __builtin_bit_cast(bf16x8, u);
     }
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb) {
+    for (int cb = 0; cb < NCB; ++cb) {
       if (cb >= ncb) break;
       f32x16 acc = {};
       // smallest pieces first
@@ -363,7 +367,7 @@ __global__ __launch_bounds__(256) void k_split_rows(SplitArgs a) {
 // ============================================================================
 // a4/a8: Lloyd assignment.  One bf16 MFMA product of centre images (A, 32
 // centres x 16 dims) against point rows (B, 16 dims x 32 points) per k-step,
-// fused with the argmin.  256 points per workgroup, 64 per wave.
+// fused with the argmin.  256 points per workgroup, 32 or 64 per wave.
 // MFMA 32x32x16 lane layout: A[m][k]: m = lane%32, k = 8*(lane/32)+j;
 // B[k][n]: k = 8*(lane/32)+j, n = lane%32; D[i][j]: j = lane%32,
 // i = (r%4) + 8*(r/4) + 4*(lane/32) for accumulator register r.
@@ -393,12 +397,178 @@ __device__ inline float block_argmin16(const f32x16& acc, const float* sb, int* 
   return v[0];
 }
 
+// Largest of the 16 accumulator values a lane holds for a 32-centre block
+// (same register order as above); ties keep the lower register.
+__device__ inline float block_argmax16(const f32x16& acc, int* ridx) {
+  float v[16];
+  int id[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    v[r] = acc[r];
+    id[r] = r;
+  }
+#pragma unroll
+  for (int w = 1; w < 16; w <<= 1)
+#pragma unroll
+    for (int r = 0; r < 16; r += 2 * w) {
+      const bool right = v[r + w] > v[r];
+      v[r] = right ? v[r + w] : v[r];
+      id[r] = right ? id[r + w] : id[r];
+    }
+  *ridx = id[0];
+  return v[0];
+}
+
+template <int D>
+__global__ __launch_bounds__(512) void k_kmeans_assign(AssignArgs a) {
+  // Form for wide bf16 rows (d = 128) and G <= 256, where restaging the
+  // centres per 256 points (the staged form below) costs twice the points'
+  // own traffic.  A workgroup stages all G <= 256 centre images of one (b, h)
+  // in LDS once
+  // and covers a.cpw consecutive 256-point chunks of it.  Its eight waves run
+  // without further barriers: each takes 64-point blocks in turn (two
+  // 32-point MFMA columns held as B operands in registers, the next block's
+  // rows loaded while the current one computes), runs through all centres
+  // 32 at a time (A operands from LDS, one fragment feeding both columns),
+  // keeps each point's nearest centre (ties keep the lower centre), and adds
+  // its labels to the chunk histograms with integer atomics (the workgroup
+  // clears its chunks' rows first, so the counts are exact).  The
+  // accumulators start at -c_g / 2, so they end at
+  // x . y_g - c_g / 2 = -(c_g - 2 x . y_g) / 2 and the nearest centre is the
+  // largest value.
+  constexpr int KS = D / 16, LDI = D + 8, NT = 512, NW = 8, PB = 2, BP = 32 * PB;
+  __shared__ __attribute__((aligned(16))) bf16_t sh[256 * LDI];
+  __shared__ __attribute__((aligned(16))) bf16_t sl[256 * LDI];
+  __shared__ __attribute__((aligned(16))) float sbias[256];
+  const int bh = blockIdx.y, tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int half = lane >> 5, col = lane & 31;
+  const int N = a.N, G = a.G, G32 = (G + 31) & ~31;
+  const int c_begin = blockIdx.x * a.cpw;
+  const int c_end = min(a.nchunk, c_begin + a.cpw);
+  if (c_begin >= c_end) return;  // whole workgroup
+  const int n_begin = c_begin * kChunk, n_end = min(N, c_end * kChunk);
+  const int nblk = (n_end - n_begin + BP - 1) / BP;
+
+  // clear this workgroup's histogram rows; stage the centre images (rows
+  // past G are zero with an infinite bias)
+  for (int e = tid; e < (c_end - c_begin) * G; e += NT) {
+    const int cc = e / G, g = e - cc * G;
+    a.counts[((long long)bh * a.nchunk + c_begin + cc) * a.gstride + g] = 0;
+  }
+  {
+    const bf16_t* yh = a.yhi + (long long)bh * a.gstride * a.ystride;
+    const bf16_t* yl = a.ylo + (long long)bh * a.gstride * a.ystride;
+    constexpr int PPR = D / 8;
+    for (int e0 = 0; e0 < G32 * PPR; e0 += 4 * NT) {
+      u32x4 vh[4], vl[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int e = e0 + tid + NT * u, r = e / PPR, cc = e % PPR;
+        vh[u] = vl[u] = u32x4{0, 0, 0, 0};
+        if (r < G) {
+          vh[u] = *reinterpret_cast<const u32x4*>(yh + (long long)r * a.ystride + cc * 8);
+          vl[u] = *reinterpret_cast<const u32x4*>(yl + (long long)r * a.ystride + cc * 8);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int e = e0 + tid + NT * u, r = e / PPR, cc = e % PPR;
+        if (r < G32) {
+          *reinterpret_cast<u32x4*>(sh + r * LDI + cc * 8) = vh[u];
+          *reinterpret_cast<u32x4*>(sl + r * LDI + cc * 8) = vl[u];
+        }
+      }
+    }
+    for (int e = tid; e < G32; e += NT) sbias[e] = e < G ? a.ybias[(long long)bh * a.gstride + e] : INFINITY;
+  }
+  __syncthreads();
+
+  const bf16_t* pbase = static_cast<const bf16_t*>(a.pts.p) + a.pts.row_off(bh, 0);
+  const long long psn = a.pts.sn;
+  int* cnt = a.counts + (long long)bh * a.nchunk * a.gstride;
+  u32x4 ph[PB][KS];
+  // block b's fragments: lane (col, half) holds dims 16 ks + 8 half .. + 7 of
+  // point n_begin + BP b + 32 pb + col (rows past the end repeat the last row)
+#define SP_LOAD_BLOCK(b, DH)                                                                      \
+  _Pragma("unroll") for (int pb = 0; pb < PB; ++pb) {                                             \
+    const int n = min(n_begin + BP * (b) + 32 * pb + col, N - 1);                                 \
+    _Pragma("unroll") for (int ks = 0; ks < KS; ++ks) {                                           \
+      DH[pb][ks] = *reinterpret_cast<const u32x4*>(pbase + n * psn + 16 * ks + 8 * half);         \
+    }                                                                                             \
+  }
+  if (w < nblk) SP_LOAD_BLOCK(w, ph)
+  for (int b = w; b < nblk; b += NW) {
+    u32x4 nh[PB][KS];
+    SP_LOAD_BLOCK(min(b + NW, nblk - 1), nh)
+    float best[PB];
+    int bidx[PB];
+#pragma unroll
+    for (int pb = 0; pb < PB; ++pb) {
+      best[pb] = -INFINITY;
+      bidx[pb] = 0;
+    }
+    for (int cb = 0; cb < G32; cb += 32) {
+      // -c_g / 2 of this lane's centres: four runs of four consecutive centres
+      f32x16 cinit;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float4 f = *reinterpret_cast<const float4*>(sbias + cb + 8 * q + 4 * half);
+        cinit[4 * q] = -0.5f * f.x;
+        cinit[4 * q + 1] = -0.5f * f.y;
+        cinit[4 * q + 2] = -0.5f * f.z;
+        cinit[4 * q + 3] = -0.5f * f.w;
+      }
+      f32x16 acc[PB];
+#pragma unroll
+      for (int pb = 0; pb < PB; ++pb) acc[pb] = cinit;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const int o = (cb + col) * LDI + 16 * ks + 8 * half;
+        const bf16x8 ah = *reinterpret_cast<const bf16x8*>(sh + o);
+        const bf16x8 al = *reinterpret_cast<const bf16x8*>(sl + o);
+#pragma unroll
+        for (int pb = 0; pb < PB; ++pb) {
+          const bf16x8 xh = __builtin_bit_cast(bf16x8, ph[pb][ks]);
+          acc[pb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, xh, acc[pb], 0, 0, 0);
+          acc[pb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, xh, acc[pb], 0, 0, 0);
+        }
+      }
+#pragma unroll
+      for (int pb = 0; pb < PB; ++pb) {
+        int rr;
+        const float sc = block_argmax16(acc[pb], &rr);
+        if (sc > best[pb]) {
+          best[pb] = sc;
+          bidx[pb] = cb + (rr & 3) + 8 * (rr >> 2) + 4 * half;
+        }
+      }
+    }
+#pragma unroll
+    for (int pb = 0; pb < PB; ++pb) {
+      const float ob = __shfl_xor(best[pb], 32, 64);
+      const int oi = __shfl_xor(bidx[pb], 32, 64);
+      if (ob > best[pb] || (ob == best[pb] && oi < bidx[pb])) bidx[pb] = oi;
+      const int n = n_begin + BP * b + 32 * pb + col;
+      if (half == 0 && n < n_end) {
+        a.labels[(long long)bh * N + n] = bidx[pb];
+        atomicAdd(cnt + (long long)(n / kChunk) * a.gstride + bidx[pb], 1);
+      }
+    }
+#pragma unroll
+    for (int pb = 0; pb < PB; ++pb)
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) ph[pb][ks] = nh[pb][ks];
+  }
+#undef SP_LOAD_BLOCK
+}
+
 template <int D, bool LO, int CG>
-__global__ __launch_bounds__(512, 4) void k_kmeans_assign(AssignArgs a) {
-  // One 256-point histogram chunk per workgroup (8 waves x one 32-point MFMA
-  // column, points held as B operands in registers), two workgroups per CU;
-  // the centre images are staged through LDS CG at a time (two barriers per
-  // CG centres) and read as A operands, two 32-centre blocks at a time.
+__global__ __launch_bounds__(512, 4) void k_kmeans_assign_staged(AssignArgs a) {
+  // General form (any D, any G <= kMaxGroups).  One 256-point histogram chunk per
+  // workgroup (8 waves x one 32-point MFMA column, points held as B operands
+  // in registers); the centre images are staged through LDS CG at a time
+  // (two barriers per CG centres) and read as A operands, two 32-centre
+  // blocks at a time.
   constexpr int KS = D / 16;
   constexpr int LDI = D + 8;  // padded LDS row (bank spread)
   constexpr int NT = 512;
@@ -966,6 +1136,31 @@ __global__ __launch_bounds__(256) void k_gather(GatherArgs a) {
     if (e_ != hipSuccess) return e_;                                 \
   } while (0)
 
+#define SP_LAUNCH_FN(fn, g, b, s, arg)                               \
+  do {                                                               \
+    void* args_[] = {(void*)&(arg)};                                 \
+    hipError_t e_ = hipLaunchKernel(fn, g, b, args_, 0, s);          \
+    if (e_ != hipSuccess) return e_;                                 \
+  } while (0)
+
+// workgroups of `fn` (with `threads` threads) resident at once on the current
+// device, cached per device and kernel
+static long long resident_slots(const void* fn, int threads) {
+  static std::mutex mu;
+  static std::map<std::pair<int, const void*>, long long> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  std::lock_guard<std::mutex> lk(mu);
+  auto it = cache.find({dev, fn});
+  if (it != cache.end()) return it->second;
+  int per_cu = 0, ncu = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, threads, 0) != hipSuccess) per_cu = 1;
+  if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) ncu = 256;
+  const long long v = (long long)std::max(1, per_cu) * std::max(1, ncu);
+  cache[{dev, fn}] = v;
+  return v;
+}
+
 hipError_t launch_sample_metric(const Plan& p, hipStream_t s) {
   SampleArgs a{p.q, p.N, p.Ms, p.seed, p.sample, p.mk};
   if (p.dtype == SPARSEPR_BF16) {
@@ -990,8 +1185,13 @@ hipError_t launch_key_coords(const Plan& p, hipStream_t s) {
   dim3 g((p.N + 63) / 64, p.BH);
   if (p.dtype == SPARSEPR_BF16) {
     const dim3 gm((p.N + 1023) / 1024, p.BH);
-    if (p.d == 128) SP_LAUNCH((k_key_coords_mfma<128>), gm, dim3(256), s, a);
-    else SP_LAUNCH((k_key_coords_mfma<64>), gm, dim3(256), s, a);
+    if (p.rK <= 32) {
+      if (p.d == 128) SP_LAUNCH((k_key_coords_mfma<128, 1>), gm, dim3(256), s, a);
+      else SP_LAUNCH((k_key_coords_mfma<64, 1>), gm, dim3(256), s, a);
+    } else {
+      if (p.d == 128) SP_LAUNCH((k_key_coords_mfma<128, 2>), gm, dim3(256), s, a);
+      else SP_LAUNCH((k_key_coords_mfma<64, 2>), gm, dim3(256), s, a);
+    }
   } else {
     if (p.d == 128) SP_LAUNCH((k_key_coords<float, 128>), g, dim3(256), s, a);
     else SP_LAUNCH((k_key_coords<float, 64>), g, dim3(256), s, a);
@@ -1006,25 +1206,38 @@ hipError_t launch_split_rows(const Plan& p, const View4& x, hipStream_t s) {
   return hipSuccess;
 }
 
-hipError_t launch_assign(const Plan& p, const AssignArgs& a, int D, bool lo, hipStream_t s) {
-  static_assert(kChunk == 256, "one assign workgroup covers one histogram chunk");
-  dim3 g(p.nchunk, p.BH);
-  const dim3 b(512);
+hipError_t launch_assign(const Plan& p, const AssignArgs& args, int D, bool lo, hipStream_t s) {
+  if (args.G < 1 || args.G > kMaxGroups) return hipErrorInvalidValue;
+  if (D == 128 && !lo && args.G <= 256) {
+    // resident centres; chunks per workgroup: the workgroups of one round
+    // over the GPU's resident slots share the chunks as evenly as whole
+    // chunks allow
+    AssignArgs a = args;
+    const void* fn = (const void*)k_kmeans_assign<128>;
+    const long long slots = resident_slots(fn, 512);
+    const long long per_bh = std::max(1LL, slots / p.BH);
+    a.cpw = (int)std::max(1LL, (p.nchunk + per_bh - 1) / per_bh);
+    const dim3 g((unsigned)((p.nchunk + a.cpw - 1) / a.cpw), p.BH);
+    SP_LAUNCH_FN(fn, g, dim3(512), s, a);
+    return hipSuccess;
+  }
+  // staged centres, one workgroup per histogram chunk
+  const dim3 g(p.nchunk, p.BH), b(512);
   if (D == 16) {
-    if (lo) SP_LAUNCH((k_kmeans_assign<16, true, 256>), g, b, s, a);
-    else SP_LAUNCH((k_kmeans_assign<16, false, 256>), g, b, s, a);
+    if (lo) SP_LAUNCH((k_kmeans_assign_staged<16, true, 256>), g, b, s, args);
+    else SP_LAUNCH((k_kmeans_assign_staged<16, false, 256>), g, b, s, args);
   } else if (D == 32) {
-    if (lo) SP_LAUNCH((k_kmeans_assign<32, true, 256>), g, b, s, a);
-    else SP_LAUNCH((k_kmeans_assign<32, false, 256>), g, b, s, a);
+    if (lo) SP_LAUNCH((k_kmeans_assign_staged<32, true, 256>), g, b, s, args);
+    else SP_LAUNCH((k_kmeans_assign_staged<32, false, 256>), g, b, s, args);
   } else if (D == 48) {
-    if (lo) SP_LAUNCH((k_kmeans_assign<48, true, 256>), g, b, s, a);
-    else SP_LAUNCH((k_kmeans_assign<48, false, 256>), g, b, s, a);
+    if (lo) SP_LAUNCH((k_kmeans_assign_staged<48, true, 256>), g, b, s, args);
+    else SP_LAUNCH((k_kmeans_assign_staged<48, false, 256>), g, b, s, args);
   } else if (D == 64) {
-    if (lo) SP_LAUNCH((k_kmeans_assign<64, true, 128>), g, b, s, a);
-    else SP_LAUNCH((k_kmeans_assign<64, false, 128>), g, b, s, a);
+    if (lo) SP_LAUNCH((k_kmeans_assign_staged<64, true, 128>), g, b, s, args);
+    else SP_LAUNCH((k_kmeans_assign_staged<64, false, 128>), g, b, s, args);
   } else if (D == 128) {
-    if (lo) SP_LAUNCH((k_kmeans_assign<128, true, 128>), g, b, s, a);
-    else SP_LAUNCH((k_kmeans_assign<128, false, 128>), g, b, s, a);
+    if (lo) SP_LAUNCH((k_kmeans_assign_staged<128, true, 128>), g, b, s, args);
+    else SP_LAUNCH((k_kmeans_assign_staged<128, false, 128>), g, b, s, args);
   } else {
     return hipErrorInvalidValue;
   }

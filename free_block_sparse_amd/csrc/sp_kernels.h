@@ -48,6 +48,7 @@ struct AssignArgs {
   int* labels;            // [BH, N]
   int* counts;            // [BH, nchunk, gstride]
   int nchunk;
+  int cpw;                // histogram chunks per workgroup (set by the launcher)
 };
 
 struct CountArgs {

@@ -58,6 +58,9 @@ CASES = {
     # two heads of the 8k video-DiT call
     "c2_two_heads": Case("c2_two_heads", 8, 32, 32, 2, 64, "bf16", 64, 64, 0.25, 64, 32,
                          workload="c2_dit_8k"),
+    # many groups: 300 key groups (more than one assignment workgroup's waves
+    # hold) and 200 query groups at d = 128
+    "many_groups": Case("many_groups", 4, 16, 40, 1, 128, "bf16", 300, 200, 0.3, 32, 8, seed=14),
 }
 
 
