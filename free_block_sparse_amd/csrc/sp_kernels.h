@@ -48,7 +48,7 @@ struct AssignArgs {
   int* labels;            // [BH, N]
   int* counts;            // [BH, nchunk, gstride]
   int nchunk;
-  int cpw;                // histogram chunks per workgroup (set by the launcher)
+  int cpw;                // histogram chunks per workgroup (resident form; set by the launcher)
 };
 
 struct CountArgs {

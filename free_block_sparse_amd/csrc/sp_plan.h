@@ -10,7 +10,6 @@
 namespace sp {
 
 constexpr int kChunk = 256;      // points per k-means histogram chunk
-constexpr int kMaxAssignChunks = 4;  // histogram chunks per assignment workgroup (at most)
 constexpr int kTileRows = 128;   // query rows per sparse-attention workgroup
 constexpr int kProbeChunk = 1024;  // keys per probe-attention workgroup
 constexpr int kMaxProbe = 256;
