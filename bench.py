@@ -62,8 +62,8 @@ def time_fn(fn, reps: int, torch) -> list:
     return out
 
 
-def cpu_baseline(x, w, cfg_kw, routed_first_head: int, n: int, d: int, m: int) -> dict:
-    """Time the oracle on head 0 only (a bounded sample of the call)."""
+def cpu_baseline(x, w, cfg_kw, n: int, d: int, m: int, heads: int = 4) -> dict:
+    """Time the oracle on the first `heads` heads (a bounded sample of the call)."""
     try:
         from threadpoolctl import threadpool_info
     except Exception:  # pragma: no cover
@@ -71,20 +71,23 @@ def cpu_baseline(x, w, cfg_kw, routed_first_head: int, n: int, d: int, m: int) -
     from oracle import OracleConfig, sparsepr_head
 
     cfg = OracleConfig(**cfg_kw)
-    q = x["q"][0, 0].double().numpy()
-    k = x["k"][0, 0].double().numpy()
-    v = x["v"][0, 0].double().numpy()
+    heads = min(heads, w.heads)
+    pairs = 0
     t0 = time.perf_counter()
-    r = sparsepr_head(q, k, v, cfg, bh=0)
+    for h in range(heads):
+        q = x["q"][0, h].double().numpy()
+        k = x["k"][0, h].double().numpy()
+        v = x["v"][0, h].double().numpy()
+        r = sparsepr_head(q, k, v, cfg, bh=h)
+        pairs += r["route"]["routed_pairs"] + m * n
     dt = time.perf_counter() - t0
-    pairs = r["route"]["routed_pairs"] + m * n
     cores = len(os.sched_getaffinity(0))
     if threadpool_info is not None:
         th = [p.get("num_threads", 0) for p in threadpool_info() if p.get("user_api") == "blas"]
         if th:
             cores = max(th)
     return {"value": 4.0 * d * pairs / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-            "sample": f"head 0 of {w.heads} of {w.name} (one full per-head call, {dt:.1f} s)",
+            "sample": f"heads 0-{heads - 1} of {w.heads} of {w.name} (full per-head calls, {dt:.1f} s)",
             "seconds": round(dt, 3)}
 
 
@@ -194,8 +197,8 @@ def main() -> int:
 
     cpu = None
     if not args.no_cpu_baseline:
-        log("timing the CPU oracle on one head (bounded sample)")
-        cpu = cpu_baseline(x, w, cfg_kw, heads[0]["routed_pairs"], N, d, w.probe_rows)
+        log("timing the CPU oracle on the first heads (bounded sample)")
+        cpu = cpu_baseline(x, w, cfg_kw, N, d, w.probe_rows)
         log(f"oracle: {cpu['value']:.4f} TFLOP/s on {cpu['cores']} threads ({cpu['seconds']} s)")
 
     res = {
