@@ -768,16 +768,18 @@ __global__ __launch_bounds__(256) void k_probe_attn_vec(ProbeArgs a) {
 }
 
 // Probe rows on the matrix cores (bf16 Q/K, fp16-scaled V).  One workgroup
-// of two waves takes 64 probe rows against one chunk of kProbeChunk keys;
-// wave w owns probes 32w..32w+31, one per lane column, and keeps two online
-// softmaxes: dense over every key, and sparse over the keys whose K/V group
-// is granted to the probe's query group.  Both products share each V
-// fragment.  Partials (unnormalised o, reference max in log2 units, sum) are
-// combined across chunks by k_probe_merge.
+// of four waves takes 64 probe rows against one chunk of kProbeChunk keys.
+// Waves 0 and 1 keep the dense online softmax (every key) of probes 0..31
+// and 32..63, one per lane column; waves 2 and 3 keep the sparse one (the
+// keys whose K/V group is granted to the probe's query group) of the same
+// probes.  All four read the same K/V stages; each wave holds one
+// accumulator set, so the kernel fits two waves per SIMD (holding both sets
+// in one wave did not).  Partials (unnormalised o, reference max in log2
+// units, sum) are combined across chunks by k_probe_merge.
 template <int D>
-__global__ __launch_bounds__(128, 2) void k_probe_attn_mfma(ProbeArgs a) {
+__global__ __launch_bounds__(256, 2) void k_probe_attn_mfma(ProbeArgs a) {
   constexpr int KS = D / 16, DB = D / 32;
-  constexpr int CPR = D / 8, RPI = 64 / CPR, IPW = 64 / RPI / 2;
+  constexpr int CPR = D / 8, RPI = 64 / CPR, IPW = 64 / RPI / 4;
   constexpr int VOFF = 64 * D * 2;
   constexpr int MW = kMaxGroups / 32;
   __shared__ __attribute__((aligned(1024))) bf16_t KV0[2 * 64 * D];
@@ -786,17 +788,18 @@ __global__ __launch_bounds__(128, 2) void k_probe_attn_mfma(ProbeArgs a) {
   __shared__ uint32_t msk[64 * MW];
   const int bh = blockIdx.z, pb = blockIdx.y, ch = blockIdx.x, tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63, half = lane >> 5, col = lane & 31;
+  const bool sparse_role = w >= 2;
   const int k0 = ch * kProbeChunk, k1 = min(a.N, k0 + kProbeChunk);
   const int L = k1 - k0;
   if (L <= 0) return;
   // grant masks of the probes' query groups
-  for (int e = tid; e < 64 * a.gwords; e += 128) {
+  for (int e = tid; e < 64 * a.gwords; e += 256) {
     const int r = e / a.gwords, wd = e - r * a.gwords;
     const int pp = pb * 64 + r;
     msk[r * MW + wd] =
         pp < a.M ? a.gmask[((long long)bh * a.GQ + a.pgroup[(long long)bh * a.M + pp]) * a.gwords + wd] : 0u;
   }
-  const int pl = 32 * w + col;
+  const int pl = 32 * (w & 1) + col;
   const int p = pb * 64 + pl;
   const bool valid = p < a.M;
   const bf16_t* qb = static_cast<const bf16_t*>(a.qv.p);
@@ -811,19 +814,12 @@ __global__ __launch_bounds__(128, 2) void k_probe_attn_mfma(ProbeArgs a) {
     if (valid) u = *reinterpret_cast<const uint4*>(qb + a.qv.row_off(bh, ptok) + 16 * ks + 8 * half);
     qf[ks] = __builtin_bit_cast(bf16x8, u);
   }
-  f32x16 od[DB], os[DB];
-#pragma unroll
-  for (int b = 0; b < DB; ++b) {
-    od[b] = f32x16{};
-    os[b] = f32x16{};
-  }
-  float md = -INFINITY, ld = 0.f, ms = -INFINITY, ls = 0.f;
   const float c = a.scale * 1.4426950408889634f;
   const int* kgrp = a.kgroup + (long long)bh * a.N;
 
   typedef __attribute__((address_space(3))) char lds_char;
   // the keys of a chunk are consecutive rows of the permuted K/V
-  auto issue = [&](lds_char* __restrict__ dst, int tt) {
+  auto issue = [&](lds_char* __restrict__ dst, int tt) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < IPW; ++i) {
       const int rb = (w * IPW + i) * RPI;
@@ -841,160 +837,145 @@ __global__ __launch_bounds__(128, 2) void k_probe_attn_mfma(ProbeArgs a) {
                           16 * (2 * (gi & 1) + (qq >> 1)) + 8 * (qq & 1);
   typedef _Float16 h2 __attribute__((ext_vector_type(2)));
   const h2 one2 = {(_Float16)1.f, (_Float16)1.f};
-
-  auto compute = [&](const lds_char* __restrict__ lds, const int* __restrict__ kgt,
-                     const uint32_t* __restrict__ mrow, int kt0) {
-    uint32_t kb0 = kbase0, vb0 = vbase0;
-    asm volatile("" : "+v"(kb0), "+v"(vb0));
-    f32x16 sacc[2];
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt) sacc[kt] = f32x16{};
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const uint32_t ka = kb0 ^ (32u * ks);
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        const bf16x8 kf = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(lds + ka + kt * 32 * 2 * D);
-        sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], sacc[kt], 0, 0, 0);
-      }
-    }
-    // which of this lane's 32 keys are granted to its probe's query group
-    uint32_t amask = 0;
-    const int h0 = kgt[0];
-    if (h0 == kgt[63]) {
-      amask = ((mrow[h0 >> 5] >> (h0 & 31)) & 1u) ? 0xffffffffu : 0u;
-    } else {
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int h = kgt[32 * kt + (r & 3) + 8 * (r >> 2) + 4 * half];
-          amask |= ((mrow[h >> 5] >> (h & 31)) & 1u) << (16 * kt + r);
-        }
-    }
-    float mld = -INFINITY, mls = -INFINITY;
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = 32 * kt + (r & 3) + 8 * (r >> 2) + 4 * half;
-        float sv = sacc[kt][r];
-        if (kt0 + key >= L) sv = -INFINITY;
-        sacc[kt][r] = sv;
-        mld = fmaxf(mld, sv);
-        if ((amask >> (16 * kt + r)) & 1u) mls = fmaxf(mls, sv);
-      }
-    mld = fmaxf(mld, __shfl_xor(mld, 32, 64)) * c;
-    mls = fmaxf(mls, __shfl_xor(mls, 32, 64)) * c;
-    // lazy rescaling of either reference max (p <= 2^8 stays exact in fp16)
-    if (__builtin_amdgcn_ballot_w64(mld > md + 8.f)) {
-      const float mn = fmaxf(md, mld);
-      const float al = md == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(md - mn);
-      ld *= al;
-#pragma unroll
-      for (int b = 0; b < DB; ++b) od[b] *= al;
-      md = mn;
-    }
-    if (__builtin_amdgcn_ballot_w64(mls > ms + 8.f)) {
-      const float mn = fmaxf(ms, mls);
-      const float al = ms == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ms - mn);
-      ls *= al;
-#pragma unroll
-      for (int b = 0; b < DB; ++b) os[b] *= al;
-      ms = mn;
-    }
-    const float mbd = md == -INFINITY ? 0.f : md;
-    const float mbs = ms == -INFINITY ? 0.f : ms;
-    uint32_t va[DB];
-#pragma unroll
-    for (int b = 0; b < DB; ++b) va[b] = vb0 ^ (64u * b);
-#pragma unroll
-    for (int sp = 0; sp < 4; ++sp) {
-      const int kt = sp >> 1, rb = 8 * (sp & 1);
-      uint32_t pwd[4], pws[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int r0 = rb + 2 * j, r1 = r0 + 1;
-        const float s0 = sacc[kt][r0], s1 = sacc[kt][r1];
-        const float d0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s0, c, -mbd));
-        const float d1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s1, c, -mbd));
-        // ungranted keys get exponent -inf, i.e. probability 0
-        const float x0 = ((amask >> (16 * kt + r0)) & 1u) ? __builtin_fmaf(s0, c, -mbs) : -INFINITY;
-        const float x1 = ((amask >> (16 * kt + r1)) & 1u) ? __builtin_fmaf(s1, c, -mbs) : -INFINITY;
-        const float e0 = __builtin_amdgcn_exp2f(x0);
-        const float e1 = __builtin_amdgcn_exp2f(x1);
-        const h2 hd = {(_Float16)d0, (_Float16)d1};
-        const h2 hs = {(_Float16)e0, (_Float16)e1};
-        pwd[j] = __builtin_bit_cast(uint32_t, hd);
-        pws[j] = __builtin_bit_cast(uint32_t, hs);
-        ld = __builtin_amdgcn_fdot2(hd, one2, ld, false);
-        ls = __builtin_amdgcn_fdot2(hs, one2, ls, false);
-      }
-      const f16x8 pkd = __builtin_bit_cast(f16x8, make_uint4(pwd[0], pwd[1], pwd[2], pwd[3]));
-      const f16x8 pks = __builtin_bit_cast(f16x8, make_uint4(pws[0], pws[1], pws[2], pws[3]));
-#pragma unroll
-      for (int b = 0; b < DB; ++b) {
-        const v4i16 t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            reinterpret_cast<__attribute__((address_space(3))) v4i16*>(const_cast<lds_char*>(lds) + va[b] + sp * 32 * D));
-        const v4i16 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            reinterpret_cast<__attribute__((address_space(3))) v4i16*>(const_cast<lds_char*>(lds) + va[b] + sp * 32 * D + 16 * D));
-        const uint2 u0 = __builtin_bit_cast(uint2, t0), u1 = __builtin_bit_cast(uint2, t1);
-        const f16x8 vv = __builtin_bit_cast(f16x8, make_uint4(u0.x, u0.y, u1.x, u1.y));
-        od[b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vv, pkd, od[b], 0, 0, 0);
-        os[b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vv, pks, os[b], 0, 0, 0);
-      }
-    }
-  };
-
   lds_char* const s0 = (lds_char*)KV0;
   lds_char* const s1 = (lds_char*)KV1;
   const int ntile = (L + 63) / 64;
   const uint32_t* mrow = msk + pl * MW;
-  // one pipeline step: DMA of tile t+1 and its group ids, compute tile t
   // the tile's 64 group ids travel by LDS-DMA too (wave 0, 4 bytes a lane)
-  auto issue_groups = [&](int* kgn, int tt) {
+  auto issue_groups = [&](int* kgn, int tt) __attribute__((always_inline)) {
     if (w == 0)
       __builtin_amdgcn_global_load_lds(SP_GLB(kgrp + k0 + min(64 * tt + lane, L - 1)), SP_LDS(kgn), 4, 0, 0);
   };
-  auto step = [&](lds_char* cur, lds_char* nxt, const int* kgc, int* kgn, int t) {
-    if (t + 1 < ntile) {
-      issue(nxt, t + 1);
-      issue_groups(kgn, t + 1);
-    }
-    compute(cur, kgc, mrow, 64 * t);
+  float* const base = a.ppart + (((long long)bh * a.n_pchunk + ch) * 2) * a.M * (D + 2);
+
+  // the whole chunk for one role: SPARSE masks the ungranted keys
+  auto run = [&](auto sparse_tag) __attribute__((always_inline)) {
+    constexpr bool SPARSE = decltype(sparse_tag)::value;
+    f32x16 o[DB];
+#pragma unroll
+    for (int b = 0; b < DB; ++b) o[b] = f32x16{};
+    float m = -INFINITY, l = 0.f;
+    auto compute = [&](const lds_char* __restrict__ lds, const int* __restrict__ kgt, int kt0)
+                       __attribute__((always_inline)) {
+      uint32_t kb0 = kbase0, vb0 = vbase0;
+      asm volatile("" : "+v"(kb0), "+v"(vb0));
+      f32x16 sacc[2];
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) sacc[kt] = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const uint32_t ka = kb0 ^ (32u * ks);
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+          const bf16x8 kf = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(lds + ka + kt * 32 * 2 * D);
+          sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], sacc[kt], 0, 0, 0);
+        }
+      }
+      // which of this lane's 32 keys count: all (dense), or those granted to
+      // the probe's query group (sparse)
+      uint32_t amask = 0xffffffffu;
+      if constexpr (SPARSE) {
+        amask = 0;
+        const int h0 = kgt[0];
+        if (h0 == kgt[63]) {
+          amask = ((mrow[h0 >> 5] >> (h0 & 31)) & 1u) ? 0xffffffffu : 0u;
+        } else {
+#pragma unroll
+          for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int h = kgt[32 * kt + (r & 3) + 8 * (r >> 2) + 4 * half];
+              amask |= ((mrow[h >> 5] >> (h & 31)) & 1u) << (16 * kt + r);
+            }
+        }
+      }
+      float mloc = -INFINITY;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = 32 * kt + (r & 3) + 8 * (r >> 2) + 4 * half;
+          float sv = sacc[kt][r];
+          if (kt0 + key >= L || !((amask >> (16 * kt + r)) & 1u)) sv = -INFINITY;
+          sacc[kt][r] = sv;
+          mloc = fmaxf(mloc, sv);
+        }
+      mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64)) * c;
+      // lazy rescaling of the reference max (p <= 2^8 stays exact in fp16)
+      if (__builtin_amdgcn_ballot_w64(mloc > m + 8.f)) {
+        const float mn = fmaxf(m, mloc);
+        const float al = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - mn);
+        l *= al;
+#pragma unroll
+        for (int b = 0; b < DB; ++b) o[b] *= al;
+        m = mn;
+      }
+      const float mb = m == -INFINITY ? 0.f : m;
+      uint32_t va[DB];
+#pragma unroll
+      for (int b = 0; b < DB; ++b) va[b] = vb0 ^ (64u * b);
+#pragma unroll
+      for (int sp = 0; sp < 4; ++sp) {
+        const int kt = sp >> 1, rb = 8 * (sp & 1);
+        uint32_t pw[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          // excluded keys carry score -inf, i.e. probability 0
+          const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kt][rb + 2 * j], c, -mb));
+          const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kt][rb + 2 * j + 1], c, -mb));
+          const h2 hv = {(_Float16)e0, (_Float16)e1};
+          pw[j] = __builtin_bit_cast(uint32_t, hv);
+          l = __builtin_amdgcn_fdot2(hv, one2, l, false);
+        }
+        const f16x8 pk = __builtin_bit_cast(f16x8, make_uint4(pw[0], pw[1], pw[2], pw[3]));
+#pragma unroll
+        for (int b = 0; b < DB; ++b) {
+          const v4i16 t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              reinterpret_cast<__attribute__((address_space(3))) v4i16*>(const_cast<lds_char*>(lds) + va[b] + sp * 32 * D));
+          const v4i16 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<__attribute__((address_space(3))) v4i16*>(
+              const_cast<lds_char*>(lds) + va[b] + sp * 32 * D + 16 * D));
+          const uint2 u0 = __builtin_bit_cast(uint2, t0), u1 = __builtin_bit_cast(uint2, t1);
+          const f16x8 vv = __builtin_bit_cast(f16x8, make_uint4(u0.x, u0.y, u1.x, u1.y));
+          o[b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vv, pk, o[b], 0, 0, 0);
+        }
+      }
+    };
+    // one pipeline step: DMA of tile t+1 and its group ids, compute tile t
+    auto step = [&](lds_char* cur, lds_char* nxt, const int* kgc, int* kgn, int t) __attribute__((always_inline)) {
+      if (t + 1 < ntile) {
+        issue(nxt, t + 1);
+        issue_groups(kgn, t + 1);
+      }
+      compute(cur, kgc, 64 * t);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+    };
+    issue_groups(kg0, 0);
+    issue(s0, 0);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-  };
-  issue_groups(kg0, 0);
-  issue(s0, 0);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-  for (int t = 0; t < ntile; t += 2) {
-    step(s0, s1, kg0, kg1, t);
-    if (t + 1 < ntile) step(s1, s0, kg1, kg0, t + 1);
-  }
-
-  ld += __shfl_xor(ld, 32, 64);
-  ls += __shfl_xor(ls, 32, 64);
-  if (!valid) return;
-  const float vs = ldexpf(1.0f, a.vexp[bh]);
-  float* base = a.ppart + (((long long)bh * a.n_pchunk + ch) * 2) * a.M * (D + 2);
-  float* pd = base + (long long)p * (D + 2);
-  float* ps = base + ((long long)a.M + p) * (D + 2);
-#pragma unroll
-  for (int b = 0; b < DB; ++b)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int dim = 32 * b + (r & 3) + 8 * (r >> 2) + 4 * half;
-      pd[dim] = od[b][r] * vs;
-      ps[dim] = os[b][r] * vs;
+    for (int t = 0; t < ntile; t += 2) {
+      step(s0, s1, kg0, kg1, t);
+      if (t + 1 < ntile) step(s1, s0, kg1, kg0, t + 1);
     }
-  if (half == 0) {
-    pd[D] = md;
-    pd[D + 1] = ld;
-    ps[D] = ms;
-    ps[D + 1] = ls;
-  }
+    l += __shfl_xor(l, 32, 64);
+    if (!valid) return;
+    const float vs = ldexpf(1.0f, a.vexp[bh]);
+    float* po = base + ((SPARSE ? (long long)a.M : 0LL) + p) * (D + 2);
+#pragma unroll
+    for (int b = 0; b < DB; ++b)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int dim = 32 * b + (r & 3) + 8 * (r >> 2) + 4 * half;
+        po[dim] = o[b][r] * vs;
+      }
+    if (half == 0) {
+      po[D] = m;
+      po[D + 1] = l;
+    }
+  };
+  if (sparse_role) run(std::true_type{});
+  else run(std::false_type{});
 }
 
 template <int D>
@@ -1146,8 +1127,8 @@ hipError_t launch_probe_attention(const Plan& p, hipStream_t s) {
   dim3 g(p.n_pchunk, (p.M + 63) / 64, p.BH);
   if (p.dtype == SPARSEPR_BF16) {
     a.vexp = p.vexp;
-    if (p.d == 128) hipLaunchKernelGGL((k_probe_attn_mfma<128>), g, dim3(128), 0, s, a);
-    else hipLaunchKernelGGL((k_probe_attn_mfma<64>), g, dim3(128), 0, s, a);
+    if (p.d == 128) hipLaunchKernelGGL((k_probe_attn_mfma<128>), g, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((k_probe_attn_mfma<64>), g, dim3(256), 0, s, a);
   } else {
     a.vexp = nullptr;
     if (p.d == 128) hipLaunchKernelGGL((k_probe_attn_vec<float, float, 128>), g, dim3(256), 0, s, a);
