@@ -33,6 +33,7 @@ from .sparsepr_oracle import (  # noqa: F401
     kmeans,
     query_coordinates,
     route,
+    route_alpha,
     sample_queries,
     select_probes,
     sparse_attention,

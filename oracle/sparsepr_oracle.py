@@ -66,6 +66,8 @@ class OracleConfig:
     seed: int = 0
     partition_mode: str = "response_coupled"   # or "independent"
     rank_cut: float = 1e-6
+    router: str = "budget"         # "budget" (pair budget from density) or "alpha" (per-group coverage)
+    alpha: float = 0.9             # target retained mass of the "alpha" router
 
 
 def softmax_scale(cfg: OracleConfig, d: int) -> float:
@@ -228,29 +230,18 @@ def query_coordinates(q: np.ndarray, cbar_nonempty: np.ndarray, s: float) -> np.
 # ----------------------------------------------------------------------------
 # a10: router
 # ----------------------------------------------------------------------------
-def route(qbar: np.ndarray, nq: np.ndarray, cbar: np.ndarray, nk: np.ndarray,
-          s: float, density: float, n: int, m: int) -> dict:
-    """Grant (query-group, key-group) cells under the pair budget.
+def _cell_estimates(qbar: np.ndarray, nq: np.ndarray, cbar: np.ndarray, nk: np.ndarray, s: float):
+    """Per-cell estimates shared by both routers (U7).
 
-    The budget is spent in true pairs, the product of the two groups' token
-    counts, not in cells ([NE] NE/exec).  U7: the estimated log-probability of
-    one key of group h for a query of group g is
-        key_gh = mu_gh - log sum_h' n_h' exp(mu_gh'),  mu_gh = s qbar_g . cbar_h,
-    every non-empty g first gets its best cell argmax_h mu_gh, then the other
-    cells are taken in order (key desc, g asc, h asc) as the longest prefix
-    that fits.  mu is a sequential fp64 dot product without fused multiply-add.
+    mu_gh = s qbar_g . cbar_h (a sequential fp64 dot product without fused
+    multiply-add); key_gh = mu_gh - log sum_h' n_h' exp(mu_gh') is the
+    estimated log-probability of one key of group h for a query of group g;
+    the mandatory cell of g is its first argmax_h mu_gh.
     """
     gq, gk = len(nq), len(nk)
     d = qbar.shape[1]
     valid_q = nq > 0
     valid_k = nk > 0
-    cost = np.outer(nq, nk).astype(np.int64)
-    result = {"mu": None, "key": None, "mandatory": np.full(gq, -1, dtype=np.int64)}
-    if float(np.float32(density)) >= 1.0:
-        granted = valid_q[:, None] & valid_k[None, :]
-        result.update(granted=granted, budget=n * n, mandatory_cost=0)
-        return _route_stats(result, cost, n, m)
-
     qz = np.where(valid_q[:, None], qbar, 0.0)
     cz = np.where(valid_k[:, None], cbar, 0.0)
     acc = np.zeros((gq, gk))
@@ -278,11 +269,33 @@ def route(qbar: np.ndarray, nq: np.ndarray, cbar: np.ndarray, nk: np.ndarray,
             tot = tot + float(nk[h]) * math.exp(row[h] - mx)
         ell = mx + math.log(tot)
         key[g, hs] = row[hs] - ell
+    return mu, key, mandatory
 
+
+def route(qbar: np.ndarray, nq: np.ndarray, cbar: np.ndarray, nk: np.ndarray,
+          s: float, density: float, n: int, m: int) -> dict:
+    """Grant (query-group, key-group) cells under the pair budget.
+
+    The budget is spent in true pairs, the product of the two groups' token
+    counts, not in cells ([NE] NE/exec).  U7: with the cell estimates of
+    _cell_estimates, every non-empty g first gets its best cell
+    argmax_h mu_gh, then the other cells are taken in order
+    (key desc, g asc, h asc) as the longest prefix that fits.
+    """
+    valid_q = nq > 0
+    valid_k = nk > 0
+    cost = np.outer(nq, nk).astype(np.int64)
+    result = {"mu": None, "key": None, "mandatory": np.full(len(nq), -1, dtype=np.int64)}
+    if float(np.float32(density)) >= 1.0:
+        granted = valid_q[:, None] & valid_k[None, :]
+        result.update(granted=granted, budget=n * n, mandatory_cost=0)
+        return _route_stats(result, cost, n, m)
+
+    mu, key, mandatory = _cell_estimates(qbar, nq, cbar, nk, s)
     budget = budget_pairs(density, n, m)
-    granted = np.zeros((gq, gk), dtype=bool)
+    granted = np.zeros((len(nq), len(nk)), dtype=bool)
     mand_cost = 0
-    for g in range(gq):
+    for g in range(len(nq)):
         if mandatory[g] >= 0:
             granted[g, mandatory[g]] = True
             mand_cost += int(cost[g, mandatory[g]])
@@ -295,6 +308,49 @@ def route(qbar: np.ndarray, nq: np.ndarray, cbar: np.ndarray, nk: np.ndarray,
     result.update(mu=mu, key=key, mandatory=mandatory, granted=granted, budget=budget,
                   mandatory_cost=mand_cost, order_g=cand_g[order], order_h=cand_h[order],
                   n_prefix=take)
+    return _route_stats(result, cost, n, m)
+
+
+def route_alpha(qbar: np.ndarray, nq: np.ndarray, cbar: np.ndarray, nk: np.ndarray,
+                s: float, alpha: float, n: int, m: int) -> dict:
+    """Target-retained-mass router: per query group, cover alpha of its mass.
+
+    The pages picture, for a target retained mass alpha, the key groups a
+    query group must cover jointly ([NE] NE/method, Figure 2).  Reading: the
+    estimated share of g's attention that falls on key group h is
+    mass_gh = n_h exp(key_gh) (these sum to one over h); every non-empty g
+    keeps its mandatory best cell (as in `route`), then takes the other
+    non-empty key groups in order (mass desc, h asc) while the retained mass,
+    summed one cell after another in that order starting from the best
+    cell's, is below alpha.  There is no pair budget.
+    """
+    valid_q = nq > 0
+    valid_k = nk > 0
+    cost = np.outer(nq, nk).astype(np.int64)
+    mu, key, mandatory = _cell_estimates(qbar, nq, cbar, nk, s)
+    # n_h exp(key_gh), one scalar exp each, as the normaliser above uses
+    mass = np.zeros((len(nq), len(nk)))
+    for g in np.nonzero(mandatory >= 0)[0]:
+        for h in np.nonzero(valid_k)[0]:
+            mass[g, h] = float(nk[h]) * math.exp(key[g, h])
+    a = float(np.float32(alpha))
+    granted = np.zeros((len(nq), len(nk)), dtype=bool)
+    for g in range(len(nq)):
+        if mandatory[g] < 0:
+            continue
+        b = int(mandatory[g])
+        granted[g, b] = True
+        kept = float(mass[g, b])
+        hs = [h for h in np.nonzero(valid_k)[0] if h != b]
+        hs.sort(key=lambda h: (-mass[g, h], h))
+        for h in hs:
+            if kept >= a:
+                break
+            granted[g, h] = True
+            kept = kept + float(mass[g, h])
+    result = {"mu": mu, "key": key, "mandatory": mandatory, "mass": mass, "granted": granted,
+              "budget": n * n, "mandatory_cost": int(sum(cost[g, mandatory[g]] for g in range(len(nq))
+                                                          if mandatory[g] >= 0))}
     return _route_stats(result, cost, n, m)
 
 
@@ -490,7 +546,10 @@ def sparsepr_head(q: np.ndarray, k: np.ndarray, v: np.ndarray, cfg: OracleConfig
     cbar = group_means(k64, perm_k, off_k)
     qbar = group_means(q64, perm_q, off_q)
     m = min(cfg.probe_rows, n)
-    rt = route(qbar, nq, cbar, nk, s, cfg.density, n, m)
+    if cfg.router == "alpha":
+        rt = route_alpha(qbar, nq, cbar, nk, s, cfg.alpha, n, m)
+    else:
+        rt = route(qbar, nq, cbar, nk, s, cfg.density, n, m)
 
     qp, kp, vp = q64[perm_q], k64[perm_k], v64[perm_k]
     o_sp = sparse_attention(qp, kp, vp, rt["granted"], off_q, off_k, s)

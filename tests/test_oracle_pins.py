@@ -26,6 +26,7 @@ from oracle import (
     kmeans,
     query_coordinates,
     route,
+    route_alpha,
     sample_queries,
     select_probes,
     sparse_attention,
@@ -247,6 +248,76 @@ def test_router_prefix_budget_and_mandatory_cells():
                 cand = [(-rt["key"][a, b], a, b) for a, b in zip(*np.nonzero(opt_n))]
                 _, a, b = min(cand)
                 assert total + cost[a, b] > rt["budget"]
+
+
+def test_alpha_router_is_a_minimum_cover_found_by_brute_force():
+    """For every query group, no smaller set of key groups that keeps the
+    mandatory best cell retains at least alpha of the estimated mass; the
+    granted set retains at least alpha (or takes every key group)."""
+    import itertools
+
+    for seed in range(5):
+        qbar, nq, cbar, nk, n = _route_case(seed, gq=5, gk=6)
+        s = 0.8
+        for alpha in (0.3, 0.6, 0.85, 0.97):
+            rt = route_alpha(qbar, nq, cbar, nk, s, alpha, n, 0)
+            g_ = rt["granted"]
+            assert not g_[nq == 0].any() and not g_[:, nk == 0].any()
+            ok = np.nonzero(nk > 0)[0]
+            for g in np.nonzero(nq > 0)[0]:
+                # estimated shares written out from the logits directly
+                logit = np.array([s * sum(qbar[g, t] * cbar[h, t] for t in range(qbar.shape[1])) for h in ok])
+                w = nk[ok] * np.exp(logit - logit.max())
+                share = dict(zip(ok, w / w.sum()))
+                best = int(ok[np.argmax(logit)])
+                assert g_[g, best]
+                got = [int(h) for h in np.nonzero(g_[g])[0]]
+                kept = sum(share[h] for h in got)
+                a = float(np.float32(alpha))
+                assert kept >= a - 1e-12 or len(got) == len(ok)
+                others = [int(h) for h in ok if h != best]
+                smallest = len(ok)
+                for r in range(len(others) + 1):
+                    if any(share[best] + sum(share[h] for h in c) >= a + 1e-12 for c in itertools.combinations(others, r)):
+                        smallest = r + 1
+                        break
+                assert len(got) <= smallest
+
+
+def test_alpha_router_mass_rows_nesting_and_limits():
+    qbar, nq, cbar, nk, n = _route_case(4, gq=8, gk=8)
+    ok_q, ok_k = nq > 0, nk > 0
+    rt = route_alpha(qbar, nq, cbar, nk, 0.6, 0.5, n, 0)
+    # the estimated shares of every non-empty query group sum to one
+    assert np.allclose(rt["mass"][ok_q].sum(axis=1), 1.0, rtol=0, atol=1e-12)
+    prev = None
+    for alpha in np.linspace(0.05, 0.99, 20):
+        g_ = route_alpha(qbar, nq, cbar, nk, 0.6, alpha, n, 0)["granted"]
+        if prev is not None:
+            assert (g_ | ~prev).all()  # granted at a smaller alpha stays granted
+        prev = g_
+    # a vanishing target keeps only the best cells, a full one takes everything
+    tiny = route_alpha(qbar, nq, cbar, nk, 0.6, 1e-9, n, 0)
+    assert tiny["granted"].sum() == ok_q.sum()
+    assert all(tiny["granted"][g, tiny["mandatory"][g]] for g in np.nonzero(ok_q)[0])
+    full = route_alpha(qbar, nq, cbar, nk, 0.6, 1.0, n, 0)["granted"]
+    assert (full == (ok_q[:, None] & ok_k[None, :])).all()
+
+
+def test_alpha_router_runs_through_the_full_call():
+    """The per-head call with the alpha router: the routed cells cover alpha
+    of every query group's estimated mass, and the corrected output is
+    closer to dense attention than the uncorrected sparse output."""
+    x = make_video_qkv(2, 8, 16, 1, 32, "fp32", 5, [0.08])
+    q, k, v = (x[t][0, 0].double().numpy() for t in ("q", "k", "v"))
+    cfg = OracleConfig(probe_rows=16, n_kv_groups=8, n_q_groups=8, residual_rank=4, router="alpha", alpha=0.8)
+    r = sparsepr_head(q, k, v, cfg, bh=0)
+    rt = r["route"]
+    kept = (rt["mass"] * rt["granted"]).sum(axis=1)
+    assert (kept[rt["mandatory"] >= 0] >= np.float32(0.8) - 1e-12).all()
+    dense = dense_attention(q, k, v, r["scale"])
+    err = lambda o: np.linalg.norm(o - dense) / np.linalg.norm(dense)
+    assert err(r["out"]) < err(r["hard_drop"])
 
 
 def test_router_is_nested_in_density_and_full_at_one():
