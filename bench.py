@@ -39,6 +39,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="c3_dit_32k")
     ap.add_argument("--density", type=float, default=None)
+    ap.add_argument("--router", choices=("budget", "alpha"), default="budget",
+                    help="cell selection: pair budget from the density, or per-group target retained mass")
+    ap.add_argument("--alpha", type=float, default=0.9, help="target retained mass of --router alpha")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--profile-runs", type=int, default=3, help="calls timed per stage (at least 1)")
@@ -127,7 +130,7 @@ def main() -> int:
     q, k, v = (x[t].cuda() for t in ("q", "k", "v"))
     B, H, N, d = q.shape
     cfg_kw = dict(density=w.density, probe_rows=w.probe_rows, n_kv_groups=w.n_kv_groups,
-                  n_q_groups=w.n_q_groups, residual_rank=w.residual_rank)
+                  n_q_groups=w.n_q_groups, residual_rank=w.residual_rank, router=args.router, alpha=args.alpha)
     cfg = sp.make_config(N, d, **cfg_kw)
     ws = sp.Workspace()
     out = torch.empty_like(q)
@@ -216,7 +219,8 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": w.name, "B": B, "H": H, "N": N, "d": d, "density": w.density,
                    "n_kv_groups": w.n_kv_groups, "n_q_groups": w.n_q_groups, "probe_rows": w.probe_rows,
-                   "residual_rank": w.residual_rank, "kmeans_iters": cfg.kmeans_iters, "parallelism": "none"},
+                   "residual_rank": w.residual_rank, "kmeans_iters": cfg.kmeans_iters, "router": args.router,
+                   **({"alpha": args.alpha} if args.router == "alpha" else {}), "parallelism": "none"},
         "roofline": {"bound": "mfma", "achieved": round(kernel_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(kernel_tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
                      "kernel": "k_sparse_attn_mfma (block-sparse attention, fused correction)",

@@ -14,6 +14,8 @@ from typing import Optional
 from ._lib import (  # noqa: F401
     PART_INDEPENDENT,
     PART_RESPONSE_COUPLED,
+    ROUTER_ALPHA,
+    ROUTER_BUDGET,
     SPARSEPR_BF16,
     SPARSEPR_FP32,
     SparsePRError,
@@ -51,6 +53,8 @@ def make_config(n: int, d: int, **kw) -> SparseprConfig:
             v = {"response_coupled": PART_RESPONSE_COUPLED, "independent": PART_INDEPENDENT}[v]
         if k == "ridge_mode" and isinstance(v, str):
             v = {"relative": 0, "absolute": 1}[v]
+        if k == "router" and isinstance(v, str):
+            v = {"budget": ROUTER_BUDGET, "alpha": ROUTER_ALPHA}[v]
         if not hasattr(cfg, k):
             raise KeyError(k)
         setattr(cfg, k, v)

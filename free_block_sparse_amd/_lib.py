@@ -19,6 +19,8 @@ PART_RESPONSE_COUPLED = 0
 PART_INDEPENDENT = 1
 RIDGE_RELATIVE = 0
 RIDGE_ABSOLUTE = 1
+ROUTER_BUDGET = 0
+ROUTER_ALPHA = 1
 
 
 class SparseprConfig(ctypes.Structure):
@@ -37,6 +39,8 @@ class SparseprConfig(ctypes.Structure):
         ("partition_mode", ctypes.c_int),
         ("ridge_mode", ctypes.c_int),
         ("seed", ctypes.c_ulonglong),
+        ("router", ctypes.c_int),
+        ("alpha", ctypes.c_float),
     ]
 
     def as_dict(self):

@@ -11,7 +11,7 @@
 //   [NE] section "SparsePR：先把误差聚拢，再用少量“抽查”去纠正": probes are picked evenly
 //        from every query group (query-group-stratified), 64 rows per head.
 //
-// Rule (a reading; the pages give no formula): mu_gh = s qbar_g . cbar_h is the
+// Budget rule (a reading; the pages give no formula): mu_gh = s qbar_g . cbar_h is the
 // logit of the mean query of group g against the mean key of group h;
 // key_gh = mu_gh - log sum_h' n_h' exp(mu_gh') estimates the attention
 // probability of one key of h for a query of g.  Every non-empty query group
@@ -32,8 +32,10 @@ struct RouteArgs {
   double s;
   long long budget;
   int dense_route;
+  double alpha;     // target retained mass (alpha router)
   double* mu;
   uint64_t* ckey;
+  double* rmass;    // [BH, GQ, GK] estimated mass shares n_h exp(key_gh) (alpha router), else null
   int* mand;
   long long* thr;
   int* csr_ptr;
@@ -97,7 +99,10 @@ __global__ __launch_bounds__(256) void k_route_keys(RouteArgs a) {
   const long long row = ((long long)bh * a.GQ + g) * GK;
   const int nq = offq[g + 1] - offq[g];
   if (nq <= 0) {
-    for (int h = lane; h < GK; h += 64) a.ckey[row + h] = kExcluded;
+    for (int h = lane; h < GK; h += 64) {
+      a.ckey[row + h] = kExcluded;
+      if (a.rmass) a.rmass[row + h] = 0.0;
+    }
     if (lane == 0) a.mand[(long long)bh * a.GQ + g] = -1;
     return;
   }
@@ -143,12 +148,82 @@ __global__ __launch_bounds__(256) void k_route_keys(RouteArgs a) {
   ell = __shfl(ell, 0, 64);
   for (int h = lane; h < GK; h += 64) {
     uint64_t ck = kExcluded;
-    if (offk[h + 1] > offk[h] && h != best) {
+    double ms = 0.0;
+    if (offk[h + 1] > offk[h]) {
       double key = finite ? __dsub_rn(a.mu[row + h], ell) : -INFINITY;
       if (key != key) key = -INFINITY;
-      ck = ~ord_f64(key);
+      if (h != best) ck = ~ord_f64(key);
+      if (a.rmass) ms = __dmul_rn((double)(offk[h + 1] - offk[h]), exp(key));
     }
     a.ckey[row + h] = ck;
+    if (a.rmass) a.rmass[row + h] = ms;
+  }
+}
+
+// ---------------------------------------------------------------- alpha
+// Alpha router (in place of the budget selection): query group g keeps its
+// best cell, then takes the other non-empty key groups in order (mass desc,
+// h asc) while the retained mass -- summed one cell after another in that
+// order from the best cell's -- is below alpha.  The granted cells get
+// composite key 0 and the threshold "key below 1", so k_route_emit grants
+// exactly them (and the best cells, as always).  One workgroup per group:
+// a bitonic sort in LDS, then one thread adds up the prefix.
+__global__ __launch_bounds__(256) void k_route_alpha(RouteArgs a) {
+  __shared__ double sm[kMaxGroups];
+  __shared__ int shh[kMaxGroups];
+  const int bh = blockIdx.y, g = blockIdx.x, tid = threadIdx.x;
+  const int GK = a.GK;
+  const int* offk = a.off_k + (long long)bh * (a.GK + 1);
+  const long long row = ((long long)bh * a.GQ + g) * GK;
+  if (g == 0 && tid == 0) {
+    long long* thr = a.thr + (long long)bh * 4;
+    thr[0] = 1;
+    thr[1] = 0;
+    thr[2] = 64;
+    thr[3] = 2;
+  }
+  const int best = a.mand[(long long)bh * a.GQ + g];
+  int P2 = 1;
+  while (P2 < GK) P2 <<= 1;
+  // candidates (masses are >= 0; padding -1 sorts last)
+  for (int h = tid; h < P2; h += 256) {
+    double m = -1.0;
+    int hh = 0x7fffffff;
+    if (h < GK && best >= 0 && h != best && offk[h + 1] > offk[h]) {
+      m = a.rmass[row + h];
+      hh = h;
+    }
+    sm[h] = m;
+    shh[h] = hh;
+    if (h < GK) a.ckey[row + h] = kExcluded;
+  }
+  __syncthreads();
+  for (int k = 2; k <= P2; k <<= 1)
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      for (int i = tid; i < P2; i += 256) {
+        const int l = i ^ j;
+        if (l > i) {
+          const double mi = sm[i], ml = sm[l];
+          const int hi = shh[i], hl = shh[l];
+          const bool l_first = ml > mi || (ml == mi && hl < hi);
+          if (l_first == ((i & k) == 0)) {
+            sm[i] = ml;
+            sm[l] = mi;
+            shh[i] = hl;
+            shh[l] = hi;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  if (tid == 0 && best >= 0) {
+    double kept = a.rmass[row + best];
+    for (int i = 0; i < P2; ++i) {
+      const int h = shh[i];
+      if (h == 0x7fffffff || kept >= a.alpha) break;
+      a.ckey[row + h] = 0;
+      kept = __dadd_rn(kept, sm[i]);
+    }
   }
 }
 
@@ -617,6 +692,8 @@ hipError_t launch_route(const Plan& p, hipStream_t s) {
   a.dense_route = p.dense_route ? 1 : 0;
   a.mu = p.mu;
   a.ckey = p.ckey;
+  a.rmass = p.rmass;
+  a.alpha = (double)p.alpha;
   a.mand = p.mand;
   a.thr = p.thr;
   a.csr_ptr = p.csr_ptr;
@@ -630,7 +707,10 @@ hipError_t launch_route(const Plan& p, hipStream_t s) {
   a.stats = p.stats;
   hipLaunchKernelGGL(k_route_mu, dim3((p.GQ + 15) / 16, p.BH), dim3(256), 0, s, a);
   hipLaunchKernelGGL(k_route_keys, dim3((p.GQ + 3) / 4, p.BH), dim3(256), 0, s, a);
-  hipLaunchKernelGGL(k_route_select, dim3(p.BH), dim3(1024), 0, s, a);
+  if (p.router == SPARSEPR_ROUTER_ALPHA)
+    hipLaunchKernelGGL(k_route_alpha, dim3(p.GQ, p.BH), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(k_route_select, dim3(p.BH), dim3(1024), 0, s, a);
   hipLaunchKernelGGL(k_route_emit, dim3(p.BH), dim3(256), 0, s, a);
   return hipGetLastError();
 }

@@ -255,6 +255,8 @@ sparsepr_status sparsepr_config_default(int N, int d, sparsepr_config* out) {
   out->rank_cut = 1e-6f;
   out->partition_mode = SPARSEPR_PART_RESPONSE_COUPLED;
   out->seed = 0;
+  out->router = SPARSEPR_ROUTER_BUDGET;
+  out->alpha = 0.9f;
   return SPARSEPR_OK;
 }
 

@@ -33,6 +33,9 @@ sparsepr_status plan_init(Plan* p, const sparsepr_config* cfg, int B, int H, int
   if (cfg->partition_mode != SPARSEPR_PART_RESPONSE_COUPLED &&
       cfg->partition_mode != SPARSEPR_PART_INDEPENDENT)
     return SPARSEPR_ERR_INVALID_ARG;
+  if (cfg->router != SPARSEPR_ROUTER_BUDGET && cfg->router != SPARSEPR_ROUTER_ALPHA) return SPARSEPR_ERR_INVALID_ARG;
+  if (cfg->router == SPARSEPR_ROUTER_ALPHA && (!(cfg->alpha > 0.0f) || !(cfg->alpha <= 1.0f)))
+    return SPARSEPR_ERR_INVALID_ARG;
   if (cfg->ridge_mode != SPARSEPR_RIDGE_RELATIVE && cfg->ridge_mode != SPARSEPR_RIDGE_ABSOLUTE)
     return SPARSEPR_ERR_INVALID_ARG;
 
@@ -68,9 +71,16 @@ sparsepr_status plan_init(Plan* p, const sparsepr_config* cfg, int B, int H, int
   p->ridge_mode = cfg->ridge_mode;
   p->rank_cut = cfg->rank_cut;
   p->seed = cfg->seed;
-  p->dense_route = cfg->density >= 1.0f;
+  p->router = cfg->router;
+  p->alpha = cfg->alpha;
   double nn = (double)N * (double)N;
-  p->budget = (long long)floor((double)cfg->density * nn) - (long long)p->M * N;
+  if (p->router == SPARSEPR_ROUTER_ALPHA) {
+    p->dense_route = false;  // the alpha rule decides every cell; no budget
+    p->budget = (long long)N * N;
+  } else {
+    p->dense_route = cfg->density >= 1.0f;
+    p->budget = (long long)floor((double)cfg->density * nn) - (long long)p->M * N;
+  }
   return SPARSEPR_OK;
 }
 
@@ -156,6 +166,7 @@ void plan_carve(Plan* p, char* base) {
   p->vexp = c.take<int>(BH);
   p->mu = c.take<double>(BH * (long long)p->GQ * p->GK);
   p->ckey = c.take<uint64_t>(BH * (long long)p->GQ * p->GK);
+  p->rmass = p->router == SPARSEPR_ROUTER_ALPHA ? c.take<double>(BH * (long long)p->GQ * p->GK) : nullptr;
   p->mand = c.take<int>(BH * p->GQ);
   p->thr = c.take<long long>(BH * 4);
   p->csr_ptr = c.take<int>(BH * (p->GQ + 1));

@@ -29,7 +29,9 @@ struct Plan {
   int gwords;        // ceil(GK / 32)
   float scale, density, lambda, rank_cut;
   unsigned long long seed;
-  long long budget;  // routed-pair budget per (b,h)
+  long long budget;  // routed-pair budget per (b,h) (N^2 under the alpha router)
+  int router;        // sparsepr_router
+  float alpha;       // target retained mass of the alpha router
   bool dense_route;  // density >= 1: every cell granted
 
   View4 q, k, v;
@@ -70,6 +72,7 @@ struct Plan {
   int* vexp;              // [BH] power-of-two exponent k: the permuted V holds v * 2^-k in fp16
   double* mu;             // [BH, GQ, GK]
   uint64_t* ckey;         // [BH, GQ, GK] orderable descending log-probability
+  double* rmass;          // [BH, GQ, GK] estimated mass shares (alpha router only, else null)
   int* mand;              // [BH, GQ] best key group per query group (-1 if empty)
   long long* thr;         // [BH, 4] selection threshold
   int* csr_ptr;           // [BH, GQ + 1]

@@ -74,6 +74,16 @@ typedef enum {
   SPARSEPR_RIDGE_ABSOLUTE = 1
 } sparsepr_ridge_mode;
 
+typedef enum {
+  /* cells by estimated per-key probability under the pair budget of
+     `density` ([NE] NE/exec: the budget counts true pairs) */
+  SPARSEPR_ROUTER_BUDGET = 0,
+  /* per query group, its best cell and then key groups by estimated mass
+     until `alpha` of the group's mass is retained ([NE] NE/method, Figure 2:
+     key groups covered jointly for a target retained mass); no budget */
+  SPARSEPR_ROUTER_ALPHA = 1
+} sparsepr_router;
+
 /* Method settings.  Every field is a value the pages leave open unless noted;
    sparsepr_config_default() fills the documented defaults. */
 typedef struct {
@@ -92,6 +102,8 @@ typedef struct {
   int partition_mode;     /* sparsepr_partition_mode */
   int ridge_mode;         /* sparsepr_ridge_mode */
   unsigned long long seed;/* seed of the query sample (splitmix64) */
+  int router;             /* sparsepr_router */
+  float alpha;            /* target retained mass in (0, 1] of SPARSEPR_ROUTER_ALPHA */
 } sparsepr_config;
 
 /* Input/output description.  Strides are in elements, order [b, h, n, d]. */
@@ -112,7 +124,7 @@ typedef struct {
    (device memory, B*H entries, row-major over (b,h)). */
 typedef struct {
   long long routed_pairs;     /* sum over granted cells of |Q_g| * |K_h| */
-  long long budget_pairs;     /* floor(rho N^2) - M N */
+  long long budget_pairs;     /* floor(rho N^2) - M N (N^2 under the alpha router: no budget) */
   long long mandatory_pairs;  /* cost of the best cell of every query group */
   long long probe_pairs;      /* M N */
   int granted_cells;
@@ -131,7 +143,8 @@ typedef struct {
 /* Fill `out` with the defaults for a call of N tokens and head dim d:
    density 0.25, 64 probe rows, G_K = G_Q = clamp(N/128, 1, 256), r = 32,
    relative ridge lambda 1.0, T = 10, M_s = 256, r_K = 32, scale 0,
-   rank_cut 1e-6, response-coupled partition, seed 0. */
+   rank_cut 1e-6, response-coupled partition, seed 0, budget router
+   (alpha 0.9 for the alpha router). */
 sparsepr_status sparsepr_config_default(int N, int d, sparsepr_config* out);
 
 /* Check a config against a shape (no device work). */

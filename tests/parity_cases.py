@@ -30,6 +30,8 @@ class Case:
     seed: int = 7
     mode: str = "response_coupled"
     workload: str = ""
+    router: str = "budget"
+    alpha: float = 0.9
 
     @property
     def n(self):
@@ -37,11 +39,13 @@ class Case:
 
     def oracle_cfg(self) -> OracleConfig:
         return OracleConfig(density=self.density, probe_rows=self.probes, n_kv_groups=self.gk,
-                            n_q_groups=self.gq, residual_rank=self.rank, partition_mode=self.mode)
+                            n_q_groups=self.gq, residual_rank=self.rank, partition_mode=self.mode,
+                            router=self.router, alpha=self.alpha)
 
     def lib_cfg_kwargs(self) -> dict:
         return dict(density=self.density, probe_rows=self.probes, n_kv_groups=self.gk, n_q_groups=self.gq,
-                    residual_rank=self.rank, partition_mode=0 if self.mode == "response_coupled" else 1)
+                    residual_rank=self.rank, partition_mode=0 if self.mode == "response_coupled" else 1,
+                    router=0 if self.router == "budget" else 1, alpha=self.alpha)
 
 
 CASES = {
@@ -61,6 +65,11 @@ CASES = {
     # many groups: 300 key groups (more than one assignment workgroup's waves
     # hold) and 200 query groups at d = 128
     "many_groups": Case("many_groups", 4, 16, 40, 1, 128, "bf16", 300, 200, 0.3, 32, 8, seed=14),
+    # alpha-coverage router: ragged groups at d = 64, and two heads of the 8k call
+    "alpha_bf16_d64": Case("alpha_bf16_d64", 4, 10, 25, 2, 64, "bf16", 12, 10, 0.3, 32, 8, seed=15,
+                           router="alpha", alpha=0.8),
+    "alpha_c2": Case("alpha_c2", 8, 32, 32, 2, 64, "bf16", 64, 64, 0.25, 64, 32, workload="c2_dit_8k",
+                     router="alpha", alpha=0.9),
 }
 
 

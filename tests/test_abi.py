@@ -30,10 +30,34 @@ def test_library_exports_every_declared_symbol():
     assert set(names) <= set(_lib._SIGS), set(names) - set(_lib._SIGS)
 
 
-def test_struct_sizes_match_header_layout():
-    assert ctypes.sizeof(SparseprConfig) == 64
-    assert ctypes.sizeof(SparseprTensors) == 4 * 8 + 16 * 8 + 5 * 4 + 4  # padded to 8
-    assert ctypes.sizeof(SparseprHeadStats) == 4 * 8 + 8 * 4 + 2 * 8 + 4 * 8
+def test_struct_sizes_match_header_layout(tmp_path):
+    """Sizes and field offsets of the ctypes structures equal what a C
+    compiler makes of include/sparsepr.h."""
+    import shutil
+    import subprocess
+
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    structs = {"sparsepr_config": SparseprConfig, "sparsepr_tensors": SparseprTensors,
+               "sparsepr_head_stats": SparseprHeadStats}
+    lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "sparsepr.h"', "int main(void) {"]
+    for cname, cls in structs.items():
+        lines.append(f'  printf("{cname} %zu\\n", sizeof({cname}));')
+        for f, _ in cls._fields_:
+            lines.append(f'  printf("{cname}.{f} %zu\\n", offsetof({cname}, {f}));')
+    lines += ["  return 0;", "}"]
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines) + "\n")
+    exe = tmp_path / "layout"
+    inc = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include")
+    subprocess.run([cc, "-std=c11", "-I", inc, str(src), "-o", str(exe)], check=True)
+    got = dict(line.split() for line in subprocess.run([str(exe)], capture_output=True, text=True,
+                                                          check=True).stdout.splitlines())
+    for cname, cls in structs.items():
+        assert int(got[cname]) == ctypes.sizeof(cls), cname
+        for f, _ in cls._fields_:
+            assert int(got[f"{cname}.{f}"]) == getattr(cls, f).offset, (cname, f)
 
 
 def test_config_defaults():
@@ -43,6 +67,7 @@ def test_config_defaults():
     assert cfg.residual_rank == 32 and cfg.kmeans_iters == 10
     assert cfg.n_sample_q == 256 and cfg.key_coord_rank == 32
     assert cfg.ridge_lambda == pytest.approx(1.0) and cfg.ridge_mode == 0
+    assert cfg.router == 0 and cfg.alpha == pytest.approx(0.9)
     assert sparsepr_config_default(100000, 64).n_kv_groups == 256
 
 
@@ -50,7 +75,7 @@ def test_config_defaults():
     ("density", 0.0), ("density", -1.0), ("probe_rows", -1), ("probe_rows", 300),
     ("n_kv_groups", 0), ("n_q_groups", 2000), ("residual_rank", 65), ("ridge_lambda", -1.0),
     ("kmeans_iters", 0), ("n_sample_q", 0), ("n_sample_q", 257), ("key_coord_rank", 0),
-    ("rank_cut", 1.0), ("partition_mode", 7), ("ridge_mode", 2),
+    ("rank_cut", 1.0), ("partition_mode", 7), ("ridge_mode", 2), ("router", 2),
 ])
 def test_validation_rejects_bad_settings(field, value):
     cfg = make_config(4096, 64, n_kv_groups=32, n_q_groups=32)
@@ -105,3 +130,9 @@ def test_entry_points_reject_null_arguments_before_any_device_work():
 def test_status_strings():
     assert lib().sparsepr_status_string(0) == b"ok"
     assert b"workspace" in lib().sparsepr_status_string(-3)
+
+
+@pytest.mark.parametrize("alpha,ok", [(0.9, True), (1.0, True), (0.0, False), (-0.1, False), (1.5, False)])
+def test_alpha_router_target_must_lie_in_0_1(alpha, ok):
+    cfg = make_config(4096, 64, n_kv_groups=32, n_q_groups=32, router="alpha", alpha=alpha)
+    assert (sparsepr_validate(cfg, 1, 2, 4096, 64, 0) == 0) == ok
