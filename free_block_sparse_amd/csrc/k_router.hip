@@ -589,18 +589,39 @@ __global__ __launch_bounds__(256) void k_route_emit(RouteArgs a) {
     tcnt[g] = tiles_of_group(nq[g]);
     a.lg[(long long)bh * GQ + g] = L;
   }
-  // Tiles are listed by the mandatory (best) key group of their query group,
-  // then by group: query groups that attend to the same keys come next to
-  // each other, and the attention kernel runs neighbouring tiles on one XCD,
-  // where they share the L2.  (A stable order by that key; it only decides
-  // which tiles run together, never a result.)
+  // Tiles are listed by their query group's granted key groups, read as a
+  // word in ascending key group (a group granted the lowest key group on
+  // which two grant sets differ comes first), then by group.  A tile streams
+  // its granted groups in ascending order, so neighbouring tiles -- which the
+  // attention kernel runs together on one XCD -- read the same K/V rows at
+  // about the same time and share the L2.  (A stable order; it only decides
+  // which tiles run together, never a result.)  The comparison runs on the
+  // bit-reversed mask words, most significant first: a 64-bit key of the
+  // first two words, the remaining words only on ties.
+  __shared__ unsigned long long lkey[kMaxGroups];
   __syncthreads();
   for (int g = tid; g < GQ; g += 256) {
-    const int mg = mands[g] >= 0 ? mands[g] : 0;
+    const uint32_t w0 = gm[(long long)g * a.gwords];
+    const uint32_t w1 = a.gwords > 1 ? gm[(long long)g * a.gwords + 1] : 0u;
+    lkey[g] = ((unsigned long long)__builtin_bitreverse32(w0) << 32) | __builtin_bitreverse32(w1);
+  }
+  __syncthreads();
+  for (int g = tid; g < GQ; g += 256) {
+    const unsigned long long kg = lkey[g];
     int pos = 0;
     for (int q = 0; q < GQ; ++q) {
-      const int mq = mands[q] >= 0 ? mands[q] : 0;
-      pos += mq < mg || (mq == mg && q < g);
+      const unsigned long long kq = lkey[q];
+      bool before = kq > kg;
+      if (kq == kg && q != g) {
+        int c = 0;  // -1: q first, 1: g first
+        for (int w = 2; w < a.gwords && c == 0; ++w) {
+          const uint32_t rq = __builtin_bitreverse32(gm[(long long)q * a.gwords + w]);
+          const uint32_t rg = __builtin_bitreverse32(gm[(long long)g * a.gwords + w]);
+          if (rq != rg) c = rq > rg ? -1 : 1;
+        }
+        before = c < 0 || (c == 0 && q < g);
+      }
+      pos += before;
     }
     ord[pos] = g;
   }
