@@ -42,6 +42,10 @@ def parse():
     ap.add_argument("--router", choices=("budget", "alpha"), default="budget",
                     help="cell selection: pair budget from the density, or per-group target retained mass")
     ap.add_argument("--alpha", type=float, default=0.9, help="target retained mass of --router alpha")
+    ap.add_argument("--sweep", action="store_true",
+                    help="instead of the bench line: one JSON line per (partition, density) point of the "
+                         "density curve (ms/call, rho_exec, corrected and hard-drop error vs dense)")
+    ap.add_argument("--densities", default="0.12,0.15,0.18,0.21,0.25,0.30,0.35")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--profile-runs", type=int, default=3, help="calls timed per stage (at least 1)")
@@ -94,6 +98,34 @@ def cpu_baseline(x, w, cfg_kw, n: int, d: int, m: int, heads: int = 4) -> dict:
             "seconds": round(dt, 3)}
 
 
+def density_sweep(args, sp, torch, w, x) -> int:
+    """Density curve of both partitions against the library's dense output."""
+    q, k, v = (x[t].cuda() for t in ("q", "k", "v"))
+    B, H, N, d = q.shape
+    dense = sp.sparsepr_dense_attention(q, k, v).float()
+    dn = float(dense.norm())
+    out = torch.empty_like(q)
+    ws = sp.Workspace()
+    for mode in ("response_coupled", "independent"):
+        for rho in (float(r) for r in args.densities.split(",")):
+            cfg = sp.make_config(N, d, density=rho, probe_rows=w.probe_rows, n_kv_groups=w.n_kv_groups,
+                                 n_q_groups=w.n_q_groups, residual_rank=w.residual_rank, partition_mode=mode)
+            sp.sparsepr_attention(q, k, v, cfg, out=out, workspace=ws)  # warm-up
+            ms = min(time_fn(lambda: sp.sparsepr_attention(q, k, v, cfg, out=out, workspace=ws), 3, torch))
+            _, _, st = sp.sparsepr_attention_profile(q, k, v, cfg, out=out, workspace=ws)
+            heads = sp.stats_to_dicts(st)
+            err = float((out.float() - dense).norm()) / dn
+            ql, kl = sp.sparsepr_partition(q, k, v, cfg, workspace=ws)
+            hard = sp.sparsepr_sparse_attention(q, k, v, cfg, ql, kl, workspace=ws)
+            herr = float((hard.float() - dense).norm()) / dn
+            rho_exec = sum(h["routed_pairs"] + h["probe_pairs"] for h in heads) / (B * H * N * N)
+            print(json.dumps({"sweep": "density", "workload": w.name, "partition": mode, "density": rho,
+                              "rho_exec": round(rho_exec, 5), "ms_per_call": round(ms, 4),
+                              "rel_err_corrected": round(err, 5), "rel_err_hard_drop": round(herr, 5)}), flush=True)
+            log(f"{mode} rho {rho}: {ms:.2f} ms, err {err:.4f} (hard drop {herr:.4f})")
+    return 0
+
+
 def main() -> int:
     args = parse()
     if args.gpus != 1:
@@ -127,6 +159,8 @@ def main() -> int:
     t0 = time.time()
     x = make_workload_inputs(w)
     log(f"inputs ready in {time.time() - t0:.1f}s")
+    if args.sweep:
+        return density_sweep(args, sp, torch, w, x)
     q, k, v = (x[t].cuda() for t in ("q", "k", "v"))
     B, H, N, d = q.shape
     cfg_kw = dict(density=w.density, probe_rows=w.probe_rows, n_kv_groups=w.n_kv_groups,
