@@ -323,7 +323,10 @@ __global__ __launch_bounds__(256, 2) void k_sparse_attn_mfma(AttnArgs a) {
         for (int i = 0; i < 16; ++i) asm volatile("v_mul_f32 %0, %1, %0" : "+v"(o[b][i]) : "v"(alpha));
       m = mnew;
     }
-    const float mb = m;
+    // a row that has seen no key yet (the key-half wave of a split tile whose
+    // granted keys all lie in the other half) keeps m = -inf; its masked
+    // scores must give p = 0, not exp2(-inf + inf)
+    const float mb = m == -INFINITY ? 0.f : m;
     float psum = 0.f;
 #pragma unroll
     for (int kt = 0; kt < NKT; ++kt)

@@ -65,6 +65,9 @@ CASES = {
     # many groups: 300 key groups (more than one assignment workgroup's waves
     # hold) and 200 query groups at d = 128
     "many_groups": Case("many_groups", 4, 16, 40, 1, 128, "bf16", 300, 200, 0.3, 32, 8, seed=14),
+    # a query group with one granted key group of <= 32 keys and a <= 64-row
+    # remainder: one key half of its split tile sees no key at all
+    "split_tiny_cell": Case("split_tiny_cell", 4, 10, 25, 2, 64, "bf16", 12, 10, 0.3, 32, 8, seed=21),
     # alpha-coverage router: ragged groups at d = 64, and two heads of the 8k call
     "alpha_bf16_d64": Case("alpha_bf16_d64", 4, 10, 25, 2, 64, "bf16", 12, 10, 0.3, 32, 8, seed=15,
                            router="alpha", alpha=0.8),
