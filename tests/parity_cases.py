@@ -76,9 +76,27 @@ CASES = {
 }
 
 
+# Degenerate settings and random seeds (tests/test_gpu_edge_cases.py): one
+# group on each side, no probes, rank 0, mandatory cells only (over budget),
+# fewer tokens than one tile, and seeds with many small cells and split tiles.
+EDGE_CASES = {
+    "one_group": Case("one_group", 2, 8, 20, 1, 64, "bf16", 1, 1, 0.3, 16, 4, seed=31),
+    "no_probes": Case("no_probes", 2, 8, 20, 1, 64, "bf16", 6, 5, 0.3, 0, 4, seed=32),
+    "rank0": Case("rank0", 2, 8, 20, 1, 64, "bf16", 6, 5, 0.3, 16, 0, seed=33),
+    "mandatory_only": Case("mandatory_only", 2, 8, 20, 1, 64, "bf16", 8, 8, 0.02, 16, 4, seed=34),
+    "tiny_n": Case("tiny_n", 1, 10, 10, 1, 64, "bf16", 4, 4, 0.5, 8, 2, seed=35),
+    **{f"seed{s}": Case(f"seed{s}", 2, 10, 20, 2, 64 if s % 2 else 128, "bf16", 10, 6, 0.25, 16, 4, seed=40 + s)
+       for s in range(6)},
+}
+
+
+def case(name: str) -> Case:
+    return CASES[name] if name in CASES else EDGE_CASES[name]
+
+
 @functools.lru_cache(maxsize=None)
 def inputs(name: str):
-    c = CASES[name]
+    c = case(name)
     if c.workload:
         return make_workload_inputs(workload(c.workload), heads=c.heads)
     return make_video_qkv(c.frames, c.height, c.width, c.heads, c.d, c.dtype, c.seed, [c.f90] * c.heads)
@@ -86,7 +104,7 @@ def inputs(name: str):
 
 @functools.lru_cache(maxsize=None)
 def oracle_result(name: str):
-    c = CASES[name]
+    c = case(name)
     x = inputs(name)
     cfg = c.oracle_cfg()
     heads = []
@@ -122,7 +140,7 @@ def tolerances(dtype: str):
 
 def oracle_key_labels_from_metric(name: str, h: int, m_k) -> np.ndarray:
     """The oracle's key k-means run on coordinates built from a given M_K."""
-    c = CASES[name]
+    c = case(name)
     cfg = c.oracle_cfg()
     k64 = inputs(name)["k"][0, h].double().numpy()
     n, d = k64.shape
@@ -135,7 +153,7 @@ def oracle_key_labels_from_metric(name: str, h: int, m_k) -> np.ndarray:
 
 def oracle_out_given_partition(name: str, h: int, q_labels, kv_labels) -> np.ndarray:
     """The oracle's corrected output of head h on a given partition."""
-    c = CASES[name]
+    c = case(name)
     x = inputs(name)
     q, k, v = (x[t][0, h].double().numpy() for t in ("q", "k", "v"))
     r = sparsepr_head(q, k, v, c.oracle_cfg(), bh=h, q_labels=np.asarray(q_labels, dtype=np.int64),
@@ -146,7 +164,7 @@ def oracle_out_given_partition(name: str, h: int, q_labels, kv_labels) -> np.nda
 def oracle_query_labels_given_keys(name: str, h: int, kv_labels) -> np.ndarray:
     """The oracle's query k-means run on the query coordinates that a given
     key partition defines."""
-    c = CASES[name]
+    c = case(name)
     cfg = c.oracle_cfg()
     x = inputs(name)
     q64 = x["q"][0, h].double().numpy()
