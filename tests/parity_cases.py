@@ -138,17 +138,30 @@ def tolerances(dtype: str):
     return (2e-2, 5e-3) if dtype == "bf16" else (1e-4, 1e-5)
 
 
-def oracle_key_labels_from_metric(name: str, h: int, m_k) -> np.ndarray:
+def key_labels_from_metric(k64: np.ndarray, m_k, cfg: OracleConfig) -> np.ndarray:
     """The oracle's key k-means run on coordinates built from a given M_K."""
-    c = case(name)
-    cfg = c.oracle_cfg()
-    k64 = inputs(name)["k"][0, h].double().numpy()
     n, d = k64.shape
     s = softmax_scale(cfg, d)
     r_k = min(cfg.key_coord_rank, d, min(cfg.n_sample_q, n))
     z, _, _ = key_coordinates(k64, np.asarray(m_k, dtype=np.float64), r_k, s)
-    labels, _ = kmeans(z, c.gk, cfg.kmeans_iters)
+    labels, _ = kmeans(z, cfg.n_kv_groups, cfg.kmeans_iters)
     return labels
+
+
+def query_labels_given_keys(q64: np.ndarray, k64: np.ndarray, kv_labels, cfg: OracleConfig) -> np.ndarray:
+    """The oracle's query k-means run on the query coordinates that a given
+    key partition defines."""
+    s = softmax_scale(cfg, q64.shape[1])
+    perm_k, nk, off_k = group_by_labels(np.asarray(kv_labels, dtype=np.int64), cfg.n_kv_groups)
+    cbar = group_means(k64, perm_k, off_k)
+    u = query_coordinates(q64, cbar[nk > 0], s)
+    labels, _ = kmeans(u, cfg.n_q_groups, cfg.kmeans_iters)
+    return labels
+
+
+def oracle_key_labels_from_metric(name: str, h: int, m_k) -> np.ndarray:
+    """key_labels_from_metric on head h of a named case."""
+    return key_labels_from_metric(inputs(name)["k"][0, h].double().numpy(), m_k, case(name).oracle_cfg())
 
 
 def oracle_out_given_partition(name: str, h: int, q_labels, kv_labels) -> np.ndarray:
@@ -162,16 +175,7 @@ def oracle_out_given_partition(name: str, h: int, q_labels, kv_labels) -> np.nda
 
 
 def oracle_query_labels_given_keys(name: str, h: int, kv_labels) -> np.ndarray:
-    """The oracle's query k-means run on the query coordinates that a given
-    key partition defines."""
-    c = case(name)
-    cfg = c.oracle_cfg()
+    """query_labels_given_keys on head h of a named case."""
     x = inputs(name)
-    q64 = x["q"][0, h].double().numpy()
-    k64 = x["k"][0, h].double().numpy()
-    s = softmax_scale(cfg, q64.shape[1])
-    perm_k, nk, off_k = group_by_labels(np.asarray(kv_labels, dtype=np.int64), c.gk)
-    cbar = group_means(k64, perm_k, off_k)
-    u = query_coordinates(q64, cbar[nk > 0], s)
-    labels, _ = kmeans(u, c.gq, cfg.kmeans_iters)
-    return labels
+    return query_labels_given_keys(x["q"][0, h].double().numpy(), x["k"][0, h].double().numpy(), kv_labels,
+                                   case(name).oracle_cfg())

@@ -1,0 +1,92 @@
+"""The 32,760-token, 40-head call at full size, in the configuration the
+benchmark times, checked on sampled heads (GPU, C ABI).
+
+The whole call runs for all 40 heads.  The oracle then runs on two of them,
+the least and the most concentrated (heads 0 and 39).  For those heads:
+- the k-means partitions agree on >= 99% of tokens, each against the
+  oracle's k-means on the inputs that k-means actually gets;
+- the corrected error against dense attention is within 1.1x the oracle's
+  on the same partition;
+- with the oracle's labels injected, the routing is bit-exact and the
+  corrected output stays within the bf16 bounds.
+Every head's output must be finite.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import free_block_sparse_amd as sp
+from oracle import OracleConfig, dense_attention, sparsepr_head
+from parity_cases import (key_labels_from_metric, max_abs, query_labels_given_keys, rel_frob,
+                          tolerances)
+from synth import make_workload_inputs, workload
+
+pytestmark = pytest.mark.gpu
+
+HEADS = (0, 39)
+
+
+def dense_rows(q64, k64, v64, s, chunk=2048):
+    """The oracle's dense attention, a block of rows at a time (bounded memory)."""
+    return np.concatenate([dense_attention(q64[i:i + chunk], k64, v64, s) for i in range(0, len(q64), chunk)])
+
+
+def test_c3_full_size_on_sampled_heads():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    w = workload("c3_dit_32k")
+    print(f"[full] generating {w.name}: H={w.heads} N={w.n} d={w.d}", flush=True)
+    x = make_workload_inputs(w)
+    q, k, v = (x[t].cuda() for t in ("q", "k", "v"))
+    kw = dict(density=w.density, probe_rows=w.probe_rows, n_kv_groups=w.n_kv_groups, n_q_groups=w.n_q_groups,
+              residual_rank=w.residual_rank)
+    cfg = sp.make_config(w.n, w.d, **kw)
+    ocfg = OracleConfig(**kw)
+    ws = sp.Workspace()
+    out = sp.sparsepr_attention(q, k, v, cfg, workspace=ws)
+    ql, kl = sp.sparsepr_partition(q, k, v, cfg, workspace=ws)
+    _, mk, _, _ = sp.sparsepr_key_metric(q, k, v, cfg, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out.float()).all()
+
+    ql_mix, kl_mix = ql.clone(), kl.clone()
+    refs = {}
+    for h in HEADS:
+        print(f"[full] oracle on head {h}", flush=True)
+        q64, k64, v64 = (x[t][0, h].double().numpy() for t in ("q", "k", "v"))
+        r = sparsepr_head(q64, k64, v64, ocfg, bh=h)
+        dense = dense_rows(q64, k64, v64, r["scale"])
+        refs[h] = r
+        kl_h, ql_h = kl[h].cpu().numpy(), ql[h].cpu().numpy()
+        agree_k = (kl_h == key_labels_from_metric(k64, mk[h].cpu().double().numpy(), ocfg)).mean()
+        agree_q = (ql_h == query_labels_given_keys(q64, k64, kl_h, ocfg)).mean()
+        r_gpu = sparsepr_head(q64, k64, v64, ocfg, bh=h, q_labels=ql_h.astype(np.int64),
+                              kv_labels=kl_h.astype(np.int64))
+        err_gpu = rel_frob(out[0, h].double().cpu().numpy(), dense)
+        err_cond = rel_frob(r_gpu["out"], dense)
+        err_ora = rel_frob(r["out"], dense)
+        print(f"  head {h}: agreement K {agree_k:.4f} Q {agree_q:.4f} (unconditional K "
+              f"{(kl_h == r['kv_labels']).mean():.4f} Q {(ql_h == r['q_labels']).mean():.4f}); err vs dense "
+              f"gpu {err_gpu:.4f} oracle on the GPU partition {err_cond:.4f} oracle {err_ora:.4f}", flush=True)
+        assert agree_k >= 0.99 and agree_q >= 0.99
+        assert err_gpu <= 1.1 * err_cond
+        ql_mix[h] = torch.from_numpy(r["q_labels"].astype(np.int32))
+        kl_mix[h] = torch.from_numpy(r["kv_labels"].astype(np.int32))
+
+    ql_mix, kl_mix = ql_mix.cuda(), kl_mix.cuda()
+    res = sp.sparsepr_route(q, k, v, cfg, ql_mix, kl_mix, workspace=ws)
+    corr = sp.sparsepr_attention_with_partition(q, k, v, cfg, ql_mix, kl_mix, workspace=ws)
+    torch.cuda.synchronize()
+    stats = sp.stats_to_dicts(res["stats"])
+    ma, rf = tolerances("bf16")
+    for h in HEADS:
+        rt = refs[h]["route"]
+        rp = res["csr_rowptr"][h].cpu().numpy()
+        assert np.array_equal(rp, rt["csr_rowptr"])
+        assert np.array_equal(res["csr_cols"][h, :rp[-1]].cpu().numpy(), rt["csr_cols"])
+        assert stats[h]["routed_pairs"] == rt["routed_pairs"]
+        got = corr[0, h].double().cpu().numpy()
+        print(f"  head {h}: oracle partition: corrected max-abs {max_abs(got, refs[h]['out']):.3e} "
+              f"rel {rel_frob(got, refs[h]['out']):.3e}", flush=True)
+        assert max_abs(got, refs[h]["out"]) <= ma and rel_frob(got, refs[h]["out"]) <= rf
