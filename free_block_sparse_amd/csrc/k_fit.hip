@@ -205,20 +205,29 @@ __device__ inline double dot4(const TA* x, int sx, const TB* y, int sy, int n) {
   return (a0 + a1) + (a2 + a3);
 }
 
-// ALL_LDS: M <= 64 probes and r <= 32, so every matrix lives in LDS; the
-// pointers below are then known to be LDS pointers and compile to LDS
-// accesses instead of generic ones.
-template <bool ALL_LDS>
+// MODE 1 (ALL_LDS): M <= 64 probes and r <= 32, so every matrix lives in
+// LDS; the pointers below are then known to be LDS pointers and compile to
+// LDS accesses instead of generic ones.  MODE 0: M <= 64 with r > 32 (Y in
+// the global slice).  MODE 2 (BIG): more than 64 probes; the Gram of order
+// min(M, d) <= 128, and later the ridge system, sit in one LDS block so the
+// eigensolver and the Cholesky factorisation run on LDS (in the global slice
+// they took 50x longer); R, X and the eigenvectors use the global slice.
+template <int MODE>
 __global__ __launch_bounds__(1024) void k_fit(FitArgs a) {
+  constexpr bool ALL_LDS = MODE == 1;
+  constexpr bool BIG = MODE == 2;
   // LDS path for M <= 64: R and X as fp32 rows of stride d + 1, the Gram /
   // ridge system and eigenvectors as fp64 rows of stride 65 (odd strides keep
   // column walks on distinct banks).  Larger probe budgets use the
-  // per-(b,h) global scratch slice with unpadded strides.
+  // per-(b,h) global scratch slice with unpadded strides, except the BIG
+  // block above.
   constexpr int SM = 64, SLX = 129, SLG = SM + 1;
-  __shared__ float Rl[SM * SLX];
-  __shared__ float Xl[SM * SLX];
-  __shared__ double Gl[SM * SLG];
-  __shared__ double Ul[SM * SLG];
+  constexpr int EN = BIG ? 128 : 64;  // largest order of the eigen problem
+  __shared__ float Rl[BIG ? 1 : SM * SLX];
+  __shared__ float Xl[BIG ? 1 : SM * SLX];
+  __shared__ double Gl[BIG ? 1 : SM * SLG];
+  __shared__ double Ul[BIG ? 1 : SM * SLG];
+  __shared__ double Gb[BIG ? 128 * 129 : 1];  // BIG: the Gram, later the ridge system
   __shared__ double rcs[2 * 64];
   __shared__ int rpq[2 * 64];
   __shared__ double red[32];
@@ -229,8 +238,8 @@ __global__ __launch_bounds__(1024) void k_fit(FitArgs a) {
   __shared__ double xb[128];
   __shared__ double yb[64];
   __shared__ double bp[64];
-  __shared__ double edg[128 + 2], eeo[64 + 2], etau[64], evb[64], epb[64], erot[4 * 64];
-  __shared__ double Ycl[SM * 32];  // Y (M x rk) when M <= 64 and rk <= 32
+  __shared__ double edg[128 + 2], eeo[EN + 2], etau[EN], evb[EN], epb[EN], erot[4 * EN];
+  __shared__ double Ycl[BIG ? 1 : SM * 32];  // Y (M x rk) when M <= 64 and rk <= 32
   __shared__ double wl[kMaxProbe];  // the probe weights
   __shared__ int ectl[8];
   const int bh = blockIdx.x, tid = threadIdx.x, nt = blockDim.x;
@@ -239,18 +248,21 @@ __global__ __launch_bounds__(1024) void k_fit(FitArgs a) {
   const bool small = M <= d;
   const int n = small ? M : d;
   const int ne = n + (n & 1);
-  const bool lds = ALL_LDS || M <= SM;
+  const bool lds = ALL_LDS || (!BIG && M <= SM);
   const int ldx = lds ? SLX : d;
-  const bool glds = ALL_LDS || ne <= SM;
-  const int ldg = glds ? SLG : ne;
+  const bool glds = ALL_LDS || (!BIG && ne <= SM);
+  // BIG (more than 64 probes): the Gram / ridge block (order ne <= 128) in LDS
+  // with an odd stride, the eigenvectors in the global slice
+  const int ldg = BIG ? ne + 1 : (glds ? SLG : ne);
+  const int ldu = BIG ? ne : ldg;
   float* Rf = lds ? Rl : reinterpret_cast<float*>(S);                        // M x d
   float* Xf = lds ? Xl : reinterpret_cast<float*>(S) + 256 * 128;            // M x d (centred below)
-  double* G = glds ? Gl : S + 256 * 128;                                     // ne x ne, later the ridge system
+  double* G = BIG ? Gb : (glds ? Gl : S + 256 * 128);                      // ne x ne, later the ridge system
   double* U = glds ? Ul : S + 256 * 128 + 128 * 128;                         // ne x ne
   double* Vr = S + 256 * 128 + 2 * 128 * 128;                                // d x Rmax
   double* Wm = Vr + 128 * 64;                                                // d x rk (also the primal rhs)
   double* Yc = (ALL_LDS || (lds && a.Rcfg <= 32)) ? Ycl : Wm + 128 * 64;    // M x rk
-  double* Kp = Wm + 128 * 64 + 256 * 64;                                     // primal system d x d (M > d)
+  double* Kp = BIG ? Gb : Wm + 128 * 64 + 256 * 64;                          // primal system d x d (M > d)
   const float* ode = a.ode + (long long)bh * M * d;
   const float* osp = a.osp + (long long)bh * M * d;
   const double* wg = a.pw + (long long)bh * M;
@@ -299,12 +311,12 @@ __global__ __launch_bounds__(1024) void k_fit(FitArgs a) {
   }
   block_sync();
   bool fast = false;  // leading eigenpairs by multisection + twisted factorisations
-  if (glds) {
+  if (glds || BIG) {
     // Householder tridiagonalisation, then the leading eigenvalues by
     // multisection (the rank follows from them) and their vectors by twisted
     // factorisations; shifted QR on all of them when two leading eigenvalues
     // cannot be told apart.  Everything in LDS.
-    const EigWork<double> ew{G, ldg, U, ldg, edg, eeo, etau, evb, epb, erot, ectl};
+    const EigWork<double> ew{G, ldg, U, ldu, edg, eeo, etau, evb, epb, erot, ectl};
     eig_tridiagonalize<double, kFitThreads>(ew, ne);
     int nval = a.Rcfg > 4 ? a.Rcfg : 4;
     if (nval > ne) nval = ne;
@@ -371,9 +383,9 @@ __global__ __launch_bounds__(1024) void k_fit(FitArgs a) {
     const int ci = idx_s[k];
     double v;
     if (small) {
-      v = dot4(Rf + dm, ldx, U + ci, ldg, M) / sig_s[k];
+      v = dot4(Rf + dm, ldx, U + ci, ldu, M) / sig_s[k];
     } else {
-      v = U[dm * ldg + ci];
+      v = U[dm * ldu + ci];
     }
     Vr[dm * Rmax + k] = v;
   }
@@ -383,7 +395,7 @@ __global__ __launch_bounds__(1024) void k_fit(FitArgs a) {
     const int mm = e / rk, k = e - (e / rk) * rk;
     double acc = 0.0;
     if (small) {
-      acc = U[mm * ldg + idx_s[k]] * sig_s[k];
+      acc = U[mm * ldu + idx_s[k]] * sig_s[k];
     } else {
       for (int dm = 0; dm < d; ++dm) acc += (double)Rf[mm * ldx + dm] * Vr[dm * Rmax + k];
     }
@@ -560,8 +572,9 @@ hipError_t launch_fit(const Plan& p, hipStream_t s) {
   a.b = p.fitb;
   a.rank = p.fitrank;
   a.stats = p.stats;
-  if (a.M <= 64 && a.Rcfg <= 32) hipLaunchKernelGGL(k_fit<true>, dim3(p.BH), dim3(kFitThreads), 0, s, a);
-  else hipLaunchKernelGGL(k_fit<false>, dim3(p.BH), dim3(kFitThreads), 0, s, a);
+  if (a.M <= 64 && a.Rcfg <= 32) hipLaunchKernelGGL(k_fit<1>, dim3(p.BH), dim3(kFitThreads), 0, s, a);
+  else if (a.M <= 64) hipLaunchKernelGGL(k_fit<0>, dim3(p.BH), dim3(kFitThreads), 0, s, a);
+  else hipLaunchKernelGGL(k_fit<2>, dim3(p.BH), dim3(kFitThreads), 0, s, a);
   return hipGetLastError();
 }
 
