@@ -42,10 +42,11 @@ def parse():
     ap.add_argument("--router", choices=("budget", "alpha"), default="budget",
                     help="cell selection: pair budget from the density, or per-group target retained mass")
     ap.add_argument("--alpha", type=float, default=0.9, help="target retained mass of --router alpha")
-    ap.add_argument("--sweep", action="store_true",
-                    help="instead of the bench line: one JSON line per (partition, density) point of the "
-                         "density curve (ms/call, rho_exec, corrected and hard-drop error vs dense)")
-    ap.add_argument("--densities", default="0.12,0.15,0.18,0.21,0.25,0.30,0.35")
+    ap.add_argument("--sweep", choices=("density", "probes", "headdim", "all"), default=None,
+                    help="instead of the bench line: one JSON line per point of a quality/efficiency sweep "
+                         "(both partitions; ms/call, rho_exec, corrected and hard-drop error vs dense)")
+    ap.add_argument("--densities", default="0.10,0.12,0.15,0.18,0.21,0.22,0.25,0.26,0.30,0.35,0.40")
+    ap.add_argument("--probe-budgets", default="16,32,64,128,256")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--profile-runs", type=int, default=3, help="calls timed per stage (at least 1)")
@@ -98,17 +99,31 @@ def cpu_baseline(x, w, cfg_kw, n: int, d: int, m: int, heads: int = 4) -> dict:
             "seconds": round(dt, 3)}
 
 
-def density_sweep(args, sp, torch, w, x) -> int:
-    """Density curve of both partitions against the library's dense output."""
-    q, k, v = (x[t].cuda() for t in ("q", "k", "v"))
-    B, H, N, d = q.shape
-    dense = sp.sparsepr_dense_attention(q, k, v).float()
-    dn = float(dense.norm())
-    out = torch.empty_like(q)
+def sweep(args, sp, torch, w, x) -> int:
+    """Quality/efficiency sweep of both partitions against the library's dense output."""
+    from synth import make_workload_inputs
+
+    points = []  # (axis, d, density, probe rows)
+    if args.sweep in ("density", "all"):
+        points += [("density", w.d, float(r), w.probe_rows) for r in args.densities.split(",")]
+    if args.sweep in ("probes", "all"):
+        points += [("probes", w.d, w.density, int(m)) for m in args.probe_budgets.split(",")]
+    if args.sweep in ("headdim", "all"):
+        points += [("headdim", dd, w.density, w.probe_rows) for dd in (64, 128)]
     ws = sp.Workspace()
-    for mode in ("response_coupled", "independent"):
-        for rho in (float(r) for r in args.densities.split(",")):
-            cfg = sp.make_config(N, d, density=rho, probe_rows=w.probe_rows, n_kv_groups=w.n_kv_groups,
+    cache = {}
+    for axis, dd, rho, m in points:
+        if dd not in cache:
+            xx = x if dd == w.d else make_workload_inputs(w, d=dd)
+            q, k, v = (xx[t].cuda() for t in ("q", "k", "v"))
+            dense = sp.sparsepr_dense_attention(q, k, v).float()
+            cache.clear()
+            cache[dd] = (q, k, v, dense, float(dense.norm()))
+        q, k, v, dense, dn = cache[dd]
+        B, H, N, _ = q.shape
+        out = torch.empty_like(q)
+        for mode in ("response_coupled", "independent"):
+            cfg = sp.make_config(N, dd, density=rho, probe_rows=m, n_kv_groups=w.n_kv_groups,
                                  n_q_groups=w.n_q_groups, residual_rank=w.residual_rank, partition_mode=mode)
             sp.sparsepr_attention(q, k, v, cfg, out=out, workspace=ws)  # warm-up
             ms = min(time_fn(lambda: sp.sparsepr_attention(q, k, v, cfg, out=out, workspace=ws), 3, torch))
@@ -119,10 +134,10 @@ def density_sweep(args, sp, torch, w, x) -> int:
             hard = sp.sparsepr_sparse_attention(q, k, v, cfg, ql, kl, workspace=ws)
             herr = float((hard.float() - dense).norm()) / dn
             rho_exec = sum(h["routed_pairs"] + h["probe_pairs"] for h in heads) / (B * H * N * N)
-            print(json.dumps({"sweep": "density", "workload": w.name, "partition": mode, "density": rho,
-                              "rho_exec": round(rho_exec, 5), "ms_per_call": round(ms, 4),
+            print(json.dumps({"sweep": axis, "workload": w.name, "partition": mode, "d": dd, "density": rho,
+                              "probe_rows": m, "rho_exec": round(rho_exec, 5), "ms_per_call": round(ms, 4),
                               "rel_err_corrected": round(err, 5), "rel_err_hard_drop": round(herr, 5)}), flush=True)
-            log(f"{mode} rho {rho}: {ms:.2f} ms, err {err:.4f} (hard drop {herr:.4f})")
+            log(f"{axis} {mode} d {dd} rho {rho} M {m}: {ms:.2f} ms, err {err:.4f} (hard drop {herr:.4f})")
     return 0
 
 
@@ -160,7 +175,7 @@ def main() -> int:
     x = make_workload_inputs(w)
     log(f"inputs ready in {time.time() - t0:.1f}s")
     if args.sweep:
-        return density_sweep(args, sp, torch, w, x)
+        return sweep(args, sp, torch, w, x)
     q, k, v = (x[t].cuda() for t in ("q", "k", "v"))
     B, H, N, d = q.shape
     cfg_kw = dict(density=w.density, probe_rows=w.probe_rows, n_kv_groups=w.n_kv_groups,
