@@ -372,33 +372,10 @@ __global__ __launch_bounds__(256) void k_split_rows(SplitArgs a) {
 // B[k][n]: k = 8*(lane/32)+j, n = lane%32; D[i][j]: j = lane%32,
 // i = (r%4) + 8*(r/4) + 4*(lane/32) for accumulator register r.
 // ============================================================================
-// Smallest of the 16 distances c - 2 x.y held by one lane for a 32-centre
-// block (register r belongs to centre (r&3) + 8(r>>2) + 4*half, increasing
-// in r).  Pairwise tree (depth 4); on ties the lower register, i.e. the
-// lower centre index, is kept.  Returns the distance and writes the
-// register index.
-__device__ inline float block_argmin16(const f32x16& acc, const float* sb, int* ridx) {
-  float v[16];
-  int id[16];
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    v[r] = __builtin_fmaf(-2.0f, acc[r], sb[r]);
-    id[r] = r;
-  }
-#pragma unroll
-  for (int w = 1; w < 16; w <<= 1)
-#pragma unroll
-    for (int r = 0; r < 16; r += 2 * w) {
-      const bool right = v[r + w] < v[r];
-      v[r] = right ? v[r + w] : v[r];
-      id[r] = right ? id[r + w] : id[r];
-    }
-  *ridx = id[0];
-  return v[0];
-}
-
 // Largest of the 16 accumulator values a lane holds for a 32-centre block
-// (same register order as above); ties keep the lower register.
+// (register r belongs to centre (r&3) + 8(r>>2) + 4*half, increasing in r).
+// Pairwise tree (depth 4); on ties the lower register, i.e. the lower centre
+// index, is kept.  Returns the value and writes the register index.
 __device__ inline float block_argmax16(const f32x16& acc, int* ridx) {
   float v[16];
   int id[16];
@@ -479,7 +456,8 @@ __global__ __launch_bounds__(512) void k_kmeans_assign(AssignArgs a) {
         }
       }
     }
-    for (int e = tid; e < G32; e += NT) sbias[e] = e < G ? a.ybias[(long long)bh * a.gstride + e] : INFINITY;
+    // -c_g / 2, the accumulators' start (centres past G never win)
+    for (int e = tid; e < G32; e += NT) sbias[e] = e < G ? -0.5f * a.ybias[(long long)bh * a.gstride + e] : -INFINITY;
   }
   __syncthreads();
 
@@ -513,10 +491,10 @@ __global__ __launch_bounds__(512) void k_kmeans_assign(AssignArgs a) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const float4 f = *reinterpret_cast<const float4*>(sbias + cb + 8 * q + 4 * half);
-        cinit[4 * q] = -0.5f * f.x;
-        cinit[4 * q + 1] = -0.5f * f.y;
-        cinit[4 * q + 2] = -0.5f * f.z;
-        cinit[4 * q + 3] = -0.5f * f.w;
+        cinit[4 * q] = f.x;
+        cinit[4 * q + 1] = f.y;
+        cinit[4 * q + 2] = f.z;
+        cinit[4 * q + 3] = f.w;
       }
       f32x16 acc[PB];
 #pragma unroll
@@ -568,7 +546,8 @@ __global__ __launch_bounds__(512, 4) void k_kmeans_assign_staged(AssignArgs a) {
   // workgroup (8 waves x one 32-point MFMA column, points held as B operands
   // in registers); the centre images are staged through LDS CG at a time
   // (two barriers per CG centres) and read as A operands, two 32-centre
-  // blocks at a time.
+  // blocks at a time.  The accumulators start at -c_g / 2, so they end at
+  // x . y_g - c_g / 2 and the nearest centre is the largest value.
   constexpr int KS = D / 16;
   constexpr int LDI = D + 8;  // padded LDS row (bank spread)
   constexpr int NT = 512;
@@ -598,7 +577,7 @@ __global__ __launch_bounds__(512, 4) void k_kmeans_assign_staged(AssignArgs a) {
     ph[ks] = __builtin_bit_cast(bf16x8, v);
     if (LO) pl[LO ? ks : 0] = __builtin_bit_cast(bf16x8, w);
   }
-  float best = INFINITY;
+  float best = -INFINITY;
   int bidx = 0;
   const bf16_t* yh = a.yhi + (long long)bh * a.gstride * a.ystride;
   const bf16_t* yl = a.ylo + (long long)bh * a.gstride * a.ystride;
@@ -616,13 +595,27 @@ __global__ __launch_bounds__(512, 4) void k_kmeans_assign_staged(AssignArgs a) {
       *reinterpret_cast<uint4*>(sh + r * LDI + cc * 8) = vh;
       *reinterpret_cast<uint4*>(sl + r * LDI + cc * 8) = vl;
     }
-    for (int e = tid; e < CG; e += NT) sbias[e] = (c0 + e < G) ? yb[c0 + e] : INFINITY;
+    for (int e = tid; e < CG; e += NT) sbias[e] = (c0 + e < G) ? -0.5f * yb[c0 + e] : -INFINITY;
     __syncthreads();
     const int nblk = min(CG, G - c0);
     // two 32-centre blocks at a time: independent accumulator chains
     for (int cb = 0; cb < nblk; cb += 64) {
       const bool two = cb + 32 < nblk;
-      f32x16 acc0 = {}, acc1 = {};
+      // -c_g / 2 of this lane's centres: four runs of four consecutive centres
+      f32x16 acc0, acc1;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float4 f0 = *reinterpret_cast<const float4*>(sbias + cb + 8 * q + 4 * half);
+        const float4 f1 = *reinterpret_cast<const float4*>(sbias + min(cb + 32, CG - 32) + 8 * q + 4 * half);
+        acc0[4 * q] = f0.x;
+        acc0[4 * q + 1] = f0.y;
+        acc0[4 * q + 2] = f0.z;
+        acc0[4 * q + 3] = f0.w;
+        acc1[4 * q] = f1.x;
+        acc1[4 * q + 1] = f1.y;
+        acc1[4 * q + 2] = f1.z;
+        acc1[4 * q + 3] = f1.w;
+      }
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         const bf16_t* r0 = sh + (cb + col) * LDI + 16 * ks + 8 * half;
@@ -640,34 +633,16 @@ __global__ __launch_bounds__(512, 4) void k_kmeans_assign_staged(AssignArgs a) {
           acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah1, pl[LO ? ks : 0], acc1, 0, 0, 0);
         }
       }
-      // biases of this lane's centres: four runs of four consecutive centres
-      float sb[16];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float4 f = *reinterpret_cast<const float4*>(sbias + cb + 8 * q + 4 * half);
-        sb[4 * q] = f.x;
-        sb[4 * q + 1] = f.y;
-        sb[4 * q + 2] = f.z;
-        sb[4 * q + 3] = f.w;
-      }
       int rr;
-      float dist = block_argmin16(acc0, sb, &rr);
-      if (dist < best) {
-        best = dist;
+      float sc = block_argmax16(acc0, &rr);
+      if (sc > best) {
+        best = sc;
         bidx = c0 + cb + (rr & 3) + 8 * (rr >> 2) + 4 * half;
       }
       if (two) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const float4 f = *reinterpret_cast<const float4*>(sbias + cb + 32 + 8 * q + 4 * half);
-          sb[4 * q] = f.x;
-          sb[4 * q + 1] = f.y;
-          sb[4 * q + 2] = f.z;
-          sb[4 * q + 3] = f.w;
-        }
-        dist = block_argmin16(acc1, sb, &rr);
-        if (dist < best) {
-          best = dist;
+        sc = block_argmax16(acc1, &rr);
+        if (sc > best) {
+          best = sc;
           bidx = c0 + cb + 32 + (rr & 3) + 8 * (rr >> 2) + 4 * half;
         }
       }
@@ -676,7 +651,7 @@ __global__ __launch_bounds__(512, 4) void k_kmeans_assign_staged(AssignArgs a) {
   {
     const float ob = __shfl_xor(best, 32, 64);
     const int oi = __shfl_xor(bidx, 32, 64);
-    if (ob < best || (ob == best && oi < bidx)) {
+    if (ob > best || (ob == best && oi < bidx)) {
       best = ob;
       bidx = oi;
     }
