@@ -331,56 +331,76 @@ __global__ __launch_bounds__(1024) void k_route_select(RouteArgs a) {
     const uint64_t ph = ph_s;
     const uint32_t pl = pl_s;
     const int lane = tid & 63;
-    for (int c0 = 0; c0 < ncell; c0 += 1024) {
-      const int c = c0 + tid;
-      bool take = false;
-      int dig = 0;
-      unsigned long long cost = 0;
-      if (c < ncell) {
-        const uint64_t k = ck[c];
-        if (k != kExcluded && comp_prefix_eq(k, (uint32_t)c, nbits, ph, pl)) {
-          take = true;
-          comp_digits(k, (uint32_t)c, pass, &dig);
-          const int g = c / GK, h = c - (c / GK) * GK;
-          cost = (unsigned long long)((long long)nq[g] * nk[h]);
-        }
+    // four cells per thread per round, their keys loaded together
+    constexpr int U = 4;
+    for (int c00 = 0; c00 < ncell; c00 += U * 1024) {
+      uint64_t kk[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int c = c00 + u * 1024 + tid;
+        kk[u] = c < ncell ? ck[c] : kExcluded;
       }
-      // early passes put almost every cell in one bin: when all the wave's
-      // cells share a digit, one lane adds the wave's total
-      const unsigned long long act = __builtin_amdgcn_ballot_w64(take);
-      if (act == 0ull) continue;
-      const int first = __builtin_ctzll(act);
-      const int d0 = __shfl(dig, first, 64);
-      if (__builtin_amdgcn_ballot_w64(take && dig == d0) == act) {
-        unsigned long long t = cost;
-        for (int o = 32; o > 0; o >>= 1) t += __shfl_xor(t, o, 64);
-        if (lane == first) {
-          atomicAdd(&hist[wave][d0], t);
-          atomicAdd(&cnth[d0], __builtin_popcountll(act));
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int c = c00 + u * 1024 + tid;
+        bool take = false;
+        int dig = 0;
+        unsigned long long cost = 0;
+        {
+          const uint64_t k = kk[u];
+          if (k != kExcluded && comp_prefix_eq(k, (uint32_t)c, nbits, ph, pl)) {
+            take = true;
+            comp_digits(k, (uint32_t)c, pass, &dig);
+            const int g = c / GK, h = c - (c / GK) * GK;
+            cost = (unsigned long long)((long long)nq[g] * nk[h]);
+          }
         }
-      } else if (take) {
-        atomicAdd(&hist[wave][dig], cost);
-        atomicAdd(&cnth[dig], 1);
+        // early passes put almost every cell in one bin: when all the wave's
+        // cells share a digit, one lane adds the wave's total
+        const unsigned long long act = __builtin_amdgcn_ballot_w64(take);
+        if (act == 0ull) continue;
+        const int first = __builtin_ctzll(act);
+        const int d0 = __shfl(dig, first, 64);
+        if (__builtin_amdgcn_ballot_w64(take && dig == d0) == act) {
+          unsigned long long t = cost;
+          for (int o = 32; o > 0; o >>= 1) t += __shfl_xor(t, o, 64);
+          if (lane == first) {
+            atomicAdd(&hist[wave][d0], t);
+            atomicAdd(&cnth[d0], __builtin_popcountll(act));
+          }
+        } else if (take) {
+          atomicAdd(&hist[wave][dig], cost);
+          atomicAdd(&cnth[dig], 1);
+        }
       }
     }
     __syncthreads();
+    // bin totals and their inclusive prefix (threads 0-255, four waves); the
+    // chosen bin is the first whose prefix exceeds what is left of the budget
+    long long pre = 0;
     if (tid < 256) {
       unsigned long long t = 0;
       for (int w = 0; w < 16; ++w) t += hist[w][tid];
-      hist[0][tid] = t;
+      pre = (long long)t;
+      for (int o = 1; o < 64; o <<= 1) {
+        const long long u = __shfl_up(pre, o, 64);
+        if (lane >= o) pre += u;
+      }
+      if (lane == 63) red[wave] = pre;
+    }
+    __syncthreads();
+    if (tid < 256) {
+      for (int w = 0; w < wave; ++w) pre += red[w];
+      const unsigned long long over = __builtin_amdgcn_ballot_w64(pre > rem_s);
+      if (lane == 0) red[8 + wave] = over ? 64 * wave + __builtin_ctzll(over) : 256;
+      hist[1][tid] = (unsigned long long)pre;  // row 1 is free after the totals above
     }
     __syncthreads();
     if (tid == 0) {
+      int chosen = (int)min(min(red[8], red[9]), min(red[10], red[11]));
       long long acc = 0;
-      int chosen = -1;
-      for (int b = 0; b < 256; ++b) {
-        const long long hb = (long long)hist[0][b];
-        if (acc + hb > rem_s) {
-          chosen = b;
-          break;
-        }
-        acc += hb;
-      }
+      if (chosen >= 256) chosen = -1;
+      else if (chosen > 0) acc = (long long)hist[1][chosen - 1];
       if (chosen < 0) {
         mode_s = 3;  // every remaining candidate fits
         done_s = 1;
@@ -408,14 +428,24 @@ __global__ __launch_bounds__(1024) void k_route_select(RouteArgs a) {
       found_s = 0;
     }
     __syncthreads();
-    for (int c = tid; c < ncell; c += 1024) {
-      const uint64_t k = ck[c];
-      if (k == kExcluded || !comp_prefix_eq(k, (uint32_t)c, nbits, ph, pl)) continue;
-      const int slot = atomicAdd(&ncand_s, 1);
-      const int g = c / GK, h = c - (c / GK) * GK;
-      sk[slot] = k;
-      scell[slot] = (unsigned)c;
-      scost[slot] = (long long)nq[g] * nk[h];
+    for (int c00 = 0; c00 < ncell; c00 += 4 * 1024) {
+      uint64_t kk[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int c = c00 + u * 1024 + tid;
+        kk[u] = c < ncell ? ck[c] : kExcluded;
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int c = c00 + u * 1024 + tid;
+        const uint64_t k = kk[u];
+        if (k == kExcluded || !comp_prefix_eq(k, (uint32_t)c, nbits, ph, pl)) continue;
+        const int slot = atomicAdd(&ncand_s, 1);
+        const int g = c / GK, h = c - (c / GK) * GK;
+        sk[slot] = k;
+        scell[slot] = (unsigned)c;
+        scost[slot] = (long long)nq[g] * nk[h];
+      }
     }
     __syncthreads();
     const int nc = ncand_s;
