@@ -133,8 +133,13 @@ def _cast(x: torch.Tensor, dtype: str) -> torch.Tensor:
 def make_video_qkv(frames: int, height: int, width: int, heads: int, d: int,
                    dtype: str = "bf16", seed: int = 0,
                    f90_targets: Optional[Sequence[float]] = None,
-                   n_calib: int = 256) -> dict:
-    """Return {"q","k","v": [1, heads, N, d] CPU tensors, "tau", "f90_target"}."""
+                   n_calib: int = 256, device: str = "cpu") -> dict:
+    """Return {"q","k","v": [1, heads, N, d] tensors on `device`, "tau", "f90_target"}.
+
+    The random draws are made on the host either way; `device` only moves the
+    per-head projections and the temperature calibration (values may differ
+    from a host run in the last bits, so a test that compares the two sides
+    hands both the same generated tensors)."""
     if d % 2:
         raise ValueError("d must be even")
     n = frames * height * width
@@ -160,17 +165,17 @@ def make_video_qkv(frames: int, height: int, width: int, heads: int, d: int,
     dist = (((p[:, None, :] - anchors[None, :, :]) * wts) ** 2).sum(-1)
     obj = dist.argmin(axis=1)
     X = phi + offsets[obj] + rng.normal(0.0, 0.1, size=(n, d))
-    Xt = torch.from_numpy(X.astype(np.float32))
+    Xt = torch.from_numpy(X.astype(np.float32)).to(device)
 
     scale = 1.0 / math.sqrt(d)
-    calib_idx = torch.from_numpy(((2 * np.arange(min(n_calib, n)) + 1) * n) // (2 * min(n_calib, n)))
+    calib_idx = torch.from_numpy(((2 * np.arange(min(n_calib, n)) + 1) * n) // (2 * min(n_calib, n))).to(device)
     qs, ks, vs, taus = [], [], [], []
     for h, ssh in enumerate(ss_heads.spawn(heads)):
         rh = np.random.default_rng(ssh)
         std = math.sqrt(1.0 / d)
-        Wq = torch.from_numpy(rh.normal(0.0, std, size=(d, d)).astype(np.float32))
-        Wk = torch.from_numpy(rh.normal(0.0, std, size=(d, d)).astype(np.float32))
-        Wv = torch.from_numpy(rh.normal(0.0, std, size=(d, d)).astype(np.float32))
+        Wq = torch.from_numpy(rh.normal(0.0, std, size=(d, d)).astype(np.float32)).to(device)
+        Wk = torch.from_numpy(rh.normal(0.0, std, size=(d, d)).astype(np.float32)).to(device)
+        Wv = torch.from_numpy(rh.normal(0.0, std, size=(d, d)).astype(np.float32)).to(device)
         q0 = Xt @ Wq
         kh = Xt @ Wk
         vh = Xt @ Wv
@@ -187,15 +192,15 @@ def make_video_qkv(frames: int, height: int, width: int, heads: int, d: int,
         "v": torch.stack(vs)[None].contiguous(),
         "tau": np.array(taus),
         "f90_target": np.array(f90_targets),
-        "calib_idx": calib_idx.numpy(),
+        "calib_idx": calib_idx.cpu().numpy(),
     }
 
 
 def make_workload_inputs(w: Workload, seed: Optional[int] = None, heads: Optional[int] = None,
-                         d: Optional[int] = None) -> dict:
+                         d: Optional[int] = None, device: str = "cpu") -> dict:
     """Inputs for a named workload (optionally fewer heads or another head dim)."""
     H = w.heads if heads is None else heads
     dd = w.d if d is None else d
     targets = dataclasses.replace(w, heads=w.heads).f90_targets()[:H]
     return make_video_qkv(w.frames, w.height, w.width, H, dd, w.dtype,
-                          w.seed if seed is None else seed, targets)
+                          w.seed if seed is None else seed, targets, device=device)
