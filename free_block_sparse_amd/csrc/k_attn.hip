@@ -471,14 +471,52 @@ __global__ __launch_bounds__(256, 2) void k_sparse_attn_mfma(AttnArgs a) {
     for (int r = 0; r < 16; ++r) x[b][r] = o[b][r] * inv;
   const int rank = (a.correct && a.fitrank) ? a.fitrank[bh] : 0;
   if (rank > 0) {
-    float* Wl = reinterpret_cast<float*>(KV0);  // D x 33 floats fit in one stage's K tile
-    float* Vl = reinterpret_cast<float*>(KV1);
-    float corr[DB][16];
+    // Correction on the matrix cores, in the accumulators' own layout:
+    //   T^T (rank x rows) = W^T X^T,   out^T (dims x rows) = X^T + b + V T^T,
+    // so out^T lands where each lane already holds its row's dims.  X, T, W
+    // and V are split into hi + lo bf16; each product adds hi.hi + lo.hi +
+    // hi.lo (relative error about 2^-16).  W^T and V pass through the idle
+    // stage buffers, 32 rank columns at a time, rows padded so that the
+    // fragment reads are free of bank conflicts.
+    constexpr int WLD = D + 8, VLD = 40;
+    bf16_t* Wh = KV0;             // [32][WLD]: W^T, hi
+    bf16_t* Wlo = KV0 + 32 * WLD;  // lo
+    bf16_t* Vh = KV1;             // [D][VLD]: V, hi
+    bf16_t* Vlo = KV1 + D * VLD;   // lo
+    // B operands take 8 consecutive dims (ranks) per lane: dims 16 c + 8 half
+    // + 0..7 of the lane's row for chunk c.  The accumulator layout holds
+    // dims (r & 3) + 8 (r >> 2) + 4 half, so registers 8 sub + q and
+    // 8 sub + 4 + q are exchanged between lanes i and i + 32.
+    auto to_b = [&](const float* v16, bf16x8* hi, bf16x8* lo) __attribute__((always_inline)) {
+      float v[8];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(v16[q]), __float_as_uint(v16[4 + q]), false,
+                                                         false);
+        v[q] = __uint_as_float(sw[0]);
+        v[4 + q] = __uint_as_float(sw[1]);
+      }
+      uint32_t ph[4], pl[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const bf16_t h0 = f32_to_bf16(v[2 * j]), h1 = f32_to_bf16(v[2 * j + 1]);
+        const bf16_t l0 = f32_to_bf16(v[2 * j] - bf16_to_f32(h0)), l1 = f32_to_bf16(v[2 * j + 1] - bf16_to_f32(h1));
+        ph[j] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+        pl[j] = (uint32_t)l0 | ((uint32_t)l1 << 16);
+      }
+      *hi = __builtin_bit_cast(bf16x8, make_uint4(ph[0], ph[1], ph[2], ph[3]));
+      *lo = __builtin_bit_cast(bf16x8, make_uint4(pl[0], pl[1], pl[2], pl[3]));
+    };
+    bf16x8 xh[KS], xl[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) to_b(&x[ks >> 1][8 * (ks & 1)], &xh[ks], &xl[ks]);
+    // accumulators start at x + b
+    f32x16 cacc[DB];
     const float* fb = a.fitb + (long long)bh * D;
 #pragma unroll
     for (int b = 0; b < DB; ++b)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) corr[b][r] = fb[32 * b + (r & 3) + 8 * (r >> 2) + 4 * half];
+      for (int r = 0; r < 16; ++r) cacc[b][r] = x[b][r] + fb[32 * b + (r & 3) + 8 * (r >> 2) + 4 * half];
     const float* fw = a.fitW + (long long)bh * D * a.R;
     const float* fv = a.fitV + (long long)bh * D * a.R;
     for (int j0 = 0; j0 < rank; j0 += 32) {
@@ -486,41 +524,49 @@ __global__ __launch_bounds__(256, 2) void k_sparse_attn_mfma(AttnArgs a) {
       __syncthreads();
       for (int e = tid; e < D * 32; e += 256) {
         const int dm = e >> 5, j = e & 31;
-        Wl[dm * 33 + j] = j < nj ? fw[(long long)dm * a.R + j0 + j] : 0.f;
-        Vl[dm * 33 + j] = j < nj ? fv[(long long)dm * a.R + j0 + j] : 0.f;
+        const float wv = j < nj ? fw[(long long)dm * a.R + j0 + j] : 0.f;
+        const float vv = j < nj ? fv[(long long)dm * a.R + j0 + j] : 0.f;
+        const bf16_t wh = f32_to_bf16(wv), vh = f32_to_bf16(vv);
+        Wh[j * WLD + dm] = wh;
+        Wlo[j * WLD + dm] = f32_to_bf16(wv - bf16_to_f32(wh));
+        Vh[dm * VLD + j] = vh;
+        Vlo[dm * VLD + j] = f32_to_bf16(vv - bf16_to_f32(vh));
       }
       __syncthreads();
       if (owner) {
-        float t[32];
+        // T^T = W^T X^T: A = rows of W^T (rank col, dims 16 ks + 8 half ..)
+        f32x16 t = f32x16{};
 #pragma unroll
-        for (int j = 0; j < 32; ++j) t[j] = 0.f;
+        for (int ks = 0; ks < KS; ++ks) {
+          const bf16x8 ah = *reinterpret_cast<const bf16x8*>(Wh + col * WLD + 16 * ks + 8 * half);
+          const bf16x8 al = *reinterpret_cast<const bf16x8*>(Wlo + col * WLD + 16 * ks + 8 * half);
+          t = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, xh[ks], t, 0, 0, 0);
+          t = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, xh[ks], t, 0, 0, 0);
+          t = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, xl[ks], t, 0, 0, 0);
+        }
+        bf16x8 th[2], tl[2];
+        float tv[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) tv[r] = t[r];
+#pragma unroll
+        for (int kr = 0; kr < 2; ++kr) to_b(&tv[8 * kr], &th[kr], &tl[kr]);
+        // out^T += V T^T: A = rows of V (dim 32 b + col, ranks 16 kr + 8 half ..)
 #pragma unroll
         for (int b = 0; b < DB; ++b)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int dm = 32 * b + (r & 3) + 8 * (r >> 2) + 4 * half;
-            const float xv = x[b][r];
-#pragma unroll
-            for (int j = 0; j < 32; ++j) t[j] += xv * Wl[dm * 33 + j];
-          }
-#pragma unroll
-        for (int j = 0; j < 32; ++j) t[j] += __shfl_xor(t[j], 32, 64);
-#pragma unroll
-        for (int b = 0; b < DB; ++b)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int dm = 32 * b + (r & 3) + 8 * (r >> 2) + 4 * half;
-            float acc = 0.f;
-#pragma unroll
-            for (int j = 0; j < 32; ++j) acc += t[j] * Vl[dm * 33 + j];
-            corr[b][r] += acc;
+          for (int kr = 0; kr < 2; ++kr) {
+            const bf16x8 vh = *reinterpret_cast<const bf16x8*>(Vh + (32 * b + col) * VLD + 16 * kr + 8 * half);
+            const bf16x8 vl = *reinterpret_cast<const bf16x8*>(Vlo + (32 * b + col) * VLD + 16 * kr + 8 * half);
+            cacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vh, th[kr], cacc[b], 0, 0, 0);
+            cacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vl, th[kr], cacc[b], 0, 0, 0);
+            cacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vh, tl[kr], cacc[b], 0, 0, 0);
           }
       }
     }
 #pragma unroll
     for (int b = 0; b < DB; ++b)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) x[b][r] += corr[b][r];
+      for (int r = 0; r < 16; ++r) x[b][r] = cacc[b][r];
   }
   if (!(owner && qvalid)) return;
   const int pos = row0 + qr;
