@@ -38,6 +38,8 @@ struct AttnArgs {
   const float* fitV;
   const float* fitb;
   const int* fitrank;
+  const bf16_t* fitpk;  // hi/lo bf16 W^T [Rp, D] and V [D, Rp] per head (MFMA epilogue)
+  int Rp;
   int R;
   int N, GK, GQ;
   float scale;
@@ -354,7 +356,7 @@ __global__ __launch_bounds__(256, 2) void k_sparse_attn_mfma(AttnArgs a) {
           const h2 hv = {(_Float16)sacc[kt][rb + 2 * j], (_Float16)sacc[kt][rb + 2 * j + 1]};
           pw[j] = __builtin_bit_cast(uint32_t, hv);
         } else {
-          pw[j] = (uint32_t)f32_to_bf16(sacc[kt][rb + 2 * j]) | ((uint32_t)f32_to_bf16(sacc[kt][rb + 2 * j + 1]) << 16);
+          pw[j] = pack_bf16x2(sacc[kt][rb + 2 * j], sacc[kt][rb + 2 * j + 1]);
         }
       }
       const uint4 pk = make_uint4(pw[0], pw[1], pw[2], pw[3]);
@@ -475,14 +477,15 @@ __global__ __launch_bounds__(256, 2) void k_sparse_attn_mfma(AttnArgs a) {
     //   T^T (rank x rows) = W^T X^T,   out^T (dims x rows) = X^T + b + V T^T,
     // so out^T lands where each lane already holds its row's dims.  X, T, W
     // and V are split into hi + lo bf16; each product adds hi.hi + lo.hi +
-    // hi.lo (relative error about 2^-16).  W^T and V pass through the idle
-    // stage buffers, 32 rank columns at a time, rows padded so that the
-    // fragment reads are free of bank conflicts.
-    constexpr int WLD = D + 8, VLD = 40;
-    bf16_t* Wh = KV0;             // [32][WLD]: W^T, hi
-    bf16_t* Wlo = KV0 + 32 * WLD;  // lo
-    bf16_t* Vh = KV1;             // [D][VLD]: V, hi
-    bf16_t* Vlo = KV1 + D * VLD;   // lo
+    // hi.lo (relative error about 2^-16).  W^T and V come from the per-head
+    // packed copies (hi/lo bf16, rank columns past the head's rank zero),
+    // which every workgroup of the head reads through the L2; only the
+    // owner waves read them, 32 rank columns at a time.
+    const int Rp = a.Rp;
+    const bf16_t* Wh = a.fitpk + (long long)bh * 4 * Rp * D;  // [Rp][D]: W^T, hi
+    const bf16_t* Wlo = Wh + (long long)Rp * D;               // lo
+    const bf16_t* Vh = Wlo + (long long)Rp * D;               // [D][Rp]: V, hi
+    const bf16_t* Vlo = Vh + (long long)Rp * D;               // lo
     // B operands take 8 consecutive dims (ranks) per lane: dims 16 c + 8 half
     // + 0..7 of the lane's row for chunk c.  The accumulator layout holds
     // dims (r & 3) + 8 (r >> 2) + 4 half, so registers 8 sub + q and
@@ -499,10 +502,8 @@ __global__ __launch_bounds__(256, 2) void k_sparse_attn_mfma(AttnArgs a) {
       uint32_t ph[4], pl[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const bf16_t h0 = f32_to_bf16(v[2 * j]), h1 = f32_to_bf16(v[2 * j + 1]);
-        const bf16_t l0 = f32_to_bf16(v[2 * j] - bf16_to_f32(h0)), l1 = f32_to_bf16(v[2 * j + 1] - bf16_to_f32(h1));
-        ph[j] = (uint32_t)h0 | ((uint32_t)h1 << 16);
-        pl[j] = (uint32_t)l0 | ((uint32_t)l1 << 16);
+        ph[j] = pack_bf16x2(v[2 * j], v[2 * j + 1]);
+        pl[j] = pack_bf16x2(v[2 * j] - __uint_as_float(ph[j] << 16), v[2 * j + 1] - __uint_as_float(ph[j] & 0xffff0000u));
       }
       *hi = __builtin_bit_cast(bf16x8, make_uint4(ph[0], ph[1], ph[2], ph[3]));
       *lo = __builtin_bit_cast(bf16x8, make_uint4(pl[0], pl[1], pl[2], pl[3]));
@@ -517,29 +518,15 @@ __global__ __launch_bounds__(256, 2) void k_sparse_attn_mfma(AttnArgs a) {
     for (int b = 0; b < DB; ++b)
 #pragma unroll
       for (int r = 0; r < 16; ++r) cacc[b][r] = x[b][r] + fb[32 * b + (r & 3) + 8 * (r >> 2) + 4 * half];
-    const float* fw = a.fitW + (long long)bh * D * a.R;
-    const float* fv = a.fitV + (long long)bh * D * a.R;
-    for (int j0 = 0; j0 < rank; j0 += 32) {
-      const int nj = min(32, rank - j0);
-      __syncthreads();
-      for (int e = tid; e < D * 32; e += 256) {
-        const int dm = e >> 5, j = e & 31;
-        const float wv = j < nj ? fw[(long long)dm * a.R + j0 + j] : 0.f;
-        const float vv = j < nj ? fv[(long long)dm * a.R + j0 + j] : 0.f;
-        const bf16_t wh = f32_to_bf16(wv), vh = f32_to_bf16(vv);
-        Wh[j * WLD + dm] = wh;
-        Wlo[j * WLD + dm] = f32_to_bf16(wv - bf16_to_f32(wh));
-        Vh[dm * VLD + j] = vh;
-        Vlo[dm * VLD + j] = f32_to_bf16(vv - bf16_to_f32(vh));
-      }
-      __syncthreads();
-      if (owner) {
+    for (int j0 = 0; j0 < rank && owner; j0 += 32) {
+      {
         // T^T = W^T X^T: A = rows of W^T (rank col, dims 16 ks + 8 half ..)
         f32x16 t = f32x16{};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-          const bf16x8 ah = *reinterpret_cast<const bf16x8*>(Wh + col * WLD + 16 * ks + 8 * half);
-          const bf16x8 al = *reinterpret_cast<const bf16x8*>(Wlo + col * WLD + 16 * ks + 8 * half);
+          const long long wo = (long long)(j0 + col) * D + 16 * ks + 8 * half;
+          const bf16x8 ah = *reinterpret_cast<const bf16x8*>(Wh + wo);
+          const bf16x8 al = *reinterpret_cast<const bf16x8*>(Wlo + wo);
           t = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, xh[ks], t, 0, 0, 0);
           t = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, xh[ks], t, 0, 0, 0);
           t = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, xl[ks], t, 0, 0, 0);
@@ -555,8 +542,9 @@ __global__ __launch_bounds__(256, 2) void k_sparse_attn_mfma(AttnArgs a) {
         for (int b = 0; b < DB; ++b)
 #pragma unroll
           for (int kr = 0; kr < 2; ++kr) {
-            const bf16x8 vh = *reinterpret_cast<const bf16x8*>(Vh + (32 * b + col) * VLD + 16 * kr + 8 * half);
-            const bf16x8 vl = *reinterpret_cast<const bf16x8*>(Vlo + (32 * b + col) * VLD + 16 * kr + 8 * half);
+            const long long vo = (long long)(32 * b + col) * Rp + j0 + 16 * kr + 8 * half;
+            const bf16x8 vh = *reinterpret_cast<const bf16x8*>(Vh + vo);
+            const bf16x8 vl = *reinterpret_cast<const bf16x8*>(Vlo + vo);
             cacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vh, th[kr], cacc[b], 0, 0, 0);
             cacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vl, th[kr], cacc[b], 0, 0, 0);
             cacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vh, tl[kr], cacc[b], 0, 0, 0);
@@ -578,10 +566,34 @@ __global__ __launch_bounds__(256, 2) void k_sparse_attn_mfma(AttnArgs a) {
     for (int r4 = 0; r4 < 4; ++r4) {
       const int dm = 32 * b + 8 * r4 + 4 * half;
       uint2 pk;
-      pk.x = (uint32_t)f32_to_bf16(x[b][4 * r4 + 0]) | ((uint32_t)f32_to_bf16(x[b][4 * r4 + 1]) << 16);
-      pk.y = (uint32_t)f32_to_bf16(x[b][4 * r4 + 2]) | ((uint32_t)f32_to_bf16(x[b][4 * r4 + 3]) << 16);
+      pk.x = pack_bf16x2(x[b][4 * r4 + 0], x[b][4 * r4 + 1]);
+      pk.y = pack_bf16x2(x[b][4 * r4 + 2], x[b][4 * r4 + 3]);
       *reinterpret_cast<uint2*>(orow + dm) = pk;
     }
+}
+
+// hi/lo bf16 copies of each head's fitted maps in the layouts the MFMA
+// correction reads its A fragments in: W^T [Rp][D] and V [D][Rp], rank
+// columns at or past the head's rank set to zero.
+__global__ __launch_bounds__(256) void k_fit_pack(const float* fitW, const float* fitV, const int* fitrank, int D,
+                                                  int R, int Rp, bf16_t* pk) {
+  const int bh = blockIdx.x;
+  const int rank = fitrank[bh];
+  bf16_t* wh = pk + (long long)bh * 4 * Rp * D;
+  bf16_t* wl = wh + (long long)Rp * D;
+  bf16_t* vh = wl + (long long)Rp * D;
+  bf16_t* vl = vh + (long long)Rp * D;
+  for (int e = threadIdx.x; e < D * Rp; e += 256) {
+    const int dm = e / Rp, j = e - (e / Rp) * Rp;
+    const bool in = j < rank && j < R;
+    const float wv = in ? fitW[((long long)bh * D + dm) * R + j] : 0.f;
+    const float vv = in ? fitV[((long long)bh * D + dm) * R + j] : 0.f;
+    const bf16_t w0 = f32_to_bf16(wv), v0 = f32_to_bf16(vv);
+    wh[(long long)j * D + dm] = w0;
+    wl[(long long)j * D + dm] = f32_to_bf16(wv - bf16_to_f32(w0));
+    vh[(long long)dm * Rp + j] = v0;
+    vl[(long long)dm * Rp + j] = f32_to_bf16(vv - bf16_to_f32(v0));
+  }
 }
 
 // ============================================================================
@@ -1100,6 +1112,8 @@ static AttnArgs attn_args(const Plan& p, bool correct) {
   a.fitV = p.fitV;
   a.fitb = p.fitb;
   a.fitrank = p.fitrank;
+  a.fitpk = p.fitpk;
+  a.Rp = p.Rp;
   a.R = p.R > 0 ? p.R : 1;
   a.N = p.N;
   a.GK = p.GK;
@@ -1134,6 +1148,11 @@ static hipError_t launch_attn(AttnArgs a, int grid_x, int BH, int d, int dtype, 
 
 hipError_t launch_sparse_attention(const Plan& p, bool correct, hipStream_t s) {
   AttnArgs a = attn_args(p, correct);
+  if (a.correct && p.dtype == SPARSEPR_BF16) {
+    hipLaunchKernelGGL(k_fit_pack, dim3(p.BH), dim3(256), 0, s, p.fitW, p.fitV, p.fitrank, p.d, a.R, p.Rp, p.fitpk);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   return launch_attn(a, p.max_tiles, p.BH, p.d, p.dtype, s);
 }
 

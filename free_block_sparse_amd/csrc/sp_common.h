@@ -34,6 +34,14 @@ __host__ __device__ inline bf16_t f32_to_bf16(float f) {
   return static_cast<bf16_t>(c.u >> 16);
 }
 
+// Two fp32 values rounded to nearest-even bf16 and packed (the first in the
+// low half): one v_cvt_pk_bf16_f32 on gfx950, the same rounding as f32_to_bf16.
+__device__ inline uint32_t pack_bf16x2(float a, float b) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){a, b}, bf16x2_t));
+}
+
 template <typename T> struct Elem;
 template <> struct Elem<float> {
   __device__ static inline float load(const float* p) { return *p; }

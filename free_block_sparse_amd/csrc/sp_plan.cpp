@@ -187,6 +187,8 @@ void plan_carve(Plan* p, char* base) {
   p->fitV = c.take<float>(BH * d * R);
   p->fitb = c.take<float>(BH * d);
   p->fitrank = c.take<int>(BH);
+  p->Rp = (int)((R + 31) / 32 * 32);
+  p->fitpk = c.take<bf16_t>(BH * 4 * p->Rp * d);
   p->fitscratch = c.take<double>(BH * kFitScratchDoubles);
   p->stats = c.take<sparsepr_head_stats>(BH);
   p->ws_bytes = (c.off + 255) & ~(size_t)255;

@@ -91,6 +91,8 @@ struct Plan {
   float* fitV;            // [BH, d, R]
   float* fitb;            // [BH, d]
   int* fitrank;           // [BH]
+  int Rp;                 // R rounded up to 32 (at least 32)
+  bf16_t* fitpk;          // [BH, 4, Rp * d] bf16: W^T hi, W^T lo ([Rp, d]), V hi, V lo ([d, Rp])
   double* fitscratch;     // [BH, kFitScratchDoubles]
   sparsepr_head_stats* stats;  // [BH]
 
