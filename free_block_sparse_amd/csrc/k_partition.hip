@@ -334,18 +334,15 @@ __global__ __launch_bounds__(256) void k_key_coords_mfma(CoordArgs a) {
       for (int q = 0; q < 4; ++q) {
         const int c = 32 * cb + 8 * q + 4 * half;  // coordinates c..c+3 of token n
         if (c >= rKpad) continue;
-        float4 zf;
-        bf16_t hv[4], lv[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float x = acc[4 * q + i];
-          (&zf.x)[i] = x;
-          hv[i] = f32_to_bf16(x);
-          lv[i] = f32_to_bf16(x - bf16_to_f32(hv[i]));
-        }
+        const float4 zf = make_float4(acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]);
+        uint2 hp, lp;
+        hp.x = pack_bf16x2(zf.x, zf.y);
+        hp.y = pack_bf16x2(zf.z, zf.w);
+        lp.x = pack_bf16x2(zf.x - __uint_as_float(hp.x << 16), zf.y - __uint_as_float(hp.x & 0xffff0000u));
+        lp.y = pack_bf16x2(zf.z - __uint_as_float(hp.y << 16), zf.w - __uint_as_float(hp.y & 0xffff0000u));
         *reinterpret_cast<float4*>(a.z32 + zrow + c) = zf;
-        *reinterpret_cast<uint2*>(a.zhi + zrow + c) = *reinterpret_cast<const uint2*>(hv);
-        *reinterpret_cast<uint2*>(a.zlo + zrow + c) = *reinterpret_cast<const uint2*>(lv);
+        *reinterpret_cast<uint2*>(a.zhi + zrow + c) = hp;
+        *reinterpret_cast<uint2*>(a.zlo + zrow + c) = lp;
       }
     }
   }
