@@ -78,8 +78,8 @@ CASES = {
 
 # Degenerate settings and random seeds (tests/test_gpu_edge_cases.py): one
 # group on each side, no probes, rank 0, mandatory cells only (over budget),
-# fewer tokens than one tile, more than 64 probes, and seeds with many small
-# cells and split tiles.
+# fewer tokens than one tile, more than 64 probes, a residual rank above 32,
+# and seeds with many small cells and split tiles.
 EDGE_CASES = {
     "one_group": Case("one_group", 2, 8, 20, 1, 64, "bf16", 1, 1, 0.3, 16, 4, seed=31),
     "no_probes": Case("no_probes", 2, 8, 20, 1, 64, "bf16", 6, 5, 0.3, 0, 4, seed=32),
@@ -90,6 +90,9 @@ EDGE_CASES = {
     # and M = 200 > d = 64 (the primal d x d system)
     "probes128": Case("probes128", 2, 16, 32, 1, 128, "bf16", 16, 4, 0.3, 128, 16, seed=36),
     "probes200_d64": Case("probes200_d64", 2, 16, 32, 1, 64, "bf16", 16, 8, 0.3, 200, 16, seed=37),
+    # residual rank 48 > 32: the correction runs over a second, partial block
+    # of 32 rank columns (the rest of it zero)
+    "rank48": Case("rank48", 2, 16, 32, 1, 128, "bf16", 16, 8, 0.3, 64, 48, seed=38),
     **{f"seed{s}": Case(f"seed{s}", 2, 10, 20, 2, 64 if s % 2 else 128, "bf16", 10, 6, 0.25, 16, 4, seed=40 + s)
        for s in range(6)},
 }
