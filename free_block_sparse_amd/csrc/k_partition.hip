@@ -51,7 +51,7 @@ __global__ __launch_bounds__(256) void k_sample_metric(SampleArgs a) {
   const int Ms = a.Ms, N = a.N;
   int t = 0;
   if (tid < Ms) {
-    uint64_t z = (a.seed ^ ((uint64_t)bh * kGolden64)) + (uint64_t)(tid + 1) * kGolden64;
+    uint64_t z = (a.seed ^ ((uint64_t)(bh + a.bh0) * kGolden64)) + (uint64_t)(tid + 1) * kGolden64;
     z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
     z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
     z ^= z >> 31;
@@ -1134,7 +1134,7 @@ static long long resident_slots(const void* fn, int threads) {
 }
 
 hipError_t launch_sample_metric(const Plan& p, hipStream_t s) {
-  SampleArgs a{p.q, p.N, p.Ms, p.seed, p.sample, p.mk};
+  SampleArgs a{p.q, p.N, p.Ms, p.bh0, p.seed, p.sample, p.mk};
   if (p.dtype == SPARSEPR_BF16) {
     if (p.d == 128) SP_LAUNCH((k_sample_metric<bf16_t, 128>), dim3(p.BH), dim3(256), s, a);
     else SP_LAUNCH((k_sample_metric<bf16_t, 64>), dim3(p.BH), dim3(256), s, a);

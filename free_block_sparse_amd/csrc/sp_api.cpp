@@ -2,6 +2,9 @@
 // stream.  The host never synchronises and never reads device data.
 #include <string.h>
 
+#include <map>
+#include <mutex>
+
 #include "sp_kernels.h"
 
 using namespace sp;
@@ -162,14 +165,18 @@ sparsepr_status raw_means(Plan& p, const View4& raw, const int* perm, const int*
   return SPARSEPR_OK;
 }
 
-sparsepr_status run_partition(Plan& p, hipStream_t s, Stager* st = nullptr) {
+// after_eig (optional) is recorded once the key eigensolve is enqueued (at the
+// start in the independent mode, which has none)
+sparsepr_status run_partition(Plan& p, hipStream_t s, Stager* st = nullptr, hipEvent_t after_eig = nullptr) {
   const bool rcp = p.mode == SPARSEPR_PART_RESPONSE_COUPLED;
   SPCHK(mark(st, -1));
+  if (after_eig && !rcp) HIPCHK(hipEventRecord(after_eig, s));
   if (rcp) {
     HIPCHK(launch_sample_metric(p, s));
     SPCHK(mark(st, SPARSEPR_STAGE_SAMPLE_METRIC));
     HIPCHK(launch_key_eig(p, s));
     SPCHK(mark(st, SPARSEPR_STAGE_KEY_EIGEN));
+    if (after_eig) HIPCHK(hipEventRecord(after_eig, s));
     HIPCHK(launch_key_coords(p, s));
     SPCHK(mark(st, SPARSEPR_STAGE_KEY_COORDS));
   }
@@ -231,6 +238,54 @@ sparsepr_status copy_out(T* dst, const T* src, long long count, hipStream_t s) {
 }
 
 // copy a [BH, G+1] offsets array (all the same stride) out
+
+// The main call runs its heads in two halves (B = 1, H >= 2): the second half
+// on a second stream, so that one half's latency-bound stages (eigensolve,
+// router selection, fit: one workgroup per head) overlap the other half's
+// throughput-bound kernels.  Every head is an independent problem; only the
+// query sample's seed names the head, and it takes the global index (bh0).
+// Returns the first half's head count, 0 for no split.
+int split_heads(int B, int H) { return (B == 1 && H >= 2) ? H / 2 : 0; }
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Per-device side stream (default priority) and fork/join events, created on
+// first use and kept for the life of the process.  The mutex is held while a
+// call enqueues its fork-to-join sequence, so that concurrent calls on one
+// device cannot interleave records of the shared events.
+struct SideRes {
+  hipStream_t s;
+  hipEvent_t fork, join;
+};
+std::mutex g_side_mu;
+
+sparsepr_status side_resources(SideRes* out) {
+  static std::map<int, SideRes> res;
+  int dev = 0;
+  HIPCHK(hipGetDevice(&dev));
+  auto it = res.find(dev);
+  if (it == res.end()) {
+    SideRes r;
+    HIPCHK(hipStreamCreateWithFlags(&r.s, hipStreamNonBlocking));
+    HIPCHK(hipEventCreateWithFlags(&r.fork, hipEventDisableTiming));
+    HIPCHK(hipEventCreateWithFlags(&r.join, hipEventDisableTiming));
+    it = res.emplace(dev, r).first;
+  }
+  *out = it->second;
+  return SPARSEPR_OK;
+}
+
+// workspace of the split call: both halves' plans, 256-byte aligned
+sparsepr_status split_ws_bytes(const sparsepr_config* cfg, int B, int H, int N, int d, int dtype, int h1,
+                               size_t* bytes) {
+  Plan a, b;
+  SPCHK(plan_init(&a, cfg, B, h1, N, d, dtype));
+  plan_carve(&a, nullptr);
+  SPCHK(plan_init(&b, cfg, B, H - h1, N, d, dtype));
+  plan_carve(&b, nullptr);
+  *bytes = align256(a.ws_bytes) + b.ws_bytes;
+  return SPARSEPR_OK;
+}
 }  // namespace
 
 extern "C" {
@@ -272,16 +327,61 @@ sparsepr_status sparsepr_workspace_size(const sparsepr_config* cfg, int B, int H
   SPCHK(plan_init(&p, cfg, B, H, N, d, dtype));
   plan_carve(&p, nullptr);
   *bytes = p.ws_bytes;
+  // the main call splits its heads; the stage entry points use one plan
+  const int h1 = split_heads(B, H);
+  if (h1) {
+    size_t sb = 0;
+    SPCHK(split_ws_bytes(cfg, B, H, N, d, dtype, h1, &sb));
+    if (sb > *bytes) *bytes = sb;
+  }
   return SPARSEPR_OK;
 }
 
 sparsepr_status sparsepr_attention(const sparsepr_config* cfg, const sparsepr_tensors* io, void* workspace,
                                    size_t workspace_bytes, void* stream, sparsepr_head_stats* stats) {
-  Plan p;
-  SPCHK(prepare(p, cfg, io, workspace, workspace_bytes));
   hipStream_t s = static_cast<hipStream_t>(stream);
-  SPCHK(run_partition(p, s));
-  return run_after_partition(p, s, stats);
+  const int h1 = io ? split_heads(io->B, io->H) : 0;
+  if (!h1) {
+    Plan p;
+    SPCHK(prepare(p, cfg, io, workspace, workspace_bytes));
+    SPCHK(run_partition(p, s));
+    return run_after_partition(p, s, stats);
+  }
+  // the whole call is validated first, so errors are those of the unsplit call
+  {
+    Plan pf;
+    SPCHK(prepare(pf, cfg, io, workspace, workspace_bytes));
+  }
+  size_t need = 0;
+  SPCHK(split_ws_bytes(cfg, io->B, io->H, io->N, io->d, io->dtype, h1, &need));
+  if (workspace_bytes < need) return SPARSEPR_ERR_WORKSPACE;
+  sparsepr_tensors io1 = *io, io2 = *io;
+  io1.H = h1;
+  io2.H = io->H - h1;
+  const long long es = io->dtype == SPARSEPR_BF16 ? 2 : 4;
+  io2.q = static_cast<const char*>(io->q) + h1 * io->q_strides[1] * es;
+  io2.k = static_cast<const char*>(io->k) + h1 * io->k_strides[1] * es;
+  io2.v = static_cast<const char*>(io->v) + h1 * io->v_strides[1] * es;
+  io2.o = static_cast<char*>(io->o) + h1 * io->o_strides[1] * es;
+  Plan p1, p2;
+  SPCHK(prepare(p1, cfg, &io1, workspace, workspace_bytes));
+  const size_t off2 = align256(p1.ws_bytes);
+  SPCHK(prepare(p2, cfg, &io2, static_cast<char*>(workspace) + off2, workspace_bytes - off2));
+  p2.bh0 = h1;
+  std::lock_guard<std::mutex> lk(g_side_mu);
+  SideRes r;
+  SPCHK(side_resources(&r));
+  // the second half starts once the first half's eigensolve is done, so
+  // that the halves' latency-bound stages fall on each other's
+  // throughput-bound ones instead of on each other
+  SPCHK(run_partition(p1, s, nullptr, r.fork));
+  HIPCHK(hipStreamWaitEvent(r.s, r.fork, 0));
+  SPCHK(run_after_partition(p1, s, stats));
+  SPCHK(run_partition(p2, r.s));
+  SPCHK(run_after_partition(p2, r.s, stats ? stats + h1 : nullptr));
+  HIPCHK(hipEventRecord(r.join, r.s));
+  HIPCHK(hipStreamWaitEvent(s, r.join, 0));
+  return SPARSEPR_OK;
 }
 
 sparsepr_status sparsepr_attention_profile(const sparsepr_config* cfg, const sparsepr_tensors* io,

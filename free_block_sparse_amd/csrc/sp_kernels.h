@@ -8,6 +8,7 @@ namespace sp {
 struct SampleArgs {
   View4 q;
   int N, Ms;
+  int bh0;  // global index of head 0 of the launch
   unsigned long long seed;
   int* sample;
   float* mk;

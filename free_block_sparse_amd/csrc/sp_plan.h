@@ -20,6 +20,7 @@ constexpr long long kFitScratchDoubles = 7LL * 128 * 128;  // per (b,h) fit scra
 struct Plan {
   // shape and settings
   int B, H, BH, N, d, dtype, esize;
+  int bh0;  // index of this plan's first head in the caller's call (seeds the query sample)
   int GK, GQ, Gmax, M, R, Ms, rK, rKpad, T, mode;
   int Dk;            // key-side k-means point dimension (padded to 16)
   int ridge_mode;

@@ -151,14 +151,23 @@ sparsepr_status sparsepr_config_default(int N, int d, sparsepr_config* out);
 sparsepr_status sparsepr_validate(const sparsepr_config* cfg, int B, int H, int N, int d, int dtype);
 
 /* Bytes of workspace every entry point below needs for this shape (256-byte
-   aligned base required). */
+   aligned base required; with B = 1 and H >= 2 it covers both halves of
+   sparsepr_attention). */
 sparsepr_status sparsepr_workspace_size(const sparsepr_config* cfg, int B, int H, int N, int d,
                                         int dtype, size_t* bytes);
 
 /* The full call ([NE] NE/exec latency chain: partition construction, routing,
    tensor reorder, sparse attention, exact probe rows, residual fit,
    correction, output restoration).  Writes o in the original token order.
-   `stats` (device pointer, nullable) receives B*H sparsepr_head_stats. */
+   `stats` (device pointer, nullable) receives B*H sparsepr_head_stats.
+   With B = 1 and H >= 2 the heads run in two halves: the second half on a
+   stream the library keeps per device (created on first use, default
+   priority), forked from `stream` once the first half's key eigensolve is
+   enqueued and joined back to `stream` with an event before the call
+   returns.  Work enqueued on `stream` after the call therefore sees the whole
+   output, and the fork and join are recorded by HIP graph capture of
+   `stream` like any other work.  The result is the same as the unsplit
+   call's.  Concurrent calls on one device serialise only their enqueueing. */
 sparsepr_status sparsepr_attention(const sparsepr_config* cfg, const sparsepr_tensors* io,
                                    void* workspace, size_t workspace_bytes, void* stream,
                                    sparsepr_head_stats* stats);
