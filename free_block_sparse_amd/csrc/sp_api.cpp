@@ -340,7 +340,15 @@ sparsepr_status sparsepr_workspace_size(const sparsepr_config* cfg, int B, int H
 sparsepr_status sparsepr_attention(const sparsepr_config* cfg, const sparsepr_tensors* io, void* workspace,
                                    size_t workspace_bytes, void* stream, sparsepr_head_stats* stats) {
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const int h1 = io ? split_heads(io->B, io->H) : 0;
+  int h1 = io ? split_heads(io->B, io->H) : 0;
+  if (h1 && s) {
+    // the second stream lives on the current device: split only when the
+    // caller's stream does too
+    int cur = 0, sdev = 0;
+    HIPCHK(hipGetDevice(&cur));
+    HIPCHK(hipStreamGetDevice(s, &sdev));
+    if (sdev != cur) h1 = 0;
+  }
   if (!h1) {
     Plan p;
     SPCHK(prepare(p, cfg, io, workspace, workspace_bytes));
