@@ -13,7 +13,7 @@ import pytest
 import torch
 
 import free_block_sparse_amd as sp
-from parity_cases import (CASES, inputs, max_abs, oracle_key_labels_from_metric, oracle_out_given_partition,
+from parity_cases import (CASES, case, inputs, max_abs, oracle_key_labels_from_metric, oracle_out_given_partition,
                           oracle_query_labels_given_keys, oracle_result, rel_frob, tolerances)
 
 pytestmark = pytest.mark.gpu
@@ -285,3 +285,23 @@ def test_full_density_is_dense_attention():
     for h, r in enumerate(oracle_result(name)):
         got = out[0, h].double().cpu().numpy()
         assert max_abs(got, r["dense"]) <= ma and rel_frob(got, r["dense"]) <= rf
+
+
+def test_two_stream_call_equals_one_stream():
+    """The main call runs its heads in two halves on two streams (B = 1).  With
+    three heads (halves of 1 and 2) its output and statistics must equal,
+    bit for bit, those of the profiling entry point, which runs every head on
+    one stream: the second half's query sample is seeded by its global head
+    index and its tensors are addressed at the right head offset."""
+    from synth.generator import make_video_qkv
+
+    c = case("bf16_d64")
+    x = make_video_qkv(c.frames, c.height, c.width, 3, c.d, c.dtype, c.seed, [c.f90] * 3)
+    q, k, v = (x[t].cuda() for t in ("q", "k", "v"))
+    cfg = sp.make_config(c.n, c.d, **c.lib_cfg_kwargs())
+    ws = sp.Workspace()
+    out_two, st_two = sp.sparsepr_attention(q, k, v, cfg, workspace=ws, with_stats=True)
+    out_one, _, st_one = sp.sparsepr_attention_profile(q, k, v, cfg, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(out_two.view(torch.int16), out_one.view(torch.int16))
+    assert torch.equal(st_two, st_one)
