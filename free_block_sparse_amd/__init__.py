@@ -31,6 +31,7 @@ __all__ = [
     "sparsepr_attention_with_partition", "sparsepr_key_metric", "sparsepr_partition", "sparsepr_route",
     "sparsepr_sparse_attention", "sparsepr_probe_fit", "sparsepr_dense_attention", "make_config",
     "stats_to_dicts", "SparseprConfig", "SparsePRError", "sparsepr_attention_profile", "Workspace",
+    "sparsepr_mfma_rounding_check",
 ]
 
 
@@ -200,10 +201,10 @@ def sparsepr_key_metric(q, k, v, cfg, workspace=None, stream=None):
     io = _tensors(q, k, v, dummy_o)
     buf, nbytes = _ws(cfg, q, workspace)
     smp = torch.empty(B * H, ms, dtype=torch.int32, device=q.device)
-    mk = torch.empty(B * H, d, d, dtype=torch.float32, device=q.device)
-    ev = torch.empty(B * H, d, dtype=torch.float32, device=q.device)
+    mk = torch.empty(B * H, d, d, dtype=torch.float64, device=q.device)
+    ev = torch.empty(B * H, d, dtype=torch.float64, device=q.device)
     rk = min(cfg.key_coord_rank, d, ms)
-    km = torch.empty(B * H, d, rk, dtype=torch.float32, device=q.device)
+    km = torch.empty(B * H, d, rk, dtype=torch.float64, device=q.device)
     check(lib().sparsepr_key_metric(ctypes.byref(cfg), ctypes.byref(io), buf.data_ptr(), nbytes,
                                     _stream(stream), smp.data_ptr(), mk.data_ptr(), ev.data_ptr(),
                                     km.data_ptr()),
@@ -297,4 +298,17 @@ def sparsepr_dense_attention(q, k, v, out=None, scale: float = 0.0, stream=None)
     io = _tensors(q, k, v, out)
     check(lib().sparsepr_dense_attention(ctypes.byref(io), float(scale), _stream(stream)),
           "sparsepr_dense_attention")
+    return out
+
+
+def sparsepr_mfma_rounding_check(patterns, stream=None):
+    """Element (0, 0) of one bf16 32x32x16 matrix-core product per pattern.
+
+    patterns: device float32 [n, 33] (16 values of row 0 of A, 16 of column 0
+    of B, exact in bf16, then the accumulator).  Returns device float32 [n]."""
+    torch = _torch()
+    pats = patterns.to(torch.float32).contiguous()
+    out = torch.empty(pats.shape[0], dtype=torch.float32, device=pats.device)
+    check(lib().sparsepr_mfma_rounding_check(pats.data_ptr(), int(pats.shape[0]), out.data_ptr(), _stream(stream)),
+          "sparsepr_mfma_rounding_check")
     return out

@@ -78,7 +78,7 @@ class SparseprHeadStats(ctypes.Structure):
         ("residual_rank", ctypes.c_int),
         ("over_budget", ctypes.c_int),
         ("q_tiles", ctypes.c_int),
-        ("reserved", ctypes.c_int),
+        ("kmeans_redecided", ctypes.c_int),
         ("rho_route", ctypes.c_double),
         ("rho_exec", ctypes.c_double),
         ("sigma", ctypes.c_double * 4),
@@ -113,6 +113,7 @@ _SIGS = {
     "sparsepr_probe_fit": (_I, [ctypes.POINTER(SparseprConfig), ctypes.POINTER(SparseprTensors), _P, _P, _P,
                                 ctypes.c_size_t, _P, _P, _P, _P, _P, _P, _P, _P]),
     "sparsepr_dense_attention": (_I, [ctypes.POINTER(SparseprTensors), ctypes.c_float, _P]),
+    "sparsepr_mfma_rounding_check": (_I, [_P, ctypes.c_int, _P, _P]),
     "sparsepr_attention_profile": (_I, [ctypes.POINTER(SparseprConfig), ctypes.POINTER(SparseprTensors), _P,
                                         ctypes.c_size_t, _P, _P, ctypes.POINTER(ctypes.c_float)]),
     "sparsepr_status_string": (ctypes.c_char_p, [_I]),

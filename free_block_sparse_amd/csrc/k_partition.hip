@@ -27,7 +27,7 @@
 namespace sp {
 
 // ============================================================================
-// a1: query sample (partial Fisher-Yates on splitmix64) and M_K
+// a1: query sample (partial Fisher-Yates on splitmix64) and M_K (fp64)
 // ============================================================================
 // Step j of the partial shuffle swaps slot j with slot t_j = j + (x_j mod
 // (N - j)), where x_j is the generator's j-th output; the draws do not depend
@@ -38,16 +38,12 @@ namespace sp {
 // latest earlier step with the same target, and the value slot j held is
 // found by following "latest earlier step aiming at slot j" links to a step
 // with none; the links are followed by pointer jumping.
-template <typename T, int D>
-__global__ __launch_bounds__(256) void k_sample_metric(SampleArgs a) {
+__global__ __launch_bounds__(256) void k_query_sample(SampleArgs a) {
   const int bh = blockIdx.x, tid = threadIdx.x;
   __shared__ int tgt[256];
   __shared__ int held[256];  // value slot j held when step j ran
   __shared__ int lnk[256];
   __shared__ int srt[256];
-  constexpr int QLD = 256 + 8;  // samples per dimension row (+8: 16-byte rows off the bank stride)
-  __shared__ __align__(16) bf16_t qt[std::is_same<T, bf16_t>::value ? D * QLD : 8];
-  __shared__ float qs[std::is_same<T, bf16_t>::value ? 1 : 64][D + 1];
   const int Ms = a.Ms, N = a.N;
   int t = 0;
   if (tid < Ms) {
@@ -95,97 +91,86 @@ __global__ __launch_bounds__(256) void k_sample_metric(SampleArgs a) {
     }
   }
   if (tid < Ms) a.sample[(long long)bh * Ms + tid] = srt[tid];
+}
 
-  const float inv = 1.0f / (float)Ms;
-  float* mk = a.mk + (long long)bh * D * D;
-  const T* qbase = static_cast<const T*>(a.q.p);
-  if constexpr (std::is_same<T, bf16_t>::value) {
-    // bf16 rows: M_K on the matrix cores.  The sampled rows are staged
-    // transposed (dimension-major, samples zero-padded to a multiple of 16),
-    // so both MFMA operands are 16-byte LDS reads; bf16 products are exact
-    // and accumulate in fp32.
-    const int Mp = (Ms + 15) & ~15;
-    constexpr int CPR = D / 8;  // 16-byte pieces per row
-    for (int e = tid; e < Mp * CPR; e += 256) {
-      const int c = (e / Mp) * 8, r = e - (e / Mp) * Mp;  // consecutive threads: consecutive samples
-      uint4 u = make_uint4(0, 0, 0, 0);
-      if (r < Ms) u = *reinterpret_cast<const uint4*>(qbase + a.q.row_off(bh, srt[r]) + c);
-      const bf16_t* ev = reinterpret_cast<const bf16_t*>(&u);
+// M_K = Q_s^T Q_s / M_s in fp64 (a d x d block per (b,h), 4 x 4 outputs per
+// thread).  The sampled rows are staged 64 at a time as fp32 (bf16 and fp32
+// inputs are exact there); products of two fp32 values are exact in fp64, so
+// only the additions round.
+template <typename T, int D>
+__global__ __launch_bounds__(1024) void k_key_metric64(SampleArgs a) {
+  constexpr int LDQ = D + 4;  // 16-byte rows
+  __shared__ __align__(16) float qs[64][LDQ];
+  __shared__ int smp[256];
+  const int bh = blockIdx.x, tid = threadIdx.x;
+  const int Ms = a.Ms;
+  if (tid < Ms) smp[tid] = a.sample[(long long)bh * Ms + tid];
+  constexpr int NB = D / 4;  // 4 x 4 blocks per side
+  const int bi = tid / NB, bj = tid - (tid / NB) * NB;
+  const bool act = bi < NB;
+  double acc[4][4];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) qt[(c + j) * QLD + r] = ev[j];
+  for (int x = 0; x < 4; ++x)
+#pragma unroll
+    for (int y = 0; y < 4; ++y) acc[x][y] = 0.0;
+  const T* qbase = static_cast<const T*>(a.q.p);
+  constexpr int VEC = 16 / sizeof(T);
+  for (int c0 = 0; c0 < Ms; c0 += 64) {
+    const int nr = min(64, Ms - c0);
+    __syncthreads();
+    for (int e = tid; e < nr * (D / VEC); e += 1024) {
+      const int r = e / (D / VEC), c = (e - r * (D / VEC)) * VEC;
+      const uint4 u = *reinterpret_cast<const uint4*>(qbase + a.q.row_off(bh, smp[c0 + r]) + c);
+      const T* ev = reinterpret_cast<const T*>(&u);
+#pragma unroll
+      for (int j = 0; j < VEC; ++j) qs[r][c + j] = Elem<T>::load(ev + j);
     }
     __syncthreads();
-    const int w = tid >> 6, lane = tid & 63, half = lane >> 5, col = lane & 31;
-    constexpr int NB = D / 32;  // 32 x 32 output blocks per side
-    for (int blk = w; blk < NB * NB; blk += 4) {
-      const int bi = blk / NB, bj = blk - (blk / NB) * NB;
-      f32x16 acc = {};
-      for (int k0 = 0; k0 < Mp; k0 += 16) {
-        const bf16x8 av = *reinterpret_cast<const bf16x8*>(qt + (32 * bi + col) * QLD + k0 + 8 * half);
-        const bf16x8 bv = *reinterpret_cast<const bf16x8*>(qt + (32 * bj + col) * QLD + k0 + 8 * half);
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, acc, 0, 0, 0);
-      }
-      // D[i][j]: j = lane % 32, i = (r & 3) + 8 (r >> 2) + 4 (lane / 32)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int i = (r & 3) + 8 * (r >> 2) + 4 * half;
-        mk[(32 * bi + i) * D + 32 * bj + col] = acc[r] * inv;
-      }
-    }
-  } else {
-    constexpr int TB = D / 16;
-    const int i0 = (tid >> 4) * TB, j0 = (tid & 15) * TB;
-    float acc[TB][TB];
-#pragma unroll
-    for (int x = 0; x < TB; ++x)
-#pragma unroll
-      for (int y = 0; y < TB; ++y) acc[x][y] = 0.f;
-    for (int c0 = 0; c0 < Ms; c0 += 64) {
-      const int nr = min(64, Ms - c0);
-      __syncthreads();
-      for (int e = tid; e < nr * D; e += 256) {
-        const int r = e / D, col = e - (e / D) * D;
-        qs[r][col] = Elem<T>::load(qbase + a.q.row_off(bh, srt[c0 + r]) + col);
-      }
-      __syncthreads();
+    if (act)
       for (int r = 0; r < nr; ++r) {
-        float xi[TB], xj[TB];
+        const float4 u = *reinterpret_cast<const float4*>(&qs[r][4 * bi]);
+        const float4 v = *reinterpret_cast<const float4*>(&qs[r][4 * bj]);
+        const double uu[4] = {u.x, u.y, u.z, u.w}, vv[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-        for (int t2 = 0; t2 < TB; ++t2) {
-          xi[t2] = qs[r][i0 + t2];
-          xj[t2] = qs[r][j0 + t2];
-        }
+        for (int x = 0; x < 4; ++x)
 #pragma unroll
-        for (int x = 0; x < TB; ++x)
-#pragma unroll
-          for (int y = 0; y < TB; ++y) acc[x][y] += xi[x] * xj[y];
+          for (int y = 0; y < 4; ++y) acc[x][y] = __builtin_fma(uu[x], vv[y], acc[x][y]);
       }
-    }
-#pragma unroll
-    for (int x = 0; x < TB; ++x)
-#pragma unroll
-      for (int y = 0; y < TB; ++y) mk[(i0 + x) * D + j0 + y] = acc[x][y] * inv;
   }
+  if (!act) return;
+  double* mk = a.mk + (long long)bh * D * D;
+#pragma unroll
+  for (int x = 0; x < 4; ++x)
+#pragma unroll
+    for (int y = 0; y < 4; ++y) mk[(4 * bi + x) * D + 4 * bj + y] = acc[x][y] / (double)Ms;
 }
 
 // ============================================================================
 // a2: symmetric eigensolver for M_K (one workgroup per (b,h), all in LDS)
 // ============================================================================
+// The metric is held in LDS in fp64 (132 KB at d = 128) for the reduction to
+// tridiagonal form.  The same LDS then holds the reflectors (column-major,
+// packed) behind the eigenvectors of the tridiagonal matrix (the leading rK
+// and the factorisation scratch, odd row stride); the shifted-QR fallback, and
+// ranks above 32, keep their eigenvector matrix in the workspace.
 template <int D>
 __global__ __launch_bounds__(1024) void k_key_eig(EigArgs a) {
   constexpr int LD = D + 1;  // odd row stride: column walks hit distinct banks
   constexpr int NT = 1024;
-  __shared__ float A[D * LD];
-  __shared__ float Z[D * LD];
-  __shared__ float dg[D + 2], eo[D + 2], tau[D], vb[D], pb[D];
-  __shared__ float rot[4 * D];
+  constexpr int RKL = 32;    // largest rK whose vectors share the LDS with the reflectors
+  constexpr int NPK = D * (D - 1) / 2;
+  constexpr int NA = D * LD > D * (2 * RKL + 1) + NPK ? D * LD : D * (2 * RKL + 1) + NPK;
+  constexpr int PER = D * D / NT;
+  __shared__ double A[NA];
+  __shared__ double dg[D + 2], eo[D + 2], tau[D], vb[D], pb[D];
+  __shared__ double rot[4 * D];
   __shared__ int ctl[8];
   __shared__ int top[D];
-  __shared__ float lamv[D];  // eigenvalue of column i of Z
+  __shared__ double lamv[D];  // eigenvalue of column i of Z
   const int bh = blockIdx.x, tid = threadIdx.x;
-  const float* mk = a.mk + (long long)bh * D * D;
+  const double* mk = a.mk + (long long)bh * D * D;
   {
-    float t[D * D / NT];
+    double t[D * D / NT];
 #pragma unroll
     for (int u = 0; u < D * D / NT; ++u) t[u] = mk[tid + NT * u];
 #pragma unroll
@@ -195,27 +180,50 @@ __global__ __launch_bounds__(1024) void k_key_eig(EigArgs a) {
     }
   }
   __syncthreads();
-  const EigWork<float> w{A, LD, Z, LD, dg, eo, tau, vb, pb, rot, ctl};
-  eig_tridiagonalize<float, NT>(w, D);
-  // every eigenvalue by multisection (all of them are reported), vectors
-  // of the leading rK by twisted factorisations; shifted QR when two of the
-  // leading eigenvalues cannot be told apart
-  eig_bisect<float, NT>(w, D, D);
+  const EigWork<double> w{A, LD, nullptr, 0, dg, eo, tau, vb, pb, rot, ctl};
+  eig_tridiagonalize<double, NT>(w, D);
+  // every eigenvalue by multisection (all of them are reported)
+  eig_bisect<double, NT>(w, D, D);
   for (int i = tid; i < D; i += NT) lamv[i] = rot[D + i];
+  // reflectors: column-major packed, through registers, behind the vector block
+  const bool lds_vecs = a.rK <= RKL;
+  const int zl = lds_vecs ? 2 * a.rK + 1 : D;
+  double* Rp = A + D * (2 * RKL + 1);
+  {
+    // element (r, c), r > c, goes to c (D - 1) - c (c - 1) / 2 + r - c - 1
+    double t[PER];
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int e = tid + NT * u, r = e / D, c = e - (e / D) * D;
+      t[u] = r > c ? A[r * LD + c] : 0.0;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int e = tid + NT * u, r = e / D, c = e - (e / D) * D;
+      if (r > c) Rp[c * (D - 1) - (c * (c - 1)) / 2 + r - c - 1] = t[u];
+    }
+  }
   __syncthreads();
-  if (eig_twisted<float, NT>(w, D, a.rK)) {
+  double* Z = lds_vecs ? A : a.eigz + (long long)bh * D * D;
+  EigWork<double> wz{nullptr, 0, Z, zl, dg, eo, tau, vb, pb, rot, ctl};
+  if (eig_twisted<double, NT>(wz, D, a.rK)) {
     for (int i = tid; i < D; i += NT) {
       if (a.eigval) a.eigval[(long long)bh * D + i] = lamv[i];
       if (i < a.rK) top[i] = i;
     }
   } else {
-    eig_tridiagonal_qr<float, NT>(w, D);
+    // shifted QR over the whole tridiagonal matrix, vectors in the workspace
+    Z = a.eigz + (long long)bh * D * D;
+    wz.Z = Z;
+    wz.ldz = D;
+    eig_tridiagonal_qr<double, NT>(wz, D);
     // rank eigenvalues (descending, ties by index)
     for (int i = tid; i < D; i += NT) {
-      const float li = dg[i];
+      const double li = dg[i];
       int rank = 0;
       for (int j = 0; j < D; ++j) {
-        const float lj = dg[j];
+        const double lj = dg[j];
         rank += (lj > li) || (lj == li && j < i);
       }
       if (a.eigval) a.eigval[(long long)bh * D + rank] = li;
@@ -224,126 +232,175 @@ __global__ __launch_bounds__(1024) void k_key_eig(EigArgs a) {
     }
   }
   __syncthreads();
-  eig_back_transform<float, NT, 32>(w, D, top, a.rK);
-  // coordinate map: column k of kmap = s sqrt(lambda_k) u_k
-  float* km = a.kmap + (long long)bh * D * a.rK;
-  for (int e = tid; e < D * a.rK; e += NT) {
-    const int r = e / D, k = e - (e / D) * D;
-    const int i = top[r];
-    const float f = a.scale * sqrtf(fmaxf(lamv[i], 0.f));
-    km[k * a.rK + r] = f * Z[k * LD + i];
+  eig_back_transform_packed<double, NT, 32>(wz, Rp, D, top, a.rK);
+  // coordinate map: column k of kmap = s sqrt(lambda_k) u_k (also zero-padded
+  // to rKpad columns)
+  double* km = a.kmap + (long long)bh * D * a.rK;
+  double* kp = a.kmap_pad + (long long)bh * D * a.rKpad;
+  for (int e = tid; e < D * a.rKpad; e += NT) {
+    const int k = e / a.rKpad, r = e - (e / a.rKpad) * a.rKpad;
+    double v = 0.0;
+    if (r < a.rK) {
+      const int i = top[r];
+      v = (double)a.scale * sqrt(fmax(lamv[i], 0.0)) * Z[k * wz.ldz + i];
+      km[k * a.rK + r] = v;
+    }
+    kp[e] = v;
   }
 }
 
 // ============================================================================
-// a3: key-response coordinates z = K kmap (fp32), stored also as hi/lo bf16
+// a3: key-response coordinates z = K kmap in fp64, kept also as a hi/lo bf16
+// pair of its fp32 rounding (the k-means assignment's operands)
 // ============================================================================
-template <typename T, int D>
-__global__ __launch_bounds__(256) void k_key_coords(CoordArgs a) {
-  __shared__ float km[D][64];
-  __shared__ float kr[64][D + 1];
+// One key per thread, 256 keys per workgroup staged through LDS with
+// coalesced loads.  The map (zero-padded to RP columns) is the same for every
+// lane, so its entries are wave-uniform loads that feed the fp64 FMAs as
+// scalar operands.  Inputs are exact in fp32, so every product is exact in
+// fp64.
+template <typename T, int D, int RP>
+__global__ __launch_bounds__(256) void k_key_coords64(CoordArgs a) {
+  constexpr int CH = 32;                      // dims per staged chunk
+  constexpr int KL = CH + 4 / (int)sizeof(T);  // row stride: an odd number of 4-byte words
+  constexpr int VEC = 16 / sizeof(T), PPR = CH / VEC, NP = 256 * PPR / 256;
+  __shared__ __align__(16) T kr[256 * KL];
   const int bh = blockIdx.y, tid = threadIdx.x;
-  const int n0 = blockIdx.x * 64;
-  const int rK = a.rK, rKpad = a.rKpad, N = a.N;
-  const float* kmap = a.kmap + (long long)bh * D * rK;
-  for (int e = tid; e < D * rK; e += 256) km[e / rK][e % rK] = kmap[e];
+  const int n0 = blockIdx.x * 256, N = a.N;
   const T* kb = static_cast<const T*>(a.k.p);
-  constexpr int VEC = 16 / sizeof(T);
-  for (int e = tid; e < 64 * (D / VEC); e += 256) {
-    const int r = e / (D / VEC), c = (e - (e / (D / VEC)) * (D / VEC)) * VEC;
-    const int n = n0 + r;
-    uint4 u = make_uint4(0, 0, 0, 0);
-    if (n < N) u = *reinterpret_cast<const uint4*>(kb + a.k.row_off(bh, n) + c);
-    const T* ev = reinterpret_cast<const T*>(&u);
+  const double* km = a.kmap_pad + (long long)bh * D * RP;
+  double acc[RP];
 #pragma unroll
-    for (int j = 0; j < VEC; ++j) kr[r][c + j] = n < N ? Elem<T>::load(ev + j) : 0.f;
+  for (int r = 0; r < RP; ++r) acc[r] = 0.0;
+  const T* row = kr + tid * KL;
+  for (int c0 = 0; c0 < D; c0 += CH) {
+    uint4 u[NP];
+#pragma unroll
+    for (int q = 0; q < NP; ++q) {
+      const int e = tid + 256 * q, r = e / PPR, c = (e - r * PPR) * VEC;
+      u[q] = make_uint4(0, 0, 0, 0);
+      if (n0 + r < N) u[q] = *reinterpret_cast<const uint4*>(kb + a.k.row_off(bh, n0 + r) + c0 + c);
+    }
+    __syncthreads();  // the previous chunk's readers are done
+#pragma unroll
+    for (int q = 0; q < NP; ++q) {
+      const int e = tid + 256 * q, r = e / PPR, c = (e - r * PPR) * VEC;
+      uint32_t* dst = reinterpret_cast<uint32_t*>(kr + r * KL + c);
+      dst[0] = u[q].x;
+      dst[1] = u[q].y;
+      dst[2] = u[q].z;
+      dst[3] = u[q].w;
+    }
+    __syncthreads();
+    for (int c = 0; c < CH; ++c) {
+      const double x = (double)Elem<T>::load(row + c);
+#pragma unroll
+      for (int r = 0; r < RP; ++r) acc[r] = __builtin_fma(x, km[(c0 + c) * RP + r], acc[r]);
+    }
   }
-  __syncthreads();
-  const int r = tid >> 2;
-  const int n = n0 + r;
+  const int n = n0 + tid;
   if (n >= N) return;
-  const long long zrow = (long long)bh * N + n;
-  for (int j = tid & 3; j < rKpad; j += 4) {
-    float acc = 0.f;
-    if (j < rK)
-      for (int c = 0; c < D; ++c) acc += kr[r][c] * km[c][j];
-    a.z32[zrow * rKpad + j] = acc;
-    const bf16_t hi = f32_to_bf16(acc);
-    a.zhi[zrow * rKpad + j] = hi;
-    a.zlo[zrow * rKpad + j] = f32_to_bf16(acc - bf16_to_f32(hi));
+  const long long zrow = ((long long)bh * N + n) * RP;
+  double res2 = 0.0, lo2 = 0.0;  // |z - hi - lo|^2 and |lo|^2 of the split pair
+#pragma unroll
+  for (int r = 0; r < RP; r += 8) {
+    uint32_t hw[4], lw[4];
+#pragma unroll
+    for (int j = 0; j < 8; j += 2) {
+      const float f0 = (float)acc[r + j], f1 = (float)acc[r + j + 1];
+      hw[j >> 1] = pack_bf16x2(f0, f1);
+      lw[j >> 1] = pack_bf16x2(f0 - __uint_as_float(hw[j >> 1] << 16), f1 - __uint_as_float(hw[j >> 1] & 0xffff0000u));
+      const double l0 = (double)__uint_as_float(lw[j >> 1] << 16), l1 = (double)__uint_as_float(lw[j >> 1] & 0xffff0000u);
+      const double e0 = (acc[r + j] - (double)__uint_as_float(hw[j >> 1] << 16)) - l0;
+      const double e1 = (acc[r + j + 1] - (double)__uint_as_float(hw[j >> 1] & 0xffff0000u)) - l1;
+      res2 = __builtin_fma(e0, e0, __builtin_fma(e1, e1, res2));
+      lo2 = __builtin_fma(l0, l0, __builtin_fma(l1, l1, lo2));
+    }
+#pragma unroll
+    for (int j = 0; j < 8; j += 2)
+      *reinterpret_cast<double2*>(a.z64 + zrow + r + j) = make_double2(acc[r + j], acc[r + j + 1]);
+    *reinterpret_cast<uint4*>(a.zhi + zrow + r) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+    *reinterpret_cast<uint4*>(a.zlo + zrow + r) = make_uint4(lw[0], lw[1], lw[2], lw[3]);
   }
+  // fp32 upper bounds (the relative margin covers the fp64 roundings above)
+  a.xbound[(long long)bh * N + n] = make_float2((float)(sqrt(res2) * (1.0 + 0x1p-20)), (float)(sqrt(lo2) * (1.0 + 0x1p-20)));
 }
 
-// bf16 keys on the matrix cores: z^T = kmap^T K^T with kmap split into three
-// bf16 pieces (24 significant bits, like fp32); products with bf16 keys are
-// exact and accumulate in fp32.  Each wave takes 32-token blocks; lanes hold
-// the map as the A operand for up to two blocks of 32 coordinates.
-template <int D, int NCB>
-__global__ __launch_bounds__(256) void k_key_coords_mfma(CoordArgs a) {
-  constexpr int KS = D / 16;
-  const int bh = blockIdx.y, tid = threadIdx.x;
-  const int w = tid >> 6, lane = tid & 63, half = lane >> 5, col = lane & 31;
-  const int rK = a.rK, rKpad = a.rKpad, N = a.N;
-  const int ncb = (rK + 31) / 32;
-  const float* kmap = a.kmap + (long long)bh * D * rK;
-  bf16x8 mp[3][NCB][KS];  // NCB 32-coordinate blocks (r_K <= 32 NCB)
+// fp64 matrix-core form for rKpad <= 32: v_mfma_f64_16x16x4f64 over 16-key
+// tiles.  Lane layout (A 16x4, B 4x16, D 16x16): A[i][k] in lane i + 16k,
+// B[k][j] in lane j + 16k, D[i][j] in lane 16 (i % 4) + j, register i / 4.
+// Each wave keeps the whole map as B fragments in registers (d/4 k-steps x
+// RP/16 column tiles) and stages 16 keys at a time in its own LDS slice.
+template <typename T, int D, int RP>
+__global__ __launch_bounds__(256) void k_key_coords_f64mfma(CoordArgs a) {
+  typedef double f64x4_t __attribute__((ext_vector_type(4)));
+  constexpr int KS = D / 4, NJ = RP / 16, KT = 4, KL = D + 4;
+  constexpr int VEC = 16 / sizeof(T), PPR = D / VEC;
+  __shared__ float kr[4][16 * KL];
+  const int bh = blockIdx.y, tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int N = a.N;
+  const int li = lane & 15, lk = lane >> 4;
+  const double* km = a.kmap_pad + (long long)bh * D * RP;
+  double bfr[KS][NJ];
 #pragma unroll
-  for (int cb = 0; cb < NCB; ++cb)
+  for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+    for (int t = 0; t < NJ; ++t) bfr[ks][t] = km[(4 * ks + lk) * RP + 16 * t + li];
+  const T* kb = static_cast<const T*>(a.k.p);
+  float* my = kr[w];
+  for (int kt = 0; kt < KT; ++kt) {
+    const int key0 = (blockIdx.x * 4 + w) * (16 * KT) + 16 * kt;
+    if (key0 >= N) break;  // uniform per wave
+    // stage the tile's 16 rows (the wave's own slice: order its writes before its reads)
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    for (int e = lane; e < 16 * PPR; e += 64) {
+      const int r = e / PPR, c = (e - r * PPR) * VEC;
+      uint4 u = make_uint4(0, 0, 0, 0);
+      if (key0 + r < N) u = *reinterpret_cast<const uint4*>(kb + a.k.row_off(bh, key0 + r) + c);
+      const T* ev = reinterpret_cast<const T*>(&u);
+#pragma unroll
+      for (int j = 0; j < VEC; ++j) my[r * KL + c + j] = Elem<T>::load(ev + j);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    f64x4_t acc[NJ];
+#pragma unroll
+    for (int t = 0; t < NJ; ++t) acc[t] = f64x4_t{0.0, 0.0, 0.0, 0.0};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      bf16_t pv[3][8];
-      const int cc = 32 * cb + col;
+      const double av = (double)my[li * KL + 4 * ks + lk];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        float x = (cb < ncb && cc < rK) ? kmap[(16 * ks + 8 * half + j) * rK + cc] : 0.f;
+      for (int t = 0; t < NJ; ++t) acc[t] = __builtin_amdgcn_mfma_f64_16x16x4f64(av, bfr[ks][t], acc[t], 0, 0, 0);
+    }
+    // lane holds keys key0 + 4 r + lk (r < 4), coordinate 16 t + li
 #pragma unroll
-        for (int q = 0; q < 3; ++q) {
-          pv[q][j] = f32_to_bf16(x);
-          x -= bf16_to_f32(pv[q][j]);
+    for (int r = 0; r < 4; ++r) {
+      const int n = key0 + 4 * r + lk;
+      double res2 = 0.0, lo2 = 0.0;
+#pragma unroll
+      for (int t = 0; t < NJ; ++t) {
+        const double z = acc[t][r];
+        const float zf = (float)z;
+        const bf16_t hi = f32_to_bf16(zf);
+        const bf16_t lo = f32_to_bf16(zf - bf16_to_f32(hi));
+        const double e = (z - (double)bf16_to_f32(hi)) - (double)bf16_to_f32(lo);
+        res2 = __builtin_fma(e, e, res2);
+        lo2 = __builtin_fma((double)bf16_to_f32(lo), (double)bf16_to_f32(lo), lo2);
+        if (n < N) {
+          const long long o = ((long long)bh * N + n) * RP + 16 * t + li;
+          a.z64[o] = z;
+          a.zhi[o] = hi;
+          a.zlo[o] = lo;
         }
       }
-#pragma unroll
-      for (int q = 0; q < 3; ++q) mp[q][cb][ks] = *reinterpret_cast<const bf16x8*>(pv[q]);
-    }
-  const bf16_t* kb = static_cast<const bf16_t*>(a.k.p);
-  // each wave covers 8 consecutive 32-token blocks (the map fragments above
-  // are built once per wave)
-  for (int blk = 0; blk < 8; ++blk) {
-    const int n0 = blockIdx.x * 1024 + 256 * w + 32 * blk;
-    if (n0 >= N) break;
-    const int n = n0 + col;
-    bf16x8 kf[KS];
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      uint4 u = make_uint4(0, 0, 0, 0);
-      if (n < N) u = *reinterpret_cast<const uint4*>(kb + a.k.row_off(bh, n) + 16 * ks + 8 * half);
-      kf[ks] = __builtin_bit_cast(bf16x8, u);
-    }
-#pragma unroll
-    for (int cb = 0; cb < NCB; ++cb) {
-      if (cb >= ncb) break;
-      f32x16 acc = {};
-      // smallest pieces first
-#pragma unroll
-      for (int q = 2; q >= 0; --q)
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(mp[q][cb][ks], kf[ks], acc, 0, 0, 0);
-      if (n >= N) continue;
-      const long long zrow = ((long long)bh * N + n) * rKpad;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int c = 32 * cb + 8 * q + 4 * half;  // coordinates c..c+3 of token n
-        if (c >= rKpad) continue;
-        const float4 zf = make_float4(acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]);
-        uint2 hp, lp;
-        hp.x = pack_bf16x2(zf.x, zf.y);
-        hp.y = pack_bf16x2(zf.z, zf.w);
-        lp.x = pack_bf16x2(zf.x - __uint_as_float(hp.x << 16), zf.y - __uint_as_float(hp.x & 0xffff0000u));
-        lp.y = pack_bf16x2(zf.z - __uint_as_float(hp.y << 16), zf.w - __uint_as_float(hp.y & 0xffff0000u));
-        *reinterpret_cast<float4*>(a.z32 + zrow + c) = zf;
-        *reinterpret_cast<uint2*>(a.zhi + zrow + c) = hp;
-        *reinterpret_cast<uint2*>(a.zlo + zrow + c) = lp;
+      for (int o = 8; o > 0; o >>= 1) {
+        res2 += __shfl_xor(res2, o, 16);
+        lo2 += __shfl_xor(lo2, o, 16);
       }
+      if (li == 0 && n < N)
+        a.xbound[(long long)bh * N + n] = make_float2((float)(sqrt(res2) * (1.0 + 0x1p-20)), (float)(sqrt(lo2) * (1.0 + 0x1p-20)));
     }
   }
 }
@@ -369,28 +426,156 @@ __global__ __launch_bounds__(256) void k_split_rows(SplitArgs a) {
 // B[k][n]: k = 8*(lane/32)+j, n = lane%32; D[i][j]: j = lane%32,
 // i = (r%4) + 8*(r/4) + 4*(lane/32) for accumulator register r.
 // ============================================================================
-// Largest of the 16 accumulator values a lane holds for a 32-centre block
-// (register r belongs to centre (r&3) + 8(r>>2) + 4*half, increasing in r).
-// Pairwise tree (depth 4); on ties the lower register, i.e. the lower centre
-// index, is kept.  Returns the value and writes the register index.
-__device__ inline float block_argmax16(const f32x16& acc, int* ridx) {
-  float v[16];
-  int id[16];
+// Largest three of the 16 accumulator values a lane holds for a 32-centre
+// block.  Each value first carries its register index r in the low 4 bits of
+// its mantissa (a change below 2^-19 of its magnitude, which the error bound
+// includes), so plain max/min/median operations keep track of which centre a
+// value belongs to: register r is centre (r & 3) + 8 (r >> 2) + 4 (lane / 32)
+// of the block.  Pairs are split into (larger, smaller), pairs merge into
+// sorted triples, and triples merge as the largest three of two sorted lists.
+// Padding centres carry a large negative but finite bias, so no value is
+// infinite and no packed value is a NaN.
+__device__ inline float pack_reg(float v, int r) {
+  return __uint_as_float((__float_as_uint(v) & ~0xfu) | (uint32_t)r);
+}
+__device__ inline int packed_centre(float v, int base) {
+  const int r = (int)(__float_as_uint(v) & 0xfu);
+  return base + (r & 3) + 8 * (r >> 2);
+}
+struct Top3 {
+  float t1, t2, t3;
+};
+// the largest three of two sorted triples
+__device__ inline Top3 merge_top3(const Top3& a, const Top3& b) {
+  Top3 t;
+  t.t1 = fmaxf(a.t1, b.t1);
+  t.t2 = __builtin_amdgcn_fmed3f(a.t1, b.t1, fmaxf(a.t2, b.t2));
+  t.t3 = fmaxf(fmaxf(a.t3, b.t3), fmaxf(fminf(a.t2, b.t1), fminf(a.t1, b.t2)));
+  return t;
+}
+__device__ inline Top3 block_top3_16(const f32x16& acc) {
+  Top3 q[4];
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    v[r] = acc[r];
-    id[r] = r;
+  for (int k = 0; k < 4; ++k) {
+    const float p0 = pack_reg(acc[4 * k], 4 * k), p1 = pack_reg(acc[4 * k + 1], 4 * k + 1);
+    const float p2 = pack_reg(acc[4 * k + 2], 4 * k + 2), p3 = pack_reg(acc[4 * k + 3], 4 * k + 3);
+    const float h0 = fmaxf(p0, p1), l0 = fminf(p0, p1), h1 = fmaxf(p2, p3), l1 = fminf(p2, p3);
+    const float ml = fmaxf(l0, l1);
+    q[k].t1 = fmaxf(h0, h1);
+    q[k].t2 = __builtin_amdgcn_fmed3f(h0, h1, ml);
+    q[k].t3 = fminf(ml, fminf(h0, h1));
   }
+  return merge_top3(merge_top3(q[0], q[1]), merge_top3(q[2], q[3]));
+}
+
+// A point's running state: the largest three packed values over the centres
+// seen so far and the centres of the first two.
+struct Best3 {
+  float b, s, t;
+  int bi, si;
+};
+__device__ inline Best3 best3_init() { return Best3{-INFINITY, -INFINITY, -INFINITY, 0, 0}; }
+// fold in three more sorted values whose first two belong to centres i1, i2
+// (equal values keep the earlier state's centre first)
+__device__ inline void best3_add(Best3& st, float v1, float v2, float v3, int i1, int i2) {
+  const float nt = fmaxf(fmaxf(st.t, v3), fmaxf(fminf(st.s, v1), fminf(st.b, v2)));
+  if (v1 > st.b) {
+    const bool keep = st.b >= v2;
+    st.s = keep ? st.b : v2;
+    st.si = keep ? st.bi : i2;
+    st.b = v1;
+    st.bi = i1;
+  } else {
+    const bool keep = st.s >= v1;
+    st.s = keep ? st.s : v1;
+    st.si = keep ? st.si : i1;
+  }
+  st.t = nt;
+}
+__device__ inline void best3_add_block(Best3& st, const f32x16& acc, int base) {
+  const Top3 t = block_top3_16(acc);
+  best3_add(st, t.t1, t.t2, t.t3, packed_centre(t.t1, base), packed_centre(t.t2, base));
+}
+// merge with the state of lane ^ 32 (the other half of the same point's centres)
+__device__ inline void best3_merge_halves(Best3& st) {
+  const float ob = __shfl_xor(st.b, 32, 64), os = __shfl_xor(st.s, 32, 64), ot = __shfl_xor(st.t, 32, 64);
+  const int obi = __shfl_xor(st.bi, 32, 64), osi = __shfl_xor(st.si, 32, 64);
+  if ((threadIdx.x & 63) < 32) {
+    best3_add(st, ob, os, ot, obi, osi);
+  } else {
+    Best3 o{ob, os, ot, obi, osi};
+    best3_add(o, st.b, st.s, st.t, st.bi, st.si);
+    st = o;
+  }
+}
+
+// Sum of squares of 8 bf16 values (exact products, fp32 sums).
+__device__ inline float sumsq_bf16x8(const u32x4& v) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  float t = 0.f;
 #pragma unroll
-  for (int w = 1; w < 16; w <<= 1)
-#pragma unroll
-    for (int r = 0; r < 16; r += 2 * w) {
-      const bool right = v[r + w] > v[r];
-      v[r] = right ? v[r + w] : v[r];
-      id[r] = right ? id[r + w] : id[r];
-    }
-  *ridx = id[0];
-  return v[0];
+  for (int j = 0; j < 4; ++j) {
+    const bf16x2_t u = __builtin_bit_cast(bf16x2_t, v[j]);
+    t = __builtin_amdgcn_fdot2_f32_bf16(u, u, t, false);
+  }
+  return t;
+}
+
+// Largest bound of |y_g|, |c_g| and of the split residual |y_g - hi_g - lo_g|
+// over the G centres of (b,h); every lane of the calling wave gets them.
+struct CentreBounds {
+  float y, c, r, l;
+};
+__device__ inline CentreBounds centre_bounds(const AssignArgs& a, int bh) {
+  const float4* yb = reinterpret_cast<const float4*>(a.ybound) + (long long)bh * a.gstride;
+  float ym = 0.f, cm = 0.f, rm = 0.f, lm = 0.f;
+  for (int g = threadIdx.x & 63; g < a.G; g += 64) {
+    const float4 b = yb[g];
+    ym = fmaxf(ym, b.x);
+    cm = fmaxf(cm, b.y);
+    rm = fmaxf(rm, b.z);
+    lm = fmaxf(lm, b.w);
+  }
+  return CentreBounds{wave_max(ym), wave_max(cm), wave_max(rm), wave_max(lm)};
+}
+
+// Wave 0 of the workgroup reduces the bounds into `sb` (visible to the other
+// waves after the caller's next workgroup barrier).
+__device__ inline void centre_bounds_to_lds(const AssignArgs& a, int bh, CentreBounds* sb) {
+  if ((threadIdx.x >> 6) != 0) return;
+  const CentreBounds cb = centre_bounds(a, bh);
+  if (threadIdx.x == 0) *sb = cb;
+}
+
+// Error bound of a point's approximate values x~.y~_g - c~_g/2 against the
+// exact x.y_g - c_g/2, given the bound xn of |x~|:
+//   |y~ - y| |x~| + |y| |x~ - x| + |y_lo| |x_lo| + accumulation error,
+// with |x~ - x| and |x_lo| from the point's own split (xb) when known, else
+// eps_x |x~| for both.
+__device__ inline float value_bound(const AssignArgs& a, const CentreBounds& cb, float xn, float2 xb) {
+  const float xs = a.xbound ? xb.x * cb.y + xb.y * cb.l : xn * a.eps_x * cb.y;
+  // the register index packed into the low mantissa bits moves a value by
+  // less than 2^-19 of its magnitude, itself at most |x~||y| + |c|/2
+  return 1.01f * (xn * cb.r + xs + (a.eps_acc + 0x1p-19f) * (xn * cb.y + 0.5f * cb.c));
+}
+
+// A point whose best and second values lie within twice the error bound e
+// of each other is a near tie: it goes to the flag list of (b,h) with its
+// two candidates, and with full = 1 when the third value is within 2e of the
+// best as well (then every centre must be re-decided).  One counter update
+// per wave; every lane of the wave must call it.
+__device__ inline void flag_append(const AssignArgs& a, int bh, bool live, const Best3& st, float e, int n) {
+  const bool flag = live && st.b - st.s <= 2.0f * e;
+  const unsigned long long m = __builtin_amdgcn_ballot_w64(flag);
+  if (m == 0ull) return;
+  const int lane = threadIdx.x & 63;
+  const int leader = __builtin_ctzll(m);
+  int base = 0;
+  if (lane == leader) base = atomicAdd(a.fcnt + (long long)bh * a.fcstride, __builtin_popcountll(m));
+  base = __shfl(base, leader, 64);
+  const int slot = base + __builtin_popcountll(m & ((1ull << lane) - 1ull));
+  if (flag && slot < a.N)
+    a.flist[(long long)bh * a.N + slot] = make_int4(n, st.bi, st.si, st.b - st.t <= 2.0f * e ? 1 : 0);
 }
 
 template <int D>
@@ -414,6 +599,7 @@ __global__ __launch_bounds__(512) void k_kmeans_assign(AssignArgs a) {
   __shared__ __attribute__((aligned(16))) bf16_t sh[256 * LDI];
   __shared__ __attribute__((aligned(16))) bf16_t sl[256 * LDI];
   __shared__ __attribute__((aligned(16))) float sbias[256];
+  __shared__ CentreBounds sbound;
   const int bh = blockIdx.y, tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   const int half = lane >> 5, col = lane & 31;
   const int N = a.N, G = a.G, G32 = (G + 31) & ~31;
@@ -453,10 +639,12 @@ __global__ __launch_bounds__(512) void k_kmeans_assign(AssignArgs a) {
         }
       }
     }
+    centre_bounds_to_lds(a, bh, &sbound);
     // -c_g / 2, the accumulators' start (centres past G never win)
-    for (int e = tid; e < G32; e += NT) sbias[e] = e < G ? -0.5f * a.ybias[(long long)bh * a.gstride + e] : -INFINITY;
+    for (int e = tid; e < G32; e += NT) sbias[e] = e < G ? -0.5f * a.ybias[(long long)bh * a.gstride + e] : -0x1p126f;
   }
   __syncthreads();
+  const CentreBounds cbd = sbound;
 
   const bf16_t* pbase = static_cast<const bf16_t*>(a.pts.p) + a.pts.row_off(bh, 0);
   const long long psn = a.pts.sn;
@@ -475,12 +663,14 @@ __global__ __launch_bounds__(512) void k_kmeans_assign(AssignArgs a) {
   for (int b = w; b < nblk; b += NW) {
     u32x4 nh[PB][KS];
     SP_LOAD_BLOCK(min(b + NW, nblk - 1), nh)
-    float best[PB];
-    int bidx[PB];
+    Best3 st[PB];
+    float xsq[PB];
 #pragma unroll
     for (int pb = 0; pb < PB; ++pb) {
-      best[pb] = -INFINITY;
-      bidx[pb] = 0;
+      st[pb] = best3_init();
+      xsq[pb] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) xsq[pb] += sumsq_bf16x8(ph[pb][ks]);
     }
     for (int cb = 0; cb < G32; cb += 32) {
       // -c_g / 2 of this lane's centres: four runs of four consecutive centres
@@ -509,24 +699,19 @@ __global__ __launch_bounds__(512) void k_kmeans_assign(AssignArgs a) {
         }
       }
 #pragma unroll
-      for (int pb = 0; pb < PB; ++pb) {
-        int rr;
-        const float sc = block_argmax16(acc[pb], &rr);
-        if (sc > best[pb]) {
-          best[pb] = sc;
-          bidx[pb] = cb + (rr & 3) + 8 * (rr >> 2) + 4 * half;
-        }
-      }
+      for (int pb = 0; pb < PB; ++pb) best3_add_block(st[pb], acc[pb], cb + 4 * half);
     }
 #pragma unroll
     for (int pb = 0; pb < PB; ++pb) {
-      const float ob = __shfl_xor(best[pb], 32, 64);
-      const int oi = __shfl_xor(bidx[pb], 32, 64);
-      if (ob > best[pb] || (ob == best[pb] && oi < bidx[pb])) bidx[pb] = oi;
+      best3_merge_halves(st[pb]);
+      const float x2 = xsq[pb] + __shfl_xor(xsq[pb], 32, 64);
+      const float e = value_bound(a, cbd, sqrtf(x2) * (1.0f + 0x1p-12f), make_float2(0.f, 0.f));
       const int n = n_begin + BP * b + 32 * pb + col;
-      if (half == 0 && n < n_end) {
-        a.labels[(long long)bh * N + n] = bidx[pb];
-        atomicAdd(cnt + (long long)(n / kChunk) * a.gstride + bidx[pb], 1);
+      const bool live = half == 0 && n < n_end;
+      flag_append(a, bh, live, st[pb], e, n);
+      if (live) {
+        a.labels[(long long)bh * N + n] = st[pb].bi;
+        atomicAdd(cnt + (long long)(n / kChunk) * a.gstride + st[pb].bi, 1);
       }
     }
 #pragma unroll
@@ -538,7 +723,7 @@ __global__ __launch_bounds__(512) void k_kmeans_assign(AssignArgs a) {
 }
 
 template <int D, bool LO, int CG>
-__global__ __launch_bounds__(512, 4) void k_kmeans_assign_staged(AssignArgs a) {
+__global__ __launch_bounds__(512, (LO && D >= 64) ? 2 : 4) void k_kmeans_assign_staged(AssignArgs a) {
   // General form (any D, any G <= kMaxGroups).  One 256-point histogram chunk per
   // workgroup (8 waves x one 32-point MFMA column, points held as B operands
   // in registers); the centre images are staged through LDS CG at a time
@@ -552,6 +737,7 @@ __global__ __launch_bounds__(512, 4) void k_kmeans_assign_staged(AssignArgs a) {
   __shared__ __attribute__((aligned(16))) bf16_t sl[CG * LDI];
   __shared__ __attribute__((aligned(16))) float sbias[CG];
   __shared__ int hist[kMaxGroups];
+  __shared__ CentreBounds sbound;
   const int bh = blockIdx.y, blk = blockIdx.x;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int N = a.N, G = a.G;
@@ -574,8 +760,11 @@ __global__ __launch_bounds__(512, 4) void k_kmeans_assign_staged(AssignArgs a) {
     ph[ks] = __builtin_bit_cast(bf16x8, v);
     if (LO) pl[LO ? ks : 0] = __builtin_bit_cast(bf16x8, w);
   }
-  float best = -INFINITY;
-  int bidx = 0;
+  Best3 st = best3_init();
+  float xsq = 0.f;
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) xsq += sumsq_bf16x8(__builtin_bit_cast(u32x4, ph[ks]));
+  centre_bounds_to_lds(a, bh, &sbound);
   const bf16_t* yh = a.yhi + (long long)bh * a.gstride * a.ystride;
   const bf16_t* yl = a.ylo + (long long)bh * a.gstride * a.ystride;
   const float* yb = a.ybias + (long long)bh * a.gstride;
@@ -592,7 +781,7 @@ __global__ __launch_bounds__(512, 4) void k_kmeans_assign_staged(AssignArgs a) {
       *reinterpret_cast<uint4*>(sh + r * LDI + cc * 8) = vh;
       *reinterpret_cast<uint4*>(sl + r * LDI + cc * 8) = vl;
     }
-    for (int e = tid; e < CG; e += NT) sbias[e] = (c0 + e < G) ? -0.5f * yb[c0 + e] : -INFINITY;
+    for (int e = tid; e < CG; e += NT) sbias[e] = (c0 + e < G) ? -0.5f * yb[c0 + e] : -0x1p126f;
     __syncthreads();
     const int nblk = min(CG, G - c0);
     // two 32-centre blocks at a time: independent accumulator chains
@@ -630,37 +819,168 @@ __global__ __launch_bounds__(512, 4) void k_kmeans_assign_staged(AssignArgs a) {
           acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah1, pl[LO ? ks : 0], acc1, 0, 0, 0);
         }
       }
-      int rr;
-      float sc = block_argmax16(acc0, &rr);
-      if (sc > best) {
-        best = sc;
-        bidx = c0 + cb + (rr & 3) + 8 * (rr >> 2) + 4 * half;
-      }
-      if (two) {
-        sc = block_argmax16(acc1, &rr);
-        if (sc > best) {
-          best = sc;
-          bidx = c0 + cb + 32 + (rr & 3) + 8 * (rr >> 2) + 4 * half;
-        }
-      }
+      best3_add_block(st, acc0, c0 + cb + 4 * half);
+      if (two) best3_add_block(st, acc1, c0 + cb + 32 + 4 * half);
     }
   }
+  best3_merge_halves(st);
   {
-    const float ob = __shfl_xor(best, 32, 64);
-    const int oi = __shfl_xor(bidx, 32, 64);
-    if (ob > best || (ob == best && oi < bidx)) {
-      best = ob;
-      bidx = oi;
-    }
+    const CentreBounds cbd = sbound;  // written before the staging barriers
+    // split points: |x~| <= |x_hi| (1 + 2^-7)
+    const float x2 = xsq + __shfl_xor(xsq, 32, 64);
+    const float2 xb = (a.xbound && n < N) ? a.xbound[(long long)bh * N + n] : make_float2(0.f, 0.f);
+    const float e = value_bound(a, cbd, sqrtf(x2) * (LO ? 1.0f + 0x1p-7f : 1.0f + 0x1p-12f), xb);
+    flag_append(a, bh, half == 0 && n < N, st, e, n);
   }
   __syncthreads();
   if (half == 0 && n < N) {
-    a.labels[(long long)bh * N + n] = bidx;
-    atomicAdd(&hist[bidx], 1);
+    a.labels[(long long)bh * N + n] = st.bi;
+    atomicAdd(&hist[st.bi], 1);
   }
   __syncthreads();
   int* cnt = a.counts + ((long long)bh * a.nchunk + blk) * a.gstride;
   for (int g = tid; g < G; g += NT) cnt[g] = hist[g];
+}
+
+// Exact re-decision of the points a Lloyd step flagged as near ties.  The
+// values x . y_g - c_g / 2 are computed in fp64 from the exact point row (raw
+// row, or the fp64 key coordinates) and the fp64 images; the largest is kept,
+// ties to the lower centre.  When only the point's two candidates are within
+// twice the error bound of its best value, every other centre is provably
+// below both and the two dot products decide: one wave per such point, lanes
+// over dimensions, row-major images.  The rare points with a third centre in
+// range are then re-decided over every centre by a whole workgroup (one
+// centre per thread, dimension-major images, 32 loads in flight).  A changed
+// label moves the point between the chunk histograms with integer atomics.
+template <typename T>
+__device__ inline double point_value(const RedecideArgs& a, const T* row, int k) {
+  return (double)Elem<T>::load(row + k);
+}
+
+__device__ inline void relabel(const RedecideArgs& a, int bh, int n, int win) {
+  if (win < 0 || win >= a.G) return;
+  int* lab = a.labels + (long long)bh * a.N + n;
+  const int old = *lab;
+  if (win != old) {
+    *lab = win;
+    int* cnt_row = a.counts + ((long long)bh * a.nchunk + n / kChunk) * a.gstride;
+    atomicSub(cnt_row + old, 1);
+    atomicAdd(cnt_row + win, 1);
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void k_kmeans_redecide(RedecideArgs a) {
+  constexpr int NW = 4, KU = 32;
+  __shared__ double sv[NW];
+  __shared__ int si[NW];
+  const int bh = blockIdx.y, tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int cnt = min(a.fcnt[(long long)bh * a.fcstride], a.N);
+  const int4* fl = a.flist + (long long)bh * a.N;
+  const double* yr = a.y64 + (long long)bh * a.gstride * a.ystride;   // [gstride][Dimg]
+  const double* yt = a.y64t + (long long)bh * a.ystride * a.gstride;  // [Dimg][gstride]
+  const double* cb = a.c64 + (long long)bh * a.gstride;
+  const int Dx = a.Dx, G = a.G, gs = a.gstride;
+  const T* rawb = static_cast<const T*>(a.raw.p);
+  // pass 1: two candidates; four points per wave at a time, 16 lanes each
+  const int sub = lane & 15, grp = lane >> 4;
+  for (int e0 = (blockIdx.x * NW + w) * 4; e0 < cnt; e0 += gridDim.x * NW * 4) {
+    const int e = e0 + grp;
+    const int4 ent = e < cnt ? fl[e] : make_int4(0, 0, 0, 1);
+    const bool act = ent.w == 0;
+    const int n = ent.x, b = ent.y, s = ent.z;
+    double db = 0.0, ds = 0.0;
+    if (act) {
+      const double* x64 = a.x64 ? a.x64 + ((long long)bh * a.N + n) * a.x64stride : nullptr;
+      const T* xr = a.x64 ? nullptr : rawb + a.raw.row_off(bh, n);
+      for (int k = sub; k < Dx; k += 16) {
+        const double x = x64 ? x64[k] : point_value<T>(a, xr, k);
+        db = __builtin_fma(x, yr[(long long)b * a.ystride + k], db);
+        ds = __builtin_fma(x, yr[(long long)s * a.ystride + k], ds);
+      }
+    }
+    for (int o = 8; o > 0; o >>= 1) {
+      db += __shfl_xor(db, o, 16);
+      ds += __shfl_xor(ds, o, 16);
+    }
+    if (act && sub == 0) {
+      db -= 0.5 * cb[b];
+      ds -= 0.5 * cb[s];
+      relabel(a, bh, n, (ds > db || (ds == db && s < b)) ? s : b);
+    }
+  }
+  // pass 2: every centre, one workgroup per point
+  for (int e = blockIdx.x; e < cnt; e += gridDim.x) {
+    const int4 ent = fl[e];
+    if (ent.w == 0) continue;  // uniform across the workgroup
+    const int n = ent.x;
+    const double* x64 = a.x64 ? a.x64 + ((long long)bh * a.N + n) * a.x64stride : nullptr;
+    const T* xr = a.x64 ? nullptr : rawb + a.raw.row_off(bh, n);
+    double best = -INFINITY;
+    int bi = 0x7fffffff;
+    for (int g0 = 0; g0 < G; g0 += 256) {
+      const int g = g0 + tid;
+      double acc = 0.0;
+      for (int k0 = 0; k0 < Dx; k0 += KU) {
+        double y[KU];
+#pragma unroll
+        for (int u = 0; u < KU; ++u) y[u] = (g < G && k0 + u < Dx) ? yt[(long long)(k0 + u) * gs + g] : 0.0;
+#pragma unroll
+        for (int u = 0; u < KU; ++u)
+          if (k0 + u < Dx) acc = __builtin_fma(x64 ? x64[k0 + u] : point_value<T>(a, xr, k0 + u), y[u], acc);
+      }
+      if (g < G) {
+        const double v = acc - 0.5 * cb[g];
+        if (v > best) {  // centres ascend per thread: ties keep the lower one
+          best = v;
+          bi = g;
+        }
+      }
+    }
+    for (int o = 32; o > 0; o >>= 1) {
+      const double ov = __shfl_xor(best, o, 64);
+      const int oi = __shfl_xor(bi, o, 64);
+      if (ov > best || (ov == best && oi < bi)) {
+        best = ov;
+        bi = oi;
+      }
+    }
+    if (lane == 0) {
+      sv[w] = best;
+      si[w] = bi;
+    }
+    __syncthreads();
+    if (tid == 0) {
+      for (int q = 1; q < NW; ++q)
+        if (sv[q] > best || (sv[q] == best && si[q] < bi)) {
+          best = sv[q];
+          bi = si[q];
+        }
+      relabel(a, bh, n, bi);
+    }
+    __syncthreads();  // sv, si are reused by the next point
+  }
+}
+
+// One bf16 32x32x16 matrix-core product per pattern, restricted to output
+// element (0, 0): row 0 of A and column 0 of B carry the pattern's 16 values,
+// every other operand element is zero, the accumulator starts at the
+// pattern's value.  One wave per pattern.
+__global__ __launch_bounds__(64) void k_mfma_rounding(const float* pats, int n, float* out) {
+  const int p = blockIdx.x, lane = threadIdx.x, half = lane >> 5, col = lane & 31;
+  if (p >= n) return;
+  const float* pa = pats + (long long)p * 33;
+  bf16x8 av, bv;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int k = 8 * half + j;
+    av[j] = (__bf16)(col == 0 ? pa[k] : 0.f);
+    bv[j] = (__bf16)(col == 0 ? pa[16 + k] : 0.f);
+  }
+  f32x16 acc = {};
+  if (lane == 0) acc[0] = pa[32];  // D[0][0]: lane 0, register 0
+  acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, acc, 0, 0, 0);
+  if (lane == 0) out[p] = acc[0];
 }
 
 // histogram of given labels (partition supplied by the caller); labels outside
@@ -798,6 +1118,8 @@ __global__ __launch_bounds__(256) void k_group_mean(UpdateArgs a) {
   if (a.init) {
     const long long sidx = ((2LL * g + 1) * a.N) / (2LL * a.G);
     for (int j = tid; j < Dp; j += NT) cm[j] = (double)Elem<TP>::load(xb + a.pts.row_off(bh, sidx) + j);
+    if (g == 0 && a.fcount)
+      for (int t = tid; t < a.T; t += NT) a.fcount[(long long)bh * 2 * a.T + t] = 0;
     return;
   }
   const int* off = a.off + (long long)bh * a.offstride;
@@ -811,9 +1133,9 @@ __global__ __launch_bounds__(256) void k_group_mean(UpdateArgs a) {
     if (tid < Dp) {
       int r = a0;
       for (; r + 7 < a1; r += 8) {
-        float v[8];
+        double v[8];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) v[u] = Elem<TP>::load(xb + a.pts.row_off(bh, perm[r + u]) + tid);
+        for (int u = 0; u < 8; ++u) v[u] = (double)Elem<TP>::load(xb + a.pts.row_off(bh, perm[r + u]) + tid);
 #pragma unroll
         for (int u = 0; u < 8; ++u) s = __dadd_rn(s, (double)v[u]);
       }
@@ -869,14 +1191,16 @@ __global__ __launch_bounds__(256) void k_group_mean(UpdateArgs a) {
     a.means_out[((long long)bh * a.mo_gstride + g) * Dp + tid] = n_g > 0 ? mean : __builtin_nan("");
 }
 
-// centre update, step 2: image y = M mean (or the mean itself), stored as a
-// hi/lo bf16 pair, and bias mean . y (fp64 accumulation).
+// centre update, step 2: image y = M mean (or the mean itself) in fp64 and
+// its bias c = mean . y; kept in fp64 (for the exact re-decision), as a
+// hi/lo bf16 pair and an fp32 bias (the assignment's operands), with bounds
+// of |y|, |c| and of the pair's residual |y - hi - lo| (its error bound).
 // 16 groups per workgroup; 16 threads per group, each owning 8 consecutive
 // dimensions; M is staged through LDS 32 rows at a time.
 __global__ __launch_bounds__(256) void k_centre_images(UpdateArgs a) {
-  constexpr int GB = 16, MR = 32;
+  constexpr int GB = 16, MR = 32, LDM = 130;
   __shared__ double smean[GB][129];
-  __shared__ __attribute__((aligned(16))) float sm[MR][132];
+  __shared__ __attribute__((aligned(16))) double sm[MR][LDM];
   const int bh = blockIdx.y, g0 = blockIdx.x * GB, tid = threadIdx.x;
   const int Dp = a.Dp, Dimg = a.Dimg;
   const int ng = min(GB, a.G - g0);
@@ -896,7 +1220,7 @@ __global__ __launch_bounds__(256) void k_centre_images(UpdateArgs a) {
   }
   // thread (group gl, piece jj) owns dims 8 jj .. 8 jj + 7
   const int gl = tid >> 4, jj = tid & 15;
-  const float* M = a.metric ? a.metric + (long long)bh * Dp * Dp : nullptr;
+  const double* M = a.metric ? a.metric + (long long)bh * Dp * Dp : nullptr;
   double y[8];
 #pragma unroll
   for (int k = 0; k < 8; ++k) y[k] = 0.0;
@@ -905,38 +1229,34 @@ __global__ __launch_bounds__(256) void k_centre_images(UpdateArgs a) {
     for (int i0 = 0; i0 < Dp; i0 += MR) {
       const int nr = min(MR, Dp - i0);
       __syncthreads();
-      if ((Dp & 3) == 0) {
-        // float4 pieces, up to four per thread in flight together
-        const int np = nr * Dp / 4;
-        float4 t[MR * 128 / 4 / 256];
+      // 16-byte pieces, four per thread in flight together
+      const int np = nr * Dp / 2;
+      for (int e0 = 0; e0 < np; e0 += 4 * 256) {
+        double2 t[4];
 #pragma unroll
-        for (int u = 0; u < MR * 128 / 4 / 256; ++u) {
-          const int e = tid + 256 * u;
-          if (e < np) t[u] = *reinterpret_cast<const float4*>(M + (long long)i0 * Dp + 4 * e);
+        for (int u = 0; u < 4; ++u) {
+          const int e = e0 + tid + 256 * u;
+          t[u] = e < np ? *reinterpret_cast<const double2*>(M + (long long)i0 * Dp + 2 * e) : make_double2(0.0, 0.0);
         }
 #pragma unroll
-        for (int u = 0; u < MR * 128 / 4 / 256; ++u) {
-          const int e = tid + 256 * u;
+        for (int u = 0; u < 4; ++u) {
+          const int e = e0 + tid + 256 * u;
           if (e < np) {
-            const int r = (4 * e) / Dp, c = 4 * e - r * Dp;
-            *reinterpret_cast<float4*>(&sm[r][c]) = t[u];
+            const int r = (2 * e) / Dp, c = 2 * e - r * Dp;
+            *reinterpret_cast<double2*>(&sm[r][c]) = t[u];
           }
-        }
-      } else {
-        for (int e = tid; e < nr * Dp; e += 256) {
-          const int r = e / Dp, c = e - (e / Dp) * Dp;
-          sm[r][c] = M[(long long)(i0 + r) * Dp + c];
         }
       }
       __syncthreads();
       if (8 * jj < Dp) {
         for (int r = 0; r < nr; ++r) {
           const double mv = smean[gl][i0 + r];
-          const float4 m0 = *reinterpret_cast<const float4*>(&sm[r][8 * jj]);
-          const float4 m1 = *reinterpret_cast<const float4*>(&sm[r][8 * jj + 4]);
-          const float mm[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
 #pragma unroll
-          for (int k = 0; k < 8; ++k) y[k] = __builtin_fma((double)mm[k], mv, y[k]);
+          for (int k = 0; k < 8; k += 2) {
+            const double2 m2 = *reinterpret_cast<const double2*>(&sm[r][8 * jj + k]);
+            y[k] = __builtin_fma(m2.x, mv, y[k]);
+            y[k + 1] = __builtin_fma(m2.y, mv, y[k + 1]);
+          }
         }
       }
     }
@@ -947,28 +1267,59 @@ __global__ __launch_bounds__(256) void k_centre_images(UpdateArgs a) {
       y[k] = j < Dp ? smean[gl][j] : 0.0;
     }
   }
-  double b = 0.0;
+  double b = 0.0, yy = 0.0, rr = 0.0, ll = 0.0;
+  uint32_t hw[4], lw[4];
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
     const int j = 8 * jj + k;
+    if (j >= Dp) y[k] = 0.0;
     if (j < Dp) b = __builtin_fma(y[k], smean[gl][j], b);
-  }
-  for (int o = 8; o > 0; o >>= 1) b += __shfl_xor(b, o, 16);
-  if (gl >= ng) return;
-  const long long yo = ((long long)bh * a.gstride + g0 + gl) * a.ystride;
-  if (8 * jj < Dimg) {
-    bf16_t hv[8], lv[8];
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const int j = 8 * jj + k;
-      const float yf = j < Dp ? (float)y[k] : 0.f;
-      hv[k] = f32_to_bf16(yf);
-      lv[k] = f32_to_bf16(yf - bf16_to_f32(hv[k]));
+    yy = __builtin_fma(y[k], y[k], yy);
+    const float yf = (float)y[k];
+    const bf16_t h = f32_to_bf16(yf);
+    const bf16_t l = f32_to_bf16(yf - bf16_to_f32(h));
+    const double res = (y[k] - (double)bf16_to_f32(h)) - (double)bf16_to_f32(l);
+    rr = __builtin_fma(res, res, rr);
+    ll = __builtin_fma((double)bf16_to_f32(l), (double)bf16_to_f32(l), ll);
+    if (k & 1) {
+      hw[k >> 1] |= (uint32_t)h << 16;
+      lw[k >> 1] |= (uint32_t)l << 16;
+    } else {
+      hw[k >> 1] = h;
+      lw[k >> 1] = l;
     }
-    *reinterpret_cast<uint4*>(a.yhi + yo + 8 * jj) = *reinterpret_cast<const uint4*>(hv);
-    *reinterpret_cast<uint4*>(a.ylo + yo + 8 * jj) = *reinterpret_cast<const uint4*>(lv);
   }
-  if (jj == 0) a.ybias[(long long)bh * a.gstride + g0 + gl] = (float)b;
+  for (int o = 8; o > 0; o >>= 1) {
+    b += __shfl_xor(b, o, 16);
+    yy += __shfl_xor(yy, o, 16);
+    rr += __shfl_xor(rr, o, 16);
+    ll += __shfl_xor(ll, o, 16);
+  }
+  if (gl >= ng) return;
+  const long long go = (long long)bh * a.gstride + g0 + gl;
+  const long long yo = go * a.ystride;
+  if (8 * jj < Dimg) {
+    *reinterpret_cast<uint4*>(a.yhi + yo + 8 * jj) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+    *reinterpret_cast<uint4*>(a.ylo + yo + 8 * jj) = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+    if (a.y64) {
+#pragma unroll
+      for (int k = 0; k < 8; k += 2) *reinterpret_cast<double2*>(a.y64 + yo + 8 * jj + k) = make_double2(y[k], y[k + 1]);
+      // and dimension-major [Dimg][gstride] per (b,h), read with lanes over centres
+      double* yt = a.y64t + (long long)bh * a.ystride * a.gstride + g0 + gl;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) yt[(long long)(8 * jj + k) * a.gstride] = y[k];
+    }
+  }
+  if (jj == 0) {
+    a.ybias[go] = (float)b;
+    if (a.c64) a.c64[go] = b;
+    if (a.ybound) {
+      // fp32 upper bounds; the relative margin covers the roundings above
+      const float4 bd = make_float4((float)(sqrt(yy) * (1.0 + 0x1p-20)), (float)(fabs(b) * (1.0 + 0x1p-20)),
+                                    (float)(sqrt(rr) * (1.0 + 0x1p-20)), (float)(sqrt(ll) * (1.0 + 0x1p-20)));
+      reinterpret_cast<float4*>(a.ybound)[go] = bd;
+    }
+  }
 }
 
 // M_Q = s^2 sum over non-empty key groups of cbar_h cbar_h^T (d x d per (b,h));
@@ -1015,7 +1366,7 @@ __global__ __launch_bounds__(1024) void k_query_metric(QMetricArgs a) {
 #pragma unroll
   for (int x = 0; x < 4; ++x)
 #pragma unroll
-    for (int y = 0; y < 4; ++y) a.mq[(long long)bh * d * d + (4 * bi + x) * d + 4 * bj + y] = (float)(s2 * acc[x][y]);
+    for (int y = 0; y < 4; ++y) a.mq[(long long)bh * d * d + (4 * bi + x) * d + 4 * bj + y] = s2 * acc[x][y];
 }
 
 // ============================================================================
@@ -1135,40 +1486,42 @@ static long long resident_slots(const void* fn, int threads) {
 
 hipError_t launch_sample_metric(const Plan& p, hipStream_t s) {
   SampleArgs a{p.q, p.N, p.Ms, p.bh0, p.seed, p.sample, p.mk};
+  SP_LAUNCH(k_query_sample, dim3(p.BH), dim3(256), s, a);
   if (p.dtype == SPARSEPR_BF16) {
-    if (p.d == 128) SP_LAUNCH((k_sample_metric<bf16_t, 128>), dim3(p.BH), dim3(256), s, a);
-    else SP_LAUNCH((k_sample_metric<bf16_t, 64>), dim3(p.BH), dim3(256), s, a);
+    if (p.d == 128) SP_LAUNCH((k_key_metric64<bf16_t, 128>), dim3(p.BH), dim3(1024), s, a);
+    else SP_LAUNCH((k_key_metric64<bf16_t, 64>), dim3(p.BH), dim3(1024), s, a);
   } else {
-    if (p.d == 128) SP_LAUNCH((k_sample_metric<float, 128>), dim3(p.BH), dim3(256), s, a);
-    else SP_LAUNCH((k_sample_metric<float, 64>), dim3(p.BH), dim3(256), s, a);
+    if (p.d == 128) SP_LAUNCH((k_key_metric64<float, 128>), dim3(p.BH), dim3(1024), s, a);
+    else SP_LAUNCH((k_key_metric64<float, 64>), dim3(p.BH), dim3(1024), s, a);
   }
   return hipSuccess;
 }
 
 hipError_t launch_key_eig(const Plan& p, hipStream_t s) {
-  EigArgs a{p.mk, p.eigval, p.kmap, p.rK, p.scale};
+  EigArgs a{p.mk, p.eigval, p.kmap, p.kmap_pad, p.eigz, p.rK, p.rKpad, p.scale};
   if (p.d == 128) SP_LAUNCH(k_key_eig<128>, dim3(p.BH), dim3(1024), s, a);
   else SP_LAUNCH(k_key_eig<64>, dim3(p.BH), dim3(1024), s, a);
   return hipSuccess;
 }
 
-hipError_t launch_key_coords(const Plan& p, hipStream_t s) {
-  CoordArgs a{p.k, p.kmap, p.N, p.rK, p.rKpad, p.z32, p.zhi, p.zlo};
-  dim3 g((p.N + 63) / 64, p.BH);
-  if (p.dtype == SPARSEPR_BF16) {
-    const dim3 gm((p.N + 1023) / 1024, p.BH);
-    if (p.rK <= 32) {
-      if (p.d == 128) SP_LAUNCH((k_key_coords_mfma<128, 1>), gm, dim3(256), s, a);
-      else SP_LAUNCH((k_key_coords_mfma<64, 1>), gm, dim3(256), s, a);
-    } else {
-      if (p.d == 128) SP_LAUNCH((k_key_coords_mfma<128, 2>), gm, dim3(256), s, a);
-      else SP_LAUNCH((k_key_coords_mfma<64, 2>), gm, dim3(256), s, a);
-    }
-  } else {
-    if (p.d == 128) SP_LAUNCH((k_key_coords<float, 128>), g, dim3(256), s, a);
-    else SP_LAUNCH((k_key_coords<float, 64>), g, dim3(256), s, a);
+template <typename T, int D>
+static hipError_t launch_key_coords_t(const Plan& p, const CoordArgs& a, hipStream_t s) {
+  const dim3 g((p.N + 255) / 256, p.BH);
+  switch (p.rKpad) {
+    case 16: SP_LAUNCH((k_key_coords_f64mfma<T, D, 16>), g, dim3(256), s, a); break;
+    case 32: SP_LAUNCH((k_key_coords_f64mfma<T, D, 32>), g, dim3(256), s, a); break;
+    case 48: SP_LAUNCH((k_key_coords64<T, D, 48>), g, dim3(256), s, a); break;
+    case 64: SP_LAUNCH((k_key_coords64<T, D, 64>), g, dim3(256), s, a); break;
+    default: return hipErrorInvalidValue;
   }
   return hipSuccess;
+}
+
+hipError_t launch_key_coords(const Plan& p, hipStream_t s) {
+  CoordArgs a{p.k, p.kmap_pad, p.N, p.rK, p.rKpad, p.z64, p.zhi, p.zlo, p.xbound};
+  if (p.dtype == SPARSEPR_BF16)
+    return p.d == 128 ? launch_key_coords_t<bf16_t, 128>(p, a, s) : launch_key_coords_t<bf16_t, 64>(p, a, s);
+  return p.d == 128 ? launch_key_coords_t<float, 128>(p, a, s) : launch_key_coords_t<float, 64>(p, a, s);
 }
 
 hipError_t launch_split_rows(const Plan& p, const View4& x, hipStream_t s) {
@@ -1216,6 +1569,22 @@ hipError_t launch_assign(const Plan& p, const AssignArgs& args, int D, bool lo, 
   return hipSuccess;
 }
 
+hipError_t launch_redecide(const Plan& p, const RedecideArgs& a, int raw_type, hipStream_t s) {
+  if (a.Dx < 1 || a.Dx > 128) return hipErrorInvalidValue;
+  // enough workgroups per (b,h) that a step's flagged points (typically well
+  // under 2% of N) take one or two batches each
+  const int nwg = std::max(1, std::min(32, (p.N + 1023) / 1024));  // four points at a time each
+  const dim3 g(nwg, p.BH);
+  if (raw_type == 0) SP_LAUNCH(k_kmeans_redecide<bf16_t>, g, dim3(256), s, a);
+  else SP_LAUNCH(k_kmeans_redecide<float>, g, dim3(256), s, a);
+  return hipSuccess;
+}
+
+hipError_t launch_mfma_rounding(const float* pats, int n, float* out, hipStream_t s) {
+  SP_LAUNCH(k_mfma_rounding, dim3(n), dim3(64), s, pats, n, out);
+  return hipSuccess;
+}
+
 hipError_t launch_count_labels(const Plan& p, const CountArgs& a, hipStream_t s) {
   SP_LAUNCH(k_count_labels, dim3(p.nchunk, p.BH), dim3(256), s, a);
   return hipSuccess;
@@ -1234,7 +1603,8 @@ hipError_t launch_group_scatter(const Plan& p, const ScatterArgs& a, hipStream_t
 hipError_t launch_centre_update(const Plan& p, const UpdateArgs& a, int pts_type, hipStream_t s) {
   dim3 g(a.G, p.BH);
   if (pts_type == 0) SP_LAUNCH(k_group_mean<bf16_t>, g, dim3(256), s, a);
-  else SP_LAUNCH(k_group_mean<float>, g, dim3(256), s, a);
+  else if (pts_type == 1) SP_LAUNCH(k_group_mean<float>, g, dim3(256), s, a);
+  else SP_LAUNCH(k_group_mean<double>, g, dim3(256), s, a);
   if (a.means_only) return hipSuccess;
   SP_LAUNCH(k_centre_images, dim3((a.G + 15) / 16, p.BH), dim3(256), s, a);
   return hipSuccess;

@@ -47,6 +47,8 @@ struct RouteArgs {
   int* ntiles;
   int max_tiles;
   sparsepr_head_stats* stats;
+  const int* fcount;  // [BH, 2T] k-means flag counts (null: partition given)
+  int T;
 };
 
 constexpr uint64_t kExcluded = ~0ull;
@@ -695,7 +697,10 @@ __global__ __launch_bounds__(256) void k_route_emit(RouteArgs a) {
     st.residual_rank = 0;
     st.over_budget = a.dense_route ? 0 : (routed > a.budget ? 1 : 0);
     st.q_tiles = tacc;
-    st.reserved = 0;
+    int red = 0;
+    if (a.fcount)
+      for (int t = 0; t < 2 * a.T; ++t) red += a.fcount[(long long)bh * 2 * a.T + t];
+    st.kmeans_redecided = red;
     st.rho_route = (double)routed / nn;
     st.rho_exec = (double)(routed + (long long)a.M * a.N) / nn;
     for (int i = 0; i < 4; ++i) st.sigma[i] = 0.0;
@@ -756,6 +761,8 @@ hipError_t launch_route(const Plan& p, hipStream_t s) {
   a.ntiles = p.ntiles;
   a.max_tiles = p.max_tiles;
   a.stats = p.stats;
+  a.fcount = p.kmeans_ran ? p.fcount : nullptr;
+  a.T = p.T;
   hipLaunchKernelGGL(k_route_mu, dim3((p.GQ + 15) / 16, p.BH), dim3(256), 0, s, a);
   hipLaunchKernelGGL(k_route_keys, dim3((p.GQ + 3) / 4, p.BH), dim3(256), 0, s, a);
   if (p.router == SPARSEPR_ROUTER_ALPHA)

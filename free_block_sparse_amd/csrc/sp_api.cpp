@@ -63,8 +63,28 @@ View4 contig(const void* ptr, const Plan& p, int D) {
   return View4{ptr, (long long)p.H * nd, nd, D, p.H};
 }
 
+// Relative error constants of the k-means assignment's approximate values
+// for a point dimension D (multiple of 16).  Every accumulation chain adds
+// mf MFMAs per 16 dims (hi and lo image rows, and with split points the lo
+// point row) onto the fp32 bias.  One bf16 MFMA is taken to be off by at
+// most 18 u (|acc| + sum |products|): its 17 terms aligned to the largest
+// one with 24-bit truncation, then one rounding (the bound is checked on the
+// device by sparsepr_mfma_rounding_check; it also covers 16 sequential fp32
+// additions).  A chain of m MFMAs is then within gamma_K, K = 18 m, of the
+// sum of magnitudes.  Split points without per-point bounds (fp32 inputs)
+// add their residual (at most 2^-16 of |x|) and the dropped lo.lo product
+// (2^-16 |x| |y|).
+static void assign_eps(int D, bool lo, float* eps_x, float* eps_acc) {
+  const double u = 0x1p-24;
+  const double K = 18.0 * (lo ? 3 : 2) * (D / 16);
+  *eps_acc = (float)(1.05 * K * u / (1.0 - K * u) + 4.0 * u);
+  *eps_x = lo ? (float)(1.05 * (0x1p-16 + 0x1p-16 + u)) : 0.f;
+}
+
 // Lloyd k-means on one side.  side 0 = keys, 1 = queries.  Leaves the final
-// labels in `labels_out`, the stable grouping in perm_out / off_out.
+// labels in `labels_out`, the stable grouping in perm_out / off_out.  Each
+// assignment is followed by the exact re-decision of its flagged near ties,
+// so the labels are those of an fp64 assignment.
 sparsepr_status kmeans_side(Plan& p, int side, int G, int* labels_out, int* perm_out, int* off_out,
                             hipStream_t s) {
   const bool rcp = p.mode == SPARSEPR_PART_RESPONSE_COUPLED;
@@ -74,19 +94,24 @@ sparsepr_status kmeans_side(Plan& p, int side, int G, int* labels_out, int* perm
   memset(&aa, 0, sizeof(aa));
   UpdateArgs ua;
   memset(&ua, 0, sizeof(ua));
+  RedecideArgs ra;
+  memset(&ra, 0, sizeof(ra));
   int D;
   bool lo;
-  int pts_type;  // 0 bf16, 1 fp32 for the update kernel
+  int pts_type;  // 0 bf16, 1 fp32, 2 fp64 for the update kernel
   if (side == 0 && rcp) {
     D = p.rKpad;
     lo = true;
     aa.pts = contig(p.zhi, p, D);
     aa.pts_lo = p.zlo;
-    ua.pts = contig(p.z32, p, p.rKpad);
+    ua.pts = View4{p.z64, (long long)p.H * p.N * p.rKpad, (long long)p.N * p.rKpad, p.rKpad, p.H};
     ua.Dp = p.rK;
     ua.Dimg = p.rKpad;
     ua.metric = nullptr;
-    pts_type = 1;
+    pts_type = 2;
+    ra.x64 = p.z64;
+    ra.x64stride = p.rKpad;
+    ra.Dx = p.rK;
   } else {
     D = p.d;
     if (f32) {
@@ -104,6 +129,8 @@ sparsepr_status kmeans_side(Plan& p, int side, int G, int* labels_out, int* perm
     ua.Dimg = p.d;
     ua.metric = (side == 1 && rcp) ? p.mq : nullptr;
     pts_type = f32 ? 1 : 0;
+    ra.raw = raw;
+    ra.Dx = p.d;
   }
   const int Dmax = p.Dk > p.d ? p.Dk : p.d;
   aa.yhi = p.yhi;
@@ -116,6 +143,26 @@ sparsepr_status kmeans_side(Plan& p, int side, int G, int* labels_out, int* perm
   aa.labels = p.labels;
   aa.counts = p.counts;
   aa.nchunk = p.nchunk;
+  aa.ybound = p.ybound;
+  aa.xbound = (side == 0 && rcp) ? p.xbound : nullptr;
+  assign_eps(D, lo, &aa.eps_x, &aa.eps_acc);
+  int* fc = p.fcount + side * p.T;  // key side: steps 0..T-1, query side: T..2T-1
+  aa.fcstride = 2 * p.T;
+  aa.flist = p.flist;
+
+  ra.y64 = p.y64;
+  ra.y64t = p.y64t;
+  ra.c64 = p.c64;
+  ra.ystride = Dmax;
+  ra.gstride = p.Gmax;
+  ra.N = p.N;
+  ra.G = G;
+  ra.fcstride = 2 * p.T;
+  ra.flist = p.flist;
+  ra.labels = p.labels;
+  ra.counts = p.counts;
+  ra.nchunk = p.nchunk;
+  const int raw_type = f32 ? 1 : 0;
 
   ua.perm = p.perm_w;
   ua.off = p.off_w;
@@ -125,16 +172,25 @@ sparsepr_status kmeans_side(Plan& p, int side, int G, int* labels_out, int* perm
   ua.yhi = p.yhi;
   ua.ylo = p.ylo;
   ua.ybias = p.ybias;
+  ua.y64 = p.y64;
+  ua.y64t = p.y64t;
+  ua.c64 = p.c64;
+  ua.ybound = p.ybound;
   ua.ystride = Dmax;
   ua.gstride = p.Gmax;
   ua.G = G;
   ua.N = p.N;
+  ua.fcount = fc;
+  ua.T = p.T;
   ua.init = 1;
   HIPCHK(launch_centre_update(p, ua, pts_type, s));
   ua.init = 0;
   for (int t = 0; t < p.T; ++t) {
     const bool last = t == p.T - 1;
+    aa.fcnt = fc + t;
+    ra.fcnt = fc + t;
     HIPCHK(launch_assign(p, aa, D, lo, s));
+    HIPCHK(launch_redecide(p, ra, raw_type, s));
     ScanArgs sa{p.counts, p.chunkoff, last ? off_out : p.off_w, last ? G + 1 : p.Gmax + 1, p.nchunk, G, p.Gmax, p.N};
     HIPCHK(launch_group_scan(p, sa, s));
     ScatterArgs sc{p.labels, p.chunkoff, last ? perm_out : p.perm_w, last ? labels_out : nullptr, p.N, p.nchunk,
@@ -186,6 +242,7 @@ sparsepr_status run_partition(Plan& p, hipStream_t s, Stager* st = nullptr, hipE
   if (rcp) HIPCHK(launch_query_metric(p, s));
   SPCHK(mark(st, SPARSEPR_STAGE_KEY_CENTRES));
   SPCHK(kmeans_side(p, 1, p.GQ, p.q_labels, p.perm_q, p.off_q, s));
+  p.kmeans_ran = true;
   SPCHK(mark(st, SPARSEPR_STAGE_QUERY_KMEANS));
   SPCHK(raw_means(p, p.q, p.perm_q, p.off_q, p.GQ, p.qbar, s));
   SPCHK(mark(st, SPARSEPR_STAGE_QUERY_CENTRES));
@@ -442,8 +499,8 @@ sparsepr_status sparsepr_attention_with_partition(const sparsepr_config* cfg, co
 }
 
 sparsepr_status sparsepr_key_metric(const sparsepr_config* cfg, const sparsepr_tensors* io, void* workspace,
-                                    size_t workspace_bytes, void* stream, int* sample_idx, float* m_k,
-                                    float* eigvals, float* key_map) {
+                                    size_t workspace_bytes, void* stream, int* sample_idx, double* m_k,
+                                    double* eigvals, double* key_map) {
   Plan p;
   SPCHK(prepare(p, cfg, io, workspace, workspace_bytes));
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -533,6 +590,12 @@ sparsepr_status sparsepr_dense_attention(const sparsepr_tensors* io, float scale
   SPCHK(plan_io(&p, io));
   const float s = scale > 0.f ? scale : p.scale;
   HIPCHK(launch_dense_attention(p.q, p.k, p.v, p.o, p.BH, p.N, p.d, p.dtype, s, static_cast<hipStream_t>(stream)));
+  return SPARSEPR_OK;
+}
+
+sparsepr_status sparsepr_mfma_rounding_check(const float* patterns, int n, float* out, void* stream) {
+  if (!patterns || !out || n < 1 || n > (1 << 20)) return SPARSEPR_ERR_INVALID_ARG;
+  HIPCHK(launch_mfma_rounding(patterns, n, out, static_cast<hipStream_t>(stream)));
   return SPARSEPR_OK;
 }
 

@@ -43,6 +43,10 @@ __device__ inline uint32_t pack_bf16x2(float a, float b) {
 }
 
 template <typename T> struct Elem;
+template <> struct Elem<double> {
+  __device__ static inline double load(const double* p) { return *p; }
+  __device__ static inline void store(double* p, double v) { *p = v; }
+};
 template <> struct Elem<float> {
   __device__ static inline float load(const float* p) { return *p; }
   __device__ static inline void store(float* p, float v) { *p = v; }

@@ -512,6 +512,28 @@ __device__ bool eig_twisted(const EigWork<T>& w, int n, int nvec) {
   return true;
 }
 
+// Step 3 with the reflectors stored column-major and packed: column k
+// (rows k+1 .. n-1) starts at refl + k (n - 1) - k (k - 1) / 2.
+template <typename T, int NT, int GW>
+__device__ void eig_back_transform_packed(const EigWork<T>& w, const T* refl, int n, const int* cols, int ncol) {
+  const int tid = threadIdx.x, g = tid / GW, sub = tid - (tid / GW) * GW;
+  constexpr int NG = NT / GW;
+  for (int c = g; c < ncol; c += NG) {
+    const int j = cols ? cols[c] : c;
+    for (int k = n - 3; k >= 0; --k) {
+      const T tau = w.tau[k];
+      if (tau == T(0)) continue;
+      const int m = n - k - 1;
+      const T* v = refl + k * (n - 1) - (k * (k - 1)) / 2;
+      T s = 0;
+      for (int i = sub; i < m; i += GW) s += v[i] * w.Z[(k + 1 + i) * w.ldz + j];
+      s = eig_sum(s, GW) * tau;
+      for (int i = sub; i < m; i += GW) w.Z[(k + 1 + i) * w.ldz + j] -= s * v[i];
+    }
+  }
+  __syncthreads();
+}
+
 // Step 3: Z[:, cols[c]] <- Q Z[:, cols[c]] for c < ncol (cols == nullptr: c).
 // GW consecutive threads (one wave or part of one) take a column.
 template <typename T, int NT, int GW>

@@ -11,24 +11,27 @@ struct SampleArgs {
   int bh0;  // global index of head 0 of the launch
   unsigned long long seed;
   int* sample;
-  float* mk;
+  double* mk;
 };
 
 struct EigArgs {
-  const float* mk;
-  float* eigval;
-  float* kmap;
-  int rK;
+  const double* mk;
+  double* eigval;
+  double* kmap;      // [BH, d, rK]
+  double* kmap_pad;  // [BH, d, rKpad]
+  double* eigz;      // [BH, d, d] eigenvector scratch (shifted-QR fallback, rK > 32)
+  int rK, rKpad;
   float scale;
 };
 
 struct CoordArgs {
   View4 k;
-  const float* kmap;
+  const double* kmap_pad;  // [BH, d, rKpad] coordinate map, zero beyond rK
   int N, rK, rKpad;
-  float* z32;
+  double* z64;
   bf16_t* zhi;
   bf16_t* zlo;
+  float2* xbound;  // [BH, N]: |z - hi - lo| and |lo| of each key's split coordinates
 };
 
 struct SplitArgs {
@@ -50,6 +53,34 @@ struct AssignArgs {
   int* counts;            // [BH, nchunk, gstride]
   int nchunk;
   int cpw;                // histogram chunks per workgroup (resident form; set by the launcher)
+  // near-tie flags: a point is flagged when its best and second-best values
+  // lie within twice the error bound of the approximate values
+  const float* ybound;    // [BH, gstride, 4]: bounds of |y_g|, |c_g|, |y_g - hi_g - lo_g|, |lo_g|
+  const float2* xbound;   // [BH, N]: bounds of |x - x~| and |x_lo| of split points, or null
+  float eps_x;            // without xbound: bound of |x - x~| / |x~| and |x_lo||y_lo| / (|x~||y|)
+  float eps_acc;          // relative bound of the fp32 accumulation chain
+  int* fcnt;              // this step's flag counter of (b,h) is fcnt[bh * fcstride]
+  int fcstride;
+  int4* flist;            // [BH, N] flagged points: (point, best centre, second centre, full re-decision)
+};
+
+// Exact (fp64) re-decision of the flagged points of one Lloyd step.
+struct RedecideArgs {
+  View4 raw;              // raw point rows (bf16 or fp32) when x64 is null
+  const double* x64;      // [BH, N, x64stride] exact point rows (key coordinates), or null
+  int x64stride;
+  int Dx;                 // point dims
+  const double* y64;      // [BH, gstride, ystride] centre images
+  const double* y64t;     // [BH, ystride, gstride] the same, dimension-major
+  const double* c64;      // [BH, gstride] centre biases
+  int ystride, gstride;
+  int N, G;
+  const int* fcnt;
+  int fcstride;
+  const int4* flist;
+  int* labels;
+  int* counts;            // [BH, nchunk, gstride]
+  int nchunk;
 };
 
 struct CountArgs {
@@ -82,15 +113,21 @@ struct UpdateArgs {
   const int* perm;      // [BH, N]
   const int* off;       // [BH, offstride]
   int offstride;
-  const float* metric;  // [BH, Dp, Dp] or null (identity)
+  const double* metric;  // [BH, Dp, Dp] or null (identity)
   double* cmean;        // [BH, gstride, cstride]
   int cstride;
   bf16_t* yhi;
   bf16_t* ylo;
   float* ybias;
+  double* y64;          // [BH, gstride, ystride] images in fp64
+  double* y64t;         // [BH, ystride, gstride] the same, dimension-major
+  double* c64;          // [BH, gstride] biases in fp64
+  float* ybound;        // [BH, gstride, 4]: bounds of |y_g|, |c_g|, |y_g - hi - lo|, |lo|
   int ystride, gstride;
   int G, N;
   int init;             // centres = points at strided seed indices
+  int* fcount;          // this side's flag counters, fcount[bh * 2T + t] for t < T, cleared by the init launch
+  int T;
   int means_only;       // only write means_out
   double* means_out;    // [BH, mo_gstride, Dp] or null; NaN for empty groups
   int mo_gstride;
@@ -101,7 +138,7 @@ struct QMetricArgs {
   const int* off_k;
   int GK, d;
   float scale;
-  float* mq;
+  double* mq;
 };
 
 struct GatherArgs {
@@ -121,6 +158,8 @@ hipError_t launch_key_eig(const Plan& p, hipStream_t s);
 hipError_t launch_key_coords(const Plan& p, hipStream_t s);
 hipError_t launch_split_rows(const Plan& p, const View4& x, hipStream_t s);
 hipError_t launch_assign(const Plan& p, const AssignArgs& a, int D, bool lo, hipStream_t s);
+hipError_t launch_redecide(const Plan& p, const RedecideArgs& a, int raw_type, hipStream_t s);
+hipError_t launch_mfma_rounding(const float* pats, int n, float* out, hipStream_t s);
 hipError_t launch_count_labels(const Plan& p, const CountArgs& a, hipStream_t s);
 hipError_t launch_group_scan(const Plan& p, const ScanArgs& a, hipStream_t s);
 hipError_t launch_group_scatter(const Plan& p, const ScatterArgs& a, hipStream_t s);

@@ -131,11 +131,14 @@ void plan_carve(Plan* p, char* base) {
   const long long BH = p->BH, N = p->N, d = p->d;
   const long long Dmax = p->Dk > p->d ? p->Dk : p->d;
   p->sample = c.take<int>(BH * p->Ms);
-  p->mk = c.take<float>(BH * d * d);
-  p->eigval = c.take<float>(BH * d);
-  p->kmap = c.take<float>(BH * d * p->rK);
+  p->mk = c.take<double>(BH * d * d);
+  p->eigval = c.take<double>(BH * d);
+  p->kmap = c.take<double>(BH * d * p->rK);
+  p->kmap_pad = c.take<double>(BH * d * p->rKpad);
+  p->eigz = c.take<double>(BH * d * d);
   const bool rcp = p->mode == SPARSEPR_PART_RESPONSE_COUPLED;
-  p->z32 = rcp ? c.take<float>(BH * N * p->rKpad) : nullptr;
+  p->z64 = rcp ? c.take<double>(BH * N * p->rKpad) : nullptr;
+  p->xbound = rcp ? c.take<float2>(BH * N) : nullptr;
   p->zhi = rcp ? c.take<bf16_t>(BH * N * p->rKpad) : nullptr;
   p->zlo = rcp ? c.take<bf16_t>(BH * N * p->rKpad) : nullptr;
   const bool f32 = p->dtype == SPARSEPR_FP32;
@@ -145,6 +148,12 @@ void plan_carve(Plan* p, char* base) {
   p->yhi = c.take<bf16_t>(BH * p->Gmax * Dmax);
   p->ylo = c.take<bf16_t>(BH * p->Gmax * Dmax);
   p->ybias = c.take<float>(BH * p->Gmax);
+  p->y64 = c.take<double>(BH * p->Gmax * Dmax);
+  p->y64t = c.take<double>(BH * p->Gmax * Dmax);
+  p->c64 = c.take<double>(BH * p->Gmax);
+  p->ybound = c.take<float>(BH * p->Gmax * 4);
+  p->fcount = c.take<int>(BH * 2 * p->T);
+  p->flist = c.take<int4>(BH * N);
   p->labels = c.take<int>(BH * N);
   p->counts = c.take<int>(BH * p->nchunk * p->Gmax);
   p->chunkoff = c.take<int>(BH * p->nchunk * p->Gmax);
@@ -158,7 +167,7 @@ void plan_carve(Plan* p, char* base) {
   p->off_q = c.take<int>(BH * (p->GQ + 1));
   p->cbar = c.take<double>(BH * p->GK * d);
   p->qbar = c.take<double>(BH * p->GQ * d);
-  p->mq = c.take<float>(BH * d * d);
+  p->mq = c.take<double>(BH * d * d);
   p->kp = c.take<char>(BH * N * d * p->esize);
   p->vp = c.take<char>(BH * N * d * p->esize);
   p->kgroup = c.take<int>(BH * N);

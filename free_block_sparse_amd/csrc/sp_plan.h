@@ -40,10 +40,13 @@ struct Plan {
 
   // ---- workspace (device pointers) ----
   int* sample;            // [BH, Ms]
-  float* mk;              // [BH, d, d]
-  float* eigval;          // [BH, d]
-  float* kmap;            // [BH, d, rK]
-  float* z32;             // [BH, N, rKpad] (zero beyond rK)
+  double* mk;             // [BH, d, d]
+  double* eigval;         // [BH, d]
+  double* kmap;           // [BH, d, rK]
+  double* kmap_pad;       // [BH, d, rKpad] the same, zero beyond rK
+  double* eigz;           // [BH, d, d] eigensolver vectors (scratch)
+  double* z64;            // [BH, N, rKpad] key coordinates (zero beyond rK)
+  float2* xbound;         // [BH, N] bounds of each key's hi/lo split residual and lo part
   bf16_t* zhi;            // [BH, N, rKpad]
   bf16_t* zlo;            // [BH, N, rKpad]
   bf16_t* phi;            // [BH, N, d] raw points split (fp32 inputs only)
@@ -52,6 +55,13 @@ struct Plan {
   bf16_t* yhi;            // [BH, Gmax, Dmax] centre images (hi part)
   bf16_t* ylo;            // [BH, Gmax, Dmax] centre images (lo part)
   float* ybias;           // [BH, Gmax]
+  double* y64;            // [BH, Gmax, Dmax] centre images in fp64
+  double* y64t;           // [BH, Dmax, Gmax] the same, dimension-major
+  double* c64;            // [BH, Gmax] centre bias x.y of the images in fp64
+  float* ybound;          // [BH, Gmax, 4] upper bounds of |y_g|, |c_g|, |y_g - hi - lo| and |lo|
+  int* fcount;            // [BH, 2T] near-tie points flagged per Lloyd step (key side, then query side)
+  bool kmeans_ran;        // set once this plan's partition came from its own k-means
+  int4* flist;            // [BH, N] flagged points of the current step (point, two candidates, full flag)
   int* labels;            // [BH, N] working labels
   int* counts;            // [BH, nchunk, Gmax]
   int* chunkoff;          // [BH, nchunk, Gmax]
@@ -65,7 +75,7 @@ struct Plan {
   int* off_q;             // [BH, GQ + 1]
   double* cbar;           // [BH, GK, d] raw key means
   double* qbar;           // [BH, GQ, d] raw query means
-  float* mq;              // [BH, d, d] query metric s^2 Cbar^T Cbar
+  double* mq;             // [BH, d, d] query metric s^2 Cbar^T Cbar
   void* kp;               // [BH, N, d] permuted copies of K (input dtype) and V
   void* vp;
   int* kgroup;            // [BH, N] key-group id of each permuted key position

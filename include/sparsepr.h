@@ -134,7 +134,8 @@ typedef struct {
   int residual_rank;          /* r' actually used by the fit */
   int over_budget;            /* 1 when the mandatory cells alone exceed the budget */
   int q_tiles;                /* query tiles run by the sparse kernel */
-  int reserved;
+  int kmeans_redecided;       /* k-means assignments re-decided in fp64 (both sides, all Lloyd
+                                 steps; 0 when the partition was given) */
   double rho_route;           /* routed_pairs / N^2 */
   double rho_exec;            /* (routed_pairs + probe_pairs) / N^2 */
   double sigma[4];            /* leading singular values of the probe residuals */
@@ -208,15 +209,15 @@ sparsepr_status sparsepr_attention_with_partition(const sparsepr_config* cfg,
                                                   void* stream, sparsepr_head_stats* stats);
 
 /* Stages a1-a2 ([TS] 2.A): the sampled query rows (device int32 [B*H, M_s],
-   ascending), M_K = Q_s^T Q_s / M_s (device float [B*H, d, d]), the
-   eigenvalues of M_K in descending order (device float [B*H, d]) and the key
-   coordinate map (device float [B*H, d, r_K], row-major: column r is
+   ascending), M_K = Q_s^T Q_s / M_s (device double [B*H, d, d]), the
+   eigenvalues of M_K in descending order (device double [B*H, d]) and the key
+   coordinate map (device double [B*H, d, r_K], row-major: column r is
    s sqrt(lambda_r) u_r for the r-th largest eigenpair, r_K =
-   min(key_coord_rank, d, M_s); the sign of each column is unspecified).  Any
-   output pointer may be NULL. */
+   min(key_coord_rank, d, M_s); the sign of each column is unspecified).  All
+   three are computed in fp64.  Any output pointer may be NULL. */
 sparsepr_status sparsepr_key_metric(const sparsepr_config* cfg, const sparsepr_tensors* io,
                                     void* workspace, size_t workspace_bytes, void* stream,
-                                    int* sample_idx, float* m_k, float* eigvals, float* key_map);
+                                    int* sample_idx, double* m_k, double* eigvals, double* key_map);
 
 /* Stages a1-a8: response-coupled (or independent) partition.  Writes the
    labels of the last Lloyd step (device int32 [B*H, N] each). */
@@ -256,6 +257,16 @@ sparsepr_status sparsepr_probe_fit(const sparsepr_config* cfg, const sparsepr_te
 /* Dense softmax attention over all keys (the speed baseline), bf16 or fp32,
    no workspace; scale 0 => 1/sqrt(d). */
 sparsepr_status sparsepr_dense_attention(const sparsepr_tensors* io, float scale, void* stream);
+
+/* Device property the k-means assignment's error bound relies on: one bf16
+   matrix-core product (32x32x16, fp32 accumulate) lands within 18 units of
+   fp32 roundoff of the sum of magnitudes of its accumulator and its 16
+   products.  For each of n patterns (device float
+   [n, 33]: 16 values of row 0 of A, 16 of column 0 of B, all exact in bf16,
+   then the accumulator) writes element (0, 0) of the product (device float
+   [n]); the caller compares it with the exact sum.  Not used by the call
+   itself; n in [1, 1 << 20]. */
+sparsepr_status sparsepr_mfma_rounding_check(const float* patterns, int n, float* out, void* stream);
 
 const char* sparsepr_status_string(sparsepr_status s);
 int sparsepr_last_hip_error(void);

@@ -2,11 +2,12 @@
 
 Every function follows one step of the method as the pages describe it, in
 the pages' order; the citation legend is in ``oracle/__init__.py``.  Floating
-point is fp64 everywhere except the two k-means assignment decisions, which
-are taken in fp32 because the GPU kernels take them in fp32 (an argmin is a
-floating-point decision of an integer and both sides must decide in the same
-precision).  Group statistics that feed the router are sequential fp64 sums
-in ascending token order, so the GPU can reproduce them bit for bit.
+point is fp64 everywhere, the two k-means assignment decisions included: an
+argmin is a floating-point decision of an integer, both sides must decide in
+the same precision, and the GPU kernels decide in fp64 (their fast path has a
+proven error bound and every point it cannot separate is re-decided in fp64).
+Group statistics that feed the router are sequential fp64 sums in ascending
+token order, so the GPU can reproduce them bit for bit.
 
 Readings where the pages are silent (numbers refer to the table of readings
 kept with the design notes; each is a field of ``OracleConfig``):
@@ -168,7 +169,7 @@ def kmeans(x: np.ndarray, g: int, iters: int):
     """Lloyd's k-means with the readings of U3.
 
     Each step assigns every point to its nearest centre (argmin of
-    ||c||^2 - 2 x.c in float32, lowest index on ties) and then moves every
+    ||c||^2 - 2 x.c in fp64, lowest index on ties) and then moves every
     non-empty centre to the fp64 mean of its members; empty centres stay put.
     Returns the labels of the last assignment and the final centres.
     """
@@ -176,10 +177,8 @@ def kmeans(x: np.ndarray, g: int, iters: int):
     x64 = x.astype(np.float64)
     c = x64[strided_seeds(n, g)].copy()
     labels = np.zeros(n, dtype=np.int64)
-    x32 = x64.astype(np.float32)
     for _ in range(iters):
-        c32 = c.astype(np.float32)
-        dist = (c32 * c32).sum(axis=1)[None, :] - np.float32(2.0) * (x32 @ c32.T)
+        dist = (c * c).sum(axis=1)[None, :] - 2.0 * (x64 @ c.T)
         labels = np.argmin(dist, axis=1)
         for j in range(g):
             members = np.nonzero(labels == j)[0]
