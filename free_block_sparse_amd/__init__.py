@@ -31,7 +31,7 @@ __all__ = [
     "sparsepr_attention_with_partition", "sparsepr_key_metric", "sparsepr_partition", "sparsepr_route",
     "sparsepr_sparse_attention", "sparsepr_probe_fit", "sparsepr_dense_attention", "make_config",
     "stats_to_dicts", "SparseprConfig", "SparsePRError", "sparsepr_attention_profile", "Workspace",
-    "sparsepr_mfma_rounding_check",
+    "sparsepr_mfma_rounding_check", "sparsepr_attention_noalloc", "noalloc_scratch_bytes",
 ]
 
 
@@ -160,6 +160,22 @@ def sparsepr_attention(q, k, v, cfg: SparseprConfig, out=None, workspace: Option
     check(lib().sparsepr_attention(ctypes.byref(cfg), ctypes.byref(io), buf.data_ptr(), nbytes,
                                    _stream(stream), _ptr(st)), "sparsepr_attention")
     return (out, st) if with_stats else out
+
+
+def sparsepr_attention_noalloc(q, k, v, cfg: SparseprConfig, out=None, stream=None, with_stats: bool = False):
+    """The full call in the library's fixed per-GPU scratch (no workspace, no
+    allocation by the library; `out` and the stats buffer are the caller's)."""
+    torch = _torch()
+    out = torch.empty_like(q) if out is None else out
+    io = _tensors(q, k, v, out)
+    st = _stats_buf(q) if with_stats else None
+    check(lib().sparsepr_attention_noalloc(ctypes.byref(cfg), ctypes.byref(io), _stream(stream), _ptr(st)),
+          "sparsepr_attention_noalloc")
+    return (out, st) if with_stats else out
+
+
+def noalloc_scratch_bytes() -> int:
+    return int(lib().sparsepr_noalloc_scratch_bytes())
 
 
 def sparsepr_attention_profile(q, k, v, cfg, out=None, workspace: Optional[Workspace] = None, stream=None):

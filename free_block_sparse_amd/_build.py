@@ -16,7 +16,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libsparsepr.so")
 
-SOURCES = ["sp_plan.cpp", "sp_api.cpp", "k_partition.hip", "k_router.hip", "k_attn.hip", "k_fit.hip"]
+SOURCES = ["sp_plan.cpp", "sp_api.cpp", "k_partition.hip", "k_router.hip", "k_attn.hip", "k_fit.hip",
+           "sp_noalloc.hip"]
 
 HIP_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

@@ -114,6 +114,8 @@ _SIGS = {
                                 ctypes.c_size_t, _P, _P, _P, _P, _P, _P, _P, _P]),
     "sparsepr_dense_attention": (_I, [ctypes.POINTER(SparseprTensors), ctypes.c_float, _P]),
     "sparsepr_mfma_rounding_check": (_I, [_P, ctypes.c_int, _P, _P]),
+    "sparsepr_attention_noalloc": (_I, [ctypes.POINTER(SparseprConfig), ctypes.POINTER(SparseprTensors), _P, _P]),
+    "sparsepr_noalloc_scratch_bytes": (ctypes.c_size_t, []),
     "sparsepr_attention_profile": (_I, [ctypes.POINTER(SparseprConfig), ctypes.POINTER(SparseprTensors), _P,
                                         ctypes.c_size_t, _P, _P, ctypes.POINTER(ctypes.c_float)]),
     "sparsepr_status_string": (ctypes.c_char_p, [_I]),

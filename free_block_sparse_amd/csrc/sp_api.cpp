@@ -449,6 +449,32 @@ sparsepr_status sparsepr_attention(const sparsepr_config* cfg, const sparsepr_te
   return SPARSEPR_OK;
 }
 
+sparsepr_status sparsepr_attention_noalloc(const sparsepr_config* cfg, const sparsepr_tensors* io, void* stream,
+                                           sparsepr_head_stats* stats) {
+  // shape and size checks first: no device call for a rejected request
+  if (!io) return SPARSEPR_ERR_INVALID_ARG;
+  Plan p;
+  SPCHK(plan_init(&p, cfg, io->B, io->H, io->N, io->d, io->dtype));
+  SPCHK(plan_io(&p, io));
+  plan_carve(&p, nullptr);
+  if (p.ws_bytes > kNoAllocScratchBytes) return SPARSEPR_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (s) {
+    // the scratch used is the current device's: the stream must live there
+    int cur = 0, sdev = 0;
+    HIPCHK(hipGetDevice(&cur));
+    HIPCHK(hipStreamGetDevice(s, &sdev));
+    if (sdev != cur) return SPARSEPR_ERR_INVALID_ARG;
+  }
+  void* base = nullptr;
+  HIPCHK(noalloc_scratch(&base));
+  SPCHK(prepare(p, cfg, io, base, kNoAllocScratchBytes));
+  SPCHK(run_partition(p, s));
+  return run_after_partition(p, s, stats);
+}
+
+size_t sparsepr_noalloc_scratch_bytes(void) { return kNoAllocScratchBytes; }
+
 sparsepr_status sparsepr_attention_profile(const sparsepr_config* cfg, const sparsepr_tensors* io,
                                            void* workspace, size_t workspace_bytes, void* stream,
                                            sparsepr_head_stats* stats, float* stage_ms) {

@@ -160,6 +160,9 @@ hipError_t launch_split_rows(const Plan& p, const View4& x, hipStream_t s);
 hipError_t launch_assign(const Plan& p, const AssignArgs& a, int D, bool lo, hipStream_t s);
 hipError_t launch_redecide(const Plan& p, const RedecideArgs& a, int raw_type, hipStream_t s);
 hipError_t launch_mfma_rounding(const float* pats, int n, float* out, hipStream_t s);
+
+// allocation-free entry point (sp_noalloc.hip): this device's fixed scratch
+hipError_t noalloc_scratch(void** ptr);
 hipError_t launch_count_labels(const Plan& p, const CountArgs& a, hipStream_t s);
 hipError_t launch_group_scan(const Plan& p, const ScanArgs& a, hipStream_t s);
 hipError_t launch_group_scatter(const Plan& p, const ScatterArgs& a, hipStream_t s);

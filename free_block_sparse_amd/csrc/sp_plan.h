@@ -16,6 +16,7 @@ constexpr int kMaxProbe = 256;
 constexpr int kMaxRank = 64;
 constexpr int kMaxGroups = 1024;
 constexpr long long kFitScratchDoubles = 7LL * 128 * 128;  // per (b,h) fit scratch
+constexpr size_t kNoAllocScratchBytes = (size_t)128 << 20;  // fixed scratch of sparsepr_attention_noalloc
 
 struct Plan {
   // shape and settings

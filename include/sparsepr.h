@@ -173,6 +173,23 @@ sparsepr_status sparsepr_attention(const sparsepr_config* cfg, const sparsepr_te
                                    void* workspace, size_t workspace_bytes, void* stream,
                                    sparsepr_head_stats* stats);
 
+/* The full call for callers that cannot allocate (code under HIP graph
+   capture, tight serving loops, harnesses that forbid hipMalloc): the same
+   computation and result as sparsepr_attention, run entirely on `stream`
+   (no head split, no second stream), with the intermediates in a fixed
+   scratch array of sparsepr_noalloc_scratch_bytes() bytes (128 MiB) that the
+   library holds on each GPU it runs on until the process ends.  No memory
+   is allocated or freed by the call.  A call whose workspace would exceed
+   the scratch (sparsepr_workspace_size) returns SPARSEPR_ERR_WORKSPACE
+   before any device work; `stream` must belong to the current device
+   (SPARSEPR_ERR_INVALID_ARG otherwise).  Every call on a GPU shares that
+   GPU's scratch and it keeps the last call's contents (the call clears what
+   it needs itself): calls that overlap in time on one GPU race and must be
+   ordered by the caller.  `stats` as for sparsepr_attention. */
+sparsepr_status sparsepr_attention_noalloc(const sparsepr_config* cfg, const sparsepr_tensors* io, void* stream,
+                                           sparsepr_head_stats* stats);
+size_t sparsepr_noalloc_scratch_bytes(void);
+
 /* Stages timed by sparsepr_attention_profile(). */
 enum {
   SPARSEPR_STAGE_SAMPLE_METRIC = 0,   /* a1 query sample and M_K */

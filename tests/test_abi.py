@@ -136,3 +136,26 @@ def test_status_strings():
 def test_alpha_router_target_must_lie_in_0_1(alpha, ok):
     cfg = make_config(4096, 64, n_kv_groups=32, n_q_groups=32, router="alpha", alpha=alpha)
     assert (sparsepr_validate(cfg, 1, 2, 4096, 64, 0) == 0) == ok
+
+
+def test_noalloc_rejects_requests_beyond_its_scratch_before_any_device_call():
+    """A call whose workspace exceeds the fixed scratch returns the workspace
+    error from the host-side checks, before the library touches a device
+    (the pointers below are never dereferenced)."""
+    import free_block_sparse_amd as sp
+    from free_block_sparse_amd import _lib
+
+    L = _lib.lib()
+    H, N, d = 40, 32760, 128
+    cfg = sp.make_config(N, d, n_kv_groups=256, n_q_groups=256)
+    nb = ctypes.c_size_t(0)
+    assert L.sparsepr_workspace_size(ctypes.byref(cfg), 1, H, N, d, 0, ctypes.byref(nb)) == 0
+    assert nb.value > L.sparsepr_noalloc_scratch_bytes()
+    io = _lib.SparseprTensors()
+    fake = [4096, 8192, 12288, 16384]
+    io.q, io.k, io.v, io.o = fake
+    st = [H * N * d, N * d, d, 1]
+    for f in ("q_strides", "k_strides", "v_strides", "o_strides"):
+        getattr(io, f)[:] = st
+    io.B, io.H, io.N, io.d, io.dtype = 1, H, N, d, 0
+    assert L.sparsepr_attention_noalloc(ctypes.byref(cfg), ctypes.byref(io), None, None) == -3
