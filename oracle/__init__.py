@@ -17,6 +17,8 @@ Citation legend used in the docstrings (page title, then section):
         NE/mass    "保留了多少注意力权重，不等于输出的误差有多小"
         NE/method  "SparsePR：先把误差聚拢，再用少量“抽查”去纠正" (incl. Figure 2)
         NE/exec    "稀疏执行怎么落地，误差怎么算才公平"
+        NE/pool    "问题就出在"打包成组"这一步" (per-query vs shared-route support)
+        NE/repair  "怎么分组，直接决定了剩下的误差好不好"修补"" (affine-explainable residual)
 
 Parity status per function is listed in the header of ``sparsepr_oracle``.
 """
@@ -41,4 +43,7 @@ from .sparsepr_oracle import (  # noqa: F401
     sparsepr_head,
     splitmix64,
     softmax_scale,
+    structural_diagnostics,
+    support_fraction,
+    support_set,
 )

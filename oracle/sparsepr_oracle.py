@@ -501,6 +501,83 @@ def fit_residual(r: np.ndarray, x: np.ndarray, w: np.ndarray, rank: int, lam: fl
 
 
 # ----------------------------------------------------------------------------
+# structural diagnostics (analysis of a partition; not part of the call)
+# ----------------------------------------------------------------------------
+def support_fraction(p: np.ndarray, mass: float = 0.9) -> float:
+    """Smallest fraction of keys whose probabilities sum to at least `mass`.
+
+    Per-query attention is concentrated, but that alone does not fix what a
+    shared route must keep ([NE] NE/pool: 6.2% of keys hold 90% of one query's
+    mass; [TS] 3, structural analysis).
+    The smallest such set is the largest probabilities taken in order.
+    """
+    q = np.sort(np.asarray(p, dtype=np.float64))[::-1]
+    c = np.cumsum(q)
+    k = int(np.searchsorted(c, mass * c[-1] * (1 - 1e-12), side="left")) + 1
+    return min(k, len(q)) / float(len(q))
+
+
+def support_set(p: np.ndarray, mass: float = 0.9) -> np.ndarray:
+    """The keys of that smallest set (ties by index)."""
+    order = np.lexsort((np.arange(len(p)), -np.asarray(p, dtype=np.float64)))
+    k = int(round(support_fraction(p, mass) * len(p)))
+    return np.sort(order[:k])
+
+
+def structural_diagnostics(q: np.ndarray, k: np.ndarray, v: np.ndarray, q_labels: np.ndarray,
+                           o_sparse: np.ndarray, s: float, rows=None, mass: float = 0.9) -> dict:
+    """Support and residual measures of one partition of one (b, h) slice.
+
+    Readings of the pages' structural claims ([NE] NE/pool and NE/repair;
+    [TS] 3 and 4):
+      * per_query_support: mean over queries of the smallest fraction of keys
+        holding `mass` of the query's softmax mass;
+      * pooled_support: for each query group, the fraction of keys in the
+        union of its members' supports (what one shared route must keep for
+        every member), averaged over queries (each group weighted by size);
+      * hard_drop_error: ||O_dense - O_sparse||_F / ||O_dense||_F;
+      * affine_explained: share of the residual R = O_dense - O_sparse that
+        the best affine function of the sparse output explains, 1 -
+        ||R - (1 a + O_sparse A)||_F^2 / ||R||_F^2 with (a, A) least squares
+        over all rows;
+      * orthogonal_energy: the unexplained part ||R - (1 a + O_sparse A)||_F^2
+        relative to ||O_dense||_F^2.
+    `o_sparse` is the sparse output in token order.  `rows` restricts the
+    support measures to a subset of query groups' rows (all rows by default);
+    the residual measures always use every row.
+    """
+    q64, k64, v64 = (np.asarray(t, dtype=np.float64) for t in (q, k, v))
+    n = q64.shape[0]
+    logits = s * (q64 @ k64.T)
+    p = np.exp(logits - logits.max(axis=1, keepdims=True))
+    p /= p.sum(axis=1, keepdims=True)
+    dense = p @ v64
+    labels = np.asarray(q_labels)
+    sel = np.arange(n) if rows is None else np.asarray(rows)
+    per_q = np.array([support_fraction(p[i], mass) for i in sel])
+    pooled = []
+    for g in np.unique(labels[sel]):
+        members = sel[labels[sel] == g]
+        union = np.zeros(n, dtype=bool)
+        for i in members:
+            union[support_set(p[i], mass)] = True
+        pooled.extend([union.mean()] * len(members))
+    osp = np.asarray(o_sparse, dtype=np.float64)
+    r = dense - osp
+    xa = np.hstack([np.ones((n, 1)), osp])
+    coef, *_ = np.linalg.lstsq(xa, r, rcond=None)
+    left = r - xa @ coef
+    rr = float((r * r).sum())
+    return {
+        "per_query_support": float(per_q.mean()),
+        "pooled_support": float(np.mean(pooled)),
+        "hard_drop_error": float(np.linalg.norm(r) / np.linalg.norm(dense)),
+        "affine_explained": 1.0 - float((left * left).sum()) / rr if rr > 0 else 1.0,
+        "orthogonal_energy": float((left * left).sum()) / float((dense * dense).sum()),
+    }
+
+
+# ----------------------------------------------------------------------------
 # whole call
 # ----------------------------------------------------------------------------
 def sparsepr_head(q: np.ndarray, k: np.ndarray, v: np.ndarray, cfg: OracleConfig, bh: int = 0,

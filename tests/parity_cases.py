@@ -32,6 +32,8 @@ class Case:
     workload: str = ""
     router: str = "budget"
     alpha: float = 0.9
+    ridge_mode: str = "relative"
+    ridge_lambda: float = 1.0
 
     @property
     def n(self):
@@ -40,12 +42,14 @@ class Case:
     def oracle_cfg(self) -> OracleConfig:
         return OracleConfig(density=self.density, probe_rows=self.probes, n_kv_groups=self.gk,
                             n_q_groups=self.gq, residual_rank=self.rank, partition_mode=self.mode,
-                            router=self.router, alpha=self.alpha)
+                            router=self.router, alpha=self.alpha, ridge_mode=self.ridge_mode,
+                            ridge_lambda=self.ridge_lambda)
 
     def lib_cfg_kwargs(self) -> dict:
         return dict(density=self.density, probe_rows=self.probes, n_kv_groups=self.gk, n_q_groups=self.gq,
                     residual_rank=self.rank, partition_mode=0 if self.mode == "response_coupled" else 1,
-                    router=0 if self.router == "budget" else 1, alpha=self.alpha)
+                    router=0 if self.router == "budget" else 1, alpha=self.alpha, ridge_mode=self.ridge_mode,
+                    ridge_lambda=self.ridge_lambda)
 
 
 CASES = {
@@ -73,6 +77,12 @@ CASES = {
                            router="alpha", alpha=0.8),
     "alpha_c2": Case("alpha_c2", 8, 32, 32, 2, 64, "bf16", 64, 64, 0.25, 64, 32, workload="c2_dit_8k",
                      router="alpha", alpha=0.9),
+    # absolute ridge lambda: the tiny fp32 call with the lambda = 1e-3 its
+    # workload states, and a bf16 case
+    "c1_abs_lambda": Case("c1_abs_lambda", 4, 16, 16, 1, 64, "fp32", 16, 16, 0.25, 64, 16,
+                          workload="c1_tiny_fp32", ridge_mode="absolute", ridge_lambda=1e-3),
+    "bf16_d128_abs": Case("bf16_d128_abs", 2, 16, 32, 2, 128, "bf16", 16, 4, 0.3, 48, 8, seed=12,
+                          ridge_mode="absolute", ridge_lambda=0.05),
 }
 
 

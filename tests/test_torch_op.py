@@ -80,3 +80,30 @@ def test_opcheck_schema_and_fake():
     q, k, v = _qkv(1)
     torch.library.opcheck(torch.ops.sparsepr.attention.default, (q, k, v), KW,
                           test_utils=("test_schema", "test_faketensor"))
+
+
+@pytest.mark.gpu
+def test_operator_token_major_batch_of_two_matches_the_oracle():
+    """torch.ops.sparsepr.attention on [B, N, H, d] inputs with B = 2 against
+    the oracle's call on the same tensors: every (b, h) slice is its own
+    problem, seeded by its index b H + h on both sides."""
+    import numpy as np
+
+    from oracle import OracleConfig, sparsepr_call
+
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    q, k, v = _qkv(4, seed=23)
+    qb, kb, vb = (t.reshape(2, 2, *t.shape[2:]).permute(0, 2, 1, 3).contiguous() for t in (q, k, v))
+    got = torch.ops.sparsepr.attention(qb, kb, vb, layout="bnhd", **KW)
+    torch.cuda.synchronize()
+    ref = sparsepr_call(*(t.permute(0, 2, 1, 3).cpu() for t in (qb, kb, vb)),
+                        OracleConfig(density=0.3, n_kv_groups=12, n_q_groups=10, probe_rows=32, residual_rank=8))
+    out = got.permute(0, 2, 1, 3).double().cpu().numpy()
+    for b in range(2):
+        for h in range(2):
+            a, r = out[b, h], ref[b, h]
+            ma = float(np.abs(a - r).max())
+            rf = float(np.linalg.norm(a - r) / np.linalg.norm(r))
+            print(f"  (b={b}, h={h}): max-abs {ma:.2e} rel-Frobenius {rf:.2e}")
+            assert ma <= 2e-2 and rf <= 5e-3
