@@ -156,6 +156,125 @@ __device__ inline bool setup_item(const AttnArgs& a, int bh, int tile, int* seg_
   return true;
 }
 
+// Epilogue of the attention kernels: normalise, correct (b + x W V^T) on the
+// matrix cores, restore token order.  o holds the wave's 32 rows in the
+// S^T-accumulator layout (lane = row within the block, both lane halves carry
+// partial sums l of the row).
+template <int D, bool VF16>
+__device__ __attribute__((always_inline)) inline void attn_epilogue(const AttnArgs& a, int bh, f32x16 (&o)[D / 32],
+                                                                    float l, int lane, bool owner, bool qvalid,
+                                                                    int row0, int qr) {
+  constexpr int KS = D / 16, DB = D / 32;
+  const int half = lane >> 5, col = lane & 31;
+  const float ltot = l + __shfl_xor(l, 32, 64);
+  float inv = ltot > 0.f ? 1.f / ltot : 0.f;
+  if (VF16) inv = ldexpf(inv, a.vexp[bh]);
+  float x[DB][16];
+#pragma unroll
+  for (int b = 0; b < DB; ++b)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) x[b][r] = o[b][r] * inv;
+  const int rank = (a.correct && a.fitrank) ? a.fitrank[bh] : 0;
+  if (rank > 0) {
+    // Correction on the matrix cores, in the accumulators' own layout:
+    //   T^T (rank x rows) = W^T X^T,   out^T (dims x rows) = X^T + b + V T^T,
+    // so out^T lands where each lane already holds its row's dims.  X, T, W
+    // and V are split into hi + lo bf16; each product adds hi.hi + lo.hi +
+    // hi.lo (relative error about 2^-16).  W^T and V come from the per-head
+    // packed copies (hi/lo bf16, rank columns past the head's rank zero),
+    // which every workgroup of the head reads through the L2; only the
+    // owner waves read them, 32 rank columns at a time.
+    const int Rp = a.Rp;
+    const bf16_t* Wh = a.fitpk + (long long)bh * 4 * Rp * D;  // [Rp][D]: W^T, hi
+    const bf16_t* Wlo = Wh + (long long)Rp * D;               // lo
+    const bf16_t* Vh = Wlo + (long long)Rp * D;               // [D][Rp]: V, hi
+    const bf16_t* Vlo = Vh + (long long)Rp * D;               // lo
+    // B operands take 8 consecutive dims (ranks) per lane: dims 16 c + 8 half
+    // + 0..7 of the lane's row for chunk c.  The accumulator layout holds
+    // dims (r & 3) + 8 (r >> 2) + 4 half, so registers 8 sub + q and
+    // 8 sub + 4 + q are exchanged between lanes i and i + 32.
+    auto to_b = [&](const float* v16, bf16x8* hi, bf16x8* lo) __attribute__((always_inline)) {
+      float v[8];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(v16[q]), __float_as_uint(v16[4 + q]), false,
+                                                         false);
+        v[q] = __uint_as_float(sw[0]);
+        v[4 + q] = __uint_as_float(sw[1]);
+      }
+      uint32_t ph[4], pl[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        ph[j] = pack_bf16x2(v[2 * j], v[2 * j + 1]);
+        pl[j] = pack_bf16x2(v[2 * j] - __uint_as_float(ph[j] << 16), v[2 * j + 1] - __uint_as_float(ph[j] & 0xffff0000u));
+      }
+      *hi = __builtin_bit_cast(bf16x8, make_uint4(ph[0], ph[1], ph[2], ph[3]));
+      *lo = __builtin_bit_cast(bf16x8, make_uint4(pl[0], pl[1], pl[2], pl[3]));
+    };
+    bf16x8 xh[KS], xl[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) to_b(&x[ks >> 1][8 * (ks & 1)], &xh[ks], &xl[ks]);
+    // accumulators start at x + b
+    f32x16 cacc[DB];
+    const float* fb = a.fitb + (long long)bh * D;
+#pragma unroll
+    for (int b = 0; b < DB; ++b)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) cacc[b][r] = x[b][r] + fb[32 * b + (r & 3) + 8 * (r >> 2) + 4 * half];
+    for (int j0 = 0; j0 < rank && owner; j0 += 32) {
+      {
+        // T^T = W^T X^T: A = rows of W^T (rank col, dims 16 ks + 8 half ..)
+        f32x16 t = f32x16{};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const long long wo = (long long)(j0 + col) * D + 16 * ks + 8 * half;
+          const bf16x8 ah = *reinterpret_cast<const bf16x8*>(Wh + wo);
+          const bf16x8 al = *reinterpret_cast<const bf16x8*>(Wlo + wo);
+          t = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, xh[ks], t, 0, 0, 0);
+          t = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, xh[ks], t, 0, 0, 0);
+          t = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, xl[ks], t, 0, 0, 0);
+        }
+        bf16x8 th[2], tl[2];
+        float tv[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) tv[r] = t[r];
+#pragma unroll
+        for (int kr = 0; kr < 2; ++kr) to_b(&tv[8 * kr], &th[kr], &tl[kr]);
+        // out^T += V T^T: A = rows of V (dim 32 b + col, ranks 16 kr + 8 half ..)
+#pragma unroll
+        for (int b = 0; b < DB; ++b)
+#pragma unroll
+          for (int kr = 0; kr < 2; ++kr) {
+            const long long vo = (long long)(32 * b + col) * Rp + j0 + 16 * kr + 8 * half;
+            const bf16x8 vh = *reinterpret_cast<const bf16x8*>(Vh + vo);
+            const bf16x8 vl = *reinterpret_cast<const bf16x8*>(Vlo + vo);
+            cacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vh, th[kr], cacc[b], 0, 0, 0);
+            cacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vl, th[kr], cacc[b], 0, 0, 0);
+            cacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vh, tl[kr], cacc[b], 0, 0, 0);
+          }
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < DB; ++b)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) x[b][r] = cacc[b][r];
+  }
+  if (!(owner && qvalid)) return;
+  const int pos = row0 + qr;
+  const int token = a.perm_q ? a.perm_q[(long long)bh * a.N + pos] : pos;
+  bf16_t* orow = static_cast<bf16_t*>(a.o.p) + a.o.row_off(bh, token);
+#pragma unroll
+  for (int b = 0; b < DB; ++b)
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const int dm = 32 * b + 8 * r4 + 4 * half;
+      uint2 pk;
+      pk.x = pack_bf16x2(x[b][4 * r4 + 0], x[b][4 * r4 + 1]);
+      pk.y = pack_bf16x2(x[b][4 * r4 + 2], x[b][4 * r4 + 3]);
+      *reinterpret_cast<uint2*>(orow + dm) = pk;
+    }
+}
+
 // ============================================================================
 // bf16 MFMA kernel.  Per wave: 32 query rows.  S^T = K Q^T (A = K tile from
 // LDS, B = Q rows in registers) so each lane holds one query row; the online
@@ -462,114 +581,7 @@ __global__ __launch_bounds__(256, 2) void k_sparse_attn_mfma(AttnArgs a) {
     run(std::false_type{});
   }
 
-  // ---- epilogue: normalise, correct (b + x W V^T), restore token order
-  const float ltot = l + __shfl_xor(l, 32, 64);
-  float inv = ltot > 0.f ? 1.f / ltot : 0.f;
-  if (VF16) inv = ldexpf(inv, a.vexp[bh]);
-  float x[DB][16];
-#pragma unroll
-  for (int b = 0; b < DB; ++b)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) x[b][r] = o[b][r] * inv;
-  const int rank = (a.correct && a.fitrank) ? a.fitrank[bh] : 0;
-  if (rank > 0) {
-    // Correction on the matrix cores, in the accumulators' own layout:
-    //   T^T (rank x rows) = W^T X^T,   out^T (dims x rows) = X^T + b + V T^T,
-    // so out^T lands where each lane already holds its row's dims.  X, T, W
-    // and V are split into hi + lo bf16; each product adds hi.hi + lo.hi +
-    // hi.lo (relative error about 2^-16).  W^T and V come from the per-head
-    // packed copies (hi/lo bf16, rank columns past the head's rank zero),
-    // which every workgroup of the head reads through the L2; only the
-    // owner waves read them, 32 rank columns at a time.
-    const int Rp = a.Rp;
-    const bf16_t* Wh = a.fitpk + (long long)bh * 4 * Rp * D;  // [Rp][D]: W^T, hi
-    const bf16_t* Wlo = Wh + (long long)Rp * D;               // lo
-    const bf16_t* Vh = Wlo + (long long)Rp * D;               // [D][Rp]: V, hi
-    const bf16_t* Vlo = Vh + (long long)Rp * D;               // lo
-    // B operands take 8 consecutive dims (ranks) per lane: dims 16 c + 8 half
-    // + 0..7 of the lane's row for chunk c.  The accumulator layout holds
-    // dims (r & 3) + 8 (r >> 2) + 4 half, so registers 8 sub + q and
-    // 8 sub + 4 + q are exchanged between lanes i and i + 32.
-    auto to_b = [&](const float* v16, bf16x8* hi, bf16x8* lo) __attribute__((always_inline)) {
-      float v[8];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(v16[q]), __float_as_uint(v16[4 + q]), false,
-                                                         false);
-        v[q] = __uint_as_float(sw[0]);
-        v[4 + q] = __uint_as_float(sw[1]);
-      }
-      uint32_t ph[4], pl[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        ph[j] = pack_bf16x2(v[2 * j], v[2 * j + 1]);
-        pl[j] = pack_bf16x2(v[2 * j] - __uint_as_float(ph[j] << 16), v[2 * j + 1] - __uint_as_float(ph[j] & 0xffff0000u));
-      }
-      *hi = __builtin_bit_cast(bf16x8, make_uint4(ph[0], ph[1], ph[2], ph[3]));
-      *lo = __builtin_bit_cast(bf16x8, make_uint4(pl[0], pl[1], pl[2], pl[3]));
-    };
-    bf16x8 xh[KS], xl[KS];
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) to_b(&x[ks >> 1][8 * (ks & 1)], &xh[ks], &xl[ks]);
-    // accumulators start at x + b
-    f32x16 cacc[DB];
-    const float* fb = a.fitb + (long long)bh * D;
-#pragma unroll
-    for (int b = 0; b < DB; ++b)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) cacc[b][r] = x[b][r] + fb[32 * b + (r & 3) + 8 * (r >> 2) + 4 * half];
-    for (int j0 = 0; j0 < rank && owner; j0 += 32) {
-      {
-        // T^T = W^T X^T: A = rows of W^T (rank col, dims 16 ks + 8 half ..)
-        f32x16 t = f32x16{};
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          const long long wo = (long long)(j0 + col) * D + 16 * ks + 8 * half;
-          const bf16x8 ah = *reinterpret_cast<const bf16x8*>(Wh + wo);
-          const bf16x8 al = *reinterpret_cast<const bf16x8*>(Wlo + wo);
-          t = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, xh[ks], t, 0, 0, 0);
-          t = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, xh[ks], t, 0, 0, 0);
-          t = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, xl[ks], t, 0, 0, 0);
-        }
-        bf16x8 th[2], tl[2];
-        float tv[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) tv[r] = t[r];
-#pragma unroll
-        for (int kr = 0; kr < 2; ++kr) to_b(&tv[8 * kr], &th[kr], &tl[kr]);
-        // out^T += V T^T: A = rows of V (dim 32 b + col, ranks 16 kr + 8 half ..)
-#pragma unroll
-        for (int b = 0; b < DB; ++b)
-#pragma unroll
-          for (int kr = 0; kr < 2; ++kr) {
-            const long long vo = (long long)(32 * b + col) * Rp + j0 + 16 * kr + 8 * half;
-            const bf16x8 vh = *reinterpret_cast<const bf16x8*>(Vh + vo);
-            const bf16x8 vl = *reinterpret_cast<const bf16x8*>(Vlo + vo);
-            cacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vh, th[kr], cacc[b], 0, 0, 0);
-            cacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vl, th[kr], cacc[b], 0, 0, 0);
-            cacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vh, tl[kr], cacc[b], 0, 0, 0);
-          }
-      }
-    }
-#pragma unroll
-    for (int b = 0; b < DB; ++b)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) x[b][r] = cacc[b][r];
-  }
-  if (!(owner && qvalid)) return;
-  const int pos = row0 + qr;
-  const int token = a.perm_q ? a.perm_q[(long long)bh * a.N + pos] : pos;
-  bf16_t* orow = static_cast<bf16_t*>(a.o.p) + a.o.row_off(bh, token);
-#pragma unroll
-  for (int b = 0; b < DB; ++b)
-#pragma unroll
-    for (int r4 = 0; r4 < 4; ++r4) {
-      const int dm = 32 * b + 8 * r4 + 4 * half;
-      uint2 pk;
-      pk.x = pack_bf16x2(x[b][4 * r4 + 0], x[b][4 * r4 + 1]);
-      pk.y = pack_bf16x2(x[b][4 * r4 + 2], x[b][4 * r4 + 3]);
-      *reinterpret_cast<uint2*>(orow + dm) = pk;
-    }
+  attn_epilogue<D, VF16>(a, bh, o, l, lane, owner, qvalid, row0, qr);
 }
 
 // hi/lo bf16 copies of each head's fitted maps in the layouts the MFMA

@@ -426,87 +426,91 @@ __global__ __launch_bounds__(256) void k_split_rows(SplitArgs a) {
 // B[k][n]: k = 8*(lane/32)+j, n = lane%32; D[i][j]: j = lane%32,
 // i = (r%4) + 8*(r/4) + 4*(lane/32) for accumulator register r.
 // ============================================================================
-// Largest three of the 16 accumulator values a lane holds for a 32-centre
-// block.  Each value first carries its register index r in the low 4 bits of
-// its mantissa (a change below 2^-19 of its magnitude, which the error bound
-// includes), so plain max/min/median operations keep track of which centre a
-// value belongs to: register r is centre (r & 3) + 8 (r >> 2) + 4 (lane / 32)
-// of the block.  Pairs are split into (larger, smaller), pairs merge into
-// sorted triples, and triples merge as the largest three of two sorted lists.
+// Running largest three of a point's values x . y_g - c_g / 2.  Each value
+// first carries the index of its 32-centre block and its accumulator register
+// r in the low pbits = 4 + ceil(log2(blocks)) bits of its mantissa (a change
+// below 2^(pbits - 23) of its magnitude, which the error bound includes), so
+// plain max and median operations keep track of which centre a value belongs
+// to: register r of block k is centre 32 k + (r & 3) + 8 (r >> 2) + 4 (lane / 32).
 // Padding centres carry a large negative but finite bias, so no value is
 // infinite and no packed value is a NaN.
-__device__ inline float pack_reg(float v, int r) {
-  return __uint_as_float((__float_as_uint(v) & ~0xfu) | (uint32_t)r);
+//
+// Plain min/max/median instructions: the values are finite by construction,
+// so the quieting of signalling NaN inputs that the compiler puts in front of
+// fminf/fmaxf (one instruction per value coming out of an integer operation)
+// is not needed.
+__device__ inline float vmax(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
 }
-__device__ inline int packed_centre(float v, int base) {
-  const int r = (int)(__float_as_uint(v) & 0xfu);
-  return base + (r & 3) + 8 * (r >> 2);
+__device__ inline float vmed3(float a, float b, float c) {
+  float r;
+  asm("v_med3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
 }
-struct Top3 {
-  float t1, t2, t3;
+struct Seq3 {
+  float b, s, t;  // b >= s >= t, packed
 };
-// the largest three of two sorted triples
-__device__ inline Top3 merge_top3(const Top3& a, const Top3& b) {
-  Top3 t;
-  t.t1 = fmaxf(a.t1, b.t1);
-  t.t2 = __builtin_amdgcn_fmed3f(a.t1, b.t1, fmaxf(a.t2, b.t2));
-  t.t3 = fmaxf(fmaxf(a.t3, b.t3), fmaxf(fminf(a.t2, b.t1), fminf(a.t1, b.t2)));
-  return t;
-}
-__device__ inline Top3 block_top3_16(const f32x16& acc) {
-  Top3 q[4];
+__device__ inline Seq3 seq3_init() { return Seq3{-INFINITY, -INFINITY, -INFINITY}; }
+// fold in the 16 values a lane holds for 32-centre block k: with b >= s >= t,
+// t' = med3(s, t, p), s' = med3(b, s, p), b' = max(b, p)
+// The packing reads the matrix-core accumulators, so it is plain code: the
+// compiler then places the wait states a vector instruction needs before it
+// reads the result of a matrix-core instruction (it does not for inline
+// assembly).  keep, the mask of the bits a value keeps, sits in a vector
+// register so that the packing is one v_and_or_b32 with the index as its
+// scalar operand.
+__device__ inline void seq3_add_block(Seq3& st, const f32x16& acc, uint32_t keep, int k) {
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const float p0 = pack_reg(acc[4 * k], 4 * k), p1 = pack_reg(acc[4 * k + 1], 4 * k + 1);
-    const float p2 = pack_reg(acc[4 * k + 2], 4 * k + 2), p3 = pack_reg(acc[4 * k + 3], 4 * k + 3);
-    const float h0 = fmaxf(p0, p1), l0 = fminf(p0, p1), h1 = fmaxf(p2, p3), l1 = fminf(p2, p3);
-    const float ml = fmaxf(l0, l1);
-    q[k].t1 = fmaxf(h0, h1);
-    q[k].t2 = __builtin_amdgcn_fmed3f(h0, h1, ml);
-    q[k].t3 = fminf(ml, fminf(h0, h1));
+  for (int r = 0; r < 16; ++r) {
+    const float p = __uint_as_float((__float_as_uint(acc[r]) & keep) | (uint32_t)(16 * k + r));
+    st.t = vmed3(st.s, st.t, p);
+    st.s = vmed3(st.b, st.s, p);
+    st.b = vmax(st.b, p);
   }
-  return merge_top3(merge_top3(q[0], q[1]), merge_top3(q[2], q[3]));
 }
-
-// A point's running state: the largest three packed values over the centres
-// seen so far and the centres of the first two.
+__device__ inline uint32_t seq3_keep(int pbits) {
+  uint32_t v;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(v) : "s"(~((1u << pbits) - 1u)));
+  return v;
+}
+__device__ inline int seq3_centre(float v, int pbits, int half) {
+  const uint32_t bits = __float_as_uint(v) & ((1u << pbits) - 1u);
+  const int r = (int)(bits & 15u), k = (int)(bits >> 4);
+  return 32 * k + (r & 3) + 8 * (r >> 2) + 4 * half;
+}
+// A point's result: the largest three values over all its centres and the
+// centres of the first two.
 struct Best3 {
   float b, s, t;
   int bi, si;
 };
-__device__ inline Best3 best3_init() { return Best3{-INFINITY, -INFINITY, -INFINITY, 0, 0}; }
-// fold in three more sorted values whose first two belong to centres i1, i2
-// (equal values keep the earlier state's centre first)
-__device__ inline void best3_add(Best3& st, float v1, float v2, float v3, int i1, int i2) {
-  const float nt = fmaxf(fmaxf(st.t, v3), fmaxf(fminf(st.s, v1), fminf(st.b, v2)));
-  if (v1 > st.b) {
-    const bool keep = st.b >= v2;
-    st.s = keep ? st.b : v2;
-    st.si = keep ? st.bi : i2;
-    st.b = v1;
-    st.bi = i1;
-  } else {
-    const bool keep = st.s >= v1;
-    st.s = keep ? st.s : v1;
-    st.si = keep ? st.si : i1;
-  }
-  st.t = nt;
+// merge the lane's state with that of lane ^ 32 (the other half of the same
+// point's centres): the largest three of two sorted triples, the lower half
+// first on equal values (its centre is the lower one)
+__device__ inline Best3 seq3_finish(const Seq3& st, int pbits) {
+  const int half = (threadIdx.x >> 5) & 1;
+  const Seq3 o{__shfl_xor(st.b, 32, 64), __shfl_xor(st.s, 32, 64), __shfl_xor(st.t, 32, 64)};
+  const Seq3 a = half ? o : st, c = half ? st : o;  // half 0, half 1
+  const bool x1 = a.b >= c.b;
+  const float a1 = x1 ? a.s : a.b, a2 = x1 ? a.t : a.s;
+  const float c1 = x1 ? c.b : c.s, c2 = x1 ? c.s : c.t;
+  const bool x2 = a1 >= c1;
+  Best3 r;
+  r.b = x1 ? a.b : c.b;
+  r.s = x2 ? a1 : c1;
+  r.t = x2 ? (a2 >= c1 ? a2 : c1) : (a1 >= c2 ? a1 : c2);
+  r.bi = seq3_centre(r.b, pbits, x1 ? 0 : 1);
+  r.si = seq3_centre(r.s, pbits, x2 ? 0 : 1);
+  return r;
 }
-__device__ inline void best3_add_block(Best3& st, const f32x16& acc, int base) {
-  const Top3 t = block_top3_16(acc);
-  best3_add(st, t.t1, t.t2, t.t3, packed_centre(t.t1, base), packed_centre(t.t2, base));
-}
-// merge with the state of lane ^ 32 (the other half of the same point's centres)
-__device__ inline void best3_merge_halves(Best3& st) {
-  const float ob = __shfl_xor(st.b, 32, 64), os = __shfl_xor(st.s, 32, 64), ot = __shfl_xor(st.t, 32, 64);
-  const int obi = __shfl_xor(st.bi, 32, 64), osi = __shfl_xor(st.si, 32, 64);
-  if ((threadIdx.x & 63) < 32) {
-    best3_add(st, ob, os, ot, obi, osi);
-  } else {
-    Best3 o{ob, os, ot, obi, osi};
-    best3_add(o, st.b, st.s, st.t, st.bi, st.si);
-    st = o;
-  }
+// the decoded centres, kept to the G real ones (a padding centre never ranks
+// first or second while a point has two real centres; with G = 1 the second
+// is a padding centre and never used)
+__device__ inline void best3_clamp(Best3& r, int G) {
+  r.bi = min(r.bi, G - 1);
+  r.si = min(r.si, G - 1);
 }
 
 // Sum of squares of 8 bf16 values (exact products, fp32 sums).
@@ -554,9 +558,10 @@ __device__ inline void centre_bounds_to_lds(const AssignArgs& a, int bh, CentreB
 // eps_x |x~| for both.
 __device__ inline float value_bound(const AssignArgs& a, const CentreBounds& cb, float xn, float2 xb) {
   const float xs = a.xbound ? xb.x * cb.y + xb.y * cb.l : xn * a.eps_x * cb.y;
-  // the register index packed into the low mantissa bits moves a value by
-  // less than 2^-19 of its magnitude, itself at most |x~||y| + |c|/2
-  return 1.01f * (xn * cb.r + xs + (a.eps_acc + 0x1p-19f) * (xn * cb.y + 0.5f * cb.c));
+  // the block and register index packed into the low mantissa bits move a
+  // value by less than 2^(pbits - 23) of its magnitude, itself at most
+  // |x~||y| + |c|/2
+  return 1.01f * (xn * cb.r + xs + (a.eps_acc + ldexpf(1.0f, a.pbits - 23)) * (xn * cb.y + 0.5f * cb.c));
 }
 
 // A point whose best and second values lie within twice the error bound e
@@ -645,6 +650,7 @@ __global__ __launch_bounds__(512) void k_kmeans_assign(AssignArgs a) {
   }
   __syncthreads();
   const CentreBounds cbd = sbound;
+  const uint32_t keep = seq3_keep(a.pbits);
 
   const bf16_t* pbase = static_cast<const bf16_t*>(a.pts.p) + a.pts.row_off(bh, 0);
   const long long psn = a.pts.sn;
@@ -663,11 +669,11 @@ __global__ __launch_bounds__(512) void k_kmeans_assign(AssignArgs a) {
   for (int b = w; b < nblk; b += NW) {
     u32x4 nh[PB][KS];
     SP_LOAD_BLOCK(min(b + NW, nblk - 1), nh)
-    Best3 st[PB];
+    Seq3 st[PB];
     float xsq[PB];
 #pragma unroll
     for (int pb = 0; pb < PB; ++pb) {
-      st[pb] = best3_init();
+      st[pb] = seq3_init();
       xsq[pb] = 0.f;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) xsq[pb] += sumsq_bf16x8(ph[pb][ks]);
@@ -699,19 +705,20 @@ __global__ __launch_bounds__(512) void k_kmeans_assign(AssignArgs a) {
         }
       }
 #pragma unroll
-      for (int pb = 0; pb < PB; ++pb) best3_add_block(st[pb], acc[pb], cb + 4 * half);
+      for (int pb = 0; pb < PB; ++pb) seq3_add_block(st[pb], acc[pb], keep, cb >> 5);
     }
 #pragma unroll
     for (int pb = 0; pb < PB; ++pb) {
-      best3_merge_halves(st[pb]);
+      Best3 fin = seq3_finish(st[pb], a.pbits);
+      best3_clamp(fin, G);
       const float x2 = xsq[pb] + __shfl_xor(xsq[pb], 32, 64);
       const float e = value_bound(a, cbd, sqrtf(x2) * (1.0f + 0x1p-12f), make_float2(0.f, 0.f));
       const int n = n_begin + BP * b + 32 * pb + col;
       const bool live = half == 0 && n < n_end;
-      flag_append(a, bh, live, st[pb], e, n);
+      flag_append(a, bh, live, fin, e, n);
       if (live) {
-        a.labels[(long long)bh * N + n] = st[pb].bi;
-        atomicAdd(cnt + (long long)(n / kChunk) * a.gstride + st[pb].bi, 1);
+        a.labels[(long long)bh * N + n] = fin.bi;
+        atomicAdd(cnt + (long long)(n / kChunk) * a.gstride + fin.bi, 1);
       }
     }
 #pragma unroll
@@ -760,7 +767,8 @@ __global__ __launch_bounds__(512, (LO && D >= 64) ? 2 : 4) void k_kmeans_assign_
     ph[ks] = __builtin_bit_cast(bf16x8, v);
     if (LO) pl[LO ? ks : 0] = __builtin_bit_cast(bf16x8, w);
   }
-  Best3 st = best3_init();
+  Seq3 st = seq3_init();
+  const uint32_t keep = seq3_keep(a.pbits);
   float xsq = 0.f;
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) xsq += sumsq_bf16x8(__builtin_bit_cast(u32x4, ph[ks]));
@@ -819,23 +827,24 @@ __global__ __launch_bounds__(512, (LO && D >= 64) ? 2 : 4) void k_kmeans_assign_
           acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah1, pl[LO ? ks : 0], acc1, 0, 0, 0);
         }
       }
-      best3_add_block(st, acc0, c0 + cb + 4 * half);
-      if (two) best3_add_block(st, acc1, c0 + cb + 32 + 4 * half);
+      seq3_add_block(st, acc0, keep, (c0 + cb) >> 5);
+      if (two) seq3_add_block(st, acc1, keep, (c0 + cb + 32) >> 5);
     }
   }
-  best3_merge_halves(st);
+  Best3 fin = seq3_finish(st, a.pbits);
+  best3_clamp(fin, G);
   {
     const CentreBounds cbd = sbound;  // written before the staging barriers
     // split points: |x~| <= |x_hi| (1 + 2^-7)
     const float x2 = xsq + __shfl_xor(xsq, 32, 64);
     const float2 xb = (a.xbound && n < N) ? a.xbound[(long long)bh * N + n] : make_float2(0.f, 0.f);
     const float e = value_bound(a, cbd, sqrtf(x2) * (LO ? 1.0f + 0x1p-7f : 1.0f + 0x1p-12f), xb);
-    flag_append(a, bh, half == 0 && n < N, st, e, n);
+    flag_append(a, bh, half == 0 && n < N, fin, e, n);
   }
   __syncthreads();
   if (half == 0 && n < N) {
-    a.labels[(long long)bh * N + n] = st.bi;
-    atomicAdd(&hist[st.bi], 1);
+    a.labels[(long long)bh * N + n] = fin.bi;
+    atomicAdd(&hist[fin.bi], 1);
   }
   __syncthreads();
   int* cnt = a.counts + ((long long)bh * a.nchunk + blk) * a.gstride;

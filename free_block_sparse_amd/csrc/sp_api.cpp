@@ -146,6 +146,10 @@ sparsepr_status kmeans_side(Plan& p, int side, int G, int* labels_out, int* perm
   aa.ybound = p.ybound;
   aa.xbound = (side == 0 && rcp) ? p.xbound : nullptr;
   assign_eps(D, lo, &aa.eps_x, &aa.eps_acc);
+  // the assignment packs a value's 32-centre block and accumulator register
+  // into its low 4 + ceil(log2(blocks)) mantissa bits
+  aa.pbits = 4;
+  while ((1 << (aa.pbits - 4)) * 32 < G) ++aa.pbits;
   int* fc = p.fcount + side * p.T;  // key side: steps 0..T-1, query side: T..2T-1
   aa.fcstride = 2 * p.T;
   aa.flist = p.flist;

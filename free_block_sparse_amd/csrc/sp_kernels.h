@@ -59,6 +59,7 @@ struct AssignArgs {
   const float2* xbound;   // [BH, N]: bounds of |x - x~| and |x_lo| of split points, or null
   float eps_x;            // without xbound: bound of |x - x~| / |x~| and |x_lo||y_lo| / (|x~||y|)
   float eps_acc;          // relative bound of the fp32 accumulation chain
+  int pbits;              // low mantissa bits carrying a value's block and register index
   int* fcnt;              // this step's flag counter of (b,h) is fcnt[bh * fcstride]
   int fcstride;
   int4* flist;            // [BH, N] flagged points: (point, best centre, second centre, full re-decision)
