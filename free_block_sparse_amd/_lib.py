@@ -41,6 +41,9 @@ class SparseprConfig(ctypes.Structure):
         ("seed", ctypes.c_ulonglong),
         ("router", ctypes.c_int),
         ("alpha", ctypes.c_float),
+        ("rank_cap", ctypes.c_float),
+        ("svd_weighted", ctypes.c_int),
+        ("centred_query_coords", ctypes.c_int),
     ]
 
     def as_dict(self):

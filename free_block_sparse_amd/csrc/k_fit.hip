@@ -30,6 +30,7 @@ struct FitArgs {
   const double* pw;
   int M, d, R, Rcfg;
   int relative;
+  int weighted;  // subspace from the SVD of D^(1/2) R
   double lambda, cut;
   double* scratch;  // per bh: kFitScratch doubles
   float* W;
@@ -297,15 +298,21 @@ __global__ __launch_bounds__(1024) void k_fit(FitArgs a) {
   for (int dm = tid; dm < d; dm += nt) {
     xb[dm] = dot4(w, 1, Xf + dm, ldx, M) / ws;
   }
-  // Gram of the smaller side of R
+  block_sync();
+  // Gram of the smaller side of D^(1/2) R (D = I unless the subspace is weighted):
+  // sqrt(w_i w_j) r_i . r_j, or sum_m w_m r_m r_m^T
   for (int e = tid; e < ne * ne; e += nt) {
     const int i = e / ne, j = e - (e / ne) * ne;
     double acc = 0.0;
     if (i < n && j < n) {
-      if (small)
+      if (small) {
         for (int k = 0; k < d; ++k) acc += (double)Rf[i * ldx + k] * (double)Rf[j * ldx + k];
-      else
+        if (a.weighted) acc *= sqrt(w[i]) * sqrt(w[j]);
+      } else if (a.weighted) {
+        for (int mm = 0; mm < M; ++mm) acc += w[mm] * ((double)Rf[mm * ldx + i] * (double)Rf[mm * ldx + j]);
+      } else {
         for (int mm = 0; mm < M; ++mm) acc += (double)Rf[mm * ldx + i] * (double)Rf[mm * ldx + j];
+      }
     }
     G[i * ldg + j] = acc;
   }
@@ -382,7 +389,12 @@ __global__ __launch_bounds__(1024) void k_fit(FitArgs a) {
     const int dm = e / rk, k = e - (e / rk) * rk;
     const int ci = idx_s[k];
     double v;
-    if (small) {
+    if (small && a.weighted) {
+      // V = (D^(1/2) R)^T U / sigma
+      double acc = 0.0;
+      for (int mm = 0; mm < M; ++mm) acc += (double)Rf[mm * ldx + dm] * (sqrt(w[mm]) * U[mm * ldu + ci]);
+      v = acc / sig_s[k];
+    } else if (small) {
       v = dot4(Rf + dm, ldx, U + ci, ldu, M) / sig_s[k];
     } else {
       v = U[dm * ldu + ci];
@@ -394,7 +406,7 @@ __global__ __launch_bounds__(1024) void k_fit(FitArgs a) {
   for (int e = tid; e < M * rk; e += nt) {
     const int mm = e / rk, k = e - (e / rk) * rk;
     double acc = 0.0;
-    if (small) {
+    if (small && !a.weighted) {
       acc = U[mm * ldu + idx_s[k]] * sig_s[k];
     } else {
       for (int dm = 0; dm < d; ++dm) acc += (double)Rf[mm * ldx + dm] * Vr[dm * Rmax + k];
@@ -562,8 +574,9 @@ hipError_t launch_fit(const Plan& p, hipStream_t s) {
   a.M = p.M;
   a.d = p.d;
   a.R = p.R > 0 ? p.R : 1;
-  a.Rcfg = p.R;
+  a.Rcfg = p.Rfit;
   a.relative = p.ridge_mode == SPARSEPR_RIDGE_RELATIVE ? 1 : 0;
+  a.weighted = p.svd_weighted;
   a.lambda = (double)p.lambda;
   a.cut = (double)p.rank_cut;
   a.scratch = p.fitscratch;

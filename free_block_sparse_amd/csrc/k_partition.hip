@@ -1332,13 +1332,28 @@ __global__ __launch_bounds__(256) void k_centre_images(UpdateArgs a) {
 }
 
 // M_Q = s^2 sum over non-empty key groups of cbar_h cbar_h^T (d x d per (b,h));
-// 16 key groups at a time are staged in LDS, each thread owns a 4x4 block
+// 16 key groups at a time are staged in LDS, each thread owns a 4x4 block.
+// Centred query coordinates u_i - mean_h(u_ih) have the metric
+// s^2 sum_h (cbar_h - m)(cbar_h - m)^T with m the mean of the non-empty
+// centres, so the centres are centred before the outer products.
 __global__ __launch_bounds__(1024) void k_query_metric(QMetricArgs a) {
   constexpr int HB = 16;
   __shared__ double cs[HB][128];
+  __shared__ double cmean[128];
   const int bh = blockIdx.x, d = a.d, tid = threadIdx.x;
   const double* cb = a.cbar + (long long)bh * a.GK * d;
   const int* off = a.off_k + (long long)bh * (a.GK + 1);
+  if (tid < d) {
+    double sm = 0.0;
+    int cnt = 0;
+    if (a.centred)
+      for (int h = 0; h < a.GK; ++h)
+        if (off[h + 1] > off[h]) {
+          sm += cb[(long long)h * d + tid];
+          ++cnt;
+        }
+    cmean[tid] = cnt > 0 ? sm / (double)cnt : 0.0;
+  }
   const int nb = d / 4;  // 4x4 blocks per row of blocks
   const int bi = tid / nb, bj = tid - (tid / nb) * nb;
   const bool act = bi < nb;
@@ -1352,7 +1367,7 @@ __global__ __launch_bounds__(1024) void k_query_metric(QMetricArgs a) {
     for (int e = tid; e < HB * d; e += 1024) {
       const int hl = e / d, j = e - (e / d) * d;
       const int h = h0 + hl;
-      cs[hl][j] = (h < a.GK && off[h + 1] > off[h]) ? cb[(long long)h * d + j] : 0.0;
+      cs[hl][j] = (h < a.GK && off[h + 1] > off[h]) ? cb[(long long)h * d + j] - cmean[j] : 0.0;
     }
     __syncthreads();
     if (act) {
@@ -1620,7 +1635,7 @@ hipError_t launch_centre_update(const Plan& p, const UpdateArgs& a, int pts_type
 }
 
 hipError_t launch_query_metric(const Plan& p, hipStream_t s) {
-  QMetricArgs a{p.cbar, p.off_k, p.GK, p.d, p.scale, p.mq};
+  QMetricArgs a{p.cbar, p.off_k, p.GK, p.d, p.scale, p.centred_qc, p.mq};
   SP_LAUNCH(k_query_metric, dim3(p.BH), dim3(1024), s, a);
   return hipSuccess;
 }

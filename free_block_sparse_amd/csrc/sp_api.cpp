@@ -373,6 +373,9 @@ sparsepr_status sparsepr_config_default(int N, int d, sparsepr_config* out) {
   out->seed = 0;
   out->router = SPARSEPR_ROUTER_BUDGET;
   out->alpha = 0.9f;
+  out->rank_cap = 1.0f;
+  out->svd_weighted = 0;
+  out->centred_query_coords = 0;
   return SPARSEPR_OK;
 }
 

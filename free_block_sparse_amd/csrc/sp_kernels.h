@@ -139,6 +139,7 @@ struct QMetricArgs {
   const int* off_k;
   int GK, d;
   float scale;
+  int centred;  // centre the key-group centres first (query coordinates minus their mean)
   double* mq;
 };
 

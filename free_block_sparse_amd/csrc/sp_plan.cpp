@@ -38,6 +38,10 @@ sparsepr_status plan_init(Plan* p, const sparsepr_config* cfg, int B, int H, int
     return SPARSEPR_ERR_INVALID_ARG;
   if (cfg->ridge_mode != SPARSEPR_RIDGE_RELATIVE && cfg->ridge_mode != SPARSEPR_RIDGE_ABSOLUTE)
     return SPARSEPR_ERR_INVALID_ARG;
+  if (!(cfg->rank_cap > 0.0f) || !(cfg->rank_cap <= 1.0f)) return SPARSEPR_ERR_INVALID_ARG;
+  if ((cfg->svd_weighted != 0 && cfg->svd_weighted != 1) ||
+      (cfg->centred_query_coords != 0 && cfg->centred_query_coords != 1))
+    return SPARSEPR_ERR_INVALID_ARG;
 
   p->B = B;
   p->H = H;
@@ -51,6 +55,11 @@ sparsepr_status plan_init(Plan* p, const sparsepr_config* cfg, int B, int H, int
   p->Gmax = p->GK > p->GQ ? p->GK : p->GQ;
   p->M = cfg->probe_rows;
   p->R = cfg->residual_rank;
+  // the rank the fit may use: at most floor(rank_cap * M) (float32 cap times M, in fp64)
+  p->Rfit = (int)floor((double)cfg->rank_cap * (double)p->M);
+  if (p->Rfit > p->R) p->Rfit = p->R;
+  p->svd_weighted = cfg->svd_weighted;
+  p->centred_qc = cfg->centred_query_coords;
   p->Ms = cfg->n_sample_q < N ? cfg->n_sample_q : N;
   int rk = cfg->key_coord_rank;
   if (rk > d) rk = d;

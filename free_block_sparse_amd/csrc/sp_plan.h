@@ -25,6 +25,9 @@ struct Plan {
   int GK, GQ, Gmax, M, R, Ms, rK, rKpad, T, mode;
   int Dk;            // key-side k-means point dimension (padded to 16)
   int ridge_mode;
+  int Rfit;          // fit rank bound: min(R, floor(rank_cap * M))
+  int svd_weighted;  // residual subspace from the SVD of D^(1/2) R
+  int centred_qc;    // query coordinates centred per query
   int nchunk;        // ceil(N / kChunk)
   int max_tiles;     // per (b,h) upper bound of query tiles
   int n_pchunk;      // probe key chunks per (b,h)

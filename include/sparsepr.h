@@ -104,6 +104,14 @@ typedef struct {
   unsigned long long seed;/* seed of the query sample (splitmix64) */
   int router;             /* sparsepr_router */
   float alpha;            /* target retained mass in (0, 1] of SPARSEPR_ROUTER_ALPHA */
+  /* Fit and coordinate variants ([TS] 2.B "Restricción de Subespacio" and
+     "Calibración Afín"; [DG] 方法/关键模块: the weighted affine fit; [TS] 2.A:
+     query coordinates are pre-softmax logits): */
+  float rank_cap;         /* residual rank at most floor(rank_cap * M), in (0, 1]; 1 = at most M */
+  int svd_weighted;       /* 1: residual subspace from the SVD of D^(1/2) R (probe weights on the
+                             rows); 0: from the SVD of R */
+  int centred_query_coords; /* 1: query coordinates minus each query's mean logit over the
+                               non-empty key groups; 0: raw logits */
 } sparsepr_config;
 
 /* Input/output description.  Strides are in elements, order [b, h, n, d]. */
@@ -145,7 +153,8 @@ typedef struct {
    density 0.25, 64 probe rows, G_K = G_Q = clamp(N/128, 1, 256), r = 32,
    relative ridge lambda 1.0, T = 10, M_s = 256, r_K = 32, scale 0,
    rank_cut 1e-6, response-coupled partition, seed 0, budget router
-   (alpha 0.9 for the alpha router). */
+   (alpha 0.9 for the alpha router), rank_cap 1, unweighted residual
+   subspace, raw (uncentred) query coordinates. */
 sparsepr_status sparsepr_config_default(int N, int d, sparsepr_config* out);
 
 /* Check a config against a shape (no device work). */

@@ -69,6 +69,9 @@ class OracleConfig:
     rank_cut: float = 1e-6
     router: str = "budget"         # "budget" (pair budget from density) or "alpha" (per-group coverage)
     alpha: float = 0.9             # target retained mass of the "alpha" router
+    rank_cap: float = 1.0          # residual rank at most floor(rank_cap * M) (1.0: at most M)
+    svd_weighted: bool = False     # subspace from the SVD of D^1/2 R instead of R
+    centred_query_coords: bool = False  # query coordinates minus each query's mean logit
 
 
 def softmax_scale(cfg: OracleConfig, d: int) -> float:
@@ -220,10 +223,16 @@ def group_means(x: np.ndarray, perm: np.ndarray, offsets: np.ndarray) -> np.ndar
 # ----------------------------------------------------------------------------
 # a7: query-response coordinates
 # ----------------------------------------------------------------------------
-def query_coordinates(q: np.ndarray, cbar_nonempty: np.ndarray, s: float) -> np.ndarray:
+def query_coordinates(q: np.ndarray, cbar_nonempty: np.ndarray, s: float, centred: bool = False) -> np.ndarray:
     """u_{i,h} = s * q_i . cbar_h: each query's pre-softmax logits against the
-    K/V group centres ([TS] 2.A, [NE] NE/method).  U4: raw, uncentred."""
-    return s * (q.astype(np.float64) @ cbar_nonempty.T)
+    K/V group centres ([TS] 2.A, [NE] NE/method).  U4: raw, uncentred by
+    default; with ``centred`` each query's mean logit over the groups is
+    removed (the softmax does not see a constant added to a query's logits).
+    """
+    u = s * (q.astype(np.float64) @ cbar_nonempty.T)
+    if centred:
+        u = u - u.mean(axis=1, keepdims=True)
+    return u
 
 
 # ----------------------------------------------------------------------------
@@ -456,7 +465,8 @@ def sparse_attention(qp: np.ndarray, kp: np.ndarray, vp: np.ndarray, granted: np
 # a14: probe-fitted residual reconstruction
 # ----------------------------------------------------------------------------
 def fit_residual(r: np.ndarray, x: np.ndarray, w: np.ndarray, rank: int, lam: float,
-                 cut: float = 1e-6, relative: bool = False) -> dict:
+                 cut: float = 1e-6, relative: bool = False, rank_cap: float = 1.0,
+                 svd_weighted: bool = False) -> dict:
     """Fit R ~ b + x B inside the top singular subspace of the probe residuals.
 
     The residual of a probe row is its exact dense output minus its sparse
@@ -470,17 +480,24 @@ def fit_residual(r: np.ndarray, x: np.ndarray, w: np.ndarray, rank: int, lam: fl
         W = (Xc^T D Xc + lam I)^-1 Xc^T D Yc,  Y = R V,  b' = ybar - xbar W,
         B = W V^T,  b = b' V^T.
     With ``relative`` the penalty is lam * trace(Xc^T D Xc) / d.
+    Variants: ``rank_cap`` also bounds r' by floor(rank_cap * M) (a fit of
+    rank M plus an intercept interpolates M probe rows); ``svd_weighted`` takes
+    the subspace from the SVD of D^(1/2) R, the probe weights applied to the
+    rows, instead of R.
     """
     m, d = r.shape
     out = {"rank": 0, "sigma": np.zeros(0), "V": np.zeros((d, 0)), "W": np.zeros((d, 0)),
            "B": np.zeros((d, d)), "b": np.zeros(d)}
     if m == 0:
         return out
-    _, sig, vt = np.linalg.svd(r, full_matrices=False)
+    rs = np.sqrt(w)[:, None] * r if svd_weighted else r
+    _, sig, vt = np.linalg.svd(rs, full_matrices=False)
     out["sigma"] = sig
     if sig.size == 0 or not (sig[0] > 0):
         return out
-    rp = int(min(rank, m, d, int((sig > cut * sig[0]).sum())))
+    # the cap arrives as a float32 value (as the library stores it), times M in fp64
+    cap = int(math.floor(float(np.float32(rank_cap)) * m))
+    rp = int(min(rank, m, cap, d, int((sig > cut * sig[0]).sum())))
     if rp == 0:
         return out
     v = vt[:rp].T
@@ -606,7 +623,7 @@ def sparsepr_head(q: np.ndarray, k: np.ndarray, v: np.ndarray, cfg: OracleConfig
             kv_labels, _ = kmeans(z, gk, cfg.kmeans_iters)
             perm_k, nk, off_k = group_by_labels(kv_labels, gk)
             cbar = group_means(k64, perm_k, off_k)
-            u = query_coordinates(q64, cbar[nk > 0], s)
+            u = query_coordinates(q64, cbar[nk > 0], s, centred=cfg.centred_query_coords)
             q_labels, _ = kmeans(u, gq, cfg.kmeans_iters)
             res.update(sample=sample, m_k=m_k, eigvals=lam, eigvecs=vec, z=z, u=u)
         elif cfg.partition_mode == "independent":
@@ -634,7 +651,8 @@ def sparsepr_head(q: np.ndarray, k: np.ndarray, v: np.ndarray, cfg: OracleConfig
     o_de = dense_attention(qp[probes], kp, vp, s) if probes.size else np.zeros((0, d))
     resid = o_de - o_sp[probes]
     fit = fit_residual(resid, o_sp[probes], w, cfg.residual_rank, cfg.ridge_lambda, cfg.rank_cut,
-                       relative=cfg.ridge_mode == "relative")
+                       relative=cfg.ridge_mode == "relative", rank_cap=cfg.rank_cap,
+                       svd_weighted=cfg.svd_weighted)
 
     corrected = o_sp + fit["b"][None, :] + o_sp @ fit["B"]
     corrected[probes] = o_de

@@ -34,6 +34,9 @@ class Case:
     alpha: float = 0.9
     ridge_mode: str = "relative"
     ridge_lambda: float = 1.0
+    rank_cap: float = 1.0
+    svd_weighted: bool = False
+    centred: bool = False
 
     @property
     def n(self):
@@ -43,13 +46,15 @@ class Case:
         return OracleConfig(density=self.density, probe_rows=self.probes, n_kv_groups=self.gk,
                             n_q_groups=self.gq, residual_rank=self.rank, partition_mode=self.mode,
                             router=self.router, alpha=self.alpha, ridge_mode=self.ridge_mode,
-                            ridge_lambda=self.ridge_lambda)
+                            ridge_lambda=self.ridge_lambda, rank_cap=self.rank_cap,
+                            svd_weighted=self.svd_weighted, centred_query_coords=self.centred)
 
     def lib_cfg_kwargs(self) -> dict:
         return dict(density=self.density, probe_rows=self.probes, n_kv_groups=self.gk, n_q_groups=self.gq,
                     residual_rank=self.rank, partition_mode=0 if self.mode == "response_coupled" else 1,
                     router=0 if self.router == "budget" else 1, alpha=self.alpha, ridge_mode=self.ridge_mode,
-                    ridge_lambda=self.ridge_lambda)
+                    ridge_lambda=self.ridge_lambda, rank_cap=self.rank_cap, svd_weighted=int(self.svd_weighted),
+                    centred_query_coords=int(self.centred))
 
 
 CASES = {
@@ -83,6 +88,15 @@ CASES = {
                           workload="c1_tiny_fp32", ridge_mode="absolute", ridge_lambda=1e-3),
     "bf16_d128_abs": Case("bf16_d128_abs", 2, 16, 32, 2, 128, "bf16", 16, 4, 0.3, 48, 8, seed=12,
                           ridge_mode="absolute", ridge_lambda=0.05),
+    # fit and coordinate variants: the residual subspace from the weighted
+    # SVD (a d x d Gram with 200 > d probes, and the dual M x M form), a rank
+    # capped at half the probes (16 probes, rank 16 -> 8), centred query
+    # coordinates
+    "wsvd_d64": Case("wsvd_d64", 4, 10, 25, 2, 64, "bf16", 12, 10, 0.3, 32, 8, seed=16, svd_weighted=True),
+    "wsvd_primal": Case("wsvd_primal", 2, 16, 32, 1, 64, "bf16", 16, 8, 0.3, 200, 16, seed=17, svd_weighted=True),
+    "cap_m16": Case("cap_m16", 4, 16, 16, 2, 64, "bf16", 16, 16, 0.25, 16, 16, seed=18, rank_cap=0.5),
+    "centred_c2": Case("centred_c2", 8, 32, 32, 2, 64, "bf16", 64, 64, 0.25, 64, 32, workload="c2_dit_8k",
+                       centred=True),
 }
 
 
@@ -172,7 +186,7 @@ def query_labels_given_keys(q64: np.ndarray, k64: np.ndarray, kv_labels, cfg: Or
     s = softmax_scale(cfg, q64.shape[1])
     perm_k, nk, off_k = group_by_labels(np.asarray(kv_labels, dtype=np.int64), cfg.n_kv_groups)
     cbar = group_means(k64, perm_k, off_k)
-    u = query_coordinates(q64, cbar[nk > 0], s)
+    u = query_coordinates(q64, cbar[nk > 0], s, centred=cfg.centred_query_coords)
     labels, _ = kmeans(u, cfg.n_q_groups, cfg.kmeans_iters)
     return labels
 

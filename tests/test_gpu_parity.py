@@ -197,7 +197,8 @@ def test_fit_matches_oracle_fit_on_the_same_probe_rows(name):
         od = res["o_dense"][h].double().cpu().numpy()
         os_ = res["o_sparse"][h].double().cpu().numpy()
         f = fit_residual(od - os_, os_, r["probe_weights"], oc.residual_rank, oc.ridge_lambda, oc.rank_cut,
-                         relative=oc.ridge_mode == "relative")
+                         relative=oc.ridge_mode == "relative", rank_cap=oc.rank_cap,
+                         svd_weighted=oc.svd_weighted)
         rk = int(res["rank"][h])
         assert rk == f["rank"]
         wm = res["W"][h].double().cpu().numpy()[:, :rk]
