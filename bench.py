@@ -42,6 +42,13 @@ def parse():
     ap.add_argument("--router", choices=("budget", "alpha"), default="budget",
                     help="cell selection: pair budget from the density, or per-group target retained mass")
     ap.add_argument("--alpha", type=float, default=0.9, help="target retained mass of --router alpha")
+    ap.add_argument("--diagnostics", action="store_true",
+                    help="structural diagnostics of both partitions (support, affine-explainable residual)")
+    ap.add_argument("--diag-heads", type=int, default=4, help="heads measured by --diagnostics")
+    ap.add_argument("--diag-rows", type=int, default=8, help="measured queries per query group")
+    ap.add_argument("--rank-cap", type=float, default=1.0, help="residual rank at most floor(cap * M)")
+    ap.add_argument("--svd-weighted", action="store_true", help="residual subspace from the weighted SVD")
+    ap.add_argument("--centred", action="store_true", help="centred query coordinates")
     ap.add_argument("--sweep", choices=("density", "probes", "headdim", "all"), default=None,
                     help="instead of the bench line: one JSON line per point of a quality/efficiency sweep "
                          "(both partitions; ms/call, rho_exec, corrected and hard-drop error vs dense)")
@@ -127,7 +134,9 @@ def sweep(args, sp, torch, w, x) -> int:
         out = torch.empty_like(q)
         for mode in ("response_coupled", "independent"):
             cfg = sp.make_config(N, dd, density=rho, probe_rows=m, n_kv_groups=w.n_kv_groups,
-                                 n_q_groups=w.n_q_groups, residual_rank=w.residual_rank, partition_mode=mode)
+                                 n_q_groups=w.n_q_groups, residual_rank=w.residual_rank, partition_mode=mode,
+                                 rank_cap=args.rank_cap, svd_weighted=int(args.svd_weighted),
+                                 centred_query_coords=int(args.centred))
             sp.sparsepr_attention(q, k, v, cfg, out=out, workspace=ws)  # warm-up
             ms = min(time_fn(lambda: sp.sparsepr_attention(q, k, v, cfg, out=out, workspace=ws), 3, torch))
             _, _, st = sp.sparsepr_attention_profile(q, k, v, cfg, out=out, workspace=ws)
@@ -138,9 +147,40 @@ def sweep(args, sp, torch, w, x) -> int:
             herr = float((hard.float() - dense).norm()) / dn
             rho_exec = sum(h["routed_pairs"] + h["probe_pairs"] for h in heads) / (B * H * N * N)
             print(json.dumps({"sweep": axis, "workload": w.name, "partition": mode, "d": dd, "density": rho,
-                              "probe_rows": m, "rho_exec": round(rho_exec, 5), "ms_per_call": round(ms, 4),
+                              "probe_rows": m, "rank_cap": args.rank_cap, "svd_weighted": bool(args.svd_weighted),
+                              "centred": bool(args.centred), "rho_exec": round(rho_exec, 5),
+                              "ms_per_call": round(ms, 4),
                               "rel_err_corrected": round(err, 5), "rel_err_hard_drop": round(herr, 5)}), flush=True)
             log(f"{axis} {mode} d {dd} rho {rho} M {m}: {ms:.2f} ms, err {err:.4f} (hard drop {herr:.4f})")
+    return 0
+
+
+def diagnostics(args, sp, torch, w, x) -> int:
+    """Structural diagnostics of both partitions on the first heads of the workload."""
+    import numpy as np
+    from free_block_sparse_amd.diagnostics import structural_diagnostics
+
+    hh = min(args.diag_heads, w.heads)
+    q, k, v = (x[t][:, :hh].contiguous().cuda() for t in ("q", "k", "v"))
+    B, H, N, d = q.shape
+    rng = np.random.default_rng(0)
+    for mode in ("response_coupled", "independent"):
+        cfg = sp.make_config(N, d, density=w.density, probe_rows=w.probe_rows, n_kv_groups=w.n_kv_groups,
+                             n_q_groups=w.n_q_groups, residual_rank=w.residual_rank, partition_mode=mode)
+        ql, _ = sp.sparsepr_partition(q, k, v, cfg)
+        # the same number of measured queries from every query group of head 0
+        lab = ql[0].cpu().numpy()
+        rows = []
+        for g in np.unique(lab):
+            members = np.nonzero(lab == g)[0]
+            rows += list(rng.choice(members, size=min(args.diag_rows, members.size), replace=False))
+        t0 = time.time()
+        res = structural_diagnostics(q, k, v, cfg, rows=sorted(int(r) for r in rows))
+        for h, r in enumerate(res):
+            print(json.dumps({"diagnostics": mode, "workload": w.name, "head": h, "density": w.density,
+                              "measured_rows": len(rows), **{kk: round(vv, 5) for kk, vv in r.items()}}),
+                  flush=True)
+        log(f"diagnostics {mode}: {len(res)} heads in {time.time() - t0:.1f}s")
     return 0
 
 
@@ -179,6 +219,8 @@ def main() -> int:
     log(f"inputs ready in {time.time() - t0:.1f}s")
     if args.sweep:
         return sweep(args, sp, torch, w, x)
+    if args.diagnostics:
+        return diagnostics(args, sp, torch, w, x)
     q, k, v = (x[t].cuda() for t in ("q", "k", "v"))
     B, H, N, d = q.shape
     cfg_kw = dict(density=w.density, probe_rows=w.probe_rows, n_kv_groups=w.n_kv_groups,
