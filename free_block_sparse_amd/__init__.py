@@ -106,25 +106,51 @@ def sparsepr_workspace_size(cfg: SparseprConfig, B: int, H: int, N: int, d: int,
 
 
 class Workspace:
-    """A reusable device workspace (grown on demand)."""
+    """Reusable device workspaces, one per (device, stream).
+
+    Calls that share a workspace must be ordered; keeping one buffer per
+    stream means calls on different streams never share one.  A buffer is
+    never released while the Workspace lives: when a call needs more, a larger
+    buffer (at least twice the size) replaces it for later calls and the old
+    one is kept, so a HIP graph captured with the old pointer stays valid.
+    """
 
     def __init__(self):
-        self.buf = None
+        self.bufs = {}     # (device index, stream handle) -> current buffer
+        self.retired = []  # superseded buffers, kept alive
 
-    def get(self, nbytes: int, device):
+    def get(self, nbytes: int, device, stream=None):
         torch = _torch()
-        if self.buf is None or self.buf.numel() < nbytes or self.buf.device != device:
-            self.buf = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
-        return self.buf
+        s = stream if stream is not None else torch.cuda.current_stream(device)
+        key = (device.index if device.index is not None else torch.cuda.current_device(), s.cuda_stream)
+        buf = self.bufs.get(key)
+        if buf is None or buf.numel() < nbytes:
+            if buf is not None:
+                self.retired.append(buf)
+                nbytes = max(nbytes, 2 * buf.numel())
+            with torch.cuda.stream(s):
+                buf = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+            self.bufs[key] = buf
+        return buf
 
 
 _default_ws = Workspace()
 
 
-def _ws(cfg, q, workspace):
+def _ws(cfg, q, workspace, stream=None):
     nbytes = sparsepr_workspace_size(cfg, *q.shape, _dtype_code(q))
-    buf = (workspace or _default_ws).get(nbytes, q.device)
+    buf = (workspace or _default_ws).get(nbytes, q.device, stream)
     return buf, nbytes
+
+
+def _on_stream(stream, *tensors) -> None:
+    """Tell the caching allocator that a call on an explicit stream uses these
+    tensors, so their memory is not reused before that stream's work ends."""
+    if stream is None:
+        return
+    for t in tensors:
+        if t is not None:
+            t.record_stream(stream)
 
 
 def _ptr(t) -> Optional[int]:
@@ -155,10 +181,11 @@ def sparsepr_attention(q, k, v, cfg: SparseprConfig, out=None, workspace: Option
     torch = _torch()
     out = torch.empty_like(q) if out is None else out
     io = _tensors(q, k, v, out)
-    buf, nbytes = _ws(cfg, q, workspace)
+    buf, nbytes = _ws(cfg, q, workspace, stream)
     st = _stats_buf(q) if with_stats else None
     check(lib().sparsepr_attention(ctypes.byref(cfg), ctypes.byref(io), buf.data_ptr(), nbytes,
                                    _stream(stream), _ptr(st)), "sparsepr_attention")
+    _on_stream(stream, out, st)
     return (out, st) if with_stats else out
 
 
@@ -171,6 +198,7 @@ def sparsepr_attention_noalloc(q, k, v, cfg: SparseprConfig, out=None, stream=No
     st = _stats_buf(q) if with_stats else None
     check(lib().sparsepr_attention_noalloc(ctypes.byref(cfg), ctypes.byref(io), _stream(stream), _ptr(st)),
           "sparsepr_attention_noalloc")
+    _on_stream(stream, out, st)
     return (out, st) if with_stats else out
 
 
@@ -184,11 +212,12 @@ def sparsepr_attention_profile(q, k, v, cfg, out=None, workspace: Optional[Works
     torch = _torch()
     out = torch.empty_like(q) if out is None else out
     io = _tensors(q, k, v, out)
-    buf, nbytes = _ws(cfg, q, workspace)
+    buf, nbytes = _ws(cfg, q, workspace, stream)
     st = _stats_buf(q)
     ms = (ctypes.c_float * len(STAGES))()
     check(lib().sparsepr_attention_profile(ctypes.byref(cfg), ctypes.byref(io), buf.data_ptr(), nbytes,
                                            _stream(stream), st.data_ptr(), ms), "sparsepr_attention_profile")
+    _on_stream(stream, out, st)
     return out, dict(zip(STAGES, list(ms))), st
 
 
@@ -197,13 +226,14 @@ def sparsepr_attention_with_partition(q, k, v, cfg, q_labels, kv_labels, out=Non
     torch = _torch()
     out = torch.empty_like(q) if out is None else out
     io = _tensors(q, k, v, out)
-    buf, nbytes = _ws(cfg, q, workspace)
+    buf, nbytes = _ws(cfg, q, workspace, stream)
     st = _stats_buf(q) if with_stats else None
     ql = q_labels.to(torch.int32).contiguous()
     kl = kv_labels.to(torch.int32).contiguous()
     check(lib().sparsepr_attention_with_partition(ctypes.byref(cfg), ctypes.byref(io), ql.data_ptr(),
                                                   kl.data_ptr(), buf.data_ptr(), nbytes, _stream(stream),
                                                   _ptr(st)), "sparsepr_attention_with_partition")
+    _on_stream(stream, out, st, ql, kl)
     return (out, st) if with_stats else out
 
 
@@ -215,7 +245,7 @@ def sparsepr_key_metric(q, k, v, cfg, workspace=None, stream=None):
     ms = min(cfg.n_sample_q, N)
     dummy_o = torch.empty_like(q)
     io = _tensors(q, k, v, dummy_o)
-    buf, nbytes = _ws(cfg, q, workspace)
+    buf, nbytes = _ws(cfg, q, workspace, stream)
     smp = torch.empty(B * H, ms, dtype=torch.int32, device=q.device)
     mk = torch.empty(B * H, d, d, dtype=torch.float64, device=q.device)
     ev = torch.empty(B * H, d, dtype=torch.float64, device=q.device)
@@ -233,7 +263,7 @@ def sparsepr_partition(q, k, v, cfg, workspace=None, stream=None):
     torch = _torch()
     B, H, N, d = q.shape
     io = _tensors(q, k, v, torch.empty_like(q))
-    buf, nbytes = _ws(cfg, q, workspace)
+    buf, nbytes = _ws(cfg, q, workspace, stream)
     ql = torch.empty(B * H, N, dtype=torch.int32, device=q.device)
     kl = torch.empty(B * H, N, dtype=torch.int32, device=q.device)
     check(lib().sparsepr_partition(ctypes.byref(cfg), ctypes.byref(io), buf.data_ptr(), nbytes,
@@ -246,7 +276,7 @@ def sparsepr_route(q, k, v, cfg, q_labels, kv_labels, workspace=None, stream=Non
     torch = _torch()
     B, H, N, d = q.shape
     io = _tensors(q, k, v, torch.empty_like(q))
-    buf, nbytes = _ws(cfg, q, workspace)
+    buf, nbytes = _ws(cfg, q, workspace, stream)
     dev = q.device
     BH, GQ, GK = B * H, cfg.n_q_groups, cfg.n_kv_groups
     res = {
@@ -273,11 +303,12 @@ def sparsepr_sparse_attention(q, k, v, cfg, q_labels, kv_labels, out=None, works
     torch = _torch()
     out = torch.empty_like(q) if out is None else out
     io = _tensors(q, k, v, out)
-    buf, nbytes = _ws(cfg, q, workspace)
+    buf, nbytes = _ws(cfg, q, workspace, stream)
     ql = q_labels.to(torch.int32).contiguous()
     kl = kv_labels.to(torch.int32).contiguous()
     check(lib().sparsepr_sparse_attention(ctypes.byref(cfg), ctypes.byref(io), ql.data_ptr(), kl.data_ptr(),
                                           buf.data_ptr(), nbytes, _stream(stream)), "sparsepr_sparse_attention")
+    _on_stream(stream, out, ql, kl)
     return out
 
 
@@ -287,7 +318,7 @@ def sparsepr_probe_fit(q, k, v, cfg, q_labels, kv_labels, workspace=None, stream
     B, H, N, d = q.shape
     BH, M, R = B * H, cfg.probe_rows, max(cfg.residual_rank, 1)
     io = _tensors(q, k, v, torch.empty_like(q))
-    buf, nbytes = _ws(cfg, q, workspace)
+    buf, nbytes = _ws(cfg, q, workspace, stream)
     dev = q.device
     res = {
         "probe_pos": torch.empty(BH, M, dtype=torch.int32, device=dev),
@@ -305,6 +336,7 @@ def sparsepr_probe_fit(q, k, v, cfg, q_labels, kv_labels, workspace=None, stream
                                    res["o_dense"].data_ptr(), res["o_sparse"].data_ptr(), res["W"].data_ptr(),
                                    res["V"].data_ptr(), res["b"].data_ptr(), res["rank"].data_ptr()),
           "sparsepr_probe_fit")
+    _on_stream(stream, ql, kl, *res.values())
     return res
 
 
@@ -314,6 +346,7 @@ def sparsepr_dense_attention(q, k, v, out=None, scale: float = 0.0, stream=None)
     io = _tensors(q, k, v, out)
     check(lib().sparsepr_dense_attention(ctypes.byref(io), float(scale), _stream(stream)),
           "sparsepr_dense_attention")
+    _on_stream(stream, out)
     return out
 
 

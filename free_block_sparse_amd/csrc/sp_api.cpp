@@ -310,29 +310,45 @@ int split_heads(int B, int H) { return (B == 1 && H >= 2) ? H / 2 : 0; }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// Per-device side stream (default priority) and fork/join events, created on
-// first use and kept for the life of the process.  The mutex is held while a
-// call enqueues its fork-to-join sequence, so that concurrent calls on one
-// device cannot interleave records of the shared events.
+// A side stream (default priority) and fork/join events per caller stream
+// and device, created on the first two-stream call on that stream and kept
+// for the life of the process: scheduling objects only, no data passes
+// between calls through them.  Calls on different caller streams use
+// different side streams, so they neither serialise on one another nor land
+// in one another's graph capture.  Nothing is created while the caller's
+// stream is capturing: a call with no side stream yet then runs on the
+// caller's stream alone.  The mutex is held while a call enqueues its
+// fork-to-join sequence, so that concurrent calls on one caller stream cannot
+// interleave records of its events.
 struct SideRes {
   hipStream_t s;
   hipEvent_t fork, join;
 };
 std::mutex g_side_mu;
 
-sparsepr_status side_resources(SideRes* out) {
-  static std::map<int, SideRes> res;
+// *out is left null (and OK returned) when the side stream would have to be
+// created during a capture.  Called with g_side_mu held.
+sparsepr_status side_resources(hipStream_t caller, SideRes* out, bool* have) {
+  static std::map<std::pair<int, hipStream_t>, SideRes> res;
   int dev = 0;
   HIPCHK(hipGetDevice(&dev));
-  auto it = res.find(dev);
+  const auto key = std::make_pair(dev, caller);
+  auto it = res.find(key);
   if (it == res.end()) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (caller) HIPCHK(hipStreamIsCapturing(caller, &cs));
+    if (cs != hipStreamCaptureStatusNone) {
+      *have = false;
+      return SPARSEPR_OK;
+    }
     SideRes r;
     HIPCHK(hipStreamCreateWithFlags(&r.s, hipStreamNonBlocking));
     HIPCHK(hipEventCreateWithFlags(&r.fork, hipEventDisableTiming));
     HIPCHK(hipEventCreateWithFlags(&r.join, hipEventDisableTiming));
-    it = res.emplace(dev, r).first;
+    it = res.emplace(key, r).first;
   }
   *out = it->second;
+  *have = true;
   return SPARSEPR_OK;
 }
 
@@ -442,7 +458,14 @@ sparsepr_status sparsepr_attention(const sparsepr_config* cfg, const sparsepr_te
   p2.bh0 = h1;
   std::lock_guard<std::mutex> lk(g_side_mu);
   SideRes r;
-  SPCHK(side_resources(&r));
+  bool have = false;
+  SPCHK(side_resources(s, &r, &have));
+  if (!have) {
+    Plan p;
+    SPCHK(prepare(p, cfg, io, workspace, workspace_bytes));
+    SPCHK(run_partition(p, s));
+    return run_after_partition(p, s, stats);
+  }
   // the second half starts once the first half's eigensolve is done, so
   // that the halves' latency-bound stages fall on each other's
   // throughput-bound ones instead of on each other

@@ -171,13 +171,24 @@ sparsepr_status sparsepr_workspace_size(const sparsepr_config* cfg, int B, int H
    correction, output restoration).  Writes o in the original token order.
    `stats` (device pointer, nullable) receives B*H sparsepr_head_stats.
    With B = 1 and H >= 2 the heads run in two halves: the second half on a
-   stream the library keeps per device (created on first use, default
-   priority), forked from `stream` once the first half's key eigensolve is
-   enqueued and joined back to `stream` with an event before the call
-   returns.  Work enqueued on `stream` after the call therefore sees the whole
-   output, and the fork and join are recorded by HIP graph capture of
-   `stream` like any other work.  The result is the same as the unsplit
-   call's.  Concurrent calls on one device serialise only their enqueueing. */
+   side stream that the library keeps for this caller stream and device,
+   forked from `stream` once the first half's key eigensolve is enqueued and
+   joined back to `stream` with an event before the call returns.  Work
+   enqueued on `stream` after the call therefore sees the whole output, and
+   the fork and join are recorded by HIP graph capture of `stream` like any
+   other work.  The result is the same as the unsplit call's.
+   State: the side stream and its two events are created on the first split
+   call on a caller stream (default priority) and kept until the process
+   ends; they order work and carry no data between calls (every
+   intermediate lives in `workspace`, as the pages' per-call calibration
+   with no persistent state requires -- [DG] "Partition the Support,
+   Reconstruct the Residual" digest, 行业影响/与现有工作流的接口).  Nothing
+   is created while `stream` is capturing: a first call on a stream under
+   capture runs both halves on `stream` (one stream, same result).  Calls on
+   different caller streams use different side streams and may run
+   concurrently; calls on one caller stream serialise only their enqueueing
+   (a process-wide mutex), and, sharing a workspace, must be ordered by the
+   caller as every call must. */
 sparsepr_status sparsepr_attention(const sparsepr_config* cfg, const sparsepr_tensors* io,
                                    void* workspace, size_t workspace_bytes, void* stream,
                                    sparsepr_head_stats* stats);
@@ -245,8 +256,13 @@ sparsepr_status sparsepr_key_metric(const sparsepr_config* cfg, const sparsepr_t
                                     void* workspace, size_t workspace_bytes, void* stream,
                                     int* sample_idx, double* m_k, double* eigvals, double* key_map);
 
-/* Stages a1-a8: response-coupled (or independent) partition.  Writes the
-   labels of the last Lloyd step (device int32 [B*H, N] each). */
+/* Stages a1-a8: response-coupled (or independent) partition ([TS] 2.A:
+   sampled queries define the key metric, keys are grouped by k-means in its
+   leading eigenvectors, queries by k-means on their logits against the key
+   groups' centres, in one asymmetric pass; [NE] NE/method, which also sets
+   the independent comparison partition against it).  Writes the labels of the last
+   Lloyd step (device int32 [B*H, N] each): the assignment of an fp64 Lloyd
+   iteration (near ties re-decided in fp64).  Errors as sparsepr_attention. */
 sparsepr_status sparsepr_partition(const sparsepr_config* cfg, const sparsepr_tensors* io,
                                    void* workspace, size_t workspace_bytes, void* stream,
                                    int* q_labels, int* kv_labels);
@@ -262,8 +278,11 @@ sparsepr_status sparsepr_route(const sparsepr_config* cfg, const sparsepr_tensor
                                int* perm_q, int* perm_k, int* off_q, int* off_k,
                                int* csr_rowptr, int* csr_cols, sparsepr_head_stats* stats);
 
-/* Stage a12 alone from given labels: the uncorrected ("hard-drop") sparse
-   output written to io->o in the original token order. */
+/* Stage a12 alone from given labels ([TS] 2.C: attention over the granted
+   blocks of the group-contiguous layout; [NE] NE/exec): the uncorrected
+   ("hard-drop") sparse output, each query's softmax taken over its group's
+   granted keys only, written to io->o in the original token order.  Labels
+   outside [0, G) are clamped.  Errors as sparsepr_attention. */
 sparsepr_status sparsepr_sparse_attention(const sparsepr_config* cfg, const sparsepr_tensors* io,
                                           const int* q_labels, const int* kv_labels,
                                           void* workspace, size_t workspace_bytes, void* stream);

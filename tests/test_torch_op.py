@@ -58,7 +58,7 @@ def test_hip_graph_capture_replays_match_eager():
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
     q, k, v = _qkv(2)
-    eager = torch.ops.sparsepr.attention(q, k, v, **KW)  # also sizes the workspace before capture
+    eager = torch.ops.sparsepr.attention(q, k, v, **KW)
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
@@ -107,3 +107,33 @@ def test_operator_token_major_batch_of_two_matches_the_oracle():
             rf = float(np.linalg.norm(a - r) / np.linalg.norm(r))
             print(f"  (b={b}, h={h}): max-abs {ma:.2e} rel-Frobenius {rf:.2e}")
             assert ma <= 2e-2 and rf <= 5e-3
+
+
+@pytest.mark.gpu
+def test_first_call_ever_on_a_stream_under_capture():
+    """A capture stream that no call has used: the library creates no side
+    stream during the capture and runs the call on the capture stream alone;
+    its workspace is that stream's own buffer (allocated in the capture's
+    pool).  Replays, with eager calls on the default stream between them,
+    match the eager result."""
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import free_block_sparse_amd as sp
+
+    q, k, v = _qkv(2)  # B = 1, H = 2: the call that splits its heads over two streams
+    B, H, N, d = q.shape
+    cfg = sp.make_config(N, d, density=0.25, probe_rows=32, residual_rank=8)
+    ws = sp.Workspace()
+    eager = sp.sparsepr_attention(q, k, v, cfg, workspace=ws)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    with torch.cuda.graph(g, stream=cap):
+        static_out = sp.sparsepr_attention(q, k, v, cfg, workspace=ws)
+    for _ in range(3):
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(static_out, eager)
+        again = sp.sparsepr_attention(q, k, v, cfg, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(again, eager)
