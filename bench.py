@@ -25,6 +25,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 / fp16 MFMA
+PEAK_FP32_TFLOPS = 157.3   # MI355X fp32 vector: 256 CUs x 128 FMA per clock x 2 flops x 2.4 GHz
 PEAK_HBM_GBS = 8000.0
 
 
@@ -275,12 +276,18 @@ def main() -> int:
         own_ms = time_fn(lambda: sp.sparsepr_dense_attention(q, k, v, out=dense_out), 3, torch)
         ref = F.scaled_dot_product_attention(q, k, v).float()
         err = float((out.float() - ref).norm() / ref.norm())
+        # the uncorrected (hard-drop) output of the same partition, for comparison
+        ql, kl = sp.sparsepr_partition(q, k, v, cfg, workspace=ws)
+        hard = sp.sparsepr_sparse_attention(q, k, v, cfg, ql, kl, workspace=ws)
+        herr = float((hard.float() - ref).norm() / ref.norm())
+        del hard, ql, kl
         dense_ms = min(min(sdpa_ms), min(own_ms))
         result_extra.update(dense_ms=round(dense_ms, 4), dense_ms_torch_sdpa=round(min(sdpa_ms), 4),
                             dense_ms_own_kernel=round(min(own_ms), 4),
-                            speedup_vs_dense=round(dense_ms / ms_call, 4), rel_err_vs_dense=round(err, 5))
+                            speedup_vs_dense=round(dense_ms / ms_call, 4), rel_err_vs_dense=round(err, 5),
+                            rel_err_hard_drop=round(herr, 5))
         log(f"dense: sdpa {min(sdpa_ms):.3f} ms, own {min(own_ms):.3f} ms; speedup {dense_ms / ms_call:.3f}; "
-            f"rel err vs dense {err:.4f}")
+            f"rel err vs dense {err:.4f} (hard drop {herr:.4f})")
         del dense_out, ref
 
     traffic = None
@@ -309,16 +316,21 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "f32" if w.dtype == "fp32" else "bf16",
         "data": "synthetic",
         "config": {"workload": w.name, "B": B, "H": H, "N": N, "d": d, "density": w.density,
                    "n_kv_groups": w.n_kv_groups, "n_q_groups": w.n_q_groups, "probe_rows": w.probe_rows,
                    "residual_rank": w.residual_rank, "kmeans_iters": cfg.kmeans_iters, "router": args.router,
                    **({"alpha": args.alpha} if args.router == "alpha" else {}), "parallelism": "none"},
-        "roofline": {"bound": "mfma", "achieved": round(kernel_tflops, 2), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(kernel_tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
-                     "kernel": "k_sparse_attn_mfma (block-sparse attention, fused correction)",
-                     "kernel_ms": round(t_kernel, 4), "flops_per_launch": kernel_flops},
+        "roofline": ({"bound": "mfma", "achieved": round(kernel_tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                      "unit": "TFLOP/s", "frac": round(kernel_tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+                      "kernel": "k_sparse_attn_mfma (block-sparse attention, fused correction)",
+                      "kernel_ms": round(t_kernel, 4), "flops_per_launch": kernel_flops}
+                     if w.dtype != "fp32" else
+                     {"bound": "alu", "achieved": round(kernel_tflops, 2), "peak": PEAK_FP32_TFLOPS,
+                      "unit": "TFLOP/s", "frac": round(kernel_tflops / PEAK_FP32_TFLOPS, 4), "traffic": None,
+                      "kernel": "k_sparse_attn_vec (fp32 block-sparse attention, fused correction)",
+                      "kernel_ms": round(t_kernel, 4), "flops_per_launch": kernel_flops}),
         "cpu_baseline": cpu,
         "call_pct_peak": round(100 * call_tflops / PEAK_BF16_TFLOPS, 2),
         "rho_exec": round(rho_exec, 5),
