@@ -1204,8 +1204,11 @@ __global__ __launch_bounds__(256) void k_group_mean(UpdateArgs a) {
 // its bias c = mean . y; kept in fp64 (for the exact re-decision), as a
 // hi/lo bf16 pair and an fp32 bias (the assignment's operands), with bounds
 // of |y|, |c| and of the pair's residual |y - hi - lo| (its error bound).
-// 16 groups per workgroup; 16 threads per group, each owning 8 consecutive
-// dimensions; M is staged through LDS 32 rows at a time.
+// 16 groups per workgroup; 16 threads per group, thread jj owning the
+// dimensions jj, jj + 16, ...: in the product the 16 threads of a group read
+// 16 consecutive fp64 entries of a staged row of M (distinct banks) and the
+// four groups of a wave read the same ones (one broadcast).  M is staged
+// through LDS 32 rows at a time.
 __global__ __launch_bounds__(256) void k_centre_images(UpdateArgs a) {
   constexpr int GB = 16, MR = 32, LDM = 130;
   __shared__ double smean[GB][129];
@@ -1227,7 +1230,6 @@ __global__ __launch_bounds__(256) void k_centre_images(UpdateArgs a) {
       smean[e >> 7][e & 127] = t[u];
     }
   }
-  // thread (group gl, piece jj) owns dims 8 jj .. 8 jj + 7
   const int gl = tid >> 4, jj = tid & 15;
   const double* M = a.metric ? a.metric + (long long)bh * Dp * Dp : nullptr;
   double y[8];
@@ -1257,46 +1259,34 @@ __global__ __launch_bounds__(256) void k_centre_images(UpdateArgs a) {
         }
       }
       __syncthreads();
-      if (8 * jj < Dp) {
-        for (int r = 0; r < nr; ++r) {
-          const double mv = smean[gl][i0 + r];
+      for (int r = 0; r < nr; ++r) {
+        const double mv = smean[gl][i0 + r];
 #pragma unroll
-          for (int k = 0; k < 8; k += 2) {
-            const double2 m2 = *reinterpret_cast<const double2*>(&sm[r][8 * jj + k]);
-            y[k] = __builtin_fma(m2.x, mv, y[k]);
-            y[k + 1] = __builtin_fma(m2.y, mv, y[k + 1]);
-          }
-        }
+        for (int k = 0; k < 8; ++k)
+          if (jj + 16 * k < Dp) y[k] = __builtin_fma(sm[r][jj + 16 * k], mv, y[k]);
       }
     }
   } else {
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-      const int j = 8 * jj + k;
+      const int j = jj + 16 * k;
       y[k] = j < Dp ? smean[gl][j] : 0.0;
     }
   }
   double b = 0.0, yy = 0.0, rr = 0.0, ll = 0.0;
-  uint32_t hw[4], lw[4];
+  bf16_t hs[8], ls[8];
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
-    const int j = 8 * jj + k;
+    const int j = jj + 16 * k;
     if (j >= Dp) y[k] = 0.0;
     if (j < Dp) b = __builtin_fma(y[k], smean[gl][j], b);
     yy = __builtin_fma(y[k], y[k], yy);
     const float yf = (float)y[k];
-    const bf16_t h = f32_to_bf16(yf);
-    const bf16_t l = f32_to_bf16(yf - bf16_to_f32(h));
-    const double res = (y[k] - (double)bf16_to_f32(h)) - (double)bf16_to_f32(l);
+    hs[k] = f32_to_bf16(yf);
+    ls[k] = f32_to_bf16(yf - bf16_to_f32(hs[k]));
+    const double res = (y[k] - (double)bf16_to_f32(hs[k])) - (double)bf16_to_f32(ls[k]);
     rr = __builtin_fma(res, res, rr);
-    ll = __builtin_fma((double)bf16_to_f32(l), (double)bf16_to_f32(l), ll);
-    if (k & 1) {
-      hw[k >> 1] |= (uint32_t)h << 16;
-      lw[k >> 1] |= (uint32_t)l << 16;
-    } else {
-      hw[k >> 1] = h;
-      lw[k >> 1] = l;
-    }
+    ll = __builtin_fma((double)bf16_to_f32(ls[k]), (double)bf16_to_f32(ls[k]), ll);
   }
   for (int o = 8; o > 0; o >>= 1) {
     b += __shfl_xor(b, o, 16);
@@ -1307,16 +1297,18 @@ __global__ __launch_bounds__(256) void k_centre_images(UpdateArgs a) {
   if (gl >= ng) return;
   const long long go = (long long)bh * a.gstride + g0 + gl;
   const long long yo = go * a.ystride;
-  if (8 * jj < Dimg) {
-    *reinterpret_cast<uint4*>(a.yhi + yo + 8 * jj) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
-    *reinterpret_cast<uint4*>(a.ylo + yo + 8 * jj) = make_uint4(lw[0], lw[1], lw[2], lw[3]);
-    if (a.y64) {
+  double* yt = a.y64 ? a.y64t + (long long)bh * a.ystride * a.gstride + g0 + gl : nullptr;
 #pragma unroll
-      for (int k = 0; k < 8; k += 2) *reinterpret_cast<double2*>(a.y64 + yo + 8 * jj + k) = make_double2(y[k], y[k + 1]);
-      // and dimension-major [Dimg][gstride] per (b,h), read with lanes over centres
-      double* yt = a.y64t + (long long)bh * a.ystride * a.gstride + g0 + gl;
-#pragma unroll
-      for (int k = 0; k < 8; ++k) yt[(long long)(8 * jj + k) * a.gstride] = y[k];
+  for (int k = 0; k < 8; ++k) {
+    const int j = jj + 16 * k;
+    if (j < Dimg) {
+      a.yhi[yo + j] = hs[k];
+      a.ylo[yo + j] = ls[k];
+      if (a.y64) {
+        a.y64[yo + j] = y[k];
+        // and dimension-major [Dimg][gstride] per (b,h), read with lanes over centres
+        yt[(long long)j * a.gstride] = y[k];
+      }
     }
   }
   if (jj == 0) {
