@@ -54,7 +54,6 @@ struct AttnArgs {
 // i % 8), and each XCD has its own L2.  Give every XCD one contiguous range of
 // (head, tile) slots so that the workgroups resident on an XCD work on the same
 // head and on neighbouring query groups, whose key ranges overlap.
-constexpr int kXcds = 8;
 __device__ inline void xcd_item(const AttnArgs& a, int* bh, int* tile) {
   const int total = a.grid_tiles * a.BH;
   const int per = (total + kXcds - 1) / kXcds;

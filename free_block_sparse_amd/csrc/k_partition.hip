@@ -461,10 +461,19 @@ __device__ inline Seq3 seq3_init() { return Seq3{-INFINITY, -INFINITY, -INFINITY
 // assembly).  keep, the mask of the bits a value keeps, sits in a vector
 // register so that the packing is one v_and_or_b32 with the index as its
 // scalar operand.
-__device__ inline void seq3_add_block(Seq3& st, const f32x16& acc, uint32_t keep, int k) {
+// The packing adds an opaque zero z (a scalar register the compiler cannot
+// see through) to the index 16 k + r: otherwise it splits the packing into
+// v_and_b32 + v_or3_b32 (16 k and r as separate operands), two vector
+// instructions where v_and_or_b32 with one scalar operand is one.
+__device__ inline uint32_t seq3_zero() {
+  uint32_t z;
+  asm volatile("s_mov_b32 %0, 0" : "=s"(z));
+  return z;
+}
+__device__ inline void seq3_add_block(Seq3& st, const f32x16& acc, uint32_t keep, int k, uint32_t z) {
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
-    const float p = __uint_as_float((__float_as_uint(acc[r]) & keep) | (uint32_t)(16 * k + r));
+    const float p = __uint_as_float((__float_as_uint(acc[r]) & keep) | ((uint32_t)(16 * k + r) + z));
     st.t = vmed3(st.s, st.t, p);
     st.s = vmed3(st.b, st.s, p);
     st.b = vmax(st.b, p);
@@ -583,6 +592,9 @@ __device__ inline void flag_append(const AssignArgs& a, int bh, bool live, const
     a.flist[(long long)bh * a.N + slot] = make_int4(n, st.bi, st.si, st.b - st.t <= 2.0f * e ? 1 : 0);
 }
 
+#ifndef SP_ASSIGN_PIPE
+#define SP_ASSIGN_PIPE 0
+#endif
 template <int D>
 __global__ __launch_bounds__(512) void k_kmeans_assign(AssignArgs a) {
   // Form for wide bf16 rows (d = 128) and G <= 256, where restaging the
@@ -607,7 +619,12 @@ __global__ __launch_bounds__(512) void k_kmeans_assign(AssignArgs a) {
   __shared__ CentreBounds sbound;
   const int bh = blockIdx.y, tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   const int half = lane >> 5, col = lane & 31;
-  const int N = a.N, G = a.G, G32 = (G + 31) & ~31;
+  const int N = a.N, G = a.G, G32 = (G + 31) & ~31, G64 = (G + 63) & ~63;
+#if SP_ASSIGN_PIPE
+  const int Gst = G64;  // staged rows: the pipelined loop runs over 64 centres at a time
+#else
+  const int Gst = G32;
+#endif
   const int c_begin = blockIdx.x * a.cpw;
   const int c_end = min(a.nchunk, c_begin + a.cpw);
   if (c_begin >= c_end) return;  // whole workgroup
@@ -624,7 +641,7 @@ __global__ __launch_bounds__(512) void k_kmeans_assign(AssignArgs a) {
     const bf16_t* yh = a.yhi + (long long)bh * a.gstride * a.ystride;
     const bf16_t* yl = a.ylo + (long long)bh * a.gstride * a.ystride;
     constexpr int PPR = D / 8;
-    for (int e0 = 0; e0 < G32 * PPR; e0 += 4 * NT) {
+    for (int e0 = 0; e0 < Gst * PPR; e0 += 4 * NT) {
       u32x4 vh[4], vl[4];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
@@ -638,7 +655,7 @@ __global__ __launch_bounds__(512) void k_kmeans_assign(AssignArgs a) {
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int e = e0 + tid + NT * u, r = e / PPR, cc = e % PPR;
-        if (r < G32) {
+        if (r < Gst) {
           *reinterpret_cast<u32x4*>(sh + r * LDI + cc * 8) = vh[u];
           *reinterpret_cast<u32x4*>(sl + r * LDI + cc * 8) = vl[u];
         }
@@ -646,11 +663,11 @@ __global__ __launch_bounds__(512) void k_kmeans_assign(AssignArgs a) {
     }
     centre_bounds_to_lds(a, bh, &sbound);
     // -c_g / 2, the accumulators' start (centres past G never win)
-    for (int e = tid; e < G32; e += NT) sbias[e] = e < G ? -0.5f * a.ybias[(long long)bh * a.gstride + e] : -0x1p126f;
+    for (int e = tid; e < Gst; e += NT) sbias[e] = e < G ? -0.5f * a.ybias[(long long)bh * a.gstride + e] : -0x1p126f;
   }
   __syncthreads();
   const CentreBounds cbd = sbound;
-  const uint32_t keep = seq3_keep(a.pbits);
+  const uint32_t keep = seq3_keep(a.pbits), z0 = seq3_zero();
 
   const bf16_t* pbase = static_cast<const bf16_t*>(a.pts.p) + a.pts.row_off(bh, 0);
   const long long psn = a.pts.sn;
@@ -678,35 +695,56 @@ __global__ __launch_bounds__(512) void k_kmeans_assign(AssignArgs a) {
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) xsq[pb] += sumsq_bf16x8(ph[pb][ks]);
     }
-    for (int cb = 0; cb < G32; cb += 32) {
-      // -c_g / 2 of this lane's centres: four runs of four consecutive centres
-      f32x16 cinit;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float4 f = *reinterpret_cast<const float4*>(sbias + cb + 8 * q + 4 * half);
-        cinit[4 * q] = f.x;
-        cinit[4 * q + 1] = f.y;
-        cinit[4 * q + 2] = f.z;
-        cinit[4 * q + 3] = f.w;
-      }
-      f32x16 acc[PB];
-#pragma unroll
-      for (int pb = 0; pb < PB; ++pb) acc[pb] = cinit;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const int o = (cb + col) * LDI + 16 * ks + 8 * half;
-        const bf16x8 ah = *reinterpret_cast<const bf16x8*>(sh + o);
-        const bf16x8 al = *reinterpret_cast<const bf16x8*>(sl + o);
-#pragma unroll
-        for (int pb = 0; pb < PB; ++pb) {
-          const bf16x8 xh = __builtin_bit_cast(bf16x8, ph[pb][ks]);
-          acc[pb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, xh, acc[pb], 0, 0, 0);
-          acc[pb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, xh, acc[pb], 0, 0, 0);
-        }
-      }
-#pragma unroll
-      for (int pb = 0; pb < PB; ++pb) seq3_add_block(st[pb], acc[pb], keep, cb >> 5);
+    // products of the 32 centres from cb on with both point columns;
+    // -c_g / 2 of this lane's centres (four runs of four consecutive centres)
+    // is the accumulators' start
+#define SP_CENTRE_BLOCK(ACC, CB)                                                                  \
+  {                                                                                               \
+    f32x16 cinit;                                                                                 \
+    _Pragma("unroll") for (int q = 0; q < 4; ++q) {                                               \
+      const float4 f = *reinterpret_cast<const float4*>(sbias + (CB) + 8 * q + 4 * half);         \
+      cinit[4 * q] = f.x;                                                                         \
+      cinit[4 * q + 1] = f.y;                                                                     \
+      cinit[4 * q + 2] = f.z;                                                                     \
+      cinit[4 * q + 3] = f.w;                                                                     \
+    }                                                                                             \
+    _Pragma("unroll") for (int pb = 0; pb < PB; ++pb) ACC[pb] = cinit;                            \
+    _Pragma("unroll") for (int ks = 0; ks < KS; ++ks) {                                           \
+      const int o = ((CB) + col) * LDI + 16 * ks + 8 * half;                                      \
+      const bf16x8 ah = *reinterpret_cast<const bf16x8*>(sh + o);                                 \
+      const bf16x8 al = *reinterpret_cast<const bf16x8*>(sl + o);                                 \
+      _Pragma("unroll") for (int pb = 0; pb < PB; ++pb) {                                         \
+        const bf16x8 xh = __builtin_bit_cast(bf16x8, ph[pb][ks]);                                 \
+        ACC[pb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, xh, ACC[pb], 0, 0, 0);              \
+        ACC[pb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, xh, ACC[pb], 0, 0, 0);              \
+      }                                                                                           \
+    }                                                                                             \
+  }
+#define SP_TRACK(ACC, CB) _Pragma("unroll") for (int pb = 0; pb < PB; ++pb) seq3_add_block(st[pb], ACC[pb], keep, (CB) >> 5, z0);
+#if SP_ASSIGN_PIPE
+    // two accumulator sets: the products of the next 32 centres are issued
+    // beside the running top three of the current ones
+    f32x16 accA[PB], accB[PB];
+    SP_CENTRE_BLOCK(accA, 0)
+    int cb = 0;
+    for (; cb + 64 < G64; cb += 64) {
+      SP_CENTRE_BLOCK(accB, cb + 32)
+      SP_TRACK(accA, cb)
+      SP_CENTRE_BLOCK(accA, cb + 64)
+      SP_TRACK(accB, cb + 32)
     }
+    SP_CENTRE_BLOCK(accB, cb + 32)
+    SP_TRACK(accA, cb)
+    SP_TRACK(accB, cb + 32)
+#else
+    for (int cb = 0; cb < G32; cb += 32) {
+      f32x16 acc[PB];
+      SP_CENTRE_BLOCK(acc, cb)
+      SP_TRACK(acc, cb)
+    }
+#endif
+#undef SP_TRACK
+#undef SP_CENTRE_BLOCK
 #pragma unroll
     for (int pb = 0; pb < PB; ++pb) {
       Best3 fin = seq3_finish(st[pb], a.pbits);
@@ -768,7 +806,7 @@ __global__ __launch_bounds__(512, (LO && D >= 64) ? 2 : 4) void k_kmeans_assign_
     if (LO) pl[LO ? ks : 0] = __builtin_bit_cast(bf16x8, w);
   }
   Seq3 st = seq3_init();
-  const uint32_t keep = seq3_keep(a.pbits);
+  const uint32_t keep = seq3_keep(a.pbits), z0 = seq3_zero();
   float xsq = 0.f;
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) xsq += sumsq_bf16x8(__builtin_bit_cast(u32x4, ph[ks]));
@@ -827,8 +865,8 @@ __global__ __launch_bounds__(512, (LO && D >= 64) ? 2 : 4) void k_kmeans_assign_
           acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah1, pl[LO ? ks : 0], acc1, 0, 0, 0);
         }
       }
-      seq3_add_block(st, acc0, keep, (c0 + cb) >> 5);
-      if (two) seq3_add_block(st, acc1, keep, (c0 + cb + 32) >> 5);
+      seq3_add_block(st, acc0, keep, (c0 + cb) >> 5, z0);
+      if (two) seq3_add_block(st, acc1, keep, (c0 + cb + 32) >> 5, z0);
     }
   }
   Best3 fin = seq3_finish(st, a.pbits);
@@ -883,7 +921,9 @@ __global__ __launch_bounds__(256) void k_kmeans_redecide(RedecideArgs a) {
   constexpr int NW = 4, KU = 32;
   __shared__ double sv[NW];
   __shared__ int si[NW];
-  const int bh = blockIdx.y, tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  int bh, wx;
+  xcd_slice(blockIdx.x, gridDim.x, a.nwg, bh, wx);
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   const int cnt = min(a.fcnt[(long long)bh * a.fcstride], a.N);
   const int4* fl = a.flist + (long long)bh * a.N;
   const double* yr = a.y64 + (long long)bh * a.gstride * a.ystride;   // [gstride][Dimg]
@@ -893,7 +933,7 @@ __global__ __launch_bounds__(256) void k_kmeans_redecide(RedecideArgs a) {
   const T* rawb = static_cast<const T*>(a.raw.p);
   // pass 1: two candidates; four points per wave at a time, 16 lanes each
   const int sub = lane & 15, grp = lane >> 4;
-  for (int e0 = (blockIdx.x * NW + w) * 4; e0 < cnt; e0 += gridDim.x * NW * 4) {
+  for (int e0 = (wx * NW + w) * 4; e0 < cnt; e0 += a.nwg * NW * 4) {
     const int e = e0 + grp;
     const int4 ent = e < cnt ? fl[e] : make_int4(0, 0, 0, 1);
     const bool act = ent.w == 0;
@@ -919,7 +959,7 @@ __global__ __launch_bounds__(256) void k_kmeans_redecide(RedecideArgs a) {
     }
   }
   // pass 2: every centre, one workgroup per point
-  for (int e = blockIdx.x; e < cnt; e += gridDim.x) {
+  for (int e = wx; e < cnt; e += a.nwg) {
     const int4 ent = fl[e];
     if (ent.w == 0) continue;  // uniform across the workgroup
     const int n = ent.x;
@@ -1323,6 +1363,106 @@ __global__ __launch_bounds__(256) void k_centre_images(UpdateArgs a) {
   }
 }
 
+// The same images when a metric is given (query side, Dimg = Dp = DP), on
+// fp64 matrix cores: Y (16 centres x DP) = means (16 x DP) . M, one
+// v_mfma_f64_16x16x4f64 per 16-dimension column tile and k-step of four
+// (layouts as in the key coordinates: A[i][k] in lane i + 16k, B[k][j] in
+// lane j + 16k, D[i][j] in lane 16 (i % 4) + j, register i / 4).  Wave w owns
+// the column tiles w, w + 4, ...; B fragments come straight from M, which the
+// slice mapping keeps in one XCD's L2 for all blocks of a (b,h).  The bias,
+// |y|^2 and the split residuals are reduced over a group's 16 lanes, then
+// over the four waves in a fixed order.
+template <int DP>
+__global__ __launch_bounds__(256) void k_centre_images_f64mfma(UpdateArgs a) {
+  typedef double f64x4_t __attribute__((ext_vector_type(4)));
+  constexpr int GB = 16, NJ = DP / 16, TPW = NJ / 4, KS = DP / 4, LDA = DP + 2, KU = 8;
+  static_assert(NJ % 4 == 0, "whole column tiles per wave");
+  __shared__ double smean[GB][LDA];
+  __shared__ double red[4][GB][4];
+  const int nb = (a.G + GB - 1) / GB;
+  int bh, blk;
+  xcd_slice(blockIdx.x, gridDim.x, nb, bh, blk);
+  const int g0 = blk * GB, tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int li = lane & 15, lk = lane >> 4;
+  const int ng = min(GB, a.G - g0);
+  for (int e = tid; e < GB * DP; e += 256) {
+    const int gl = e / DP, j = e - gl * DP;
+    smean[gl][j] = gl < ng ? a.cmean[((long long)bh * a.gstride + g0 + gl) * a.cstride + j] : 0.0;
+  }
+  __syncthreads();
+  const double* M = a.metric + (long long)bh * DP * DP;
+  f64x4_t acc[TPW];
+#pragma unroll
+  for (int t = 0; t < TPW; ++t) acc[t] = f64x4_t{0.0, 0.0, 0.0, 0.0};
+  for (int k0 = 0; k0 < KS; k0 += KU) {
+    double bv[KU][TPW];
+#pragma unroll
+    for (int u = 0; u < KU; ++u)
+#pragma unroll
+      for (int t = 0; t < TPW; ++t) bv[u][t] = M[(long long)(4 * (k0 + u) + lk) * DP + 16 * (w + 4 * t) + li];
+#pragma unroll
+    for (int u = 0; u < KU; ++u) {
+      const double av = smean[li][4 * (k0 + u) + lk];
+#pragma unroll
+      for (int t = 0; t < TPW; ++t) acc[t] = __builtin_amdgcn_mfma_f64_16x16x4f64(av, bv[u][t], acc[t], 0, 0, 0);
+    }
+  }
+  // lane holds groups 4 r + lk (r < 4), dimension 16 (w + 4 t) + li
+  double* yt = a.y64t + (long long)bh * a.ystride * a.gstride;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int gl = 4 * r + lk;
+    const long long go = (long long)bh * a.gstride + g0 + gl;
+    double b = 0.0, yy = 0.0, rr = 0.0, ll = 0.0;
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) {
+      const int j = 16 * (w + 4 * t) + li;
+      const double y = acc[t][r];
+      b = __builtin_fma(y, smean[gl][j], b);
+      yy = __builtin_fma(y, y, yy);
+      const float yf = (float)y;
+      const bf16_t hs = f32_to_bf16(yf);
+      const bf16_t ls = f32_to_bf16(yf - bf16_to_f32(hs));
+      const double res = (y - (double)bf16_to_f32(hs)) - (double)bf16_to_f32(ls);
+      rr = __builtin_fma(res, res, rr);
+      ll = __builtin_fma((double)bf16_to_f32(ls), (double)bf16_to_f32(ls), ll);
+      if (gl < ng) {
+        const long long yo = go * a.ystride + j;
+        a.yhi[yo] = hs;
+        a.ylo[yo] = ls;
+        a.y64[yo] = y;
+        yt[(long long)j * a.gstride + g0 + gl] = y;
+      }
+    }
+    for (int o = 8; o > 0; o >>= 1) {
+      b += __shfl_xor(b, o, 16);
+      yy += __shfl_xor(yy, o, 16);
+      rr += __shfl_xor(rr, o, 16);
+      ll += __shfl_xor(ll, o, 16);
+    }
+    if (li == 0) {
+      red[w][gl][0] = b;
+      red[w][gl][1] = yy;
+      red[w][gl][2] = rr;
+      red[w][gl][3] = ll;
+    }
+  }
+  __syncthreads();
+  if (tid >= ng) return;
+  double q[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) q[c] = ((red[0][tid][c] + red[1][tid][c]) + red[2][tid][c]) + red[3][tid][c];
+  const long long go = (long long)bh * a.gstride + g0 + tid;
+  a.ybias[go] = (float)q[0];
+  a.c64[go] = q[0];
+  if (a.ybound) {
+    // fp32 upper bounds; the relative margin covers the roundings above
+    const float4 bd = make_float4((float)(sqrt(q[1]) * (1.0 + 0x1p-20)), (float)(fabs(q[0]) * (1.0 + 0x1p-20)),
+                                  (float)(sqrt(q[2]) * (1.0 + 0x1p-20)), (float)(sqrt(q[3]) * (1.0 + 0x1p-20)));
+    reinterpret_cast<float4*>(a.ybound)[go] = bd;
+  }
+}
+
 // M_Q = s^2 sum over non-empty key groups of cbar_h cbar_h^T (d x d per (b,h));
 // 16 key groups at a time are staged in LDS, each thread owns a 4x4 block.
 // Centred query coordinates u_i - mean_h(u_ih) have the metric
@@ -1589,10 +1729,12 @@ hipError_t launch_redecide(const Plan& p, const RedecideArgs& a, int raw_type, h
   if (a.Dx < 1 || a.Dx > 128) return hipErrorInvalidValue;
   // enough workgroups per (b,h) that a step's flagged points (typically well
   // under 2% of N) take one or two batches each
-  const int nwg = std::max(1, std::min(32, (p.N + 1023) / 1024));  // four points at a time each
-  const dim3 g(nwg, p.BH);
-  if (raw_type == 0) SP_LAUNCH(k_kmeans_redecide<bf16_t>, g, dim3(256), s, a);
-  else SP_LAUNCH(k_kmeans_redecide<float>, g, dim3(256), s, a);
+  // (the workgroups of one (b,h) on one XCD: they all read its centre images)
+  RedecideArgs ra = a;
+  ra.nwg = std::max(1, std::min(32, (p.N + 1023) / 1024));  // four points at a time each
+  const dim3 g((unsigned)(ra.nwg * p.BH));
+  if (raw_type == 0) SP_LAUNCH(k_kmeans_redecide<bf16_t>, g, dim3(256), s, ra);
+  else SP_LAUNCH(k_kmeans_redecide<float>, g, dim3(256), s, ra);
   return hipSuccess;
 }
 
@@ -1622,7 +1764,13 @@ hipError_t launch_centre_update(const Plan& p, const UpdateArgs& a, int pts_type
   else if (pts_type == 1) SP_LAUNCH(k_group_mean<float>, g, dim3(256), s, a);
   else SP_LAUNCH(k_group_mean<double>, g, dim3(256), s, a);
   if (a.means_only) return hipSuccess;
-  SP_LAUNCH(k_centre_images, dim3((a.G + 15) / 16, p.BH), dim3(256), s, a);
+  const unsigned nb = (unsigned)((a.G + 15) / 16);
+  if (a.metric && a.y64 && a.y64t && a.c64 && a.Dimg == a.Dp && (a.Dp == 128 || a.Dp == 64)) {
+    if (a.Dp == 128) SP_LAUNCH(k_centre_images_f64mfma<128>, dim3(nb * p.BH), dim3(256), s, a);
+    else SP_LAUNCH(k_centre_images_f64mfma<64>, dim3(nb * p.BH), dim3(256), s, a);
+    return hipSuccess;
+  }
+  SP_LAUNCH(k_centre_images, dim3(nb, p.BH), dim3(256), s, a);
   return hipSuccess;
 }
 

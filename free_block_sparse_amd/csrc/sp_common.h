@@ -94,6 +94,22 @@ __device__ inline double wave_sum_d(double v) {
   return v;
 }
 
+// Workgroup i of a one-dimensional grid of W workgroups, seen as block blk of
+// slice `slice` (nb blocks per slice, W = nb * slices).  The hardware hands
+// consecutive workgroups of a grid to the eight XCDs in turn, so the slices
+// are laid out as eight contiguous runs, one per XCD: every block of a slice
+// then runs on one XCD and the slice's shared operands stay in that XCD's L2.
+// A bijection for any W and nb; only the placement depends on the dispatch
+// order.
+constexpr int kXcds = 8;
+__device__ inline void xcd_slice(int i, int W, int nb, int& slice, int& blk) {
+  const int x = i % kXcds, k = i / kXcds;
+  const int q = W / kXcds, r = W % kXcds;
+  const int t = x * q + (x < r ? x : r) + k;
+  slice = t / nb;
+  blk = t - slice * nb;
+}
+
 // Orderable unsigned image of a double: a < b  <=>  ord(a) < ord(b) (NaN excluded).
 __host__ __device__ inline uint64_t ord_f64(double x) {
   union { double d; uint64_t u; } c;

@@ -82,6 +82,7 @@ struct RedecideArgs {
   int* labels;
   int* counts;            // [BH, nchunk, gstride]
   int nchunk;
+  int nwg;                // workgroups per (b,h) (set by the launcher)
 };
 
 struct CountArgs {
