@@ -575,26 +575,37 @@ __device__ inline float value_bound(const AssignArgs& a, const CentreBounds& cb,
 
 // A point whose best and second values lie within twice the error bound e
 // of each other is a near tie: it goes to the flag list of (b,h) with its
-// two candidates, and with full = 1 when the third value is within 2e of the
-// best as well (then every centre must be re-decided).  One counter update
-// per wave; every lane of the wave must call it.
-__device__ inline void flag_append(const AssignArgs& a, int bh, bool live, const Best3& st, float e, int n) {
-  const bool flag = live && st.b - st.s <= 2.0f * e;
-  const unsigned long long m = __builtin_amdgcn_ballot_w64(flag);
-  if (m == 0ull) return;
+// two candidates.  When the third value is within 2e of the best as well,
+// every centre must be re-decided: such "full" flags are counted apart and
+// fill the list from its end (a point is flagged at most once per step, so
+// the two parts never meet).  One counter update per wave and kind; every
+// lane of the wave must call it.
+__device__ inline int flag_slot(int* counter, unsigned long long m) {
   const int lane = threadIdx.x & 63;
   const int leader = __builtin_ctzll(m);
   int base = 0;
-  if (lane == leader) base = atomicAdd(a.fcnt + (long long)bh * a.fcstride, __builtin_popcountll(m));
+  if (lane == leader) base = atomicAdd(counter, __builtin_popcountll(m));
   base = __shfl(base, leader, 64);
-  const int slot = base + __builtin_popcountll(m & ((1ull << lane) - 1ull));
-  if (flag && slot < a.N)
-    a.flist[(long long)bh * a.N + slot] = make_int4(n, st.bi, st.si, st.b - st.t <= 2.0f * e ? 1 : 0);
+  return base + __builtin_popcountll(m & ((1ull << lane) - 1ull));
+}
+__device__ inline void flag_append(const AssignArgs& a, int bh, bool live, const Best3& st, float e, int n) {
+  const bool flag = live && st.b - st.s <= 2.0f * e;
+  const bool full = flag && st.b - st.t <= 2.0f * e;
+  const bool pair = flag && !full;
+  const unsigned long long mp = __builtin_amdgcn_ballot_w64(pair);
+  const unsigned long long mf = __builtin_amdgcn_ballot_w64(full);
+  int4* fl = a.flist + (long long)bh * a.N;
+  int* cnt = a.fcnt + (long long)bh * a.fcstride;
+  if (mp) {
+    const int slot = flag_slot(cnt, mp);
+    if (pair && slot < a.N) fl[slot] = make_int4(n, st.bi, st.si, 0);
+  }
+  if (mf) {
+    const int slot = a.N - 1 - flag_slot(cnt + a.fcfull, mf);
+    if (full && slot >= 0) fl[slot] = make_int4(n, st.bi, st.si, 1);
+  }
 }
 
-#ifndef SP_ASSIGN_PIPE
-#define SP_ASSIGN_PIPE 0
-#endif
 template <int D>
 __global__ __launch_bounds__(512) void k_kmeans_assign(AssignArgs a) {
   // Form for wide bf16 rows (d = 128) and G <= 256, where restaging the
@@ -619,12 +630,7 @@ __global__ __launch_bounds__(512) void k_kmeans_assign(AssignArgs a) {
   __shared__ CentreBounds sbound;
   const int bh = blockIdx.y, tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   const int half = lane >> 5, col = lane & 31;
-  const int N = a.N, G = a.G, G32 = (G + 31) & ~31, G64 = (G + 63) & ~63;
-#if SP_ASSIGN_PIPE
-  const int Gst = G64;  // staged rows: the pipelined loop runs over 64 centres at a time
-#else
-  const int Gst = G32;
-#endif
+  const int N = a.N, G = a.G, G32 = (G + 31) & ~31;
   const int c_begin = blockIdx.x * a.cpw;
   const int c_end = min(a.nchunk, c_begin + a.cpw);
   if (c_begin >= c_end) return;  // whole workgroup
@@ -641,7 +647,7 @@ __global__ __launch_bounds__(512) void k_kmeans_assign(AssignArgs a) {
     const bf16_t* yh = a.yhi + (long long)bh * a.gstride * a.ystride;
     const bf16_t* yl = a.ylo + (long long)bh * a.gstride * a.ystride;
     constexpr int PPR = D / 8;
-    for (int e0 = 0; e0 < Gst * PPR; e0 += 4 * NT) {
+    for (int e0 = 0; e0 < G32 * PPR; e0 += 4 * NT) {
       u32x4 vh[4], vl[4];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
@@ -655,7 +661,7 @@ __global__ __launch_bounds__(512) void k_kmeans_assign(AssignArgs a) {
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int e = e0 + tid + NT * u, r = e / PPR, cc = e % PPR;
-        if (r < Gst) {
+        if (r < G32) {
           *reinterpret_cast<u32x4*>(sh + r * LDI + cc * 8) = vh[u];
           *reinterpret_cast<u32x4*>(sl + r * LDI + cc * 8) = vl[u];
         }
@@ -663,7 +669,7 @@ __global__ __launch_bounds__(512) void k_kmeans_assign(AssignArgs a) {
     }
     centre_bounds_to_lds(a, bh, &sbound);
     // -c_g / 2, the accumulators' start (centres past G never win)
-    for (int e = tid; e < Gst; e += NT) sbias[e] = e < G ? -0.5f * a.ybias[(long long)bh * a.gstride + e] : -0x1p126f;
+    for (int e = tid; e < G32; e += NT) sbias[e] = e < G ? -0.5f * a.ybias[(long long)bh * a.gstride + e] : -0x1p126f;
   }
   __syncthreads();
   const CentreBounds cbd = sbound;
@@ -695,56 +701,35 @@ __global__ __launch_bounds__(512) void k_kmeans_assign(AssignArgs a) {
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) xsq[pb] += sumsq_bf16x8(ph[pb][ks]);
     }
-    // products of the 32 centres from cb on with both point columns;
-    // -c_g / 2 of this lane's centres (four runs of four consecutive centres)
-    // is the accumulators' start
-#define SP_CENTRE_BLOCK(ACC, CB)                                                                  \
-  {                                                                                               \
-    f32x16 cinit;                                                                                 \
-    _Pragma("unroll") for (int q = 0; q < 4; ++q) {                                               \
-      const float4 f = *reinterpret_cast<const float4*>(sbias + (CB) + 8 * q + 4 * half);         \
-      cinit[4 * q] = f.x;                                                                         \
-      cinit[4 * q + 1] = f.y;                                                                     \
-      cinit[4 * q + 2] = f.z;                                                                     \
-      cinit[4 * q + 3] = f.w;                                                                     \
-    }                                                                                             \
-    _Pragma("unroll") for (int pb = 0; pb < PB; ++pb) ACC[pb] = cinit;                            \
-    _Pragma("unroll") for (int ks = 0; ks < KS; ++ks) {                                           \
-      const int o = ((CB) + col) * LDI + 16 * ks + 8 * half;                                      \
-      const bf16x8 ah = *reinterpret_cast<const bf16x8*>(sh + o);                                 \
-      const bf16x8 al = *reinterpret_cast<const bf16x8*>(sl + o);                                 \
-      _Pragma("unroll") for (int pb = 0; pb < PB; ++pb) {                                         \
-        const bf16x8 xh = __builtin_bit_cast(bf16x8, ph[pb][ks]);                                 \
-        ACC[pb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, xh, ACC[pb], 0, 0, 0);              \
-        ACC[pb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, xh, ACC[pb], 0, 0, 0);              \
-      }                                                                                           \
-    }                                                                                             \
-  }
-#define SP_TRACK(ACC, CB) _Pragma("unroll") for (int pb = 0; pb < PB; ++pb) seq3_add_block(st[pb], ACC[pb], keep, (CB) >> 5, z0);
-#if SP_ASSIGN_PIPE
-    // two accumulator sets: the products of the next 32 centres are issued
-    // beside the running top three of the current ones
-    f32x16 accA[PB], accB[PB];
-    SP_CENTRE_BLOCK(accA, 0)
-    int cb = 0;
-    for (; cb + 64 < G64; cb += 64) {
-      SP_CENTRE_BLOCK(accB, cb + 32)
-      SP_TRACK(accA, cb)
-      SP_CENTRE_BLOCK(accA, cb + 64)
-      SP_TRACK(accB, cb + 32)
-    }
-    SP_CENTRE_BLOCK(accB, cb + 32)
-    SP_TRACK(accA, cb)
-    SP_TRACK(accB, cb + 32)
-#else
     for (int cb = 0; cb < G32; cb += 32) {
+      // -c_g / 2 of this lane's centres: four runs of four consecutive centres
+      f32x16 cinit;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float4 f = *reinterpret_cast<const float4*>(sbias + cb + 8 * q + 4 * half);
+        cinit[4 * q] = f.x;
+        cinit[4 * q + 1] = f.y;
+        cinit[4 * q + 2] = f.z;
+        cinit[4 * q + 3] = f.w;
+      }
       f32x16 acc[PB];
-      SP_CENTRE_BLOCK(acc, cb)
-      SP_TRACK(acc, cb)
+#pragma unroll
+      for (int pb = 0; pb < PB; ++pb) acc[pb] = cinit;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const int o = (cb + col) * LDI + 16 * ks + 8 * half;
+        const bf16x8 ah = *reinterpret_cast<const bf16x8*>(sh + o);
+        const bf16x8 al = *reinterpret_cast<const bf16x8*>(sl + o);
+#pragma unroll
+        for (int pb = 0; pb < PB; ++pb) {
+          const bf16x8 xh = __builtin_bit_cast(bf16x8, ph[pb][ks]);
+          acc[pb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, xh, acc[pb], 0, 0, 0);
+          acc[pb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, xh, acc[pb], 0, 0, 0);
+        }
+      }
+#pragma unroll
+      for (int pb = 0; pb < PB; ++pb) seq3_add_block(st[pb], acc[pb], keep, cb >> 5, z0);
     }
-#endif
-#undef SP_TRACK
-#undef SP_CENTRE_BLOCK
 #pragma unroll
     for (int pb = 0; pb < PB; ++pb) {
       Best3 fin = seq3_finish(st[pb], a.pbits);
@@ -893,12 +878,13 @@ __global__ __launch_bounds__(512, (LO && D >= 64) ? 2 : 4) void k_kmeans_assign_
 // values x . y_g - c_g / 2 are computed in fp64 from the exact point row (raw
 // row, or the fp64 key coordinates) and the fp64 images; the largest is kept,
 // ties to the lower centre.  When only the point's two candidates are within
-// twice the error bound of its best value, every other centre is provably
-// below both and the two dot products decide: one wave per such point, lanes
-// over dimensions, row-major images.  The rare points with a third centre in
-// range are then re-decided over every centre by a whole workgroup (one
-// centre per thread, dimension-major images, 32 loads in flight).  A changed
-// label moves the point between the chunk histograms with integer atomics.
+// twice the error bound of its best value (the front of the flag list),
+// every other centre is provably below both and the two dot products decide:
+// 16 lanes per such point, lanes over dimensions, row-major images.  The
+// points with a third centre in range (the back of the list) are re-decided
+// over every centre by a whole workgroup (one centre per thread,
+// dimension-major images, 32 loads in flight).  A changed label moves the
+// point between the chunk histograms with integer atomics.
 template <typename T>
 __device__ inline double point_value(const RedecideArgs& a, const T* row, int k) {
   return (double)Elem<T>::load(row + k);
@@ -921,22 +907,25 @@ __global__ __launch_bounds__(256) void k_kmeans_redecide(RedecideArgs a) {
   constexpr int NW = 4, KU = 32;
   __shared__ double sv[NW];
   __shared__ int si[NW];
+  __shared__ double sx[128];
   int bh, wx;
   xcd_slice(blockIdx.x, gridDim.x, a.nwg, bh, wx);
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
-  const int cnt = min(a.fcnt[(long long)bh * a.fcstride], a.N);
+  const int* cntp = a.fcnt + (long long)bh * a.fcstride;
+  const int cnt = min(cntp[0], a.N), cntf = min(cntp[a.fcfull], a.N - cnt);
   const int4* fl = a.flist + (long long)bh * a.N;
   const double* yr = a.y64 + (long long)bh * a.gstride * a.ystride;   // [gstride][Dimg]
   const double* yt = a.y64t + (long long)bh * a.ystride * a.gstride;  // [Dimg][gstride]
   const double* cb = a.c64 + (long long)bh * a.gstride;
   const int Dx = a.Dx, G = a.G, gs = a.gstride;
   const T* rawb = static_cast<const T*>(a.raw.p);
-  // pass 1: two candidates; four points per wave at a time, 16 lanes each
+  // two-candidate flags (the front of the list): four points per wave at a
+  // time, 16 lanes each
   const int sub = lane & 15, grp = lane >> 4;
   for (int e0 = (wx * NW + w) * 4; e0 < cnt; e0 += a.nwg * NW * 4) {
     const int e = e0 + grp;
-    const int4 ent = e < cnt ? fl[e] : make_int4(0, 0, 0, 1);
-    const bool act = ent.w == 0;
+    const bool act = e < cnt;
+    const int4 ent = act ? fl[e] : make_int4(0, 0, 0, 0);
     const int n = ent.x, b = ent.y, s = ent.z;
     double db = 0.0, ds = 0.0;
     if (act) {
@@ -958,13 +947,15 @@ __global__ __launch_bounds__(256) void k_kmeans_redecide(RedecideArgs a) {
       relabel(a, bh, n, (ds > db || (ds == db && s < b)) ? s : b);
     }
   }
-  // pass 2: every centre, one workgroup per point
-  for (int e = wx; e < cnt; e += a.nwg) {
-    const int4 ent = fl[e];
-    if (ent.w == 0) continue;  // uniform across the workgroup
-    const int n = ent.x;
-    const double* x64 = a.x64 ? a.x64 + ((long long)bh * a.N + n) * a.x64stride : nullptr;
-    const T* xr = a.x64 ? nullptr : rawb + a.raw.row_off(bh, n);
+  // full flags (the back of the list): every centre, one workgroup per
+  // point, its row staged in LDS in fp64
+  for (int e = wx; e < cntf; e += a.nwg) {
+    const int n = fl[a.N - 1 - e].x;
+    if (tid < Dx) {
+      if (a.x64) sx[tid] = a.x64[((long long)bh * a.N + n) * a.x64stride + tid];
+      else sx[tid] = point_value<T>(a, rawb + a.raw.row_off(bh, n), tid);
+    }
+    __syncthreads();
     double best = -INFINITY;
     int bi = 0x7fffffff;
     for (int g0 = 0; g0 < G; g0 += 256) {
@@ -976,7 +967,7 @@ __global__ __launch_bounds__(256) void k_kmeans_redecide(RedecideArgs a) {
         for (int u = 0; u < KU; ++u) y[u] = (g < G && k0 + u < Dx) ? yt[(long long)(k0 + u) * gs + g] : 0.0;
 #pragma unroll
         for (int u = 0; u < KU; ++u)
-          if (k0 + u < Dx) acc = __builtin_fma(x64 ? x64[k0 + u] : point_value<T>(a, xr, k0 + u), y[u], acc);
+          if (k0 + u < Dx) acc = __builtin_fma(sx[k0 + u], y[u], acc);
       }
       if (g < G) {
         const double v = acc - 0.5 * cb[g];
@@ -1007,7 +998,7 @@ __global__ __launch_bounds__(256) void k_kmeans_redecide(RedecideArgs a) {
         }
       relabel(a, bh, n, bi);
     }
-    __syncthreads();  // sv, si are reused by the next point
+    __syncthreads();  // sx, sv, si are reused by the next point
   }
 }
 
@@ -1168,7 +1159,10 @@ __global__ __launch_bounds__(256) void k_group_mean(UpdateArgs a) {
     const long long sidx = ((2LL * g + 1) * a.N) / (2LL * a.G);
     for (int j = tid; j < Dp; j += NT) cm[j] = (double)Elem<TP>::load(xb + a.pts.row_off(bh, sidx) + j);
     if (g == 0 && a.fcount)
-      for (int t = tid; t < a.T; t += NT) a.fcount[(long long)bh * 2 * a.T + t] = 0;
+      for (int t = tid; t < a.T; t += NT) {
+        a.fcount[(long long)bh * 4 * a.T + t] = 0;
+        a.fcount[(long long)bh * 4 * a.T + 2 * a.T + t] = 0;
+      }
     return;
   }
   const int* off = a.off + (long long)bh * a.offstride;

@@ -47,7 +47,7 @@ struct RouteArgs {
   int* ntiles;
   int max_tiles;
   sparsepr_head_stats* stats;
-  const int* fcount;  // [BH, 2T] k-means flag counts (null: partition given)
+  const int* fcount;  // [BH, 4T] k-means flag counts (null: partition given)
   int T;
 };
 
@@ -699,7 +699,7 @@ __global__ __launch_bounds__(256) void k_route_emit(RouteArgs a) {
     st.q_tiles = tacc;
     int red = 0;
     if (a.fcount)
-      for (int t = 0; t < 2 * a.T; ++t) red += a.fcount[(long long)bh * 2 * a.T + t];
+      for (int t = 0; t < 4 * a.T; ++t) red += a.fcount[(long long)bh * 4 * a.T + t];
     st.kmeans_redecided = red;
     st.rho_route = (double)routed / nn;
     st.rho_exec = (double)(routed + (long long)a.M * a.N) / nn;

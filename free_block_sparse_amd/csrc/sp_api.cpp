@@ -150,8 +150,9 @@ sparsepr_status kmeans_side(Plan& p, int side, int G, int* labels_out, int* perm
   // into its low 4 + ceil(log2(blocks)) mantissa bits
   aa.pbits = 4;
   while ((1 << (aa.pbits - 4)) * 32 < G) ++aa.pbits;
-  int* fc = p.fcount + side * p.T;  // key side: steps 0..T-1, query side: T..2T-1
-  aa.fcstride = 2 * p.T;
+  int* fc = p.fcount + side * p.T;  // key side: steps 0..T-1, query side: T..2T-1 (full flags: + 2T)
+  aa.fcstride = 4 * p.T;
+  aa.fcfull = 2 * p.T;
   aa.flist = p.flist;
 
   ra.y64 = p.y64;
@@ -161,7 +162,8 @@ sparsepr_status kmeans_side(Plan& p, int side, int G, int* labels_out, int* perm
   ra.gstride = p.Gmax;
   ra.N = p.N;
   ra.G = G;
-  ra.fcstride = 2 * p.T;
+  ra.fcstride = 4 * p.T;
+  ra.fcfull = 2 * p.T;
   ra.flist = p.flist;
   ra.labels = p.labels;
   ra.counts = p.counts;

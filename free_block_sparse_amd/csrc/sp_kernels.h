@@ -62,7 +62,9 @@ struct AssignArgs {
   int pbits;              // low mantissa bits carrying a value's block and register index
   int* fcnt;              // this step's flag counter of (b,h) is fcnt[bh * fcstride]
   int fcstride;
-  int4* flist;            // [BH, N] flagged points: (point, best centre, second centre, full re-decision)
+  int fcfull;             // the full-flag counter is fcnt[bh * fcstride + fcfull]
+  int4* flist;            // [BH, N] flagged points (point, best centre, second centre, full): two-candidate
+                          // flags from the front, full flags from the back
 };
 
 // Exact (fp64) re-decision of the flagged points of one Lloyd step.
@@ -78,6 +80,7 @@ struct RedecideArgs {
   int N, G;
   const int* fcnt;
   int fcstride;
+  int fcfull;
   const int4* flist;
   int* labels;
   int* counts;            // [BH, nchunk, gstride]
@@ -128,7 +131,8 @@ struct UpdateArgs {
   int ystride, gstride;
   int G, N;
   int init;             // centres = points at strided seed indices
-  int* fcount;          // this side's flag counters, fcount[bh * 2T + t] for t < T, cleared by the init launch
+  int* fcount;          // this side's flag counters fcount[bh * 4T + t] and fcount[bh * 4T + 2T + t], t < T,
+                        // cleared by the init launch
   int T;
   int means_only;       // only write means_out
   double* means_out;    // [BH, mo_gstride, Dp] or null; NaN for empty groups

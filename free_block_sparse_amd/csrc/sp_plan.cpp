@@ -161,7 +161,7 @@ void plan_carve(Plan* p, char* base) {
   p->y64t = c.take<double>(BH * p->Gmax * Dmax);
   p->c64 = c.take<double>(BH * p->Gmax);
   p->ybound = c.take<float>(BH * p->Gmax * 4);
-  p->fcount = c.take<int>(BH * 2 * p->T);
+  p->fcount = c.take<int>(BH * 4 * p->T);
   p->flist = c.take<int4>(BH * N);
   p->labels = c.take<int>(BH * N);
   p->counts = c.take<int>(BH * p->nchunk * p->Gmax);

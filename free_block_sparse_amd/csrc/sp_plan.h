@@ -63,7 +63,8 @@ struct Plan {
   double* y64t;           // [BH, Dmax, Gmax] the same, dimension-major
   double* c64;            // [BH, Gmax] centre bias x.y of the images in fp64
   float* ybound;          // [BH, Gmax, 4] upper bounds of |y_g|, |c_g|, |y_g - hi - lo| and |lo|
-  int* fcount;            // [BH, 2T] near-tie points flagged per Lloyd step (key side, then query side)
+  int* fcount;            // [BH, 4T] near-tie points flagged per Lloyd step: two-candidate flags (key
+                          // side, then query side), then full flags (key side, then query side)
   bool kmeans_ran;        // set once this plan's partition came from its own k-means
   int4* flist;            // [BH, N] flagged points of the current step (point, two candidates, full flag)
   int* labels;            // [BH, N] working labels
