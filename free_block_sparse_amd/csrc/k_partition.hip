@@ -182,9 +182,11 @@ __global__ __launch_bounds__(1024) void k_key_eig(EigArgs a) {
   __syncthreads();
   const EigWork<double> w{A, LD, nullptr, 0, dg, eo, tau, vb, pb, rot, ctl};
   eig_tridiagonalize<double, NT>(w, D);
-  // every eigenvalue by multisection (all of them are reported)
-  eig_bisect<double, NT>(w, D, D);
-  for (int i = tid; i < D; i += NT) lamv[i] = rot[D + i];
+  // the largest nval eigenvalues by multisection (fewer eigenvalues: more
+  // threads per bracket, fewer rounds)
+  const int nval = min(max(a.nval, a.rK), D);
+  eig_bisect<double, NT>(w, D, nval);
+  for (int i = tid; i < D; i += NT) lamv[i] = i < nval ? rot[D + i] : 0.0;
   // reflectors: column-major packed, through registers, behind the vector block
   const bool lds_vecs = a.rK <= RKL;
   const int zl = lds_vecs ? 2 * a.rK + 1 : D;
@@ -209,7 +211,7 @@ __global__ __launch_bounds__(1024) void k_key_eig(EigArgs a) {
   EigWork<double> wz{nullptr, 0, Z, zl, dg, eo, tau, vb, pb, rot, ctl};
   if (eig_twisted<double, NT>(wz, D, a.rK)) {
     for (int i = tid; i < D; i += NT) {
-      if (a.eigval) a.eigval[(long long)bh * D + i] = lamv[i];
+      if (a.eigval && i < nval) a.eigval[(long long)bh * D + i] = lamv[i];
       if (i < a.rK) top[i] = i;
     }
   } else {
@@ -752,8 +754,10 @@ __global__ __launch_bounds__(512) void k_kmeans_assign(AssignArgs a) {
 #undef SP_LOAD_BLOCK
 }
 
+// (second launch bound: waves per SIMD; at D <= 32 six, so that three
+// workgroups share a CU, as many as the staged centres' LDS allows)
 template <int D, bool LO, int CG>
-__global__ __launch_bounds__(512, (LO && D >= 64) ? 2 : 4) void k_kmeans_assign_staged(AssignArgs a) {
+__global__ __launch_bounds__(512, (LO && D >= 64) ? 2 : (D <= 32 ? 6 : 4)) void k_kmeans_assign_staged(AssignArgs a) {
   // General form (any D, any G <= kMaxGroups).  One 256-point histogram chunk per
   // workgroup (8 waves x one 32-point MFMA column, points held as B operands
   // in registers); the centre images are staged through LDS CG at a time
@@ -1647,8 +1651,10 @@ hipError_t launch_sample_metric(const Plan& p, hipStream_t s) {
   return hipSuccess;
 }
 
-hipError_t launch_key_eig(const Plan& p, hipStream_t s) {
-  EigArgs a{p.mk, p.eigval, p.kmap, p.kmap_pad, p.eigz, p.rK, p.rKpad, p.scale};
+hipError_t launch_key_eig(const Plan& p, hipStream_t s, bool all_eigenvalues) {
+  // the call itself needs only the leading rK eigenpairs; the whole spectrum
+  // is computed when it is reported
+  EigArgs a{p.mk, p.eigval, p.kmap, p.kmap_pad, p.eigz, p.rK, p.rKpad, p.scale, all_eigenvalues ? p.d : p.rK};
   if (p.d == 128) SP_LAUNCH(k_key_eig<128>, dim3(p.BH), dim3(1024), s, a);
   else SP_LAUNCH(k_key_eig<64>, dim3(p.BH), dim3(1024), s, a);
   return hipSuccess;

@@ -22,6 +22,7 @@ struct EigArgs {
   double* eigz;      // [BH, d, d] eigenvector scratch (shifted-QR fallback, rK > 32)
   int rK, rKpad;
   float scale;
+  int nval;          // eigenvalues computed and reported: the largest nval (rK <= nval <= d)
 };
 
 struct CoordArgs {
@@ -161,7 +162,7 @@ struct GatherArgs {
 };
 
 hipError_t launch_sample_metric(const Plan& p, hipStream_t s);
-hipError_t launch_key_eig(const Plan& p, hipStream_t s);
+hipError_t launch_key_eig(const Plan& p, hipStream_t s, bool all_eigenvalues);
 hipError_t launch_key_coords(const Plan& p, hipStream_t s);
 hipError_t launch_split_rows(const Plan& p, const View4& x, hipStream_t s);
 hipError_t launch_assign(const Plan& p, const AssignArgs& a, int D, bool lo, hipStream_t s);

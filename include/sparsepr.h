@@ -161,8 +161,7 @@ sparsepr_status sparsepr_config_default(int N, int d, sparsepr_config* out);
 sparsepr_status sparsepr_validate(const sparsepr_config* cfg, int B, int H, int N, int d, int dtype);
 
 /* Bytes of workspace every entry point below needs for this shape (256-byte
-   aligned base required; with B = 1 and H >= 2 it covers both halves of
-   sparsepr_attention). */
+   aligned base required). */
 sparsepr_status sparsepr_workspace_size(const sparsepr_config* cfg, int B, int H, int N, int d,
                                         int dtype, size_t* bytes);
 
@@ -170,33 +169,21 @@ sparsepr_status sparsepr_workspace_size(const sparsepr_config* cfg, int B, int H
    tensor reorder, sparse attention, exact probe rows, residual fit,
    correction, output restoration).  Writes o in the original token order.
    `stats` (device pointer, nullable) receives B*H sparsepr_head_stats.
-   With B = 1 and H >= 2 the heads run in two halves: the second half on a
-   side stream that the library keeps for this caller stream and device,
-   forked from `stream` once the first half's key eigensolve is enqueued and
-   joined back to `stream` with an event before the call returns.  Work
-   enqueued on `stream` after the call therefore sees the whole output, and
-   the fork and join are recorded by HIP graph capture of `stream` like any
-   other work.  The result is the same as the unsplit call's.
-   State: the side stream and its two events are created on the first split
-   call on a caller stream (default priority) and kept until the process
-   ends; they order work and carry no data between calls (every
-   intermediate lives in `workspace`, as the pages' per-call calibration
-   with no persistent state requires -- [DG] "Partition the Support,
-   Reconstruct the Residual" digest, 行业影响/与现有工作流的接口).  Nothing
-   is created while `stream` is capturing: a first call on a stream under
-   capture runs both halves on `stream` (one stream, same result).  Calls on
-   different caller streams use different side streams and may run
-   concurrently; calls on one caller stream serialise only their enqueueing
-   (a process-wide mutex), and, sharing a workspace, must be ordered by the
-   caller as every call must. */
+   Every kernel of the call is enqueued on `stream`, in order, so work
+   enqueued on `stream` after the call sees the whole output, and HIP graph
+   capture of `stream` records the call like any other work.
+   State: none.  Every intermediate lives in `workspace`, as the pages'
+   per-call calibration with no persistent state requires ([DG] "Partition
+   the Support, Reconstruct the Residual" digest, 行业影响/与现有工作流的接口);
+   calls that share a workspace must be ordered by the caller. */
 sparsepr_status sparsepr_attention(const sparsepr_config* cfg, const sparsepr_tensors* io,
                                    void* workspace, size_t workspace_bytes, void* stream,
                                    sparsepr_head_stats* stats);
 
 /* The full call for callers that cannot allocate (code under HIP graph
    capture, tight serving loops, harnesses that forbid hipMalloc): the same
-   computation and result as sparsepr_attention, run entirely on `stream`
-   (no head split, no second stream), with the intermediates in a fixed
+   computation and result as sparsepr_attention, run entirely on `stream`,
+   with the intermediates in a fixed
    scratch array of sparsepr_noalloc_scratch_bytes() bytes (128 MiB) that the
    library holds on each GPU it runs on until the process ends.  No memory
    is allocated or freed by the call.  A call whose workspace would exceed

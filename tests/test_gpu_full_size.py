@@ -44,8 +44,8 @@ def test_c3_full_size_on_sampled_heads():
     ocfg = OracleConfig(**kw)
     ws = sp.Workspace()
     out = sp.sparsepr_attention(q, k, v, cfg, workspace=ws)
-    # the timed configuration is deterministic: a second call (two streams,
-    # all 40 heads) reproduces the output bit for bit
+    # the timed configuration is deterministic: a second call (all 40
+    # heads) reproduces the output bit for bit
     again = sp.sparsepr_attention(q, k, v, cfg, workspace=ws)
     torch.cuda.synchronize()
     assert torch.equal(out, again)

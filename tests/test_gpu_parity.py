@@ -328,12 +328,11 @@ def test_full_density_is_dense_attention():
         assert max_abs(got, r["dense"]) <= ma and rel_frob(got, r["dense"]) <= rf
 
 
-def test_two_stream_call_equals_one_stream():
-    """The main call runs its heads in two halves on two streams (B = 1).  With
-    three heads (halves of 1 and 2) its output and statistics must equal,
-    bit for bit, those of the profiling entry point, which runs every head on
-    one stream: the second half's query sample is seeded by its global head
-    index and its tensors are addressed at the right head offset."""
+def test_main_call_equals_profiled_call():
+    """With three heads the main call's output and statistics equal, bit for
+    bit, those of the profiling entry point (the same kernels with timing
+    events between the stages): every head's query sample is seeded by its
+    own head index and its tensors are addressed at its own head offset."""
     from synth.generator import make_video_qkv
 
     c = case("bf16_d64")

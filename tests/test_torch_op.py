@@ -111,16 +111,15 @@ def test_operator_token_major_batch_of_two_matches_the_oracle():
 
 @pytest.mark.gpu
 def test_first_call_ever_on_a_stream_under_capture():
-    """A capture stream that no call has used: the library creates no side
-    stream during the capture and runs the call on the capture stream alone;
-    its workspace is that stream's own buffer (allocated in the capture's
+    """A capture stream that no call has used: the call runs on the capture
+    stream and its workspace is that stream's own buffer (allocated in the capture's
     pool).  Replays, with eager calls on the default stream between them,
     match the eager result."""
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
     import free_block_sparse_amd as sp
 
-    q, k, v = _qkv(2)  # B = 1, H = 2: the call that splits its heads over two streams
+    q, k, v = _qkv(2)  # B = 1, H = 2
     B, H, N, d = q.shape
     cfg = sp.make_config(N, d, density=0.25, probe_rows=32, residual_rank=8)
     ws = sp.Workspace()
