@@ -887,7 +887,7 @@ __global__ __launch_bounds__(512, (LO && D >= 64) ? 2 : (D <= 32 ? 6 : 4)) void 
 // 16 lanes per such point, lanes over dimensions, row-major images.  The
 // points with a third centre in range (the back of the list) are re-decided
 // over every centre by a whole workgroup (one centre per thread,
-// dimension-major images, 32 loads in flight).  A changed label moves the
+// dimension-major images, 64 loads in flight).  A changed label moves the
 // point between the chunk histograms with integer atomics.
 template <typename T>
 __device__ inline double point_value(const RedecideArgs& a, const T* row, int k) {
@@ -908,7 +908,7 @@ __device__ inline void relabel(const RedecideArgs& a, int bh, int n, int win) {
 
 template <typename T>
 __global__ __launch_bounds__(256) void k_kmeans_redecide(RedecideArgs a) {
-  constexpr int NW = 4, KU = 32;
+  constexpr int NW = 4, KU = 64;
   __shared__ double sv[NW];
   __shared__ int si[NW];
   __shared__ double sx[128];
@@ -933,12 +933,26 @@ __global__ __launch_bounds__(256) void k_kmeans_redecide(RedecideArgs a) {
     const int n = ent.x, b = ent.y, s = ent.z;
     double db = 0.0, ds = 0.0;
     if (act) {
+      // every load of the point's row and of both images first (Dx <= 128:
+      // at most eight dimensions per lane), then the products in order
+      constexpr int KI = 128 / 16;
       const double* x64 = a.x64 ? a.x64 + ((long long)bh * a.N + n) * a.x64stride : nullptr;
       const T* xr = a.x64 ? nullptr : rawb + a.raw.row_off(bh, n);
-      for (int k = sub; k < Dx; k += 16) {
-        const double x = x64 ? x64[k] : point_value<T>(a, xr, k);
-        db = __builtin_fma(x, yr[(long long)b * a.ystride + k], db);
-        ds = __builtin_fma(x, yr[(long long)s * a.ystride + k], ds);
+      const double* yb = yr + (long long)b * a.ystride;
+      const double* ys = yr + (long long)s * a.ystride;
+      double xv[KI], bv[KI], sv2[KI];
+#pragma unroll
+      for (int i = 0; i < KI; ++i) {
+        const int k = sub + 16 * i;
+        const bool ok = k < Dx;
+        xv[i] = ok ? (x64 ? x64[k] : point_value<T>(a, xr, k)) : 0.0;
+        bv[i] = ok ? yb[k] : 0.0;
+        sv2[i] = ok ? ys[k] : 0.0;
+      }
+#pragma unroll
+      for (int i = 0; i < KI; ++i) {
+        db = __builtin_fma(xv[i], bv[i], db);
+        ds = __builtin_fma(xv[i], sv2[i], ds);
       }
     }
     for (int o = 8; o > 0; o >>= 1) {
