@@ -1190,17 +1190,26 @@ __global__ __launch_bounds__(256) void k_group_mean(UpdateArgs a) {
   double s = 0.0;
   if (a.means_out) {
     // Means handed to the router: rows summed one after another in ascending
-    // token order, as the reference computation does (one thread per dim).
-    if (tid < Dp) {
-      int r = a0;
-      for (; r + 7 < a1; r += 8) {
-        double v[8];
+    // token order, the order of the mean's plain definition (one thread per
+    // dim).  The group's row indices are staged NT at a time in LDS; each
+    // thread keeps 16 row loads in flight.
+    __shared__ int sidx[NT];
+    for (int c0 = a0; c0 < a1; c0 += NT) {
+      const int nr = min(NT, a1 - c0);
+      __syncthreads();  // the previous indices are consumed
+      if (tid < nr) sidx[tid] = perm[c0 + tid];
+      __syncthreads();
+      if (tid < Dp) {
+        int r = 0;
+        for (; r + 15 < nr; r += 16) {
+          double v[16];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) v[u] = (double)Elem<TP>::load(xb + a.pts.row_off(bh, perm[r + u]) + tid);
+          for (int u = 0; u < 16; ++u) v[u] = (double)Elem<TP>::load(xb + a.pts.row_off(bh, sidx[r + u]) + tid);
 #pragma unroll
-        for (int u = 0; u < 8; ++u) s = __dadd_rn(s, (double)v[u]);
+          for (int u = 0; u < 16; ++u) s = __dadd_rn(s, v[u]);
+        }
+        for (; r < nr; ++r) s = __dadd_rn(s, (double)Elem<TP>::load(xb + a.pts.row_off(bh, sidx[r]) + tid));
       }
-      for (; r < a1; ++r) s = __dadd_rn(s, (double)Elem<TP>::load(xb + a.pts.row_off(bh, perm[r]) + tid));
     }
   } else {
     // Lloyd updates: 16-byte row pieces; thread (piece c, subset pt) sums the
@@ -1214,24 +1223,25 @@ __global__ __launch_bounds__(256) void k_group_mean(UpdateArgs a) {
 #pragma unroll
     for (int q = 0; q < VEC; ++q) acc[q] = 0.0;
     if (pt < P) {
-      int r = a0 + pt;
-      for (; r + 3 * P < a1; r += 4 * P) {
-        uint4 u[4];
+      // eight rows of the subset at a time: their indices, then their
+      // pieces, all loads in flight together; summed in ascending row order
+      constexpr int RB = 8;
+      for (int r = a0 + pt; r < a1; r += RB * P) {
+        int idx[RB];
 #pragma unroll
-        for (int k = 0; k < 4; ++k)
-          u[k] = *reinterpret_cast<const uint4*>(xb + a.pts.row_off(bh, perm[r + k * P]) + c * VEC);
+        for (int k = 0; k < RB; ++k) idx[k] = r + k * P < a1 ? perm[r + k * P] : -1;
+        uint4 u[RB];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
+        for (int k = 0; k < RB; ++k)
+          u[k] = idx[k] >= 0 ? *reinterpret_cast<const uint4*>(xb + a.pts.row_off(bh, idx[k]) + c * VEC)
+                             : make_uint4(0, 0, 0, 0);
+#pragma unroll
+        for (int k = 0; k < RB; ++k) {
+          if (idx[k] < 0) break;
           const TP* ev = reinterpret_cast<const TP*>(&u[k]);
 #pragma unroll
           for (int q = 0; q < VEC; ++q) acc[q] = __dadd_rn(acc[q], (double)Elem<TP>::load(ev + q));
         }
-      }
-      for (; r < a1; r += P) {
-        const uint4 u = *reinterpret_cast<const uint4*>(xb + a.pts.row_off(bh, perm[r]) + c * VEC);
-        const TP* ev = reinterpret_cast<const TP*>(&u);
-#pragma unroll
-        for (int q = 0; q < VEC; ++q) acc[q] = __dadd_rn(acc[q], (double)Elem<TP>::load(ev + q));
       }
 #pragma unroll
       for (int q = 0; q < VEC; ++q) part[pt * (cpr * VEC) + c * VEC + q] = acc[q];
