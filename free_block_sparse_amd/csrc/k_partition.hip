@@ -96,17 +96,20 @@ __global__ __launch_bounds__(256) void k_query_sample(SampleArgs a) {
 // M_K = Q_s^T Q_s / M_s in fp64 (a d x d block per (b,h), 4 x 4 outputs per
 // thread).  The sampled rows are staged 64 at a time as fp32 (bf16 and fp32
 // inputs are exact there); products of two fp32 values are exact in fp64, so
-// only the additions round.
+// only the additions round.  (D/4)^2 / 256 workgroups of 256 threads per
+// (b,h), each owning a band of block rows.
 template <typename T, int D>
-__global__ __launch_bounds__(1024) void k_key_metric64(SampleArgs a) {
+__global__ __launch_bounds__(256) void k_key_metric64(SampleArgs a) {
   constexpr int LDQ = D + 4;  // 16-byte rows
+  constexpr int NT = 256;
   __shared__ __align__(16) float qs[64][LDQ];
   __shared__ int smp[256];
-  const int bh = blockIdx.x, tid = threadIdx.x;
+  const int bh = blockIdx.y, tid = threadIdx.x;
   const int Ms = a.Ms;
   if (tid < Ms) smp[tid] = a.sample[(long long)bh * Ms + tid];
   constexpr int NB = D / 4;  // 4 x 4 blocks per side
-  const int bi = tid / NB, bj = tid - (tid / NB) * NB;
+  const int blk = blockIdx.x * NT + tid;
+  const int bi = blk / NB, bj = blk - (blk / NB) * NB;
   const bool act = bi < NB;
   double acc[4][4];
 #pragma unroll
@@ -118,7 +121,7 @@ __global__ __launch_bounds__(1024) void k_key_metric64(SampleArgs a) {
   for (int c0 = 0; c0 < Ms; c0 += 64) {
     const int nr = min(64, Ms - c0);
     __syncthreads();
-    for (int e = tid; e < nr * (D / VEC); e += 1024) {
+    for (int e = tid; e < nr * (D / VEC); e += NT) {
       const int r = e / (D / VEC), c = (e - r * (D / VEC)) * VEC;
       const uint4 u = *reinterpret_cast<const uint4*>(qbase + a.q.row_off(bh, smp[c0 + r]) + c);
       const T* ev = reinterpret_cast<const T*>(&u);
@@ -1490,47 +1493,65 @@ __global__ __launch_bounds__(256) void k_centre_images_f64mfma(UpdateArgs a) {
 // Centred query coordinates u_i - mean_h(u_ih) have the metric
 // s^2 sum_h (cbar_h - m)(cbar_h - m)^T with m the mean of the non-empty
 // centres, so the centres are centred before the outer products.
-__global__ __launch_bounds__(1024) void k_query_metric(QMetricArgs a) {
-  constexpr int HB = 16;
-  __shared__ double cs[HB][128];
+__global__ __launch_bounds__(256) void k_query_metric(QMetricArgs a) {
+  constexpr int HB = 16, NT = 256, PER = HB * 128 / NT;
+  __shared__ double cs[2][HB][128];  // two stages: one barrier per stage
   __shared__ double cmean[128];
-  const int bh = blockIdx.x, d = a.d, tid = threadIdx.x;
+  __shared__ unsigned char ne[kMaxGroups];
+  const int bh = blockIdx.y, d = a.d, tid = threadIdx.x;
   const double* cb = a.cbar + (long long)bh * a.GK * d;
   const int* off = a.off_k + (long long)bh * (a.GK + 1);
+  for (int h = tid; h < a.GK; h += NT) ne[h] = off[h + 1] > off[h] ? 1 : 0;
+  __syncthreads();
   if (tid < d) {
     double sm = 0.0;
     int cnt = 0;
     if (a.centred)
       for (int h = 0; h < a.GK; ++h)
-        if (off[h + 1] > off[h]) {
+        if (ne[h]) {
           sm += cb[(long long)h * d + tid];
           ++cnt;
         }
     cmean[tid] = cnt > 0 ? sm / (double)cnt : 0.0;
   }
   const int nb = d / 4;  // 4x4 blocks per row of blocks
-  const int bi = tid / nb, bj = tid - (tid / nb) * nb;
+  const int blk = blockIdx.x * NT + tid;  // (d/4)^2 / 256 workgroups per (b,h), one band of block rows each
+  const int bi = blk / nb, bj = blk - (blk / nb) * nb;
   const bool act = bi < nb;
   double acc[4][4];
 #pragma unroll
   for (int x = 0; x < 4; ++x)
 #pragma unroll
     for (int y = 0; y < 4; ++y) acc[x][y] = 0.0;
-  for (int h0 = 0; h0 < a.GK; h0 += HB) {
-    __syncthreads();
-    for (int e = tid; e < HB * d; e += 1024) {
-      const int hl = e / d, j = e - (e / d) * d;
+  // the next stage's centres are loaded into registers while the current
+  // stage is multiplied
+  double pre[PER];
+  auto load = [&](int h0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int e = tid + NT * u, hl = e / d, j = e - (e / d) * d;
       const int h = h0 + hl;
-      cs[hl][j] = (h < a.GK && off[h + 1] > off[h]) ? cb[(long long)h * d + j] - cmean[j] : 0.0;
+      pre[u] = (hl < HB && h < a.GK && ne[h]) ? cb[(long long)h * d + j] : 0.0;
+    }
+  };
+  load(0);
+  __syncthreads();  // cmean
+  int buf = 0;
+  for (int h0 = 0; h0 < a.GK; h0 += HB, buf ^= 1) {
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int e = tid + NT * u, hl = e / d, j = e - (e / d) * d;
+      if (hl < HB) cs[buf][hl][j] = (h0 + hl < a.GK && ne[h0 + hl]) ? pre[u] - cmean[j] : 0.0;
     }
     __syncthreads();
+    if (h0 + HB < a.GK) load(h0 + HB);
     if (act) {
       for (int hl = 0; hl < HB; ++hl) {
         double u[4], v[4];
 #pragma unroll
         for (int x = 0; x < 4; ++x) {
-          u[x] = cs[hl][4 * bi + x];
-          v[x] = cs[hl][4 * bj + x];
+          u[x] = cs[buf][hl][4 * bi + x];
+          v[x] = cs[buf][hl][4 * bj + x];
         }
 #pragma unroll
         for (int x = 0; x < 4; ++x)
@@ -1666,11 +1687,11 @@ hipError_t launch_sample_metric(const Plan& p, hipStream_t s) {
   SampleArgs a{p.q, p.N, p.Ms, p.bh0, p.seed, p.sample, p.mk};
   SP_LAUNCH(k_query_sample, dim3(p.BH), dim3(256), s, a);
   if (p.dtype == SPARSEPR_BF16) {
-    if (p.d == 128) SP_LAUNCH((k_key_metric64<bf16_t, 128>), dim3(p.BH), dim3(1024), s, a);
-    else SP_LAUNCH((k_key_metric64<bf16_t, 64>), dim3(p.BH), dim3(1024), s, a);
+    if (p.d == 128) SP_LAUNCH((k_key_metric64<bf16_t, 128>), dim3(4, p.BH), dim3(256), s, a);
+    else SP_LAUNCH((k_key_metric64<bf16_t, 64>), dim3(1, p.BH), dim3(256), s, a);
   } else {
-    if (p.d == 128) SP_LAUNCH((k_key_metric64<float, 128>), dim3(p.BH), dim3(1024), s, a);
-    else SP_LAUNCH((k_key_metric64<float, 64>), dim3(p.BH), dim3(1024), s, a);
+    if (p.d == 128) SP_LAUNCH((k_key_metric64<float, 128>), dim3(4, p.BH), dim3(256), s, a);
+    else SP_LAUNCH((k_key_metric64<float, 64>), dim3(1, p.BH), dim3(256), s, a);
   }
   return hipSuccess;
 }
@@ -1800,7 +1821,7 @@ hipError_t launch_centre_update(const Plan& p, const UpdateArgs& a, int pts_type
 
 hipError_t launch_query_metric(const Plan& p, hipStream_t s) {
   QMetricArgs a{p.cbar, p.off_k, p.GK, p.d, p.scale, p.centred_qc, p.mq};
-  SP_LAUNCH(k_query_metric, dim3(p.BH), dim3(1024), s, a);
+  SP_LAUNCH(k_query_metric, dim3((unsigned)((p.d / 4) * (p.d / 4) / 256), p.BH), dim3(256), s, a);
   return hipSuccess;
 }
 
