@@ -92,12 +92,15 @@ __global__ __launch_bounds__(256) void k_route_mu(RouteArgs a) {
 // One wave per query group (four per workgroup); no workgroup barriers.
 __global__ __launch_bounds__(256) void k_route_keys(RouteArgs a) {
   __shared__ double term[4][kMaxGroups];
+  __shared__ int nks[kMaxGroups];  // key group sizes, staged once for the four waves
   const int bh = blockIdx.y, wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int g = blockIdx.x * 4 + wv;
-  if (g >= a.GQ) return;
   const int GK = a.GK;
   const int* offq = a.off_q + (long long)bh * (a.GQ + 1);
   const int* offk = a.off_k + (long long)bh * (a.GK + 1);
+  for (int h = threadIdx.x; h < GK; h += 256) nks[h] = offk[h + 1] - offk[h];
+  __syncthreads();
+  const int g = blockIdx.x * 4 + wv;
+  if (g >= a.GQ) return;
   const long long row = ((long long)bh * a.GQ + g) * GK;
   const int nq = offq[g + 1] - offq[g];
   if (nq <= 0) {
@@ -112,7 +115,7 @@ __global__ __launch_bounds__(256) void k_route_keys(RouteArgs a) {
   double bm = -INFINITY;
   int bi = 0x7fffffff;
   for (int h = lane; h < GK; h += 64) {
-    if (offk[h + 1] <= offk[h]) continue;
+    if (nks[h] <= 0) continue;
     const double m = a.mu[row + h];
     if (bi == 0x7fffffff || m > bm) {  // strided per-lane scan keeps the first maximum
       bm = m;
@@ -134,7 +137,7 @@ __global__ __launch_bounds__(256) void k_route_keys(RouteArgs a) {
   double* tm = term[wv];
   for (int h = lane; h < GK; h += 64) {
     double t = 0.0;
-    if (finite && offk[h + 1] > offk[h]) t = __dmul_rn((double)(offk[h + 1] - offk[h]), exp(__dsub_rn(a.mu[row + h], mx)));
+    if (finite && nks[h] > 0) t = __dmul_rn((double)nks[h], exp(__dsub_rn(a.mu[row + h], mx)));
     tm[h] = t;
   }
   // sequential sum in ascending h (lane 0); this wave's LDS writes above are
@@ -143,7 +146,7 @@ __global__ __launch_bounds__(256) void k_route_keys(RouteArgs a) {
   if (lane == 0) {
     double tot = 0.0;
     for (int h = 0; h < GK; ++h)
-      if (offk[h + 1] > offk[h]) tot = __dadd_rn(tot, tm[h]);
+      if (nks[h] > 0) tot = __dadd_rn(tot, tm[h]);
     ell = finite ? __dadd_rn(mx, log(tot)) : 0.0;
     a.mand[(long long)bh * a.GQ + g] = best == 0x7fffffff ? -1 : best;
   }
@@ -151,11 +154,11 @@ __global__ __launch_bounds__(256) void k_route_keys(RouteArgs a) {
   for (int h = lane; h < GK; h += 64) {
     uint64_t ck = kExcluded;
     double ms = 0.0;
-    if (offk[h + 1] > offk[h]) {
+    if (nks[h] > 0) {
       double key = finite ? __dsub_rn(a.mu[row + h], ell) : -INFINITY;
       if (key != key) key = -INFINITY;
       if (h != best) ck = ~ord_f64(key);
-      if (a.rmass) ms = __dmul_rn((double)(offk[h + 1] - offk[h]), exp(key));
+      if (a.rmass) ms = __dmul_rn((double)nks[h], exp(key));
     }
     a.ckey[row + h] = ck;
     if (a.rmass) a.rmass[row + h] = ms;
