@@ -854,10 +854,11 @@ __global__ __launch_bounds__(256, 2) void k_probe_attn_mfma(ProbeArgs a) {
   constexpr int CPR = D / 8, RPI = 64 / CPR, IPW = 64 / RPI / 4;
   constexpr int VOFF = 64 * D * 2;
   constexpr int MW = kMaxGroups / 32;
+  constexpr int MS = MW + 1;  // odd row stride: the lanes' probes read distinct banks
   __shared__ __attribute__((aligned(1024))) bf16_t KV0[2 * 64 * D];
   __shared__ __attribute__((aligned(1024))) bf16_t KV1[2 * 64 * D];
   __shared__ int kg0[64], kg1[64];
-  __shared__ uint32_t msk[64 * MW];
+  __shared__ uint32_t msk[64 * MS];
   const int bh = blockIdx.z, pb = blockIdx.y, ch = blockIdx.x, tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63, half = lane >> 5, col = lane & 31;
   const bool sparse_role = w >= 2;
@@ -868,7 +869,7 @@ __global__ __launch_bounds__(256, 2) void k_probe_attn_mfma(ProbeArgs a) {
   for (int e = tid; e < 64 * a.gwords; e += 256) {
     const int r = e / a.gwords, wd = e - r * a.gwords;
     const int pp = pb * 64 + r;
-    msk[r * MW + wd] =
+    msk[r * MS + wd] =
         pp < a.M ? a.gmask[((long long)bh * a.GQ + a.pgroup[(long long)bh * a.M + pp]) * a.gwords + wd] : 0u;
   }
   const int pl = 32 * (w & 1) + col;
@@ -912,7 +913,7 @@ __global__ __launch_bounds__(256, 2) void k_probe_attn_mfma(ProbeArgs a) {
   lds_char* const s0 = (lds_char*)KV0;
   lds_char* const s1 = (lds_char*)KV1;
   const int ntile = (L + 63) / 64;
-  const uint32_t* mrow = msk + pl * MW;
+  const uint32_t* mrow = msk + pl * MS;
   // the tile's 64 group ids travel by LDS-DMA too (wave 0, 4 bytes a lane)
   auto issue_groups = [&](int* kgn, int tt) __attribute__((always_inline)) {
     if (w == 0)
