@@ -352,21 +352,40 @@ __global__ __launch_bounds__(256) void k_key_coords_f64mfma(CoordArgs a) {
     for (int t = 0; t < NJ; ++t) bfr[ks][t] = km[(4 * ks + lk) * RP + 16 * t + li];
   const T* kb = static_cast<const T*>(a.k.p);
   float* my = kr[w];
+  // the next tile's rows are loaded into registers while the current tile is
+  // multiplied (16 rows x PPR pieces, NPL pieces per lane)
+  constexpr int NPL = 16 * PPR / 64;
+  static_assert(16 * PPR % 64 == 0, "whole pieces per lane");
+  const int kbase = (blockIdx.x * 4 + w) * (16 * KT);
+  uint4 pre[NPL];
+  auto load_tile = [&](int key0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int q = 0; q < NPL; ++q) {
+      const int e = lane + 64 * q, r = e / PPR, c = (e - r * PPR) * VEC;
+      pre[q] = key0 + r < N ? *reinterpret_cast<const uint4*>(kb + a.k.row_off(bh, key0 + r) + c)
+                            : make_uint4(0, 0, 0, 0);
+    }
+  };
+  if (kbase < N) load_tile(kbase);
   for (int kt = 0; kt < KT; ++kt) {
-    const int key0 = (blockIdx.x * 4 + w) * (16 * KT) + 16 * kt;
+    const int key0 = kbase + 16 * kt;
     if (key0 >= N) break;  // uniform per wave
     // stage the tile's 16 rows (the wave's own slice: order its writes before its reads)
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    for (int e = lane; e < 16 * PPR; e += 64) {
-      const int r = e / PPR, c = (e - r * PPR) * VEC;
-      uint4 u = make_uint4(0, 0, 0, 0);
-      if (key0 + r < N) u = *reinterpret_cast<const uint4*>(kb + a.k.row_off(bh, key0 + r) + c);
-      const T* ev = reinterpret_cast<const T*>(&u);
 #pragma unroll
-      for (int j = 0; j < VEC; ++j) my[r * KL + c + j] = Elem<T>::load(ev + j);
+    for (int q = 0; q < NPL; ++q) {
+      const int e = lane + 64 * q, r = e / PPR, c = (e - r * PPR) * VEC;
+      const T* ev = reinterpret_cast<const T*>(&pre[q]);
+      float f[VEC];
+#pragma unroll
+      for (int j = 0; j < VEC; ++j) f[j] = Elem<T>::load(ev + j);
+#pragma unroll
+      for (int j = 0; j < VEC; j += 4)
+        *reinterpret_cast<float4*>(&my[r * KL + c + j]) = make_float4(f[j], f[j + 1], f[j + 2], f[j + 3]);
     }
+    if (kt + 1 < KT && key0 + 16 < N) load_tile(key0 + 16);
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
