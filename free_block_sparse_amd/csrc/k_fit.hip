@@ -306,7 +306,7 @@ __global__ __launch_bounds__(1024) void k_fit(FitArgs a) {
     double acc = 0.0;
     if (i < n && j < n) {
       if (small) {
-        for (int k = 0; k < d; ++k) acc += (double)Rf[i * ldx + k] * (double)Rf[j * ldx + k];
+        acc = dot4(Rf + i * ldx, 1, Rf + j * ldx, 1, d);
         if (a.weighted) acc *= sqrt(w[i]) * sqrt(w[j]);
       } else if (a.weighted) {
         for (int mm = 0; mm < M; ++mm) acc += w[mm] * ((double)Rf[mm * ldx + i] * (double)Rf[mm * ldx + j]);
@@ -444,8 +444,7 @@ __global__ __launch_bounds__(1024) void k_fit(FitArgs a) {
       double* K = G;
       for (int e = tid; e < M * M; e += nt) {
         const int i = e / M, j = e - (e / M) * M;
-        double acc = 0.0;
-        for (int dm = 0; dm < d; ++dm) acc += (double)Xf[i * ldx + dm] * (double)Xf[j * ldx + dm];
+        const double acc = dot4(Xf + i * ldx, 1, Xf + j * ldx, 1, d);
         K[i * ldg + j] = sqrt(w[i] * w[j]) * acc + (i == j ? lam : 0.0);
       }
       for (int e = tid; e < M * rk; e += nt) Yc[e] *= sqrt(w[e / rk]);

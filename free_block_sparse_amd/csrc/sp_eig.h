@@ -103,65 +103,133 @@ struct EigWork {
   int* ctl;  // [8]
 };
 
-// Step 1.  NT threads; every thread calls it.
+// Reflector of the column x (x[0] and the squared norm sig of x[1..m)): the
+// scalars of step k.  Returns the scale of x[1..m) in v.
+template <typename T>
+__device__ inline T eig_reflector(const EigWork<T>& w, int k, T x0, T sig, T diag) {
+  T tau = 0, beta = x0, scale = 0;
+  if (sig != T(0)) {
+    const T nrm = sqrt(x0 * x0 + sig);
+    beta = x0 >= T(0) ? -nrm : nrm;
+    tau = (beta - x0) / beta;
+    scale = T(1) / (x0 - beta);
+  }
+  if ((threadIdx.x & 63) == 0) {
+    w.tau[k] = tau;
+    w.eo[k] = beta;
+    w.dg[k] = diag;
+  }
+  return scale;
+}
+
+// Step 1.  NT >= 256 threads; every thread calls it.  Step k: p = tau A22 v
+// (all threads), then wave 0 applies the rank-2 update to the first column
+// of A22 alone and forms the next step's reflector from it (in registers)
+// while the other waves update the rest of A22: one workgroup barrier fewer
+// per step, and the reflector's serial work runs beside the update.  The
+// reflectors alternate between w.vb and w.rot (free until step 2).
 template <typename T, int NT>
 __device__ void eig_tridiagonalize(const EigWork<T>& w, int n) {
+  static_assert(NT >= 256, "wave 0 forms the reflectors beside the other waves' update");
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   T* A = w.A;
   const int lda = w.lda;
-  constexpr int TPR = NT >= 256 ? NT / 128 : 1;  // threads per row of the product
-  for (int k = 0; k + 2 < n; ++k) {
+  constexpr int TPR = NT / 128;              // threads per row of the product
+  constexpr int TPU = (NT - 64) / 128;       // threads per row of the update (waves 1..)
+  constexpr int RGU = (NT - 64) / TPU;       // rows updated at once
+  // reflector of step k from column k of A as it stands in LDS (wave 0)
+  auto reflect_lds = [&](int k, T* vout) __attribute__((always_inline)) {
     const int m = n - k - 1;
     T* x = A + (k + 1) * lda + k;  // x[i * lda], i < m
-    if (wv == 0) {
-      T sig = 0;
-      for (int i = 1 + lane; i < m; i += 64) sig += x[i * lda] * x[i * lda];
-      sig = eig_sum(sig, 64);
-      const T x0 = x[0];
-      T tau = 0, beta = x0, scale = 0;
-      if (sig != T(0)) {
-        const T nrm = sqrt(x0 * x0 + sig);
-        beta = x0 >= T(0) ? -nrm : nrm;
-        tau = (beta - x0) / beta;
-        scale = T(1) / (x0 - beta);
-      }
-      for (int i = lane; i < m; i += 64) {
-        const T vi = i == 0 ? T(1) : x[i * lda] * scale;
-        w.vb[i] = vi;
-        x[i * lda] = vi;
-      }
-      if (lane == 0) {
-        w.tau[k] = tau;
-        w.eo[k] = beta;
-        w.dg[k] = A[k * lda + k];
-      }
+    T sig = 0;
+    for (int i = 1 + lane; i < m; i += 64) sig += x[i * lda] * x[i * lda];
+    sig = eig_sum(sig, 64);
+    const T scale = eig_reflector(w, k, x[0], sig, A[k * lda + k]);
+    for (int i = lane; i < m; i += 64) {
+      const T vi = i == 0 ? T(1) : x[i * lda] * scale;
+      vout[i] = vi;
+      x[i * lda] = vi;
     }
-    __syncthreads();
+  };
+  if (n > 2 && wv == 0) reflect_lds(0, w.vb);
+  __syncthreads();
+  for (int k = 0; k + 2 < n; ++k) {
+    const int m = n - k - 1;
+    const T* vb = (k & 1) ? w.rot : w.vb;
+    T* vnext = (k & 1) ? w.vb : w.rot;
+    const bool next = k + 3 < n;  // a reflector of step k + 1 follows
     const T tau = w.tau[k];
-    if (tau == T(0)) continue;
+    if (tau == T(0)) {
+      if (next && wv == 0) reflect_lds(k + 1, vnext);
+      __syncthreads();
+      continue;
+    }
     {
       const int row = tid / TPR, sub = tid - row * TPR;
       T acc = 0;
       if (row < m) {
         const T* ar = A + (k + 1 + row) * lda + (k + 1);
-        for (int j = sub; j < m; j += TPR) acc += ar[j] * w.vb[j];
+        for (int j = sub; j < m; j += TPR) acc += ar[j] * vb[j];
       }
-      if (TPR > 1) acc = eig_sum(acc, TPR);
+      acc = eig_sum(acc, TPR);
       if (row < m && sub == 0) w.pb[row] = tau * acc;
     }
     __syncthreads();
     T kk = 0;
-    for (int i = lane; i < m; i += 64) kk += w.vb[i] * w.pb[i];
+    for (int i = lane; i < m; i += 64) kk += vb[i] * w.pb[i];
     kk = eig_sum(kk, 64) * (tau * T(0.5));
-    // rank-2 update, row by row with the same thread layout as the product
-    // above: A22 -= v w^T + w v^T with w = p - kk v
-    for (int row = tid / TPR; row < m; row += NT / TPR) {
-      const int sub = tid - (tid / TPR) * TPR;
-      const T vi = w.vb[row], wi = w.pb[row] - kk * vi;
-      T* ar = A + (k + 1 + row) * lda + (k + 1);
-      for (int j = sub; j < m; j += TPR) {
-        const T vj = w.vb[j], wj = w.pb[j] - kk * vj;
-        ar[j] -= vi * wj + wi * vj;
+    // A22 -= v w^T + w v^T with w = p - kk v
+    if (wv == 0) {
+      // column 0 of A22 (rows lane and lane + 64), updated in registers
+      const T v0 = vb[0], w0 = w.pb[0] - kk * v0;
+      T c[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int r = lane + 64 * h;
+        c[h] = 0;
+        if (r < m) {
+          const T vi = vb[r], wi = w.pb[r] - kk * vi;
+          c[h] = A[(k + 1 + r) * lda + (k + 1)] - (vi * w0 + wi * v0);
+        }
+      }
+      if (next) {
+        // next column below its diagonal: x'[i] = c[i + 1], i < m - 1
+        T sig = 0;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int r = lane + 64 * h;
+          if (r >= 2 && r < m) sig += c[h] * c[h];
+        }
+        sig = eig_sum(sig, 64);
+        const T x0 = __shfl(c[0], 1, 64), diag = __shfl(c[0], 0, 64);
+        const T scale = eig_reflector(w, k + 1, x0, sig, diag);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int r = lane + 64 * h;
+          if (r >= 1 && r < m) {
+            const T vi = r == 1 ? T(1) : c[h] * scale;
+            vnext[r - 1] = vi;
+            A[(k + 1 + r) * lda + (k + 1)] = vi;
+          }
+        }
+      } else {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int r = lane + 64 * h;
+          if (r < m) A[(k + 1 + r) * lda + (k + 1)] = c[h];
+        }
+      }
+    } else {
+      // rows and columns 1.. of A22 (row 0 is never read again)
+      const int t = tid - 64;
+      const int sub = t % TPU;
+      for (int row = 1 + t / TPU; row < m; row += RGU) {
+        const T vi = vb[row], wi = w.pb[row] - kk * vi;
+        T* ar = A + (k + 1 + row) * lda + (k + 1);
+        for (int j = 1 + sub; j < m; j += TPU) {
+          const T vj = vb[j], wj = w.pb[j] - kk * vj;
+          ar[j] -= vi * wj + wi * vj;
+        }
       }
     }
     __syncthreads();
