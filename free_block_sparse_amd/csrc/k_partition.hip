@@ -739,6 +739,10 @@ __global__ __launch_bounds__(512) void k_kmeans_assign(AssignArgs a) {
       f32x16 acc[PB];
 #pragma unroll
       for (int pb = 0; pb < PB; ++pb) acc[pb] = cinit;
+      // the products at raised wave priority, the top-three updates at the
+      // normal one: the SIMD's other wave then fills the matrix core's
+      // gaps with its VALU work rather than both waves queueing MFMAs
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         const int o = (cb + col) * LDI + 16 * ks + 8 * half;
@@ -751,6 +755,7 @@ __global__ __launch_bounds__(512) void k_kmeans_assign(AssignArgs a) {
           acc[pb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, xh, acc[pb], 0, 0, 0);
         }
       }
+      __builtin_amdgcn_s_setprio(0);
 #pragma unroll
       for (int pb = 0; pb < PB; ++pb) seq3_add_block(st[pb], acc[pb], keep, cb >> 5, z0);
     }
