@@ -82,6 +82,8 @@ class SparseprHeadStats(ctypes.Structure):
         ("over_budget", ctypes.c_int),
         ("q_tiles", ctypes.c_int),
         ("kmeans_redecided", ctypes.c_int),
+        ("fit_fallback", ctypes.c_int),
+        ("reserved", ctypes.c_int),
         ("rho_route", ctypes.c_double),
         ("rho_exec", ctypes.c_double),
         ("sigma", ctypes.c_double * 4),

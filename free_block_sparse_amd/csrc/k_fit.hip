@@ -535,6 +535,7 @@ __global__ __launch_bounds__(1024) void k_fit(FitArgs a) {
     }
     block_sync();
   }
+  const bool fallback = rk > 0 && !ok;
   if (!ok) rk = 0;
   // outputs: W (d x R) and V (d x R) zero beyond rk, b = (ybar - xbar W) V^T
   for (int k = tid; k < rk; k += nt) {
@@ -559,6 +560,7 @@ __global__ __launch_bounds__(1024) void k_fit(FitArgs a) {
     a.rank[bh] = rk;
     if (a.stats) {
       a.stats[bh].residual_rank = rk;
+      a.stats[bh].fit_fallback = fallback ? 1 : 0;
       for (int i = 0; i < 4; ++i) a.stats[bh].sigma[i] = i < n ? sig_s[i] : 0.0;
     }
   }

@@ -704,6 +704,8 @@ __global__ __launch_bounds__(256) void k_route_emit(RouteArgs a) {
     if (a.fcount)
       for (int t = 0; t < 4 * a.T; ++t) red += a.fcount[(long long)bh * 4 * a.T + t];
     st.kmeans_redecided = red;
+    st.fit_fallback = 0;
+    st.reserved = 0;
     st.rho_route = (double)routed / nn;
     st.rho_exec = (double)(routed + (long long)a.M * a.N) / nn;
     for (int i = 0; i < 4; ++i) st.sigma[i] = 0.0;

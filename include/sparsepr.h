@@ -144,6 +144,9 @@ typedef struct {
   int q_tiles;                /* query tiles run by the sparse kernel */
   int kmeans_redecided;       /* k-means assignments re-decided in fp64 (both sides, all Lloyd
                                  steps; 0 when the partition was given) */
+  int fit_fallback;           /* 1 when the ridge system of the fit was not numerically positive
+                                 definite and the correction was dropped (residual_rank 0) */
+  int reserved;               /* 0 (keeps the structure free of padding) */
   double rho_route;           /* routed_pairs / N^2 */
   double rho_exec;            /* (routed_pairs + probe_pairs) / N^2 */
   double sigma[4];            /* leading singular values of the probe residuals */

@@ -269,6 +269,8 @@ def test_end_to_end_partition_agreement_and_error(name):
         kl_h, ql_h = kl[h].cpu().numpy(), ql[h].cpu().numpy()
         print(f"  head {h}: {stats[h]['kmeans_redecided']} k-means assignments re-decided in fp64 over "
               f"{2 * cfg.kmeans_iters} Lloyd steps of {c.n} points")
+        # every case's ridge system is positive definite: no head drops its correction
+        assert stats[h]["fit_fallback"] == 0
         if c.mode == "response_coupled":
             ref_k = oracle_key_labels_from_metric(name, h, mk[h].cpu().numpy())
             ref_q = oracle_query_labels_given_keys(name, h, kl_h)
