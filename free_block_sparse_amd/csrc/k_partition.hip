@@ -1154,9 +1154,10 @@ __global__ __launch_bounds__(1024) void k_group_scan(ScanArgs a) {
 }
 
 // Stable scatter of one chunk: the rank of a point among the earlier points
-// of its chunk with the same label.  Inside a wave, lanes with equal labels
-// are matched with one ballot per distinct label; earlier waves contribute
-// their per-label counts.
+// of its chunk with the same label.  Inside a wave, the lanes holding a
+// lane's label are the AND over the label's bits of one ballot per bit (or
+// its complement): ten ballots for up to 1024 groups, whatever the number of
+// distinct labels; earlier waves contribute their per-label counts.
 __global__ __launch_bounds__(256) void k_group_scatter(ScatterArgs a) {
   __shared__ int hist[4][kMaxGroups];
   const int bh = blockIdx.y, chunk = blockIdx.x, tid = threadIdx.x;
@@ -1166,17 +1167,16 @@ __global__ __launch_bounds__(256) void k_group_scatter(ScatterArgs a) {
   const int n = chunk * kChunk + tid;
   const int my = n < a.N ? a.labels[(long long)bh * a.N + n] : -1;
   const unsigned long long lt = (1ull << lane) - 1ull;
-  unsigned long long todo = __builtin_amdgcn_ballot_w64(my >= 0);
+  unsigned long long eq = __builtin_amdgcn_ballot_w64(my >= 0);
+  static_assert(kMaxGroups <= 1024, "ten label bits");
+  for (int b = 0; b < 10 && (a.gstride - 1) >> b; ++b) {
+    const unsigned long long bb = __builtin_amdgcn_ballot_w64(my >= 0 && ((my >> b) & 1));
+    eq &= ((my >> b) & 1) ? bb : ~bb;
+  }
   int rank = 0;
-  while (todo) {
-    const int leader = __builtin_ctzll(todo);
-    const int lab = __builtin_amdgcn_readlane(my, leader);
-    const unsigned long long m = __builtin_amdgcn_ballot_w64(my == lab);
-    if (my == lab) {
-      rank = __builtin_popcountll(m & lt);
-      if (lane == leader) hist[w][lab] = __builtin_popcountll(m);
-    }
-    todo &= ~m;
+  if (my >= 0) {
+    rank = __builtin_popcountll(eq & lt);
+    if (rank == 0) hist[w][my] = __builtin_popcountll(eq);  // the label's first lane
   }
   __syncthreads();
   if (my < 0) return;
