@@ -723,6 +723,7 @@ struct ProbeArgs {
   const uint32_t* gmask;
   int gwords;
   int N, M, GQ, n_pchunk;
+  int pchunk;        // keys per workgroup (a multiple of 64)
   float scale;
   float* ppart;  // [BH, n_pchunk, 2, M, D + 2]
   float* ode;
@@ -760,7 +761,7 @@ __global__ __launch_bounds__(256) void k_probe_attn_vec(ProbeArgs a) {
   }
   float md = -INFINITY, ld = 0.f, ms = -INFINITY, ls = 0.f;
   const float c = a.scale * 1.4426950408889634f;
-  const int k0 = ch * kProbeChunk, k1 = min(a.N, k0 + kProbeChunk);
+  const int k0 = ch * a.pchunk, k1 = min(a.N, k0 + a.pchunk);
   for (int kt0 = k0; kt0 < k1; kt0 += 32) {
     __syncthreads();
     for (int e = tid; e < 32 * D; e += 256) {
@@ -840,7 +841,7 @@ __global__ __launch_bounds__(256) void k_probe_attn_vec(ProbeArgs a) {
 }
 
 // Probe rows on the matrix cores (bf16 Q/K, fp16-scaled V).  One workgroup
-// of four waves takes 64 probe rows against one chunk of kProbeChunk keys.
+// of four waves takes 64 probe rows against one chunk of a.pchunk keys.
 // Waves 0 and 1 keep the dense online softmax (every key) of probes 0..31
 // and 32..63, one per lane column; waves 2 and 3 keep the sparse one (the
 // keys whose K/V group is granted to the probe's query group) of the same
@@ -862,7 +863,7 @@ __global__ __launch_bounds__(256, 2) void k_probe_attn_mfma(ProbeArgs a) {
   const int bh = blockIdx.z, pb = blockIdx.y, ch = blockIdx.x, tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63, half = lane >> 5, col = lane & 31;
   const bool sparse_role = w >= 2;
-  const int k0 = ch * kProbeChunk, k1 = min(a.N, k0 + kProbeChunk);
+  const int k0 = ch * a.pchunk, k1 = min(a.N, k0 + a.pchunk);
   const int L = k1 - k0;
   if (L <= 0) return;
   // grant masks of the probes' query groups
@@ -1200,6 +1201,7 @@ hipError_t launch_probe_attention(const Plan& p, hipStream_t s) {
   a.M = p.M;
   a.GQ = p.GQ;
   a.n_pchunk = p.n_pchunk;
+  a.pchunk = p.pchunk;
   a.scale = p.scale;
   a.ppart = p.ppart;
   a.ode = p.ode;

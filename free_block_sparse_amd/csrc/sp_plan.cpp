@@ -71,7 +71,16 @@ sparsepr_status plan_init(Plan* p, const sparsepr_config* cfg, int B, int H, int
   p->Dk = p->mode == SPARSEPR_PART_RESPONSE_COUPLED ? p->rKpad : d;
   p->nchunk = (int)cdiv(N, kChunk);
   p->max_tiles = (int)cdiv(N, kTileRows) + p->GQ;
-  p->n_pchunk = (int)cdiv(N, kProbeChunk);
+  {
+    // keys per probe workgroup: small calls split the keys finer, so that
+    // about kProbeSlots workgroups share the chip instead of a few long ones
+    const long long pblocks = cdiv(p->M > 0 ? p->M : 1, 64) * (long long)p->BH;
+    long long want = cdiv(cdiv((long long)N * pblocks, kProbeSlots), 64) * 64;
+    if (want < 64) want = 64;
+    if (want > kProbeChunkMax) want = kProbeChunkMax;
+    p->pchunk = (int)want;
+  }
+  p->n_pchunk = (int)cdiv(N, p->pchunk);
   p->gwords = (int)cdiv(p->GK, 32);
   float s = cfg->scale > 0.0f ? cfg->scale : (float)(1.0 / sqrt((double)d));
   p->scale = s;

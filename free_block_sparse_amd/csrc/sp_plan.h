@@ -11,7 +11,8 @@ namespace sp {
 
 constexpr int kChunk = 256;      // points per k-means histogram chunk
 constexpr int kTileRows = 128;   // query rows per sparse-attention workgroup
-constexpr int kProbeChunk = 1024;  // keys per probe-attention workgroup
+constexpr int kProbeChunkMax = 1024;  // most keys per probe-attention workgroup
+constexpr int kProbeSlots = 512;      // probe workgroups wanted per call (two per CU)
 constexpr int kMaxProbe = 256;
 constexpr int kMaxRank = 64;
 constexpr int kMaxGroups = 1024;
@@ -30,6 +31,7 @@ struct Plan {
   int centred_qc;    // query coordinates centred per query
   int nchunk;        // ceil(N / kChunk)
   int max_tiles;     // per (b,h) upper bound of query tiles
+  int pchunk;        // keys per probe-attention workgroup (a multiple of 64)
   int n_pchunk;      // probe key chunks per (b,h)
   int gwords;        // ceil(GK / 32)
   float scale, density, lambda, rank_cut;
