@@ -156,10 +156,12 @@ __global__ __launch_bounds__(256) void k_key_metric64(SampleArgs a) {
 // packed) behind the eigenvectors of the tridiagonal matrix (the leading rK
 // and the factorisation scratch, odd row stride); the shifted-QR fallback, and
 // ranks above 32, keep their eigenvector matrix in the workspace.
-template <int D>
-__global__ __launch_bounds__(1024) void k_key_eig(EigArgs a) {
+// NT threads per workgroup: 512 at d = 128 and 1024 at d = 64, the fastest
+// of 256, 512 and 1024 at each size (the steps are short, so fewer waves meet
+// at the barriers sooner, until the per-thread share of a step grows too long).
+template <int D, int NT>
+__global__ __launch_bounds__(NT) void k_key_eig(EigArgs a) {
   constexpr int LD = D + 1;  // odd row stride: column walks hit distinct banks
-  constexpr int NT = 1024;
   constexpr int RKL = 32;    // largest rK whose vectors share the LDS with the reflectors
   constexpr int NPK = D * (D - 1) / 2;
   constexpr int NA = D * LD > D * (2 * RKL + 1) + NPK ? D * LD : D * (2 * RKL + 1) + NPK;
@@ -237,7 +239,7 @@ __global__ __launch_bounds__(1024) void k_key_eig(EigArgs a) {
     }
   }
   __syncthreads();
-  eig_back_transform_packed<double, NT, 32>(wz, Rp, D, top, a.rK);
+  eig_back_transform_packed<double, NT, NT / 32>(wz, Rp, D, top, a.rK);
   // coordinate map: column k of kmap = s sqrt(lambda_k) u_k (also zero-padded
   // to rKpad columns)
   double* km = a.kmap + (long long)bh * D * a.rK;
@@ -1724,8 +1726,8 @@ hipError_t launch_key_eig(const Plan& p, hipStream_t s, bool all_eigenvalues) {
   // the call itself needs only the leading rK eigenpairs; the whole spectrum
   // is computed when it is reported
   EigArgs a{p.mk, p.eigval, p.kmap, p.kmap_pad, p.eigz, p.rK, p.rKpad, p.scale, all_eigenvalues ? p.d : p.rK};
-  if (p.d == 128) SP_LAUNCH(k_key_eig<128>, dim3(p.BH), dim3(1024), s, a);
-  else SP_LAUNCH(k_key_eig<64>, dim3(p.BH), dim3(1024), s, a);
+  if (p.d == 128) SP_LAUNCH((k_key_eig<128, 512>), dim3(p.BH), dim3(512), s, a);
+  else SP_LAUNCH((k_key_eig<64, 1024>), dim3(p.BH), dim3(1024), s, a);
   return hipSuccess;
 }
 
