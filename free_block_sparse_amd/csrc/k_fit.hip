@@ -123,57 +123,6 @@ __device__ void jacobi_sym_f64(double* A, double* V, int n, double* rcs, int* rp
   }
 }
 
-// In-place Cholesky (lower) of an SPD n x n matrix; returns false on a
-// non-positive pivot.  All threads call it.
-__device__ bool cholesky_f64(double* K, int n, int ld, int* bad) {
-  const int tid = threadIdx.x, nt = blockDim.x;
-  if (tid == 0) *bad = 0;
-  block_sync();
-  for (int k = 0; k < n; ++k) {
-    if (tid == 0) {
-      const double piv = K[k * ld + k];
-      if (!(piv > 0.0)) *bad = 1;
-      K[k * ld + k] = sqrt(piv > 0.0 ? piv : 1.0);
-    }
-    block_sync();
-    const double lkk = K[k * ld + k];
-    for (int i = k + 1 + tid; i < n; i += nt) K[i * ld + k] /= lkk;
-    block_sync();
-    const int m = n - k - 1;
-    for (int e = tid; e < m * m; e += nt) {
-      const int i = k + 1 + e / m, j = k + 1 + e % m;
-      if (j <= i) K[i * ld + j] -= K[i * ld + k] * K[j * ld + k];
-    }
-    block_sync();
-  }
-  return *bad == 0;
-}
-
-// Solve L L^T Y = Y in place for the nc columns of Y (row stride ldy), with
-// the lower Cholesky factor L (row stride ld).  Column-parallel: one pivot
-// at a time, its row scaled, then eliminated from the remaining rows.
-__device__ void chol_solve_f64(const double* L, int n, int ld, double* Y, int nc, int ldy) {
-  const int tid = threadIdx.x, nt = blockDim.x;
-  for (int j = 0; j < n; ++j) {
-    for (int c = tid; c < nc; c += nt) Y[j * ldy + c] /= L[j * ld + j];
-    block_sync();
-    for (int e = tid; e < (n - 1 - j) * nc; e += nt) {
-      const int i = j + 1 + e / nc, c = e - (e / nc) * nc;
-      Y[i * ldy + c] -= L[i * ld + j] * Y[j * ldy + c];
-    }
-    block_sync();
-  }
-  for (int i = n - 1; i >= 0; --i) {
-    for (int c = tid; c < nc; c += nt) Y[i * ldy + c] /= L[i * ld + i];
-    block_sync();
-    for (int e = tid; e < i * nc; e += nt) {
-      const int j = e / nc, c = e - (e / nc) * nc;
-      Y[j * ldy + c] -= L[i * ld + j] * Y[i * ldy + c];
-    }
-    block_sync();
-  }
-}
-
 // Sum over the workgroup (every thread gets the result); red holds one
 // double per wave.
 __device__ double block_sum_d(double v, double* red) {
@@ -204,6 +153,80 @@ __device__ inline double dot4(const TA* x, int sx, const TB* y, int sy, int n) {
   }
   for (; k < n; ++k) a0 += (double)x[k * sx] * (double)y[k * sy];
   return (a0 + a1) + (a2 + a3);
+}
+
+// In-place Cholesky (lower) of an SPD n x n matrix (n <= 128, row stride
+// ld, in LDS) and the solve L L^T Y = Y for the nc columns of Y (row stride
+// ldy).  Wave 0 factors column by column, lanes owning rows ln and ln + 64
+// (left-looking dot products); then every wave solves columns of Y, two at
+// a time, lanes as rows.  No workgroup barrier inside either; all threads
+// call it.  Returns false (all threads) on a non-positive pivot, with Y
+// untouched.
+__device__ bool chol_factor_solve128(double* K, int n, int ld, double* Y, int nc, int ldy, int* bad) {
+  const int tid = threadIdx.x, wv = tid >> 6, ln = tid & 63, nt = blockDim.x;
+  const int r0 = ln, r1 = ln + 64;
+  if (wv == 0) {
+    bool badl = false;
+    for (int k = 0; k < n; ++k) {
+      double a0 = 0.0, a1 = 0.0;
+      if (r0 < n && r0 >= k) a0 = K[r0 * ld + k] - dot4(K + r0 * ld, 1, K + k * ld, 1, k);
+      if (r1 < n && r1 >= k) a1 = K[r1 * ld + k] - dot4(K + r1 * ld, 1, K + k * ld, 1, k);
+      const double piv = __shfl(k < 64 ? a0 : a1, k & 63, 64);
+      badl |= !(piv > 0.0);
+      const double lkk = sqrt(piv > 0.0 ? piv : 1.0);
+      // a wave's LDS accesses complete in order, and the next column's reads
+      // may alias these writes, so they are not moved above them
+      if (r0 == k) K[k * ld + k] = lkk;
+      else if (r0 > k && r0 < n) K[r0 * ld + k] = a0 / lkk;
+      if (r1 == k) K[k * ld + k] = lkk;
+      else if (r1 > k && r1 < n) K[r1 * ld + k] = a1 / lkk;
+    }
+    if (ln == 0) *bad = badl ? 1 : 0;
+  }
+  block_sync();
+  if (*bad) return false;
+  const double dv0 = r0 < n ? 1.0 / K[r0 * ld + r0] : 0.0;
+  const double dv1 = r1 < n ? 1.0 / K[r1 * ld + r1] : 0.0;
+  const int nw = nt >> 6;
+  for (int c0 = wv; c0 < nc; c0 += 2 * nw) {
+    const int c1 = c0 + nw;
+    const bool two = c1 < nc;
+    // y[q][h]: column c_q, row ln + 64 h
+    double y00 = r0 < n ? Y[r0 * ldy + c0] : 0.0, y01 = r1 < n ? Y[r1 * ldy + c0] : 0.0;
+    double y10 = (two && r0 < n) ? Y[r0 * ldy + c1] : 0.0, y11 = (two && r1 < n) ? Y[r1 * ldy + c1] : 0.0;
+    for (int j = 0; j < n; ++j) {  // L z = y
+      const bool hi = j >= 64;
+      const double z0 = __shfl(hi ? y01 * dv1 : y00 * dv0, j & 63, 64);
+      const double z1 = __shfl(hi ? y11 * dv1 : y10 * dv0, j & 63, 64);
+      const double l0 = (r0 > j && r0 < n) ? K[r0 * ld + j] : 0.0;
+      const double l1 = (r1 > j && r1 < n) ? K[r1 * ld + j] : 0.0;
+      y00 = r0 == j ? z0 : y00 - l0 * z0;
+      y10 = r0 == j ? z1 : y10 - l0 * z1;
+      y01 = r1 == j ? z0 : y01 - l1 * z0;
+      y11 = r1 == j ? z1 : y11 - l1 * z1;
+    }
+    for (int i = n - 1; i >= 0; --i) {  // L^T x = z
+      const bool hi = i >= 64;
+      const double x0 = __shfl(hi ? y01 * dv1 : y00 * dv0, i & 63, 64);
+      const double x1 = __shfl(hi ? y11 * dv1 : y10 * dv0, i & 63, 64);
+      const double l0 = r0 < i ? K[i * ld + r0] : 0.0;
+      const double l1 = r1 < i ? K[i * ld + r1] : 0.0;
+      y00 = r0 == i ? x0 : y00 - l0 * x0;
+      y10 = r0 == i ? x1 : y10 - l0 * x1;
+      y01 = r1 == i ? x0 : y01 - l1 * x0;
+      y11 = r1 == i ? x1 : y11 - l1 * x1;
+    }
+    if (r0 < n) {
+      Y[r0 * ldy + c0] = y00;
+      if (two) Y[r0 * ldy + c1] = y10;
+    }
+    if (r1 < n) {
+      Y[r1 * ldy + c0] = y01;
+      if (two) Y[r1 * ldy + c1] = y11;
+    }
+  }
+  block_sync();
+  return true;
 }
 
 // MODE 1 (ALL_LDS): M <= 64 probes and r <= 32, so every matrix lives in
@@ -266,6 +289,30 @@ __global__ __launch_bounds__(1024) void k_fit(FitArgs a) {
   double* Kp = BIG ? Gb : Wm + 128 * 64 + 256 * 64;                          // primal system d x d (M > d)
   const float* ode = a.ode + (long long)bh * M * d;
   const float* osp = a.osp + (long long)bh * M * d;
+  // BIG: the products over R or Xc read an LDS copy of the M x d matrix
+  // (stride d + 1) held in the Gram block while that block is free; the
+  // symmetric results go through the global block Gt into the Gram block.
+  // (In the global slice, with one row per lane, these loops took most of
+  // the fit.)
+  double* const Gt = S + 256 * 128;
+  float* const Ls = reinterpret_cast<float*>(Gb);
+  const int lsd = d + 1;
+  auto stage_rows = [&](const float* src) __attribute__((always_inline)) {
+    block_sync();  // the Gram block's previous contents are no longer read
+    for (int e = tid; e < M * d; e += nt) {
+      const int mm = e / d, dm = e - (e / d) * d;
+      Ls[mm * lsd + dm] = src[mm * ldx + dm];
+    }
+    block_sync();
+  };
+  auto gt_to_lds = [&](double* dst, int nn, int ldd) __attribute__((always_inline)) {
+    block_sync();  // every product read the staged rows
+    for (int e = tid; e < nn * nn; e += nt) {
+      const int i = e / nn, j = e - (e / nn) * nn;
+      dst[i * ldd + j] = Gt[e];
+    }
+    block_sync();
+  };
   const double* wg = a.pw + (long long)bh * M;
   const double* w = wl;
 
@@ -301,22 +348,29 @@ __global__ __launch_bounds__(1024) void k_fit(FitArgs a) {
   block_sync();
   // Gram of the smaller side of D^(1/2) R (D = I unless the subspace is weighted):
   // sqrt(w_i w_j) r_i . r_j, or sum_m w_m r_m r_m^T
-  for (int e = tid; e < ne * ne; e += nt) {
-    const int i = e / ne, j = e - (e / ne) * ne;
-    double acc = 0.0;
-    if (i < n && j < n) {
-      if (small) {
-        acc = dot4(Rf + i * ldx, 1, Rf + j * ldx, 1, d);
-        if (a.weighted) acc *= sqrt(w[i]) * sqrt(w[j]);
-      } else if (a.weighted) {
-        for (int mm = 0; mm < M; ++mm) acc += w[mm] * ((double)Rf[mm * ldx + i] * (double)Rf[mm * ldx + j]);
-      } else {
-        for (int mm = 0; mm < M; ++mm) acc += (double)Rf[mm * ldx + i] * (double)Rf[mm * ldx + j];
+  {
+    const float* Rg = BIG ? Ls : Rf;
+    const int ldr = BIG ? lsd : ldx;
+    if (BIG) stage_rows(Rf);
+    for (int e = tid; e < ne * ne; e += nt) {
+      const int i = e / ne, j = e - (e / ne) * ne;
+      double acc = 0.0;
+      if (i < n && j < n) {
+        if (small) {
+          acc = dot4(Rg + i * ldr, 1, Rg + j * ldr, 1, d);
+          if (a.weighted) acc *= sqrt(w[i]) * sqrt(w[j]);
+        } else if (a.weighted) {
+          for (int mm = 0; mm < M; ++mm) acc += w[mm] * ((double)Rg[mm * ldr + i] * (double)Rg[mm * ldr + j]);
+        } else {
+          for (int mm = 0; mm < M; ++mm) acc += (double)Rg[mm * ldr + i] * (double)Rg[mm * ldr + j];
+        }
       }
+      if (BIG) Gt[e] = acc;
+      else G[i * ldg + j] = acc;
     }
-    G[i * ldg + j] = acc;
+    if (BIG) gt_to_lds(G, ne, ldg);
+    else block_sync();
   }
-  block_sync();
   bool fast = false;  // leading eigenpairs by multisection + twisted factorisations
   if (glds || BIG) {
     // Householder tridiagonalisation, then the leading eigenvalues by
@@ -345,12 +399,52 @@ __global__ __launch_bounds__(1024) void k_fit(FitArgs a) {
       rk_s = rk;
     }
     block_sync();
-    fast = eig_twisted<double, kFitThreads>(ew, ne, rk_s);
-    if (fast) {
-      eig_back_transform<double, kFitThreads, 16>(ew, ne, nullptr, rk_s);
+    if (BIG && rk_s <= 32) {
+      // As in the key eigensolve: the reflectors packed column-major behind
+      // an LDS block for the leading vectors (2 rk + 1 columns, the twisted
+      // factorisations' scratch included), so that the vectors are formed
+      // and transformed in LDS rather than in the global slice.  Element
+      // (r, c), r > c, of the reflectors goes to c (ne - 1) - c (c - 1) / 2 + r - c - 1.
+      constexpr int PERF = 128 * 128 / kFitThreads;
+      const int zl = 2 * rk_s + 1;
+      double* const Zl = Gb;
+      double* const Rp = Gb + ne * (2 * 32 + 1);
+      double t[PERF];
+#pragma unroll
+      for (int u = 0; u < PERF; ++u) {
+        const int e = tid + kFitThreads * u, r = e / ne, c = e - (e / ne) * ne;
+        t[u] = (e < ne * ne && r > c) ? G[r * ldg + c] : 0.0;
+      }
+      block_sync();
+#pragma unroll
+      for (int u = 0; u < PERF; ++u) {
+        const int e = tid + kFitThreads * u, r = e / ne, c = e - (e / ne) * ne;
+        if (e < ne * ne && r > c) Rp[c * (ne - 1) - (c * (c - 1)) / 2 + r - c - 1] = t[u];
+      }
+      block_sync();
+      const EigWork<double> wz{nullptr, 0, Zl, zl, edg, eeo, etau, evb, epb, erot, ectl};
+      fast = eig_twisted<double, kFitThreads>(wz, ne, rk_s);
+      if (fast) {
+        eig_back_transform_packed<double, kFitThreads, 32>(wz, Rp, ne, nullptr, rk_s);
+        // the leading vectors to the global slice, where the products below read them
+        for (int e = tid; e < ne * rk_s; e += nt) {
+          const int i = e / rk_s, c = e - (e / rk_s) * rk_s;
+          U[i * ldu + c] = Zl[i * zl + c];
+        }
+        block_sync();
+      } else {
+        const EigWork<double> wu{nullptr, 0, U, ldu, edg, eeo, etau, evb, epb, erot, ectl};
+        eig_tridiagonal_qr<double, kFitThreads>(wu, ne);
+        eig_back_transform_packed<double, kFitThreads, 32>(wu, Rp, ne, nullptr, ne);
+      }
     } else {
-      eig_tridiagonal_qr<double, kFitThreads>(ew, ne);
-      eig_back_transform<double, kFitThreads, 16>(ew, ne, nullptr, ne);
+      fast = eig_twisted<double, kFitThreads>(ew, ne, rk_s);
+      if (fast) {
+        eig_back_transform<double, kFitThreads, 16>(ew, ne, nullptr, rk_s);
+      } else {
+        eig_tridiagonal_qr<double, kFitThreads>(ew, ne);
+        eig_back_transform<double, kFitThreads, 16>(ew, ne, nullptr, ne);
+      }
     }
   } else {
     jacobi_sym_f64(G, U, ne, rcs, rpq, &stop, red);
@@ -384,6 +478,9 @@ __global__ __launch_bounds__(1024) void k_fit(FitArgs a) {
   }
   block_sync();
   int rk = rk_s;
+  const float* Rv = BIG ? Ls : Rf;
+  const int ldv = BIG ? lsd : ldx;
+  if (BIG) stage_rows(Rf);  // the eigen work in the Gram block is done
   // right singular vectors
   for (int e = tid; e < d * rk; e += nt) {
     const int dm = e / rk, k = e - (e / rk) * rk;
@@ -392,10 +489,10 @@ __global__ __launch_bounds__(1024) void k_fit(FitArgs a) {
     if (small && a.weighted) {
       // V = (D^(1/2) R)^T U / sigma
       double acc = 0.0;
-      for (int mm = 0; mm < M; ++mm) acc += (double)Rf[mm * ldx + dm] * (sqrt(w[mm]) * U[mm * ldu + ci]);
+      for (int mm = 0; mm < M; ++mm) acc += (double)Rv[mm * ldv + dm] * (sqrt(w[mm]) * U[mm * ldu + ci]);
       v = acc / sig_s[k];
     } else if (small) {
-      v = dot4(Rf + dm, ldx, U + ci, ldu, M) / sig_s[k];
+      v = dot4(Rv + dm, ldv, U + ci, ldu, M) / sig_s[k];
     } else {
       v = U[dm * ldu + ci];
     }
@@ -409,7 +506,7 @@ __global__ __launch_bounds__(1024) void k_fit(FitArgs a) {
     if (small && !a.weighted) {
       acc = U[mm * ldu + idx_s[k]] * sig_s[k];
     } else {
-      for (int dm = 0; dm < d; ++dm) acc += (double)Rf[mm * ldx + dm] * Vr[dm * Rmax + k];
+      for (int dm = 0; dm < d; ++dm) acc += (double)Rv[mm * ldv + dm] * Vr[dm * Rmax + k];
     }
     Yc[mm * rk + k] = acc;
   }
@@ -442,13 +539,19 @@ __global__ __launch_bounds__(1024) void k_fit(FitArgs a) {
     if (small) {
       // dual: K = D^1/2 Xc Xc^T D^1/2 + lambda I  (M x M) in the Gram buffer, rhs = D^1/2 Yc
       double* K = G;
+      const float* Xk = BIG ? Ls : Xf;
+      const int ldk = BIG ? lsd : ldx;
+      if (BIG) stage_rows(Xf);
       for (int e = tid; e < M * M; e += nt) {
         const int i = e / M, j = e - (e / M) * M;
-        const double acc = dot4(Xf + i * ldx, 1, Xf + j * ldx, 1, d);
-        K[i * ldg + j] = sqrt(w[i] * w[j]) * acc + (i == j ? lam : 0.0);
+        const double acc = dot4(Xk + i * ldk, 1, Xk + j * ldk, 1, d);
+        const double kij = sqrt(w[i] * w[j]) * acc + (i == j ? lam : 0.0);
+        if (BIG) Gt[e] = kij;
+        else K[i * ldg + j] = kij;
       }
       for (int e = tid; e < M * rk; e += nt) Yc[e] *= sqrt(w[e / rk]);
-      block_sync();
+      if (BIG) gt_to_lds(K, M, ldg);
+      else block_sync();
       if (M <= 64) {
         // one wave factors K column by column (lane i owns row i of L, left-
         // looking dot products), then every wave solves its columns of Y with
@@ -502,36 +605,42 @@ __global__ __launch_bounds__(1024) void k_fit(FitArgs a) {
         }
         block_sync();
       } else {
-        ok = cholesky_f64(K, M, ldg, &bad);
-        if (ok) chol_solve_f64(K, M, ldg, Yc, rk, rk);
+        ok = chol_factor_solve128(K, M, ldg, Yc, rk, rk, &bad);
       }
       if (ok) {
         // W = Xc^T D^1/2 Y
         for (int e = tid; e < M * rk; e += nt) Yc[e] *= sqrt(w[e / rk]);
-        block_sync();
+        const float* Xw = BIG ? Ls : Xf;
+        const int ldw = BIG ? lsd : ldx;
+        if (BIG) stage_rows(Xf);  // the factor is no longer read
+        else block_sync();
         for (int e = tid; e < d * rk; e += nt) {
           const int dm = e / rk, k = e - (e / rk) * rk;
-          Wm[dm * rk + k] = dot4(Xf + dm, ldx, Yc + k, rk, M);
+          Wm[dm * rk + k] = dot4(Xw + dm, ldw, Yc + k, rk, M);
         }
       }
     } else {
       // primal: K = Xc^T D Xc + lambda I (d x d), rhs = Xc^T D Yc (d x rk)
       double* K = Kp;
+      const float* Xp = BIG ? Ls : Xf;
+      const int ldp = BIG ? lsd : ldx;
+      if (BIG) stage_rows(Xf);
       for (int e = tid; e < d * d; e += nt) {
         const int i = e / d, j = e - (e / d) * d;
         double acc = 0.0;
-        for (int mm = 0; mm < M; ++mm) acc += w[mm] * (double)Xf[mm * ldx + i] * (double)Xf[mm * ldx + j];
-        K[e] = acc + (i == j ? lam : 0.0);
+        for (int mm = 0; mm < M; ++mm) acc += w[mm] * (double)Xp[mm * ldp + i] * (double)Xp[mm * ldp + j];
+        if (BIG) Gt[e] = acc + (i == j ? lam : 0.0);
+        else K[e] = acc + (i == j ? lam : 0.0);
       }
       for (int e = tid; e < d * rk; e += nt) {
         const int i = e / rk, k = e - (e / rk) * rk;
         double acc = 0.0;
-        for (int mm = 0; mm < M; ++mm) acc += w[mm] * (double)Xf[mm * ldx + i] * Yc[mm * rk + k];
+        for (int mm = 0; mm < M; ++mm) acc += w[mm] * (double)Xp[mm * ldp + i] * Yc[mm * rk + k];
         Wm[e] = acc;
       }
-      block_sync();
-      ok = cholesky_f64(K, d, d, &bad);
-      if (ok) chol_solve_f64(K, d, d, Wm, rk, rk);
+      if (BIG) gt_to_lds(K, d, d);
+      else block_sync();
+      ok = chol_factor_solve128(K, d, d, Wm, rk, rk, &bad);
     }
     block_sync();
   }
