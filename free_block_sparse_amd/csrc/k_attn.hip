@@ -1095,8 +1095,9 @@ __global__ __launch_bounds__(D) void k_probe_merge(ProbeArgs a) {
 template <typename T>
 __global__ __launch_bounds__(256) void k_probe_overwrite(MutView4 o, const int* perm_q, const int* ppos,
                                                          const float* ode, int N, int M, int D) {
+  // one element per thread: the row lookups of every element run at once
   const int bh = blockIdx.x;
-  for (int e = threadIdx.x; e < M * D; e += 256) {
+  for (int e = blockIdx.y * 256 + threadIdx.x; e < M * D; e += gridDim.y * 256) {
     const int p = e / D, dm = e - (e / D) * D;
     const int token = perm_q[(long long)bh * N + ppos[(long long)bh * M + p]];
     T* row = static_cast<T*>(o.p) + o.row_off(bh, token);
@@ -1226,11 +1227,11 @@ hipError_t launch_probe_attention(const Plan& p, hipStream_t s) {
 hipError_t launch_probe_overwrite(const Plan& p, hipStream_t s) {
   if (p.M <= 0) return hipSuccess;
   if (p.dtype == SPARSEPR_BF16)
-    hipLaunchKernelGGL(k_probe_overwrite<bf16_t>, dim3(p.BH), dim3(256), 0, s, p.o, p.perm_q, p.ppos, p.ode, p.N,
-                       p.M, p.d);
+    hipLaunchKernelGGL(k_probe_overwrite<bf16_t>, dim3(p.BH, (p.M * p.d + 255) / 256), dim3(256), 0, s, p.o, p.perm_q,
+                       p.ppos, p.ode, p.N, p.M, p.d);
   else
-    hipLaunchKernelGGL(k_probe_overwrite<float>, dim3(p.BH), dim3(256), 0, s, p.o, p.perm_q, p.ppos, p.ode, p.N,
-                       p.M, p.d);
+    hipLaunchKernelGGL(k_probe_overwrite<float>, dim3(p.BH, (p.M * p.d + 255) / 256), dim3(256), 0, s, p.o, p.perm_q,
+                       p.ppos, p.ode, p.N, p.M, p.d);
   return hipGetLastError();
 }
 

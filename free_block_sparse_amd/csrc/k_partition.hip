@@ -1614,14 +1614,27 @@ __global__ __launch_bounds__(256) void k_vmax(View4 v, int N, int d, uint32_t* v
   const int cpr = d / VEC;
   const long long total = (long long)N * cpr;
   float m = 0.f;
-  for (long long e = (long long)blockIdx.x * 256 + threadIdx.x; e < total; e += (long long)gridDim.x * 256) {
-    const int row = (int)(e / cpr), c = (int)(e - (e / cpr) * cpr) * VEC;
-    const uint4 u = *reinterpret_cast<const uint4*>(static_cast<const T*>(v.p) + v.row_off(bh, row) + c);
-    const T* ev = reinterpret_cast<const T*>(&u);
+  // four 16-byte loads in flight per thread
+  const long long stride = (long long)gridDim.x * 256;
+  for (long long e0 = (long long)blockIdx.x * 256 + threadIdx.x; e0 < total; e0 += 4 * stride) {
+    uint4 u[4];
 #pragma unroll
-    for (int j = 0; j < VEC; ++j) {
-      const float x = fabsf(Elem<T>::load(ev + j));
-      m = (x > m || x != x) ? x : m;
+    for (int q = 0; q < 4; ++q) {
+      const long long e = e0 + q * stride;
+      u[q] = make_uint4(0, 0, 0, 0);
+      if (e < total) {
+        const int row = (int)(e / cpr), c = (int)(e - (e / cpr) * cpr) * VEC;
+        u[q] = *reinterpret_cast<const uint4*>(static_cast<const T*>(v.p) + v.row_off(bh, row) + c);
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const T* ev = reinterpret_cast<const T*>(&u[q]);
+#pragma unroll
+      for (int j = 0; j < VEC; ++j) {
+        const float x = fabsf(Elem<T>::load(ev + j));
+        m = (x > m || x != x) ? x : m;
+      }
     }
   }
   for (int o = 32; o > 0; o >>= 1) {
