@@ -594,7 +594,7 @@ __global__ __launch_bounds__(256) void k_fit_pack(const float* fitW, const float
   bf16_t* wl = wh + (long long)Rp * D;
   bf16_t* vh = wl + (long long)Rp * D;
   bf16_t* vl = vh + (long long)Rp * D;
-  for (int e = threadIdx.x; e < D * Rp; e += 256) {
+  for (int e = blockIdx.y * 256 + threadIdx.x; e < D * Rp; e += gridDim.y * 256) {
     const int dm = e / Rp, j = e - (e / Rp) * Rp;
     const bool in = j < rank && j < R;
     const float wv = in ? fitW[((long long)bh * D + dm) * R + j] : 0.f;
@@ -1163,7 +1163,8 @@ static hipError_t launch_attn(AttnArgs a, int grid_x, int BH, int d, int dtype, 
 hipError_t launch_sparse_attention(const Plan& p, bool correct, hipStream_t s) {
   AttnArgs a = attn_args(p, correct);
   if (a.correct && p.dtype == SPARSEPR_BF16) {
-    hipLaunchKernelGGL(k_fit_pack, dim3(p.BH), dim3(256), 0, s, p.fitW, p.fitV, p.fitrank, p.d, a.R, p.Rp, p.fitpk);
+    hipLaunchKernelGGL(k_fit_pack, dim3(p.BH, (p.d * p.Rp + 255) / 256), dim3(256), 0, s, p.fitW, p.fitV, p.fitrank,
+                       p.d, a.R, p.Rp, p.fitpk);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -1104,9 +1104,16 @@ __global__ __launch_bounds__(1024) void k_group_scan(ScanArgs a) {
   const int c0 = act ? (int)((long long)pt * nch / P) : 0;
   const int c1 = act ? (int)((long long)(pt + 1) * nch / P) : 0;
   const int* cnt = a.counts + (long long)bh * nch * a.gstride;
-  // loads eight at a time, so they are in flight together
+  // the thread's first CV counts are loaded together and kept in registers
+  // for the second pass; any further ones are loaded eight at a time
+  constexpr int CV = 32;
+  int cv[CV];
+#pragma unroll
+  for (int u = 0; u < CV; ++u) cv[u] = c0 + u < c1 ? cnt[(long long)(c0 + u) * a.gstride + g] : 0;
   int sum = 0;
-  int c = c0;
+#pragma unroll
+  for (int u = 0; u < CV; ++u) sum += cv[u];
+  int c = c0 + CV;
   for (; c + 8 <= c1; c += 8) {
     int v[8];
 #pragma unroll
@@ -1138,7 +1145,13 @@ __global__ __launch_bounds__(1024) void k_group_scan(ScanArgs a) {
   if (tid == 0) off[G] = a.N;
   for (int q = 0; q < pt; ++q) base += part[q * G + g];
   int* co = a.chunkoff + (long long)bh * nch * a.gstride;
-  int c2 = c0;
+#pragma unroll
+  for (int u = 0; u < CV; ++u)
+    if (c0 + u < c1) {
+      co[(long long)(c0 + u) * a.gstride + g] = base;
+      base += cv[u];
+    }
+  int c2 = c0 + CV;
   for (; c2 + 8 <= c1; c2 += 8) {
     int v[8];
 #pragma unroll
