@@ -165,6 +165,7 @@ __device__ inline double dot4(const TA* x, int sx, const TB* y, int sy, int n) {
 __device__ bool chol_factor_solve128(double* K, int n, int ld, double* Y, int nc, int ldy, int* bad) {
   const int tid = threadIdx.x, wv = tid >> 6, ln = tid & 63, nt = blockDim.x;
   const int r0 = ln, r1 = ln + 64;
+  if (n > 128) return false;  // two rows per lane at most (the callers' orders are <= 128)
   if (wv == 0) {
     bool badl = false;
     for (int k = 0; k < n; ++k) {
